@@ -1,0 +1,243 @@
+/*
+ * lca.h — C ABI of the MI355X (gfx950) hybrid compressed attention library.
+ *
+ * The library implements the attention hot path described on the source pages
+ * (DeepSeek-V4 hybrid attention): the CSA path (token compressor with m = 4,
+ * Lightning Indexer scores, top-k selection, multi-query attention over the
+ * selected compressed entries plus a 128-token raw sliding window and a
+ * learnable sink logit) and the HCA path (m' = 128 compression and dense
+ * multi-query attention over all compressed entries plus the same window and
+ * sink). Page short names in citations:
+ *   [PACMAN] "DeepSeek-V4 technical report share" (THU PACMAN group, 10100.com)
+ *   [Qiaomu] "DeepSeek-V4论文解析" (乔木博客 mirror)
+ *   [cdjax]  "未来科技" DeepSeek-V4 essay (cdjax.com)
+ *   [kwkr]   kwkr.cn DeepSeek-V4 report walk-through
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are device pointers to contiguous, row-major memory with the
+ *   batch index outermost. The caller owns every buffer; the library never
+ *   allocates, frees or synchronises. Scratch memory comes from a caller
+ *   workspace sized by the matching *_workspace() call.
+ * - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *   Kernels are enqueued asynchronously on it; execution errors surface at
+ *   the caller's next synchronisation.
+ * - Every argument is validated on the host before anything is launched, so
+ *   a non-zero status means nothing was enqueued and nothing was written.
+ *   The text of the last error of the calling thread is in lca_last_error().
+ * - Query t of a call sits at absolute position q_pos0 + t (the same for all
+ *   sequences of the batch). Compressed entry j covers tokens [j*m, (j+1)*m)
+ *   and is visible to a query at position p iff j < (p + 1) / m.
+ * - A window buffer `win` has W - 1 + Tq rows per sequence; row r holds the
+ *   raw KV of position q_pos0 - (W - 1) + r. Rows at negative positions are
+ *   never read. A query at p attends positions [max(0, p - W + 1), p].
+ * - Results are bitwise deterministic run to run, and the result of sequence
+ *   b does not depend on B or on the other sequences (work splits depend only
+ *   on per-sequence shapes).
+ * - Device pointers must be 16-byte aligned; float32 side arrays 4-byte.
+ */
+#ifndef LCA_H
+#define LCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define LCA_OK               0
+#define LCA_ERR_ARG         (-1) /* null pointer, bad dimension or position */
+#define LCA_ERR_UNSUPPORTED (-2) /* dtype / shape combination not built     */
+#define LCA_ERR_ALIGN       (-3) /* pointer not 16-byte aligned             */
+#define LCA_ERR_WORKSPACE   (-4) /* workspace null or too small             */
+#define LCA_ERR_HIP         (-5) /* kernel launch failed (see last_error)   */
+
+/* ---- element formats --------------------------------------------------- */
+#define LCA_F32       0 /* float32                                             */
+#define LCA_BF16      1 /* bfloat16 stored as uint16                            */
+#define LCA_KV_MIXED  2 /* KV row: (D - R) e4m3fn bytes, then R bf16 values;
+                           plus one float32 scale per row in a side array.
+                           [cdjax] §1.1: RoPE channels BF16, the rest FP8.      */
+#define LCA_MXFP4     3 /* e2m1 codes packed two per byte (element 2i in the
+                           low nibble), one e8m0 scale byte per 32 elements in
+                           a side array. [Qiaomu] FP4量化感知训练, [kwkr] §3.4:
+                           the indexer QK path runs in FP4.                     */
+
+/* ---- flags ------------------------------------------------------------- */
+#define LCA_NORM        1u /* compress: RMSNorm of each entry (gain norm_w)    */
+#define LCA_ROPE        2u /* compress: RoPE of the last rope_dims channels at
+                              the block start position pos0 + j*m             */
+#define LCA_INV_ROPE    4u /* attend: rotate the output's last rope_dims
+                              channels by the negative query position         */
+#define LCA_SCORE_BF16  8u /* index_topk: round scores to bf16 before top-k    */
+
+/* ---------------------------------------------------------------------------
+ * csa_compress — gated softmax-weighted token compressor (CSA and HCA).
+ *
+ * [kwkr] §3.1: two independent KV sequences are merged with softmax-normalised
+ * gate weights, and adjacent compressed blocks overlap. [Qiaomu] 混合注意力机制:
+ * every 4 tokens fold into one entry (CSA); HCA folds every 128 ([PACMAN] §3.2).
+ *
+ * With overlap = 1, entry j = sum over the 2m rows {stream a, block j-1} and
+ * {stream b, block j} of softmax(their gate logits) * row. For j = 0 the
+ * block j-1 rows are prev_ca / prev_za (the last m tokens of stream a before
+ * this call) or, when prev_ca is NULL, absent. With overlap = 0 only stream b
+ * is used (ca, za, prev_* must be NULL). The trailing T % m tokens emit nothing.
+ * Then, per flags: RMSNorm (norm_w [D], eps), RoPE at position pos0 + j*m
+ * (interleaved channel pairs of the last rope_dims channels, frequency
+ * rope_base^(-2i/rope_dims)), then conversion to dt_out.
+ *
+ *   ca, cb    [B, T, D]   dt_in (LCA_F32 or LCA_BF16)
+ *   za, zb    [B, T]      float32 gate logits
+ *   prev_ca   [B, m, D]   dt_in, prev_za [B, m] float32 (both NULL or both set)
+ *   out       [B, out_rows, ...] entry j of sequence b at row b*out_rows + j:
+ *               LCA_F32 / LCA_BF16: D values;
+ *               LCA_KV_MIXED: D - rope_dims + 2*rope_dims bytes,
+ *                             out_scale float32 [B, out_rows];
+ *               LCA_MXFP4: D/2 bytes, out_scale uint8 [B, out_rows, D/32].
+ *   out_rows  row stride per sequence (>= T/m), lets entries land inside a
+ *             larger cache; 0 means T/m.
+ * Requirements: B >= 1, T >= 0, m >= 1, D % 32 == 0, D <= 1024,
+ *   pos0 % m == 0, rope_dims even and <= D (0 with no LCA_ROPE unless
+ *   dt_out is LCA_KV_MIXED, where it sets the bf16 channel count).
+ * ------------------------------------------------------------------------- */
+int csa_compress(void* stream, int dt_in, int dt_out, int B, int T, int D, int m,
+                 int overlap, int64_t pos0,
+                 const void* ca, const float* za, const void* cb, const float* zb,
+                 const void* prev_ca, const float* prev_za,
+                 uint32_t flags, const float* norm_w, float eps,
+                 float rope_base, int rope_dims,
+                 void* out, void* out_scale, int64_t out_rows);
+
+/* ---------------------------------------------------------------------------
+ * lca_quantize_rows — quantise-on-write of float32 rows to a storage format.
+ *
+ * LCA_KV_MIXED ([cdjax] §1.1): per row s = amax/448 over the first D - R
+ * channels (float32 division; s = 1 if amax = 0); byte c = e4m3fn(x_c / s),
+ * round to nearest even, saturating at 448; the last R channels are bf16
+ * (round to nearest even). out [n_rows, D - R + 2R] bytes, out_scale float32
+ * [n_rows].
+ * LCA_MXFP4 ([kwkr] §3.4, OCP MX v1.0): per block of 32 channels, E8M0 scale
+ * X = 2^(floor(log2 amax) - 2) (byte 0 and zero codes if amax = 0); element
+ * code e2m1(x / X), round to nearest even, saturating at 6. out [n_rows, D/2],
+ * out_scale uint8 [n_rows, D/32].
+ * Requirements: n_rows >= 0, D % 32 == 0, D <= 1024; MIXED: 0 <= R <= D, R even.
+ * ------------------------------------------------------------------------- */
+int lca_quantize_rows(void* stream, int dt_out, int64_t n_rows, int D, int rope_dims,
+                      const float* src, void* out, void* out_scale);
+
+/* ---------------------------------------------------------------------------
+ * csa_index_topk — Lightning Indexer scores of every visible entry + top-k.
+ *
+ * [Qiaomu] 混合注意力机制: cheap indexer queries score every compressed block and
+ * the top-k most relevant are kept; [PACMAN] §3.1: k = 512 (Flash) / 1024
+ * (Pro). Score (the pages print no formula; [kwkr] §3.1 says CSA runs
+ * DeepSeek Sparse Attention on the entries): s_j = sum_h w_h * relu(qI_h . kI_j)
+ * over the H_I indexer heads, for j < n_vis = (q_pos0 + t + 1) / m, accumulated
+ * in float32. With LCA_SCORE_BF16 each score is rounded to bf16 first
+ * ([Qiaomu] FP4量化感知训练: BF16 scores make top-k twice as fast).
+ * Selection: the min(k, n_vis) largest scores, ties to the lower index.
+ *
+ *   dt        LCA_F32, LCA_BF16 (qI and kI in that type) or LCA_MXFP4
+ *             (qI and kI packed e2m1, scales in qI_scale / kI_scale)
+ *   qI        [B, Tq, H_I, d_I]       qI_scale [B, Tq, H_I, d_I/32] (MXFP4)
+ *   w         [B, Tq, H_I] float32
+ *   kI        [B, N_cap, d_I]         kI_scale [B, N_cap, d_I/32]  (MXFP4)
+ *   idx_out   [B, Tq, k] int32: the selected entries in increasing index
+ *             order, then -1 padding
+ *   score_out [B, Tq, k] float32 or NULL: the score of each idx_out entry
+ *             (-inf for padding)
+ * Requirements: N_cap >= n_vis of the last query; 1 <= k <= 4096;
+ *   d_I % 32 == 0 and d_I <= 256; H_I in {1, 2, 4, 8, 16} for LCA_BF16 and
+ *   LCA_MXFP4 (any H_I <= 64 for LCA_F32); MXFP4 needs d_I == 128.
+ * ------------------------------------------------------------------------- */
+size_t csa_index_topk_workspace(int dt, int B, int Tq, int H_I, int d_I, int64_t N_cap,
+                                int m, int k, int64_t q_pos0, uint32_t flags);
+int csa_index_topk(void* stream, int dt, int B, int Tq, int H_I, int d_I, int64_t N_cap,
+                   int m, int k, int64_t q_pos0,
+                   const void* qI, const void* qI_scale, const float* w,
+                   const void* kI, const void* kI_scale, uint32_t flags,
+                   int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------
+ * csa_attend — CSA core attention over selected entries + window + sink.
+ *
+ * [PACMAN] §3.1: only the top-k compressed entries are attended, plus a recent
+ * uncompressed window; [kwkr] §3.3: the 128 window rows join the core
+ * computation together with the sink (a learnable term in the softmax
+ * denominator); [cdjax] §1.1: multi-query form (one KV row serves as key and
+ * value for every head) and RoPE at the negative query position on the output.
+ *
+ * For query t (position p) and head h, over rows X = {kv[idx[t, i]] : idx >= 0}
+ * followed by the window rows of positions [max(0, p-W+1), p]:
+ *   l_x = scale * q_h . x,  M = max(sink_h, max l),
+ *   Z = exp(sink_h - M) + sum exp(l_x - M),  out = sum exp(l_x - M) x / Z,
+ *   lse = M + log Z; with LCA_INV_ROPE the last rope_dims channels of out are
+ *   rotated by -p.
+ *
+ *   dt_q      LCA_F32 or LCA_BF16 (q and out)
+ *   dt_kv     LCA_F32 (with dt_q = LCA_F32), LCA_BF16 or LCA_KV_MIXED
+ *   q         [B, Tq, H, D]            out [B, Tq, H, D] dt_q
+ *   kv        [B, N_cap, D] (MIXED: row of D - rope_dims + 2*rope_dims bytes,
+ *             kv_scale float32 [B, N_cap])
+ *   idx       [B, Tq, k] int32; entries < 0 or >= N_cap are skipped
+ *   win       [B, W - 1 + Tq, D] same format as kv (win_scale [B, W-1+Tq])
+ *   sink      [H] float32
+ *   lse_out   [B, Tq, H] float32 or NULL
+ * Requirements: D % 32 == 0, D <= 512; H % 16 == 0 unless dt_kv == LCA_F32;
+ *   1 <= W <= 4096; 1 <= k <= 4096; q_pos0 >= 0.
+ * ------------------------------------------------------------------------- */
+size_t csa_attend_workspace(int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+                            int m, int k, int W, int64_t q_pos0);
+int csa_attend(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+               int m, int k, int W, int64_t q_pos0,
+               const void* q, const void* kv, const float* kv_scale, const int32_t* idx,
+               const void* win, const float* win_scale, const float* sink, float scale,
+               uint32_t flags, float rope_base, int rope_dims,
+               void* out, float* lse_out, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------
+ * hca_attend — HCA dense attention over every visible entry + window + sink.
+ *
+ * [PACMAN] §3.2 and [kwkr] §3.2: no sparse selection; dense multi-query
+ * attention over all heavily compressed entries (m' = 128), with the same
+ * sliding window and sink as CSA. Identical to csa_attend with the selected
+ * set replaced by all entries j < (p + 1) / m. Arguments as for csa_attend.
+ * ------------------------------------------------------------------------- */
+size_t hca_attend_workspace(int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+                            int m, int W, int64_t q_pos0);
+int hca_attend(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+               int m, int W, int64_t q_pos0,
+               const void* q, const void* kv, const float* kv_scale,
+               const void* win, const float* win_scale, const float* sink, float scale,
+               uint32_t flags, float rope_base, int rope_dims,
+               void* out, float* lse_out, void* ws, size_t ws_bytes);
+
+/* ---- diagnostics ------------------------------------------------------- */
+const char* lca_status_str(int status);
+const char* lca_last_error(void); /* thread-local text of the last failure */
+int lca_version(void);            /* major*10000 + minor*100 + patch       */
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing (diagnostic; not for production paths). When enabled, every
+ * kernel the library enqueues is bracketed by a pair of HIP events recorded
+ * on the caller's stream. lca_profile_collect waits for those events, sums
+ * the durations per kernel name into `out` (at most max_entries, returns the
+ * count written, or a negative status) and clears the record. This is the
+ * one piece of process-global state; do not enable it while several threads
+ * call the library.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  char name[64];
+  int64_t launches;
+  double total_ms;
+} lca_kernel_stat;
+int lca_profile_enable(int on);
+int lca_profile_collect(lca_kernel_stat* out, int max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCA_H */

@@ -1,0 +1,212 @@
+"""MI355X (gfx950) hybrid compressed attention: CSA / HCA hot path.
+
+Thin ctypes binding over ``liblca.so`` (C ABI declared in ``include/lca.h``).
+Each function here only marshals arguments: tensor pointers, shapes read from
+the tensors, the current HIP stream, and a workspace tensor when the caller
+gives none. Every step of the computation runs in the library's HIP kernels;
+there is no fallback. If the library is missing, the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "F32", "BF16", "KV_MIXED", "MXFP4",
+    "NORM", "ROPE", "INV_ROPE", "SCORE_BF16",
+    "LcaError", "lib", "lib_path",
+    "csa_compress", "lca_quantize_rows",
+    "csa_index_topk", "csa_index_topk_workspace",
+    "csa_attend", "csa_attend_workspace",
+    "hca_attend", "hca_attend_workspace",
+    "lca_version", "lca_profile_enable", "lca_profile_collect",
+]
+
+F32, BF16, KV_MIXED, MXFP4 = 0, 1, 2, 3
+NORM, ROPE, INV_ROPE, SCORE_BF16 = 1, 2, 4, 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "liblca.so")
+_LIB = None
+
+
+class LcaError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"lca status {status}: {text}")
+        self.status = status
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+def _declare(L):
+    vp, i32, i64, u32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
+    sz = ctypes.c_size_t
+    L.csa_compress.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp,
+                               u32, vp, f32, f32, i32, vp, vp, i64]
+    L.csa_compress.restype = i32
+    L.lca_quantize_rows.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp]
+    L.lca_quantize_rows.restype = i32
+    L.csa_index_topk_workspace.argtypes = [i32, i32, i32, i32, i32, i64, i32, i32, i64, u32]
+    L.csa_index_topk_workspace.restype = sz
+    L.csa_index_topk.argtypes = [vp, i32, i32, i32, i32, i32, i64, i32, i32, i64, vp, vp, vp, vp, vp,
+                                 u32, vp, vp, vp, sz]
+    L.csa_index_topk.restype = i32
+    L.csa_attend_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, i64]
+    L.csa_attend_workspace.restype = sz
+    L.csa_attend.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, i64, vp, vp, vp, vp,
+                             vp, vp, vp, f32, u32, f32, i32, vp, vp, vp, sz]
+    L.csa_attend.restype = i32
+    L.hca_attend_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, i32, i64]
+    L.hca_attend_workspace.restype = sz
+    L.hca_attend.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i64, vp, vp, vp, vp, vp,
+                             vp, f32, u32, f32, i32, vp, vp, vp, sz]
+    L.hca_attend.restype = i32
+    L.lca_status_str.argtypes = [i32]
+    L.lca_status_str.restype = ctypes.c_char_p
+    L.lca_last_error.argtypes = []
+    L.lca_last_error.restype = ctypes.c_char_p
+    L.lca_version.argtypes = []
+    L.lca_version.restype = i32
+    L.lca_profile_enable.argtypes = [i32]
+    L.lca_profile_enable.restype = i32
+    L.lca_profile_collect.argtypes = [ctypes.POINTER(KernelStat), i32]
+    L.lca_profile_collect.restype = i32
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is missing: build it with "
+                               "`python -m long_context_attention_12_amd.build`")
+        L = ctypes.CDLL(lib_path)
+        _declare(L)
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int):
+    if status != 0:
+        raise LcaError(status, lib().lca_last_error().decode())
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _workspace(nbytes: int, like: torch.Tensor):
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=like.device)
+
+
+# ---------------------------------------------------------------------------
+
+def csa_compress(dt_in, dt_out, cb, zb, m, *, ca=None, za=None, prev_ca=None, prev_za=None,
+                 overlap=True, pos0=0, flags=0, norm_w=None, eps=1e-6, rope_base=10000.0,
+                 rope_dims=0, out=None, out_scale=None, out_rows=0, stream=None):
+    """Token compressor; see csa_compress in include/lca.h. cb: [B, T, D]."""
+    B, T, D = cb.shape
+    st = lib().csa_compress(_stream(stream), dt_in, dt_out, B, T, D, m, 1 if overlap else 0, pos0,
+                            _p(ca), _p(za), _p(cb), _p(zb), _p(prev_ca), _p(prev_za), flags,
+                            _p(norm_w), eps, rope_base, rope_dims, _p(out), _p(out_scale), out_rows)
+    _check(st)
+
+
+def lca_quantize_rows(dt_out, src, out, out_scale, *, rope_dims=64, stream=None):
+    """Quantise float32 rows [n, D] to KV_MIXED or MXFP4; see include/lca.h."""
+    D = src.shape[-1]
+    n = src.numel() // D
+    _check(lib().lca_quantize_rows(_stream(stream), dt_out, n, D, rope_dims, _p(src), _p(out),
+                                   _p(out_scale)))
+
+
+def csa_index_topk_workspace(dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0, flags=0):
+    return int(lib().csa_index_topk_workspace(dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0, flags))
+
+
+def csa_index_topk(dt, qI, w, kI, idx_out, *, m, k, q_pos0, d_I=None, qI_scale=None, kI_scale=None,
+                   flags=0, score_out=None, ws=None, stream=None):
+    """Indexer scores + top-k. qI [B, Tq, H_I, d_I(/2)], kI [B, N_cap, d_I(/2)]."""
+    B, Tq, H_I = qI.shape[0], qI.shape[1], qI.shape[2]
+    if d_I is None:
+        d_I = qI.shape[3] * (2 if dt == MXFP4 else 1)
+    N_cap = kI.shape[1]
+    need = csa_index_topk_workspace(dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0, flags)
+    if ws is None:
+        ws = _workspace(need, kI)
+    _check(lib().csa_index_topk(_stream(stream), dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0, _p(qI),
+                                _p(qI_scale), _p(w), _p(kI), _p(kI_scale), flags, _p(idx_out),
+                                _p(score_out), _p(ws), ws.numel() * ws.element_size()))
+
+
+def csa_attend_workspace(dt_q, dt_kv, B, Tq, H, D, N_cap, m, k, W, q_pos0):
+    return int(lib().csa_attend_workspace(dt_q, dt_kv, B, Tq, H, D, N_cap, m, k, W, q_pos0))
+
+
+def hca_attend_workspace(dt_q, dt_kv, B, Tq, H, D, N_cap, m, W, q_pos0):
+    return int(lib().hca_attend_workspace(dt_q, dt_kv, B, Tq, H, D, N_cap, m, W, q_pos0))
+
+
+def csa_attend(dt_q, dt_kv, q, kv, idx, win, sink, out, *, m, W, q_pos0, scale, N_cap=None,
+               kv_scale=None, win_scale=None, flags=0, rope_base=10000.0, rope_dims=0, lse_out=None,
+               ws=None, stream=None):
+    """CSA core attention; q [B, Tq, H, D], kv [B, N_cap, ...], idx [B, Tq, k]."""
+    B, Tq, H, D = q.shape
+    k = idx.shape[2]
+    N_cap = kv.shape[1] if N_cap is None else N_cap
+    need = csa_attend_workspace(dt_q, dt_kv, B, Tq, H, D, N_cap, m, k, W, q_pos0)
+    if ws is None:
+        ws = _workspace(need, q)
+    _check(lib().csa_attend(_stream(stream), dt_q, dt_kv, B, Tq, H, D, N_cap, m, k, W, q_pos0,
+                            _p(q), _p(kv), _p(kv_scale), _p(idx), _p(win), _p(win_scale), _p(sink),
+                            scale, flags, rope_base, rope_dims, _p(out), _p(lse_out), _p(ws),
+                            ws.numel() * ws.element_size()))
+
+
+def hca_attend(dt_q, dt_kv, q, kv, win, sink, out, *, m, W, q_pos0, scale, N_cap=None, kv_scale=None,
+               win_scale=None, flags=0, rope_base=10000.0, rope_dims=0, lse_out=None, ws=None,
+               stream=None):
+    """HCA dense attention over every visible entry; arguments as csa_attend without idx."""
+    B, Tq, H, D = q.shape
+    N_cap = kv.shape[1] if N_cap is None else N_cap
+    need = hca_attend_workspace(dt_q, dt_kv, B, Tq, H, D, N_cap, m, W, q_pos0)
+    if ws is None:
+        ws = _workspace(need, q)
+    _check(lib().hca_attend(_stream(stream), dt_q, dt_kv, B, Tq, H, D, N_cap, m, W, q_pos0, _p(q),
+                            _p(kv), _p(kv_scale), _p(win), _p(win_scale), _p(sink), scale, flags,
+                            rope_base, rope_dims, _p(out), _p(lse_out), _p(ws),
+                            ws.numel() * ws.element_size()))
+
+
+def lca_version():
+    return int(lib().lca_version())
+
+
+def lca_profile_enable(on: bool):
+    _check(lib().lca_profile_enable(1 if on else 0))
+
+
+def lca_profile_collect(max_entries: int = 64):
+    """Per-kernel {name: (launches, total_ms)} of the launches since the last collect."""
+    arr = (KernelStat * max_entries)()
+    n = lib().lca_profile_collect(arr, max_entries)
+    if n < 0:
+        _check(n)
+    return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms)) for i in range(n)}

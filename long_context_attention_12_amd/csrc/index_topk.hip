@@ -1,0 +1,365 @@
+// index_topk.hip — Lightning Indexer scores of every visible compressed entry
+// and top-k selection.
+//
+// [Qiaomu] 混合注意力机制: cheap indexer queries score every compressed block and
+// only the top-k are kept; [kwkr] §3.1: CSA runs DeepSeek Sparse Attention on
+// the compressed entries, whose indexer score is s_j = sum_h w_h relu(q_h.k_j);
+// [Qiaomu] FP4量化感知训练 and [kwkr] §4.4: scores rounded to BF16 before top-k.
+//
+// Scoring streams the indexer keys once from HBM (the bulk of a CSA decode
+// step's bytes). bf16 keys go through v_mfma_f32_16x16x32_bf16 with the 16
+// M-rows holding (16 / H_I) queries x H_I heads, so each lane's 4 accumulator
+// registers carry the H_I head dots of one (query, key) pair when H_I = 4 and
+// the ReLU-weighted head sum needs no cross-lane traffic. Scores go to the
+// workspace (float32, 4 B per entry: small next to the 256 B key row).
+//
+// Selection is an MSB-first radix select per query in one 1024-thread
+// workgroup (LDS histograms of 12/10/10-bit digits, 10/6 bits for bf16
+// scores), followed by an order-preserving compaction: output indices come out
+// in increasing order and ties at the threshold go to the lowest indices, so
+// the result is deterministic.
+#include "lca_device.h"
+#include "lca_internal.h"
+#include "../../include/lca.h"
+
+namespace lca {
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kKeysPerWG = 1024;   // keys per scoring workgroup (4 waves x 256)
+
+// ---------------------------------------------------------------------------
+// bf16 scoring with MFMA 16x16x32 (A = 16 indexer query-head rows, B = 16 keys)
+// ---------------------------------------------------------------------------
+template <int HI, int DI>
+__global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
+    float* __restrict__ scores, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, int m,
+    bool round_bf16) {
+  constexpr int QPB = 16 / HI;       // queries per M tile
+  constexpr int KS = DI / 32;        // K steps
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int b = blockIdx.z;
+  const int tq0 = t_off + blockIdx.y * QPB;          // first query of this M tile
+  const int t_end = min(Tq, t_off + Tc);             // queries of this chunk only
+  const int tq_last = min(tq0 + QPB, t_end) - 1;
+  int64_t nv_max = n_visible(q_pos0 + tq_last, m);
+  if (nv_max > N_cap) nv_max = N_cap;
+  const int64_t key0 = static_cast<int64_t>(blockIdx.x) * kKeysPerWG + wid * (kKeysPerWG / 4);
+  if (key0 >= nv_max) return;
+
+  // A operand: row r16 -> (query tq0 + r16 / HI, head r16 % HI); K chunk 8g..8g+7
+  bf16x8 aq[KS];
+  {
+    const int qt = tq0 + r16 / HI, h = r16 % HI;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qt < t_end) v = *reinterpret_cast<const uint4*>(qI + ((static_cast<int64_t>(b) * Tq + qt) * HI + h) * DI + 32 * s + 8 * g);
+      aq[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // per-accumulator-row weights: row 4g+i -> (query (4g+i)/HI, head (4g+i)%HI)
+  float wv[4];
+  int64_t nvq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * g + i, qt = tq0 + row / HI, h = row % HI;
+    wv[i] = qt < t_end ? w[(static_cast<int64_t>(b) * Tq + qt) * HI + h] : 0.f;
+    nvq[i] = qt < t_end ? n_visible(q_pos0 + qt, m) : 0;
+  }
+  const uint16_t* kb = kI + static_cast<int64_t>(b) * N_cap * DI;
+  const int64_t key_end = min(key0 + kKeysPerWG / 4, nv_max);
+
+  constexpr int UNR = 4;             // key groups of 16 in flight per wave
+  for (int64_t j0 = key0; j0 < key_end; j0 += 16 * UNR) {
+    uint4 kv[UNR][KS];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      int64_t j = j0 + 16 * u + r16;
+      if (j >= nv_max) j = nv_max - 1;             // stay in bounds; result discarded
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        kv[u][s] = *reinterpret_cast<const uint4*>(kb + j * DI + 32 * s + 8 * g);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], __builtin_bit_cast(bf16x8, kv[u][s]), acc, 0, 0, 0);
+      const int64_t j = j0 + 16 * u + r16;
+      // acc[i] = qI(row 4g+i) . kI(j); fold ReLU and head weights per query
+      float part[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[i] = wv[i] * fmaxf(acc[i], 0.f);
+      if constexpr (HI == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int qt = tq0 + 4 * g + i;
+          if (qt < t_end && j < nvq[i]) {
+            const float sc = round_bf16 ? bf16_round(part[i]) : part[i];
+            scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * N_cap + j] = sc;
+          }
+        }
+      } else if constexpr (HI == 2) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int qt = tq0 + 2 * g + p;
+          const float sc0 = part[2 * p] + part[2 * p + 1];
+          if (qt < t_end && j < nvq[2 * p]) {
+            const float sc = round_bf16 ? bf16_round(sc0) : sc0;
+            scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * N_cap + j] = sc;
+          }
+        }
+      } else {
+        float sc0 = (part[0] + part[1]) + (part[2] + part[3]);
+        if constexpr (HI >= 8) sc0 += __shfl_xor(sc0, 16, 64);
+        if constexpr (HI >= 16) sc0 += __shfl_xor(sc0, 32, 64);
+        const int qt = tq0 + (4 * g) / HI;
+        const bool writer = (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0;
+        if (writer && qt < t_end && j < nvq[0]) {
+          const float sc = round_bf16 ? bf16_round(sc0) : sc0;
+          scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * N_cap + j] = sc;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 scoring on the vector ALUs (small fp32 layers)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kScoreThreads) void index_score_f32_kernel(
+    const float* __restrict__ qI, const float* __restrict__ w, const float* __restrict__ kI,
+    float* __restrict__ scores, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, int m,
+    int HI, int DI, bool round_bf16) {
+  extern __shared__ float qs[];                 // [HI * DI + HI]
+  const int b = blockIdx.z, tl = blockIdx.y, t = t_off + tl;
+  int64_t nv = n_visible(q_pos0 + t, m);
+  if (nv > N_cap) nv = N_cap;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * kScoreThreads + threadIdx.x;
+  if (static_cast<int64_t>(blockIdx.x) * kScoreThreads >= nv) return;
+  for (int i = threadIdx.x; i < HI * DI; i += kScoreThreads)
+    qs[i] = qI[(static_cast<int64_t>(b) * Tq + t) * HI * DI + i];
+  for (int i = threadIdx.x; i < HI; i += kScoreThreads)
+    qs[HI * DI + i] = w[(static_cast<int64_t>(b) * Tq + t) * HI + i];
+  __syncthreads();
+  if (j >= nv) return;
+  const float* kr = kI + (static_cast<int64_t>(b) * N_cap + j) * DI;
+  float sc = 0.f;
+  for (int h = 0; h < HI; ++h) {
+    float dot = 0.f;
+    for (int d = 0; d < DI; ++d) dot = fmaf(qs[h * DI + d], kr[d], dot);
+    sc += qs[HI * DI + h] * fmaxf(dot, 0.f);
+  }
+  if (round_bf16) sc = bf16_round(sc);
+  scores[(static_cast<int64_t>(b) * Tc + tl) * N_cap + j] = sc;
+}
+
+// ---------------------------------------------------------------------------
+// Radix select + ordered compaction
+// ---------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+constexpr int kMaxBins = 4096;
+
+// Order-preserving key: larger score -> larger unsigned key; -0 folds into +0.
+__device__ __forceinline__ uint32_t score_key(float v, bool key16) {
+  if (v == 0.f) v = 0.f;
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return key16 ? (k >> 16) : k;
+}
+
+// Block-wide exclusive scan of one value per thread (1024 threads, 16 waves).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kSelThreads / 64; ++i) {
+    const uint32_t s = wsum[i];
+    before += i < wid ? s : 0u;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const float* __restrict__ scores, int64_t N_cap, int Tq, int t_off, int Tc, int64_t q_pos0,
+    int m, int k, bool key16, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+  __shared__ uint32_t hist[kMaxBins];
+  __shared__ uint32_t wsum[kSelThreads / 64];
+  __shared__ uint32_t sh_digit, sh_krem;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y, tl = blockIdx.x, t = t_off + tl;
+  int64_t n = n_visible(q_pos0 + t, m);
+  if (n > N_cap) n = N_cap;
+  const float* s = scores + (static_cast<int64_t>(b) * Tc + tl) * N_cap;
+  int32_t* io = idx_out + (static_cast<int64_t>(b) * Tq + t) * k;
+  float* so = score_out ? score_out + (static_cast<int64_t>(b) * Tq + t) * k : nullptr;
+
+  if (n <= k) {
+    for (int i = tid; i < k; i += kSelThreads) {
+      io[i] = i < n ? i : -1;
+      if (so) so[i] = i < n ? s[i] : -INFINITY;
+    }
+    return;
+  }
+
+  // MSB-first digits: 32-bit keys 12/10/10, 16-bit keys 10/6
+  const int nd = key16 ? 2 : 3;
+  const int widths32[3] = {12, 10, 10};
+  const int widths16[3] = {10, 6, 0};
+  uint32_t prefix = 0, pmask = 0;
+  uint32_t krem = static_cast<uint32_t>(k);
+  int shift = key16 ? 16 : 32;
+  for (int p = 0; p < nd; ++p) {
+    const int wd = key16 ? widths16[p] : widths32[p];
+    shift -= wd;
+    const int nb = 1 << wd;
+    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += kSelThreads) {
+      const uint32_t key = score_key(s[i], key16);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    // bins in descending digit order: thread owns 4 consecutive of them
+    uint32_t c[4], tsum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d = nb - 1 - (4 * tid + q);
+      c[q] = d >= 0 ? hist[d] : 0u;
+      tsum += c[q];
+    }
+    uint32_t total;
+    uint32_t before = block_excl_scan(tsum, wsum, &total);
+    if (before < krem && before + tsum >= krem) {
+      uint32_t cum = before;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (cum < krem && cum + c[q] >= krem) {
+          sh_digit = static_cast<uint32_t>(nb - 1 - (4 * tid + q));
+          sh_krem = krem - cum;
+        }
+        cum += c[q];
+      }
+    }
+    __syncthreads();
+    prefix |= sh_digit << shift;
+    pmask |= static_cast<uint32_t>(nb - 1) << shift;
+    krem = sh_krem;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;       // key of the k-th largest score
+
+  // ordered compaction: contiguous index ranges per thread
+  const int64_t chunk = (n + kSelThreads - 1) / kSelThreads;
+  const int64_t i0 = tid * chunk, i1 = min(n, i0 + chunk);
+  uint32_t gt = 0, eq = 0;
+  for (int64_t i = i0; i < i1; ++i) {
+    const uint32_t key = score_key(s[i], key16);
+    gt += key > thr;
+    eq += key == thr;
+  }
+  uint32_t tot;
+  const uint32_t gt_pre = block_excl_scan(gt, wsum, &tot);
+  const uint32_t eq_pre = block_excl_scan(eq, wsum, &tot);
+  uint32_t pos = gt_pre + min(eq_pre, krem);
+  uint32_t eq_rank = eq_pre;
+  for (int64_t i = i0; i < i1; ++i) {
+    const float v = s[i];
+    const uint32_t key = score_key(v, key16);
+    bool take = key > thr;
+    if (key == thr) { take = eq_rank < krem; ++eq_rank; }
+    if (take) {
+      io[pos] = static_cast<int32_t>(i);
+      if (so) so[pos] = v;
+      ++pos;
+    }
+  }
+}
+
+template <int HI>
+void launch_score_bf16_hi(hipStream_t s, const IndexArgs& a, float* sc, int t_off, int Tc, dim3 grid) {
+  const bool rb = (a.flags & LCA_SCORE_BF16) != 0;
+  const uint16_t* q = static_cast<const uint16_t*>(a.qI);
+  const uint16_t* k = static_cast<const uint16_t*>(a.kI);
+  switch (a.d_I) {
+    case 64: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 64>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    case 128: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 128>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    case 256: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 256>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    default: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 32>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+  }
+}
+
+// queries per chunk so that the score buffer stays under a fixed budget
+int query_chunk(const IndexArgs& a) {
+  const int64_t per_q = static_cast<int64_t>(a.B) * a.N_cap * 4;
+  const int64_t budget = int64_t(512) << 20;
+  int64_t tc = per_q > 0 ? budget / per_q : a.Tq;
+  if (tc < 1) tc = 1;
+  if (tc > a.Tq) tc = a.Tq;
+  if (tc < a.Tq && tc >= 16) tc -= tc % 16;          // whole M tiles per chunk
+  return static_cast<int>(tc);
+}
+
+}  // namespace
+
+size_t index_topk_workspace(const IndexArgs& a) {
+  return static_cast<size_t>(a.B) * query_chunk(a) * a.N_cap * sizeof(float) + 256;
+}
+
+hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t) {
+  float* sc = static_cast<float*>(ws);
+  const int Tc = query_chunk(a);
+  const bool key16 = (a.flags & LCA_SCORE_BF16) != 0;
+  for (int t_off = 0; t_off < a.Tq; t_off += Tc) {
+    const int tcn = min(Tc, a.Tq - t_off);
+    int64_t nv_max = n_visible(a.q_pos0 + t_off + tcn - 1, a.m);
+    if (nv_max > a.N_cap) nv_max = a.N_cap;
+    if (nv_max > 0) {
+      LaunchScope scope(s, "index_score");
+      if (a.dt == LCA_F32) {
+        dim3 grid((nv_max + kScoreThreads - 1) / kScoreThreads, tcn, a.B);
+        hipLaunchKernelGGL(index_score_f32_kernel, grid, dim3(kScoreThreads),
+                           (a.H_I * a.d_I + a.H_I) * sizeof(float), s,
+                           static_cast<const float*>(a.qI), a.w, static_cast<const float*>(a.kI), sc,
+                           a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, a.H_I, a.d_I, key16);
+      } else {
+        const int QPB = 16 / a.H_I;
+        dim3 grid((nv_max + kKeysPerWG - 1) / kKeysPerWG, (tcn + QPB - 1) / QPB, a.B);
+        switch (a.H_I) {
+          case 1: launch_score_bf16_hi<1>(s, a, sc, t_off, Tc, grid); break;
+          case 2: launch_score_bf16_hi<2>(s, a, sc, t_off, Tc, grid); break;
+          case 4: launch_score_bf16_hi<4>(s, a, sc, t_off, Tc, grid); break;
+          case 8: launch_score_bf16_hi<8>(s, a, sc, t_off, Tc, grid); break;
+          default: launch_score_bf16_hi<16>(s, a, sc, t_off, Tc, grid); break;
+        }
+      }
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    {
+      LaunchScope scope(s, "topk_select");
+      hipLaunchKernelGGL(topk_select_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, s, sc, a.N_cap,
+                         a.Tq, t_off, Tc, a.q_pos0, a.m, a.k, key16, a.idx_out, a.score_out);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace lca

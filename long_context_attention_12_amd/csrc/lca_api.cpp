@@ -1,0 +1,324 @@
+// lca_api.cpp — the C ABI: argument validation (all of it before any launch,
+// so an error leaves nothing enqueued or written), workspace sizing, dispatch
+// to the kernel launchers, error reporting and the optional kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/lca.h"
+#include "lca_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LCA_OK;
+  return fail(LCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---- kernel timing ---------------------------------------------------------
+struct ProfRec {
+  std::string name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
+}  // namespace
+
+namespace lca {
+
+LaunchScope::LaunchScope(hipStream_t s, const char* n) : stream(s), name(n), active(false), slot(-1) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r;
+  r.name = n;
+  if (hipEventCreate(&r.start) != hipSuccess) return;
+  if (hipEventCreate(&r.stop) != hipSuccess) { (void)hipEventDestroy(r.start); return; }
+  (void)hipEventRecord(r.start, s);
+  g_prof.push_back(r);
+  slot = static_cast<int>(g_prof.size()) - 1;
+  active = true;
+}
+
+LaunchScope::~LaunchScope() {
+  if (!active) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  (void)hipEventRecord(g_prof[slot].stop, stream);
+}
+
+}  // namespace lca
+
+extern "C" {
+
+const char* lca_status_str(int s) {
+  switch (s) {
+    case LCA_OK: return "ok";
+    case LCA_ERR_ARG: return "invalid argument";
+    case LCA_ERR_UNSUPPORTED: return "unsupported dtype or shape";
+    case LCA_ERR_ALIGN: return "misaligned pointer";
+    case LCA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LCA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* lca_last_error(void) { return g_err; }
+
+int lca_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+int lca_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return LCA_OK;
+}
+
+int lca_profile_collect(lca_kernel_stat* out, int max_entries) {
+  if (!out && max_entries > 0) return fail(LCA_ERR_ARG, "lca_profile_collect: out is NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<lca_kernel_stat> acc;
+  int status = LCA_OK;
+  for (auto& r : g_prof) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) status = hip_status(e, "lca_profile_collect");
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+    bool found = false;
+    for (auto& a : acc) {
+      if (std::strncmp(a.name, r.name.c_str(), sizeof(a.name)) == 0) {
+        a.launches += 1;
+        a.total_ms += ms;
+        found = true;
+        break;
+      }
+    }
+    if (!found) {
+      lca_kernel_stat st;
+      std::memset(&st, 0, sizeof(st));
+      std::strncpy(st.name, r.name.c_str(), sizeof(st.name) - 1);
+      st.launches = 1;
+      st.total_ms = ms;
+      acc.push_back(st);
+    }
+  }
+  g_prof.clear();
+  if (status != LCA_OK) return status;
+  int n = 0;
+  for (auto& a : acc) {
+    if (n >= max_entries) break;
+    out[n++] = a;
+  }
+  return n;
+}
+
+// ---------------------------------------------------------------------------
+int csa_compress(void* stream, int dt_in, int dt_out, int B, int T, int D, int m, int overlap,
+                 int64_t pos0, const void* ca, const float* za, const void* cb, const float* zb,
+                 const void* prev_ca, const float* prev_za, uint32_t flags, const float* norm_w,
+                 float eps, float rope_base, int rope_dims, void* out, void* out_scale,
+                 int64_t out_rows) {
+  if (B < 1 || T < 0 || m < 1 || D < 32 || D > 1024 || D % 32 != 0)
+    return fail(LCA_ERR_ARG, "csa_compress: need B>=1, T>=0, m>=1, 32<=D<=1024, D%%32==0 (B=%d T=%d m=%d D=%d)", B, T, m, D);
+  if (overlap != 0 && overlap != 1) return fail(LCA_ERR_ARG, "csa_compress: overlap must be 0 or 1");
+  if (overlap == 1 ? 2 * m > 256 : m > 256) return fail(LCA_ERR_UNSUPPORTED, "csa_compress: too many rows per entry (m=%d)", m);
+  if (pos0 < 0 || pos0 % m != 0) return fail(LCA_ERR_ARG, "csa_compress: pos0 must be >= 0 and a multiple of m");
+  if (dt_in != LCA_F32 && dt_in != LCA_BF16) return fail(LCA_ERR_UNSUPPORTED, "csa_compress: dt_in must be F32 or BF16");
+  if (dt_out < LCA_F32 || dt_out > LCA_MXFP4) return fail(LCA_ERR_UNSUPPORTED, "csa_compress: unknown dt_out %d", dt_out);
+  if (flags & ~(LCA_NORM | LCA_ROPE)) return fail(LCA_ERR_ARG, "csa_compress: only LCA_NORM and LCA_ROPE apply");
+  if (!cb || !zb || !out) return fail(LCA_ERR_ARG, "csa_compress: cb, zb and out are required");
+  if (overlap) {
+    if (!ca || !za) return fail(LCA_ERR_ARG, "csa_compress: overlap needs ca and za");
+    if ((prev_ca == nullptr) != (prev_za == nullptr)) return fail(LCA_ERR_ARG, "csa_compress: prev_ca and prev_za go together");
+  } else if (ca || za || prev_ca || prev_za) {
+    return fail(LCA_ERR_ARG, "csa_compress: stream a and prev_* must be NULL without overlap");
+  }
+  if ((flags & LCA_NORM) && !norm_w) return fail(LCA_ERR_ARG, "csa_compress: LCA_NORM needs norm_w");
+  if ((flags & LCA_NORM) && !(eps >= 0.f)) return fail(LCA_ERR_ARG, "csa_compress: eps must be >= 0");
+  if (rope_dims < 0 || rope_dims > D || rope_dims % 2 != 0) return fail(LCA_ERR_ARG, "csa_compress: rope_dims must be even and in [0, D]");
+  if ((flags & LCA_ROPE) && (rope_dims == 0 || !(rope_base > 0.f))) return fail(LCA_ERR_ARG, "csa_compress: LCA_ROPE needs rope_dims > 0 and rope_base > 0");
+  if ((dt_out == LCA_KV_MIXED || dt_out == LCA_MXFP4) && !out_scale) return fail(LCA_ERR_ARG, "csa_compress: out_scale required for quantised output");
+  if (!aligned16(ca) || !aligned16(cb) || !aligned16(prev_ca) || !aligned16(out))
+    return fail(LCA_ERR_ALIGN, "csa_compress: row buffers must be 16-byte aligned");
+  if (!aligned4(za) || !aligned4(zb) || !aligned4(prev_za) || !aligned4(norm_w) || !aligned4(out_scale))
+    return fail(LCA_ERR_ALIGN, "csa_compress: float arrays must be 4-byte aligned");
+  const int64_t n_out = T / m;
+  if (out_rows == 0) out_rows = n_out;
+  if (out_rows < n_out) return fail(LCA_ERR_ARG, "csa_compress: out_rows (%lld) < T/m (%lld)", (long long)out_rows, (long long)n_out);
+  if (n_out > 2147483647LL) return fail(LCA_ERR_UNSUPPORTED, "csa_compress: too many entries");
+  lca::CompressArgs a{dt_in, dt_out, B, T, D, m, overlap, pos0, ca, cb, prev_ca, za, zb, prev_za,
+                      flags, norm_w, eps, rope_base, rope_dims, out, out_scale, out_rows};
+  return hip_status(lca::launch_compress(static_cast<hipStream_t>(stream), a), "csa_compress");
+}
+
+int lca_quantize_rows(void* stream, int dt_out, int64_t n_rows, int D, int rope_dims,
+                      const float* src, void* out, void* out_scale) {
+  if (n_rows < 0 || D < 32 || D > 1024 || D % 32 != 0)
+    return fail(LCA_ERR_ARG, "lca_quantize_rows: need n_rows>=0, 32<=D<=1024, D%%32==0");
+  if (dt_out != LCA_KV_MIXED && dt_out != LCA_MXFP4) return fail(LCA_ERR_UNSUPPORTED, "lca_quantize_rows: dt_out must be KV_MIXED or MXFP4");
+  if (dt_out == LCA_KV_MIXED && (rope_dims < 0 || rope_dims > D || rope_dims % 2))
+    return fail(LCA_ERR_ARG, "lca_quantize_rows: rope_dims must be even and in [0, D]");
+  if (!src || !out || !out_scale) return fail(LCA_ERR_ARG, "lca_quantize_rows: src, out and out_scale are required");
+  if (!aligned16(src) || !aligned16(out) || !aligned4(out_scale)) return fail(LCA_ERR_ALIGN, "lca_quantize_rows: misaligned buffer");
+  return hip_status(lca::launch_quantize_rows(static_cast<hipStream_t>(stream), dt_out, n_rows, D,
+                                              dt_out == LCA_KV_MIXED ? rope_dims : 0, src, out, out_scale),
+                    "lca_quantize_rows");
+}
+
+// ---------------------------------------------------------------------------
+static int check_index(const lca::IndexArgs& a) {
+  if (a.B < 1 || a.Tq < 1 || a.H_I < 1 || a.d_I < 32 || a.N_cap < 0 || a.m < 1 || a.q_pos0 < 0)
+    return fail(LCA_ERR_ARG, "csa_index_topk: need B,Tq,H_I>=1, d_I>=32, N_cap>=0, m>=1, q_pos0>=0");
+  if (a.k < 1 || a.k > 4096) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: k must be in [1, 4096] (k=%d)", a.k);
+  if (a.d_I % 32 != 0 || a.d_I > 256) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: d_I must be a multiple of 32, <= 256");
+  if (a.dt == LCA_F32) {
+    if (a.H_I > 64) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: F32 supports H_I <= 64");
+  } else if (a.dt == LCA_BF16 || a.dt == LCA_MXFP4) {
+    if (!(a.H_I == 1 || a.H_I == 2 || a.H_I == 4 || a.H_I == 8 || a.H_I == 16))
+      return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: H_I must be 1, 2, 4, 8 or 16 (H_I=%d)", a.H_I);
+    if (a.dt == LCA_MXFP4) {
+      if (a.d_I != 128) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: MXFP4 needs d_I == 128");
+      if (!a.qI_scale || !a.kI_scale) return fail(LCA_ERR_ARG, "csa_index_topk: MXFP4 needs qI_scale and kI_scale");
+    }
+  } else {
+    return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: dt must be F32, BF16 or MXFP4");
+  }
+  if (a.flags & ~LCA_SCORE_BF16) return fail(LCA_ERR_ARG, "csa_index_topk: only LCA_SCORE_BF16 applies");
+  const int64_t nv_last = (a.q_pos0 + a.Tq) / a.m;
+  if (a.N_cap < nv_last) return fail(LCA_ERR_ARG, "csa_index_topk: N_cap (%lld) < visible entries of the last query (%lld)", (long long)a.N_cap, (long long)nv_last);
+  if (a.N_cap > 2147483647LL) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: N_cap must fit int32 indices");
+  if (!a.qI || !a.w || !a.kI || !a.idx_out) return fail(LCA_ERR_ARG, "csa_index_topk: qI, w, kI and idx_out are required");
+  if (!aligned16(a.qI) || !aligned16(a.kI) || !aligned4(a.w) || !aligned4(a.idx_out) || !aligned4(a.score_out))
+    return fail(LCA_ERR_ALIGN, "csa_index_topk: misaligned buffer");
+  return LCA_OK;
+}
+
+size_t csa_index_topk_workspace(int dt, int B, int Tq, int H_I, int d_I, int64_t N_cap, int m, int k,
+                                int64_t q_pos0, uint32_t flags) {
+  lca::IndexArgs a{dt, B, Tq, H_I, d_I, m, k, N_cap, q_pos0, nullptr, nullptr, nullptr, nullptr, nullptr, flags, nullptr, nullptr};
+  if (B < 1 || Tq < 1 || N_cap < 0) return 0;
+  return lca::index_topk_workspace(a);
+}
+
+int csa_index_topk(void* stream, int dt, int B, int Tq, int H_I, int d_I, int64_t N_cap, int m, int k,
+                   int64_t q_pos0, const void* qI, const void* qI_scale, const float* w, const void* kI,
+                   const void* kI_scale, uint32_t flags, int32_t* idx_out, float* score_out, void* ws,
+                   size_t ws_bytes) {
+  lca::IndexArgs a{dt, B, Tq, H_I, d_I, m, k, N_cap, q_pos0, qI, qI_scale, kI, kI_scale, w, flags, idx_out, score_out};
+  int st = check_index(a);
+  if (st != LCA_OK) return st;
+  const size_t need = lca::index_topk_workspace(a);
+  if (!ws || ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "csa_index_topk: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned16(ws)) return fail(LCA_ERR_ALIGN, "csa_index_topk: workspace must be 16-byte aligned");
+  if (dt == LCA_MXFP4) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: MXFP4 scoring not built yet");
+  return hip_status(lca::launch_index_topk(static_cast<hipStream_t>(stream), a, ws, ws_bytes), "csa_index_topk");
+}
+
+// ---------------------------------------------------------------------------
+static int check_attend(const lca::AttendArgs& a, const char* fn) {
+  if (a.B < 1 || a.Tq < 1 || a.H < 1 || a.N_cap < 0 || a.m < 1 || a.q_pos0 < 0)
+    return fail(LCA_ERR_ARG, "%s: need B,Tq,H>=1, N_cap>=0, m>=1, q_pos0>=0", fn);
+  if (a.W < 1 || a.W > 4096) return fail(LCA_ERR_ARG, "%s: W must be in [1, 4096]", fn);
+  if (a.D < 32 || a.D % 32 != 0 || a.D > 512) return fail(LCA_ERR_UNSUPPORTED, "%s: D must be a multiple of 32 and <= 512", fn);
+  if (a.sparse && (a.k < 1 || a.k > 4096)) return fail(LCA_ERR_UNSUPPORTED, "%s: k must be in [1, 4096]", fn);
+  if (a.dt_kv == LCA_F32) {
+    if (a.dt_q != LCA_F32) return fail(LCA_ERR_UNSUPPORTED, "%s: F32 kv needs F32 q", fn);
+    if (a.D > 256) return fail(LCA_ERR_UNSUPPORTED, "%s: F32 path supports D <= 256", fn);
+  } else if (a.dt_kv == LCA_BF16 || a.dt_kv == LCA_KV_MIXED) {
+    if (a.dt_q != LCA_BF16) return fail(LCA_ERR_UNSUPPORTED, "%s: BF16/MIXED kv needs BF16 q", fn);
+    if (!(a.D == 64 || a.D == 128 || a.D == 256 || a.D == 512)) return fail(LCA_ERR_UNSUPPORTED, "%s: MFMA path needs D in {64,128,256,512}", fn);
+    if (a.H % 16 != 0 || (a.H > 64 && a.H % 64 != 0)) return fail(LCA_ERR_UNSUPPORTED, "%s: H must be 16, 32, 48, 64 or a multiple of 64", fn);
+    if (a.H / 64 > 2 && a.H > 128) return fail(LCA_ERR_UNSUPPORTED, "%s: H <= 128", fn);
+    if (a.dt_kv == LCA_KV_MIXED && (a.D != 512 || a.rope_dims != 64))
+      return fail(LCA_ERR_UNSUPPORTED, "%s: KV_MIXED rows need D == 512 and rope_dims == 64", fn);
+    if (a.dt_kv == LCA_KV_MIXED && (!a.kv_scale || !a.win_scale)) return fail(LCA_ERR_ARG, "%s: KV_MIXED needs kv_scale and win_scale", fn);
+  } else {
+    return fail(LCA_ERR_UNSUPPORTED, "%s: dt_kv must be F32, BF16 or KV_MIXED", fn);
+  }
+  if (a.flags & ~LCA_INV_ROPE) return fail(LCA_ERR_ARG, "%s: only LCA_INV_ROPE applies", fn);
+  if (a.rope_dims < 0 || a.rope_dims > a.D || a.rope_dims % 2) return fail(LCA_ERR_ARG, "%s: rope_dims must be even and in [0, D]", fn);
+  if ((a.flags & LCA_INV_ROPE) && (a.rope_dims == 0 || !(a.rope_base > 0.f))) return fail(LCA_ERR_ARG, "%s: LCA_INV_ROPE needs rope_dims > 0 and rope_base > 0", fn);
+  if (!(a.scale == a.scale)) return fail(LCA_ERR_ARG, "%s: scale is NaN", fn);
+  if (!a.q || !a.kv || !a.win || !a.sink || !a.out || (a.sparse && !a.idx)) return fail(LCA_ERR_ARG, "%s: missing required pointer", fn);
+  if (!a.sparse) {
+    const int64_t nv_last = (a.q_pos0 + a.Tq) / a.m;
+    if (a.N_cap < nv_last) return fail(LCA_ERR_ARG, "%s: N_cap (%lld) < visible entries of the last query (%lld)", fn, (long long)a.N_cap, (long long)nv_last);
+  }
+  if (!aligned16(a.q) || !aligned16(a.kv) || !aligned16(a.win) || !aligned16(a.out) || !aligned4(a.idx) ||
+      !aligned4(a.sink) || !aligned4(a.lse_out) || !aligned4(a.kv_scale) || !aligned4(a.win_scale))
+    return fail(LCA_ERR_ALIGN, "%s: misaligned buffer", fn);
+  return LCA_OK;
+}
+
+static int run_attend(void* stream, const lca::AttendArgs& a, void* ws, size_t ws_bytes, const char* fn) {
+  int st = check_attend(a, fn);
+  if (st != LCA_OK) return st;
+  const size_t need = lca::attend_workspace(a);
+  if (!ws || ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  if (!aligned16(ws)) return fail(LCA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  return hip_status(lca::launch_attend(static_cast<hipStream_t>(stream), a, ws, ws_bytes), fn);
+}
+
+size_t csa_attend_workspace(int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int k,
+                            int W, int64_t q_pos0) {
+  if (B < 1 || Tq < 1 || H < 1 || D < 1 || m < 1 || W < 1) return 0;
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = k; a.W = W;
+  a.sparse = true; a.N_cap = N_cap; a.q_pos0 = q_pos0;
+  return lca::attend_workspace(a);
+}
+
+int csa_attend(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int k,
+               int W, int64_t q_pos0, const void* q, const void* kv, const float* kv_scale,
+               const int32_t* idx, const void* win, const float* win_scale, const float* sink,
+               float scale, uint32_t flags, float rope_base, int rope_dims, void* out, float* lse_out,
+               void* ws, size_t ws_bytes) {
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = k; a.W = W;
+  a.sparse = true; a.N_cap = N_cap; a.q_pos0 = q_pos0; a.q = q; a.kv = kv; a.win = win;
+  a.kv_scale = kv_scale; a.win_scale = win_scale; a.sink = sink; a.idx = idx; a.scale = scale;
+  a.flags = flags; a.rope_base = rope_base; a.rope_dims = rope_dims; a.out = out; a.lse_out = lse_out;
+  return run_attend(stream, a, ws, ws_bytes, "csa_attend");
+}
+
+size_t hca_attend_workspace(int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int W,
+                            int64_t q_pos0) {
+  if (B < 1 || Tq < 1 || H < 1 || D < 1 || m < 1 || W < 1) return 0;
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = 0; a.W = W;
+  a.sparse = false; a.N_cap = N_cap; a.q_pos0 = q_pos0;
+  return lca::attend_workspace(a);
+}
+
+int hca_attend(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int W,
+               int64_t q_pos0, const void* q, const void* kv, const float* kv_scale, const void* win,
+               const float* win_scale, const float* sink, float scale, uint32_t flags, float rope_base,
+               int rope_dims, void* out, float* lse_out, void* ws, size_t ws_bytes) {
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = 0; a.W = W;
+  a.sparse = false; a.N_cap = N_cap; a.q_pos0 = q_pos0; a.q = q; a.kv = kv; a.win = win;
+  a.kv_scale = kv_scale; a.win_scale = win_scale; a.sink = sink; a.idx = nullptr; a.scale = scale;
+  a.flags = flags; a.rope_base = rope_base; a.rope_dims = rope_dims; a.out = out; a.lse_out = lse_out;
+  return run_attend(stream, a, ws, ws_bytes, "hca_attend");
+}
+
+}  // extern "C"

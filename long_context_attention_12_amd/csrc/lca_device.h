@@ -1,0 +1,108 @@
+// lca_device.h — device helpers shared by the gfx950 kernels: storage-format
+// conversions (bf16, e4m3fn, e2m1/E8M0), MFMA operand types, wave reductions
+// and the RoPE angle. Every conversion here is written from the format's
+// definition and rounds to nearest even exactly as the format specifies.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lca {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---- bfloat16 --------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round to nearest even on the 16 dropped bits.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ---- OCP FP8 E4M3FN (bias 7, max 448, subnormal step 2^-9) -------------------
+__device__ __forceinline__ uint8_t f32_to_e4m3fn(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                         // below 2^-6: multiples of 2^-9
+    code = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // 8 -> 0x08 (2^-6)
+  } else {
+    int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;
+    uint32_t q = static_cast<uint32_t>(__builtin_rintf(ldexpf(a, 3 - e)));  // [8, 16]
+    if (q == 16u) { q = 8u; ++e; }
+    int ef = e + 7;
+    if (ef > 15 || (ef == 15 && q - 8u > 6u)) { ef = 15; q = 14u; }
+    code = (static_cast<uint32_t>(ef) << 3) | (q - 8u);
+  }
+  return static_cast<uint8_t>(sign | code);
+}
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t c) {
+  uint32_t ef = (c >> 3) & 0xfu, mt = c & 7u;
+  float mag = ef == 0 ? static_cast<float>(mt) * 0.001953125f
+                      : ldexpf(static_cast<float>(8u + mt), static_cast<int>(ef) - 10);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// ---- OCP MX E2M1 element and E8M0 scale ---------------------------------------
+// Magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; halfway cases go to the even code.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  float a = fabsf(v);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+// floor(log2(amax)) - 2, clamped to the E8M0 range; amax > 0 and finite.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  int e;
+  (void)frexpf(amax, &e);                       // amax in [2^(e-1), 2^e)
+  int E = (e - 1) - 2;
+  return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
+
+// ---- wave reductions (64 lanes) -----------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---- RoPE ----------------------------------------------------------------------
+// Angle of pair i (of R/2) at position pos, reduced to [-pi, pi] in double so
+// that positions near 2^20 keep full float32 accuracy in sin/cos.
+__device__ __forceinline__ void rope_sincos(double pos, int i, int R, double base,
+                                            float* s, float* c) {
+  double freq = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(R));
+  double ang = pos * freq;
+  const double two_pi = 6.283185307179586476925286766559;
+  ang = ang - two_pi * rint(ang / two_pi);
+  *s = static_cast<float>(sin(ang));
+  *c = static_cast<float>(cos(ang));
+}
+
+__host__ __device__ __forceinline__ int64_t n_visible(int64_t p, int m) { return (p + 1) / m; }
+
+}  // namespace lca

@@ -1,0 +1,67 @@
+// lca_internal.h — launchers shared between the validated C ABI (lca_api.cpp)
+// and the kernel translation units. Arguments reaching these functions have
+// already been validated; they only compute grids and enqueue kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lca {
+
+// Kernel-launch bracket used by the optional timing mode (lca_profile_*).
+struct LaunchScope {
+  LaunchScope(hipStream_t s, const char* name);
+  ~LaunchScope();
+  hipStream_t stream;
+  const char* name;
+  bool active;
+  int slot;
+};
+
+struct CompressArgs {
+  int dt_in, dt_out, B, T, D, m, overlap;
+  int64_t pos0;
+  const void *ca, *cb, *prev_ca;
+  const float *za, *zb, *prev_za;
+  uint32_t flags;
+  const float* norm_w;
+  float eps, rope_base;
+  int rope_dims;
+  void* out;
+  void* out_scale;
+  int64_t out_rows;
+};
+hipError_t launch_compress(hipStream_t s, const CompressArgs& a);
+hipError_t launch_quantize_rows(hipStream_t s, int dt_out, int64_t n_rows, int D, int rope_dims,
+                                const float* src, void* out, void* out_scale);
+
+struct IndexArgs {
+  int dt, B, Tq, H_I, d_I, m, k;
+  int64_t N_cap, q_pos0;
+  const void *qI, *qI_scale, *kI, *kI_scale;
+  const float* w;
+  uint32_t flags;
+  int32_t* idx_out;
+  float* score_out;
+};
+size_t index_topk_workspace(const IndexArgs& a);
+hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t ws_bytes);
+
+struct AttendArgs {
+  int dt_q, dt_kv, B, Tq, H, D, m, k, W;
+  bool sparse;               // true: CSA rows from idx; false: HCA all visible rows
+  int64_t N_cap, q_pos0;
+  const void *q, *kv, *win;
+  const float *kv_scale, *win_scale, *sink;
+  const int32_t* idx;
+  float scale;
+  uint32_t flags;
+  float rope_base;
+  int rope_dims;
+  void* out;
+  float* lse_out;
+};
+size_t attend_workspace(const AttendArgs& a);
+hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t ws_bytes);
+
+}  // namespace lca

@@ -1,0 +1,342 @@
+"""Parity of each HIP entry point against the float64 oracle, at sizes the
+oracle finishes in seconds: several tiles, ragged tails, degenerate cases."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from gpu_util import (DEV, check_topk_set, dev_bf16, dev_f32, host, need_gpu, row_tol_check, say)
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# quantise-on-write: codes must equal the oracle's bit for bit
+# ---------------------------------------------------------------------------
+
+def _special_rows(rng, n, D):
+    x = (rng.standard_normal((n, D)) * np.exp(rng.uniform(-6, 3, (n, 1)))).astype(np.float32)
+    x[0] = 0.0                                   # all-zero row
+    x[1, :] = 1.0                                # constant row
+    x[2, :8] = np.float32([448, -448, 1e-6, -1e-6, 2.0 ** -9, 3.0, -0.0, 7.0])
+    return x
+
+
+def test_quantize_kv_mixed_bit_exact():
+    L = need_gpu()
+    rng = np.random.default_rng(11)
+    n, D, R = 333, 512, 64
+    x = _special_rows(rng, n, D)
+    out = torch.empty((n, D - R + 2 * R), dtype=torch.uint8, device=DEV)
+    sc = torch.empty(n, dtype=torch.float32, device=DEV)
+    L.lca_quantize_rows(L.KV_MIXED, dev_f32(x), out, sc, rope_dims=R)
+    torch.cuda.synchronize()
+    codes, rope, s = O.kv_mixed_quantize(x, R)
+    o = out.cpu().numpy()
+    np.testing.assert_array_equal(sc.cpu().numpy(), s)
+    np.testing.assert_array_equal(o[:, :D - R], codes)
+    tail = o[:, D - R:].copy().view(np.uint16).astype(np.uint32) << 16
+    np.testing.assert_array_equal(tail.view(np.float32).astype(np.float64), rope)
+
+
+def test_quantize_mxfp4_bit_exact():
+    L = need_gpu()
+    rng = np.random.default_rng(12)
+    n, D = 257, 128
+    x = _special_rows(rng, n, D)
+    x[3, :32] = np.float32([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.9] * 4) * 0.5   # exact ties
+    out = torch.empty((n, D // 2), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((n, D // 32), dtype=torch.uint8, device=DEV)
+    L.lca_quantize_rows(L.MXFP4, dev_f32(x), out, sc)
+    torch.cuda.synchronize()
+    codes, scales = O.mxfp4_quantize(x)
+    o = out.cpu().numpy()
+    np.testing.assert_array_equal(sc.cpu().numpy(), scales)
+    np.testing.assert_array_equal(o & 0xF, codes[:, 0::2])
+    np.testing.assert_array_equal(o >> 4, codes[:, 1::2])
+
+
+# ---------------------------------------------------------------------------
+# compressor
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["csa", "csa_prev", "csa_norm_rope", "hca"])
+def test_compress_matches_oracle(dt, mode):
+    L = need_gpu()
+    rng = np.random.default_rng(13)
+    B, D = 2, 128
+    m = 128 if mode == "hca" else 4
+    T = 3 * m + 3 if mode != "hca" else 2 * m + 5        # ragged tail
+    pos0 = 8 * m
+    cast = (lambda a: WL.bf16_exact(a)) if dt == "bf16" else (lambda a: a.astype(np.float32))
+    ca = cast(rng.standard_normal((B, T, D)).astype(np.float32))
+    cb = cast(rng.standard_normal((B, T, D)).astype(np.float32))
+    za = (rng.standard_normal((B, T)) * 2).astype(np.float32)
+    zb = (rng.standard_normal((B, T)) * 2).astype(np.float32)
+    pca = cast(rng.standard_normal((B, m, D)).astype(np.float32))
+    pza = rng.standard_normal((B, m)).astype(np.float32)
+    nw = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    overlap = mode != "hca"
+    use_prev = mode in ("csa_prev", "csa_norm_rope")
+    flags = (L.NORM | L.ROPE) if mode == "csa_norm_rope" else 0
+    R = 64 if flags else 0
+    up = dev_bf16 if dt == "bf16" else dev_f32
+    dti = L.BF16 if dt == "bf16" else L.F32
+    n_out = T // m
+    out = torch.empty((B, n_out, D), dtype=torch.float32, device=DEV)
+    L.csa_compress(dti, L.F32, up(cb), dev_f32(zb), m, ca=up(ca) if overlap else None,
+                   za=dev_f32(za) if overlap else None,
+                   prev_ca=up(pca) if use_prev else None, prev_za=dev_f32(pza) if use_prev else None,
+                   overlap=overlap, pos0=pos0, flags=flags, norm_w=dev_f32(nw) if flags else None,
+                   eps=1e-6, rope_base=10000.0, rope_dims=R, out=out)
+    torch.cuda.synchronize()
+    got = host(out)
+    for b in range(B):
+        ref = O.compress_sequence(cb[b], zb[b], m, ca[b] if overlap else None, za[b] if overlap else None,
+                                  pca[b] if use_prev else None, pza[b] if use_prev else None, overlap)
+        if flags:
+            ref = O.compress_epilogue(ref, pos0, m, nw, 1e-6, 10000.0, R)
+        row_tol_check(got[b], ref, 1e-5, f"compress {mode} {dt}")
+
+
+def test_compress_chunked_equals_one_shot_bitwise():
+    L = need_gpu()
+    rng = np.random.default_rng(14)
+    B, T, D, m = 2, 64, 256, 4
+    ca, cb = (WL.bf16_exact(rng.standard_normal((B, T, D)).astype(np.float32)) for _ in range(2))
+    za, zb = (rng.standard_normal((B, T)).astype(np.float32) for _ in range(2))
+    full = torch.empty((B, T // m, D), dtype=torch.bfloat16, device=DEV)
+    L.csa_compress(L.BF16, L.BF16, dev_bf16(cb), dev_f32(zb), m, ca=dev_bf16(ca), za=dev_f32(za), out=full)
+    T1 = 24
+    part = torch.empty((B, T // m, D), dtype=torch.bfloat16, device=DEV)
+    L.csa_compress(L.BF16, L.BF16, dev_bf16(cb[:, :T1]), dev_f32(zb[:, :T1]), m, ca=dev_bf16(ca[:, :T1]),
+                   za=dev_f32(za[:, :T1]), out=part, out_rows=T // m)
+    L.csa_compress(L.BF16, L.BF16, dev_bf16(cb[:, T1:]), dev_f32(zb[:, T1:]), m, ca=dev_bf16(ca[:, T1:]),
+                   za=dev_f32(za[:, T1:]), prev_ca=dev_bf16(ca[:, T1 - m:T1]),
+                   prev_za=dev_f32(za[:, T1 - m:T1]), pos0=T1, out=part[:, T1 // m:], out_rows=T // m)
+    torch.cuda.synchronize()
+    assert torch.equal(full, part)
+
+
+def test_compress_constant_sequence_quantised_outputs():
+    # constant rows compress to themselves; then the quantised outputs equal
+    # the oracle's quantisation of that row
+    L = need_gpu()
+    rng = np.random.default_rng(15)
+    B, T, D, m = 1, 16, 512, 4
+    c = rng.standard_normal(D).astype(np.float32)
+    rows = np.tile(c, (B, T, 1))
+    z = rng.standard_normal((B, T)).astype(np.float32)
+    out = torch.empty((B, T // m, D + 64), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((B, T // m), dtype=torch.float32, device=DEV)
+    L.csa_compress(L.F32, L.KV_MIXED, dev_f32(rows), dev_f32(z), m, ca=dev_f32(rows), za=dev_f32(z),
+                   rope_dims=64, out=out, out_scale=sc)
+    torch.cuda.synchronize()
+    codes, rope, s = O.kv_mixed_quantize(c[None], 64)
+    got = out.cpu().numpy()[0]
+    # fp32 softmax weights sum to 1 within rounding: allow one code step
+    dec_got = O.kv_mixed_decode(got[:, :448], (got[:, 448:].copy().view(np.uint16).astype(np.uint32) << 16)
+                                .view(np.float32).astype(np.float64), sc.cpu().numpy()[0])
+    dec_ref = O.kv_mixed_decode(codes, rope, s)[0]
+    assert np.max(np.abs(dec_got - dec_ref)) <= 2 * np.max(np.abs(c)) / 16
+
+
+# ---------------------------------------------------------------------------
+# indexer scores + top-k
+# ---------------------------------------------------------------------------
+
+def _index_case(rng, B, Tq, H_I, d_I, N_cap, spikes=True, ties=False):
+    qI = WL.bf16_exact(rng.standard_normal((B, Tq, H_I, d_I)).astype(np.float32) / np.sqrt(d_I))
+    kI = rng.standard_normal((B, N_cap, d_I)).astype(np.float32) / np.sqrt(d_I)
+    if spikes:
+        kI[:, ::97] *= 4
+    if ties:
+        kI[:, 1::3] = kI[:, 0::3][:, :kI[:, 1::3].shape[1]]       # duplicated keys -> tied scores
+    kI = WL.bf16_exact(kI)
+    w = (rng.standard_normal((B, Tq, H_I)) / np.sqrt(H_I)).astype(np.float32)
+    return qI, w, kI
+
+
+@pytest.mark.parametrize("H_I", [1, 2, 4, 8, 16])
+def test_index_topk_decode_bf16(H_I):
+    L = need_gpu()
+    rng = np.random.default_rng(20 + H_I)
+    B, Tq, d_I, m, k = 3, 1, 128, 4, 256
+    q_pos0 = 4 * 5000 + 2                    # n_vis = 5000: not a multiple of any tile
+    N_cap = 5003
+    qI, w, kI = _index_case(rng, B, Tq, H_I, d_I, N_cap)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
+                     score_out=sco)
+    torch.cuda.synchronize()
+    idx_h, sco_h = idx.cpu().numpy(), sco.cpu().numpy()
+    for b in range(B):
+        nv = O.n_visible(q_pos0, m)
+        s = O.index_scores(qI[b, 0], w[b, 0], kI[b], nv)
+        check_topk_set(idx_h[b, 0], s, k)
+        assert np.all(np.diff(idx_h[b, 0]) > 0), "indices not increasing"
+        np.testing.assert_allclose(sco_h[b, 0], s[idx_h[b, 0]], rtol=1e-4, atol=1e-6)
+
+
+@pytest.mark.parametrize("bf16_scores", [False, True])
+def test_index_topk_prefill_causal_bf16(bf16_scores):
+    L = need_gpu()
+    rng = np.random.default_rng(30)
+    B, Tq, H_I, d_I, m, k = 2, 37, 4, 64, 4, 50
+    q_pos0 = 180
+    N_cap = (q_pos0 + Tq) // m
+    qI, w, kI = _index_case(rng, B, Tq, H_I, d_I, N_cap, ties=True)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
+                     flags=L.SCORE_BF16 if bf16_scores else 0)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            nv = O.n_visible(q_pos0 + t, m)
+            s = O.index_scores(qI[b, t], w[b, t], kI[b], nv)
+            check_topk_set(idx_h[b, t], s, k, bf16_scores=bf16_scores)
+
+
+def test_index_topk_f32_from_sequence_start():
+    # queries from position 0: the first ones see no entry (all padding)
+    L = need_gpu()
+    rng = np.random.default_rng(31)
+    B, Tq, H_I, d_I, m, k = 1, 80, 4, 64, 4, 8
+    N_cap = Tq // m
+    qI = rng.standard_normal((B, Tq, H_I, d_I)).astype(np.float32)
+    kI = rng.standard_normal((B, N_cap, d_I)).astype(np.float32)
+    w = rng.standard_normal((B, Tq, H_I)).astype(np.float32)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    L.csa_index_topk(L.F32, dev_f32(qI), dev_f32(w), dev_f32(kI), idx, m=m, k=k, q_pos0=0, score_out=sco)
+    torch.cuda.synchronize()
+    idx_h, sco_h = idx.cpu().numpy(), sco.cpu().numpy()
+    assert np.all(idx_h[0, :3] == -1)
+    for t in range(Tq):
+        nv = O.n_visible(t, m)
+        s = O.index_scores(qI[0, t], w[0, t], kI[0], nv)
+        check_topk_set(idx_h[0, t], s, k)
+        sel = idx_h[0, t][idx_h[0, t] >= 0]
+        np.testing.assert_allclose(sco_h[0, t][:len(sel)], s[sel], rtol=1e-5, atol=1e-6)
+
+
+def test_index_topk_all_ties_take_lowest_indices():
+    L = need_gpu()
+    B, Tq, H_I, d_I, m, k = 1, 1, 4, 128, 4, 100
+    N_cap = 3000
+    kI = np.zeros((B, N_cap, d_I), np.float32)
+    kI[0, :, 0] = 1.0                          # every key identical
+    qI = np.zeros((B, Tq, H_I, d_I), np.float32)
+    qI[0, 0, :, 0] = 0.5
+    w = np.ones((B, Tq, H_I), np.float32)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=4 * N_cap - 1)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy()[0, 0], np.arange(k))
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _attend_case(rng, B, Tq, H, D, N_cap, W, sharp, cast):
+    q = cast((rng.standard_normal((B, Tq, H, D)) * sharp / np.sqrt(D)).astype(np.float32))
+    E = cast((rng.standard_normal((B, N_cap, D)) / np.sqrt(D)).astype(np.float32))
+    win = cast((rng.standard_normal((B, W - 1 + Tq, D)) / np.sqrt(D)).astype(np.float32))
+    sink = rng.standard_normal(H).astype(np.float32)
+    return q, E, win, sink
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+@pytest.mark.parametrize("sharp", [1.0, 30.0])
+def test_attend_matches_oracle(dt, kind, sharp):
+    L = need_gpu()
+    rng = np.random.default_rng(40)
+    H, D = (8, 128) if dt == "f32" else (64, 256)
+    B, Tq, W, m = 2, 5, 128, (4 if kind == "csa" else 128)
+    q_pos0 = 3000 if kind == "csa" else 20000
+    N_cap = (q_pos0 + Tq) // m + 3
+    k = 300
+    cast = WL.bf16_exact if dt == "bf16" else (lambda a: a)
+    q, E, win, sink = _attend_case(rng, B, Tq, H, D, N_cap, W, sharp, cast)
+    up = dev_bf16 if dt == "bf16" else dev_f32
+    dtc = L.BF16 if dt == "bf16" else L.F32
+    scale = 1 / math.sqrt(D)
+    out = torch.empty((B, Tq, H, D), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device=DEV)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+    if kind == "csa":
+        idx = np.full((B, Tq, k), -1, np.int32)
+        for b in range(B):
+            for t in range(Tq):
+                nv = O.n_visible(q_pos0 + t, m)
+                sel = rng.choice(nv, size=min(k - 7, nv), replace=False)
+                idx[b, t, :len(sel)] = np.sort(sel)
+        L.csa_attend(dtc, dtc, up(q), up(E), torch.from_numpy(idx).to(DEV), up(win), dev_f32(sink), out,
+                     m=m, W=W, q_pos0=q_pos0, scale=scale, flags=L.INV_ROPE, rope_dims=64, lse_out=lse)
+    else:
+        L.hca_attend(dtc, dtc, up(q), up(E), up(win), dev_f32(sink), out, m=m, W=W, q_pos0=q_pos0,
+                     scale=scale, flags=L.INV_ROPE, rope_dims=64, lse_out=lse)
+    torch.cuda.synchronize()
+    got, got_lse = host(out), lse.cpu().numpy()
+    tol = 1e-4 if dt == "f32" else 2e-2
+    for b in range(B):
+        if kind == "csa":
+            ref, rl = O.csa_attend(q[b], E[b], idx[b], win[b], sink, scale, q_pos0, W, True, 10000.0, 64)
+        else:
+            ref, rl = O.hca_attend(q[b], E[b], m, win[b], sink, scale, q_pos0, W, True, 10000.0, 64)
+        row_tol_check(got[b], ref, tol, f"{kind} {dt} sharp={sharp}")
+        np.testing.assert_allclose(got_lse[b], rl, atol=1e-4 if dt == "f32" else 2e-2)
+
+
+def test_attend_window_clipped_and_no_entries():
+    # queries at positions 0..9: fewer window rows than W, no visible entries
+    L = need_gpu()
+    rng = np.random.default_rng(41)
+    B, Tq, H, D, W, m = 1, 10, 16, 128, 128, 4
+    q, E, win, sink = _attend_case(rng, B, Tq, H, D, 4, W, 20.0, WL.bf16_exact)
+    out = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    idx = np.full((B, Tq, 8), -1, np.int32)
+    idx[0, 3:, 0] = 0                          # entry 0 visible from position 3 on
+    idx[0, 7:, 1] = 1
+    L.csa_attend(L.BF16, L.BF16, dev_bf16(q), dev_bf16(E), torch.from_numpy(idx).to(DEV), dev_bf16(win),
+                 dev_f32(sink), out, m=m, W=W, q_pos0=0, scale=1 / math.sqrt(D))
+    torch.cuda.synchronize()
+    ref, _ = O.csa_attend(q[0], E[0], idx[0], win[0], sink, 1 / math.sqrt(D), 0, W)
+    row_tol_check(host(out)[0], ref, 2e-2, "clipped window")
+
+
+def test_attend_mixed_kv_matches_oracle():
+    L = need_gpu()
+    rng = np.random.default_rng(42)
+    B, Tq, H, D, W, m, k = 2, 1, 128, 512, 128, 4, 200
+    q_pos0 = 4 * 3000
+    N_cap = 3001
+    q = WL.bf16_exact((rng.standard_normal((B, Tq, H, D)) * 10 / np.sqrt(D)).astype(np.float32))
+    Esrc = (rng.standard_normal((B, N_cap, D)) / np.sqrt(D)).astype(np.float32)
+    wsrc = (rng.standard_normal((B, W, D)) / np.sqrt(D)).astype(np.float32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    Eq = torch.empty((B, N_cap, D + 64), dtype=torch.uint8, device=DEV)
+    Es = torch.empty((B, N_cap), dtype=torch.float32, device=DEV)
+    Wq = torch.empty((B, W, D + 64), dtype=torch.uint8, device=DEV)
+    Ws = torch.empty((B, W), dtype=torch.float32, device=DEV)
+    L.lca_quantize_rows(L.KV_MIXED, dev_f32(Esrc), Eq, Es)
+    L.lca_quantize_rows(L.KV_MIXED, dev_f32(wsrc), Wq, Ws)
+    idx = np.stack([np.sort(rng.choice(3001, size=k, replace=False)) for _ in range(B)])[:, None].astype(np.int32)
+    out = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    L.csa_attend(L.BF16, L.KV_MIXED, dev_bf16(q), Eq, torch.from_numpy(idx).to(DEV), Wq, dev_f32(sink), out,
+                 m=m, W=W, q_pos0=q_pos0, scale=1 / math.sqrt(D), kv_scale=Es, win_scale=Ws,
+                 flags=L.INV_ROPE, rope_dims=64)
+    torch.cuda.synchronize()
+    for b in range(B):
+        Ed = O.kv_mixed_decode(*O.kv_mixed_quantize(Esrc[b], 64))
+        Wd = O.kv_mixed_decode(*O.kv_mixed_quantize(wsrc[b], 64))
+        ref, _ = O.csa_attend(q[b], Ed, idx[b], Wd, sink, 1 / math.sqrt(D), q_pos0, W, True, 10000.0, 64)
+        row_tol_check(host(out)[b], ref, 2e-2, "mixed kv")
