@@ -1,0 +1,257 @@
+"""Benchmark of the CSA decode step on one MI355X.
+
+Workload (headline): CSA decode, V4-Flash shaped: batch 16, one new token per
+sequence after 131072 context tokens (32768 compressed entries), 64 query
+heads, KV entry dim 512 bf16, indexer 4 heads x 128 bf16, top-k 512, window
+128, sink on. One step = csa_index_topk (indexer scores of every entry + top-k)
+followed by csa_attend (MQA over selected entries + window + sink, combine with
+inverse RoPE). Inputs are seeded synthetic tensors resident in HBM; several
+copies are rotated so the 256 MB last-level cache cannot serve a step from the
+previous one.
+
+Also measured (secondary, same line): HCA decode, V4-Pro shaped: batch 8,
+1048576 context tokens (8192 entries), 128 heads.
+
+Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import long_context_attention_12_amd as L  # noqa: E402
+import workloads as WL  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+DEV = "cuda"
+
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(torch.bfloat16)
+
+
+def _f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def csa_decode_setup(d, copies):
+    base = {"E": _bf16(d["E"]), "kI": _bf16(d["kI"]), "q": _bf16(d["q"]), "qI": _bf16(d["qI"]),
+            "win": _bf16(d["win"]), "w": _f32(d["w"]), "sink": _f32(d["sink"])}
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    B, H, D, m, k = d["B"], d["H"], d["D"], d["m"], d["k"]
+    N = d["E"].shape[1]
+    ws_i = torch.empty(L.csa_index_topk_workspace(L.BF16, B, 1, d["H_I"], d["d_I"], N, m, k, d["q_pos0"]),
+                       dtype=torch.uint8, device=DEV)
+    ws_a = torch.empty(L.csa_attend_workspace(L.BF16, L.BF16, B, 1, H, D, N, m, k, d["W"], d["q_pos0"]),
+                       dtype=torch.uint8, device=DEV)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=DEV)
+
+    def step(i):
+        s = sets[i % copies]
+        L.csa_index_topk(L.BF16, s["qI"], s["w"], s["kI"], idx, m=m, k=k, q_pos0=d["q_pos0"], ws=ws_i)
+        L.csa_attend(L.BF16, L.BF16, s["q"], s["E"], idx, s["win"], s["sink"], out, m=m, W=d["W"],
+                     q_pos0=d["q_pos0"], scale=1 / math.sqrt(D), flags=L.INV_ROPE, rope_dims=64, ws=ws_a)
+    return step
+
+
+def hca_decode_setup(d, copies):
+    base = {"E": _bf16(d["E"]), "q": _bf16(d["q"]), "win": _bf16(d["win"]), "sink": _f32(d["sink"])}
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    B, H, D = d["B"], d["H"], d["D"]
+    N = d["E"].shape[1]
+    ws = torch.empty(L.hca_attend_workspace(L.BF16, L.BF16, B, 1, H, D, N, d["m"], d["W"], d["q_pos0"]),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=DEV)
+
+    def step(i):
+        s = sets[i % copies]
+        L.hca_attend(L.BF16, L.BF16, s["q"], s["E"], s["win"], s["sink"], out, m=d["m"], W=d["W"],
+                     q_pos0=d["q_pos0"], scale=1 / math.sqrt(D), flags=L.INV_ROPE, rope_dims=64, ws=ws)
+    return step
+
+
+def timed(step, steps, warmup):
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def kernel_times(step, steps):
+    """Average per-launch duration of each library kernel, from HIP events the
+    library records around its launches on the caller's stream."""
+    torch.cuda.synchronize()
+    L.lca_profile_collect()
+    L.lca_profile_enable(True)
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    L.lca_profile_enable(False)
+    stats = L.lca_profile_collect()
+    return {name: {"launches": n, "avg_us": 1e3 * ms / n} for name, (n, ms) in stats.items()}
+
+
+def csa_decode_bytes(d):
+    """Algorithmic HBM bytes of one CSA decode step (what the method must move)."""
+    B, H, D, k, W = d["B"], d["H"], d["D"], d["k"], d["W"]
+    N, H_I, d_I = d["E"].shape[1], d["H_I"], d["d_I"]
+    index = B * (N * d_I * 2 + H_I * d_I * 2 + H_I * 4)      # every indexer key once, queries, weights
+    attend = B * ((k + W) * D * 2 + 2 * H * D * 2)           # selected + window rows, q and out
+    return index, attend
+
+
+def hca_decode_bytes(d):
+    B, H, D, W = d["B"], d["H"], d["D"], d["W"]
+    N = d["E"].shape[1]
+    return B * ((N + W) * D * 2 + 2 * H * D * 2)
+
+
+def hca_decode_flops(d):
+    B, H, D, W = d["B"], d["H"], d["D"], d["W"]
+    N = d["E"].shape[1]
+    return 4.0 * B * H * (N + W) * D
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, src_hash):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        rec = json.load(open(path))[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, min_seconds=10.0):
+    """The float64 oracle on the host cores, on the same workload: the whole
+    batch of sequences (scores, top-k, attention), repeated until at least
+    ``min_seconds`` of CPU work have been timed."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    D, m, k, W, B = d["D"], d["m"], d["k"], d["W"], d["B"]
+    done, reps = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for b in range(B):
+            nv = O.n_visible(d["q_pos0"], m)
+            s = O.index_scores(d["qI"][b, 0], d["w"][b, 0], d["kI"][b], nv)
+            sel = O.topk_select(s, k)
+            O.csa_attend_query(d["q"][b, 0], d["E"][b], sel, d["win"][b], d["sink"], 1 / math.sqrt(D),
+                               d["q_pos0"], d["q_pos0"], W, True, 10000.0, 64)
+            done += 1
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the full batch of {B} sequences, {reps} times ({done} decode tokens), "
+                      f"float64 numpy oracle: indexer scores, top-k, attention; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode workloads shard by sequence with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    L.lib()
+
+    d = WL.make_csa_decode()
+    step = csa_decode_setup(d, args.copies)
+    elapsed = timed(step, args.steps, args.warmup)
+    ms = 1e3 * elapsed / args.steps
+    B = d["B"]
+    kt = kernel_times(step, args.steps)
+    ib, ab = csa_decode_bytes(d)
+    score = kt.get("index_score", {"avg_us": float("nan")})
+    achieved = ib / (score["avg_us"] * 1e-6) / 1e9
+    src = source_hash(["long_context_attention_12_amd/csrc/index_topk.hip",
+                       "long_context_attention_12_amd/csrc/lca_device.h"])
+    traffic = load_traffic("index_score", "csa_decode_b16_ctx131072", src)
+    result = {
+        "metric": "CSA/HCA decode tokens/s at 128K-1M ctx; achieved HBM GB/s vs peak (1 GPU)",
+        "value": B / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian, 1% 4x-norm spikes)",
+        "config": {"workload": "csa_decode_b16_ctx131072", "batch": B, "context": d["q_pos0"],
+                   "entries": d["E"].shape[1], "heads": d["H"], "head_dim": d["D"], "index_topk": d["k"],
+                   "indexer_heads": d["H_I"], "indexer_dim": d["d_I"], "window": d["W"],
+                   "input_copies_rotated": args.copies},
+        "roofline": {"bound": "hbm", "kernel": "index_score", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": ib},
+        "step_roofline": {"algorithmic_bytes": ib + ab,
+                          "achieved_GBs": (ib + ab) / (ms * 1e-3) / 1e9,
+                          "frac": (ib + ab) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "kernels_us": {k: round(v["avg_us"], 3) for k, v in kt.items()},
+    }
+    if not args.no_secondary:
+        h = WL.make_hca_decode()
+        hstep = hca_decode_setup(h, args.copies)
+        he = timed(hstep, max(20, args.steps // 2), args.warmup)
+        hms = 1e3 * he / max(20, args.steps // 2)
+        hk = kernel_times(hstep, max(20, args.steps // 2))
+        hb, hf = hca_decode_bytes(h), hca_decode_flops(h)
+        att = hk.get("hca_attend", {"avg_us": float("nan")})["avg_us"]
+        result["secondary"] = {
+            "workload": "hca_decode_b8_ctx1048576", "tokens_per_s": h["B"] / (hms * 1e-3),
+            "ms_per_step": hms, "kernels_us": {k: round(v["avg_us"], 3) for k, v in hk.items()},
+            "hca_attend_GBs": hb / (att * 1e-6) / 1e9, "hca_attend_hbm_frac": hb / (att * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "hca_attend_TFLOPs": hf / (att * 1e-6) / 1e12, "mfma_bf16_frac": hf / (att * 1e-6) / 2.5e15,
+            "algorithmic_bytes": hb, "flops": hf,
+        }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -224,7 +224,9 @@ def test_index_topk_f32_from_sequence_start():
         s = O.index_scores(qI[0, t], w[0, t], kI[0], nv)
         check_topk_set(idx_h[0, t], s, k)
         sel = idx_h[0, t][idx_h[0, t] >= 0]
-        np.testing.assert_allclose(sco_h[0, t][:len(sel)], s[sel], rtol=1e-5, atol=1e-6)
+        # fp32 accumulation with cancellation: absolute error scales with |score| overall
+        np.testing.assert_allclose(sco_h[0, t][:len(sel)], s[sel], rtol=1e-5,
+                                   atol=1e-6 * max(1.0, float(np.max(np.abs(s))) if nv else 1.0))
 
 
 def test_index_topk_all_ties_take_lowest_indices():
