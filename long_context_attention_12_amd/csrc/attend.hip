@@ -11,9 +11,11 @@
 // Decomposition: one workgroup per (sequence, query, row split, head group of
 // up to 64 heads). All heads of a group share each staged KV row, which is
 // read from HBM once per split. Rows of a split are staged 32 at a time into
-// LDS, both row-major (for S^T = X Q^T, rows as MFMA M) and transposed (for
-// O^T = X^T P^T, rows as MFMA K). Each wave owns 16 heads: its 16 x D query
-// block stays in registers as the B operand, its 16 x D output block in
+// a row-major LDS tile (double-buffered; the next tile's loads are in flight
+// in registers while the current one is consumed). S^T = X Q^T reads the tile
+// row-wise (rows as MFMA M); O^T = X^T P^T reads it transposed with gfx950's
+// ds_read_b64_tr_b16 (rows as MFMA K). Each wave owns 16 heads: its 16 x D
+// query block stays in registers as the B operand, its 16 x D output block in
 // accumulators, and the probabilities produced by the S^T accumulators feed
 // the PV MFMA's B operand with no data movement. Online softmax runs per
 // head in float32. Each split writes (max, sum, o) partials; the combine
@@ -74,24 +76,421 @@ __device__ __forceinline__ int64_t row_source(const AttendArgs& a, int b, int t,
 // ---------------------------------------------------------------------------
 // bf16 / mixed-storage MFMA kernel
 // ---------------------------------------------------------------------------
-template <int D, bool MIXED>
-__global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a, SplitPlan sp,
-                                                          float* __restrict__ part_o,
-                                                          float* __restrict__ part_ml) {
-  constexpr int XS = D + 8;              // row stride of X (bf16 elements)
-  constexpr int TS = kTileRows + 8;      // row stride of X^T
-  constexpr int KS = D / 32;             // K steps of S^T
-  constexpr int DT = D / 16;             // 16-channel output tiles
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[kTileRows * XS];
-  __shared__ __attribute__((aligned(16))) uint16_t XTs[D * TS];
-  __shared__ int64_t src_row[kTileRows];
-  __shared__ int src_kind[kTileRows];
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-  const int nthreads = blockDim.x;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+constexpr int kMaxSplitRows = 2048;
+constexpr int kAttThreads = 256;
+
+// Row table entry: >= 0 entry row of kv; <= -2 window row (-2 - r); -1 absent.
+__device__ __forceinline__ int32_t encode_row(const AttendArgs& a, int b, int t, const RowSpan& rs,
+                                              int64_t v) {
+  int kind;
+  const int64_t src = row_source(a, b, t, rs, v, &kind);
+  if (src < 0) return -1;
+  return kind == 0 ? static_cast<int32_t>(src) : static_cast<int32_t>(-2 - src);
+}
+
+// One 32-row tile for one wave (16 heads), in two parts.
+// tile_softmax: S^T = X Q^T and the online-softmax update; returns the PV
+// operand P^T (bf16). tile_pv: O^T += X^T P^T.
+// rows[v] == -1 marks an absent row; the row table is padded with -1 to a
+// whole number of tiles.
+//
+// Fixed reference max: each head takes the max logit of its first non-empty
+// tile as m_run and keeps it. Later probabilities p = exp(l - m_run) exceed 1
+// when later logits are larger, which float32 accumulators and the bf16 P
+// operand (float32 exponent range) absorb as long as l - m_run <= kHeadroom:
+// p <= e^60 ~ 1e26 and sums stay below ~1e30. The 16 x D output accumulators
+// are therefore never rescaled in the loop. If a logit ever exceeds the
+// reference by more than kHeadroom, the split is flagged (its partial max is
+// written as NaN) and the combine kernel recomputes that split exactly.
+constexpr float kHeadroom = 60.f;
+
+// LDS tile layouts. Padded: row r at r * (D + 8) elements. Swizzled (D = 512):
+// row r at r * 512 elements with its 16-byte slots permuted, logical slot c
+// stored at physical slot c ^ swz(r), swz(r) = (2r + (r >> 3)) & 15. Both
+// layouts keep the row-wise 16-byte reads of S^T = X Q^T and the transposed
+// 8-byte reads of X^T P^T free of LDS bank conflicts.
+__device__ __forceinline__ int slot_swizzle(int r) { return (2 * r + ((r >> 3) & 1)) & 15; }
+
+template <int D, bool SWZ>
+__device__ __forceinline__ int tile_offset(int r, int col) {
+  if constexpr (!SWZ) {
+    return r * (D + 8) + col;
+  } else {
+    return r * D + ((((col >> 3) ^ slot_swizzle(r)) << 3) | (col & 7));
+  }
+}
+
+// Online-softmax update of one 32-row tile from the S^T accumulators (lane:
+// head r16, rows 16h2 + 4g + i), with a fixed reference max (see above).
+__device__ __forceinline__ void softmax_update(const f32x4 (&sacc)[2], int v0, const int32_t* rows,
+                                               float scale, int g, float& m_run, float& z_run, bool& flag,
+                                               bf16x8& pf) {
+  const int4 rv0 = *reinterpret_cast<const int4*>(rows + v0 + 4 * g);
+  const int4 rv1 = *reinterpret_cast<const int4*>(rows + v0 + 16 + 4 * g);
+  const int rr[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
+  float lg[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float l = rr[i] != -1 ? sacc[i >> 2][i & 3] * scale : -INFINITY;
+    lg[i] = l;
+    mx = fmaxf(mx, l);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (m_run == -INFINITY) m_run = mx;              // first non-empty tile sets the reference
+  flag = flag || (mx > m_run + kHeadroom);
+  float psum = 0.f;
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = lg[i] == -INFINITY ? 0.f : __expf(fminf(lg[i] - m_run, kHeadroom));
+    psum += p[i];
+  }
+  psum += __shfl_xor(psum, 16, 64);
+  psum += __shfl_xor(psum, 32, 64);
+  z_run += psum;
+  uint4 pw;
+  pw.x = pack_bf16x2(p[0], p[1]);
+  pw.y = pack_bf16x2(p[2], p[3]);
+  pw.z = pack_bf16x2(p[4], p[5]);
+  pw.w = pack_bf16x2(p[6], p[7]);
+  pf = __builtin_bit_cast(bf16x8, pw);
+}
+
+template <int D, bool SWZ = false>
+__device__ __forceinline__ void tile_softmax(const uint16_t* X, int v0, const int32_t* rows,
+                                             const bf16x8 (&qf)[D / 32], float scale, int g, int r16,
+                                             float& m_run, float& z_run, bool& flag, bf16x8& pf) {
+  constexpr int KS = D / 32;
+  // S^T (32 rows x 16 heads) in two 16-row halves; lane: head r16, rows 16h2 + 4g + i
+  f32x4 sacc[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int row = h2 * 16 + r16;
+    constexpr int XB = KS < 8 ? KS : 8;            // K-step fragments read ahead of MFMAs
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s0 = 0; s0 < KS; s0 += XB) {
+      uint4 xa[XB];
+#pragma unroll
+      for (int e = 0; e < XB; ++e)
+        xa[e] = *reinterpret_cast<const uint4*>(X + tile_offset<D, SWZ>(row, 32 * (s0 + e) + 8 * g));
+#pragma unroll
+      for (int e = 0; e < XB; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[e]), qf[s0 + e], acc, 0, 0, 0);
+    }
+    sacc[h2] = acc;
+  }
+  softmax_update(sacc, v0, rows, scale, g, m_run, z_run, flag, pf);
+}
+
+template <int D, bool SWZ = false>
+__device__ __forceinline__ void tile_pv(const uint16_t* X, const bf16x8& pf, int g, int r16,
+                                        f32x4 (&acc_o)[D / 16]) {
+  constexpr int DT = D / 16;
+  // O^T += X^T P^T. A operand = rows {4g..4g+3, 16+4g..16+4g+3} of channel 16dt + r16,
+  // read transposed from the row-major tile (ds_read_b64_tr_b16: lane L of a
+  // 16-lane group supplies row 4g + L/4, channels 16dt + 4(L%4) .. +3)
+  const int row0 = 4 * g + (r16 >> 2), row1 = row0 + 16, c0 = 4 * (r16 & 3);
+  constexpr int PB = DT < 8 ? DT : 8;              // transposed reads batched ahead of MFMAs
+#pragma unroll
+  for (int d8 = 0; d8 < DT; d8 += PB) {
+    bf16x8 af[PB];
+#pragma unroll
+    for (int e = 0; e < PB; ++e) {
+      const int dt = d8 + e;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + tile_offset<D, SWZ>(row0, 16 * dt + c0)));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + tile_offset<D, SWZ>(row1, 16 * dt + c0)));
+      const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+      af[e] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+    }
+#pragma unroll
+    for (int e = 0; e < PB; ++e)
+      acc_o[d8 + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[e], pf, acc_o[d8 + e], 0, 0, 0);
+  }
+}
+
+// Swizzled tile (D = 512) with all LDS addresses precomputed per lane: every
+// read in the tile loop is `lane base + immediate offset`.
+//   S^T reads: lane (r16, g), row 16h2 + r16, K step s = 4j + k:
+//     byte = row*1024 + 256j + 64(k ^ w2) + 16(g ^ w1),  w = swz(r16) = 4w2 + w1
+//   X^T reads: lane (g, L), row0 = 4g + L/4 (+16 for the second half),
+//     channel tile dt = 8j + k: byte = row0*1024 + 256j + 32(k ^ a) + 16(h ^ c) + 8(L & 1)
+//     with swz(row0) = 2a + c and h = (L & 3) >> 1.
+struct SwzOffsets {
+  uint32_t qk[4];   // byte offsets of K-step groups k = 0..3 (row r16)
+  uint32_t pv[8];   // byte offsets of channel tiles k = 0..7 (row0)
+};
+
+__device__ __forceinline__ SwzOffsets swz_offsets(int g, int r16) {
+  SwzOffsets o;
+  const int w = slot_swizzle(r16), w2 = w >> 2, w1 = w & 3;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o.qk[k] = r16 * 1024 + 64 * (k ^ w2) + 16 * (g ^ w1);
+  const int row0 = 4 * g + (r16 >> 2);
+  const int sw = slot_swizzle(row0), aa = sw >> 1, cc = sw & 1, hh = (r16 & 3) >> 1;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o.pv[k] = row0 * 1024 + 32 * (k ^ aa) + 16 * (hh ^ cc) + 8 * (r16 & 1);
+  return o;
+}
+
+__device__ __forceinline__ void tile_softmax_swz(const uint16_t* X, const SwzOffsets& so, int v0,
+                                                 const int32_t* rows, const bf16x8 (&qf)[16], float scale,
+                                                 int g, float& m_run, float& z_run, bool& flag, bf16x8& pf) {
+  const char* xb = reinterpret_cast<const char*>(X);
+  f32x4 sacc[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += 2) {
+      uint4 xa[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + (e >> 2), k = e & 3;
+        xa[e] = *reinterpret_cast<const uint4*>(xb + so.qk[k] + h2 * 16384 + 256 * j);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[e]), qf[4 * (j0 + (e >> 2)) + (e & 3)], acc, 0, 0, 0);
+    }
+    sacc[h2] = acc;
+  }
+  softmax_update(sacc, v0, rows, scale, g, m_run, z_run, flag, pf);
+}
+
+__device__ __forceinline__ void tile_pv_swz(const uint16_t* X, const SwzOffsets& so, const bf16x8& pf,
+                                            f32x4 (&acc_o)[32]) {
+  const char* xb = reinterpret_cast<const char*>(X);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x8 af[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(xb + so.pv[k] + 256 * j));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(xb + so.pv[k] + 256 * j + 16384));
+      const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+      af[k] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      acc_o[8 * j + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[k], pf, acc_o[8 * j + k], 0, 0, 0);
+  }
+}
+
+template <int D, bool MIXED>
+__global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, SplitPlan sp,
+                                                                  float* __restrict__ part_o,
+                                                                  float* __restrict__ part_ml) {
+  constexpr int XS = D + 8;                       // LDS row stride (bf16)
+  constexpr int KS = D / 32;                      // K steps of S^T
+  constexpr int DT = D / 16;                      // 16-channel output tiles
+  constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  constexpr int CPT = kTileRows * CPR / kAttThreads;   // chunks per thread per tile
+  constexpr int NQ = D - 64;                      // fp8 channels of a mixed row
+  constexpr int RB = MIXED ? D + 64 : 2 * D;      // bytes per stored row
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kTileRows * XS];
+  __shared__ int32_t rows[kMaxSplitRows];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
   const int g = lane >> 4, r16 = lane & 15;
-  // head group and split: consecutive workgroup ids of the same split land on
-  // the same XCD when there are two head groups (ids i and i + 8 share one).
+  int split, hg;
+  {
+    // two head groups: ids i and i + 8 (same XCD) take the two groups of one split
+    const int i = blockIdx.x;
+    if (sp.n_hg == 2) {
+      hg = (i >> 3) & 1;
+      split = ((i >> 4) << 3) | (i & 7);
+    } else {
+      hg = i % sp.n_hg;
+      split = i / sp.n_hg;
+    }
+  }
+  if (split >= sp.S) return;
+  const int t = blockIdx.y, b = blockIdx.z;
+  const bool active = wid * 16 < sp.HG;
+  const int head = hg * sp.HG + wid * 16 + r16;
+  const RowSpan rs = row_span(a, t);
+  const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
+  int64_t r_end = r_begin + sp.RS;
+  if (r_end > rs.nrows) r_end = rs.nrows;
+  const int nr = r_end > r_begin ? static_cast<int>(r_end - r_begin) : 0;
+
+  // prologue: the row table's index loads and the query loads go out together
+  int32_t myrows[kMaxSplitRows / kAttThreads];
+#pragma unroll
+  for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) {
+    const int v = tid + kAttThreads * q;
+    myrows[q] = v < nr ? encode_row(a, b, t, rs, r_begin + v) : -1;
+  }
+  // (a wave past the block's heads computes on zero queries and writes nothing;
+  // a branch around the MFMAs would make the compiler copy the accumulators)
+  bf16x8 qf[KS];
+  if (active) {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) rows[tid + kAttThreads * q] = myrows[q];
+  f32x4 acc_o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, z_run = 0.f;
+  bool flag = false;
+  const float scale = a.scale;
+  const int64_t win_rows = a.W - 1 + a.Tq;
+  __syncthreads();
+
+  // staging: each thread moves CPT 16-byte chunks of a tile. Base pointers are
+  // chosen per lane from values held in registers, so the selection never
+  // turns into a per-lane load of a kernel argument.
+  const uint8_t* kv_base = static_cast<const uint8_t*>(a.kv);
+  const uint8_t* win_base = static_cast<const uint8_t*>(a.win);
+  const float* kv_sc = a.kv_scale;
+  const float* win_sc = a.win_scale;
+  const int64_t kv_off = static_cast<int64_t>(b) * a.N_cap;
+  const int64_t win_off = static_cast<int64_t>(b) * win_rows;
+  uint4 pre[CPT];
+  float psc[CPT];
+  auto issue = [&](int tile) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int chunk = tid + kAttThreads * c;
+      const int r = chunk / CPR, d0 = (chunk % CPR) * 8;
+      const int v = tile * kTileRows + r;
+      const int32_t src = v < nr ? rows[v] : -1;
+      const bool is_kv = src >= 0;
+      const int64_t ridx = is_kv ? kv_off + src : win_off + (-2 - src);
+      const uint8_t* base = (is_kv ? kv_base : win_base) + ridx * RB;
+      pre[c] = make_uint4(0, 0, 0, 0);
+      psc[c] = 0.f;
+      if (src != -1) {
+        if constexpr (!MIXED) {
+          pre[c] = *reinterpret_cast<const uint4*>(base + 2 * d0);
+        } else {
+          if (d0 < NQ) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(base + d0);
+            pre[c] = make_uint4(raw.x, raw.y, 0, 0);
+            psc[c] = (is_kv ? kv_sc : win_sc)[ridx];
+          } else {
+            pre[c] = *reinterpret_cast<const uint4*>(base + NQ + 2 * (d0 - NQ));
+          }
+        }
+      }
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int chunk = tid + kAttThreads * c;
+      const int r = chunk / CPR, d0 = (chunk % CPR) * 8;
+      uint4 v = pre[c];
+      if constexpr (MIXED) {
+        if (d0 < NQ) {
+          const float sc = psc[c];
+          uint32_t w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t word = q < 2 ? v.x : v.y;
+            const uint32_t b0 = (word >> (16 * (q & 1))) & 0xffu;
+            const uint32_t b1 = (word >> (16 * (q & 1) + 8)) & 0xffu;
+            w[q] = pack_bf16x2(e4m3fn_to_f32(b0) * sc, e4m3fn_to_f32(b1) * sc);
+          }
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+      *reinterpret_cast<uint4*>(&Xs[buf][r * XS + d0]) = v;
+    }
+  };
+
+  const int ntiles = (nr + kTileRows - 1) / kTileRows;
+  if (ntiles > 0) {
+    issue(0);
+    commit(0);
+  }
+  // nothing may be in flight when the loop starts: the loop body then needs
+  // no wait on the query fragments, and the next tile's loads overlap compute
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) issue(it + 1);
+    {
+      const uint16_t* X = Xs[buf];
+      bf16x8 pf;
+      tile_softmax<D>(X, it * kTileRows, rows, qf, scale, g, r16, m_run, z_run, flag, pf);
+      tile_pv<D>(X, pf, g, r16, acc_o);
+    }
+    if (it + 1 < ntiles) commit(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (active) {
+    const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
+    float* po = part_o + part_idx * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+    if (g == 0) {
+      part_ml[2 * part_idx] = flag ? __builtin_nanf("") : m_run;   // NaN: recompute in combine
+      part_ml[2 * part_idx + 1] = z_run;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 rows of 512 channels: tiles are copied HBM -> LDS by the load units
+// themselves (global_load_lds_dwordx4: one 1 KB row per wave instruction, no
+// registers involved) into a ring of four LDS tiles, so three tiles (~100 KB)
+// are in flight per CU while the fourth is consumed. That depth covers the
+// loaded-memory latency at this CU's share of HBM bandwidth.
+// ---------------------------------------------------------------------------
+constexpr int kRing = 4;
+
+// One 16-byte-per-lane copy HBM -> LDS: lane l's 16 bytes at `gptr` land at
+// LDS byte address lds_addr + 16 * l. Issued as inline asm so that the
+// compiler does not track it: every wait on these copies in the ring loop is
+// explicit (wait_vmcnt), and the loop issues no other vector-memory access.
+// The instruction has no register results.
+__device__ __forceinline__ void lds_copy16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)(p)));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with vmcnt = N (6-bit field split over [3:0] and [15:14]); expcnt
+  // and lgkmcnt at their maxima, i.e. not waited on
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, SplitPlan sp,
+                                                                 float* __restrict__ part_o,
+                                                                 float* __restrict__ part_ml) {
+  constexpr int D = 512, KS = D / 32, DT = D / 16;
+  constexpr int RPW = kTileRows / 4;               // rows per wave per tile
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[kRing][kTileRows * D];
+  __shared__ int32_t rows[kMaxSplitRows];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
+  const int g = lane >> 4, r16 = lane & 15;
   int split, hg;
   {
     const int i = blockIdx.x;
@@ -103,148 +502,115 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttendArgs a, SplitPla
       split = i / sp.n_hg;
     }
   }
+  if (split >= sp.S) return;
   const int t = blockIdx.y, b = blockIdx.z;
+  const bool active = wid * 16 < sp.HG;
   const int head = hg * sp.HG + wid * 16 + r16;
   const RowSpan rs = row_span(a, t);
   const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
   int64_t r_end = r_begin + sp.RS;
   if (r_end > rs.nrows) r_end = rs.nrows;
-  const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
-  if (split >= sp.S) return;
+  const int nr = r_end > r_begin ? static_cast<int>(r_end - r_begin) : 0;
 
-  // Q fragments (B operand of S^T): head, channels 32s + 8g .. +7
+  // row table (its index loads all in flight together)
+  int32_t myrows[kMaxSplitRows / kAttThreads];
+#pragma unroll
+  for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) {
+    const int v = tid + kAttThreads * q;
+    myrows[q] = v < nr ? encode_row(a, b, t, rs, r_begin + v) : -1;
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) rows[tid + kAttThreads * q] = myrows[q];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int64_t win_rows = a.W - 1 + a.Tq;
+  const uint16_t* kvp = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(b) * a.N_cap * D;
+  const uint16_t* winp = static_cast<const uint16_t*>(a.win) + static_cast<int64_t>(b) * win_rows * D;
+  // Wave w copies rows [RPW*w, RPW*w + RPW) of a tile, one 1 KB row per
+  // instruction. Lane l fetches logical 16-byte slot l ^ swz(r), which lands at
+  // physical slot l: the tile is stored swizzled. Lanes 0..RPW-1 resolve the
+  // rows' addresses, which reach the copies through readlane. Absent rows copy
+  // window row 0 (any valid memory) and are masked out of the softmax.
+  uint32_t src_off[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr)
+    src_off[rr] = 16u * static_cast<uint32_t>((lane & 48) | ((lane & 15) ^ slot_swizzle(wid * RPW + rr)));
+  auto issue = [&](int tile, uint16_t* dst) {
+    const int v0 = tile * kTileRows + wid * RPW;
+    uint64_t my = 0;
+    if (lane < RPW) {
+      const int v = v0 + lane;
+      const int32_t sr = v < nr ? rows[v] : -1;
+      const uint16_t* rowp = sr >= 0 ? kvp + static_cast<int64_t>(sr) * D
+                                     : winp + (sr == -1 ? 0 : static_cast<int64_t>(-2 - sr) * D);
+      my = reinterpret_cast<uint64_t>(rowp);
+    }
+    const uint32_t lds0 = lds_address(dst + wid * RPW * D);
+    const uint32_t lo = static_cast<uint32_t>(my), hi = static_cast<uint32_t>(my >> 32);
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const uint64_t rb = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), rr))) << 32) |
+                          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), rr));
+      lds_copy16(reinterpret_cast<const void*>(rb + src_off[rr]), lds0 + rr * D * 2);
+    }
+  };
+  const int ntiles = (nr + kTileRows - 1) / kTileRows;
+  // Tile `tt` has landed in this wave's view once at most the copies of the
+  // tiles after it that were already issued remain outstanding (RPW each).
+  auto wait_tile = [&](int tt) {
+    const int later = min(ntiles - 1, tt + kRing - 2) - tt;
+    if (later >= 2) wait_vmcnt<2 * RPW>();
+    else if (later == 1) wait_vmcnt<RPW>();
+    else wait_vmcnt<0>();
+    // A bare barrier: the wave's own copies are complete (waited above) and
+    // every LDS read of the previous tile fed an MFMA already, so no fence is
+    // needed; a fence would also drain the later copies that must stay in flight.
+    __builtin_amdgcn_s_barrier();
+  };
+#pragma unroll
+  for (int t0 = 0; t0 < kRing - 1; ++t0)
+    if (t0 < ntiles) issue(t0, Xs[t0]);
+  // query fragments load while the first tiles are in flight
+  // (a wave past the block's heads computes on zero queries and writes nothing)
   bf16x8 qf[KS];
-  {
+  if (active) {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
   }
   f32x4 acc_o[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, z_run = 0.f;
-  const float scale = a.scale;
+  const SwzOffsets so = swz_offsets(g, r16);
+  if (0 < ntiles) wait_tile(0);
+  __builtin_amdgcn_s_waitcnt(0);      // query fragments too (tiles 1, 2 may land meanwhile)
 
-  for (int64_t t0 = r_begin; t0 < r_end; t0 += kTileRows) {
-    if (tid < kTileRows) {
-      int kind;
-      const int64_t v = t0 + tid;
-      src_row[tid] = v < r_end ? row_source(a, b, t, rs, v, &kind) : -1;
-      src_kind[tid] = v < r_end ? kind : 0;
-    }
-    __syncthreads();
-    // stage 32 rows: chunks of 8 channels
-    for (int c = tid; c < kTileRows * (D / 8); c += nthreads) {
-      const int r = c / (D / 8), d0 = (c % (D / 8)) * 8;
-      const int64_t sr = src_row[r];
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (sr >= 0) {
-        const int kind = src_kind[r];
-        if constexpr (!MIXED) {
-          const uint16_t* base = kind == 0 ? static_cast<const uint16_t*>(a.kv) + (static_cast<int64_t>(b) * a.N_cap + sr) * D
-                                           : static_cast<const uint16_t*>(a.win) + (static_cast<int64_t>(b) * (a.W - 1 + a.Tq) + sr) * D;
-          v = *reinterpret_cast<const uint4*>(base + d0);
-        } else {
-          constexpr int R = 64, NQ = D - R, RB = NQ + 2 * R;
-          const int64_t ridx = kind == 0 ? static_cast<int64_t>(b) * a.N_cap + sr
-                                         : static_cast<int64_t>(b) * (a.W - 1 + a.Tq) + sr;
-          const uint8_t* base = static_cast<const uint8_t*>(kind == 0 ? a.kv : a.win) + ridx * RB;
-          if (d0 < NQ) {
-            const float s = (kind == 0 ? a.kv_scale : a.win_scale)[ridx];
-            const uint2 raw = *reinterpret_cast<const uint2*>(base + d0);
-            uint32_t w[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t word = q < 2 ? raw.x : raw.y;
-              const uint32_t b0 = (word >> (16 * (q & 1))) & 0xffu;
-              const uint32_t b1 = (word >> (16 * (q & 1) + 8)) & 0xffu;
-              w[q] = pack_bf16x2(e4m3fn_to_f32(b0) * s, e4m3fn_to_f32(b1) * s);
-            }
-            v = make_uint4(w[0], w[1], w[2], w[3]);
-          } else {
-            v = *reinterpret_cast<const uint4*>(base + NQ + 2 * (d0 - NQ));
-          }
-        }
-      }
-      *reinterpret_cast<uint4*>(&Xs[r * XS + d0]) = v;
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) XTs[(d0 + i) * TS + r] = static_cast<uint16_t>(wv[i >> 1] >> (16 * (i & 1)));
-    }
-    __syncthreads();
-
-    // S^T (32 rows x 16 heads) in two 16-row halves
-    f32x4 sacc[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint16_t* xr = &Xs[(h2 * 16 + r16) * XS + 8 * g];
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xr + 32 * s)), qf[s], acc, 0, 0, 0);
-      sacc[h2] = acc;
-    }
-    // lane holds head r16, rows h2*16 + 4g + i
-    float lg[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = h2 * 16 + 4 * g + i;
-        const float l = src_row[r] >= 0 ? sacc[h2][i] * scale : -INFINITY;
-        lg[h2 * 4 + i] = l;
-        mx = fmaxf(mx, l);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    float alpha, psum = 0.f;
-    float p[8];
-    if (m_new == -INFINITY) {
-      alpha = 1.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.f;
-    } else {
-      alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = lg[i] == -INFINITY ? 0.f : __expf(lg[i] - m_new);
-        psum += p[i];
-      }
-    }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    z_run = z_run * alpha + psum;
-    m_run = m_new;
-    uint4 pw;
-    pw.x = pack_bf16x2(p[0], p[1]);
-    pw.y = pack_bf16x2(p[2], p[3]);
-    pw.z = pack_bf16x2(p[4], p[5]);
-    pw.w = pack_bf16x2(p[6], p[7]);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
-    // O^T += X^T P^T: A rows = channels 16dt + r16, K = rows {4g..4g+3, 16+4g..16+4g+3}
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* xt = &XTs[(16 * dt + r16) * TS + 4 * g];
-      const uint2 lo = *reinterpret_cast<const uint2*>(xt);
-      const uint2 hi = *reinterpret_cast<const uint2*>(xt + 16);
-      const bf16x8 af = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      f32x4 o = acc_o[dt];
-      o[0] *= alpha; o[1] *= alpha; o[2] *= alpha; o[3] *= alpha;
-      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o, 0, 0, 0);
-    }
-    __syncthreads();
+  // Ring step: refill the slot freed by tile it-1 with tile it+3, consume tile
+  // it, then wait for tile it+1.
+  bool flag = false;
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + kRing - 1 < ntiles) issue(it + kRing - 1, Xs[(it + kRing - 1) % kRing]);
+    bf16x8 pf;
+    tile_softmax_swz(Xs[it % kRing], so, it * kTileRows, rows, qf, a.scale, g, m_run, z_run, flag, pf);
+    tile_pv_swz(Xs[it % kRing], so, pf, acc_o);
+    if (it + 1 < ntiles) wait_tile(it + 1);
   }
 
-  // partials: o[head][16dt + 4g + i]
-  float* po = part_o + part_idx * D;
+  if (active) {
+    const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
+    float* po = part_o + part_idx * D;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
-  if (g == 0) {
-    part_ml[2 * part_idx] = m_run;
-    part_ml[2 * part_idx + 1] = z_run;
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+    if (g == 0) {
+      part_ml[2 * part_idx] = flag ? __builtin_nanf("") : m_run;   // NaN: recompute in combine
+      part_ml[2 * part_idx + 1] = z_run;
+    }
   }
 }
 
@@ -360,74 +726,186 @@ __global__ __launch_bounds__(kF32Threads) void attend_f32_kernel(AttendArgs a, S
 }
 
 // ---------------------------------------------------------------------------
-// combine: merge split partials, add the sink, normalise, inverse RoPE
+// combine: merge split partials, add the sink, normalise, inverse RoPE.
+// One workgroup per (sequence, query, head); thread c owns channel pair
+// (2c, 2c+1). Split maxima/sums and the partial rows are loaded together, so
+// the kernel makes a single round trip to memory.
 // ---------------------------------------------------------------------------
-constexpr int kCombThreads = 128;
+constexpr int kCombBatch = 16;      // splits per register batch
+constexpr int kCombMaxRows = 2048;  // logits cached by the exact recompute
 
-__global__ __launch_bounds__(kCombThreads) void combine_kernel(AttendArgs a, int S,
-                                                               const float* __restrict__ part_o,
-                                                               const float* __restrict__ part_ml) {
-  __shared__ float wsplit[256];
-  __shared__ float sh_inv;
-  __shared__ float rope_cs[2 * 256];
-  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+// Channel pair (2c, 2c+1) of one stored row, as float.
+__device__ __forceinline__ float2 load_pair(const AttendArgs& a, int b, int64_t src, int kind, int c) {
   const int D = a.D;
-  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + h;
-  const float* ml = part_ml + row * S * 2;
-  const float sink = a.sink[h];
-  if (tid == 0) {
-    float M = sink;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-    float Z = expf(sink - M);
-    for (int s = 0; s < S; ++s) {
-      const float ms = ml[2 * s];
-      const float w = ms == -INFINITY ? 0.f : expf(ms - M);
-      wsplit[s] = w;
-      Z += ml[2 * s + 1] * w;
-    }
-    sh_inv = 1.0f / Z;
-    if (a.lse_out) a.lse_out[row] = M + logf(Z);
+  const int64_t ridx = kind == 0 ? static_cast<int64_t>(b) * a.N_cap + src
+                                 : static_cast<int64_t>(b) * (a.W - 1 + a.Tq) + src;
+  const void* base = kind == 0 ? a.kv : a.win;
+  if (a.dt_kv == LCA_F32) return reinterpret_cast<const float2*>(static_cast<const float*>(base) + ridx * D)[c];
+  if (a.dt_kv == LCA_BF16) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + ridx * D)[c];
+    return make_float2(bf16_to_f32(static_cast<uint16_t>(w & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(w >> 16)));
   }
-  const bool rot = (a.flags & LCA_INV_ROPE) && a.rope_dims > 0;
-  if (rot) {
-    const double pos = -static_cast<double>(a.q_pos0 + t);
-    for (int i = tid; i < a.rope_dims / 2; i += kCombThreads) {
-      float sn, cs;
-      rope_sincos(pos, i, a.rope_dims, static_cast<double>(a.rope_base), &sn, &cs);
-      rope_cs[2 * i] = cs;
-      rope_cs[2 * i + 1] = sn;
+  const int NQ = D - a.rope_dims;                  // mixed row: fp8 body, bf16 RoPE tail
+  const uint8_t* row = static_cast<const uint8_t*>(base) + ridx * (D + a.rope_dims);
+  if (2 * c < NQ) {
+    const float sc = (kind == 0 ? a.kv_scale : a.win_scale)[ridx];
+    return make_float2(e4m3fn_to_f32(row[2 * c]) * sc, e4m3fn_to_f32(row[2 * c + 1]) * sc);
+  }
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(row + NQ + 2 * (2 * c - NQ));
+  return make_float2(bf16_to_f32(static_cast<uint16_t>(w & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(w >> 16)));
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wid] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int i = 0; i < nw; ++i) r += red[i];
+  return r;
+}
+
+// Exact float32 recompute of one split's (max, sum, o pair) for head h: the
+// slow path for splits whose logits outgrew the attention kernel's headroom.
+__device__ void recompute_split(const AttendArgs& a, int RS, int b, int t, int h, int s, float* red,
+                                float* lc, float& m_out, float& z_out, float2& o_out) {
+  const int c = threadIdx.x;
+  const bool own = 2 * c < a.D;
+  const RowSpan rs = row_span(a, t);
+  const int64_t r0 = static_cast<int64_t>(s) * RS;
+  int64_t r1 = r0 + RS;
+  if (r1 > rs.nrows) r1 = rs.nrows;
+  float2 qv = make_float2(0.f, 0.f);
+  if (own) {
+    const int64_t qrow = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + h) * a.D;
+    if (a.dt_q == LCA_F32) {
+      qv = reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qrow)[c];
+    } else {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + qrow)[c];
+      qv = make_float2(bf16_to_f32(static_cast<uint16_t>(w & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(w >> 16)));
     }
+  }
+  float M = -INFINITY;
+  for (int64_t v = r0; v < r1; ++v) {
+    int kind;
+    const int64_t src = row_source(a, b, t, rs, v, &kind);
+    float part = 0.f;
+    if (src >= 0 && own) {
+      const float2 x = load_pair(a, b, src, kind, c);
+      part = qv.x * x.x + qv.y * x.y;
+    }
+    // src depends only on (b, t, v): every thread takes the same branch
+    const float l = src >= 0 ? block_sum(part, red) * a.scale : -INFINITY;
+    if (c == 0) lc[v - r0] = l;
+    M = fmaxf(M, l);
   }
   __syncthreads();
-  const float inv = sh_inv;
+  float z = 0.f;
+  float2 o = make_float2(0.f, 0.f);
+  for (int64_t v = r0; v < r1; ++v) {
+    const float l = lc[v - r0];
+    if (l == -INFINITY) continue;
+    const float p = expf(l - M);
+    z += p;
+    if (own) {
+      int kind;
+      const int64_t src = row_source(a, b, t, rs, v, &kind);
+      const float2 x = load_pair(a, b, src, kind, c);
+      o.x = fmaf(p, x.x, o.x);
+      o.y = fmaf(p, x.y, o.y);
+    }
+  }
+  m_out = M;
+  z_out = z;
+  o_out = o;
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int S, int RS,
+                                                      const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml) {
+  __shared__ float sml[2 * 256];
+  __shared__ float red[4];
+  __shared__ float lc[kCombMaxRows];
+  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
+  const int D = a.D;
+  const bool own = 2 * c < D;
+  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + h;
+  const float* ml = part_ml + row * S * 2;
   const float* po = part_o + row * S * D;
-  const int R = rot ? a.rope_dims : 0;
-  // each thread owns channel pairs (2c, 2c+1)
-  for (int c = tid; c < D / 2; c += kCombThreads) {
-    float u = 0.f, v = 0.f;
+  for (int i = c; i < 2 * S; i += blockDim.x) sml[i] = ml[i];
+  float2 ov[kCombBatch];
+#pragma unroll
+  for (int j = 0; j < kCombBatch; ++j)
+    ov[j] = (j < S && own) ? *reinterpret_cast<const float2*>(po + static_cast<int64_t>(j) * D + 2 * c) : make_float2(0.f, 0.f);
+  const float sink = a.sink[h];
+  __syncthreads();
+  // splits flagged by the attention kernel (NaN max) are recomputed exactly
+  bool any_flag = false;
+  for (int s = 0; s < S; ++s) any_flag = any_flag || (sml[2 * s] != sml[2 * s]);
+  if (any_flag) {
     for (int s = 0; s < S; ++s) {
-      const float w = wsplit[s];
-      u = fmaf(w, po[s * D + 2 * c], u);
-      v = fmaf(w, po[s * D + 2 * c + 1], v);
+      if (sml[2 * s] == sml[2 * s]) continue;      // uniform across the block
+      float m, z;
+      float2 o;
+      recompute_split(a, RS, b, t, h, s, red, lc, m, z, o);
+      __syncthreads();
+      if (c == 0) { sml[2 * s] = m; sml[2 * s + 1] = z; }
+#pragma unroll
+      for (int j = 0; j < kCombBatch; ++j)
+        if (j == s) ov[j] = o;                     // splits past the batch: recomputed below
+      __syncthreads();
     }
-    u *= inv;
-    v *= inv;
-    const int d0 = 2 * c;
-    if (d0 >= D - R) {
-      const int i = (d0 - (D - R)) / 2;
-      const float cs = rope_cs[2 * i], sn = rope_cs[2 * i + 1];
-      const float nu = u * cs - v * sn, nv = u * sn + v * cs;
-      u = nu;
-      v = nv;
+  }
+  float M = sink;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, sml[2 * s]);
+  float Z = expf(sink - M);
+  for (int s = 0; s < S; ++s) {
+    const float ms = sml[2 * s];
+    Z += ms == -INFINITY ? 0.f : sml[2 * s + 1] * expf(ms - M);
+  }
+  float u = 0.f, v = 0.f;
+#pragma unroll
+  for (int j = 0; j < kCombBatch; ++j) {
+    if (j < S) {
+      const float ms = sml[2 * j];
+      const float w = ms == -INFINITY ? 0.f : expf(ms - M);
+      u = fmaf(w, ov[j].x, u);
+      v = fmaf(w, ov[j].y, v);
     }
-    if (a.dt_q == LCA_F32) {
-      float* o = static_cast<float*>(a.out) + row * D;
-      o[d0] = u;
-      o[d0 + 1] = v;
-    } else {
-      uint32_t* o = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + row * D);
-      o[c] = pack_bf16x2(u, v);
+  }
+  for (int s = kCombBatch; s < S; ++s) {
+    const float ms = sml[2 * s];
+    const float w = ms == -INFINITY ? 0.f : expf(ms - M);
+    float2 o = own ? *reinterpret_cast<const float2*>(po + static_cast<int64_t>(s) * D + 2 * c) : make_float2(0.f, 0.f);
+    if (any_flag && ml[2 * s] != ml[2 * s]) {       // flagged split beyond the batch: recompute again
+      float m2, z2;
+      recompute_split(a, RS, b, t, h, s, red, lc, m2, z2, o);
     }
+    u = fmaf(w, o.x, u);
+    v = fmaf(w, o.y, v);
+  }
+  if (!own) return;
+  const float inv = 1.0f / Z;
+  u *= inv;
+  v *= inv;
+  if (c == 0 && a.lse_out) a.lse_out[row] = M + logf(Z);
+  const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
+  const int d0 = 2 * c;
+  if (d0 >= D - R) {
+    float sn, cs;
+    rope_sincos(-static_cast<double>(a.q_pos0 + t), (d0 - (D - R)) / 2, R,
+                static_cast<double>(a.rope_base), &sn, &cs);
+    const float nu = u * cs - v * sn, nv = u * sn + v * cs;
+    u = nu;
+    v = nv;
+  }
+  if (a.dt_q == LCA_F32) {
+    float* o = static_cast<float*>(a.out) + row * D;
+    o[d0] = u;
+    o[d0 + 1] = v;
+  } else {
+    reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + row * D)[c] = pack_bf16x2(u, v);
   }
 }
 
@@ -454,14 +932,24 @@ SplitPlan make_plan(const AttendArgs& a) {
   }
   const int64_t win = p + 1 < a.W ? p + 1 : a.W;
   const int64_t nrows = n_ent + win;
-  const int64_t min_rows = nrows > 4096 ? 256 : 64;
-  int64_t S = (1024 + static_cast<int64_t>(a.Tq) * sp.n_hg - 1) / (static_cast<int64_t>(a.Tq) * sp.n_hg);
-  int64_t smax = (nrows + min_rows - 1) / min_rows;
-  if (S > smax) S = smax;
-  if (S < 1) S = 1;
-  int64_t RS = (nrows + S - 1) / S;
+  // Split size: each split writes a (D+2)-float partial per head, so splits
+  // shorter than min_rows move more partial bytes than rows. With two head
+  // groups (128 heads) a sequence gets 16 splits (32 workgroups), so a batch of
+  // 8 fills the 256 CUs in one round; with one head group, splits of 64 rows.
+  int64_t RS;
+  if (sp.n_hg >= 2) {
+    RS = (nrows * a.Tq + 15) / 16;
+    if (RS < 256) RS = 256;
+  } else {
+    const int64_t work = nrows * a.Tq;
+    RS = (work + 319) / 320;
+    if (RS < 64) RS = 64;
+  }
+  if (RS > nrows) RS = nrows;
   RS = (RS + kTileRows - 1) / kTileRows * kTileRows;
-  S = (nrows + RS - 1) / RS;
+  if (RS > kMaxSplitRows) RS = kMaxSplitRows;
+  if (RS < kTileRows) RS = kTileRows;
+  int64_t S = (nrows + RS - 1) / RS;
   if (S < 1) S = 1;
   if (S > 256) {                      // combine keeps split weights in LDS
     S = 256;
@@ -476,9 +964,11 @@ template <int D>
 void launch_mfma_d(hipStream_t s, const AttendArgs& a, const SplitPlan& sp, float* po, float* pml) {
   int nblk = sp.S * sp.n_hg;
   if (sp.n_hg == 2) nblk = ((sp.S + 7) / 8) * 16;     // XCD-paired id layout
-  dim3 grid(nblk, a.Tq, a.B), block(64 * (sp.HG / 16));
+  dim3 grid(nblk, a.Tq, a.B), block(kAttThreads);
   if (a.dt_kv == LCA_KV_MIXED)
     hipLaunchKernelGGL((attend_mfma_kernel<D, true>), grid, block, 0, s, a, sp, po, pml);
+  else if constexpr (D == 512)
+    hipLaunchKernelGGL(attend_dma_kernel, grid, block, 0, s, a, sp, po, pml);
   else
     hipLaunchKernelGGL((attend_mfma_kernel<D, false>), grid, block, 0, s, a, sp, po, pml);
 }
@@ -516,7 +1006,8 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
   }
   {
     LaunchScope scope(s, "attend_combine");
-    hipLaunchKernelGGL(combine_kernel, dim3(a.H, a.Tq, a.B), dim3(kCombThreads), 0, s, a, sp.S, po, pml);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.H, a.Tq, a.B), dim3(a.D / 2 > 64 ? a.D / 2 : 64), 0, s, a, sp.S,
+                       sp.RS, po, pml);
     return hipGetLastError();
   }
 }

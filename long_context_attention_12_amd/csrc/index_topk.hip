@@ -14,10 +14,12 @@
 // workspace (float32, 4 B per entry: small next to the 256 B key row).
 //
 // Selection is an MSB-first radix select per query in one 1024-thread
-// workgroup (LDS histograms of 12/10/10-bit digits, 10/6 bits for bf16
-// scores), followed by an order-preserving compaction: output indices come out
-// in increasing order and ties at the threshold go to the lowest indices, so
-// the result is deterministic.
+// workgroup (LDS histograms of 12/10/10-bit digits, 12/4 bits for bf16
+// scores). Up to 32768 scores stay in registers (32 per thread, loaded once,
+// all loads in flight together); longer lists are processed in rounds of
+// 32768. An order-preserving compaction follows: output indices come out in
+// increasing order and ties at the threshold go to the lowest indices, so the
+// result is deterministic.
 #include "lca_device.h"
 #include "lca_internal.h"
 #include "../../include/lca.h"
@@ -26,7 +28,8 @@ namespace lca {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kKeysPerWG = 1024;   // keys per scoring workgroup (4 waves x 256)
+constexpr int kKeysPerWave = 64;   // 4 MFMA key groups, all loads issued together
+constexpr int kKeysPerWG = 4 * kKeysPerWave;
 
 // ---------------------------------------------------------------------------
 // bf16 scoring with MFMA 16x16x32 (A = 16 indexer query-head rows, B = 16 keys)
@@ -34,10 +37,11 @@ constexpr int kKeysPerWG = 1024;   // keys per scoring workgroup (4 waves x 256)
 template <int HI, int DI>
 __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
-    float* __restrict__ scores, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, int m,
-    bool round_bf16) {
+    float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
+    int m, bool round_bf16) {
   constexpr int QPB = 16 / HI;       // queries per M tile
   constexpr int KS = DI / 32;        // K steps
+  constexpr int UNR = kKeysPerWave / 16;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int b = blockIdx.z;
@@ -46,9 +50,19 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
   const int tq_last = min(tq0 + QPB, t_end) - 1;
   int64_t nv_max = n_visible(q_pos0 + tq_last, m);
   if (nv_max > N_cap) nv_max = N_cap;
-  const int64_t key0 = static_cast<int64_t>(blockIdx.x) * kKeysPerWG + wid * (kKeysPerWG / 4);
+  const int64_t key0 = static_cast<int64_t>(blockIdx.x) * kKeysPerWG + wid * kKeysPerWave;
   if (key0 >= nv_max) return;
 
+  // keys first: every load of this wave is in flight before anything waits
+  const uint16_t* kb = kI + static_cast<int64_t>(b) * N_cap * DI;
+  uint4 kv[UNR][KS];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    int64_t j = key0 + 16 * u + r16;
+    if (j >= nv_max) j = nv_max - 1;               // stay in bounds; result discarded
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kv[u][s] = *reinterpret_cast<const uint4*>(kb + j * DI + 32 * s + 8 * g);
+  }
   // A operand: row r16 -> (query tq0 + r16 / HI, head r16 % HI); K chunk 8g..8g+7
   bf16x8 aq[KS];
   {
@@ -69,60 +83,45 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
     wv[i] = qt < t_end ? w[(static_cast<int64_t>(b) * Tq + qt) * HI + h] : 0.f;
     nvq[i] = qt < t_end ? n_visible(q_pos0 + qt, m) : 0;
   }
-  const uint16_t* kb = kI + static_cast<int64_t>(b) * N_cap * DI;
-  const int64_t key_end = min(key0 + kKeysPerWG / 4, nv_max);
-
-  constexpr int UNR = 4;             // key groups of 16 in flight per wave
-  for (int64_t j0 = key0; j0 < key_end; j0 += 16 * UNR) {
-    uint4 kv[UNR][KS];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      int64_t j = j0 + 16 * u + r16;
-      if (j >= nv_max) j = nv_max - 1;             // stay in bounds; result discarded
+  for (int u = 0; u < UNR; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        kv[u][s] = *reinterpret_cast<const uint4*>(kb + j * DI + 32 * s + 8 * g);
-    }
+    for (int s = 0; s < KS; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], __builtin_bit_cast(bf16x8, kv[u][s]), acc, 0, 0, 0);
+    const int64_t j = key0 + 16 * u + r16;
+    // acc[i] = qI(row 4g+i) . kI(j); fold ReLU and head weights per query
+    float part[4];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) part[i] = wv[i] * fmaxf(acc[i], 0.f);
+    if constexpr (HI == 1) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], __builtin_bit_cast(bf16x8, kv[u][s]), acc, 0, 0, 0);
-      const int64_t j = j0 + 16 * u + r16;
-      // acc[i] = qI(row 4g+i) . kI(j); fold ReLU and head weights per query
-      float part[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] = wv[i] * fmaxf(acc[i], 0.f);
-      if constexpr (HI == 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int qt = tq0 + 4 * g + i;
-          if (qt < t_end && j < nvq[i]) {
-            const float sc = round_bf16 ? bf16_round(part[i]) : part[i];
-            scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * N_cap + j] = sc;
-          }
+      for (int i = 0; i < 4; ++i) {
+        const int qt = tq0 + 4 * g + i;
+        if (qt < t_end && j < nvq[i]) {
+          const float sc = round_bf16 ? bf16_round(part[i]) : part[i];
+          scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * ld + j] = sc;
         }
-      } else if constexpr (HI == 2) {
+      }
+    } else if constexpr (HI == 2) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const int qt = tq0 + 2 * g + p;
-          const float sc0 = part[2 * p] + part[2 * p + 1];
-          if (qt < t_end && j < nvq[2 * p]) {
-            const float sc = round_bf16 ? bf16_round(sc0) : sc0;
-            scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * N_cap + j] = sc;
-          }
-        }
-      } else {
-        float sc0 = (part[0] + part[1]) + (part[2] + part[3]);
-        if constexpr (HI >= 8) sc0 += __shfl_xor(sc0, 16, 64);
-        if constexpr (HI >= 16) sc0 += __shfl_xor(sc0, 32, 64);
-        const int qt = tq0 + (4 * g) / HI;
-        const bool writer = (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0;
-        if (writer && qt < t_end && j < nvq[0]) {
+      for (int p = 0; p < 2; ++p) {
+        const int qt = tq0 + 2 * g + p;
+        const float sc0 = part[2 * p] + part[2 * p + 1];
+        if (qt < t_end && j < nvq[2 * p]) {
           const float sc = round_bf16 ? bf16_round(sc0) : sc0;
-          scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * N_cap + j] = sc;
+          scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * ld + j] = sc;
         }
+      }
+    } else {
+      float sc0 = (part[0] + part[1]) + (part[2] + part[3]);
+      if constexpr (HI >= 8) sc0 += __shfl_xor(sc0, 16, 64);
+      if constexpr (HI >= 16) sc0 += __shfl_xor(sc0, 32, 64);
+      const int qt = tq0 + (4 * g) / HI;
+      const bool writer = (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0;
+      if (writer && qt < t_end && j < nvq[0]) {
+        const float sc = round_bf16 ? bf16_round(sc0) : sc0;
+        scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * ld + j] = sc;
       }
     }
   }
@@ -133,8 +132,8 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kScoreThreads) void index_score_f32_kernel(
     const float* __restrict__ qI, const float* __restrict__ w, const float* __restrict__ kI,
-    float* __restrict__ scores, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, int m,
-    int HI, int DI, bool round_bf16) {
+    float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
+    int m, int HI, int DI, bool round_bf16) {
   extern __shared__ float qs[];                 // [HI * DI + HI]
   const int b = blockIdx.z, tl = blockIdx.y, t = t_off + tl;
   int64_t nv = n_visible(q_pos0 + t, m);
@@ -155,16 +154,20 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_f32_kernel(
     sc += qs[HI * DI + h] * fmaxf(dot, 0.f);
   }
   if (round_bf16) sc = bf16_round(sc);
-  scores[(static_cast<int64_t>(b) * Tc + tl) * N_cap + j] = sc;
+  scores[(static_cast<int64_t>(b) * Tc + tl) * ld + j] = sc;
 }
 
 // ---------------------------------------------------------------------------
 // Radix select + ordered compaction
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
+constexpr int kSelItems = 32;                   // scores per thread per round
+constexpr int kRound = kSelThreads * kSelItems; // scores per round (registers)
 constexpr int kMaxBins = 4096;
 
 // Order-preserving key: larger score -> larger unsigned key; -0 folds into +0.
+// Key 0 never comes from a real number (it would be a NaN pattern), so it
+// marks "no element" below.
 __device__ __forceinline__ uint32_t score_key(float v, bool key16) {
   if (v == 0.f) v = 0.f;
   const uint32_t u = __float_as_uint(v);
@@ -195,9 +198,31 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   return before + x - v;
 }
 
+// Thread `tid` of round r owns the contiguous indices r*kRound + tid*kSelItems + j.
+__device__ __forceinline__ void load_round(const float* __restrict__ s, int64_t n, int64_t base,
+                                           bool key16, uint32_t (&key)[kSelItems]) {
+  const int64_t i0 = base + static_cast<int64_t>(threadIdx.x) * kSelItems;
+  if (i0 + kSelItems <= n) {
+    float4 v[kSelItems / 4];
+#pragma unroll
+    for (int q = 0; q < kSelItems / 4; ++q) v[q] = *reinterpret_cast<const float4*>(s + i0 + 4 * q);
+#pragma unroll
+    for (int q = 0; q < kSelItems / 4; ++q) {
+      key[4 * q + 0] = score_key(v[q].x, key16);
+      key[4 * q + 1] = score_key(v[q].y, key16);
+      key[4 * q + 2] = score_key(v[q].z, key16);
+      key[4 * q + 3] = score_key(v[q].w, key16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) key[j] = i0 + j < n ? score_key(s[i0 + j], key16) : 0u;
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
-    const float* __restrict__ scores, int64_t N_cap, int Tq, int t_off, int Tc, int64_t q_pos0,
-    int m, int k, bool key16, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+    const float* __restrict__ scores, int64_t ld, int64_t N_cap, int Tq, int t_off, int Tc,
+    int64_t q_pos0, int m, int k, bool key16, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
   __shared__ uint32_t hist[kMaxBins];
   __shared__ uint32_t wsum[kSelThreads / 64];
   __shared__ uint32_t sh_digit, sh_krem;
@@ -205,7 +230,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const int b = blockIdx.y, tl = blockIdx.x, t = t_off + tl;
   int64_t n = n_visible(q_pos0 + t, m);
   if (n > N_cap) n = N_cap;
-  const float* s = scores + (static_cast<int64_t>(b) * Tc + tl) * N_cap;
+  const float* s = scores + (static_cast<int64_t>(b) * Tc + tl) * ld;
   int32_t* io = idx_out + (static_cast<int64_t>(b) * Tq + t) * k;
   float* so = score_out ? score_out + (static_cast<int64_t>(b) * Tq + t) * k : nullptr;
 
@@ -217,22 +242,26 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     return;
   }
 
-  // MSB-first digits: 32-bit keys 12/10/10, 16-bit keys 10/6
+  const int rounds = static_cast<int>((n + kRound - 1) / kRound);
+  uint32_t key[kSelItems];
+  if (rounds == 1) load_round(s, n, 0, key16, key);     // kept in registers for every pass
+
+  // MSB-first digits: 32-bit keys 12/10/10, 16-bit keys 12/4
   const int nd = key16 ? 2 : 3;
-  const int widths32[3] = {12, 10, 10};
-  const int widths16[3] = {10, 6, 0};
   uint32_t prefix = 0, pmask = 0;
   uint32_t krem = static_cast<uint32_t>(k);
   int shift = key16 ? 16 : 32;
   for (int p = 0; p < nd; ++p) {
-    const int wd = key16 ? widths16[p] : widths32[p];
+    const int wd = key16 ? (p == 0 ? 12 : 4) : (p == 0 ? 12 : 10);
     shift -= wd;
     const int nb = 1 << wd;
     for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kSelThreads) {
-      const uint32_t key = score_key(s[i], key16);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
+    for (int r = 0; r < rounds; ++r) {
+      if (rounds > 1) load_round(s, n, static_cast<int64_t>(r) * kRound, key16, key);
+#pragma unroll
+      for (int j = 0; j < kSelItems; ++j)
+        if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
     // bins in descending digit order: thread owns 4 consecutive of them
@@ -244,7 +273,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       tsum += c[q];
     }
     uint32_t total;
-    uint32_t before = block_excl_scan(tsum, wsum, &total);
+    const uint32_t before = block_excl_scan(tsum, wsum, &total);
     if (before < krem && before + tsum >= krem) {
       uint32_t cum = before;
 #pragma unroll
@@ -264,49 +293,58 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
   const uint32_t thr = prefix;       // key of the k-th largest score
 
-  // ordered compaction: contiguous index ranges per thread
-  const int64_t chunk = (n + kSelThreads - 1) / kSelThreads;
-  const int64_t i0 = tid * chunk, i1 = min(n, i0 + chunk);
-  uint32_t gt = 0, eq = 0;
-  for (int64_t i = i0; i < i1; ++i) {
-    const uint32_t key = score_key(s[i], key16);
-    gt += key > thr;
-    eq += key == thr;
-  }
-  uint32_t tot;
-  const uint32_t gt_pre = block_excl_scan(gt, wsum, &tot);
-  const uint32_t eq_pre = block_excl_scan(eq, wsum, &tot);
-  uint32_t pos = gt_pre + min(eq_pre, krem);
-  uint32_t eq_rank = eq_pre;
-  for (int64_t i = i0; i < i1; ++i) {
-    const float v = s[i];
-    const uint32_t key = score_key(v, key16);
-    bool take = key > thr;
-    if (key == thr) { take = eq_rank < krem; ++eq_rank; }
-    if (take) {
-      io[pos] = static_cast<int32_t>(i);
-      if (so) so[pos] = v;
-      ++pos;
+  // ordered compaction, round by round: positions follow increasing index
+  uint32_t run_gt = 0, run_eq = 0;
+  for (int r = 0; r < rounds; ++r) {
+    const int64_t base = static_cast<int64_t>(r) * kRound;
+    if (rounds > 1) load_round(s, n, base, key16, key);
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+      gt += key[j] > thr;
+      eq += key[j] == thr;
     }
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan((gt << 16) | eq, wsum, &tot);  // both < 2^16 per round
+    const uint32_t gt_pre = run_gt + (pre >> 16), eq_pre = run_eq + (pre & 0xffffu);
+    uint32_t pos = gt_pre + min(eq_pre, krem);
+    uint32_t eq_rank = eq_pre;
+    const int64_t i0 = base + static_cast<int64_t>(tid) * kSelItems;
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+      bool take = key[j] > thr;
+      if (key[j] == thr) { take = eq_rank < krem; ++eq_rank; }
+      if (take) {
+        io[pos] = static_cast<int32_t>(i0 + j);
+        if (so) so[pos] = s[i0 + j];
+        ++pos;
+      }
+    }
+    run_gt += tot >> 16;
+    run_eq += tot & 0xffffu;
   }
 }
 
 template <int HI>
-void launch_score_bf16_hi(hipStream_t s, const IndexArgs& a, float* sc, int t_off, int Tc, dim3 grid) {
+void launch_score_bf16_hi(hipStream_t s, const IndexArgs& a, float* sc, int64_t ld, int t_off, int Tc,
+                          dim3 grid) {
   const bool rb = (a.flags & LCA_SCORE_BF16) != 0;
   const uint16_t* q = static_cast<const uint16_t*>(a.qI);
   const uint16_t* k = static_cast<const uint16_t*>(a.kI);
   switch (a.d_I) {
-    case 64: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 64>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
-    case 128: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 128>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
-    case 256: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 256>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
-    default: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 32>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    case 64: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 64>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    case 128: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 128>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    case 256: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 256>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    default: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 32>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
   }
 }
 
+// row stride of the score buffer: 64-element aligned for vector loads
+int64_t score_ld(const IndexArgs& a) { return (a.N_cap + 63) / 64 * 64; }
+
 // queries per chunk so that the score buffer stays under a fixed budget
 int query_chunk(const IndexArgs& a) {
-  const int64_t per_q = static_cast<int64_t>(a.B) * a.N_cap * 4;
+  const int64_t per_q = static_cast<int64_t>(a.B) * score_ld(a) * 4;
   const int64_t budget = int64_t(512) << 20;
   int64_t tc = per_q > 0 ? budget / per_q : a.Tq;
   if (tc < 1) tc = 1;
@@ -318,12 +356,13 @@ int query_chunk(const IndexArgs& a) {
 }  // namespace
 
 size_t index_topk_workspace(const IndexArgs& a) {
-  return static_cast<size_t>(a.B) * query_chunk(a) * a.N_cap * sizeof(float) + 256;
+  return static_cast<size_t>(a.B) * query_chunk(a) * score_ld(a) * sizeof(float) + 256;
 }
 
 hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t) {
   float* sc = static_cast<float*>(ws);
   const int Tc = query_chunk(a);
+  const int64_t ld = score_ld(a);
   const bool key16 = (a.flags & LCA_SCORE_BF16) != 0;
   for (int t_off = 0; t_off < a.Tq; t_off += Tc) {
     const int tcn = min(Tc, a.Tq - t_off);
@@ -335,17 +374,17 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
         dim3 grid((nv_max + kScoreThreads - 1) / kScoreThreads, tcn, a.B);
         hipLaunchKernelGGL(index_score_f32_kernel, grid, dim3(kScoreThreads),
                            (a.H_I * a.d_I + a.H_I) * sizeof(float), s,
-                           static_cast<const float*>(a.qI), a.w, static_cast<const float*>(a.kI), sc,
+                           static_cast<const float*>(a.qI), a.w, static_cast<const float*>(a.kI), sc, ld,
                            a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, a.H_I, a.d_I, key16);
       } else {
         const int QPB = 16 / a.H_I;
         dim3 grid((nv_max + kKeysPerWG - 1) / kKeysPerWG, (tcn + QPB - 1) / QPB, a.B);
         switch (a.H_I) {
-          case 1: launch_score_bf16_hi<1>(s, a, sc, t_off, Tc, grid); break;
-          case 2: launch_score_bf16_hi<2>(s, a, sc, t_off, Tc, grid); break;
-          case 4: launch_score_bf16_hi<4>(s, a, sc, t_off, Tc, grid); break;
-          case 8: launch_score_bf16_hi<8>(s, a, sc, t_off, Tc, grid); break;
-          default: launch_score_bf16_hi<16>(s, a, sc, t_off, Tc, grid); break;
+          case 1: launch_score_bf16_hi<1>(s, a, sc, ld, t_off, Tc, grid); break;
+          case 2: launch_score_bf16_hi<2>(s, a, sc, ld, t_off, Tc, grid); break;
+          case 4: launch_score_bf16_hi<4>(s, a, sc, ld, t_off, Tc, grid); break;
+          case 8: launch_score_bf16_hi<8>(s, a, sc, ld, t_off, Tc, grid); break;
+          default: launch_score_bf16_hi<16>(s, a, sc, ld, t_off, Tc, grid); break;
         }
       }
       hipError_t e = hipGetLastError();
@@ -353,7 +392,7 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
     }
     {
       LaunchScope scope(s, "topk_select");
-      hipLaunchKernelGGL(topk_select_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, s, sc, a.N_cap,
+      hipLaunchKernelGGL(topk_select_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, s, sc, ld, a.N_cap,
                          a.Tq, t_off, Tc, a.q_pos0, a.m, a.k, key16, a.idx_out, a.score_out);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

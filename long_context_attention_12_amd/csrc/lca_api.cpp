@@ -262,6 +262,10 @@ static int check_attend(const lca::AttendArgs& a, const char* fn) {
   if (!a.sparse) {
     const int64_t nv_last = (a.q_pos0 + a.Tq) / a.m;
     if (a.N_cap < nv_last) return fail(LCA_ERR_ARG, "%s: N_cap (%lld) < visible entries of the last query (%lld)", fn, (long long)a.N_cap, (long long)nv_last);
+    // a query's rows are cut into at most 256 splits of at most 2048 rows
+    if (nv_last + a.W > 256LL * 2048)
+      return fail(LCA_ERR_UNSUPPORTED, "%s: %lld visible entries + W exceed the 524288 rows one query can attend", fn,
+                  (long long)nv_last);
   }
   if (!aligned16(a.q) || !aligned16(a.kv) || !aligned16(a.win) || !aligned16(a.out) || !aligned4(a.idx) ||
       !aligned4(a.sink) || !aligned4(a.lse_out) || !aligned4(a.kv_scale) || !aligned4(a.win_scale))

@@ -115,6 +115,10 @@ def test_attend_validation(lib):
     h = lib.hca_attend(None, 1, 1, 2, 1, 64, 512, 100, 128, 128, 1048576, fake, fake, None, fake, None,
                        fake, 0.04, 0, 10000.0, 0, fake, None, fake, 1 << 30)
     _expect(h, -1, "N_cap")
+    # dense rows per query beyond 256 splits x 2048 rows
+    h = lib.hca_attend(None, 1, 1, 1, 1, 64, 512, 1 << 20, 128, 128, 128 << 19, fake, fake, None, fake, None,
+                       fake, 0.04, 0, 10000.0, 0, fake, None, fake, 1 << 40)
+    _expect(h, -2, "524288")
 
 
 def test_quantize_validation(lib):
