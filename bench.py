@@ -13,6 +13,8 @@ Also measured (secondary, same line): HCA decode, V4-Pro shaped: batch 8,
 1048576 context tokens (8192 entries), 128 heads.
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Counter runs: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) over
+``bench.py --copy-calibration 1024``, then ``bench.py --pmc-summary F.csv W.csv``.
 """
 
 from __future__ import annotations
@@ -35,6 +37,7 @@ import long_context_attention_12_amd as L  # noqa: E402
 import workloads as WL  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+COPY_REPS = 3                  # calibration copies per counter run
 DEV = "cuda"
 
 
@@ -149,6 +152,68 @@ def load_traffic(kernel, workload, src_hash):
     return rec.get("hbm_bytes_per_launch")
 
 
+def copy_calibration(mib, reps=COPY_REPS):
+    """Plain device-to-device copies of a known size, for scaling the HBM byte
+    counters (FETCH_SIZE, WRITE_SIZE) that rocprofv3 reports per dispatch."""
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=DEV)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
+
+
+def _read_counter_csv(path, counter):
+    """(dispatch id, kernel name, grid size, value in KiB) of every dispatch in a
+    rocprofv3 counter_collection.csv, for one counter, in dispatch order."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                rows.append((int(row["Dispatch_Id"]), row["Kernel_Name"], int(row["Grid_Size"]),
+                             float(row["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def pmc_summary(fetch_csv, write_csv, copy_mib, out_json):
+    """Turn two rocprofv3 --pmc runs of ``bench.py --copy-calibration MIB`` (one
+    with FETCH_SIZE, one with WRITE_SIZE) into HBM bytes per launch of the index
+    scoring kernel. Each counter is scaled by what it reads for the plain copy of
+    known size: the last COPY_REPS copy dispatches of the run."""
+    n = copy_mib << 20
+
+    def stats(path, counter):
+        rows = _read_counter_csv(path, counter)
+        copies = [r for r in rows if "copyBuffer" in r[1]][-COPY_REPS:]
+        score = [r for r in rows if "index_score" in r[1]]
+        if len(copies) < COPY_REPS or not score:
+            raise SystemExit(f"{path}: calibration copies or index_score dispatches missing")
+        c = sum(r[3] for r in copies) / len(copies)
+        k = sum(r[3] for r in score) / len(score)
+        return c, k, score[0][1], len(score)
+
+    cf, kf, name, nd = stats(fetch_csv, "FETCH_SIZE")
+    cw, kw, _, _ = stats(write_csv, "WRITE_SIZE")
+    f_scale = n / (cf * 1024.0)
+    w_scale = n / (cw * 1024.0)
+    fb, wb = kf * 1024.0 * f_scale, kw * 1024.0 * w_scale
+    src = source_hash(["long_context_attention_12_amd/csrc/index_topk.hip",
+                       "long_context_attention_12_amd/csrc/lca_device.h"])
+    rec = {"csa_decode_b16_ctx131072": {"index_score": {
+        "source_hash": src, "kernel": name, "dispatches": nd,
+        "fetch_kib_raw": kf, "write_kib_raw": kw, "copy_bytes": n,
+        "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "hbm_read_bytes_per_launch": fb, "hbm_write_bytes_per_launch": wb,
+        "hbm_bytes_per_launch": fb + wb}}}
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def cpu_baseline(d, min_seconds=10.0):
     """The float64 oracle on the host cores, on the same workload: the whole
     batch of sequences (scores, top-k, attention), repeated until at least
@@ -187,7 +252,15 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the run, copy MIB MiB device to device (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/counters.json (no GPU)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_calibration or 1024,
+                    os.path.join(ROOT, "profiles", "counters.json"))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the decode workloads shard by sequence with no exchange). Run with --gpus 1.",
@@ -248,6 +321,8 @@ def main():
             "hca_attend_TFLOPs": hf / (att * 1e-6) / 1e12, "mfma_bf16_frac": hf / (att * 1e-6) / 2.5e15,
             "algorithmic_bytes": hb, "flops": hf,
         }
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(result), flush=True)

@@ -961,16 +961,16 @@ SplitPlan make_plan(const AttendArgs& a) {
 }
 
 template <int D>
-void launch_mfma_d(hipStream_t s, const AttendArgs& a, const SplitPlan& sp, float* po, float* pml) {
+void launch_mfma_d(LaunchScope& sc, const AttendArgs& a, const SplitPlan& sp, float* po, float* pml) {
   int nblk = sp.S * sp.n_hg;
   if (sp.n_hg == 2) nblk = ((sp.S + 7) / 8) * 16;     // XCD-paired id layout
   dim3 grid(nblk, a.Tq, a.B), block(kAttThreads);
   if (a.dt_kv == LCA_KV_MIXED)
-    hipLaunchKernelGGL((attend_mfma_kernel<D, true>), grid, block, 0, s, a, sp, po, pml);
+    sc.launch(attend_mfma_kernel<D, true>, grid, block, 0, a, sp, po, pml);
   else if constexpr (D == 512)
-    hipLaunchKernelGGL(attend_dma_kernel, grid, block, 0, s, a, sp, po, pml);
+    sc.launch(attend_dma_kernel, grid, block, 0, a, sp, po, pml);
   else
-    hipLaunchKernelGGL((attend_mfma_kernel<D, false>), grid, block, 0, s, a, sp, po, pml);
+    sc.launch(attend_mfma_kernel<D, false>, grid, block, 0, a, sp, po, pml);
 }
 
 }  // namespace
@@ -991,14 +991,14 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
     if (a.dt_kv == LCA_F32) {
       const size_t smem = (static_cast<size_t>(kTileRows) * a.D + static_cast<size_t>(sp.HG) * a.D +
                            kTileRows * sp.HG + 3 * sp.HG) * sizeof(float);
-      hipLaunchKernelGGL(attend_f32_kernel, dim3(sp.S * sp.n_hg, a.Tq, a.B), dim3(kF32Threads), smem, s,
-                         a, sp, po, pml);
+      scope.launch(attend_f32_kernel, dim3(sp.S * sp.n_hg, a.Tq, a.B), dim3(kF32Threads),
+                   static_cast<uint32_t>(smem), a, sp, po, pml);
     } else {
       switch (a.D) {
-        case 64: launch_mfma_d<64>(s, a, sp, po, pml); break;
-        case 128: launch_mfma_d<128>(s, a, sp, po, pml); break;
-        case 256: launch_mfma_d<256>(s, a, sp, po, pml); break;
-        default: launch_mfma_d<512>(s, a, sp, po, pml); break;
+        case 64: launch_mfma_d<64>(scope, a, sp, po, pml); break;
+        case 128: launch_mfma_d<128>(scope, a, sp, po, pml); break;
+        case 256: launch_mfma_d<256>(scope, a, sp, po, pml); break;
+        default: launch_mfma_d<512>(scope, a, sp, po, pml); break;
       }
     }
     hipError_t e = hipGetLastError();
@@ -1006,8 +1006,8 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
   }
   {
     LaunchScope scope(s, "attend_combine");
-    hipLaunchKernelGGL(combine_kernel, dim3(a.H, a.Tq, a.B), dim3(a.D / 2 > 64 ? a.D / 2 : 64), 0, s, a, sp.S,
-                       sp.RS, po, pml);
+    scope.launch(combine_kernel, dim3(a.H, a.Tq, a.B), dim3(a.D / 2 > 64 ? a.D / 2 : 64), 0, a, sp.S, sp.RS,
+                 static_cast<const float*>(po), static_cast<const float*>(pml));
     return hipGetLastError();
   }
 }

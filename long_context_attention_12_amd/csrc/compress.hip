@@ -176,9 +176,9 @@ hipError_t launch_compress(hipStream_t s, const CompressArgs& a) {
   LaunchScope scope(s, "compress");
   dim3 grid(n_out, a.B);
   if (a.dt_in == LCA_F32)
-    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(kThreads), 0, s, a);
+    scope.launch(compress_kernel<float>, grid, dim3(kThreads), 0, a);
   else
-    hipLaunchKernelGGL(compress_kernel<uint16_t>, grid, dim3(kThreads), 0, s, a);
+    scope.launch(compress_kernel<uint16_t>, grid, dim3(kThreads), 0, a);
   return hipGetLastError();
 }
 
@@ -194,7 +194,7 @@ hipError_t launch_quantize_rows(hipStream_t s, int dt_out, int64_t n_rows, int D
     const int64_t gy = left / gx;
     if (gy > 0) {
       const int64_t gyc = gy < 65535 ? gy : 65535;
-      hipLaunchKernelGGL(quantize_rows_kernel, dim3(gx, gyc), dim3(kThreads), 0, s, dt_out, D,
+      scope.launch(quantize_rows_kernel, dim3(gx, gyc), dim3(kThreads), 0, dt_out, D,
                          rope_dims, src + off * D,
                          dt_out == LCA_KV_MIXED ? static_cast<void*>(static_cast<uint8_t*>(out) + off * (D + rope_dims))
                                                 : static_cast<void*>(static_cast<uint8_t*>(out) + off * (D / 2)),
@@ -202,7 +202,7 @@ hipError_t launch_quantize_rows(hipStream_t s, int dt_out, int64_t n_rows, int D
                                                 : static_cast<void*>(static_cast<uint8_t*>(out_scale) + off * (D / 32)));
       off += gx * gyc;
     } else {
-      hipLaunchKernelGGL(quantize_rows_kernel, dim3(left, 1), dim3(kThreads), 0, s, dt_out, D,
+      scope.launch(quantize_rows_kernel, dim3(left, 1), dim3(kThreads), 0, dt_out, D,
                          rope_dims, src + off * D,
                          dt_out == LCA_KV_MIXED ? static_cast<void*>(static_cast<uint8_t*>(out) + off * (D + rope_dims))
                                                 : static_cast<void*>(static_cast<uint8_t*>(out) + off * (D / 2)),

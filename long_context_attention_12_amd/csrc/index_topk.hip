@@ -326,16 +326,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
 }
 
 template <int HI>
-void launch_score_bf16_hi(hipStream_t s, const IndexArgs& a, float* sc, int64_t ld, int t_off, int Tc,
+void launch_score_bf16_hi(LaunchScope& ls, const IndexArgs& a, float* sc, int64_t ld, int t_off, int Tc,
                           dim3 grid) {
   const bool rb = (a.flags & LCA_SCORE_BF16) != 0;
   const uint16_t* q = static_cast<const uint16_t*>(a.qI);
   const uint16_t* k = static_cast<const uint16_t*>(a.kI);
   switch (a.d_I) {
-    case 64: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 64>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
-    case 128: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 128>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
-    case 256: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 256>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
-    default: hipLaunchKernelGGL((index_score_bf16_kernel<HI, 32>), grid, dim3(kScoreThreads), 0, s, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    case 64: ls.launch(index_score_bf16_kernel<HI, 64>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    case 128: ls.launch(index_score_bf16_kernel<HI, 128>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    case 256: ls.launch(index_score_bf16_kernel<HI, 256>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    default: ls.launch(index_score_bf16_kernel<HI, 32>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
   }
 }
 
@@ -372,19 +372,19 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
       LaunchScope scope(s, "index_score");
       if (a.dt == LCA_F32) {
         dim3 grid((nv_max + kScoreThreads - 1) / kScoreThreads, tcn, a.B);
-        hipLaunchKernelGGL(index_score_f32_kernel, grid, dim3(kScoreThreads),
-                           (a.H_I * a.d_I + a.H_I) * sizeof(float), s,
+        scope.launch(index_score_f32_kernel, grid, dim3(kScoreThreads),
+                     static_cast<uint32_t>((a.H_I * a.d_I + a.H_I) * sizeof(float)),
                            static_cast<const float*>(a.qI), a.w, static_cast<const float*>(a.kI), sc, ld,
                            a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, a.H_I, a.d_I, key16);
       } else {
         const int QPB = 16 / a.H_I;
         dim3 grid((nv_max + kKeysPerWG - 1) / kKeysPerWG, (tcn + QPB - 1) / QPB, a.B);
         switch (a.H_I) {
-          case 1: launch_score_bf16_hi<1>(s, a, sc, ld, t_off, Tc, grid); break;
-          case 2: launch_score_bf16_hi<2>(s, a, sc, ld, t_off, Tc, grid); break;
-          case 4: launch_score_bf16_hi<4>(s, a, sc, ld, t_off, Tc, grid); break;
-          case 8: launch_score_bf16_hi<8>(s, a, sc, ld, t_off, Tc, grid); break;
-          default: launch_score_bf16_hi<16>(s, a, sc, ld, t_off, Tc, grid); break;
+          case 1: launch_score_bf16_hi<1>(scope, a, sc, ld, t_off, Tc, grid); break;
+          case 2: launch_score_bf16_hi<2>(scope, a, sc, ld, t_off, Tc, grid); break;
+          case 4: launch_score_bf16_hi<4>(scope, a, sc, ld, t_off, Tc, grid); break;
+          case 8: launch_score_bf16_hi<8>(scope, a, sc, ld, t_off, Tc, grid); break;
+          default: launch_score_bf16_hi<16>(scope, a, sc, ld, t_off, Tc, grid); break;
         }
       }
       hipError_t e = hipGetLastError();
@@ -392,7 +392,7 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
     }
     {
       LaunchScope scope(s, "topk_select");
-      hipLaunchKernelGGL(topk_select_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, s, sc, ld, a.N_cap,
+      scope.launch(topk_select_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, static_cast<const float*>(sc), ld, a.N_cap,
                          a.Tq, t_off, Tc, a.q_pos0, a.m, a.k, key16, a.idx_out, a.score_out);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;

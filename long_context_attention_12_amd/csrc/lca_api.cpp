@@ -46,23 +46,23 @@ std::vector<ProfRec> g_prof;
 
 namespace lca {
 
-LaunchScope::LaunchScope(hipStream_t s, const char* n) : stream(s), name(n), active(false), slot(-1) {
+LaunchScope::LaunchScope(hipStream_t s, const char* n)
+    : stream(s), name(n), active(false), launched(false), ev_start(nullptr), ev_stop(nullptr) {
   if (!g_prof_on) return;
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  ProfRec r;
-  r.name = n;
-  if (hipEventCreate(&r.start) != hipSuccess) return;
-  if (hipEventCreate(&r.stop) != hipSuccess) { (void)hipEventDestroy(r.start); return; }
-  (void)hipEventRecord(r.start, s);
-  g_prof.push_back(r);
-  slot = static_cast<int>(g_prof.size()) - 1;
+  if (hipEventCreate(&ev_start) != hipSuccess) return;
+  if (hipEventCreate(&ev_stop) != hipSuccess) { (void)hipEventDestroy(ev_start); return; }
   active = true;
 }
 
 LaunchScope::~LaunchScope() {
   if (!active) return;
+  if (!launched) {                       // nothing ran: nothing to time
+    (void)hipEventDestroy(ev_start);
+    (void)hipEventDestroy(ev_stop);
+    return;
+  }
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  (void)hipEventRecord(g_prof[slot].stop, stream);
+  g_prof.push_back(ProfRec{name, ev_start, ev_stop});
 }
 
 }  // namespace lca

@@ -3,19 +3,35 @@
 // already been validated; they only compute grids and enqueue kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace lca {
 
 // Kernel-launch bracket used by the optional timing mode (lca_profile_*).
+// Launches one named step's kernels on `stream`. While kernel timing is on
+// (lca_profile_enable), the launches go through hipExtLaunchKernel with a
+// start event on the first kernel and a stop event on each, so the recorded
+// time runs from the first kernel's start to the last kernel's end and holds
+// no launch or event overhead.
 struct LaunchScope {
   LaunchScope(hipStream_t s, const char* name);
   ~LaunchScope();
+  template <typename F, typename... Args>
+  void launch(F kernel, dim3 grid, dim3 block, uint32_t shmem, Args... args) {
+    if (active) {
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, launched ? nullptr : ev_start, ev_stop, 0, args...);
+      launched = true;
+    } else {
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
+    }
+  }
   hipStream_t stream;
   const char* name;
   bool active;
-  int slot;
+  bool launched;
+  hipEvent_t ev_start, ev_stop;
 };
 
 struct CompressArgs {
