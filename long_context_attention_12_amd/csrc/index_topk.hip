@@ -31,6 +31,46 @@ constexpr int kScoreThreads = 256;
 constexpr int kKeysPerWave = 64;   // 4 MFMA key groups, all loads issued together
 constexpr int kKeysPerWG = 4 * kKeysPerWave;
 
+// An MFMA reads its operands only from lanes enabled in EXEC. Its result here
+// feeds lane-conditional stores, and the compiler may otherwise sink the MFMA
+// into that divergent branch; the empty asm makes the accumulator live at a
+// point every lane reaches, so the MFMA runs with the full wave.
+__device__ __forceinline__ void pin_uniform(f32x4& acc) { asm volatile("" : "+v"(acc)); }
+
+// Scores of key j from one 16 x 16 MFMA tile: accumulator row 4g + i is the
+// dot of (query tq0 + (4g+i) / HI, head (4g+i) % HI) with key j. ReLU, the
+// head weights and the head sum are folded here, in the same order for every
+// operand type: ((p0 + p1) + (p2 + p3)), then across lane groups for HI >= 8.
+template <int HI>
+__device__ __forceinline__ void emit_scores(const f32x4& acc, const float (&wv)[4], const int64_t (&nvq)[4], int g,
+                                            int tq0, int t_off, int t_end, int64_t j, float* srow, int64_t ld,
+                                            bool round_bf16) {
+  float part[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[i] = wv[i] * fmaxf(acc[i], 0.f);
+  if constexpr (HI == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qt = tq0 + 4 * g + i;
+      if (qt < t_end && j < nvq[i]) srow[(qt - t_off) * ld + j] = round_bf16 ? bf16_round(part[i]) : part[i];
+    }
+  } else if constexpr (HI == 2) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int qt = tq0 + 2 * g + p;
+      const float sc = part[2 * p] + part[2 * p + 1];
+      if (qt < t_end && j < nvq[2 * p]) srow[(qt - t_off) * ld + j] = round_bf16 ? bf16_round(sc) : sc;
+    }
+  } else {
+    float sc = (part[0] + part[1]) + (part[2] + part[3]);
+    if constexpr (HI >= 8) sc += __shfl_xor(sc, 16, 64);
+    if constexpr (HI >= 16) sc += __shfl_xor(sc, 32, 64);
+    const int qt = tq0 + (4 * g) / HI;
+    const bool writer = (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0;
+    if (writer && qt < t_end && j < nvq[0]) srow[(qt - t_off) * ld + j] = round_bf16 ? bf16_round(sc) : sc;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 scoring with MFMA 16x16x32 (A = 16 indexer query-head rows, B = 16 keys)
 // ---------------------------------------------------------------------------
@@ -89,41 +129,84 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], __builtin_bit_cast(bf16x8, kv[u][s]), acc, 0, 0, 0);
-    const int64_t j = key0 + 16 * u + r16;
-    // acc[i] = qI(row 4g+i) . kI(j); fold ReLU and head weights per query
-    float part[4];
+    pin_uniform(acc);
+    emit_scores<HI>(acc, wv, nvq, g, tq0, t_off, t_end, key0 + 16 * u + r16,
+                    scores + static_cast<int64_t>(b) * Tc * ld, ld, round_bf16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 scoring (d_I = 128) with the scaled MFMA 16x16x128 (f8f6f4, e2m1
+// operands): lane l holds row / key l % 16 and the 32-element block l / 16 of
+// it (16 packed bytes, low nibble first) together with that block's E8M0
+// scale, so one MFMA forms the whole 128-channel dot of 16 query-head rows with
+// 16 keys, each block scaled by 2^(e_q - 127) * 2^(e_k - 127). Products of
+// e2m1 values and power-of-two scales are exact; the MFMA accumulates in fp32.
+// A key costs 64 + 4 bytes; a wave keeps 256 keys (17 KiB) in flight.
+// ---------------------------------------------------------------------------
+constexpr int kFp4KeysPerWave = 256;
+constexpr int kFp4KeysPerWG = 4 * kFp4KeysPerWave;
+
+template <int HI>
+__global__ __launch_bounds__(kScoreThreads) void index_score_fp4_kernel(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, float* __restrict__ scores, int64_t ld,
+    int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, int m, bool round_bf16) {
+  constexpr int QPB = 16 / HI;
+  constexpr int UNR = kFp4KeysPerWave / 16;
+  constexpr int ROW = 64;                          // packed bytes per 128-channel row
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int b = blockIdx.z;
+  const int tq0 = t_off + blockIdx.y * QPB;
+  const int t_end = min(Tq, t_off + Tc);
+  const int tq_last = min(tq0 + QPB, t_end) - 1;
+  int64_t nv_max = n_visible(q_pos0 + tq_last, m);
+  if (nv_max > N_cap) nv_max = N_cap;
+  const int64_t key0 = static_cast<int64_t>(blockIdx.x) * kFp4KeysPerWG + wid * kFp4KeysPerWave;
+  if (key0 >= nv_max) return;
+
+  const uint8_t* kb = kI + static_cast<int64_t>(b) * N_cap * ROW;
+  const uint32_t* ksb = reinterpret_cast<const uint32_t*>(kI_scale) + static_cast<int64_t>(b) * N_cap;
+  uint4 kc[UNR];
+  uint32_t ks[UNR];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[i] = wv[i] * fmaxf(acc[i], 0.f);
-    if constexpr (HI == 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qt = tq0 + 4 * g + i;
-        if (qt < t_end && j < nvq[i]) {
-          const float sc = round_bf16 ? bf16_round(part[i]) : part[i];
-          scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * ld + j] = sc;
-        }
-      }
-    } else if constexpr (HI == 2) {
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int qt = tq0 + 2 * g + p;
-        const float sc0 = part[2 * p] + part[2 * p + 1];
-        if (qt < t_end && j < nvq[2 * p]) {
-          const float sc = round_bf16 ? bf16_round(sc0) : sc0;
-          scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * ld + j] = sc;
-        }
-      }
-    } else {
-      float sc0 = (part[0] + part[1]) + (part[2] + part[3]);
-      if constexpr (HI >= 8) sc0 += __shfl_xor(sc0, 16, 64);
-      if constexpr (HI >= 16) sc0 += __shfl_xor(sc0, 32, 64);
-      const int qt = tq0 + (4 * g) / HI;
-      const bool writer = (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0;
-      if (writer && qt < t_end && j < nvq[0]) {
-        const float sc = round_bf16 ? bf16_round(sc0) : sc0;
-        scores[(static_cast<int64_t>(b) * Tc + (qt - t_off)) * ld + j] = sc;
-      }
+  for (int u = 0; u < UNR; ++u) {
+    int64_t j = key0 + 16 * u + r16;
+    if (j >= nv_max) j = nv_max - 1;               // stay in bounds; result discarded
+    kc[u] = *reinterpret_cast<const uint4*>(kb + j * ROW + 16 * g);
+    ks[u] = ksb[j];                                 // the key's four block scales
+  }
+  uint4 qa = make_uint4(0, 0, 0, 0);
+  int qs = 0;
+  {
+    const int qt = tq0 + r16 / HI, h = r16 % HI;
+    if (qt < t_end) {
+      const int64_t qrow = (static_cast<int64_t>(b) * Tq + qt) * HI + h;
+      qa = *reinterpret_cast<const uint4*>(qI + qrow * ROW + 16 * g);
+      qs = qI_scale[qrow * 4 + g];
     }
+  }
+  float wv[4];
+  int64_t nvq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * g + i, qt = tq0 + row / HI, h = row % HI;
+    wv[i] = qt < t_end ? w[(static_cast<int64_t>(b) * Tq + qt) * HI + h] : 0.f;
+    nvq[i] = qt < t_end ? n_visible(q_pos0 + qt, m) : 0;
+  }
+  const i32x8 A = {static_cast<int>(qa.x), static_cast<int>(qa.y), static_cast<int>(qa.z), static_cast<int>(qa.w),
+                   0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const i32x8 Bk = {static_cast<int>(kc[u].x), static_cast<int>(kc[u].y), static_cast<int>(kc[u].z),
+                      static_cast<int>(kc[u].w), 0, 0, 0, 0};
+    const int sb = static_cast<int>((ks[u] >> (8 * g)) & 0xffu);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bk, acc, 4, 4, 0, qs, 0, sb);
+    pin_uniform(acc);
+    emit_scores<HI>(acc, wv, nvq, g, tq0, t_off, t_end, key0 + 16 * u + r16,
+                    scores + static_cast<int64_t>(b) * Tc * ld, ld, round_bf16);
   }
 }
 
@@ -376,6 +459,20 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
                      static_cast<uint32_t>((a.H_I * a.d_I + a.H_I) * sizeof(float)),
                            static_cast<const float*>(a.qI), a.w, static_cast<const float*>(a.kI), sc, ld,
                            a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, a.H_I, a.d_I, key16);
+      } else if (a.dt == LCA_MXFP4) {
+        const int QPB = 16 / a.H_I;
+        dim3 grid((nv_max + kFp4KeysPerWG - 1) / kFp4KeysPerWG, (tcn + QPB - 1) / QPB, a.B);
+        const uint8_t* q = static_cast<const uint8_t*>(a.qI);
+        const uint8_t* qs = static_cast<const uint8_t*>(a.qI_scale);
+        const uint8_t* k = static_cast<const uint8_t*>(a.kI);
+        const uint8_t* ks = static_cast<const uint8_t*>(a.kI_scale);
+        switch (a.H_I) {
+          case 1: scope.launch(index_score_fp4_kernel<1>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
+          case 2: scope.launch(index_score_fp4_kernel<2>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
+          case 4: scope.launch(index_score_fp4_kernel<4>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
+          case 8: scope.launch(index_score_fp4_kernel<8>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
+          default: scope.launch(index_score_fp4_kernel<16>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
+        }
       } else {
         const int QPB = 16 / a.H_I;
         dim3 grid((nv_max + kKeysPerWG - 1) / kKeysPerWG, (tcn + QPB - 1) / QPB, a.B);

@@ -207,7 +207,8 @@ static int check_index(const lca::IndexArgs& a) {
   if (a.N_cap < nv_last) return fail(LCA_ERR_ARG, "csa_index_topk: N_cap (%lld) < visible entries of the last query (%lld)", (long long)a.N_cap, (long long)nv_last);
   if (a.N_cap > 2147483647LL) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: N_cap must fit int32 indices");
   if (!a.qI || !a.w || !a.kI || !a.idx_out) return fail(LCA_ERR_ARG, "csa_index_topk: qI, w, kI and idx_out are required");
-  if (!aligned16(a.qI) || !aligned16(a.kI) || !aligned4(a.w) || !aligned4(a.idx_out) || !aligned4(a.score_out))
+  if (!aligned16(a.qI) || !aligned16(a.kI) || !aligned4(a.w) || !aligned4(a.idx_out) || !aligned4(a.score_out) ||
+      (a.dt == LCA_MXFP4 && !aligned4(a.kI_scale)))
     return fail(LCA_ERR_ALIGN, "csa_index_topk: misaligned buffer");
   return LCA_OK;
 }
@@ -229,7 +230,6 @@ int csa_index_topk(void* stream, int dt, int B, int Tq, int H_I, int d_I, int64_
   const size_t need = lca::index_topk_workspace(a);
   if (!ws || ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "csa_index_topk: workspace %zu < %zu bytes", ws_bytes, need);
   if (!aligned16(ws)) return fail(LCA_ERR_ALIGN, "csa_index_topk: workspace must be 16-byte aligned");
-  if (dt == LCA_MXFP4) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: MXFP4 scoring not built yet");
   return hip_status(lca::launch_index_topk(static_cast<hipStream_t>(stream), a, ws, ws_bytes), "csa_index_topk");
 }
 

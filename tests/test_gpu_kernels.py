@@ -229,6 +229,56 @@ def test_index_topk_f32_from_sequence_start():
                                    atol=1e-6 * max(1.0, float(np.max(np.abs(s))) if nv else 1.0))
 
 
+def _mxfp4_on_gpu(L, x):
+    """Quantise float32 rows [..., 128] to MXFP4 on the GPU (codes checked bit-exact elsewhere)."""
+    flat = x.reshape(-1, x.shape[-1])
+    codes = torch.empty((flat.shape[0], flat.shape[1] // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((flat.shape[0], flat.shape[1] // 32), dtype=torch.uint8, device=DEV)
+    L.lca_quantize_rows(L.MXFP4, dev_f32(flat), codes, scales)
+    return codes.reshape(x.shape[:-1] + (x.shape[-1] // 2,)), scales.reshape(x.shape[:-1] + (x.shape[-1] // 32,))
+
+
+@pytest.mark.parametrize("H_I", [1, 4, 16])
+@pytest.mark.parametrize("bf16_scores", [True, False])
+def test_index_topk_mxfp4(H_I, bf16_scores):
+    # MXFP4 indexer operands (queries and keys), heavy-tailed query norms; the
+    # oracle quantises the same float32 sources itself and scores the decoded values
+    L = need_gpu()
+    rng = np.random.default_rng(50 + H_I)
+    B, Tq, d_I, m, k = 2, 2, 128, 4, 300
+    q_pos0 = 4 * 5000 + 2
+    N_cap = 5003
+    g = rng.standard_normal((B, Tq, H_I, d_I)).astype(np.float32)
+    tau = rng.standard_t(3, size=(B, Tq, H_I, 1)).astype(np.float32)
+    qI = g / np.linalg.norm(g, axis=-1, keepdims=True) * np.abs(tau)
+    kI = (rng.standard_normal((B, N_cap, d_I)) / np.sqrt(d_I)).astype(np.float32)
+    kI[:, ::97] *= 4
+    w = (rng.standard_normal((B, Tq, H_I)) / np.sqrt(H_I)).astype(np.float32)
+    qc, qs = _mxfp4_on_gpu(L, qI)
+    kc, ks = _mxfp4_on_gpu(L, kI)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    say(f"mxfp4 index H_I={H_I} bf16={bf16_scores}")
+    L.csa_index_topk(L.MXFP4, qc, dev_f32(w), kc, idx, m=m, k=k, q_pos0=q_pos0, d_I=d_I, qI_scale=qs,
+                     kI_scale=ks, flags=L.SCORE_BF16 if bf16_scores else 0, score_out=sco)
+    torch.cuda.synchronize()
+    idx_h, sco_h = idx.cpu().numpy(), sco.cpu().numpy()
+    qd = O.mxfp4_decode(*O.mxfp4_quantize(qI))
+    kd = O.mxfp4_decode(*O.mxfp4_quantize(kI))
+    for b in range(B):
+        for t in range(Tq):
+            nv = O.n_visible(q_pos0 + t, m)
+            s = O.index_scores(qd[b, t], w[b, t], kd[b], nv)
+            check_topk_set(idx_h[b, t], s, k, bf16_scores=bf16_scores)
+            sel = idx_h[b, t][idx_h[b, t] >= 0]
+            ref = O.bf16_round(s[sel]) if bf16_scores else s[sel]
+            # bf16 mode: equal unless the fp32 sum sat on a rounding midpoint (one bf16 step)
+            tol = np.abs(ref) * (2.0 ** -7 if bf16_scores else 1e-5) + 1e-6 * np.max(np.abs(s))
+            assert np.all(np.abs(sco_h[b, t][:len(sel)] - ref) <= tol)
+            if bf16_scores:
+                assert np.mean(sco_h[b, t][:len(sel)] == ref) > 0.99
+
+
 def test_index_topk_all_ties_take_lowest_indices():
     L = need_gpu()
     B, Tq, H_I, d_I, m, k = 1, 1, 4, 128, 4, 100
