@@ -86,6 +86,123 @@ def hca_decode_setup(d, copies):
     return step
 
 
+def mixed_pair_setup(B=64, ctx=1048576, H=128, D=512, H_I=4, d_I=128, k=1024, m=4, m2=128, W=128, seed=5):
+    """Mixed-precision CSA + HCA layer pair at decode (B = 64, 1048576 tokens).
+
+    Same recipe as the parity workload (entries, keys and windows N(0,1)/sqrt(dim)
+    in float32, queries with Student-t (3) norms, head weights N(0,1)/sqrt(H_I)),
+    but the 10 GB of sources are drawn on the GPU with torch's seeded generator,
+    one sequence at a time, and quantised by the library (KV_MIXED rows, MXFP4
+    indexer operands) as the path stores them. The small query tensors come from
+    numpy streams default_rng([seed, 2_000_000 + b]).
+    """
+    N, N2 = ctx // m, ctx // m2
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    u8 = dict(dtype=torch.uint8, device=DEV)
+    Eq = torch.empty((B, N, D + 64), **u8)
+    Es = torch.empty((B, N), dtype=torch.float32, device=DEV)
+    kc = torch.empty((B, N, d_I // 2), **u8)
+    ks = torch.empty((B, N, d_I // 32), **u8)
+    Wq = torch.empty((B, W, D + 64), **u8)
+    Ws = torch.empty((B, W), dtype=torch.float32, device=DEV)
+    E2q = torch.empty((B, N2, D + 64), **u8)
+    E2s = torch.empty((B, N2), dtype=torch.float32, device=DEV)
+    W2q = torch.empty((B, W, D + 64), **u8)
+    W2s = torch.empty((B, W), dtype=torch.float32, device=DEV)
+    qc = torch.empty((B, 1, H_I, d_I // 2), **u8)
+    qs = torch.empty((B, 1, H_I, d_I // 32), **u8)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=gen, device=DEV, dtype=torch.float32) / math.sqrt(shape[-1])
+
+    def student_t_rows(r, shape):
+        g = r.standard_normal(size=shape)
+        tau = r.standard_t(3, size=shape[:-1])
+        return (g / np.linalg.norm(g, axis=-1, keepdims=True) * np.abs(tau)[..., None]).astype(np.float32)
+
+    q = np.empty((B, 1, H, D), np.float32)
+    q2 = np.empty((B, 1, H, D), np.float32)
+    qI = np.empty((B, 1, H_I, d_I), np.float32)
+    w = np.empty((B, 1, H_I), np.float32)
+    for b in range(B):
+        L.lca_quantize_rows(L.KV_MIXED, randn(N, D), Eq[b], Es[b])
+        L.lca_quantize_rows(L.MXFP4, randn(N, d_I), kc[b], ks[b])
+        L.lca_quantize_rows(L.KV_MIXED, randn(W, D), Wq[b], Ws[b])
+        L.lca_quantize_rows(L.KV_MIXED, randn(N2, D), E2q[b], E2s[b])
+        L.lca_quantize_rows(L.KV_MIXED, randn(W, D), W2q[b], W2s[b])
+        r = np.random.default_rng([seed, 2_000_000 + b])
+        q[b] = student_t_rows(r, (1, H, D))
+        qI[b] = student_t_rows(r, (1, H_I, d_I))
+        w[b] = r.standard_normal((1, H_I)) / np.sqrt(H_I)
+        q2[b] = student_t_rows(r, (1, H, D))
+    torch.cuda.synchronize()
+    L.lca_quantize_rows(L.MXFP4, _f32(qI), qc, qs)
+    q_t, q2_t, w_t = _bf16(q), _bf16(q2), _f32(w)
+    r = np.random.default_rng([seed, 1_000_000])
+    sink, sink2 = _f32(r.standard_normal(H)), _f32(r.standard_normal(H))
+    ws_i = torch.empty(L.csa_index_topk_workspace(L.MXFP4, B, 1, H_I, d_I, N, m, k, ctx, L.SCORE_BF16), **u8)
+    ws_c = torch.empty(L.csa_attend_workspace(L.BF16, L.KV_MIXED, B, 1, H, D, N, m, k, W, ctx), **u8)
+    ws_h = torch.empty(L.hca_attend_workspace(L.BF16, L.KV_MIXED, B, 1, H, D, N2, m2, W, ctx), **u8)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=DEV)
+    out2 = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=DEV)
+    scale = 1 / math.sqrt(D)
+
+    def step(i):
+        L.csa_index_topk(L.MXFP4, qc, w_t, kc, idx, m=m, k=k, q_pos0=ctx, d_I=d_I, qI_scale=qs, kI_scale=ks,
+                         flags=L.SCORE_BF16, ws=ws_i)
+        L.csa_attend(L.BF16, L.KV_MIXED, q_t, Eq, idx, Wq, sink, out, m=m, W=W, q_pos0=ctx, scale=scale,
+                     kv_scale=Es, win_scale=Ws, flags=L.INV_ROPE, rope_dims=64, ws=ws_c)
+        L.hca_attend(L.BF16, L.KV_MIXED, q2_t, E2q, W2q, sink2, out2, m=m2, W=W, q_pos0=ctx, scale=scale,
+                     kv_scale=E2s, win_scale=W2s, flags=L.INV_ROPE, rope_dims=64, ws=ws_h)
+
+    # algorithmic bytes: every MXFP4 key (64 B + 4 B scales), the selected and
+    # window mixed rows (576 B + 4 B scale), every HCA mixed row, q and out
+    row = D + 64 + 4
+    nbytes = B * (N * (d_I // 2 + d_I // 32) + H_I * (d_I // 2 + d_I // 32) + H_I * 4
+                  + (k + W) * row + (N2 + W) * row + 2 * 2 * H * D * 2)
+    flops = B * (2.0 * N * H_I * d_I + 4.0 * H * (k + W) * D + 4.0 * H * (N2 + W) * D)
+    return step, nbytes, flops
+
+
+def csa_prefill_setup(d):
+    """CSA chunked prefill: compress the 4096 new tokens (entries with RMSNorm
+    and RoPE, indexer keys plain) into the cache after the 262144-entry prefix,
+    score and select top-1024 for every new query, attend."""
+    m, D, dI, Tq, N0, N_cap = d["m"], d["D"], d["d_I"], d["Tq"], d["N0"], d["N_cap"]
+    E = torch.empty((1, N_cap, D), dtype=torch.bfloat16, device=DEV)
+    KI = torch.empty((1, N_cap, dI), dtype=torch.bfloat16, device=DEV)
+    E[:, :N0] = _bf16(d["E_prefix"])
+    KI[:, :N0] = _bf16(d["kI_prefix"])
+    t = {n: _bf16(d[n]) for n in ("cb", "ca", "prev_ca", "icb", "ica", "iprev_ca", "q", "qI", "win")}
+    t.update({n: _f32(d[n]) for n in ("zb", "za", "prev_za", "izb", "iza", "iprev_za", "w", "sink", "norm_w")})
+    k, H = d["k"], d["H"]
+    ws_i = torch.empty(L.csa_index_topk_workspace(L.BF16, 1, Tq, d["H_I"], dI, N_cap, m, k, d["q_pos0"]),
+                       dtype=torch.uint8, device=DEV)
+    ws_a = torch.empty(L.csa_attend_workspace(L.BF16, L.BF16, 1, Tq, H, D, N_cap, m, k, d["W"], d["q_pos0"]),
+                       dtype=torch.uint8, device=DEV)
+    idx = torch.empty((1, Tq, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((1, Tq, H, D), dtype=torch.bfloat16, device=DEV)
+
+    def step(i):
+        L.csa_compress(L.BF16, L.BF16, t["cb"], t["zb"], m, ca=t["ca"], za=t["za"], prev_ca=t["prev_ca"],
+                       prev_za=t["prev_za"], pos0=d["pos0"], flags=L.NORM | L.ROPE, norm_w=t["norm_w"],
+                       eps=d["eps"], rope_base=d["rope_base"], rope_dims=d["rope_dims"], out=E[:, N0:],
+                       out_rows=N_cap)
+        L.csa_compress(L.BF16, L.BF16, t["icb"], t["izb"], m, ca=t["ica"], za=t["iza"], prev_ca=t["iprev_ca"],
+                       prev_za=t["iprev_za"], pos0=d["pos0"], out=KI[:, N0:], out_rows=N_cap)
+        L.csa_index_topk(L.BF16, t["qI"], t["w"], KI, idx, m=m, k=k, q_pos0=d["q_pos0"], ws=ws_i)
+        L.csa_attend(L.BF16, L.BF16, t["q"], E, idx, t["win"], t["sink"], out, m=m, W=d["W"], q_pos0=d["q_pos0"],
+                     scale=1 / math.sqrt(D), flags=L.INV_ROPE, rope_dims=d["rope_dims"], ws=ws_a)
+
+    # algorithmic FLOPs: indexer QK over every visible key for every query and
+    # head, attention QK + PV over the k selected + window rows of every query
+    nv = [(d["q_pos0"] + tt + 1) // m for tt in range(Tq)]
+    flops = 2.0 * d["H_I"] * dI * sum(nv) + 4.0 * H * D * Tq * (k + d["W"])
+    return step, flops
+
+
 def timed(step, steps, warmup):
     for i in range(warmup):
         step(i)
@@ -252,6 +369,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -320,6 +439,32 @@ def main():
             "hca_attend_GBs": hb / (att * 1e-6) / 1e9, "hca_attend_hbm_frac": hb / (att * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "hca_attend_TFLOPs": hf / (att * 1e-6) / 1e12, "mfma_bf16_frac": hf / (att * 1e-6) / 2.5e15,
             "algorithmic_bytes": hb, "flops": hf,
+        }
+    if not args.no_prefill:
+        pd = WL.make_csa_prefill()
+        pstep, pflops = csa_prefill_setup(pd)
+        del pd
+        n_p = 3
+        pe = timed(pstep, n_p, 1)
+        pms = 1e3 * pe / n_p
+        pk = kernel_times(pstep, n_p)
+        result["prefill"] = {
+            "workload": "csa_prefill_tq4096_ctx1048576", "tokens_per_s": 4096 / (pms * 1e-3),
+            "ms_per_step": pms, "kernels_us": {k: round(v["avg_us"], 3) for k, v in pk.items()},
+            "flops": pflops, "achieved_TFLOPs": pflops / (pms * 1e-3) / 1e12,
+            "mfma_bf16_frac": pflops / (pms * 1e-3) / 2.5e15,
+        }
+    if not args.no_mixed:
+        mstep, mbytes, mflops = mixed_pair_setup()
+        n_m = max(10, args.steps // 10)
+        me = timed(mstep, n_m, max(2, args.warmup // 4))
+        mms = 1e3 * me / n_m
+        mk = kernel_times(mstep, n_m)
+        result["mixed_pair"] = {
+            "workload": "mixed_csa_hca_pair_b64_ctx1048576", "tokens_per_s": 64 / (mms * 1e-3),
+            "ms_per_step": mms, "kernels_us": {k: round(v["avg_us"], 3) for k, v in mk.items()},
+            "algorithmic_bytes": mbytes, "flops": mflops,
+            "achieved_GBs": mbytes / (mms * 1e-3) / 1e9, "hbm_frac": mbytes / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         }
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)

@@ -282,6 +282,31 @@ __device__ __forceinline__ void tile_pv_swz(const uint16_t* X, const SwzOffsets&
   }
 }
 
+// Work items of one sequence: u = t * S + split over its Tq queries and S
+// splits, times n_hg head groups. Consecutive workgroup ids land on
+// consecutive XCDs (id % 8), so with two head groups the ids i and i + 8 (same
+// XCD, shared L2) take the two groups of one work item u and fetch its rows
+// once; successive u spread over all XCDs.
+__host__ __device__ __forceinline__ int64_t work_blocks(const SplitPlan& sp, int Tq) {
+  const int64_t U = static_cast<int64_t>(Tq) * sp.S;
+  return sp.n_hg == 2 ? (U + 7) / 8 * 16 : U * sp.n_hg;
+}
+
+__device__ __forceinline__ bool work_item(const SplitPlan& sp, int Tq, int i, int& split, int& hg, int& t) {
+  int64_t u;
+  if (sp.n_hg == 2) {
+    hg = (i >> 3) & 1;
+    u = (static_cast<int64_t>(i >> 4) << 3) | (i & 7);
+  } else {
+    hg = i % sp.n_hg;
+    u = i / sp.n_hg;
+  }
+  if (u >= static_cast<int64_t>(Tq) * sp.S) return false;
+  t = static_cast<int>(u / sp.S);
+  split = static_cast<int>(u % sp.S);
+  return true;
+}
+
 template <int D, bool MIXED>
 __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, SplitPlan sp,
                                                                   float* __restrict__ part_o,
@@ -299,20 +324,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
   const int g = lane >> 4, r16 = lane & 15;
-  int split, hg;
-  {
-    // two head groups: ids i and i + 8 (same XCD) take the two groups of one split
-    const int i = blockIdx.x;
-    if (sp.n_hg == 2) {
-      hg = (i >> 3) & 1;
-      split = ((i >> 4) << 3) | (i & 7);
-    } else {
-      hg = i % sp.n_hg;
-      split = i / sp.n_hg;
-    }
-  }
-  if (split >= sp.S) return;
-  const int t = blockIdx.y, b = blockIdx.z;
+  int split, hg, t;
+  if (!work_item(sp, a.Tq, blockIdx.x, split, hg, t)) return;
+  const int b = blockIdx.z;
   const bool active = wid * 16 < sp.HG;
   const int head = hg * sp.HG + wid * 16 + r16;
   const RowSpan rs = row_span(a, t);
@@ -491,19 +505,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
   const int g = lane >> 4, r16 = lane & 15;
-  int split, hg;
-  {
-    const int i = blockIdx.x;
-    if (sp.n_hg == 2) {
-      hg = (i >> 3) & 1;
-      split = ((i >> 4) << 3) | (i & 7);
-    } else {
-      hg = i % sp.n_hg;
-      split = i / sp.n_hg;
-    }
-  }
-  if (split >= sp.S) return;
-  const int t = blockIdx.y, b = blockIdx.z;
+  int split, hg, t;
+  if (!work_item(sp, a.Tq, blockIdx.x, split, hg, t)) return;
+  const int b = blockIdx.z;
   const bool active = wid * 16 < sp.HG;
   const int head = hg * sp.HG + wid * 16 + r16;
   const RowSpan rs = row_span(a, t);
@@ -962,9 +966,7 @@ SplitPlan make_plan(const AttendArgs& a) {
 
 template <int D>
 void launch_mfma_d(LaunchScope& sc, const AttendArgs& a, const SplitPlan& sp, float* po, float* pml) {
-  int nblk = sp.S * sp.n_hg;
-  if (sp.n_hg == 2) nblk = ((sp.S + 7) / 8) * 16;     // XCD-paired id layout
-  dim3 grid(nblk, a.Tq, a.B), block(kAttThreads);
+  dim3 grid(static_cast<uint32_t>(work_blocks(sp, a.Tq)), 1, a.B), block(kAttThreads);
   if (a.dt_kv == LCA_KV_MIXED)
     sc.launch(attend_mfma_kernel<D, true>, grid, block, 0, a, sp, po, pml);
   else if constexpr (D == 512)
@@ -983,6 +985,7 @@ size_t attend_workspace(const AttendArgs& a) {
 
 hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
   const SplitPlan sp = make_plan(a);
+  if (work_blocks(sp, a.Tq) > 2147483647LL) return hipErrorInvalidConfiguration;
   const size_t rows = static_cast<size_t>(a.B) * a.Tq * a.H * sp.S;
   float* po = static_cast<float*>(ws);
   float* pml = po + rows * a.D;
@@ -1005,7 +1008,7 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
     if (e != hipSuccess) return e;
   }
   {
-    LaunchScope scope(s, "attend_combine");
+    LaunchScope scope(s, a.sparse ? "csa_combine" : "hca_combine");
     scope.launch(combine_kernel, dim3(a.H, a.Tq, a.B), dim3(a.D / 2 > 64 ? a.D / 2 : 64), 0, a, sp.S, sp.RS,
                  static_cast<const float*>(po), static_cast<const float*>(pml));
     return hipGetLastError();
