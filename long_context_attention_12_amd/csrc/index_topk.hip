@@ -136,6 +136,113 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Many queries per call (prefill): the decode kernel above would re-read every
+// key once per 16-row query tile. Here a workgroup holds 256 / H_I queries in
+// registers (4 waves x 4 M tiles of 16 query-head rows, d_I = 128) and walks a
+// range of keys in 64-key tiles. Each tile is copied HBM -> LDS by the load
+// units (double-buffered, 16 KB), with the 16-byte slots of each 256-byte key
+// row XOR-swizzled by (key & 15), so the B-fragment reads (16 keys at one
+// column) hit distinct banks; every tile then feeds 64 MFMAs per wave.
+// ---------------------------------------------------------------------------
+constexpr int kTileKeys = 64;
+constexpr int kTiledMinQueries = 64;
+
+template <int HI>
+__global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
+    float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, int m,
+    int64_t keys_per_wg, bool round_bf16) {
+  constexpr int DI = 128, KS = DI / 32, MB = 4, NB = kTileKeys / 16, QPB = 16 / HI;
+  constexpr int QPW = MB * QPB, QPWG = 4 * QPW;
+  constexpr int ROWB = DI * 2;                       // bytes per key row
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kTileKeys * DI];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int b = blockIdx.z;
+  const int t_end = min(Tq, t_off + Tc);
+  const int tw0 = t_off + static_cast<int>(blockIdx.y) * QPWG;
+  if (tw0 >= t_end) return;
+  int64_t nv_max = n_visible(q_pos0 + min(tw0 + QPWG, t_end) - 1, m);
+  if (nv_max > N_cap) nv_max = N_cap;
+  const int64_t k_begin = static_cast<int64_t>(blockIdx.x) * keys_per_wg;
+  if (k_begin >= nv_max) return;
+  const int64_t k_end = min(k_begin + keys_per_wg, nv_max);
+  const int ntiles = static_cast<int>((k_end - k_begin + kTileKeys - 1) / kTileKeys);
+
+  // tile tt -> LDS buffer: 16 copies of 1 KB (4 key rows each), 4 per wave;
+  // lane l fills key 4c + l/16 at physical slot l % 16 from logical slot
+  // (l % 16) ^ (key & 15); keys past k_end repeat the last key (not scored)
+  const char* kb = reinterpret_cast<const char*>(kI) + static_cast<int64_t>(b) * N_cap * ROWB;
+  auto issue = [&](int tt, int buf) {
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int c = wid * 4 + cc;
+      const int kl = 4 * c + (lane >> 4);
+      int64_t key = k_begin + static_cast<int64_t>(tt) * kTileKeys + kl;
+      if (key >= k_end) key = k_end - 1;
+      const char* src = kb + key * ROWB + 16 * ((lane & 15) ^ (kl & 15));
+      lds_copy16(src, lds_address(&Ks[buf][0]) + c * 1024);
+    }
+  };
+  issue(0, 0);
+
+  // queries of this wave: M tile mb covers queries tq0 + r16 / HI (heads r16 % HI)
+  bf16x8 aq[MB][KS];
+  float wv[MB][4];
+  int64_t nvq[MB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int tq0 = tw0 + wid * QPW + mb * QPB;
+    const int qt = tq0 + r16 / HI, h = r16 % HI;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qt < t_end) v = *reinterpret_cast<const uint4*>(qI + ((static_cast<int64_t>(b) * Tq + qt) * HI + h) * DI + 32 * s + 8 * g);
+      aq[mb][s] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * g + i, q2 = tq0 + row / HI, h2 = row % HI;
+      wv[mb][i] = q2 < t_end ? w[(static_cast<int64_t>(b) * Tq + q2) * HI + h2] : 0.f;
+      int64_t nv = q2 < t_end ? n_visible(q_pos0 + q2, m) : 0;
+      nvq[mb][i] = nv < k_end ? nv : k_end;        // this workgroup scores keys < k_end only
+    }
+  }
+  float* srow = scores + static_cast<int64_t>(b) * Tc * ld;
+  const int slot_r = r16;                          // key & 15 of the keys this lane reads
+
+  for (int tt = 0; tt < ntiles; ++tt) {
+    // tile tt has landed (every wave waited for its own copies) and every wave
+    // is done with the buffer that tile tt + 1 overwrites
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (tt + 1 < ntiles) issue(tt + 1, (tt + 1) & 1);
+    const char* xb = reinterpret_cast<const char*>(&Ks[tt & 1][0]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4 acc[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(xb + (nb * 16 + r16) * ROWB + 16 * ((4 * s + g) ^ slot_r));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[mb][s], __builtin_bit_cast(bf16x8, kv), acc[mb], 0, 0, 0);
+      }
+      const int64_t j = k_begin + static_cast<int64_t>(tt) * kTileKeys + nb * 16 + r16;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        pin_uniform(acc[mb]);
+        emit_scores<HI>(acc[mb], wv[mb], nvq[mb], g, tw0 + wid * QPW + mb * QPB, t_off, t_end, j, srow, ld,
+                        round_bf16);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // MXFP4 scoring (d_I = 128) with the scaled MFMA 16x16x128 (f8f6f4, e2m1
 // operands): lane l holds row / key l % 16 and the 32-element block l / 16 of
 // it (16 packed bytes, low nibble first) together with that block's E8M0
@@ -472,6 +579,27 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
           case 4: scope.launch(index_score_fp4_kernel<4>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
           case 8: scope.launch(index_score_fp4_kernel<8>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
           default: scope.launch(index_score_fp4_kernel<16>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
+        }
+      } else if (a.d_I == 128 && tcn >= kTiledMinQueries) {
+        // many queries: key tiles through LDS, ~2048 workgroups over (keys, queries)
+        const int qpwg = 4 * 4 * (16 / a.H_I);
+        const int64_t n_qt = (tcn + qpwg - 1) / qpwg;
+        int64_t kc = (2048 + n_qt * a.B - 1) / (n_qt * a.B);
+        const int64_t kc_max = (nv_max + 255) / 256;
+        if (kc > kc_max) kc = kc_max;
+        if (kc < 1) kc = 1;
+        int64_t per = (nv_max + kc - 1) / kc;
+        per = (per + kTileKeys - 1) / kTileKeys * kTileKeys;
+        kc = (nv_max + per - 1) / per;
+        dim3 grid(static_cast<uint32_t>(kc), static_cast<uint32_t>(n_qt), a.B);
+        const uint16_t* q = static_cast<const uint16_t*>(a.qI);
+        const uint16_t* k = static_cast<const uint16_t*>(a.kI);
+        switch (a.H_I) {
+          case 1: scope.launch(index_score_tiled_kernel<1>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
+          case 2: scope.launch(index_score_tiled_kernel<2>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
+          case 4: scope.launch(index_score_tiled_kernel<4>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
+          case 8: scope.launch(index_score_tiled_kernel<8>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
+          default: scope.launch(index_score_tiled_kernel<16>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
         }
       } else {
         const int QPB = 16 / a.H_I;

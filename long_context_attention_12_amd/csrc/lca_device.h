@@ -78,6 +78,31 @@ __device__ __forceinline__ int mx_scale_exp(float amax) {
   return E < -127 ? -127 : (E > 127 ? 127 : E);
 }
 
+// ---- direct HBM -> LDS copies ---------------------------------------------------
+// One 16-byte-per-lane copy HBM -> LDS: lane l's 16 bytes at `gptr` land at
+// LDS byte address lds_addr + 16 * l. Issued as inline asm so that the
+// compiler does not track it: every wait on these copies in the ring loop is
+// explicit (wait_vmcnt); a loop that uses it issues no other vector-memory
+// access it would have to wait for. The instruction has no register results.
+__device__ __forceinline__ void lds_copy16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)(p)));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // s_waitcnt with vmcnt = N (6-bit field split over [3:0] and [15:14]); expcnt
+  // and lgkmcnt at their maxima, i.e. not waited on
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---- wave reductions (64 lanes) -----------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -204,6 +204,52 @@ def test_index_topk_prefill_causal_bf16(bf16_scores):
             check_topk_set(idx_h[b, t], s, k, bf16_scores=bf16_scores)
 
 
+@pytest.mark.parametrize("H_I", [1, 4, 16])
+@pytest.mark.parametrize("bf16_scores", [False, True])
+def test_index_topk_many_queries_tiled(H_I, bf16_scores):
+    # >= 64 queries with d_I = 128 take the key-tiled path: ragged query tiles,
+    # ragged key tiles and key ranges, causal limits inside a tile
+    L = need_gpu()
+    rng = np.random.default_rng(60 + H_I)
+    B, Tq, d_I, m, k = 2, 150, 128, 4, 100
+    q_pos0 = 4 * 1700 + 1
+    N_cap = (q_pos0 + Tq) // m + 5
+    qI, w, kI = _index_case(rng, B, Tq, H_I, d_I, N_cap, ties=True)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    say(f"tiled index H_I={H_I} bf16={bf16_scores}")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
+                     flags=L.SCORE_BF16 if bf16_scores else 0, score_out=sco)
+    torch.cuda.synchronize()
+    idx_h, sco_h = idx.cpu().numpy(), sco.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            nv = O.n_visible(q_pos0 + t, m)
+            s = O.index_scores(qI[b, t], w[b, t], kI[b], nv)
+            check_topk_set(idx_h[b, t], s, k, bf16_scores=bf16_scores)
+            sel = idx_h[b, t][idx_h[b, t] >= 0]
+            ref = O.bf16_round(s[sel]) if bf16_scores else s[sel]
+            tol = np.abs(ref) * (2.0 ** -7 if bf16_scores else 1e-4) + 1e-6 * np.max(np.abs(s))
+            assert np.all(np.abs(sco_h[b, t][:len(sel)] - ref) <= tol), (b, t)
+
+
+def test_index_topk_many_queries_from_sequence_start():
+    # tiled path with queries from position 0: the first ones see no entry
+    L = need_gpu()
+    rng = np.random.default_rng(61)
+    B, Tq, H_I, d_I, m, k = 1, 300, 4, 128, 4, 16
+    N_cap = Tq // m
+    qI, w, kI = _index_case(rng, B, Tq, H_I, d_I, N_cap)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=0)
+    torch.cuda.synchronize()
+    idx_h = idx.cpu().numpy()
+    assert np.all(idx_h[0, :3] == -1)
+    for t in range(Tq):
+        s = O.index_scores(qI[0, t], w[0, t], kI[0], O.n_visible(t, m))
+        check_topk_set(idx_h[0, t], s, k)
+
+
 def test_index_topk_f32_from_sequence_start():
     # queries from position 0: the first ones see no entry (all padding)
     L = need_gpu()
