@@ -365,23 +365,37 @@ __device__ __forceinline__ uint32_t score_key(float v, bool key16) {
   return key16 ? (k >> 16) : k;
 }
 
+// Inclusive scan over the 64 lanes of a wave in registers (DPP): shifts of
+// 1, 2, 4, 8 lanes inside each 16-lane row, then the row totals carried across
+// rows with the row_bcast:15 / row_bcast:31 moves of the gfx9 family.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  int v = static_cast<int>(x);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return static_cast<uint32_t>(v);
+}
+
 // Block-wide exclusive scan of one value per thread (1024 threads, 16 waves).
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) wsum[wid] = x;
   __syncthreads();
   uint32_t before = 0, all = 0;
+  const uint4* w4 = reinterpret_cast<const uint4*>(wsum);
 #pragma unroll
-  for (int i = 0; i < kSelThreads / 64; ++i) {
-    const uint32_t s = wsum[i];
-    before += i < wid ? s : 0u;
-    all += s;
+  for (int i = 0; i < kSelThreads / 256; ++i) {
+    const uint4 q = w4[i];
+    const uint32_t e[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      before += 4 * i + c < wid ? e[c] : 0u;
+      all += e[c];
+    }
   }
   __syncthreads();
   *total = all;
@@ -414,7 +428,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     int64_t q_pos0, int m, int k, bool key16, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
   __shared__ uint32_t hist[kMaxBins];
-  __shared__ uint32_t wsum[kSelThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[kSelThreads / 64];
   __shared__ uint32_t sh_digit, sh_krem;
   const int tid = threadIdx.x;
   const int b = blockIdx.y, tl = blockIdx.x, t = t_off + tl;
@@ -488,27 +502,30 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   for (int r = 0; r < rounds; ++r) {
     const int64_t base = static_cast<int64_t>(r) * kRound;
     if (rounds > 1) load_round(s, n, base, key16, key);
-    uint32_t gt = 0, eq = 0;
+    uint32_t gtm = 0, eqm = 0;
 #pragma unroll
     for (int j = 0; j < kSelItems; ++j) {
-      gt += key[j] > thr;
-      eq += key[j] == thr;
+      gtm |= static_cast<uint32_t>(key[j] > thr) << j;
+      eqm |= static_cast<uint32_t>(key[j] == thr) << j;
     }
+    const uint32_t gt = __builtin_popcount(gtm), eq = __builtin_popcount(eqm);
     uint32_t tot;
     const uint32_t pre = block_excl_scan((gt << 16) | eq, wsum, &tot);  // both < 2^16 per round
     const uint32_t gt_pre = run_gt + (pre >> 16), eq_pre = run_eq + (pre & 0xffffu);
     uint32_t pos = gt_pre + min(eq_pre, krem);
-    uint32_t eq_rank = eq_pre;
+    // ties at the threshold: the first (krem - eq_pre) of them in index order
+    uint32_t take = gtm;
+    for (uint32_t c = eq_pre; eqm && c < krem; ++c) {
+      take |= eqm & (~eqm + 1u);
+      eqm &= eqm - 1;
+    }
     const int64_t i0 = base + static_cast<int64_t>(tid) * kSelItems;
-#pragma unroll
-    for (int j = 0; j < kSelItems; ++j) {
-      bool take = key[j] > thr;
-      if (key[j] == thr) { take = eq_rank < krem; ++eq_rank; }
-      if (take) {
-        io[pos] = static_cast<int32_t>(i0 + j);
-        if (so) so[pos] = s[i0 + j];
-        ++pos;
-      }
+    while (take) {
+      const int j = __builtin_ctz(take);
+      take &= take - 1;
+      io[pos] = static_cast<int32_t>(i0 + j);
+      if (so) so[pos] = s[i0 + j];
+      ++pos;
     }
     run_gt += tot >> 16;
     run_eq += tot & 0xffffu;
