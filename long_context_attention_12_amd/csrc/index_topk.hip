@@ -28,7 +28,7 @@ namespace lca {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kKeysPerWave = 64;   // 4 MFMA key groups, all loads issued together
+constexpr int kKeysPerWave = 32;   // 2 MFMA key groups, all loads issued together (many short waves stream best)
 constexpr int kKeysPerWG = 4 * kKeysPerWave;
 
 // An MFMA reads its operands only from lanes enabled in EXEC. Its result here
