@@ -250,6 +250,38 @@ def test_index_topk_many_queries_from_sequence_start():
         check_topk_set(idx_h[0, t], s, k)
 
 
+@pytest.mark.parametrize("bf16_scores", [False, True])
+@pytest.mark.parametrize("crowded", [False, True])
+def test_index_topk_long_lists(bf16_scores, crowded):
+    # lists longer than one register round (32768) take the bounded path (group
+    # maxima -> lower bound -> candidates in LDS); crowded keys (few distinct
+    # scores) overflow the candidate buffer and fall back to full passes
+    L = need_gpu()
+    rng = np.random.default_rng(70 + 2 * crowded + bf16_scores)
+    B, Tq, H_I, d_I, m, k = 2, 1, 4, 128, 4, 1024
+    N_cap = 100003
+    q_pos0 = 4 * 100000 + 1                   # n_vis = 100000: four rounds, ragged
+    qI, w, kI = _index_case(rng, B, Tq, H_I, d_I, N_cap)
+    if crowded:
+        kI = WL.bf16_exact(kI[:, rng.integers(0, 40, size=N_cap)])   # 40 distinct keys
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    say(f"long list bf16={bf16_scores} crowded={crowded}")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
+                     flags=L.SCORE_BF16 if bf16_scores else 0, score_out=sco)
+    torch.cuda.synchronize()
+    idx_h, sco_h = idx.cpu().numpy(), sco.cpu().numpy()
+    for b in range(B):
+        nv = O.n_visible(q_pos0, m)
+        s = O.index_scores(qI[b, 0], w[b, 0], kI[b], nv)
+        check_topk_set(idx_h[b, 0], s, k, bf16_scores=bf16_scores)
+        assert np.all(np.diff(idx_h[b, 0]) > 0), "indices not increasing"
+        sel = idx_h[b, 0]
+        ref = O.bf16_round(s[sel]) if bf16_scores else s[sel]
+        tol = np.abs(ref) * (2.0 ** -7 if bf16_scores else 1e-4) + 1e-6 * np.max(np.abs(s))
+        assert np.all(np.abs(sco_h[b, 0] - ref) <= tol)
+
+
 def test_index_topk_f32_from_sequence_start():
     # queries from position 0: the first ones see no entry (all padding)
     L = need_gpu()
