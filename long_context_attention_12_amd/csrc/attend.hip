@@ -307,6 +307,64 @@ __device__ __forceinline__ bool work_item(const SplitPlan& sp, int Tq, int i, in
   return true;
 }
 
+// A query's only split is its whole row set: the head's output is final here.
+// Accumulators are relative to the fixed reference m_run; with M = max(sink,
+// m_run), out = o e^(m_run - M) / (z e^(m_run - M) + e^(sink - M)), then the
+// RoPE channels are turned back by -p. Lane (g, r16) holds channels
+// 16 dt + 4g .. +3 of head r16. The (max) slot is set to +inf (done), or NaN
+// when the logits outgrew the headroom (an exact recompute follows).
+// Angles of the inverse RoPE at query t: rope_tab[i] = (cos, sin) of pair i
+// at position -(q_pos0 + t), filled once per workgroup.
+__device__ __forceinline__ void fill_rope_table(const AttendArgs& a, int t, float2* rope_tab) {
+  const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
+  for (int i = threadIdx.x; i < R / 2; i += blockDim.x) {
+    float sn, cs;
+    rope_sincos(-static_cast<double>(a.q_pos0 + t), i, R, static_cast<double>(a.rope_base), &sn, &cs);
+    rope_tab[i] = make_float2(cs, sn);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void write_output(const AttendArgs& a, int b, int t, int head, int g,
+                                             const f32x4 (&acc_o)[D / 16], float m_run, float z_run, bool flag,
+                                             const float2* rope_tab, float* ml) {
+  constexpr int DT = D / 16;
+  if (flag) {
+    if (g == 0) ml[0] = __builtin_nanf("");
+    return;
+  }
+  const float sink = a.sink[head];
+  const float M = fmaxf(sink, m_run);
+  const float so = m_run == -INFINITY ? 0.f : __expf(m_run - M);
+  const float Zt = z_run * so + __expf(sink - M);
+  const float inv = so / Zt;
+  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + head;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + row * D;
+  const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    float v[4] = {acc_o[dt][0] * inv, acc_o[dt][1] * inv, acc_o[dt][2] * inv, acc_o[dt][3] * inv};
+    const int c0 = 16 * dt + 4 * g;
+    if (c0 >= D - R) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float2 cs = rope_tab[(c0 + 2 * p - (D - R)) / 2];
+        const float x = v[2 * p], y = v[2 * p + 1];
+        v[2 * p] = x * cs.x - y * cs.y;
+        v[2 * p + 1] = x * cs.y + y * cs.x;
+      }
+    }
+    uint2 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(op + c0) = w;
+  }
+  if (g == 0) {
+    if (a.lse_out) a.lse_out[row] = M + logf(Zt);
+    ml[0] = INFINITY;
+  }
+}
+
 template <int D, bool MIXED>
 __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, SplitPlan sp,
                                                                   float* __restrict__ part_o,
@@ -320,6 +378,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
   constexpr int RB = MIXED ? D + 64 : 2 * D;      // bytes per stored row
   __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kTileRows * XS];
   __shared__ int32_t rows[kMaxSplitRows];
+  __shared__ float2 rope_tab[D / 2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
@@ -330,6 +389,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
   const bool active = wid * 16 < sp.HG;
   const int head = hg * sp.HG + wid * 16 + r16;
   const RowSpan rs = row_span(a, t);
+  if (sp.S == 1) fill_rope_table(a, t, rope_tab);   // read after the tile loop's barriers
   const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
   int64_t r_end = r_begin + sp.RS;
   if (r_end > rs.nrows) r_end = rs.nrows;
@@ -450,13 +510,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
 
   if (active) {
     const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
-    float* po = part_o + part_idx * D;
+    if (sp.S == 1) {
+      write_output<D>(a, b, t, head, g, acc_o, m_run, z_run, flag, rope_tab, part_ml + 2 * part_idx);
+    } else {
+      float* po = part_o + part_idx * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
-    if (g == 0) {
-      part_ml[2 * part_idx] = flag ? __builtin_nanf("") : m_run;   // NaN: recompute in combine
-      part_ml[2 * part_idx + 1] = z_run;
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+      if (g == 0) {
+        part_ml[2 * part_idx] = flag ? __builtin_nanf("") : m_run;   // NaN: recompute in combine
+        part_ml[2 * part_idx + 1] = z_run;
+      }
     }
   }
 }
@@ -477,6 +541,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
   constexpr int RPW = kTileRows / 4;               // rows per wave per tile
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kRing][kTileRows * D];
   __shared__ int32_t rows[kMaxSplitRows];
+  __shared__ float2 rope_tab[D / 2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
@@ -487,6 +552,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
   const bool active = wid * 16 < sp.HG;
   const int head = hg * sp.HG + wid * 16 + r16;
   const RowSpan rs = row_span(a, t);
+  if (sp.S == 1) fill_rope_table(a, t, rope_tab);   // read after the tile loop's barriers
   const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
   int64_t r_end = r_begin + sp.RS;
   if (r_end > rs.nrows) r_end = rs.nrows;
@@ -583,13 +649,17 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
 
   if (active) {
     const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
-    float* po = part_o + part_idx * D;
+    if (sp.S == 1) {
+      write_output<D>(a, b, t, head, g, acc_o, m_run, z_run, flag, rope_tab, part_ml + 2 * part_idx);
+    } else {
+      float* po = part_o + part_idx * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
-    if (g == 0) {
-      part_ml[2 * part_idx] = flag ? __builtin_nanf("") : m_run;   // NaN: recompute in combine
-      part_ml[2 * part_idx + 1] = z_run;
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+      if (g == 0) {
+        part_ml[2 * part_idx] = flag ? __builtin_nanf("") : m_run;   // NaN: recompute in combine
+        part_ml[2 * part_idx + 1] = z_run;
+      }
     }
   }
 }
@@ -801,13 +871,15 @@ __device__ void recompute_split(const AttendArgs& a, int RS, int b, int t, int h
   o_out = o;
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int S, int RS,
-                                                      const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml) {
-  __shared__ float sml[2 * 256];
-  __shared__ float red[4];
-  __shared__ float lc[kCombMaxRows];
-  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
+// Merge the S split partials of (b, t, h): the sink enters the denominator
+// once, the result is normalised, its RoPE channels turned back by -p, and
+// written to out (and lse). Every thread of the block calls it (it holds block
+// barriers); thread c < D/2 owns channel pair (2c, 2c+1). sml holds 2S floats,
+// red one float per wave, lc kCombMaxRows floats, all in LDS.
+__device__ void combine_row(const AttendArgs& a, int S, int RS, int b, int t, int h,
+                            const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                            float* sml, float* red, float* lc) {
+  const int c = threadIdx.x;
   const int D = a.D;
   const bool own = 2 * c < D;
   const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + h;
@@ -865,28 +937,62 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int S, int R
     u = fmaf(w, o.x, u);
     v = fmaf(w, o.y, v);
   }
-  if (!own) return;
-  const float inv = 1.0f / Z;
-  u *= inv;
-  v *= inv;
-  if (c == 0 && a.lse_out) a.lse_out[row] = M + logf(Z);
-  const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
-  const int d0 = 2 * c;
-  if (d0 >= D - R) {
-    float sn, cs;
-    rope_sincos(-static_cast<double>(a.q_pos0 + t), (d0 - (D - R)) / 2, R,
-                static_cast<double>(a.rope_base), &sn, &cs);
-    const float nu = u * cs - v * sn, nv = u * sn + v * cs;
-    u = nu;
-    v = nv;
+  if (own) {
+    const float inv = 1.0f / Z;
+    u *= inv;
+    v *= inv;
+    if (c == 0 && a.lse_out) a.lse_out[row] = M + logf(Z);
+    const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
+    const int d0 = 2 * c;
+    if (d0 >= D - R) {
+      float sn, cs;
+      rope_sincos(-static_cast<double>(a.q_pos0 + t), (d0 - (D - R)) / 2, R,
+                  static_cast<double>(a.rope_base), &sn, &cs);
+      const float nu = u * cs - v * sn, nv = u * sn + v * cs;
+      u = nu;
+      v = nv;
+    }
+    if (a.dt_q == LCA_F32) {
+      float* o = static_cast<float*>(a.out) + row * D;
+      o[d0] = u;
+      o[d0 + 1] = v;
+    } else {
+      reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + row * D)[c] = pack_bf16x2(u, v);
+    }
   }
-  if (a.dt_q == LCA_F32) {
-    float* o = static_cast<float*>(a.out) + row * D;
-    o[d0] = u;
-    o[d0 + 1] = v;
-  } else {
-    reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + row * D)[c] = pack_bf16x2(u, v);
+  __syncthreads();                                 // sml / lc free for the next row
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int S, int RS,
+                                                      const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml) {
+  __shared__ float sml[2 * 256];
+  __shared__ float red[4];
+  __shared__ float lc[kCombMaxRows];
+  combine_row(a, S, RS, blockIdx.z, blockIdx.y, blockIdx.x, part_o, part_ml, sml, red, lc);
+}
+
+// One split per query: the attention kernel wrote every head's output itself
+// and left (max) = +inf, except for heads whose logits outgrew the in-kernel
+// headroom (max = NaN). One workgroup per (b, t) recomputes those exactly.
+__global__ __launch_bounds__(256) void fixup_kernel(AttendArgs a, int RS, const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml) {
+  __shared__ float sml[2 * 256];
+  __shared__ float red[4];
+  __shared__ float lc[kCombMaxRows];
+  __shared__ uint32_t todo[8];                       // one bit per head (H <= 256)
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int64_t row0 = (static_cast<int64_t>(b) * a.Tq + t) * a.H;
+  if (threadIdx.x < 8) todo[threadIdx.x] = 0u;
+  __syncthreads();
+  for (int h = threadIdx.x; h < a.H; h += blockDim.x) {
+    const float m0 = part_ml[2 * (row0 + h)];
+    if (m0 != m0) atomicOr(&todo[h >> 5], 1u << (h & 31));
   }
+  __syncthreads();
+  for (int h = 0; h < a.H; ++h)
+    if ((todo[h >> 5] >> (h & 31)) & 1u)             // uniform across the block
+      combine_row(a, 1, RS, b, t, h, part_o, part_ml, sml, red, lc);
 }
 
 SplitPlan make_plan(const AttendArgs& a) {
@@ -985,8 +1091,13 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
   }
   {
     LaunchScope scope(s, a.sparse ? "csa_combine" : "hca_combine");
-    scope.launch(combine_kernel, dim3(a.H, a.Tq, a.B), dim3(a.D / 2 > 64 ? a.D / 2 : 64), 0, a, sp.S, sp.RS,
-                 static_cast<const float*>(po), static_cast<const float*>(pml));
+    const dim3 cb(a.D / 2 > 64 ? a.D / 2 : 64);
+    if (sp.S == 1 && a.dt_kv != LCA_F32)
+      scope.launch(fixup_kernel, dim3(a.Tq, a.B), cb, 0, a, sp.RS, static_cast<const float*>(po),
+                   static_cast<const float*>(pml));
+    else
+      scope.launch(combine_kernel, dim3(a.H, a.Tq, a.B), cb, 0, a, sp.S, sp.RS, static_cast<const float*>(po),
+                   static_cast<const float*>(pml));
     return hipGetLastError();
   }
 }
