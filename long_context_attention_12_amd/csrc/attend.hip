@@ -11,17 +11,24 @@
 // Decomposition: one workgroup per (sequence, query, row split, head group of
 // up to 64 heads). All heads of a group share each staged KV row, which is
 // read from HBM once per split. Rows of a split are staged 32 at a time into
-// a row-major LDS tile (double-buffered; the next tile's loads are in flight
-// in registers while the current one is consumed). S^T = X Q^T reads the tile
-// row-wise (rows as MFMA M); O^T = X^T P^T reads it transposed with gfx950's
-// ds_read_b64_tr_b16 (rows as MFMA K). Each wave owns 16 heads: its 16 x D
-// query block stays in registers as the B operand, its 16 x D output block in
-// accumulators, and the probabilities produced by the S^T accumulators feed
-// the PV MFMA's B operand with no data movement. Online softmax runs per
-// head in float32. Each split writes (max, sum, o) partials; the combine
-// kernel merges splits in a fixed order, adds the sink once, divides and
-// applies the inverse RoPE. Split sizes depend only on per-sequence shapes,
-// so results are independent of the batch size.
+// an LDS tile. S^T = X Q^T reads the tile row-wise (rows as MFMA M); O^T =
+// X^T P^T reads it transposed with gfx950's ds_read_b64_tr_b16 (rows as MFMA
+// K). Each wave owns 16 heads: its 16 x D query block stays in registers as
+// the B operand, its 16 x D output block in accumulators, and the
+// probabilities produced by the S^T accumulators feed the PV MFMA's B operand
+// with no data movement. Three kernels stage tiles:
+//   attend_dma_kernel        bf16 rows, D = 512: HBM -> LDS copies by the
+//                            load units into a 4-tile ring (XOR-swizzled);
+//   attend_mixed_dma_kernel  fp8 + bf16 rows, D = 512: raw rows by DMA, then
+//                            an exact fp8 -> bf16 conversion pass in LDS;
+//   attend_mfma_kernel       bf16 rows, D <= 256: staged through registers
+//                            into a double-buffered padded tile.
+// The softmax keeps a fixed reference max per head (no rescaling of the
+// accumulators); see kHeadroom. Each split writes (max, sum, o) partials and
+// the combine kernel merges splits in a fixed order, adds the sink once,
+// divides and applies the inverse RoPE; a query whose rows form a single
+// split gets its output from the attention kernel itself. Split sizes depend
+// only on per-sequence shapes, so results are independent of the batch size.
 #include "lca_device.h"
 #include "lca_internal.h"
 #include "../../include/lca.h"
@@ -365,7 +372,7 @@ __device__ __forceinline__ void write_output(const AttendArgs& a, int b, int t, 
   }
 }
 
-template <int D, bool MIXED>
+template <int D>
 __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, SplitPlan sp,
                                                                   float* __restrict__ part_o,
                                                                   float* __restrict__ part_ml) {
@@ -374,8 +381,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
   constexpr int DT = D / 16;                      // 16-channel output tiles
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
   constexpr int CPT = kTileRows * CPR / kAttThreads;   // chunks per thread per tile
-  constexpr int NQ = D - 64;                      // fp8 channels of a mixed row
-  constexpr int RB = MIXED ? D + 64 : 2 * D;      // bytes per stored row
+  constexpr int RB = 2 * D;                       // bytes per stored row
   __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kTileRows * XS];
   __shared__ int32_t rows[kMaxSplitRows];
   __shared__ float2 rope_tab[D / 2];
@@ -429,12 +435,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
   // turns into a per-lane load of a kernel argument.
   const uint8_t* kv_base = static_cast<const uint8_t*>(a.kv);
   const uint8_t* win_base = static_cast<const uint8_t*>(a.win);
-  const float* kv_sc = a.kv_scale;
-  const float* win_sc = a.win_scale;
   const int64_t kv_off = static_cast<int64_t>(b) * a.N_cap;
   const int64_t win_off = static_cast<int64_t>(b) * win_rows;
   uint4 pre[CPT];
-  float psc[CPT];
   auto issue = [&](int tile) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -445,21 +448,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
       const bool is_kv = src >= 0;
       const int64_t ridx = is_kv ? kv_off + src : win_off + (-2 - src);
       const uint8_t* base = (is_kv ? kv_base : win_base) + ridx * RB;
-      pre[c] = make_uint4(0, 0, 0, 0);
-      psc[c] = 0.f;
-      if (src != -1) {
-        if constexpr (!MIXED) {
-          pre[c] = *reinterpret_cast<const uint4*>(base + 2 * d0);
-        } else {
-          if (d0 < NQ) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(base + d0);
-            pre[c] = make_uint4(raw.x, raw.y, 0, 0);
-            psc[c] = (is_kv ? kv_sc : win_sc)[ridx];
-          } else {
-            pre[c] = *reinterpret_cast<const uint4*>(base + NQ + 2 * (d0 - NQ));
-          }
-        }
-      }
+      pre[c] = src != -1 ? *reinterpret_cast<const uint4*>(base + 2 * d0) : make_uint4(0, 0, 0, 0);
     }
   };
   auto commit = [&](int buf) {
@@ -467,22 +456,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
     for (int c = 0; c < CPT; ++c) {
       const int chunk = tid + kAttThreads * c;
       const int r = chunk / CPR, d0 = (chunk % CPR) * 8;
-      uint4 v = pre[c];
-      if constexpr (MIXED) {
-        if (d0 < NQ) {
-          const float sc = psc[c];
-          uint32_t w[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t word = q < 2 ? v.x : v.y;
-            const uint32_t b0 = (word >> (16 * (q & 1))) & 0xffu;
-            const uint32_t b1 = (word >> (16 * (q & 1) + 8)) & 0xffu;
-            w[q] = pack_bf16x2(e4m3fn_to_f32(b0) * sc, e4m3fn_to_f32(b1) * sc);
-          }
-          v = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
-      *reinterpret_cast<uint4*>(&Xs[buf][r * XS + d0]) = v;
+      *reinterpret_cast<uint4*>(&Xs[buf][r * XS + d0]) = pre[c];
     }
   };
 
@@ -645,6 +619,270 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
     tile_softmax_swz(Xs[it % kRing], so, it * kTileRows, rows, qf, a.scale, g, m_run, z_run, flag, pf);
     tile_pv_swz(Xs[it % kRing], so, pf, acc_o);
     if (it + 1 < ntiles) wait_tile(it + 1);
+  }
+
+  if (active) {
+    const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
+    if (sp.S == 1) {
+      write_output<D>(a, b, t, head, g, acc_o, m_run, z_run, flag, rope_tab, part_ml + 2 * part_idx);
+    } else {
+      float* po = part_o + part_idx * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
+      if (g == 0) {
+        part_ml[2 * part_idx] = flag ? __builtin_nanf("") : m_run;   // NaN: recompute in combine
+        part_ml[2 * part_idx + 1] = z_run;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Mixed rows (448 x e4m3fn bytes + 64 x bf16, one fp32 scale per row), D = 512.
+// Raw 576-byte rows go HBM -> LDS by DMA into a ring of four raw tiles (with
+// the 32 row scales copied beside each), a conversion pass turns each tile's
+// fp8 bytes into bf16 exactly (v_cvt_scalef32_pk_bf16_fp8 at scale 1: every
+// e4m3fn value is a bf16 value), and the swizzled bf16 tile feeds the same
+// MFMA code as bf16 rows. The row scale s multiplies only the fp8 channels, so
+// the logit is s * (fp8-part dot) + (bf16-part dot) from two accumulators, and
+// the P operand is p * s for output channels 0..447 and p for 448..511.
+// ---------------------------------------------------------------------------
+constexpr int kMixRow = 576;                     // stored bytes per row
+constexpr int kRawRing = 4;
+constexpr int kRawTile = kTileRows * kMixRow;    // 18432 bytes = 18 copies of 1 KB
+constexpr int kRawSlot = kRawTile + 256;         // + 64 floats: row scales (32 used)
+
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Raw tile -> bf16 tile (row r's logical 16-byte slot c at physical slot
+// c ^ swz(r)). Work unit: one 16-byte raw chunk; 28 fp8 chunks and 8 bf16
+// chunks per row.
+__device__ __forceinline__ void convert_mixed_tile(const uint8_t* raw, uint16_t* X) {
+  char* xb = reinterpret_cast<char*>(X);
+  for (int u = threadIdx.x; u < kTileRows * 36; u += kAttThreads) {
+    const int r = u / 36, k = u - 36 * r;
+    const int sw = slot_swizzle(r);
+    const uint4 v = *reinterpret_cast<const uint4*>(raw + r * kMixRow + 16 * k);
+    char* row = xb + r * 1024;
+    if (k < 28) {
+      uint4 lo, hi;
+      lo.x = fp8x2_to_bf16x2<false>(v.x);
+      lo.y = fp8x2_to_bf16x2<true>(v.x);
+      lo.z = fp8x2_to_bf16x2<false>(v.y);
+      lo.w = fp8x2_to_bf16x2<true>(v.y);
+      hi.x = fp8x2_to_bf16x2<false>(v.z);
+      hi.y = fp8x2_to_bf16x2<true>(v.z);
+      hi.z = fp8x2_to_bf16x2<false>(v.w);
+      hi.w = fp8x2_to_bf16x2<true>(v.w);
+      *reinterpret_cast<uint4*>(row + 16 * ((2 * k) ^ sw)) = lo;
+      *reinterpret_cast<uint4*>(row + 16 * ((2 * k + 1) ^ sw)) = hi;
+    } else {
+      *reinterpret_cast<uint4*>(row + 16 * ((56 + k - 28) ^ sw)) = v;
+    }
+  }
+}
+
+__device__ __forceinline__ void softmax_update_mixed(const f32x4 (&sa)[2], const f32x4 (&sb)[2], int v0,
+                                                     const int32_t* rows, const float* rsc, float scale, int g,
+                                                     float& m_run, float& z_run, bool& flag, bf16x8& pa,
+                                                     bf16x8& pb) {
+  const int4 rv0 = *reinterpret_cast<const int4*>(rows + v0 + 4 * g);
+  const int4 rv1 = *reinterpret_cast<const int4*>(rows + v0 + 16 + 4 * g);
+  const float4 s0 = *reinterpret_cast<const float4*>(rsc + 4 * g);
+  const float4 s1 = *reinterpret_cast<const float4*>(rsc + 16 + 4 * g);
+  const int rr[8] = {rv0.x, rv0.y, rv0.z, rv0.w, rv1.x, rv1.y, rv1.z, rv1.w};
+  const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  float lg[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float l = rr[i] != -1 ? (sa[i >> 2][i & 3] * sc[i] + sb[i >> 2][i & 3]) * scale : -INFINITY;
+    lg[i] = l;
+    mx = fmaxf(mx, l);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (m_run == -INFINITY) m_run = mx;
+  flag = flag || (mx > m_run + kHeadroom);
+  float psum = 0.f;
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = lg[i] == -INFINITY ? 0.f : __expf(fminf(lg[i] - m_run, kHeadroom));
+    psum += p[i];
+  }
+  psum += __shfl_xor(psum, 16, 64);
+  psum += __shfl_xor(psum, 32, 64);
+  z_run += psum;
+  uint4 wa, wb;
+  wa.x = pack_bf16x2(p[0] * sc[0], p[1] * sc[1]);
+  wa.y = pack_bf16x2(p[2] * sc[2], p[3] * sc[3]);
+  wa.z = pack_bf16x2(p[4] * sc[4], p[5] * sc[5]);
+  wa.w = pack_bf16x2(p[6] * sc[6], p[7] * sc[7]);
+  wb.x = pack_bf16x2(p[0], p[1]);
+  wb.y = pack_bf16x2(p[2], p[3]);
+  wb.z = pack_bf16x2(p[4], p[5]);
+  wb.w = pack_bf16x2(p[6], p[7]);
+  pa = __builtin_bit_cast(bf16x8, wa);
+  pb = __builtin_bit_cast(bf16x8, wb);
+}
+
+__device__ __forceinline__ void tile_softmax_mixed(const uint16_t* X, const SwzOffsets& so, int v0,
+                                                   const int32_t* rows, const float* rsc, const bf16x8 (&qf)[16],
+                                                   float scale, int g, float& m_run, float& z_run, bool& flag,
+                                                   bf16x8& pa, bf16x8& pb) {
+  const char* xb = reinterpret_cast<const char*>(X);
+  f32x4 sa[2], sb[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j0 = 0; j0 < 4; j0 += 2) {
+      uint4 xa[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + (e >> 2), k = e & 3;
+        xa[e] = *reinterpret_cast<const uint4*>(xb + so.qk[k] + h2 * 16384 + 256 * j);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ks = 4 * (j0 + (e >> 2)) + (e & 3);          // K step: channels 32 ks .. 32 ks + 31
+        if (ks < 14) acc_a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[e]), qf[ks], acc_a, 0, 0, 0);
+        else acc_b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[e]), qf[ks], acc_b, 0, 0, 0);
+      }
+    }
+    sa[h2] = acc_a;
+    sb[h2] = acc_b;
+  }
+  softmax_update_mixed(sa, sb, v0, rows, rsc, scale, g, m_run, z_run, flag, pa, pb);
+}
+
+__device__ __forceinline__ void tile_pv_mixed(const uint16_t* X, const SwzOffsets& so, const bf16x8& pa,
+                                              const bf16x8& pb, f32x4 (&acc_o)[32]) {
+  const char* xb = reinterpret_cast<const char*>(X);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x8 af[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(xb + so.pv[k] + 256 * j));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(xb + so.pv[k] + 256 * j + 16384));
+      const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+      af[k] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)                    // channel tile 8j + k: fp8 part below 28
+      acc_o[8 * j + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[k], 8 * j + k < 28 ? pa : pb, acc_o[8 * j + k], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArgs a, SplitPlan sp,
+                                                                       float* __restrict__ part_o,
+                                                                       float* __restrict__ part_ml) {
+  constexpr int D = 512, KS = D / 32, DT = D / 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t Raw[kRawRing][kRawSlot];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kTileRows * D];
+  __shared__ __attribute__((aligned(16))) int32_t rows[kMaxSplitRows];
+  __shared__ float2 rope_tab[D / 2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  int split, hg, t;
+  if (!work_item(sp, a.Tq, blockIdx.x, split, hg, t)) return;
+  const int b = blockIdx.z;
+  const bool active = wid * 16 < sp.HG;
+  const int head = hg * sp.HG + wid * 16 + r16;
+  const RowSpan rs = row_span(a, t);
+  if (sp.S == 1) fill_rope_table(a, t, rope_tab);
+  const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
+  int64_t r_end = r_begin + sp.RS;
+  if (r_end > rs.nrows) r_end = rs.nrows;
+  const int nr = r_end > r_begin ? static_cast<int>(r_end - r_begin) : 0;
+
+  int32_t myrows[kMaxSplitRows / kAttThreads];
+#pragma unroll
+  for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) {
+    const int v = tid + kAttThreads * q;
+    myrows[q] = v < nr ? encode_row(a, b, t, rs, r_begin + v) : -1;
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) rows[tid + kAttThreads * q] = myrows[q];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int64_t win_rows = a.W - 1 + a.Tq;
+  const uint8_t* kvb = static_cast<const uint8_t*>(a.kv) + static_cast<int64_t>(b) * a.N_cap * kMixRow;
+  const uint8_t* winb = static_cast<const uint8_t*>(a.win) + static_cast<int64_t>(b) * win_rows * kMixRow;
+  const float* kvs = a.kv_scale + static_cast<int64_t>(b) * a.N_cap;
+  const float* wins = a.win_scale + static_cast<int64_t>(b) * win_rows;
+  // Tile copies: 18 of 1 KB (lane l of copy c fetches tile byte 1024 c + 16 l)
+  // and the 32 row scales (4 bytes per lane, twice so that every wave issues
+  // exactly five copies per tile). Absent rows copy window row 0.
+  auto issue = [&](int tile, int slot) {
+    const int v0 = tile * kTileRows;
+    uint8_t* base = &Raw[slot][0];
+#pragma unroll
+    for (int cc = 0; cc < 5; ++cc) {
+      const int c = wid * 5 + cc;
+      if (c < 18) {
+        const int q = c * 1024 + 16 * lane;
+        const int r = q / kMixRow, off = q - r * kMixRow;
+        const int v = v0 + r;
+        const int32_t sr = v < nr ? rows[v] : -1;
+        const uint8_t* rowp = sr >= 0 ? kvb + static_cast<int64_t>(sr) * kMixRow
+                                      : winb + (sr == -1 ? 0 : static_cast<int64_t>(-2 - sr) * kMixRow);
+        lds_copy16(rowp + off, lds_address(base) + c * 1024);
+      } else {
+        const int v = v0 + (lane < kTileRows ? lane : 0);
+        const int32_t sr = v < nr ? rows[v] : -1;
+        const float* sp_ = sr >= 0 ? kvs + sr : wins + (sr == -1 ? 0 : -2 - sr);
+        lds_copy4(sp_, lds_address(base + kRawTile));
+      }
+    }
+  };
+  const int ntiles = (nr + kTileRows - 1) / kTileRows;
+#pragma unroll
+  for (int t0 = 0; t0 < 3; ++t0)
+    if (t0 < ntiles) issue(t0, t0);
+  bf16x8 qf[KS];
+  if (active) {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+  }
+  f32x4 acc_o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, z_run = 0.f;
+  const SwzOffsets so = swz_offsets(g, r16);
+  __builtin_amdgcn_s_waitcnt(0);                   // tiles 0..2 and the query fragments
+  __builtin_amdgcn_s_barrier();
+  if (0 < ntiles) convert_mixed_tile(&Raw[0][0], Xs[0]);
+
+  // Step it: (raw tile it+1 landed, everyone past tile it-1) -> refill the raw
+  // slot of tile it-1 with tile it+3 -> convert tile it+1 -> consume tile it.
+  bool flag = false;
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) {
+      if (it + 2 < ntiles) wait_vmcnt<5>();        // tile it+2's copies may stay in flight
+      else wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+    if (it + 3 < ntiles) issue(it + 3, (it + 3) % kRawRing);
+    if (it + 1 < ntiles) convert_mixed_tile(&Raw[(it + 1) % kRawRing][0], Xs[(it + 1) & 1]);
+    bf16x8 pa, pb;
+    tile_softmax_mixed(Xs[it & 1], so, it * kTileRows, rows,
+                       reinterpret_cast<const float*>(&Raw[it % kRawRing][kRawTile]), qf, a.scale, g, m_run,
+                       z_run, flag, pa, pb);
+    tile_pv_mixed(Xs[it & 1], so, pa, pb, acc_o);
   }
 
   if (active) {
@@ -1049,12 +1287,14 @@ SplitPlan make_plan(const AttendArgs& a) {
 template <int D>
 void launch_mfma_d(LaunchScope& sc, const AttendArgs& a, const SplitPlan& sp, float* po, float* pml) {
   dim3 grid(static_cast<uint32_t>(work_blocks(sp, a.Tq)), 1, a.B), block(kAttThreads);
-  if (a.dt_kv == LCA_KV_MIXED)
-    sc.launch(attend_mfma_kernel<D, true>, grid, block, 0, a, sp, po, pml);
-  else if constexpr (D == 512)
-    sc.launch(attend_dma_kernel, grid, block, 0, a, sp, po, pml);
-  else
-    sc.launch(attend_mfma_kernel<D, false>, grid, block, 0, a, sp, po, pml);
+  if constexpr (D == 512) {                        // KV_MIXED rows exist only at D = 512
+    if (a.dt_kv == LCA_KV_MIXED)
+      sc.launch(attend_mixed_dma_kernel, grid, block, 0, a, sp, po, pml);
+    else
+      sc.launch(attend_dma_kernel, grid, block, 0, a, sp, po, pml);
+  } else {
+    sc.launch(attend_mfma_kernel<D>, grid, block, 0, a, sp, po, pml);
+  }
 }
 
 }  // namespace

@@ -91,6 +91,14 @@ __device__ __forceinline__ void lds_copy16(const void* gptr, uint32_t lds_addr) 
                : "memory", "m0");
 }
 
+// Same, 4 bytes per lane: lane l's dword at `gptr` lands at lds_addr + 4 * l.
+__device__ __forceinline__ void lds_copy4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(gptr)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) const void*)(p)));

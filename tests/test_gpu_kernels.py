@@ -443,23 +443,26 @@ def test_attend_window_clipped_and_no_entries():
     row_tol_check(host(out)[0], ref, 2e-2, "clipped window")
 
 
-def test_attend_mixed_kv_matches_oracle():
+@pytest.mark.parametrize("Tq", [1, 16])
+def test_attend_mixed_kv_matches_oracle(Tq):
+    # 16 queries x 128 heads: one split per query (output written by the kernel)
     L = need_gpu()
     rng = np.random.default_rng(42)
-    B, Tq, H, D, W, m, k = 2, 1, 128, 512, 128, 4, 200
+    B, H, D, W, m, k = 2, 128, 512, 128, 4, 200
     q_pos0 = 4 * 3000
-    N_cap = 3001
+    N_cap = (q_pos0 + Tq) // m + 1
     q = WL.bf16_exact((rng.standard_normal((B, Tq, H, D)) * 10 / np.sqrt(D)).astype(np.float32))
     Esrc = (rng.standard_normal((B, N_cap, D)) / np.sqrt(D)).astype(np.float32)
-    wsrc = (rng.standard_normal((B, W, D)) / np.sqrt(D)).astype(np.float32)
+    wsrc = (rng.standard_normal((B, W - 1 + Tq, D)) / np.sqrt(D)).astype(np.float32)
     sink = rng.standard_normal(H).astype(np.float32)
     Eq = torch.empty((B, N_cap, D + 64), dtype=torch.uint8, device=DEV)
     Es = torch.empty((B, N_cap), dtype=torch.float32, device=DEV)
-    Wq = torch.empty((B, W, D + 64), dtype=torch.uint8, device=DEV)
-    Ws = torch.empty((B, W), dtype=torch.float32, device=DEV)
+    Wq = torch.empty((B, W - 1 + Tq, D + 64), dtype=torch.uint8, device=DEV)
+    Ws = torch.empty((B, W - 1 + Tq), dtype=torch.float32, device=DEV)
     L.lca_quantize_rows(L.KV_MIXED, dev_f32(Esrc), Eq, Es)
     L.lca_quantize_rows(L.KV_MIXED, dev_f32(wsrc), Wq, Ws)
-    idx = np.stack([np.sort(rng.choice(3001, size=k, replace=False)) for _ in range(B)])[:, None].astype(np.int32)
+    idx = np.stack([np.stack([np.sort(rng.choice(3000, size=k, replace=False)) for _ in range(Tq)])
+                    for _ in range(B)]).astype(np.int32)
     out = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=DEV)
     L.csa_attend(L.BF16, L.KV_MIXED, dev_bf16(q), Eq, torch.from_numpy(idx).to(DEV), Wq, dev_f32(sink), out,
                  m=m, W=W, q_pos0=q_pos0, scale=1 / math.sqrt(D), kv_scale=Es, win_scale=Ws,
