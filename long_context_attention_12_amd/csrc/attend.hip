@@ -1210,6 +1210,100 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int S, int R
   combine_row(a, S, RS, blockIdx.z, blockIdx.y, blockIdx.x, part_o, part_ml, sml, red, lc);
 }
 
+// Four heads per workgroup, one wave per head: lane l owns channels
+// 8l .. 8l + 7 and streams two float4 of every split's partial, so each lane
+// keeps 2S loads in flight. A workgroup whose heads hold a flagged split (max
+// NaN) merges them with combine_row instead, which recomputes that split.
+__global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int RS,
+                                                       const float* __restrict__ part_o,
+                                                       const float* __restrict__ part_ml) {
+  __shared__ float sml[2 * 256];
+  __shared__ float red[4];
+  __shared__ float lc[kCombMaxRows];
+  __shared__ float2 rope_tab[256];
+  __shared__ uint32_t any_nan;
+  const int t = blockIdx.y, b = blockIdx.z, wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int D = a.D, h0 = blockIdx.x * 4, h = h0 + wid;
+  if (threadIdx.x == 0) any_nan = 0u;
+  fill_rope_table(a, t, rope_tab);
+  __syncthreads();
+  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + h;
+  const bool live = h < a.H;
+  if (live)
+    for (int i = lane; i < S; i += 64) {
+      const float m = part_ml[(row * S + i) * 2];
+      if (m != m) any_nan = 1u;
+    }
+  __syncthreads();
+  if (any_nan) {                                    // rare: exact path, head by head
+    for (int hh = h0; hh < min(h0 + 4, a.H); ++hh)
+      combine_row(a, S, RS, b, t, hh, part_o, part_ml, sml, red, lc);
+    return;
+  }
+  if (!live) return;
+  const bool own = 8 * lane < D;
+  const float* ml = part_ml + row * S * 2;
+  const float* po = part_o + row * S * D + 8 * lane;
+  const float sink = a.sink[h];
+  float M = sink;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+  float Z = __expf(sink - M);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float4 v[8][2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = own && s0 + j < S;
+      v[j][0] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[j][1] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < S) {
+        const float ms = ml[2 * (s0 + j)];
+        const float w = ms == -INFINITY ? 0.f : __expf(ms - M);
+        Z += w * ml[2 * (s0 + j) + 1];
+        acc[0] = fmaf(w, v[j][0].x, acc[0]);
+        acc[1] = fmaf(w, v[j][0].y, acc[1]);
+        acc[2] = fmaf(w, v[j][0].z, acc[2]);
+        acc[3] = fmaf(w, v[j][0].w, acc[3]);
+        acc[4] = fmaf(w, v[j][1].x, acc[4]);
+        acc[5] = fmaf(w, v[j][1].y, acc[5]);
+        acc[6] = fmaf(w, v[j][1].z, acc[6]);
+        acc[7] = fmaf(w, v[j][1].w, acc[7]);
+      }
+    }
+  }
+  if (lane == 0 && a.lse_out) a.lse_out[row] = M + logf(Z);
+  if (!own) return;
+  const float inv = 1.f / Z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] *= inv;
+  const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
+  const int c0 = 8 * lane;
+  if (c0 >= D - R) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float2 cs = rope_tab[(c0 + 2 * p - (D - R)) / 2];
+      const float x = acc[2 * p], y = acc[2 * p + 1];
+      acc[2 * p] = x * cs.x - y * cs.y;
+      acc[2 * p + 1] = x * cs.y + y * cs.x;
+    }
+  }
+  if (a.dt_q == LCA_F32) {
+    float* o = static_cast<float*>(a.out) + row * D + c0;
+    *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  } else {
+    uint4 w;
+    w.x = pack_bf16x2(acc[0], acc[1]);
+    w.y = pack_bf16x2(acc[2], acc[3]);
+    w.z = pack_bf16x2(acc[4], acc[5]);
+    w.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + row * D + c0) = w;
+  }
+}
+
 // One split per query: the attention kernel wrote every head's output itself
 // and left (max) = +inf, except for heads whose logits outgrew the in-kernel
 // headroom (max = NaN). One workgroup per (b, t) recomputes those exactly.
@@ -1336,8 +1430,8 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
       scope.launch(fixup_kernel, dim3(a.Tq, a.B), cb, 0, a, sp.RS, static_cast<const float*>(po),
                    static_cast<const float*>(pml));
     else
-      scope.launch(combine_kernel, dim3(a.H, a.Tq, a.B), cb, 0, a, sp.S, sp.RS, static_cast<const float*>(po),
-                   static_cast<const float*>(pml));
+      scope.launch(combine4_kernel, dim3((a.H + 3) / 4, a.Tq, a.B), dim3(256), 0, a, sp.S, sp.RS,
+                   static_cast<const float*>(po), static_cast<const float*>(pml));
     return hipGetLastError();
   }
 }
