@@ -423,29 +423,77 @@ __device__ __forceinline__ void load_round(const float* __restrict__ s, int64_t 
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
-    const float* __restrict__ scores, int64_t ld, int64_t N_cap, int Tq, int t_off, int Tc,
-    int64_t q_pos0, int m, int k, bool key16, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out) {
-  __shared__ uint32_t hist[kMaxBins];
-  __shared__ __attribute__((aligned(16))) uint32_t wsum[kSelThreads / 64];
-  __shared__ uint32_t sh_digit, sh_krem;
+// Histogram of one digit is in hist[0, nb); find the digit whose bin holds the
+// krem-th largest element (bins scanned in descending digit order) and that
+// element's rank inside the bin. Four bins per thread; on return the result
+// is visible to the whole block.
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, uint32_t krem, uint32_t* wsum,
+                                           uint32_t* sh_digit, uint32_t* sh_krem) {
   const int tid = threadIdx.x;
+  uint32_t c[4], tsum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int d = nb - 1 - (4 * tid + q);
+    c[q] = d >= 0 ? hist[d] : 0u;
+    tsum += c[q];
+  }
+  uint32_t total;
+  const uint32_t before = block_excl_scan(tsum, wsum, &total);
+  if (before < krem && before + tsum >= krem) {
+    uint32_t cum = before;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (cum < krem && cum + c[q] >= krem) {
+        *sh_digit = static_cast<uint32_t>(nb - 1 - (4 * tid + q));
+        *sh_krem = krem - cum;
+      }
+      cum += c[q];
+    }
+  }
+  __syncthreads();
+}
+
+// Row of one query: where its scores are, how many are visible, where its
+// k indices (and optionally scores) go.
+struct SelRow {
+  const float* s;
+  int64_t n;
+  int32_t* io;
+  float* so;
+};
+
+__device__ __forceinline__ SelRow sel_row(const float* scores, int64_t ld, int64_t N_cap, int Tq, int t_off, int Tc,
+                                          int64_t q_pos0, int m, int k, int32_t* idx_out, float* score_out) {
   const int b = blockIdx.y, tl = blockIdx.x, t = t_off + tl;
   int64_t n = n_visible(q_pos0 + t, m);
   if (n > N_cap) n = N_cap;
-  const float* s = scores + (static_cast<int64_t>(b) * Tc + tl) * ld;
-  int32_t* io = idx_out + (static_cast<int64_t>(b) * Tq + t) * k;
-  float* so = score_out ? score_out + (static_cast<int64_t>(b) * Tq + t) * k : nullptr;
+  SelRow r;
+  r.s = scores + (static_cast<int64_t>(b) * Tc + tl) * ld;
+  r.n = n;
+  r.io = idx_out + (static_cast<int64_t>(b) * Tq + t) * k;
+  r.so = score_out ? score_out + (static_cast<int64_t>(b) * Tq + t) * k : nullptr;
+  return r;
+}
 
-  if (n <= k) {
-    for (int i = tid; i < k; i += kSelThreads) {
-      io[i] = i < n ? i : -1;
-      if (so) so[i] = i < n ? s[i] : -INFINITY;
-    }
-    return;
+// Fewer visible entries than k: all of them, then -1 padding.
+__device__ __forceinline__ void select_all(const SelRow& r, int k) {
+  for (int i = threadIdx.x; i < k; i += kSelThreads) {
+    r.io[i] = i < r.n ? i : -1;
+    if (r.so) r.so[i] = i < r.n ? r.s[i] : -INFINITY;
   }
+}
 
+// Radix select by full passes over the scores: one per digit, then one that
+// writes the output. A list that fits one register round is read only once.
+__device__ __forceinline__ void select_by_passes(const SelRow& row, int k, bool key16, uint32_t* hist, uint32_t* wsum,
+                                                 uint32_t* sh_digit_p, uint32_t* sh_krem_p) {
+  uint32_t& sh_digit = *sh_digit_p;
+  uint32_t& sh_krem = *sh_krem_p;
+  const int tid = threadIdx.x;
+  const float* s = row.s;
+  const int64_t n = row.n;
+  int32_t* io = row.io;
+  float* so = row.so;
   const int rounds = static_cast<int>((n + kRound - 1) / kRound);
   uint32_t key[kSelItems];
   if (rounds == 1) load_round(s, n, 0, key16, key);     // kept in registers for every pass
@@ -468,28 +516,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
         if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
-    // bins in descending digit order: thread owns 4 consecutive of them
-    uint32_t c[4], tsum = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d = nb - 1 - (4 * tid + q);
-      c[q] = d >= 0 ? hist[d] : 0u;
-      tsum += c[q];
-    }
-    uint32_t total;
-    const uint32_t before = block_excl_scan(tsum, wsum, &total);
-    if (before < krem && before + tsum >= krem) {
-      uint32_t cum = before;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (cum < krem && cum + c[q] >= krem) {
-          sh_digit = static_cast<uint32_t>(nb - 1 - (4 * tid + q));
-          sh_krem = krem - cum;
-        }
-        cum += c[q];
-      }
-    }
-    __syncthreads();
+    find_digit(hist, nb, krem, wsum, &sh_digit, &sh_krem);
     prefix |= sh_digit << shift;
     pmask |= static_cast<uint32_t>(nb - 1) << shift;
     krem = sh_krem;
@@ -532,6 +559,193 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
 }
 
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const float* __restrict__ scores, int64_t ld, int64_t N_cap, int Tq, int t_off, int Tc,
+    int64_t q_pos0, int m, int k, bool key16, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
+  __shared__ uint32_t hist[kMaxBins];
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[kSelThreads / 64];
+  __shared__ uint32_t sh_digit, sh_krem;
+  const SelRow row = sel_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, m, k, idx_out, score_out);
+  if (row.n <= k) {
+    select_all(row, k);
+    return;
+  }
+  select_by_passes(row, k, key16, hist, wsum, &sh_digit, &sh_krem);
+}
+
+// Number of entries of the increasing array a[0, n) that are < x.
+__device__ __forceinline__ int count_below(const int32_t* a, int n, int32_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+constexpr int kMaxK = 4096;        // largest k the library accepts
+constexpr int kLongCap = 8192;     // boundary-bin candidates held in LDS
+
+// Lists longer than one register round, in two reads of the scores instead of
+// one per digit plus one for the output. Read 1 builds the first (12-bit)
+// digit's histogram, which fixes the boundary bin b* and how many of its
+// entries are taken. Read 2 puts the indices above b* and the (key, index)
+// pairs inside b* into LDS, both in increasing index order (block scans). The
+// remaining digits are resolved on the candidates alone, and the two sorted
+// lists are merged into the output: the same set and order as the pass-based
+// select. Candidates past kLongCap (a bin crowded by ties, e.g. the exact
+// zeros of a query whose head weights are all negative) keep only their index,
+// in the row's spill buffer (ld entries), and their key is read again from the
+// scores.
+__global__ __launch_bounds__(kSelThreads) void topk_select_long_kernel(
+    const float* __restrict__ scores, int64_t ld, int32_t* __restrict__ spill, int64_t N_cap, int Tq, int t_off,
+    int Tc, int64_t q_pos0, int m, int k, bool key16, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
+  __shared__ uint32_t hist[kMaxBins];
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[kSelThreads / 64];
+  __shared__ uint32_t sh_digit, sh_krem, sh_cmin, sh_cmax;
+  __shared__ int32_t a_idx[kMaxK];        // above b*, increasing index
+  __shared__ int32_t w_idx[kMaxK];        // winners inside b*, increasing index
+  __shared__ uint32_t c_key[kLongCap];    // candidates inside b*, increasing index
+  __shared__ int32_t c_idx[kLongCap];
+  const int tid = threadIdx.x;
+  const SelRow row = sel_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, m, k, idx_out, score_out);
+  if (row.n <= k) {
+    select_all(row, k);
+    return;
+  }
+  const float* s = row.s;
+  const int64_t n = row.n;
+  int32_t* sp = spill + (static_cast<int64_t>(blockIdx.y) * Tc + blockIdx.x) * ld;   // candidate kLongCap + i at sp[i]
+  const int rounds = static_cast<int>((n + kRound - 1) / kRound);
+  const int sh0 = (key16 ? 16 : 32) - 12;
+  uint32_t key[kSelItems];
+
+  // read 1: first digit
+  for (int i = tid; i < kMaxBins; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  for (int r = 0; r < rounds; ++r) {
+    load_round(s, n, static_cast<int64_t>(r) * kRound, key16, key);
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j)
+      if (key[j] != 0u) atomicAdd(&hist[key[j] >> sh0], 1u);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    sh_cmin = 0xffffffffu;
+    sh_cmax = 0u;
+  }
+  find_digit(hist, kMaxBins, static_cast<uint32_t>(k), wsum, &sh_digit, &sh_krem);
+  const uint32_t bstar = sh_digit, krem1 = sh_krem;
+  uint32_t cmin = 0xffffffffu, cmax = 0u;     // candidate key range, this thread
+
+  // read 2: entries above b* and candidates inside it, in index order
+  uint32_t run_a = 0, run_c = 0;
+  for (int r = 0; r < rounds; ++r) {
+    const int64_t base = static_cast<int64_t>(r) * kRound;
+    load_round(s, n, base, key16, key);
+    uint32_t am = 0, cm = 0;
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+      const uint32_t d = key[j] >> sh0;
+      am |= static_cast<uint32_t>(key[j] != 0u && d > bstar) << j;
+      cm |= static_cast<uint32_t>(key[j] != 0u && d == bstar) << j;
+    }
+    uint32_t tot;   // both counts < 2^16 per round
+    const uint32_t pre = block_excl_scan((static_cast<uint32_t>(__builtin_popcount(am)) << 16) |
+                                         static_cast<uint32_t>(__builtin_popcount(cm)), wsum, &tot);
+    uint32_t pa = run_a + (pre >> 16), pc = run_c + (pre & 0xffffu);
+    const int32_t i0 = static_cast<int32_t>(base) + tid * kSelItems;
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j) {
+      if ((am >> j) & 1u) a_idx[pa++] = i0 + j;
+      if ((cm >> j) & 1u) {
+        cmin = min(cmin, key[j]);
+        cmax = max(cmax, key[j]);
+        if (pc < static_cast<uint32_t>(kLongCap)) {
+          c_key[pc] = key[j];
+          c_idx[pc] = i0 + j;
+        } else {
+          sp[pc - kLongCap] = i0 + j;
+        }
+        ++pc;
+      }
+    }
+    run_a += tot >> 16;
+    run_c += tot & 0xffffu;
+  }
+  if (cmin <= cmax) {
+    atomicMin(&sh_cmin, cmin);
+    atomicMax(&sh_cmax, cmax);
+  }
+  __syncthreads();
+  const int nc = static_cast<int>(run_c);
+  const int n_w = static_cast<int>(krem1), n_a = k - n_w;
+  if (sh_cmin == sh_cmax) {
+    // one key fills the boundary bin (exact ties, e.g. zeros): the winners
+    // are its first krem1 entries in index order, all held in LDS
+    for (int i = tid; i < n_w; i += kSelThreads) w_idx[i] = c_idx[i];
+    __syncthreads();
+  } else {
+    // candidate i: from LDS, or from the spill buffer with its key read again
+    auto cand_idx = [&](int i) { return i < kLongCap ? c_idx[i] : sp[i - kLongCap]; };
+    auto cand_key = [&](int i) { return i < kLongCap ? c_key[i] : score_key(s[sp[i - kLongCap]], key16); };
+
+    // remaining digits on the candidates
+    uint32_t prefix = bstar << sh0, pmask = 0xfffu << sh0, krem = krem1;
+    int shift = sh0;
+    while (shift > 0) {
+      const int wd = shift >= 10 ? 10 : shift;
+      shift -= wd;
+      const int nb = 1 << wd;
+      for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < nc; i += kSelThreads) {
+        const uint32_t kk = cand_key(i);
+        if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & (nb - 1)], 1u);
+      }
+      __syncthreads();
+      find_digit(hist, nb, krem, wsum, &sh_digit, &sh_krem);
+      prefix |= sh_digit << shift;
+      pmask |= static_cast<uint32_t>(nb - 1) << shift;
+      krem = sh_krem;
+      __syncthreads();
+    }
+    const uint32_t thr = prefix;
+
+    // winners inside b* in index order: above thr, then the first krem equal to it
+    uint32_t run_gt = 0, run_eq = 0;
+    for (int c0 = 0; c0 < nc; c0 += kSelThreads) {
+      const int i = c0 + tid;
+      const uint32_t kk = i < nc ? cand_key(i) : 0u;
+      const uint32_t gt = i < nc && kk > thr, eq = i < nc && kk == thr;
+      uint32_t tot;
+      const uint32_t pre = block_excl_scan((gt << 16) | eq, wsum, &tot);
+      const uint32_t eq_rank = run_eq + (pre & 0xffffu);
+      if (gt || (eq && eq_rank < krem)) w_idx[run_gt + (pre >> 16) + min(eq_rank, krem)] = cand_idx(i);
+      run_gt += tot >> 16;
+      run_eq += tot & 0xffffu;
+    }
+    __syncthreads();
+  }
+
+  // merge the two increasing lists
+  for (int i = tid; i < n_a; i += kSelThreads) {
+    const int32_t x = a_idx[i];
+    const int pos = i + count_below(w_idx, n_w, x);
+    row.io[pos] = x;
+    if (row.so) row.so[pos] = s[x];
+  }
+  for (int i = tid; i < n_w; i += kSelThreads) {
+    const int32_t x = w_idx[i];
+    const int pos = i + count_below(a_idx, n_a, x);
+    row.io[pos] = x;
+    if (row.so) row.so[pos] = s[x];
+  }
+}
+
 template <int HI>
 void launch_score_bf16_hi(LaunchScope& ls, const IndexArgs& a, float* sc, int64_t ld, int t_off, int Tc,
                           dim3 grid) {
@@ -562,14 +776,20 @@ int query_chunk(const IndexArgs& a) {
 
 }  // namespace
 
+// Workspace: the chunk's scores [B, Tc, ld] (float32); for lists longer than
+// one register round, then the select's spill buffer [B, Tc, ld] (int32).
+bool long_lists(const IndexArgs& a) { return a.N_cap > kRound; }
+
 size_t index_topk_workspace(const IndexArgs& a) {
-  return static_cast<size_t>(a.B) * query_chunk(a) * score_ld(a) * sizeof(float) + 256;
+  const size_t cells = static_cast<size_t>(a.B) * query_chunk(a) * score_ld(a);
+  return cells * (sizeof(float) + (long_lists(a) ? sizeof(int32_t) : 0)) + 256;
 }
 
 hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t) {
   float* sc = static_cast<float*>(ws);
   const int Tc = query_chunk(a);
   const int64_t ld = score_ld(a);
+  int32_t* spill = reinterpret_cast<int32_t*>(sc + static_cast<int64_t>(a.B) * Tc * ld);
   const bool key16 = (a.flags & LCA_SCORE_BF16) != 0;
   for (int t_off = 0; t_off < a.Tq; t_off += Tc) {
     const int tcn = min(Tc, a.Tq - t_off);
@@ -634,8 +854,13 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
     }
     {
       LaunchScope scope(s, "topk_select");
-      scope.launch(topk_select_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, static_cast<const float*>(sc), ld, a.N_cap,
-                         a.Tq, t_off, Tc, a.q_pos0, a.m, a.k, key16, a.idx_out, a.score_out);
+      // every row's list is at most nv_max long (and nv_max > kRound implies N_cap > kRound)
+      if (nv_max > kRound)
+        scope.launch(topk_select_long_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, static_cast<const float*>(sc), ld,
+                     spill, a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.m, a.k, key16, a.idx_out, a.score_out);
+      else
+        scope.launch(topk_select_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, static_cast<const float*>(sc), ld,
+                     a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.m, a.k, key16, a.idx_out, a.score_out);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

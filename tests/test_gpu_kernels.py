@@ -251,22 +251,24 @@ def test_index_topk_many_queries_from_sequence_start():
 
 
 @pytest.mark.parametrize("bf16_scores", [False, True])
-@pytest.mark.parametrize("crowded", [False, True])
-def test_index_topk_long_lists(bf16_scores, crowded):
-    # lists longer than one register round (32768) take the bounded path (group
-    # maxima -> lower bound -> candidates in LDS); crowded keys (few distinct
-    # scores) overflow the candidate buffer and fall back to full passes
+@pytest.mark.parametrize("distinct", [None, 40, 6])
+def test_index_topk_long_lists(bf16_scores, distinct):
+    # lists longer than one register round (32768) take the two-read select:
+    # first-digit histogram, then the boundary bin's entries as candidates in
+    # LDS. 40 distinct keys: ~2500 tied candidates, resolved in LDS. 6 distinct
+    # keys: ~16700 in the boundary bin, more than LDS holds -> full passes.
     L = need_gpu()
-    rng = np.random.default_rng(70 + 2 * crowded + bf16_scores)
+    crowded = distinct is not None
+    rng = np.random.default_rng(70 + 2 * (distinct or 0) + bf16_scores)
     B, Tq, H_I, d_I, m, k = 2, 1, 4, 128, 4, 1024
     N_cap = 100003
     q_pos0 = 4 * 100000 + 1                   # n_vis = 100000: four rounds, ragged
     qI, w, kI = _index_case(rng, B, Tq, H_I, d_I, N_cap)
     if crowded:
-        kI = WL.bf16_exact(kI[:, rng.integers(0, 40, size=N_cap)])   # 40 distinct keys
+        kI = WL.bf16_exact(kI[:, rng.integers(0, distinct, size=N_cap)])
     idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
     sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
-    say(f"long list bf16={bf16_scores} crowded={crowded}")
+    say(f"long list bf16={bf16_scores} distinct={distinct}")
     L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
                      flags=L.SCORE_BF16 if bf16_scores else 0, score_out=sco)
     torch.cuda.synchronize()
