@@ -245,47 +245,211 @@ __device__ __forceinline__ SwzOffsets swz_offsets(int g, int r16) {
   return o;
 }
 
-__device__ __forceinline__ void tile_softmax_swz(const uint16_t* X, const SwzOffsets& so, int v0,
-                                                 const int32_t* rows, const bf16x8 (&qf)[16], float scale,
-                                                 int g, float& m_run, float& z_run, bool& flag, bf16x8& pf) {
-  const char* xb = reinterpret_cast<const char*>(X);
-  f32x4 sacc[2];
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j0 = 0; j0 < 4; j0 += 2) {
-      uint4 xa[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = j0 + (e >> 2), k = e & 3;
-        xa[e] = *reinterpret_cast<const uint4*>(xb + so.qk[k] + h2 * 16384 + 256 * j);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[e]), qf[4 * (j0 + (e >> 2)) + (e & 3)], acc, 0, 0, 0);
-    }
-    sacc[h2] = acc;
-  }
-  softmax_update(sacc, v0, rows, scale, g, m_run, z_run, flag, pf);
+// Reductions across lanes l and l ^ 16, l and l ^ 32 with the gfx950 lane
+// swaps (VALU only: no LDS operation that would queue behind LDS reads in
+// flight). Each swap returns the pair {x[l], x[l ^ 16 or 32]} in a fixed
+// order, so both lanes of a pair compute the same value.
+__device__ __forceinline__ float pair_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ void tile_pv_swz(const uint16_t* X, const SwzOffsets& so, const bf16x8& pf,
-                                            f32x4 (&acc_o)[32]) {
+// Online-softmax update as softmax_update, with the row table entries already
+// in registers and the reductions done by lane swaps.
+__device__ __forceinline__ void softmax_update_regs(const f32x4 (&sacc)[2], const int4 (&rv)[2], float scale,
+                                                    float& m_run, float& z_run, bool& flag, bf16x8& pf) {
+  const int rr[8] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w, rv[1].x, rv[1].y, rv[1].z, rv[1].w};
+  float lg[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float l = rr[i] != -1 ? sacc[i >> 2][i & 3] * scale : -INFINITY;
+    lg[i] = l;
+    mx = fmaxf(mx, l);
+  }
+  mx = pair_max32(pair_max16(mx));
+  if (m_run == -INFINITY) m_run = mx;              // first non-empty tile sets the reference
+  flag = flag || (mx > m_run + kHeadroom);
+  float psum = 0.f;
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = lg[i] == -INFINITY ? 0.f : __expf(fminf(lg[i] - m_run, kHeadroom));
+    psum += p[i];
+  }
+  z_run += pair_sum32(pair_sum16(psum));
+  uint4 pw;
+  pw.x = pack_bf16x2(p[0], p[1]);
+  pw.y = pack_bf16x2(p[2], p[3]);
+  pw.z = pack_bf16x2(p[4], p[5]);
+  pw.w = pack_bf16x2(p[6], p[7]);
+  pf = __builtin_bit_cast(bf16x8, pw);
+}
+
+// Stages of one 32-row tile for one wave (16 heads) on the swizzled D = 512
+// layout. qk_load: the row-table entries and the 32 S^T fragments (fragment
+// f = 16 h2 + s: rows 16 h2 .. 16 h2 + 15, K step s). qk_mfma: S^T = X Q^T,
+// two independent accumulation chains (the row halves). pv_load: the 32 X^T
+// fragments (channel tile dt). pv_mfma: O^T += X^T P^T.
+__device__ __forceinline__ void qk_load(const uint16_t* X, const SwzOffsets& so, const int32_t* rows, int v0, int g,
+                                        bf16x8 (&xf)[32], int4 (&rv)[2]) {
+  const char* xb = reinterpret_cast<const char*>(X);
+  rv[0] = *reinterpret_cast<const int4*>(rows + v0 + 4 * g);
+  rv[1] = *reinterpret_cast<const int4*>(rows + v0 + 16 + 4 * g);
+#pragma unroll
+  for (int f = 0; f < 32; ++f) {
+    const int h2 = f >> 4, st = f & 15;
+    xf[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xb + so.qk[st & 3] + h2 * 16384 + 256 * (st >> 2)));
+  }
+}
+
+__device__ __forceinline__ void qk_mfma(const bf16x8 (&xf)[32], const bf16x8 (&qf)[16], f32x4 (&sacc)[2]) {
+  sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 16; ++st)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+      sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[16 * h2 + st], qf[st], sacc[h2], 0, 0, 0);
+}
+
+template <int DT0 = 0, int NDT = 32>
+__device__ __forceinline__ void pv_load(const uint16_t* X, const SwzOffsets& so, bf16x8 (&vf)[NDT]) {
   const char* xb = reinterpret_cast<const char*>(X);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    bf16x8 af[8];
+  for (int i = 0; i < NDT; ++i) {
+    const int dt = DT0 + i;
+    const int j = dt >> 3, k = dt & 7;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(xb + so.pv[k] + 256 * j));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(xb + so.pv[k] + 256 * j + 16384));
+    const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+    vf[i] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+  }
+}
+
+template <int DT0 = 0, int NDT = 32>
+__device__ __forceinline__ void pv_mfma(const bf16x8 (&vf)[NDT], const bf16x8& pf, f32x4 (&acc_o)[32]) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(xb + so.pv[k] + 256 * j));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(xb + so.pv[k] + 256 * j + 16384));
-      const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
-      af[k] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+  for (int i = 0; i < NDT; ++i)
+    acc_o[DT0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[i], pf, acc_o[DT0 + i], 0, 0, 0);
+}
+
+// Steady state of the tile pipeline: S^T of the next tile and the output
+// update of the current one. With one wave per SIMD nothing else hides a wait,
+// so the wave itself overlaps the units:
+//   1. LDS reads: the next tile's S^T fragments, then the first half of this
+//      tile's X^T fragments;
+//   2. the next tile's S^T MFMAs interleaved with this tile's softmax on the
+//      VALU (the matrix core runs one MFMA while the wave issues several VALU
+//      instructions);
+//   3. one wait for all LDS reads (long landed by then; the LDS counter is
+//      in-order, so a later partial wait would also wait for younger reads),
+//      the second half's reads into the registers the S^T fragments freed,
+//      and the 32 PV MFMAs.
+// The sched_barrier fences keep each group in its place; the group barriers
+// ask for the MFMA / VALU interleave.
+__device__ __forceinline__ void tile_pipe_step(const uint16_t* Xc, const uint16_t* Xn, const SwzOffsets& so,
+                                               const int32_t* rows, int v0n, int g, const bf16x8 (&qf)[16],
+                                               float scale, f32x4 (&sacc)[2], int4 (&rv)[2], float& m_run,
+                                               float& z_run, bool& flag, f32x4 (&acc_o)[32]) {
+  f32x4 sn[2];
+  int4 rvn[2];
+  bf16x8 va[16], pf;
+  {
+    bf16x8 xf[32];
+    qk_load(Xn, so, rows, v0n, g, xf, rvn);
+    pv_load<0, 16>(Xc, so, va);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_mfma(xf, qf, sn);
+    softmax_update_regs(sacc, rv, scale, m_run, z_run, flag, pf);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then up to four VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_lgkmcnt0();
+  bf16x8 vb[16];
+  pv_load<16, 16>(Xc, so, vb);
+  pv_mfma<0, 16>(va, pf, acc_o);
+  pv_mfma<16, 16>(vb, pf, acc_o);
+  sacc[0] = sn[0];
+  sacc[1] = sn[1];
+  rv[0] = rvn[0];
+  rv[1] = rvn[1];
+}
+
+// One tile for a wave serving 32 heads (two 16-head tiles): every X fragment
+// read from LDS feeds two MFMAs, halving LDS reads per FLOP (the LDS is the
+// limit of the 16-head form: its reads of a 32-row tile take longer than its
+// MFMAs). Fragments stream four ahead of the MFMAs that consume them; the
+// group barriers fix that order (left alone, the compiler pairs each read with
+// its MFMA and waits on every read). S^T fragments go in the order
+// (K step s, row half h2) so that four accumulation chains alternate.
+__device__ __forceinline__ void tile_step_32(const uint16_t* X, const SwzOffsets& so, int v0, const int32_t* rows,
+                                             const bf16x8 (&qf)[2][16], float scale, int g, float (&m_run)[2],
+                                             float (&z_run)[2], bool (&flag)[2], f32x4 (&acc_o)[2][32]) {
+  const char* xb = reinterpret_cast<const char*>(X);
+  int4 rv[2];
+  rv[0] = *reinterpret_cast<const int4*>(rows + v0 + 4 * g);
+  rv[1] = *reinterpret_cast<const int4*>(rows + v0 + 16 + 4 * g);
+  f32x4 sacc[2][2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) sacc[ht][0] = sacc[ht][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    bf16x8 xf[32];
+#pragma unroll
+    for (int f = 0; f < 32; ++f) {
+      const int st = f >> 1, h2 = f & 1;
+      xf[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xb + so.qk[st & 3] + h2 * 16384 + 256 * (st >> 2)));
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      acc_o[8 * j + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[k], pf, acc_o[8 * j + k], 0, 0, 0);
+    for (int f = 0; f < 32; ++f)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+        sacc[ht][f & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[f], qf[ht][f >> 1], sacc[ht][f & 1], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);     // rows entries + first four fragments
+#pragma unroll
+    for (int i = 0; i < 28; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one fragment read ...
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // ... and the two MFMAs of a landed one
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 pf[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) softmax_update_regs(sacc[ht], rv, scale, m_run[ht], z_run[ht], flag[ht], pf[ht]);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    bf16x8 vf[32];
+    pv_load(X, so, vf);
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+        acc_o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[ht], acc_o[ht][dt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);     // first four fragments (two reads each)
+#pragma unroll
+    for (int i = 0; i < 28; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -502,12 +666,16 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
 // ---------------------------------------------------------------------------
 // bf16 rows of 512 channels: tiles are copied HBM -> LDS by the load units
 // themselves (global_load_lds_dwordx4: one 1 KB row per wave instruction, no
-// registers involved) into a ring of four LDS tiles, so three tiles (~100 KB)
-// are in flight per CU while the fourth is consumed. That depth covers the
-// loaded-memory latency at this CU's share of HBM bandwidth.
+// registers involved) into a ring of four LDS tiles. Each step works on two
+// landed tiles (S^T of the next, the output update of the current) while up
+// to two more are in flight.
 // ---------------------------------------------------------------------------
 constexpr int kRing = 4;
 
+// NHT 16-head tiles per wave: NHT = 1 serves 64 heads per workgroup, NHT = 2
+// serves 128 (half the LDS reads and tile copies per head; the per-head state
+// fills the unified register file of this one-wave-per-SIMD kernel).
+template <int NHT>
 __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, SplitPlan sp,
                                                                  float* __restrict__ part_o,
                                                                  float* __restrict__ part_ml) {
@@ -523,8 +691,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
   int split, hg, t;
   if (!work_item(sp, a.Tq, blockIdx.x, split, hg, t)) return;
   const int b = blockIdx.z;
-  const bool active = wid * 16 < sp.HG;
-  const int head = hg * sp.HG + wid * 16 + r16;
+  const bool active = wid * 16 * NHT < sp.HG;
+  const int head0 = hg * sp.HG + wid * 16 * NHT + r16;   // + 16 ht for head tile ht
   const RowSpan rs = row_span(a, t);
   if (sp.S == 1) fill_rope_table(a, t, rope_tab);   // read after the tile loop's barriers
   const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
@@ -552,10 +720,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
   // physical slot l: the tile is stored swizzled. Lanes 0..RPW-1 resolve the
   // rows' addresses, which reach the copies through readlane. Absent rows copy
   // window row 0 (any valid memory) and are masked out of the softmax.
-  uint32_t src_off[RPW];
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr)
-    src_off[rr] = 16u * static_cast<uint32_t>((lane & 48) | ((lane & 15) ^ slot_swizzle(wid * RPW + rr)));
   auto issue = [&](int tile, uint16_t* dst) {
     const int v0 = tile * kTileRows + wid * RPW;
     uint64_t my = 0;
@@ -572,19 +736,19 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
     for (int rr = 0; rr < RPW; ++rr) {
       const uint64_t rb = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), rr))) << 32) |
                           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), rr));
-      lds_copy16(reinterpret_cast<const void*>(rb + src_off[rr]), lds0 + rr * D * 2);
+      const uint32_t src_off = 16u * static_cast<uint32_t>((lane & 48) | ((lane & 15) ^ slot_swizzle(wid * RPW + rr)));
+      lds_copy16(reinterpret_cast<const void*>(rb + src_off), lds0 + rr * D * 2);
     }
   };
   const int ntiles = (nr + kTileRows - 1) / kTileRows;
-  // Tile `tt` has landed in this wave's view once at most the copies of the
-  // tiles after it that were already issued remain outstanding (RPW each).
-  auto wait_tile = [&](int tt) {
-    const int later = min(ntiles - 1, tt + kRing - 2) - tt;
-    if (later >= 2) wait_vmcnt<2 * RPW>();
-    else if (later == 1) wait_vmcnt<RPW>();
+  // Ring: tiles 0..2 are issued up front. Step `it` waits for tile it + 1
+  // (tile it + 2 may stay in flight) and, after that barrier, refills the slot
+  // of tile it - 1 (consumed by every wave in step it - 1) with tile it + 3.
+  auto wait_next = [&](int tt) {
+    if (tt + 1 < ntiles) wait_vmcnt<RPW>();
     else wait_vmcnt<0>();
     // A bare barrier: the wave's own copies are complete (waited above) and
-    // every LDS read of the previous tile fed an MFMA already, so no fence is
+    // every LDS read of the freed slot fed an MFMA already, so no fence is
     // needed; a fence would also drain the later copies that must stay in flight.
     __builtin_amdgcn_s_barrier();
   };
@@ -593,46 +757,98 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
     if (t0 < ntiles) issue(t0, Xs[t0]);
   // query fragments load while the first tiles are in flight
   // (a wave past the block's heads computes on zero queries and writes nothing)
-  bf16x8 qf[KS];
-  if (active) {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * D;
+  bf16x8 qf[NHT][KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
-  } else {
+  for (int ht = 0; ht < NHT; ++ht) {
+    if (active) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                           ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head0 + 16 * ht) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
-  }
-  f32x4 acc_o[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, z_run = 0.f;
-  const SwzOffsets so = swz_offsets(g, r16);
-  if (0 < ntiles) wait_tile(0);
-  __builtin_amdgcn_s_waitcnt(0);      // query fragments too (tiles 1, 2 may land meanwhile)
-
-  // Ring step: refill the slot freed by tile it-1 with tile it+3, consume tile
-  // it, then wait for tile it+1.
-  bool flag = false;
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + kRing - 1 < ntiles) issue(it + kRing - 1, Xs[(it + kRing - 1) % kRing]);
-    bf16x8 pf;
-    tile_softmax_swz(Xs[it % kRing], so, it * kTileRows, rows, qf, a.scale, g, m_run, z_run, flag, pf);
-    tile_pv_swz(Xs[it % kRing], so, pf, acc_o);
-    if (it + 1 < ntiles) wait_tile(it + 1);
-  }
-
-  if (active) {
-    const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
-    if (sp.S == 1) {
-      write_output<D>(a, b, t, head, g, acc_o, m_run, z_run, flag, rope_tab, part_ml + 2 * part_idx);
+      for (int s = 0; s < KS; ++s)
+        qf[ht][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
     } else {
-      float* po = part_o + part_idx * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
-      if (g == 0) {
-        part_ml[2 * part_idx] = flag ? __builtin_nanf("") : m_run;   // NaN: recompute in combine
-        part_ml[2 * part_idx + 1] = z_run;
+      for (int s = 0; s < KS; ++s) qf[ht][s] = bf16x8{};
+    }
+  }
+  f32x4 acc_o[NHT][DT];
+  float m_run[NHT], z_run[NHT];
+  bool flag[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) acc_o[ht][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[ht] = -INFINITY;
+    z_run[ht] = 0.f;
+    flag[ht] = false;
+  }
+  const SwzOffsets so = swz_offsets(g, r16);
+
+  if constexpr (NHT == 1) {
+    if (ntiles > 0) {
+      // tile 0 landed (tiles 1, 2 may still be in flight); query fragments too
+      if (ntiles > 2) wait_vmcnt<2 * RPW>();
+      else if (ntiles > 1) wait_vmcnt<RPW>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_barrier();
+      f32x4 sacc[2];
+      int4 rv[2];
+      {
+        bf16x8 xf[32];
+        qk_load(Xs[0], so, rows, 0, g, xf, rv);
+        qk_mfma(xf, qf[0], sacc);
+      }
+      for (int it = 0; it + 1 < ntiles; ++it) {
+        wait_next(it + 1);
+        if (it + kRing - 1 < ntiles) issue(it + kRing - 1, Xs[(it + kRing - 1) % kRing]);
+        tile_pipe_step(Xs[it % kRing], Xs[(it + 1) % kRing], so, rows, (it + 1) * kTileRows, g, qf[0], a.scale, sacc,
+                       rv, m_run[0], z_run[0], flag[0], acc_o[0]);
+      }
+      // last tile: output update only
+      bf16x8 vf[32], pf;
+      pv_load(Xs[(ntiles - 1) % kRing], so, vf);
+      softmax_update_regs(sacc, rv, a.scale, m_run[0], z_run[0], flag[0], pf);
+      pv_mfma(vf, pf, acc_o[0]);
+    }
+  } else {
+    // Ring step: consume tile it, then wait for tile it + 1 and refill the
+    // slot of tile it with tile it + 4 (three tiles in flight meanwhile).
+    auto wait_tile = [&](int tt) {
+      const int later = min(ntiles - 1, tt + kRing - 2) - tt;
+      if (later >= 2) wait_vmcnt<2 * RPW>();
+      else if (later == 1) wait_vmcnt<RPW>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();                 // bare: see wait_next
+    };
+    if (ntiles > 0) {
+      wait_tile(0);
+      __builtin_amdgcn_s_waitcnt(0);                // query fragments too
+    }
+    for (int it = 0; it < ntiles; ++it) {
+      if (it + kRing - 1 < ntiles) issue(it + kRing - 1, Xs[(it + kRing - 1) % kRing]);
+      tile_step_32(Xs[it % kRing], so, it * kTileRows, rows, qf, a.scale, g, m_run, z_run, flag, acc_o);
+      if (it + 1 < ntiles) wait_tile(it + 1);
+    }
+  }
+
+  if (active) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int head = head0 + 16 * ht;
+      const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
+      if (sp.S == 1) {
+        write_output<D>(a, b, t, head, g, acc_o[ht], m_run[ht], z_run[ht], flag[ht], rope_tab, part_ml + 2 * part_idx);
+      } else {
+        float* po = part_o + part_idx * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
+              make_float4(acc_o[ht][dt][0], acc_o[ht][dt][1], acc_o[ht][dt][2], acc_o[ht][dt][3]);
+        if (g == 0) {
+          part_ml[2 * part_idx] = flag[ht] ? __builtin_nanf("") : m_run[ht];   // NaN: recompute in combine
+          part_ml[2 * part_idx + 1] = z_run[ht];
+        }
       }
     }
   }
@@ -1327,6 +1543,11 @@ __global__ __launch_bounds__(256) void fixup_kernel(AttendArgs a, int RS, const 
       combine_row(a, 1, RS, b, t, h, part_o, part_ml, sml, red, lc);
 }
 
+// bf16 rows of 512 channels with a multiple of 128 heads: 32 heads per wave
+bool heads_128(const AttendArgs& a) {
+  return a.D == 512 && a.dt_q == LCA_BF16 && a.dt_kv == LCA_BF16 && a.H % 128 == 0;
+}
+
 SplitPlan make_plan(const AttendArgs& a) {
   SplitPlan sp;
   const bool f32 = a.dt_kv == LCA_F32;
@@ -1335,6 +1556,9 @@ SplitPlan make_plan(const AttendArgs& a) {
     if (hg > a.H) hg = a.H;
     sp.HG = hg;
     sp.n_hg = (a.H + hg - 1) / hg;
+  } else if (heads_128(a)) {
+    sp.HG = 128;
+    sp.n_hg = a.H / 128;
   } else {
     sp.HG = a.H < 64 ? a.H : 64;
     sp.n_hg = a.H / sp.HG;
@@ -1355,7 +1579,12 @@ SplitPlan make_plan(const AttendArgs& a) {
   // groups (128 heads) a sequence gets 16 splits (32 workgroups), so a batch of
   // 8 fills the 256 CUs in one round; with one head group, splits of 64 rows.
   int64_t RS;
-  if (sp.n_hg >= 2) {
+  if (sp.HG == 128 && !f32) {
+    // 128 heads per workgroup: as many workgroups per query as two 64-head
+    // groups with 16 splits would give (32), at least 256 rows each
+    RS = (nrows * a.Tq + 31) / 32;
+    if (RS < 256) RS = 256;
+  } else if (sp.n_hg >= 2) {
     RS = (nrows * a.Tq + 15) / 16;
     if (RS < 256) RS = 256;
   } else {
@@ -1384,8 +1613,10 @@ void launch_mfma_d(LaunchScope& sc, const AttendArgs& a, const SplitPlan& sp, fl
   if constexpr (D == 512) {                        // KV_MIXED rows exist only at D = 512
     if (a.dt_kv == LCA_KV_MIXED)
       sc.launch(attend_mixed_dma_kernel, grid, block, 0, a, sp, po, pml);
+    else if (sp.HG == 128)
+      sc.launch(attend_dma_kernel<2>, grid, block, 0, a, sp, po, pml);
     else
-      sc.launch(attend_dma_kernel, grid, block, 0, a, sp, po, pml);
+      sc.launch(attend_dma_kernel<1>, grid, block, 0, a, sp, po, pml);
   } else {
     sc.launch(attend_mfma_kernel<D>, grid, block, 0, a, sp, po, pml);
   }

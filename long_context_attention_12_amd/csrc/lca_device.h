@@ -27,8 +27,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// Two floats to two bf16 (round to nearest even) in one gfx950 instruction
+// (v_cvt_pk_bf16_f32); lo in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // ---- OCP FP8 E4M3FN (bias 7, max 448, subnormal step 2^-9) -------------------
@@ -110,6 +115,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   // and lgkmcnt at their maxima, i.e. not waited on
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// Wait for every LDS (and scalar-memory) operation of this wave: lgkmcnt = 0,
+// vmcnt and expcnt left at their maximum (no wait).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
 // ---- wave reductions (64 lanes) -----------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
