@@ -445,6 +445,49 @@ def test_attend_window_clipped_and_no_entries():
     row_tol_check(host(out)[0], ref, 2e-2, "clipped window")
 
 
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+@pytest.mark.parametrize("Tq,H", [(1, 64), (4, 16), (4, 64)])
+@pytest.mark.parametrize("q_pos0", [45, 60001])
+def test_attend_512_short_ragged_lists(kind, Tq, H, q_pos0):
+    # bf16 rows of 512 channels, few queries and a few hundred rows each (the
+    # decode shapes): row counts that are not multiples of the 32-row tile,
+    # q_pos0 = 45 clips the window and leaves few visible entries, CSA lists
+    # carry absent (-1) entries in any order, 16 heads leave 3 of 4 waves idle.
+    L = need_gpu()
+    rng = np.random.default_rng(44 + Tq + H + (q_pos0 > 100))
+    B, D, W = 3, 512, 128
+    m = 4 if kind == "csa" else 128
+    N_cap = (q_pos0 + Tq) // m + 2
+    k = 517
+    q, E, win, sink = _attend_case(rng, B, Tq, H, D, N_cap, W, 4.0, WL.bf16_exact)
+    scale = 1 / math.sqrt(D)
+    out = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+    say(f"short ragged lists {kind} Tq={Tq} H={H} q_pos0={q_pos0}")
+    if kind == "csa":
+        idx = np.full((B, Tq, k), -1, np.int32)
+        for b in range(B):
+            for t in range(Tq):
+                nv = O.n_visible(q_pos0 + t, m)
+                sel = rng.choice(nv, size=min(k - 5, nv), replace=False)
+                idx[b, t, :len(sel)] = sel                      # any order; -1 tail
+        L.csa_attend(L.BF16, L.BF16, dev_bf16(q), dev_bf16(E), torch.from_numpy(idx).to(DEV), dev_bf16(win),
+                     dev_f32(sink), out, m=m, W=W, q_pos0=q_pos0, scale=scale, flags=L.INV_ROPE, rope_dims=64,
+                     lse_out=lse)
+    else:
+        L.hca_attend(L.BF16, L.BF16, dev_bf16(q), dev_bf16(E), dev_bf16(win), dev_f32(sink), out, m=m, W=W,
+                     q_pos0=q_pos0, scale=scale, flags=L.INV_ROPE, rope_dims=64, lse_out=lse)
+    torch.cuda.synchronize()
+    got, got_lse = host(out), lse.cpu().numpy()
+    for b in range(B):
+        if kind == "csa":
+            ref, rl = O.csa_attend(q[b], E[b], idx[b], win[b], sink, scale, q_pos0, W, True, 10000.0, 64)
+        else:
+            ref, rl = O.hca_attend(q[b], E[b], m, win[b], sink, scale, q_pos0, W, True, 10000.0, 64)
+        row_tol_check(got[b], ref, 2e-2, f"short lists {kind} Tq={Tq} H={H} q_pos0={q_pos0} b={b}")
+        np.testing.assert_allclose(got_lse[b], rl, atol=2e-2)
+
+
 @pytest.mark.parametrize("Tq", [1, 16])
 def test_attend_mixed_kv_matches_oracle(Tq):
     # 16 queries x 128 heads: one split per query (output written by the kernel)
