@@ -359,6 +359,36 @@ def test_index_topk_mxfp4(H_I, bf16_scores):
                 assert np.mean(sco_h[b, t][:len(sel)] == ref) > 0.99
 
 
+@pytest.mark.parametrize("bf16_scores", [False, True])
+def test_index_topk_chunked_ties_exact(bf16_scores):
+    # 20000 entries with 5 distinct keys, k = 700: thousands of entries tie at
+    # the threshold, spread over the whole list. The result must be exactly the
+    # oracle order (score descending, index ascending) cut at k.
+    L = need_gpu()
+    rng = np.random.default_rng(71 + bf16_scores)
+    B, Tq, H_I, d_I, m, k = 2, 1, 4, 128, 4, 700
+    N_cap = 20000
+    base = WL.bf16_exact(rng.standard_normal((5, d_I)).astype(np.float32))
+    kI = np.stack([base[rng.integers(0, 5, size=N_cap)] for _ in range(B)])
+    qI = WL.bf16_exact(rng.standard_normal((B, Tq, H_I, d_I)).astype(np.float32))
+    w = np.abs(rng.standard_normal((B, Tq, H_I))).astype(np.float32)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    q_pos0 = 4 * N_cap - 1
+    say(f"chunked ties bf16={bf16_scores}")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
+                     flags=L.SCORE_BF16 if bf16_scores else 0)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b in range(B):
+        sc = O.index_scores(qI[b, 0], w[b, 0], kI[b], N_cap)
+        if bf16_scores:
+            sc = O.bf16_round(sc)
+        vals = np.unique(sc)
+        assert len(vals) == 5 and np.min(np.diff(vals)) > 1e-4 * np.max(np.abs(vals)), "keys must be apart"
+        order = np.lexsort((np.arange(N_cap), -sc))          # score descending, then index ascending
+        np.testing.assert_array_equal(got[b, 0], np.sort(order[:k]))
+
+
 def test_index_topk_all_ties_take_lowest_indices():
     L = need_gpu()
     B, Tq, H_I, d_I, m, k = 1, 1, 4, 128, 4, 100
