@@ -14,7 +14,8 @@ Also measured (secondary, same line): HCA decode, V4-Pro shaped: batch 8,
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Counter runs: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) over
-``bench.py --copy-calibration 1024``, then ``bench.py --pmc-summary F.csv W.csv``.
+``bench.py --no-secondary --no-prefill --no-mixed --copy-calibration 1024``,
+then ``bench.py --pmc-summary F.csv W.csv --copy-calibration 1024``.
 """
 
 from __future__ import annotations
@@ -305,7 +306,7 @@ def pmc_summary(fetch_csv, write_csv, copy_mib, out_json):
     def stats(path, counter):
         rows = _read_counter_csv(path, counter)
         copies = [r for r in rows if "copyBuffer" in r[1]][-COPY_REPS:]
-        score = [r for r in rows if "index_score" in r[1]]
+        score = [r for r in rows if "index_score_bf16_kernel" in r[1]]     # the CSA decode scoring kernel
         if len(copies) < COPY_REPS or not score:
             raise SystemExit(f"{path}: calibration copies or index_score dispatches missing")
         c = sum(r[3] for r in copies) / len(copies)
