@@ -920,8 +920,7 @@ __device__ __forceinline__ void softmax_update_mixed(const f32x4 (&sa)[2], const
     lg[i] = l;
     mx = fmaxf(mx, l);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = pair_max32(pair_max16(mx));
   if (m_run == -INFINITY) m_run = mx;
   flag = flag || (mx > m_run + kHeadroom);
   float psum = 0.f;
@@ -931,9 +930,7 @@ __device__ __forceinline__ void softmax_update_mixed(const f32x4 (&sa)[2], const
     p[i] = lg[i] == -INFINITY ? 0.f : __expf(fminf(lg[i] - m_run, kHeadroom));
     psum += p[i];
   }
-  psum += __shfl_xor(psum, 16, 64);
-  psum += __shfl_xor(psum, 32, 64);
-  z_run += psum;
+  z_run += pair_sum32(pair_sum16(psum));
   uint4 wa, wb;
   wa.x = pack_bf16x2(p[0] * sc[0], p[1] * sc[1]);
   wa.y = pack_bf16x2(p[2] * sc[2], p[3] * sc[3]);
@@ -996,6 +993,71 @@ __device__ __forceinline__ void tile_pv_mixed(const uint16_t* X, const SwzOffset
   }
 }
 
+// One mixed tile for a wave serving 32 heads (two 16-head tiles): as
+// tile_step_32, with S^T split into the fp8-channel accumulator (K steps
+// 0..13, scaled by the row scale in the softmax) and the bf16-channel one,
+// and P scaled by the row scale on the fp8 channel tiles.
+__device__ __forceinline__ void tile_step_mixed_32(const uint16_t* X, const SwzOffsets& so, int v0,
+                                                   const int32_t* rows, const float* rsc,
+                                                   const bf16x8 (&qf)[2][16], float scale, int g,
+                                                   float (&m_run)[2], float (&z_run)[2], bool (&flag)[2],
+                                                   f32x4 (&acc_o)[2][32]) {
+  const char* xb = reinterpret_cast<const char*>(X);
+  f32x4 sa[2][2], sb[2][2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) sa[ht][0] = sa[ht][1] = sb[ht][0] = sb[ht][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    bf16x8 xf[32];
+#pragma unroll
+    for (int f = 0; f < 32; ++f) {
+      const int st = f >> 1, h2 = f & 1;
+      xf[f] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xb + so.qk[st & 3] + h2 * 16384 + 256 * (st >> 2)));
+    }
+#pragma unroll
+    for (int f = 0; f < 32; ++f) {
+      const int st = f >> 1, h2 = f & 1;
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        if (st < 14) sa[ht][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[f], qf[ht][st], sa[ht][h2], 0, 0, 0);
+        else sb[ht][h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[f], qf[ht][st], sb[ht][h2], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // first four fragments
+#pragma unroll
+    for (int i = 0; i < 28; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one fragment read ...
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // ... and the two MFMAs of a landed one
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 pa[2], pb[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht)
+    softmax_update_mixed(sa[ht], sb[ht], v0, rows, rsc, scale, g, m_run[ht], z_run[ht], flag[ht], pa[ht], pb[ht]);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    bf16x8 vf[32];
+    pv_load(X, so, vf);
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt)                 // channel tile dt: fp8 part below 28
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht)
+        acc_o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], dt < 28 ? pa[ht] : pb[ht], acc_o[ht][dt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);     // first four fragments (two reads each)
+#pragma unroll
+    for (int i = 0; i < 28; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// NHT 16-head tiles per wave, as attend_dma_kernel.
+template <int NHT>
 __global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArgs a, SplitPlan sp,
                                                                        float* __restrict__ part_o,
                                                                        float* __restrict__ part_ml) {
@@ -1011,8 +1073,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArg
   int split, hg, t;
   if (!work_item(sp, a.Tq, blockIdx.x, split, hg, t)) return;
   const int b = blockIdx.z;
-  const bool active = wid * 16 < sp.HG;
-  const int head = hg * sp.HG + wid * 16 + r16;
+  const bool active = wid * 16 * NHT < sp.HG;
+  const int head0 = hg * sp.HG + wid * 16 * NHT + r16;   // + 16 ht for head tile ht
   const RowSpan rs = row_span(a, t);
   if (sp.S == 1) fill_rope_table(a, t, rope_tab);
   const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
@@ -1065,19 +1127,31 @@ __global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArg
 #pragma unroll
   for (int t0 = 0; t0 < 3; ++t0)
     if (t0 < ntiles) issue(t0, t0);
-  bf16x8 qf[KS];
-  if (active) {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * D;
+  bf16x8 qf[NHT][KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
-  } else {
+  for (int ht = 0; ht < NHT; ++ht) {
+    if (active) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                           ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head0 + 16 * ht) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+      for (int s = 0; s < KS; ++s)
+        qf[ht][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[ht][s] = bf16x8{};
+    }
   }
-  f32x4 acc_o[DT];
+  f32x4 acc_o[NHT][DT];
+  float m_run[NHT], z_run[NHT];
+  bool flag[NHT];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, z_run = 0.f;
+  for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) acc_o[ht][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[ht] = -INFINITY;
+    z_run[ht] = 0.f;
+    flag[ht] = false;
+  }
   const SwzOffsets so = swz_offsets(g, r16);
   __builtin_amdgcn_s_waitcnt(0);                   // tiles 0..2 and the query fragments
   __builtin_amdgcn_s_barrier();
@@ -1085,7 +1159,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArg
 
   // Step it: (raw tile it+1 landed, everyone past tile it-1) -> refill the raw
   // slot of tile it-1 with tile it+3 -> convert tile it+1 -> consume tile it.
-  bool flag = false;
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) {
       if (it + 2 < ntiles) wait_vmcnt<5>();        // tile it+2's copies may stay in flight
@@ -1094,25 +1167,34 @@ __global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArg
     __builtin_amdgcn_s_barrier();
     if (it + 3 < ntiles) issue(it + 3, (it + 3) % kRawRing);
     if (it + 1 < ntiles) convert_mixed_tile(&Raw[(it + 1) % kRawRing][0], Xs[(it + 1) & 1]);
-    bf16x8 pa, pb;
-    tile_softmax_mixed(Xs[it & 1], so, it * kTileRows, rows,
-                       reinterpret_cast<const float*>(&Raw[it % kRawRing][kRawTile]), qf, a.scale, g, m_run,
-                       z_run, flag, pa, pb);
-    tile_pv_mixed(Xs[it & 1], so, pa, pb, acc_o);
+    const float* rsc = reinterpret_cast<const float*>(&Raw[it % kRawRing][kRawTile]);
+    if constexpr (NHT == 1) {
+      bf16x8 pa, pb;
+      tile_softmax_mixed(Xs[it & 1], so, it * kTileRows, rows, rsc, qf[0], a.scale, g, m_run[0], z_run[0], flag[0],
+                         pa, pb);
+      tile_pv_mixed(Xs[it & 1], so, pa, pb, acc_o[0]);
+    } else {
+      tile_step_mixed_32(Xs[it & 1], so, it * kTileRows, rows, rsc, qf, a.scale, g, m_run, z_run, flag, acc_o);
+    }
   }
 
   if (active) {
-    const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
-    if (sp.S == 1) {
-      write_output<D>(a, b, t, head, g, acc_o, m_run, z_run, flag, rope_tab, part_ml + 2 * part_idx);
-    } else {
-      float* po = part_o + part_idx * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc_o[dt][0], acc_o[dt][1], acc_o[dt][2], acc_o[dt][3]);
-      if (g == 0) {
-        part_ml[2 * part_idx] = flag ? __builtin_nanf("") : m_run;   // NaN: recompute in combine
-        part_ml[2 * part_idx + 1] = z_run;
+    for (int ht = 0; ht < NHT; ++ht) {
+      const int head = head0 + 16 * ht;
+      const int64_t part_idx = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * sp.S + split;
+      if (sp.S == 1) {
+        write_output<D>(a, b, t, head, g, acc_o[ht], m_run[ht], z_run[ht], flag[ht], rope_tab, part_ml + 2 * part_idx);
+      } else {
+        float* po = part_o + part_idx * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
+              make_float4(acc_o[ht][dt][0], acc_o[ht][dt][1], acc_o[ht][dt][2], acc_o[ht][dt][3]);
+        if (g == 0) {
+          part_ml[2 * part_idx] = flag[ht] ? __builtin_nanf("") : m_run[ht];   // NaN: recompute in combine
+          part_ml[2 * part_idx + 1] = z_run[ht];
+        }
       }
     }
   }
@@ -1543,9 +1625,9 @@ __global__ __launch_bounds__(256) void fixup_kernel(AttendArgs a, int RS, const 
       combine_row(a, 1, RS, b, t, h, part_o, part_ml, sml, red, lc);
 }
 
-// bf16 rows of 512 channels with a multiple of 128 heads: 32 heads per wave
+// bf16 or mixed rows of 512 channels with a multiple of 128 heads: 32 heads per wave
 bool heads_128(const AttendArgs& a) {
-  return a.D == 512 && a.dt_q == LCA_BF16 && a.dt_kv == LCA_BF16 && a.H % 128 == 0;
+  return a.D == 512 && a.dt_q == LCA_BF16 && (a.dt_kv == LCA_BF16 || a.dt_kv == LCA_KV_MIXED) && a.H % 128 == 0;
 }
 
 SplitPlan make_plan(const AttendArgs& a) {
@@ -1581,9 +1663,12 @@ SplitPlan make_plan(const AttendArgs& a) {
   int64_t RS;
   if (sp.HG == 128 && !f32) {
     // 128 heads per workgroup: as many workgroups per query as two 64-head
-    // groups with 16 splits would give (32), at least 256 rows each
+    // groups with 16 splits would give (32), at least 256 rows each; mixed
+    // rows at least 512 (their tiles carry a conversion pass, and a split's
+    // fp32 partial weighs as much as 3.5 of their 576-byte rows)
     RS = (nrows * a.Tq + 31) / 32;
-    if (RS < 256) RS = 256;
+    const int64_t rs_min = a.dt_kv == LCA_KV_MIXED ? 512 : 256;
+    if (RS < rs_min) RS = rs_min;
   } else if (sp.n_hg >= 2) {
     RS = (nrows * a.Tq + 15) / 16;
     if (RS < 256) RS = 256;
@@ -1611,8 +1696,10 @@ template <int D>
 void launch_mfma_d(LaunchScope& sc, const AttendArgs& a, const SplitPlan& sp, float* po, float* pml) {
   dim3 grid(static_cast<uint32_t>(work_blocks(sp, a.Tq)), 1, a.B), block(kAttThreads);
   if constexpr (D == 512) {                        // KV_MIXED rows exist only at D = 512
-    if (a.dt_kv == LCA_KV_MIXED)
-      sc.launch(attend_mixed_dma_kernel, grid, block, 0, a, sp, po, pml);
+    if (a.dt_kv == LCA_KV_MIXED && sp.HG == 128)
+      sc.launch(attend_mixed_dma_kernel<2>, grid, block, 0, a, sp, po, pml);
+    else if (a.dt_kv == LCA_KV_MIXED)
+      sc.launch(attend_mixed_dma_kernel<1>, grid, block, 0, a, sp, po, pml);
     else if (sp.HG == 128)
       sc.launch(attend_dma_kernel<2>, grid, block, 0, a, sp, po, pml);
     else

@@ -550,6 +550,47 @@ def test_attend_mixed_kv_matches_oracle(Tq):
         row_tol_check(host(out)[b], ref, 2e-2, "mixed kv")
 
 
+@pytest.mark.parametrize("Tq", [1, 32])
+def test_attend_mixed_logit_ramp_exact_recompute(Tq):
+    # KV_MIXED rows, 128 heads (32 per wave): logits that climb by hundreds
+    # along the entries overflow the in-kernel headroom, so flagged splits are
+    # recomputed exactly from the stored fp8 / bf16 rows (1 query: 2 splits of
+    # 512 rows, merged by the combine; 32 queries: one split, fixed up after).
+    L = need_gpu()
+    rng = np.random.default_rng(45 + Tq)
+    B, H, D, W, m = 1, 128, 512, 128, 128
+    q_pos0 = m * 600
+    N_cap = (q_pos0 + Tq) // m + 1
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    ramp = np.linspace(-1.0, 1.0, N_cap)
+    Esrc = (ramp[:, None] * u[None, :] + 0.05 * rng.standard_normal((N_cap, D)) / np.sqrt(D)).astype(np.float32)
+    wsrc = (rng.standard_normal((W - 1 + Tq, D)) / np.sqrt(D)).astype(np.float32)
+    sharp = np.geomspace(1.0, 4000.0, H)
+    q = (sharp[None, :, None] * (u[None, None, :] + 0.1 * rng.standard_normal((Tq, H, D)) / np.sqrt(D)))
+    q = WL.bf16_exact((q * np.sqrt(D)).astype(np.float32))[None]
+    sink = rng.standard_normal(H).astype(np.float32)
+    Eq = torch.empty((1, N_cap, D + 64), dtype=torch.uint8, device=DEV)
+    Es = torch.empty((1, N_cap), dtype=torch.float32, device=DEV)
+    Wq = torch.empty((1, W - 1 + Tq, D + 64), dtype=torch.uint8, device=DEV)
+    Ws = torch.empty((1, W - 1 + Tq), dtype=torch.float32, device=DEV)
+    L.lca_quantize_rows(L.KV_MIXED, dev_f32(Esrc[None]), Eq, Es)
+    L.lca_quantize_rows(L.KV_MIXED, dev_f32(wsrc[None]), Wq, Ws)
+    out = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+    say(f"ramp mixed hca Tq={Tq} entries={O.n_visible(q_pos0, m)}")
+    L.hca_attend(L.BF16, L.KV_MIXED, dev_bf16(q), Eq, Wq, dev_f32(sink), out, m=m, W=W, q_pos0=q_pos0,
+                 scale=1 / math.sqrt(D), kv_scale=Es, win_scale=Ws, flags=L.INV_ROPE, rope_dims=64, lse_out=lse)
+    torch.cuda.synchronize()
+    Ed = O.kv_mixed_decode(*O.kv_mixed_quantize(Esrc, 64))
+    Wd = O.kv_mixed_decode(*O.kv_mixed_quantize(wsrc, 64))
+    ref, rl = O.hca_attend(q[0], Ed, m, Wd, sink, 1 / math.sqrt(D), q_pos0, W, True, 10000.0, 64)
+    assert np.ptp(rl) > 100.0, "the case must span a wide logit range"
+    row_tol_check(host(out)[0], ref, 2e-2, f"mixed ramp Tq={Tq}")
+    lse_err = np.abs(lse.cpu().numpy()[0] - rl) / np.maximum(1.0, np.abs(rl))
+    assert lse_err.max() <= 2e-2, f"lse relative error {lse_err.max()}"
+
+
 @pytest.mark.parametrize("kind,D,Tq,H", [("hca", 512, 1, 64), ("csa", 512, 1, 64), ("csa", 256, 1, 64),
                                           ("hca", 512, 16, 128), ("csa", 256, 16, 128)])
 def test_attend_logit_ramp_exact_recompute(kind, D, Tq, H):
