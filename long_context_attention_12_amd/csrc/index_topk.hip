@@ -599,6 +599,41 @@ constexpr int kLongCap = 8192;     // boundary-bin candidates held in LDS
 // zeros of a query whose head weights are all negative) keep only their index,
 // in the row's spill buffer (ld entries), and their key is read again from the
 // scores.
+// One round's raw scores for this thread, fetched a round ahead of their use
+// so that the next round's loads are in flight while this round's histogram
+// atomics run (read 1 of the long select; read 2 keeps one round, since its
+// block scan and ordered writes need the registers). Past the list end the
+// cells hold the bit pattern 0xffffffff, whose key is 0 ("no element").
+template <int NI = kSelItems>
+struct RoundRaw {
+  float4 v[NI / 4];
+};
+
+template <int NI>
+__device__ __forceinline__ void fetch_round(const float* __restrict__ s, int64_t n, int64_t base, RoundRaw<NI>& r) {
+  const int64_t i0 = base + static_cast<int64_t>(threadIdx.x) * NI;
+  if (i0 + NI <= n) {
+#pragma unroll
+    for (int q = 0; q < NI / 4; ++q) r.v[q] = *reinterpret_cast<const float4*>(s + i0 + 4 * q);
+  } else {
+    const float pad = __uint_as_float(0xffffffffu);
+#pragma unroll
+    for (int q = 0; q < NI / 4; ++q) {
+      const int64_t j = i0 + 4 * q;
+      r.v[q] = make_float4(j < n ? s[j] : pad, j + 1 < n ? s[j + 1] : pad, j + 2 < n ? s[j + 2] : pad,
+                           j + 3 < n ? s[j + 3] : pad);
+    }
+  }
+}
+
+// Key of cell j (a compile-time index once unrolled) of a fetched round.
+template <int NI>
+__device__ __forceinline__ uint32_t raw_key(const RoundRaw<NI>& r, int j, bool key16) {
+  const float4 q = r.v[j >> 2];
+  const float v = (j & 3) == 0 ? q.x : (j & 3) == 1 ? q.y : (j & 3) == 2 ? q.z : q.w;
+  return score_key(v, key16);
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_long_kernel(
     const float* __restrict__ scores, int64_t ld, int32_t* __restrict__ spill, int64_t N_cap, int Tq, int t_off,
     int Tc, int64_t q_pos0, int m, int k, bool key16, int32_t* __restrict__ idx_out,
@@ -621,16 +656,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_long_kernel(
   int32_t* sp = spill + (static_cast<int64_t>(blockIdx.y) * Tc + blockIdx.x) * ld;   // candidate kLongCap + i at sp[i]
   const int rounds = static_cast<int>((n + kRound - 1) / kRound);
   const int sh0 = (key16 ? 16 : 32) - 12;
-  uint32_t key[kSelItems];
 
   // read 1: first digit
   for (int i = tid; i < kMaxBins; i += kSelThreads) hist[i] = 0;
   __syncthreads();
+  RoundRaw<> nxt;
+  fetch_round(s, n, 0, nxt);
   for (int r = 0; r < rounds; ++r) {
-    load_round(s, n, static_cast<int64_t>(r) * kRound, key16, key);
+    const RoundRaw<> cur = nxt;
+    if (r + 1 < rounds) fetch_round(s, n, static_cast<int64_t>(r + 1) * kRound, nxt);
 #pragma unroll
-    for (int j = 0; j < kSelItems; ++j)
-      if (key[j] != 0u) atomicAdd(&hist[key[j] >> sh0], 1u);
+    for (int j = 0; j < kSelItems; ++j) {
+      const uint32_t kj = raw_key(cur, j, key16);
+      if (kj != 0u) atomicAdd(&hist[kj >> sh0], 1u);
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -641,14 +680,24 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_long_kernel(
   const uint32_t bstar = sh_digit, krem1 = sh_krem;
   uint32_t cmin = 0xffffffffu, cmax = 0u;     // candidate key range, this thread
 
-  // read 2: entries above b* and candidates inside it, in index order
+  // read 2: entries above b* and candidates inside it, in index order; half
+  // rounds (16 scores per thread) so that the next one's loads fit in
+  // registers beside this one's during the block scan and ordered writes
+  constexpr int kHalf = kSelItems / 2, kHalfRound = kSelThreads * kHalf;
+  const int rounds2 = static_cast<int>((n + kHalfRound - 1) / kHalfRound);
   uint32_t run_a = 0, run_c = 0;
-  for (int r = 0; r < rounds; ++r) {
-    const int64_t base = static_cast<int64_t>(r) * kRound;
-    load_round(s, n, base, key16, key);
+  RoundRaw<kHalf> nxt2;
+  fetch_round(s, n, 0, nxt2);
+  for (int r = 0; r < rounds2; ++r) {
+    const int64_t base = static_cast<int64_t>(r) * kHalfRound;
+    const RoundRaw<kHalf> cur = nxt2;
+    if (r + 1 < rounds2) fetch_round(s, n, base + kHalfRound, nxt2);
+    uint32_t key[kHalf];
+#pragma unroll
+    for (int j = 0; j < kHalf; ++j) key[j] = raw_key(cur, j, key16);
     uint32_t am = 0, cm = 0;
 #pragma unroll
-    for (int j = 0; j < kSelItems; ++j) {
+    for (int j = 0; j < kHalf; ++j) {
       const uint32_t d = key[j] >> sh0;
       am |= static_cast<uint32_t>(key[j] != 0u && d > bstar) << j;
       cm |= static_cast<uint32_t>(key[j] != 0u && d == bstar) << j;
@@ -657,15 +706,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_long_kernel(
     const uint32_t pre = block_excl_scan((static_cast<uint32_t>(__builtin_popcount(am)) << 16) |
                                          static_cast<uint32_t>(__builtin_popcount(cm)), wsum, &tot);
     uint32_t pa = run_a + (pre >> 16), pc = run_c + (pre & 0xffffu);
-    const int32_t i0 = static_cast<int32_t>(base) + tid * kSelItems;
+    const int32_t i0 = static_cast<int32_t>(base) + tid * kHalf;
 #pragma unroll
-    for (int j = 0; j < kSelItems; ++j) {
+    for (int j = 0; j < kHalf; ++j) {
       if ((am >> j) & 1u) a_idx[pa++] = i0 + j;
       if ((cm >> j) & 1u) {
-        cmin = min(cmin, key[j]);
-        cmax = max(cmax, key[j]);
+        const uint32_t kj = key[j];
+        cmin = min(cmin, kj);
+        cmax = max(cmax, kj);
         if (pc < static_cast<uint32_t>(kLongCap)) {
-          c_key[pc] = key[j];
+          c_key[pc] = kj;
           c_idx[pc] = i0 + j;
         } else {
           sp[pc - kLongCap] = i0 + j;
