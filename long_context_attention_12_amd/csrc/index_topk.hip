@@ -71,6 +71,31 @@ __device__ __forceinline__ void emit_scores(const f32x4& acc, const float (&wv)[
   }
 }
 
+// As emit_scores, but into the wave's LDS staging block (row = query of the
+// wave, column = key of the tile) instead of the score rows: the block is then
+// written out as 256-byte row segments (see index_score_tiled_kernel). HI >= 2.
+constexpr int kStageStride = 80;     // floats per staged query row (64 keys + bank shift)
+template <int HI>
+__device__ __forceinline__ void stage_scores(const f32x4& acc, const float (&wv)[4], int g, int q0, int col,
+                                             float* stage, bool round_bf16) {
+  float part[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[i] = wv[i] * fmaxf(acc[i], 0.f);
+  if constexpr (HI == 2) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float sc = part[2 * p] + part[2 * p + 1];
+      stage[(q0 + 2 * g + p) * kStageStride + col] = round_bf16 ? bf16_round(sc) : sc;
+    }
+  } else {
+    float sc = (part[0] + part[1]) + (part[2] + part[3]);
+    if constexpr (HI >= 8) sc += __shfl_xor(sc, 16, 64);
+    if constexpr (HI >= 16) sc += __shfl_xor(sc, 32, 64);
+    const bool writer = (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0;
+    if (writer) stage[(q0 + (4 * g) / HI) * kStageStride + col] = round_bf16 ? bf16_round(sc) : sc;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bf16 scoring with MFMA 16x16x32 (A = 16 indexer query-head rows, B = 16 keys)
 // ---------------------------------------------------------------------------
@@ -155,7 +180,9 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
   constexpr int DI = 128, KS = DI / 32, MB = 4, NB = kTileKeys / 16, QPB = 16 / HI;
   constexpr int QPW = MB * QPB, QPWG = 4 * QPW;
   constexpr int ROWB = DI * 2;                       // bytes per key row
+  constexpr bool kStaged = HI >= 2;                  // HI = 1: 64 queries per wave, stored directly
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kTileKeys * DI];
+  __shared__ __attribute__((aligned(16))) float St[4][kStaged ? QPW * kStageStride : 4];
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
@@ -235,9 +262,30 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         pin_uniform(acc[mb]);
-        emit_scores<HI>(acc[mb], wv[mb], nvq[mb], g, tw0 + wid * QPW + mb * QPB, t_off, t_end, j, srow, ld,
-                        round_bf16);
+        if constexpr (kStaged)
+          stage_scores<HI>(acc[mb], wv[mb], g, mb * QPB, nb * 16 + r16, St[wid], round_bf16);
+        else
+          emit_scores<HI>(acc[mb], wv[mb], nvq[mb], g, tw0 + wid * QPW + mb * QPB, t_off, t_end, j, srow, ld,
+                          round_bf16);
       }
+    }
+    if constexpr (kStaged) {
+      // The wave's QPW x 64 tile of scores leaves as 16-byte stores, 16 lanes
+      // per 256-byte row segment. Every key of the tile is written: cells past
+      // a query's visible count lie inside its row (the stride is a multiple of
+      // 64, tiles start at multiples of 64 within this workgroup's key range)
+      // and the top-k never reads them. Queries past the chunk are skipped.
+      wait_lgkmcnt0();                              // the wave's staging writes have landed
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const int64_t jt0 = k_begin + static_cast<int64_t>(tt) * kTileKeys;
+#pragma unroll
+      for (int i = 0; i < QPW / 4; ++i) {
+        const int u = i * 64 + lane, row = u >> 4, c4 = u & 15;
+        const int qt = tw0 + wid * QPW + row;
+        const float4 v = *reinterpret_cast<const float4*>(&St[wid][row * kStageStride + 4 * c4]);
+        if (qt < t_end) *reinterpret_cast<float4*>(srow + static_cast<int64_t>(qt - t_off) * ld + jt0 + 4 * c4) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // reads done before the next tile's staging
     }
   }
 }
