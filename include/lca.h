@@ -215,7 +215,48 @@ int hca_attend(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, i
                uint32_t flags, float rope_base, int rope_dims,
                void* out, float* lse_out, void* ws, size_t ws_bytes);
 
-/* ---- diagnostics ------------------------------------------------------- */
+/* ---------------------------------------------------------------------------
+ * Ragged batches: *_ragged — the same three calls with a position per sequence.
+ *
+ * [kwkr] §4.4: serving keeps a KV cache per request (state cache and classical
+ * KV cache), so the sequences of one decode batch sit at different positions.
+ * The pages leave the batching interface open; here sequence b's query t sits
+ * at position q_pos[b] + t, and everything that depends on a position follows
+ * it: visible entries n_vis = (q_pos[b] + t + 1) / m, the window rows (row r of
+ * win[b] is position q_pos[b] - (W - 1) + r) and the inverse RoPE angle.
+ *
+ *   q_pos      int64 [B] in device memory, 8-byte aligned; each in
+ *              [0, q_pos_max]. A value outside is clamped into that range
+ *              (the kernels read it on the device; the host cannot check it).
+ *   q_pos_max  the bound: it takes the place of q_pos0 in the requirements
+ *              (N_cap >= visible entries at q_pos_max + Tq - 1) and in the
+ *              workspace queries (call *_workspace with q_pos0 = q_pos_max).
+ * Every other argument, layout and requirement is that of the uniform call.
+ * Results for sequence b depend only on its own inputs, q_pos[b], q_pos_max and
+ * the query shape: with a fixed bound (say the cache capacity) they are bitwise
+ * independent of the batch, and equal to those of a uniform call with
+ * q_pos0 = q_pos[b] whenever that call has the same split plan.
+ * Returns LCA_ERR_ARG if q_pos is NULL, LCA_ERR_ALIGN if it is misaligned.
+ * ------------------------------------------------------------------------- */
+int csa_index_topk_ragged(void* stream, int dt, int B, int Tq, int H_I, int d_I, int64_t N_cap,
+                          int m, int k, int64_t q_pos_max, const int64_t* q_pos,
+                          const void* qI, const void* qI_scale, const float* w,
+                          const void* kI, const void* kI_scale, uint32_t flags,
+                          int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes);
+int csa_attend_ragged(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+                      int m, int k, int W, int64_t q_pos_max, const int64_t* q_pos,
+                      const void* q, const void* kv, const float* kv_scale, const int32_t* idx,
+                      const void* win, const float* win_scale, const float* sink, float scale,
+                      uint32_t flags, float rope_base, int rope_dims,
+                      void* out, float* lse_out, void* ws, size_t ws_bytes);
+int hca_attend_ragged(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+                      int m, int W, int64_t q_pos_max, const int64_t* q_pos,
+                      const void* q, const void* kv, const float* kv_scale,
+                      const void* win, const float* win_scale, const float* sink, float scale,
+                      uint32_t flags, float rope_base, int rope_dims,
+                      void* out, float* lse_out, void* ws, size_t ws_bytes);
+
+/* ---- diagnostics ------------------------------------------------------- *//* ---- diagnostics ------------------------------------------------------- */
 const char* lca_status_str(int status);
 const char* lca_last_error(void); /* thread-local text of the last failure */
 int lca_version(void);            /* major*10000 + minor*100 + patch       */

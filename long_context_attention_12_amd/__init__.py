@@ -66,6 +66,15 @@ def _declare(L):
     L.hca_attend.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i64, vp, vp, vp, vp, vp,
                              vp, f32, u32, f32, i32, vp, vp, vp, sz]
     L.hca_attend.restype = i32
+    L.csa_index_topk_ragged.argtypes = [vp, i32, i32, i32, i32, i32, i64, i32, i32, i64, vp, vp, vp, vp,
+                                        vp, vp, u32, vp, vp, vp, sz]
+    L.csa_index_topk_ragged.restype = i32
+    L.csa_attend_ragged.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, i64, vp, vp, vp,
+                                    vp, vp, vp, vp, vp, f32, u32, f32, i32, vp, vp, vp, sz]
+    L.csa_attend_ragged.restype = i32
+    L.hca_attend_ragged.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i64, vp, vp, vp, vp,
+                                    vp, vp, vp, f32, u32, f32, i32, vp, vp, vp, sz]
+    L.hca_attend_ragged.restype = i32
     L.lca_status_str.argtypes = [i32]
     L.lca_status_str.restype = ctypes.c_char_p
     L.lca_last_error.argtypes = []
@@ -141,9 +150,18 @@ def csa_index_topk_workspace(dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0, flags=0):
     return int(lib().csa_index_topk_workspace(dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0, flags))
 
 
+def _q_pos(q_pos, B):
+    if q_pos.dtype != torch.int64 or q_pos.numel() != B or not q_pos.is_contiguous():
+        raise ValueError(f"q_pos must be a contiguous int64 tensor of {B} positions")
+    return _p(q_pos)
+
+
 def csa_index_topk(dt, qI, w, kI, idx_out, *, m, k, q_pos0, d_I=None, qI_scale=None, kI_scale=None,
-                   flags=0, score_out=None, ws=None, stream=None):
-    """Indexer scores + top-k. qI [B, Tq, H_I, d_I(/2)], kI [B, N_cap, d_I(/2)]."""
+                   flags=0, score_out=None, ws=None, stream=None, q_pos=None):
+    """Indexer scores + top-k. qI [B, Tq, H_I, d_I(/2)], kI [B, N_cap, d_I(/2)].
+
+    q_pos: optional int64 device tensor [B] of per-sequence positions (a ragged
+    batch, csa_index_topk_ragged); q_pos0 is then their bound."""
     B, Tq, H_I = qI.shape[0], qI.shape[1], qI.shape[2]
     if d_I is None:
         d_I = qI.shape[3] * (2 if dt == MXFP4 else 1)
@@ -151,6 +169,12 @@ def csa_index_topk(dt, qI, w, kI, idx_out, *, m, k, q_pos0, d_I=None, qI_scale=N
     need = csa_index_topk_workspace(dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0, flags)
     if ws is None:
         ws = _workspace(need, kI)
+    if q_pos is not None:
+        _check(lib().csa_index_topk_ragged(_stream(stream), dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0,
+                                           _q_pos(q_pos, B), _p(qI), _p(qI_scale), _p(w), _p(kI),
+                                           _p(kI_scale), flags, _p(idx_out), _p(score_out), _p(ws),
+                                           ws.numel() * ws.element_size()))
+        return
     _check(lib().csa_index_topk(_stream(stream), dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0, _p(qI),
                                 _p(qI_scale), _p(w), _p(kI), _p(kI_scale), flags, _p(idx_out),
                                 _p(score_out), _p(ws), ws.numel() * ws.element_size()))
@@ -166,14 +190,22 @@ def hca_attend_workspace(dt_q, dt_kv, B, Tq, H, D, N_cap, m, W, q_pos0):
 
 def csa_attend(dt_q, dt_kv, q, kv, idx, win, sink, out, *, m, W, q_pos0, scale, N_cap=None,
                kv_scale=None, win_scale=None, flags=0, rope_base=10000.0, rope_dims=0, lse_out=None,
-               ws=None, stream=None):
-    """CSA core attention; q [B, Tq, H, D], kv [B, N_cap, ...], idx [B, Tq, k]."""
+               ws=None, stream=None, q_pos=None):
+    """CSA core attention; q [B, Tq, H, D], kv [B, N_cap, ...], idx [B, Tq, k].
+
+    q_pos: optional int64 device tensor [B] (csa_attend_ragged); q_pos0 is its bound."""
     B, Tq, H, D = q.shape
     k = idx.shape[2]
     N_cap = kv.shape[1] if N_cap is None else N_cap
     need = csa_attend_workspace(dt_q, dt_kv, B, Tq, H, D, N_cap, m, k, W, q_pos0)
     if ws is None:
         ws = _workspace(need, q)
+    if q_pos is not None:
+        _check(lib().csa_attend_ragged(_stream(stream), dt_q, dt_kv, B, Tq, H, D, N_cap, m, k, W, q_pos0,
+                                       _q_pos(q_pos, B), _p(q), _p(kv), _p(kv_scale), _p(idx), _p(win),
+                                       _p(win_scale), _p(sink), scale, flags, rope_base, rope_dims,
+                                       _p(out), _p(lse_out), _p(ws), ws.numel() * ws.element_size()))
+        return
     _check(lib().csa_attend(_stream(stream), dt_q, dt_kv, B, Tq, H, D, N_cap, m, k, W, q_pos0,
                             _p(q), _p(kv), _p(kv_scale), _p(idx), _p(win), _p(win_scale), _p(sink),
                             scale, flags, rope_base, rope_dims, _p(out), _p(lse_out), _p(ws),
@@ -182,13 +214,19 @@ def csa_attend(dt_q, dt_kv, q, kv, idx, win, sink, out, *, m, W, q_pos0, scale, 
 
 def hca_attend(dt_q, dt_kv, q, kv, win, sink, out, *, m, W, q_pos0, scale, N_cap=None, kv_scale=None,
                win_scale=None, flags=0, rope_base=10000.0, rope_dims=0, lse_out=None, ws=None,
-               stream=None):
+               stream=None, q_pos=None):
     """HCA dense attention over every visible entry; arguments as csa_attend without idx."""
     B, Tq, H, D = q.shape
     N_cap = kv.shape[1] if N_cap is None else N_cap
     need = hca_attend_workspace(dt_q, dt_kv, B, Tq, H, D, N_cap, m, W, q_pos0)
     if ws is None:
         ws = _workspace(need, q)
+    if q_pos is not None:
+        _check(lib().hca_attend_ragged(_stream(stream), dt_q, dt_kv, B, Tq, H, D, N_cap, m, W, q_pos0,
+                                       _q_pos(q_pos, B), _p(q), _p(kv), _p(kv_scale), _p(win),
+                                       _p(win_scale), _p(sink), scale, flags, rope_base, rope_dims,
+                                       _p(out), _p(lse_out), _p(ws), ws.numel() * ws.element_size()))
+        return
     _check(lib().hca_attend(_stream(stream), dt_q, dt_kv, B, Tq, H, D, N_cap, m, W, q_pos0, _p(q),
                             _p(kv), _p(kv_scale), _p(win), _p(win_scale), _p(sink), scale, flags,
                             rope_base, rope_dims, _p(out), _p(lse_out), _p(ws),

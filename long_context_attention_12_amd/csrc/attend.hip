@@ -46,8 +46,8 @@ struct RowSpan {
   int64_t n_ent, win_lo, nrows;
 };
 
-__device__ __forceinline__ RowSpan row_span(const AttendArgs& a, int t) {
-  const int64_t p = a.q_pos0 + t;
+__device__ __forceinline__ RowSpan row_span(const AttendArgs& a, int b, int t) {
+  const int64_t p = seq_pos(a.q_pos, a.q_pos0, b) + t;
   RowSpan r;
   if (a.sparse) {
     r.n_ent = a.k;
@@ -75,7 +75,7 @@ __device__ __forceinline__ int64_t row_source(const AttendArgs& a, int b, int t,
   if (v < rs.nrows) {
     *kind = 1;
     const int64_t pos = rs.win_lo + (v - rs.n_ent);
-    return pos - (a.q_pos0 - (a.W - 1));
+    return pos - (seq_pos(a.q_pos, a.q_pos0, b) - (a.W - 1));
   }
   return -1;
 }
@@ -486,11 +486,11 @@ __device__ __forceinline__ bool work_item(const SplitPlan& sp, int Tq, int i, in
 // when the logits outgrew the headroom (an exact recompute follows).
 // Angles of the inverse RoPE at query t: rope_tab[i] = (cos, sin) of pair i
 // at position -(q_pos0 + t), filled once per workgroup.
-__device__ __forceinline__ void fill_rope_table(const AttendArgs& a, int t, float2* rope_tab) {
+__device__ __forceinline__ void fill_rope_table(const AttendArgs& a, int b, int t, float2* rope_tab) {
   const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
   for (int i = threadIdx.x; i < R / 2; i += blockDim.x) {
     float sn, cs;
-    rope_sincos(-static_cast<double>(a.q_pos0 + t), i, R, static_cast<double>(a.rope_base), &sn, &cs);
+    rope_sincos(-static_cast<double>(seq_pos(a.q_pos, a.q_pos0, b) + t), i, R, static_cast<double>(a.rope_base), &sn, &cs);
     rope_tab[i] = make_float2(cs, sn);
   }
 }
@@ -558,8 +558,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
   const int b = blockIdx.z;
   const bool active = wid * 16 < sp.HG;
   const int head = hg * sp.HG + wid * 16 + r16;
-  const RowSpan rs = row_span(a, t);
-  if (sp.S == 1) fill_rope_table(a, t, rope_tab);   // read after the tile loop's barriers
+  const RowSpan rs = row_span(a, b, t);
+  if (sp.S == 1) fill_rope_table(a, b, t, rope_tab);   // read after the tile loop's barriers
   const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
   int64_t r_end = r_begin + sp.RS;
   if (r_end > rs.nrows) r_end = rs.nrows;
@@ -693,8 +693,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
   const int b = blockIdx.z;
   const bool active = wid * 16 * NHT < sp.HG;
   const int head0 = hg * sp.HG + wid * 16 * NHT + r16;   // + 16 ht for head tile ht
-  const RowSpan rs = row_span(a, t);
-  if (sp.S == 1) fill_rope_table(a, t, rope_tab);   // read after the tile loop's barriers
+  const RowSpan rs = row_span(a, b, t);
+  if (sp.S == 1) fill_rope_table(a, b, t, rope_tab);   // read after the tile loop's barriers
   const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
   int64_t r_end = r_begin + sp.RS;
   if (r_end > rs.nrows) r_end = rs.nrows;
@@ -1075,8 +1075,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArg
   const int b = blockIdx.z;
   const bool active = wid * 16 * NHT < sp.HG;
   const int head0 = hg * sp.HG + wid * 16 * NHT + r16;   // + 16 ht for head tile ht
-  const RowSpan rs = row_span(a, t);
-  if (sp.S == 1) fill_rope_table(a, t, rope_tab);
+  const RowSpan rs = row_span(a, b, t);
+  if (sp.S == 1) fill_rope_table(a, b, t, rope_tab);
   const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
   int64_t r_end = r_begin + sp.RS;
   if (r_end > rs.nrows) r_end = rs.nrows;
@@ -1222,7 +1222,7 @@ __global__ __launch_bounds__(kF32Threads) void attend_f32_kernel(AttendArgs a, S
   const int t = blockIdx.y, b = blockIdx.z;
   const int h0 = hg * HG;
   const int nh = min(HG, a.H - h0);
-  const RowSpan rs = row_span(a, t);
+  const RowSpan rs = row_span(a, b, t);
   const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
   int64_t r_end = r_begin + sp.RS;
   if (r_end > rs.nrows) r_end = rs.nrows;
@@ -1358,7 +1358,7 @@ __device__ void recompute_split(const AttendArgs& a, int RS, int b, int t, int h
                                 float* lc, float& m_out, float& z_out, float2& o_out) {
   const int c = threadIdx.x;
   const bool own = 2 * c < a.D;
-  const RowSpan rs = row_span(a, t);
+  const RowSpan rs = row_span(a, b, t);
   const int64_t r0 = static_cast<int64_t>(s) * RS;
   int64_t r1 = r0 + RS;
   if (r1 > rs.nrows) r1 = rs.nrows;
@@ -1482,7 +1482,7 @@ __device__ void combine_row(const AttendArgs& a, int S, int RS, int b, int t, in
     const int d0 = 2 * c;
     if (d0 >= D - R) {
       float sn, cs;
-      rope_sincos(-static_cast<double>(a.q_pos0 + t), (d0 - (D - R)) / 2, R,
+      rope_sincos(-static_cast<double>(seq_pos(a.q_pos, a.q_pos0, b) + t), (d0 - (D - R)) / 2, R,
                   static_cast<double>(a.rope_base), &sn, &cs);
       const float nu = u * cs - v * sn, nv = u * sn + v * cs;
       u = nu;
@@ -1523,7 +1523,7 @@ __global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int 
   const int t = blockIdx.y, b = blockIdx.z, wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int D = a.D, h0 = blockIdx.x * 4, h = h0 + wid;
   if (threadIdx.x == 0) any_nan = 0u;
-  fill_rope_table(a, t, rope_tab);
+  fill_rope_table(a, b, t, rope_tab);
   __syncthreads();
   const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + h;
   const bool live = h < a.H;

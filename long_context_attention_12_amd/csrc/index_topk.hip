@@ -103,13 +103,14 @@ template <int HI, int DI>
 __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
     float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
-    int m, bool round_bf16) {
+    const int64_t* __restrict__ q_pos, int m, bool round_bf16) {
   constexpr int QPB = 16 / HI;       // queries per M tile
   constexpr int KS = DI / 32;        // K steps
   constexpr int UNR = kKeysPerWave / 16;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int b = blockIdx.z;
+  q_pos0 = seq_pos(q_pos, q_pos0, b);                // this sequence's position
   const int tq0 = t_off + blockIdx.y * QPB;          // first query of this M tile
   const int t_end = min(Tq, t_off + Tc);             // queries of this chunk only
   const int tq_last = min(tq0 + QPB, t_end) - 1;
@@ -175,8 +176,8 @@ constexpr int kTiledMinQueries = 64;
 template <int HI>
 __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
-    float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, int m,
-    int64_t keys_per_wg, bool round_bf16) {
+    float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
+    const int64_t* __restrict__ q_pos, int m, int64_t keys_per_wg, bool round_bf16) {
   constexpr int DI = 128, KS = DI / 32, MB = 4, NB = kTileKeys / 16, QPB = 16 / HI;
   constexpr int QPW = MB * QPB, QPWG = 4 * QPW;
   constexpr int ROWB = DI * 2;                       // bytes per key row
@@ -187,6 +188,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int b = blockIdx.z;
+  q_pos0 = seq_pos(q_pos, q_pos0, b);                // this sequence's position
   const int t_end = min(Tq, t_off + Tc);
   const int tw0 = t_off + static_cast<int>(blockIdx.y) * QPWG;
   if (tw0 >= t_end) return;
@@ -306,13 +308,15 @@ template <int HI>
 __global__ __launch_bounds__(kScoreThreads) void index_score_fp4_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, float* __restrict__ scores, int64_t ld,
-    int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, int m, bool round_bf16) {
+    int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m,
+    bool round_bf16) {
   constexpr int QPB = 16 / HI;
   constexpr int UNR = kFp4KeysPerWave / 16;
   constexpr int ROW = 64;                          // packed bytes per 128-channel row
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int b = blockIdx.z;
+  q_pos0 = seq_pos(q_pos, q_pos0, b);                // this sequence's position
   const int tq0 = t_off + blockIdx.y * QPB;
   const int t_end = min(Tq, t_off + Tc);
   const int tq_last = min(tq0 + QPB, t_end) - 1;
@@ -371,9 +375,10 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_fp4_kernel(
 __global__ __launch_bounds__(kScoreThreads) void index_score_f32_kernel(
     const float* __restrict__ qI, const float* __restrict__ w, const float* __restrict__ kI,
     float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
-    int m, int HI, int DI, bool round_bf16) {
+    const int64_t* __restrict__ q_pos, int m, int HI, int DI, bool round_bf16) {
   extern __shared__ float qs[];                 // [HI * DI + HI]
   const int b = blockIdx.z, tl = blockIdx.y, t = t_off + tl;
+  q_pos0 = seq_pos(q_pos, q_pos0, b);           // this sequence's position
   int64_t nv = n_visible(q_pos0 + t, m);
   if (nv > N_cap) nv = N_cap;
   const int64_t j = static_cast<int64_t>(blockIdx.x) * kScoreThreads + threadIdx.x;
@@ -511,9 +516,10 @@ struct SelRow {
 };
 
 __device__ __forceinline__ SelRow sel_row(const float* scores, int64_t ld, int64_t N_cap, int Tq, int t_off, int Tc,
-                                          int64_t q_pos0, int m, int k, int32_t* idx_out, float* score_out) {
+                                          int64_t q_pos0, const int64_t* q_pos, int m, int k, int32_t* idx_out,
+                                          float* score_out) {
   const int b = blockIdx.y, tl = blockIdx.x, t = t_off + tl;
-  int64_t n = n_visible(q_pos0 + t, m);
+  int64_t n = n_visible(seq_pos(q_pos, q_pos0, b) + t, m);
   if (n > N_cap) n = N_cap;
   SelRow r;
   r.s = scores + (static_cast<int64_t>(b) * Tc + tl) * ld;
@@ -609,12 +615,12 @@ __device__ __forceinline__ void select_by_passes(const SelRow& row, int k, bool 
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t N_cap, int Tq, int t_off, int Tc,
-    int64_t q_pos0, int m, int k, bool key16, int32_t* __restrict__ idx_out,
+    int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int k, bool key16, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
   __shared__ uint32_t hist[kMaxBins];
   __shared__ __attribute__((aligned(16))) uint32_t wsum[kSelThreads / 64];
   __shared__ uint32_t sh_digit, sh_krem;
-  const SelRow row = sel_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, m, k, idx_out, score_out);
+  const SelRow row = sel_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, q_pos, m, k, idx_out, score_out);
   if (row.n <= k) {
     select_all(row, k);
     return;
@@ -684,8 +690,8 @@ __device__ __forceinline__ uint32_t raw_key(const RoundRaw<NI>& r, int j, bool k
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_long_kernel(
     const float* __restrict__ scores, int64_t ld, int32_t* __restrict__ spill, int64_t N_cap, int Tq, int t_off,
-    int Tc, int64_t q_pos0, int m, int k, bool key16, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out) {
+    int Tc, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int k, bool key16,
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
   __shared__ uint32_t hist[kMaxBins];
   __shared__ __attribute__((aligned(16))) uint32_t wsum[kSelThreads / 64];
   __shared__ uint32_t sh_digit, sh_krem, sh_cmin, sh_cmax;
@@ -694,7 +700,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_long_kernel(
   __shared__ uint32_t c_key[kLongCap];    // candidates inside b*, increasing index
   __shared__ int32_t c_idx[kLongCap];
   const int tid = threadIdx.x;
-  const SelRow row = sel_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, m, k, idx_out, score_out);
+  const SelRow row = sel_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, q_pos, m, k, idx_out, score_out);
   if (row.n <= k) {
     select_all(row, k);
     return;
@@ -851,10 +857,10 @@ void launch_score_bf16_hi(LaunchScope& ls, const IndexArgs& a, float* sc, int64_
   const uint16_t* q = static_cast<const uint16_t*>(a.qI);
   const uint16_t* k = static_cast<const uint16_t*>(a.kI);
   switch (a.d_I) {
-    case 64: ls.launch(index_score_bf16_kernel<HI, 64>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
-    case 128: ls.launch(index_score_bf16_kernel<HI, 128>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
-    case 256: ls.launch(index_score_bf16_kernel<HI, 256>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
-    default: ls.launch(index_score_bf16_kernel<HI, 32>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, rb); break;
+    case 64: ls.launch(index_score_bf16_kernel<HI, 64>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb); break;
+    case 128: ls.launch(index_score_bf16_kernel<HI, 128>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb); break;
+    case 256: ls.launch(index_score_bf16_kernel<HI, 256>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb); break;
+    default: ls.launch(index_score_bf16_kernel<HI, 32>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb); break;
   }
 }
 
@@ -900,7 +906,7 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
         scope.launch(index_score_f32_kernel, grid, dim3(kScoreThreads),
                      static_cast<uint32_t>((a.H_I * a.d_I + a.H_I) * sizeof(float)),
                            static_cast<const float*>(a.qI), a.w, static_cast<const float*>(a.kI), sc, ld,
-                           a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, a.H_I, a.d_I, key16);
+                           a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, a.H_I, a.d_I, key16);
       } else if (a.dt == LCA_MXFP4) {
         const int QPB = 16 / a.H_I;
         dim3 grid((nv_max + kFp4KeysPerWG - 1) / kFp4KeysPerWG, (tcn + QPB - 1) / QPB, a.B);
@@ -909,11 +915,11 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
         const uint8_t* k = static_cast<const uint8_t*>(a.kI);
         const uint8_t* ks = static_cast<const uint8_t*>(a.kI_scale);
         switch (a.H_I) {
-          case 1: scope.launch(index_score_fp4_kernel<1>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
-          case 2: scope.launch(index_score_fp4_kernel<2>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
-          case 4: scope.launch(index_score_fp4_kernel<4>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
-          case 8: scope.launch(index_score_fp4_kernel<8>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
-          default: scope.launch(index_score_fp4_kernel<16>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, key16); break;
+          case 1: scope.launch(index_score_fp4_kernel<1>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
+          case 2: scope.launch(index_score_fp4_kernel<2>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
+          case 4: scope.launch(index_score_fp4_kernel<4>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
+          case 8: scope.launch(index_score_fp4_kernel<8>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
+          default: scope.launch(index_score_fp4_kernel<16>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
         }
       } else if (a.d_I == 128 && tcn >= kTiledMinQueries) {
         // many queries: key tiles through LDS, ~2048 workgroups over (keys, queries)
@@ -930,11 +936,11 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
         const uint16_t* q = static_cast<const uint16_t*>(a.qI);
         const uint16_t* k = static_cast<const uint16_t*>(a.kI);
         switch (a.H_I) {
-          case 1: scope.launch(index_score_tiled_kernel<1>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
-          case 2: scope.launch(index_score_tiled_kernel<2>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
-          case 4: scope.launch(index_score_tiled_kernel<4>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
-          case 8: scope.launch(index_score_tiled_kernel<8>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
-          default: scope.launch(index_score_tiled_kernel<16>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.m, per, key16); break;
+          case 1: scope.launch(index_score_tiled_kernel<1>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
+          case 2: scope.launch(index_score_tiled_kernel<2>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
+          case 4: scope.launch(index_score_tiled_kernel<4>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
+          case 8: scope.launch(index_score_tiled_kernel<8>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
+          default: scope.launch(index_score_tiled_kernel<16>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
         }
       } else {
         const int QPB = 16 / a.H_I;
@@ -955,10 +961,10 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
       // every row's list is at most nv_max long (and nv_max > kRound implies N_cap > kRound)
       if (nv_max > kRound)
         scope.launch(topk_select_long_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, static_cast<const float*>(sc), ld,
-                     spill, a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.m, a.k, key16, a.idx_out, a.score_out);
+                     spill, a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16, a.idx_out, a.score_out);
       else
         scope.launch(topk_select_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, static_cast<const float*>(sc), ld,
-                     a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.m, a.k, key16, a.idx_out, a.score_out);
+                     a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16, a.idx_out, a.score_out);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

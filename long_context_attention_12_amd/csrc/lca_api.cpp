@@ -325,4 +325,60 @@ int hca_attend(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, i
   return run_attend(stream, a, ws, ws_bytes, "hca_attend");
 }
 
+// ---------------------------------------------------------------------------
+// Ragged batches: sequence b's queries sit at q_pos[b] + t (device array),
+// with q_pos0 the bound that sizes workspaces, plans and validation.
+static int check_q_pos(const int64_t* q_pos, const char* fn) {
+  if (!q_pos) return fail(LCA_ERR_ARG, "%s: q_pos is required", fn);
+  if (reinterpret_cast<uintptr_t>(q_pos) % 8 != 0) return fail(LCA_ERR_ALIGN, "%s: q_pos must be 8-byte aligned", fn);
+  return LCA_OK;
+}
+
+int csa_index_topk_ragged(void* stream, int dt, int B, int Tq, int H_I, int d_I, int64_t N_cap, int m, int k,
+                          int64_t q_pos_max, const int64_t* q_pos, const void* qI, const void* qI_scale,
+                          const float* w, const void* kI, const void* kI_scale, uint32_t flags, int32_t* idx_out,
+                          float* score_out, void* ws, size_t ws_bytes) {
+  int st = check_q_pos(q_pos, "csa_index_topk_ragged");
+  if (st != LCA_OK) return st;
+  lca::IndexArgs a{dt, B, Tq, H_I, d_I, m, k, N_cap, q_pos_max, qI, qI_scale, kI, kI_scale, w, flags, idx_out,
+                   score_out, q_pos};
+  st = check_index(a);
+  if (st != LCA_OK) return st;
+  const size_t need = lca::index_topk_workspace(a);
+  if (!ws || ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "csa_index_topk_ragged: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned16(ws)) return fail(LCA_ERR_ALIGN, "csa_index_topk_ragged: workspace must be 16-byte aligned");
+  return hip_status(lca::launch_index_topk(static_cast<hipStream_t>(stream), a, ws, ws_bytes), "csa_index_topk_ragged");
+}
+
+int csa_attend_ragged(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int k,
+                      int W, int64_t q_pos_max, const int64_t* q_pos, const void* q, const void* kv,
+                      const float* kv_scale, const int32_t* idx, const void* win, const float* win_scale,
+                      const float* sink, float scale, uint32_t flags, float rope_base, int rope_dims, void* out,
+                      float* lse_out, void* ws, size_t ws_bytes) {
+  int st = check_q_pos(q_pos, "csa_attend_ragged");
+  if (st != LCA_OK) return st;
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = k; a.W = W;
+  a.sparse = true; a.N_cap = N_cap; a.q_pos0 = q_pos_max; a.q = q; a.kv = kv; a.win = win;
+  a.kv_scale = kv_scale; a.win_scale = win_scale; a.sink = sink; a.idx = idx; a.scale = scale;
+  a.flags = flags; a.rope_base = rope_base; a.rope_dims = rope_dims; a.out = out; a.lse_out = lse_out;
+  a.q_pos = q_pos;
+  return run_attend(stream, a, ws, ws_bytes, "csa_attend_ragged");
+}
+
+int hca_attend_ragged(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int W,
+                      int64_t q_pos_max, const int64_t* q_pos, const void* q, const void* kv, const float* kv_scale,
+                      const void* win, const float* win_scale, const float* sink, float scale, uint32_t flags,
+                      float rope_base, int rope_dims, void* out, float* lse_out, void* ws, size_t ws_bytes) {
+  int st = check_q_pos(q_pos, "hca_attend_ragged");
+  if (st != LCA_OK) return st;
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = 0; a.W = W;
+  a.sparse = false; a.N_cap = N_cap; a.q_pos0 = q_pos_max; a.q = q; a.kv = kv; a.win = win;
+  a.kv_scale = kv_scale; a.win_scale = win_scale; a.sink = sink; a.idx = nullptr; a.scale = scale;
+  a.flags = flags; a.rope_base = rope_base; a.rope_dims = rope_dims; a.out = out; a.lse_out = lse_out;
+  a.q_pos = q_pos;
+  return run_attend(stream, a, ws, ws_bytes, "hca_attend_ragged");
+}
+
 }  // extern "C"

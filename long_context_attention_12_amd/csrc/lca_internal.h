@@ -59,6 +59,7 @@ struct IndexArgs {
   uint32_t flags;
   int32_t* idx_out;
   float* score_out;
+  const int64_t* q_pos;      // per-sequence positions (ragged batch) or null: all at q_pos0
 };
 size_t index_topk_workspace(const IndexArgs& a);
 hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t ws_bytes);
@@ -76,8 +77,18 @@ struct AttendArgs {
   int rope_dims;
   void* out;
   float* lse_out;
+  const int64_t* q_pos;      // per-sequence positions (ragged batch) or null: all at q_pos0
 };
 size_t attend_workspace(const AttendArgs& a);
+
+// Position of sequence b's first query: q_pos[b] clamped to [0, bound] for a
+// ragged batch (the bound, q_pos0, sizes every grid, plan and buffer, so a
+// clamped position keeps every access inside them), else the bound itself.
+__device__ __forceinline__ int64_t seq_pos(const int64_t* q_pos, int64_t bound, int b) {
+  if (!q_pos) return bound;
+  const int64_t p = q_pos[b];
+  return p < 0 ? 0 : (p > bound ? bound : p);
+}
 hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t ws_bytes);
 
 }  // namespace lca

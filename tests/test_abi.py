@@ -121,6 +121,35 @@ def test_attend_validation(lib):
     _expect(h, -2, "524288")
 
 
+def test_ragged_validation(lib):
+    # The ragged calls take the uniform calls' checks with q_pos0 as the bound,
+    # and need q_pos itself (device memory, 8-byte aligned).
+    fake = 0x10000
+    ws_i = lib.csa_index_topk_workspace(1, 2, 1, 4, 128, 4096, 4, 512, 16383, 0)
+
+    def idx_call(q_pos, N=4096, pos=16383):
+        return lib.csa_index_topk_ragged(None, 1, 2, 1, 4, 128, N, 4, 512, pos, q_pos, fake, None, fake,
+                                         fake, None, 0, fake, None, fake, ws_i)
+    _expect(idx_call(None), -1, "q_pos is required")
+    _expect(idx_call(fake + 4), -3, "8-byte")
+    _expect(idx_call(fake, N=100), -1, "N_cap")
+    need = lib.csa_attend_workspace(1, 1, 2, 1, 64, 512, 32768, 4, 512, 128, 131072)
+
+    def att_call(q_pos, H=64):
+        return lib.csa_attend_ragged(None, 1, 1, 2, 1, H, 512, 32768, 4, 512, 128, 131072, q_pos, fake,
+                                     fake, None, fake, fake, None, fake, 0.04, 0, 10000.0, 0, fake, None,
+                                     fake, need)
+    _expect(att_call(None), -1, "q_pos is required")
+    _expect(att_call(fake + 2), -3, "8-byte")
+    _expect(att_call(fake, H=40), -2, "H must")
+    h = lib.hca_attend_ragged(None, 1, 1, 2, 1, 64, 512, 100, 128, 128, 1048576, fake, fake, fake, None,
+                              fake, None, fake, 0.04, 0, 10000.0, 0, fake, None, fake, 1 << 30)
+    _expect(h, -1, "N_cap")
+    h = lib.hca_attend_ragged(None, 1, 1, 2, 1, 64, 512, 100, 128, 128, 1048576, None, fake, fake, None,
+                              fake, None, fake, 0.04, 0, 10000.0, 0, fake, None, fake, 1 << 30)
+    _expect(h, -1, "q_pos is required")
+
+
 def test_quantize_validation(lib):
     fake = 0x10000
     _expect(lib.lca_quantize_rows(None, 1, 4, 512, 64, fake, fake, fake), -2, "dt_out")
