@@ -10,11 +10,12 @@ copies are rotated so the 256 MB last-level cache cannot serve a step from the
 previous one.
 
 Also measured (secondary, same line): HCA decode, V4-Pro shaped: batch 8,
-1048576 context tokens (8192 entries), 128 heads.
+1048576 context tokens (8192 entries), 128 heads; both decode workloads again
+as ragged batches (each sequence at its own position, the context as bound).
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Counter runs: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) over
-``bench.py --no-secondary --no-prefill --no-mixed --copy-calibration 1024``,
+``bench.py --no-secondary --no-prefill --no-mixed --no-ragged --copy-calibration 1024``,
 then ``bench.py --pmc-summary F.csv W.csv --copy-calibration 1024``.
 """
 
@@ -40,6 +41,10 @@ import workloads as WL  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 COPY_REPS = 3                  # calibration copies per counter run
 DEV = "cuda"
+# sources of the CSA decode scoring kernel: stored counter readings hold for these bytes only
+SCORE_SOURCES = ["long_context_attention_12_amd/csrc/index_topk.hip",
+                 "long_context_attention_12_amd/csrc/lca_device.h",
+                 "long_context_attention_12_amd/csrc/lca_internal.h"]
 
 
 def _bf16(x):
@@ -60,7 +65,9 @@ def set_recall(ref, got):
     return float(np.mean(fr))
 
 
-def csa_decode_setup(d, copies):
+def csa_decode_setup(d, copies, q_pos=None):
+    """One CSA decode step over d; q_pos (int64 [B] on the GPU) makes the batch
+    ragged, with d["q_pos0"] as the bound."""
     base = {"E": _bf16(d["E"]), "kI": _bf16(d["kI"]), "q": _bf16(d["q"]), "qI": _bf16(d["qI"]),
             "win": _bf16(d["win"]), "w": _f32(d["w"]), "sink": _f32(d["sink"])}
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
@@ -75,9 +82,11 @@ def csa_decode_setup(d, copies):
 
     def step(i):
         s = sets[i % copies]
-        L.csa_index_topk(L.BF16, s["qI"], s["w"], s["kI"], idx, m=m, k=k, q_pos0=d["q_pos0"], ws=ws_i)
+        L.csa_index_topk(L.BF16, s["qI"], s["w"], s["kI"], idx, m=m, k=k, q_pos0=d["q_pos0"], ws=ws_i,
+                         q_pos=q_pos)
         L.csa_attend(L.BF16, L.BF16, s["q"], s["E"], idx, s["win"], s["sink"], out, m=m, W=d["W"],
-                     q_pos0=d["q_pos0"], scale=1 / math.sqrt(D), flags=L.INV_ROPE, rope_dims=64, ws=ws_a)
+                     q_pos0=d["q_pos0"], scale=1 / math.sqrt(D), flags=L.INV_ROPE, rope_dims=64, ws=ws_a,
+                     q_pos=q_pos)
 
     def recall():
         """Top-k on bf16-rounded scores against top-k on fp32 scores, same inputs."""
@@ -92,7 +101,7 @@ def csa_decode_setup(d, copies):
     return step
 
 
-def hca_decode_setup(d, copies):
+def hca_decode_setup(d, copies, q_pos=None):
     base = {"E": _bf16(d["E"]), "q": _bf16(d["q"]), "win": _bf16(d["win"]), "sink": _f32(d["sink"])}
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
     B, H, D = d["B"], d["H"], d["D"]
@@ -104,7 +113,8 @@ def hca_decode_setup(d, copies):
     def step(i):
         s = sets[i % copies]
         L.hca_attend(L.BF16, L.BF16, s["q"], s["E"], s["win"], s["sink"], out, m=d["m"], W=d["W"],
-                     q_pos0=d["q_pos0"], scale=1 / math.sqrt(D), flags=L.INV_ROPE, rope_dims=64, ws=ws)
+                     q_pos0=d["q_pos0"], scale=1 / math.sqrt(D), flags=L.INV_ROPE, rope_dims=64, ws=ws,
+                     q_pos=q_pos)
     return step
 
 
@@ -236,6 +246,10 @@ def csa_prefill_setup(d):
     return step, flops
 
 
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def timed(step, steps, warmup):
     for i in range(warmup):
         step(i)
@@ -274,6 +288,110 @@ def hca_decode_bytes(d):
     B, H, D, W = d["B"], d["H"], d["D"], d["W"]
     N = d["E"].shape[1]
     return B * ((N + W) * D * 2 + 2 * H * D * 2)
+
+
+def decode_state_leg(d, copies, steps, warmup, headline_ms):
+    """The headline step preceded by the decode-time state updates of the token
+    it decodes: append it to the entry compressor (RMSNorm + RoPE, bf16 cache)
+    and to the indexer-key compressor (both m = 4 with overlap), store its raw
+    row in the 128-row window ring, then index top-k + attention reading the
+    window from the ring. The token sits at position ctx - 1, so each step
+    closes a block and writes one entry and one key per sequence (the most
+    work an append does)."""
+    B, H, D, m, k, W = d["B"], d["H"], d["D"], d["m"], d["k"], d["W"]
+    N, H_I, d_I = d["E"].shape[1], d["H_I"], d["d_I"]
+    p = d["q_pos0"] - 1
+    g = torch.Generator(device=DEV)
+    g.manual_seed(21)
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=g, device=DEV) * scale).to(torch.bfloat16)
+    sets = []
+    for c in range(copies):
+        sets.append({"E": _bf16(d["E"]), "kI": _bf16(d["kI"]), "q": _bf16(d["q"]), "qI": _bf16(d["qI"]),
+                     "w": _f32(d["w"]), "ring": rnd(B, W, D, scale=D ** -0.5),
+                     "ca": rnd(B, D, scale=D ** -0.5), "cb": rnd(B, D, scale=D ** -0.5),
+                     "ica": rnd(B, d_I, scale=d_I ** -0.5), "icb": rnd(B, d_I, scale=d_I ** -0.5),
+                     "kvw": rnd(B, D, scale=D ** -0.5),
+                     "z": torch.randn(4, B, generator=g, device=DEV)})
+    sink = _f32(d["sink"])
+    norm_w = torch.ones(D, dtype=torch.float32, device=DEV)
+    stE = torch.zeros(L.csa_compress_state_bytes(L.BF16, B, D, m, True), dtype=torch.uint8, device=DEV)
+    stK = torch.zeros(L.csa_compress_state_bytes(L.BF16, B, d_I, m, True), dtype=torch.uint8, device=DEV)
+    qp = torch.full((B,), p, dtype=torch.int64, device=DEV)
+    ws_i = torch.empty(L.csa_index_topk_workspace(L.BF16, B, 1, H_I, d_I, N, m, k, p), dtype=torch.uint8,
+                       device=DEV)
+    ws_a = torch.empty(L.csa_attend_workspace(L.BF16, L.BF16, B, 1, H, D, N, m, k, W, p), dtype=torch.uint8,
+                       device=DEV)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=DEV)
+
+    for s in sets:                 # the three appends of a step as one launch (lca_decode_append)
+        s["jobs"] = [L.append_job_compress(L.BF16, L.BF16, s["cb"], s["z"][1], m, stE, s["E"], ca=s["ca"],
+                                           za=s["z"][0], flags=L.NORM | L.ROPE, norm_w=norm_w, rope_dims=64),
+                     L.append_job_compress(L.BF16, L.BF16, s["icb"], s["z"][3], m, stK, s["kI"], ca=s["ica"],
+                                           za=s["z"][2]),
+                     L.append_job_window(L.BF16, L.BF16, s["kvw"], s["ring"])]
+
+    def decode(s):
+        L.csa_index_topk(L.BF16, s["qI"], s["w"], s["kI"], idx, m=m, k=k, q_pos0=p, ws=ws_i)
+        L.csa_attend(L.BF16, L.BF16, s["q"], s["E"], idx, s["ring"], sink, out, m=m, W=W, q_pos0=p,
+                     scale=1 / math.sqrt(D), flags=L.INV_ROPE | L.WIN_RING, rope_dims=64, ws=ws_a)
+
+    def step(i):
+        s = sets[i % copies]
+        L.lca_decode_append(s["jobs"], qp, pos_max=p)
+        decode(s)
+
+    def step_separate(i):
+        s = sets[i % copies]
+        L.csa_compress_append(L.BF16, L.BF16, s["cb"], s["z"][1], m, qp, stE, s["E"], pos_max=p, ca=s["ca"],
+                              za=s["z"][0], flags=L.NORM | L.ROPE, norm_w=norm_w, rope_dims=64)
+        L.csa_compress_append(L.BF16, L.BF16, s["icb"], s["z"][3], m, qp, stK, s["kI"], pos_max=p, ca=s["ica"],
+                              za=s["z"][2])
+        L.lca_window_append(L.BF16, L.BF16, s["kvw"], qp, s["ring"], pos_max=p)
+        decode(s)
+    ms = 1e3 * timed(step, steps, warmup) / steps
+    kt = kernel_times(step, steps)
+    ms_sep = 1e3 * timed(step_separate, steps, warmup) / steps
+    kt_sep = kernel_times(step_separate, steps)
+    progress(f"csa decode step with state updates: {ms:.4f} ms/step ({ms_sep:.4f} with separate appends)")
+    return {"workload": "csa_decode_step_with_state_b16_ctx131072", "tokens_per_s": B / (ms * 1e-3),
+            "ms_per_step": ms, "headline_ms": headline_ms, "state_update_ms": ms - headline_ms,
+            "kernels_us": {k_: round(v["avg_us"], 3) for k_, v in kt.items()},
+            "separate_appends": {"ms_per_step": ms_sep,
+                                 "kernels_us": {k_: round(v["avg_us"], 3) for k_, v in kt_sep.items()}}}
+
+
+def ragged_bytes(d, pos):
+    """Algorithmic bytes of a ragged decode step: each sequence moves what its
+    own position makes visible (indexer keys and, for HCA, entries)."""
+    H, D, W, m = d["H"], d["D"], d["W"], d["m"]
+    nv = [min((int(p) + 1) // m, d["E"].shape[1]) for p in pos]
+    if "kI" in d:
+        k, H_I, d_I = d["k"], d["H_I"], d["d_I"]
+        return sum(n * d_I * 2 + H_I * d_I * 2 + H_I * 4 + (min(k, n) + W) * D * 2 + 2 * H * D * 2
+                   for n in nv)
+    return sum((n + W) * D * 2 + 2 * H * D * 2 for n in nv)
+
+
+def ragged_leg(d, copies, steps, warmup, seed, uniform_ms):
+    """The same decode batch with each sequence at its own position, drawn
+    uniformly from [window, context] (last one at the context: the bound)."""
+    pos = WL.ragged_positions(seed, d["B"], d["W"], d["q_pos0"])
+    qp = torch.from_numpy(pos).to(DEV)
+    setup = csa_decode_setup if "kI" in d else hca_decode_setup
+    rstep = setup(d, copies, q_pos=qp)
+    rms = 1e3 * timed(rstep, steps, warmup) / steps
+    rk = kernel_times(rstep, steps)
+    rb = ragged_bytes(d, pos)
+    progress(f"ragged {'csa' if 'kI' in d else 'hca'} decode: {rms:.4f} ms/step")
+    return {"tokens_per_s": d["B"] / (rms * 1e-3), "ms_per_step": rms,
+            "mean_context": float(np.mean(pos)), "bound": d["q_pos0"],
+            "uniform_at_bound_ms": uniform_ms, "speedup_vs_uniform_at_bound": uniform_ms / rms,
+            "kernels_us": {k: round(v["avg_us"], 3) for k, v in rk.items()},
+            "algorithmic_bytes": rb, "achieved_GBs": rb / (rms * 1e-3) / 1e9,
+            "hbm_frac": rb / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def hca_decode_flops(d):
@@ -350,8 +468,7 @@ def pmc_summary(fetch_csv, write_csv, copy_mib, out_json):
     f_scale = n / (cf * 1024.0)
     w_scale = n / (cw * 1024.0)
     fb, wb = kf * 1024.0 * f_scale, kw * 1024.0 * w_scale
-    src = source_hash(["long_context_attention_12_amd/csrc/index_topk.hip",
-                       "long_context_attention_12_amd/csrc/lca_device.h"])
+    src = source_hash(SCORE_SOURCES)
     rec = {"csa_decode_b16_ctx131072": {"index_score": {
         "source_hash": src, "kernel": name, "dispatches": nd,
         "fetch_kib_raw": kf, "write_kib_raw": kw, "copy_bytes": n,
@@ -404,6 +521,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -427,11 +545,11 @@ def main():
     ms = 1e3 * elapsed / args.steps
     B = d["B"]
     kt = kernel_times(step, args.steps)
+    progress(f"csa decode: {ms:.4f} ms/step")
     ib, ab = csa_decode_bytes(d)
     score = kt.get("index_score", {"avg_us": float("nan")})
     achieved = ib / (score["avg_us"] * 1e-6) / 1e9
-    src = source_hash(["long_context_attention_12_amd/csrc/index_topk.hip",
-                       "long_context_attention_12_amd/csrc/lca_device.h"])
+    src = source_hash(SCORE_SOURCES)
     traffic = load_traffic("index_score", "csa_decode_b16_ctx131072", src)
     result = {
         "metric": "CSA/HCA decode tokens/s at 128K-1M ctx; achieved HBM GB/s vs peak (1 GPU)",
@@ -461,12 +579,17 @@ def main():
         # (the pages report 99.7% on real-model data; here seeded synthetic inputs)
         "bf16_score_topk_recall": {"csa_decode": step.recall(), "pages": 0.997},
     }
+    if not args.no_ragged:
+        result["ragged"] = {"csa_decode_b16_ctx_le131072": ragged_leg(d, args.copies, args.steps, args.warmup,
+                                                                      12, ms)}
+        result["decode_state"] = decode_state_leg(d, args.copies, args.steps, args.warmup, ms)
     if not args.no_secondary:
         h = WL.make_hca_decode()
         hstep = hca_decode_setup(h, args.copies)
         he = timed(hstep, max(20, args.steps // 2), args.warmup)
         hms = 1e3 * he / max(20, args.steps // 2)
         hk = kernel_times(hstep, max(20, args.steps // 2))
+        progress(f"hca decode: {hms:.4f} ms/step")
         hb, hf = hca_decode_bytes(h), hca_decode_flops(h)
         att = hk.get("hca_attend", {"avg_us": float("nan")})["avg_us"]
         result["secondary"] = {
@@ -476,6 +599,9 @@ def main():
             "hca_attend_TFLOPs": hf / (att * 1e-6) / 1e12, "mfma_bf16_frac": hf / (att * 1e-6) / 2.5e15,
             "algorithmic_bytes": hb, "flops": hf,
         }
+        if not args.no_ragged:
+            result.setdefault("ragged", {})["hca_decode_b8_ctx_le1048576"] = ragged_leg(
+                h, args.copies, max(20, args.steps // 2), args.warmup, 13, hms)
     if not args.no_prefill:
         pd = WL.make_csa_prefill()
         pstep, pflops = csa_prefill_setup(pd)
@@ -484,6 +610,7 @@ def main():
         pe = timed(pstep, n_p, 1)
         pms = 1e3 * pe / n_p
         pk = kernel_times(pstep, n_p)
+        progress(f"csa prefill: {pms:.3f} ms/step")
         result["prefill"] = {
             "workload": "csa_prefill_tq4096_ctx1048576", "tokens_per_s": 4096 / (pms * 1e-3),
             "ms_per_step": pms, "kernels_us": {k: round(v["avg_us"], 3) for k, v in pk.items()},
@@ -496,6 +623,7 @@ def main():
         me = timed(mstep, n_m, max(2, args.warmup // 4))
         mms = 1e3 * me / n_m
         mk = kernel_times(mstep, n_m)
+        progress(f"mixed pair: {mms:.4f} ms/step")
         result["mixed_pair"] = {
             "workload": "mixed_csa_hca_pair_b64_ctx1048576", "tokens_per_s": 64 / (mms * 1e-3),
             "ms_per_step": mms, "kernels_us": {k: round(v["avg_us"], 3) for k, v in mk.items()},

@@ -72,6 +72,10 @@ extern "C" {
 #define LCA_INV_ROPE    4u /* attend: rotate the output's last rope_dims
                               channels by the negative query position         */
 #define LCA_SCORE_BF16  8u /* index_topk: round scores to bf16 before top-k    */
+#define LCA_WIN_RING   16u /* attend: win is a ring of W-1+Tq rows per sequence,
+                              position p in row p mod (W-1+Tq) (lca_window_append
+                              fills it); without it, row r is position
+                              q_pos - (W-1) + r                                */
 
 /* ---------------------------------------------------------------------------
  * csa_compress — gated softmax-weighted token compressor (CSA and HCA).
@@ -110,6 +114,84 @@ int csa_compress(void* stream, int dt_in, int dt_out, int B, int T, int D, int m
                  uint32_t flags, const float* norm_w, float eps,
                  float rope_base, int rope_dims,
                  void* out, void* out_scale, int64_t out_rows);
+
+/* ---------------------------------------------------------------------------
+ * Decode-time state: csa_compress_append, lca_window_append.
+ *
+ * [kwkr] §4.4: the KV cache of a request splits into a state cache (what stays
+ * a fixed size: the uncompressed tail of the compressor and the sliding
+ * window) and a classical KV cache (the compressed entries, growing by one
+ * entry every m tokens). These calls keep both while decoding one token per
+ * sequence per call, each sequence at its own position (a ragged batch).
+ *
+ * csa_compress_append: sequence b appends its token at position pos[b]
+ * (int64, device memory, 8-byte aligned; a sequence whose position lies
+ * outside [0, pos_max] is left untouched this call). Positions must advance
+ * one token at a time from 0 for the state to hold the right rows. The token's
+ * rows are ca / cb [B, D] (dt_in) and its gate logits za / zb [B] (float32);
+ * stream a is NULL without overlap. When the token closes block j (pos % m ==
+ * m - 1), entry j is formed exactly as csa_compress forms it — same rows, same
+ * softmax, same epilogue (RoPE at position j*m), so the same bits as a one-shot
+ * csa_compress of the whole sequence with pos0 = 0 — and written to out row
+ * b * out_rows + j (formats as csa_compress; out_rows >= (pos_max + 1) / m).
+ * state: caller-owned device buffer of csa_compress_state_bytes() bytes,
+ * 16-byte aligned, one region per sequence, no initialisation needed. Layout
+ * (rows in dt_in): per sequence R rows of D values, R = 3m with overlap (stream
+ * a of block n in rows (n mod 2)*m + i, stream b of the current block in rows
+ * 2m + i), R = m without (stream b); after all rows, from the next 256-byte
+ * boundary, float32 gate logits [B, R] indexed alike. Copying the buffer
+ * takes a checkpoint of the state and copying it back restores it (the pages'
+ * Full / Periodic / Zero SWA caching policies are such copies, made by the
+ * caller). Calls on one state buffer must not overlap in time.
+ * Returns 0 from csa_compress_state_bytes for invalid arguments.
+ *
+ * lca_window_append: sequence b stores its token's raw KV row src [B, D]
+ * (dt_in F32 or BF16) into ring row pos[b] mod ring_rows of win [B,
+ * ring_rows, ...] in dt_out (F32, BF16, or KV_MIXED with win_scale [B,
+ * ring_rows] and rope_dims bf16 channels, converted as lca_quantize_rows).
+ * Attention reads the ring with LCA_WIN_RING and ring_rows = W - 1 + Tq.
+ * ------------------------------------------------------------------------- */
+/* lca_decode_append: every append of one decode step in one launch — up to
+ * LCA_MAX_APPEND_JOBS jobs, each a compressor append (as csa_compress_append)
+ * or a window-ring store (as lca_window_append), over the same positions.
+ * Results equal those of the separate calls, bit for bit. Each job is checked
+ * as its separate call checks it; on any error nothing is launched. The jobs
+ * array is read on the host during the call. */
+#define LCA_APPEND_COMPRESS 0
+#define LCA_APPEND_WINDOW   1
+#define LCA_MAX_APPEND_JOBS 4
+typedef struct lca_append_job {
+  int kind;                 /* LCA_APPEND_COMPRESS or LCA_APPEND_WINDOW                  */
+  int dt_in, dt_out, D;
+  int m, overlap;           /* compressor: ratio and overlap                             */
+  uint32_t flags;           /* compressor: LCA_NORM | LCA_ROPE                           */
+  int rope_dims;            /* compressor: RoPE / bf16 channels; window: KV_MIXED bf16   */
+  float eps, rope_base;     /* compressor                                                */
+  const void* ca;           /* compressor, overlap: stream a row [B, D]                  */
+  const float* za;          /*                      and its gate logit [B]               */
+  const void* cb;           /* compressor: stream b row [B, D]; window: the raw row      */
+  const float* zb;          /* compressor: stream b gate logit [B]; window: NULL          */
+  const float* norm_w;      /* compressor with LCA_NORM                                  */
+  void* state;              /* compressor: its state buffer                              */
+  size_t state_bytes;
+  void* out;                /* compressor: entry cache; window: the ring                 */
+  void* out_scale;          /* scales of a quantised cache or ring                       */
+  int64_t out_rows;         /* compressor: rows per sequence; window: ring rows          */
+} lca_append_job;
+int lca_decode_append(void* stream, int B, int64_t pos_max, const int64_t* pos,
+                      const lca_append_job* jobs, int n_jobs);
+
+size_t csa_compress_state_bytes(int dt_in, int B, int D, int m, int overlap);
+int csa_compress_append(void* stream, int dt_in, int dt_out, int B, int D, int m, int overlap,
+                        int64_t pos_max, const int64_t* pos,
+                        const void* ca, const float* za, const void* cb, const float* zb,
+                        void* state, size_t state_bytes,
+                        uint32_t flags, const float* norm_w, float eps,
+                        float rope_base, int rope_dims,
+                        void* out, void* out_scale, int64_t out_rows);
+int lca_window_append(void* stream, int dt_in, int dt_out, int B, int D, int rope_dims, int ring_rows,
+                      int64_t pos_max, const int64_t* pos, const void* src, void* win,
+                      float* win_scale);
 
 /* ---------------------------------------------------------------------------
  * lca_quantize_rows — quantise-on-write of float32 rows to a storage format.

@@ -26,7 +26,7 @@ __all__ = [
 ]
 
 F32, BF16, KV_MIXED, MXFP4 = 0, 1, 2, 3
-NORM, ROPE, INV_ROPE, SCORE_BF16 = 1, 2, 4, 8
+NORM, ROPE, INV_ROPE, SCORE_BF16, WIN_RING = 1, 2, 4, 8, 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "liblca.so")
@@ -41,6 +41,20 @@ class LcaError(RuntimeError):
 
 class KernelStat(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
+class AppendJob(ctypes.Structure):
+    """lca_append_job of include/lca.h (same field order and types)."""
+    _fields_ = [("kind", ctypes.c_int), ("dt_in", ctypes.c_int), ("dt_out", ctypes.c_int), ("D", ctypes.c_int),
+                ("m", ctypes.c_int), ("overlap", ctypes.c_int), ("flags", ctypes.c_uint32),
+                ("rope_dims", ctypes.c_int), ("eps", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("ca", ctypes.c_void_p), ("za", ctypes.c_void_p), ("cb", ctypes.c_void_p),
+                ("zb", ctypes.c_void_p), ("norm_w", ctypes.c_void_p), ("state", ctypes.c_void_p),
+                ("state_bytes", ctypes.c_size_t), ("out", ctypes.c_void_p), ("out_scale", ctypes.c_void_p),
+                ("out_rows", ctypes.c_int64)]
+
+
+APPEND_COMPRESS, APPEND_WINDOW, MAX_APPEND_JOBS = 0, 1, 4
 
 
 def _declare(L):
@@ -75,6 +89,15 @@ def _declare(L):
     L.hca_attend_ragged.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i64, vp, vp, vp, vp,
                                     vp, vp, vp, f32, u32, f32, i32, vp, vp, vp, sz]
     L.hca_attend_ragged.restype = i32
+    L.csa_compress_state_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.csa_compress_state_bytes.restype = sz
+    L.csa_compress_append.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz,
+                                      u32, vp, f32, f32, i32, vp, vp, i64]
+    L.csa_compress_append.restype = i32
+    L.lca_window_append.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp]
+    L.lca_window_append.restype = i32
+    L.lca_decode_append.argtypes = [vp, i32, i64, vp, ctypes.POINTER(AppendJob), i32]
+    L.lca_decode_append.restype = i32
     L.lca_status_str.argtypes = [i32]
     L.lca_status_str.restype = ctypes.c_char_p
     L.lca_last_error.argtypes = []
@@ -144,6 +167,54 @@ def lca_quantize_rows(dt_out, src, out, out_scale, *, rope_dims=64, stream=None)
     n = src.numel() // D
     _check(lib().lca_quantize_rows(_stream(stream), dt_out, n, D, rope_dims, _p(src), _p(out),
                                    _p(out_scale)))
+
+
+def csa_compress_state_bytes(dt_in, B, D, m, overlap=True):
+    return int(lib().csa_compress_state_bytes(dt_in, B, D, m, 1 if overlap else 0))
+
+
+def csa_compress_append(dt_in, dt_out, cb, zb, m, pos, state, out, *, pos_max, ca=None, za=None,
+                        overlap=True, flags=0, norm_w=None, eps=1e-6, rope_base=10000.0, rope_dims=0,
+                        out_scale=None, out_rows=None, stream=None):
+    """Append one token per sequence (cb [B, D], zb [B]) at positions pos (int64
+    device tensor [B]); see csa_compress_append in include/lca.h. out holds
+    out_rows entries per sequence (default: out.shape[1])."""
+    B, D = cb.shape
+    out_rows = out.shape[1] if out_rows is None else out_rows
+    _check(lib().csa_compress_append(_stream(stream), dt_in, dt_out, B, D, m, 1 if overlap else 0, pos_max,
+                                     _q_pos(pos, B), _p(ca), _p(za), _p(cb), _p(zb), _p(state),
+                                     state.numel() * state.element_size(), flags, _p(norm_w), eps,
+                                     rope_base, rope_dims, _p(out), _p(out_scale), out_rows))
+
+
+def lca_window_append(dt_in, dt_out, src, pos, win, *, pos_max, win_scale=None, rope_dims=64, stream=None):
+    """Store each sequence's token row src [B, D] into ring row pos[b] mod
+    win.shape[1] of win; see lca_window_append in include/lca.h."""
+    B, D = src.shape
+    _check(lib().lca_window_append(_stream(stream), dt_in, dt_out, B, D, rope_dims, win.shape[1], pos_max,
+                                   _q_pos(pos, B), _p(src), _p(win), _p(win_scale)))
+
+
+def append_job_compress(dt_in, dt_out, cb, zb, m, state, out, *, ca=None, za=None, overlap=True, flags=0,
+                        norm_w=None, eps=1e-6, rope_base=10000.0, rope_dims=0, out_scale=None, out_rows=None):
+    """A compressor job for lca_decode_append (the tensors must outlive the call)."""
+    return AppendJob(APPEND_COMPRESS, dt_in, dt_out, cb.shape[1], m, 1 if overlap else 0, flags, rope_dims, eps,
+                     rope_base, _p(ca), _p(za), _p(cb), _p(zb), _p(norm_w), _p(state),
+                     state.numel() * state.element_size(), _p(out), _p(out_scale),
+                     out.shape[1] if out_rows is None else out_rows)
+
+
+def append_job_window(dt_in, dt_out, src, win, *, win_scale=None, rope_dims=64):
+    """A window-ring job for lca_decode_append: src [B, D] into ring win [B, rows, ...]."""
+    return AppendJob(APPEND_WINDOW, dt_in, dt_out, src.shape[1], 0, 0, 0, rope_dims, 0.0, 0.0, None, None,
+                     _p(src), None, None, None, 0, _p(win), _p(win_scale), win.shape[1])
+
+
+def lca_decode_append(jobs, pos, *, pos_max, stream=None):
+    """Run every append job of a decode step in one launch; see include/lca.h."""
+    arr = (AppendJob * len(jobs))(*jobs)
+    B = pos.numel()
+    _check(lib().lca_decode_append(_stream(stream), B, pos_max, _q_pos(pos, B), arr, len(jobs)))
 
 
 def csa_index_topk_workspace(dt, B, Tq, H_I, d_I, N_cap, m, k, q_pos0, flags=0):

@@ -75,6 +75,7 @@ __device__ __forceinline__ int64_t row_source(const AttendArgs& a, int b, int t,
   if (v < rs.nrows) {
     *kind = 1;
     const int64_t pos = rs.win_lo + (v - rs.n_ent);
+    if (a.flags & LCA_WIN_RING) return pos % (a.W - 1 + a.Tq);    // ring: position p in row p mod rows
     return pos - (seq_pos(a.q_pos, a.q_pos0, b) - (a.W - 1));
   }
   return -1;

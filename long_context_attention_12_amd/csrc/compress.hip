@@ -85,23 +85,19 @@ __device__ void emit_row(const float* e, int D, int dt_out, int rope_dims, void*
   }
 }
 
-template <typename Tin>
-__global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
-  __shared__ float wts[256];
-  __shared__ float e[kMaxD];
-  __shared__ float red[kThreads / 64];
-  __shared__ int blk_exp[kMaxD / 32];
-  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int m = a.m, D = a.D, T = a.T;
-  const bool has_a = a.overlap && (j > 0 || a.prev_ca != nullptr);
-  const int na = has_a ? m : 0, nl = na + m;
-
-  // gate logits of the rows entering entry j: stream a block j-1, stream b block j
+// One entry from its nl rows: a softmax over the rows' gate logits, the
+// weighted sum of the rows per channel (rows taken in order), then the
+// epilogue (RMSNorm; RoPE at entry_pos; conversion to dt_out) into row
+// out_row of a.out. logit(i) and row(i) give the gate logit and the row of the
+// entry's i-th row. The one-shot and the token-at-a-time compressors both go
+// through here, so an entry has the same bits whichever of them made it.
+template <typename Tin, typename LogitF, typename RowF>
+__device__ void merge_and_emit(const CompressArgs& a, int nl, LogitF logit, RowF row, int64_t entry_pos,
+                               int64_t out_row, float* wts, float* e, float* red, int* blk_exp) {
+  const int tid = threadIdx.x, D = a.D;
   float lmax = -INFINITY;
   for (int i = tid; i < nl; i += kThreads) {
-    float z;
-    if (i < na) z = j > 0 ? a.za[static_cast<int64_t>(b) * T + (j - 1) * m + i] : a.prev_za[b * m + i];
-    else z = a.zb[static_cast<int64_t>(b) * T + j * m + (i - na)];
+    const float z = logit(i);
     wts[i] = z;
     lmax = fmaxf(lmax, z);
   }
@@ -115,18 +111,19 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
   lsum = block_reduce(lsum, red, false);      // also orders the wts[] writes
   const float inv = 1.0f / lsum;
 
+  // rows are summed in order; their loads go out 8 at a time ahead of the
+  // sums, so one memory latency covers 8 rows instead of one
   for (int c = tid; c < D; c += kThreads) {
     float acc = 0.f;
-    for (int i = 0; i < nl; ++i) {
-      float x;
-      if (i < na) {
-        x = j > 0 ? load_elem<Tin>(a.ca, (static_cast<int64_t>(b) * T + (j - 1) * m + i) * D + c)
-                  : load_elem<Tin>(a.prev_ca, (static_cast<int64_t>(b) * m + i) * D + c);
-      } else {
-        x = load_elem<Tin>(a.cb, (static_cast<int64_t>(b) * T + j * m + (i - na)) * D + c);
-      }
-      acc = fmaf(wts[i], x, acc);
+    int i = 0;
+    for (; i + 8 <= nl; i += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = load_elem<Tin>(row(i + u), c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(wts[i + u], x[u], acc);
     }
+    for (; i < nl; ++i) acc = fmaf(wts[i], load_elem<Tin>(row(i), c), acc);
     e[c] = acc * inv;
   }
   __syncthreads();
@@ -143,8 +140,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
     const int R = a.rope_dims;
     for (int i = tid; i < R / 2; i += kThreads) {
       float s, cs;
-      rope_sincos(static_cast<double>(a.pos0 + static_cast<int64_t>(j) * m), i, R,
-                  static_cast<double>(a.rope_base), &s, &cs);
+      rope_sincos(static_cast<double>(entry_pos), i, R, static_cast<double>(a.rope_base), &s, &cs);
       const int c0 = D - R + 2 * i;
       const float u = e[c0], v = e[c0 + 1];
       e[c0] = u * cs - v * s;
@@ -152,8 +148,116 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
     }
     __syncthreads();
   }
-  emit_row(e, D, a.dt_out, a.rope_dims, a.out, static_cast<int64_t>(b) * a.out_rows + j,
+  emit_row(e, D, a.dt_out, a.rope_dims, a.out, out_row, a.out_scale, red, blk_exp);
+}
+
+template <typename Tin>
+__device__ __forceinline__ const Tin* row_ptr(const void* base, int64_t row, int D) {
+  return static_cast<const Tin*>(base) + row * D;
+}
+
+// One workgroup per output entry j of sequence b (a whole chunk of T tokens).
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void compress_kernel(CompressArgs a) {
+  __shared__ float wts[256];
+  __shared__ float e[kMaxD];
+  __shared__ float red[kThreads / 64];
+  __shared__ int blk_exp[kMaxD / 32];
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int m = a.m, D = a.D, T = a.T;
+  const bool has_a = a.overlap && (j > 0 || a.prev_ca != nullptr);
+  const int na = has_a ? m : 0, nl = na + m;
+  const int64_t tok_a = static_cast<int64_t>(b) * T + static_cast<int64_t>(j - 1) * m;   // block j-1
+  const int64_t tok_b = static_cast<int64_t>(b) * T + static_cast<int64_t>(j) * m;       // block j
+  // rows entering entry j: stream a block j-1 (or prev_*), then stream b block j
+  auto logit = [&](int i) -> float {
+    if (i < na) return j > 0 ? a.za[tok_a + i] : a.prev_za[b * m + i];
+    return a.zb[tok_b + (i - na)];
+  };
+  auto row = [&](int i) -> const Tin* {
+    if (i < na) return j > 0 ? row_ptr<Tin>(a.ca, tok_a + i, D) : row_ptr<Tin>(a.prev_ca, static_cast<int64_t>(b) * m + i, D);
+    return row_ptr<Tin>(a.cb, tok_b + (i - na), D);
+  };
+  merge_and_emit<Tin>(a, nl, logit, row, a.pos0 + static_cast<int64_t>(j) * m,
+                      static_cast<int64_t>(b) * a.out_rows + j, wts, e, red, blk_exp);
+}
+
+// Token-at-a-time compressor: sequence b appends the token at position p.
+// The caller-owned state keeps what a later entry still needs: stream a's
+// rows of the last two blocks (a ring of 2m rows; block n in half n mod 2) and
+// stream b's rows of the current block (m rows), each with its gate logit.
+// When the token closes its block j, entry j is merged and written to out row
+// b * out_rows + j. The token's own rows are read from the inputs, never back
+// from the state, so no workgroup reads what it wrote.
+template <typename Tin>
+__device__ void compress_append(const CompressArgs& a, void* state, int b, int64_t p, float* wts, float* e,
+                                float* red, int* blk_exp) {
+  const int tid = threadIdx.x;
+  const int m = a.m, D = a.D;
+  const int R = a.overlap ? 3 * m : m;                    // state rows per sequence
+  const int slot = static_cast<int>(p % m);
+  const int64_t j = p / m;
+  Tin* st = static_cast<Tin*>(state) + static_cast<int64_t>(b) * R * D;
+  float* sz = reinterpret_cast<float*>(static_cast<uint8_t*>(state) + compress_state_logit_offset(a)) +
+              static_cast<int64_t>(b) * R;
+  const int b0 = a.overlap ? 2 * m : 0;                   // first stream-b row
+  const int ra = static_cast<int>(j & 1) * m + slot;      // this token's stream-a row
+  const Tin* cb_new = static_cast<const Tin*>(a.cb) + static_cast<int64_t>(b) * D;
+  const Tin* ca_new = a.overlap ? static_cast<const Tin*>(a.ca) + static_cast<int64_t>(b) * D : nullptr;
+  for (int c = tid; c < D; c += kThreads) {
+    st[(b0 + slot) * D + c] = cb_new[c];
+    if (a.overlap) st[ra * D + c] = ca_new[c];
+  }
+  if (tid == 0) {
+    sz[b0 + slot] = a.zb[b];
+    if (a.overlap) sz[ra] = a.za[b];
+  }
+  if (slot != m - 1) return;
+  // the token closes block j: entry j from stream a of block j-1, stream b of block j
+  const int na = (a.overlap && j > 0) ? m : 0, nl = na + m;
+  const int ha = static_cast<int>((j - 1) & 1) * m;       // ring half of block j-1
+  auto logit = [&](int i) -> float {
+    if (i < na) return sz[ha + i];
+    return i - na == m - 1 ? a.zb[b] : sz[b0 + (i - na)];
+  };
+  auto row = [&](int i) -> const Tin* {
+    if (i < na) return st + static_cast<int64_t>(ha + i) * D;
+    return i - na == m - 1 ? cb_new : st + static_cast<int64_t>(b0 + (i - na)) * D;
+  };
+  merge_and_emit<Tin>(a, nl, logit, row, j * m, static_cast<int64_t>(b) * a.out_rows + j, wts, e, red,
+                      blk_exp);
+}
+
+// Sliding-window ring: sequence b stores the raw row of its token at position
+// p (a.cb, [B, D]) in ring row p mod a.out_rows of a.out, converted to a.dt_out.
+template <typename Tin>
+__device__ void window_append(const CompressArgs& a, int b, int64_t p, float* e, float* red, int* blk_exp) {
+  const Tin* x = static_cast<const Tin*>(a.cb) + static_cast<int64_t>(b) * a.D;
+  for (int c = threadIdx.x; c < a.D; c += kThreads) e[c] = load_elem<Tin>(x, c);
+  __syncthreads();
+  emit_row(e, a.D, a.dt_out, a.rope_dims, a.out, static_cast<int64_t>(b) * a.out_rows + p % a.out_rows,
            a.out_scale, red, blk_exp);
+}
+
+// All append jobs of a decode step in one launch: workgroup (b, i) runs job i
+// for sequence b, at position pos[b] (nothing when outside [0, pos_max]).
+__global__ __launch_bounds__(kThreads) void decode_append_kernel(AppendJobs jobs, int64_t pos_max,
+                                                                 const int64_t* __restrict__ pos) {
+  __shared__ float wts[256];
+  __shared__ float e[kMaxD];
+  __shared__ float red[kThreads / 64];
+  __shared__ int blk_exp[kMaxD / 32];
+  const int b = blockIdx.x;
+  const int64_t p = pos[b];
+  if (p < 0 || p > pos_max) return;
+  const AppendJob& job = jobs.j[blockIdx.y];
+  if (job.window) {
+    if (job.a.dt_in == LCA_F32) window_append<float>(job.a, b, p, e, red, blk_exp);
+    else window_append<uint16_t>(job.a, b, p, e, red, blk_exp);
+  } else {
+    if (job.a.dt_in == LCA_F32) compress_append<float>(job.a, job.state, b, p, wts, e, red, blk_exp);
+    else compress_append<uint16_t>(job.a, job.state, b, p, wts, e, red, blk_exp);
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(int dt_out, int D, int rope_dims,
@@ -179,6 +283,13 @@ hipError_t launch_compress(hipStream_t s, const CompressArgs& a) {
     scope.launch(compress_kernel<float>, grid, dim3(kThreads), 0, a);
   else
     scope.launch(compress_kernel<uint16_t>, grid, dim3(kThreads), 0, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(hipStream_t s, const AppendJobs& jobs, int B, int64_t pos_max, const int64_t* pos,
+                         const char* name) {
+  LaunchScope scope(s, name);
+  scope.launch(decode_append_kernel, dim3(B, jobs.n), dim3(kThreads), 0, jobs, pos_max, pos);
   return hipGetLastError();
 }
 

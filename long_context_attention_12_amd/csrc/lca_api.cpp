@@ -170,6 +170,129 @@ int csa_compress(void* stream, int dt_in, int dt_out, int B, int T, int D, int m
   return hip_status(lca::launch_compress(static_cast<hipStream_t>(stream), a), "csa_compress");
 }
 
+// ---------------------------------------------------------------------------
+// Decode-time state: token-at-a-time compressor and the sliding-window ring.
+static int check_positions(const int64_t* pos, int64_t pos_max, const char* fn) {
+  if (!pos) return fail(LCA_ERR_ARG, "%s: pos is required", fn);
+  if (reinterpret_cast<uintptr_t>(pos) % 8 != 0) return fail(LCA_ERR_ALIGN, "%s: pos must be 8-byte aligned", fn);
+  if (pos_max < 0) return fail(LCA_ERR_ARG, "%s: pos_max must be >= 0", fn);
+  return LCA_OK;
+}
+
+size_t csa_compress_state_bytes(int dt_in, int B, int D, int m, int overlap) {
+  if (B < 1 || D < 1 || m < 1 || (dt_in != LCA_F32 && dt_in != LCA_BF16)) return 0;
+  return lca::compress_state_bytes(dt_in, B, D, m, overlap ? 1 : 0);
+}
+
+// Validates one append job and fills its launch form.
+static int check_compress_job(const char* fn, int B, int64_t pos_max, const lca_append_job& j, lca::AppendJob* job) {
+  const int D = j.D, m = j.m;
+  if (m < 1 || D < 32 || D > 1024 || D % 32 != 0)
+    return fail(LCA_ERR_ARG, "%s: need m>=1, 32<=D<=1024, D%%32==0 (m=%d D=%d)", fn, m, D);
+  if (j.overlap != 0 && j.overlap != 1) return fail(LCA_ERR_ARG, "%s: overlap must be 0 or 1", fn);
+  if (j.overlap == 1 ? 2 * m > 256 : m > 256) return fail(LCA_ERR_UNSUPPORTED, "%s: too many rows per entry (m=%d)", fn, m);
+  if (j.dt_in != LCA_F32 && j.dt_in != LCA_BF16) return fail(LCA_ERR_UNSUPPORTED, "%s: dt_in must be F32 or BF16", fn);
+  if (j.dt_out < LCA_F32 || j.dt_out > LCA_MXFP4) return fail(LCA_ERR_UNSUPPORTED, "%s: unknown dt_out %d", fn, j.dt_out);
+  if (j.flags & ~(LCA_NORM | LCA_ROPE)) return fail(LCA_ERR_ARG, "%s: only LCA_NORM and LCA_ROPE apply", fn);
+  if (!j.cb || !j.zb || !j.out || !j.state) return fail(LCA_ERR_ARG, "%s: cb, zb, state and out are required", fn);
+  if (j.overlap && (!j.ca || !j.za)) return fail(LCA_ERR_ARG, "%s: overlap needs ca and za", fn);
+  if (!j.overlap && (j.ca || j.za)) return fail(LCA_ERR_ARG, "%s: stream a must be NULL without overlap", fn);
+  if ((j.flags & LCA_NORM) && !j.norm_w) return fail(LCA_ERR_ARG, "%s: LCA_NORM needs norm_w", fn);
+  if ((j.flags & LCA_NORM) && !(j.eps >= 0.f)) return fail(LCA_ERR_ARG, "%s: eps must be >= 0", fn);
+  if (j.rope_dims < 0 || j.rope_dims > D || j.rope_dims % 2 != 0) return fail(LCA_ERR_ARG, "%s: rope_dims must be even and in [0, D]", fn);
+  if ((j.flags & LCA_ROPE) && (j.rope_dims == 0 || !(j.rope_base > 0.f))) return fail(LCA_ERR_ARG, "%s: LCA_ROPE needs rope_dims > 0 and rope_base > 0", fn);
+  if ((j.dt_out == LCA_KV_MIXED || j.dt_out == LCA_MXFP4) && !j.out_scale) return fail(LCA_ERR_ARG, "%s: out_scale required for quantised output", fn);
+  if (!aligned16(j.ca) || !aligned16(j.cb) || !aligned16(j.out) || !aligned16(j.state))
+    return fail(LCA_ERR_ALIGN, "%s: row buffers and state must be 16-byte aligned", fn);
+  if (!aligned4(j.za) || !aligned4(j.zb) || !aligned4(j.norm_w) || !aligned4(j.out_scale))
+    return fail(LCA_ERR_ALIGN, "%s: float arrays must be 4-byte aligned", fn);
+  const size_t need = lca::compress_state_bytes(j.dt_in, B, D, m, j.overlap);
+  if (j.state_bytes < need) return fail(LCA_ERR_WORKSPACE, "%s: state %zu < %zu bytes", fn, j.state_bytes, need);
+  if (j.out_rows < (pos_max + 1) / m)
+    return fail(LCA_ERR_ARG, "%s: out_rows (%lld) < (pos_max + 1) / m (%lld)", fn, (long long)j.out_rows, (long long)((pos_max + 1) / m));
+  job->a = lca::CompressArgs{j.dt_in, j.dt_out, B, 1, D, m, j.overlap, 0, j.ca, j.cb, nullptr, j.za, j.zb, nullptr,
+                             j.flags, j.norm_w, j.eps, j.rope_base, j.rope_dims, j.out, j.out_scale, j.out_rows};
+  job->state = j.state;
+  job->window = 0;
+  return LCA_OK;
+}
+
+static int check_window_job(const char* fn, int B, const lca_append_job& j, lca::AppendJob* job) {
+  const int D = j.D;
+  if (j.out_rows < 1 || D < 32 || D > 1024 || D % 32 != 0)
+    return fail(LCA_ERR_ARG, "%s: need ring_rows>=1, 32<=D<=1024, D%%32==0", fn);
+  if (j.dt_in != LCA_F32 && j.dt_in != LCA_BF16) return fail(LCA_ERR_UNSUPPORTED, "%s: dt_in must be F32 or BF16", fn);
+  if (j.dt_out != LCA_F32 && j.dt_out != LCA_BF16 && j.dt_out != LCA_KV_MIXED)
+    return fail(LCA_ERR_UNSUPPORTED, "%s: dt_out must be F32, BF16 or KV_MIXED", fn);
+  if (j.dt_out == LCA_KV_MIXED && (j.rope_dims < 0 || j.rope_dims > D || j.rope_dims % 2 != 0))
+    return fail(LCA_ERR_ARG, "%s: rope_dims must be even and in [0, D]", fn);
+  if (!j.cb || !j.out) return fail(LCA_ERR_ARG, "%s: src and win are required", fn);
+  if (j.dt_out == LCA_KV_MIXED && !j.out_scale) return fail(LCA_ERR_ARG, "%s: KV_MIXED needs win_scale", fn);
+  if (!aligned16(j.cb) || !aligned16(j.out)) return fail(LCA_ERR_ALIGN, "%s: src and win must be 16-byte aligned", fn);
+  if (!aligned4(j.out_scale)) return fail(LCA_ERR_ALIGN, "%s: win_scale must be 4-byte aligned", fn);
+  job->a = lca::CompressArgs{j.dt_in, j.dt_out, B, 1, D, 1, 0, 0, nullptr, j.cb, nullptr, nullptr, nullptr, nullptr,
+                             0u, nullptr, 0.f, 0.f, j.dt_out == LCA_KV_MIXED ? j.rope_dims : 0, j.out, j.out_scale,
+                             j.out_rows};
+  job->state = nullptr;
+  job->window = 1;
+  return LCA_OK;
+}
+
+int lca_decode_append(void* stream, int B, int64_t pos_max, const int64_t* pos, const lca_append_job* jobs,
+                      int n_jobs) {
+  const char* fn = "lca_decode_append";
+  if (B < 1) return fail(LCA_ERR_ARG, "%s: need B >= 1", fn);
+  if (n_jobs < 1 || n_jobs > LCA_MAX_APPEND_JOBS || !jobs)
+    return fail(LCA_ERR_ARG, "%s: need 1 to %d jobs", fn, LCA_MAX_APPEND_JOBS);
+  int st = check_positions(pos, pos_max, fn);
+  if (st != LCA_OK) return st;
+  lca::AppendJobs js{};
+  js.n = n_jobs;
+  for (int i = 0; i < n_jobs; ++i) {
+    if (jobs[i].kind == LCA_APPEND_COMPRESS) st = check_compress_job(fn, B, pos_max, jobs[i], &js.j[i]);
+    else if (jobs[i].kind == LCA_APPEND_WINDOW) st = check_window_job(fn, B, jobs[i], &js.j[i]);
+    else st = fail(LCA_ERR_ARG, "%s: job %d has unknown kind %d", fn, i, jobs[i].kind);
+    if (st != LCA_OK) return st;
+  }
+  return hip_status(lca::launch_append(static_cast<hipStream_t>(stream), js, B, pos_max, pos, "decode_append"), fn);
+}
+
+int csa_compress_append(void* stream, int dt_in, int dt_out, int B, int D, int m, int overlap, int64_t pos_max,
+                        const int64_t* pos, const void* ca, const float* za, const void* cb, const float* zb,
+                        void* state, size_t state_bytes, uint32_t flags, const float* norm_w, float eps,
+                        float rope_base, int rope_dims, void* out, void* out_scale, int64_t out_rows) {
+  const char* fn = "csa_compress_append";
+  if (B < 1) return fail(LCA_ERR_ARG, "%s: need B >= 1", fn);
+  int st = check_positions(pos, pos_max, fn);
+  if (st != LCA_OK) return st;
+  lca_append_job j{};
+  j.kind = LCA_APPEND_COMPRESS; j.dt_in = dt_in; j.dt_out = dt_out; j.D = D; j.m = m; j.overlap = overlap;
+  j.flags = flags; j.rope_dims = rope_dims; j.eps = eps; j.rope_base = rope_base; j.ca = ca; j.za = za;
+  j.cb = cb; j.zb = zb; j.norm_w = norm_w; j.state = state; j.state_bytes = state_bytes; j.out = out;
+  j.out_scale = out_scale; j.out_rows = out_rows;
+  lca::AppendJobs js{};
+  js.n = 1;
+  st = check_compress_job(fn, B, pos_max, j, &js.j[0]);
+  if (st != LCA_OK) return st;
+  return hip_status(lca::launch_append(static_cast<hipStream_t>(stream), js, B, pos_max, pos, "compress_append"), fn);
+}
+
+int lca_window_append(void* stream, int dt_in, int dt_out, int B, int D, int rope_dims, int ring_rows,
+                      int64_t pos_max, const int64_t* pos, const void* src, void* win, float* win_scale) {
+  const char* fn = "lca_window_append";
+  if (B < 1) return fail(LCA_ERR_ARG, "%s: need B >= 1", fn);
+  int st = check_positions(pos, pos_max, fn);
+  if (st != LCA_OK) return st;
+  lca_append_job j{};
+  j.kind = LCA_APPEND_WINDOW; j.dt_in = dt_in; j.dt_out = dt_out; j.D = D; j.rope_dims = rope_dims;
+  j.cb = src; j.out = win; j.out_scale = win_scale; j.out_rows = ring_rows;
+  lca::AppendJobs js{};
+  js.n = 1;
+  st = check_window_job(fn, B, j, &js.j[0]);
+  if (st != LCA_OK) return st;
+  return hip_status(lca::launch_append(static_cast<hipStream_t>(stream), js, B, pos_max, pos, "window_append"), fn);
+}
+
 int lca_quantize_rows(void* stream, int dt_out, int64_t n_rows, int D, int rope_dims,
                       const float* src, void* out, void* out_scale) {
   if (n_rows < 0 || D < 32 || D > 1024 || D % 32 != 0)
@@ -254,7 +377,7 @@ static int check_attend(const lca::AttendArgs& a, const char* fn) {
   } else {
     return fail(LCA_ERR_UNSUPPORTED, "%s: dt_kv must be F32, BF16 or KV_MIXED", fn);
   }
-  if (a.flags & ~LCA_INV_ROPE) return fail(LCA_ERR_ARG, "%s: only LCA_INV_ROPE applies", fn);
+  if (a.flags & ~(LCA_INV_ROPE | LCA_WIN_RING)) return fail(LCA_ERR_ARG, "%s: only LCA_INV_ROPE and LCA_WIN_RING apply", fn);
   if (a.rope_dims < 0 || a.rope_dims > a.D || a.rope_dims % 2) return fail(LCA_ERR_ARG, "%s: rope_dims must be even and in [0, D]", fn);
   if ((a.flags & LCA_INV_ROPE) && (a.rope_dims == 0 || !(a.rope_base > 0.f))) return fail(LCA_ERR_ARG, "%s: LCA_INV_ROPE needs rope_dims > 0 and rope_base > 0", fn);
   if (!(a.scale == a.scale)) return fail(LCA_ERR_ARG, "%s: scale is NaN", fn);

@@ -48,6 +48,36 @@ struct CompressArgs {
   int64_t out_rows;
 };
 hipError_t launch_compress(hipStream_t s, const CompressArgs& a);
+
+// Token-at-a-time compressor state, per sequence: R = 3m rows with overlap (a
+// ring of 2m stream-a rows, then m stream-b rows), R = m without; rows in the
+// input type, then R fp32 gate logits per sequence from a 256-byte aligned offset.
+__host__ __device__ inline size_t compress_state_rows_bytes(int dt_in, int B, int D, int m, int overlap) {
+  const size_t esz = dt_in == 0 /* LCA_F32 */ ? 4 : 2;
+  const size_t R = static_cast<size_t>(overlap ? 3 * m : m);
+  return (static_cast<size_t>(B) * R * D * esz + 255) & ~static_cast<size_t>(255);
+}
+__host__ __device__ inline size_t compress_state_logit_offset(const CompressArgs& a) {
+  return compress_state_rows_bytes(a.dt_in, a.B, a.D, a.m, a.overlap);
+}
+__host__ __device__ inline size_t compress_state_bytes(int dt_in, int B, int D, int m, int overlap) {
+  return compress_state_rows_bytes(dt_in, B, D, m, overlap) + static_cast<size_t>(B) * (overlap ? 3 * m : m) * 4;
+}
+// One append of a decode step: a compressor (args + state) or, with window
+// set, a window-ring store (a.cb = the raw rows, a.out = the ring, a.out_rows
+// = ring rows, a.out_scale = its scales).
+struct AppendJob {
+  CompressArgs a;
+  void* state;
+  int window;
+};
+constexpr int kMaxAppendJobs = 4;
+struct AppendJobs {
+  AppendJob j[kMaxAppendJobs];
+  int n;
+};
+hipError_t launch_append(hipStream_t s, const AppendJobs& jobs, int B, int64_t pos_max, const int64_t* pos,
+                         const char* name);
 hipError_t launch_quantize_rows(hipStream_t s, int dt_out, int64_t n_rows, int D, int rope_dims,
                                 const float* src, void* out, void* out_scale);
 

@@ -25,6 +25,7 @@ import numpy as np
 __all__ = [
     "n_visible",
     "compress_sequence",
+    "CompressorState",
     "rms_norm",
     "rope_rotate",
     "compress_epilogue",
@@ -131,6 +132,57 @@ def compress_sequence(cb, zb, m, ca=None, za=None, prev_ca=None, prev_za=None,
         w = _softmax(np.concatenate(logits))
         out[j] = w @ x
     return out
+
+
+class CompressorState:
+    """Decode-time compressor of one sequence: tokens arrive one at a time.
+
+    [kwkr] §4.4: a request's KV cache splits into a state cache and a
+    classical KV cache. Reading used (stated in the design doc): the state cache
+    holds what the compressor has not yet folded into an entry -- both
+    streams' rows of the block in progress -- plus stream a's rows of the
+    last complete block, which the next entry still needs because adjacent
+    blocks overlap ([kwkr] §3.1). The classical cache receives entry j when
+    the token at position j*m + m - 1 closes block j; the entry is the same
+    gated softmax merge as ``compress_sequence`` (one joint softmax over
+    stream a of block j-1 and stream b of block j; block 0 has no stream-a
+    half). ``overlap=False`` keeps stream b only (HCA).
+
+    Pinned by: feeding a sequence token by token emits exactly the entries of
+    the one-shot ``compress_sequence`` (tests/test_oracle_compress.py), for
+    CSA (m = 4, overlap) and HCA (m = 128) shapes.
+    """
+
+    def __init__(self, m, overlap=True):
+        self.m = m
+        self.overlap = overlap
+        self.pos = 0                  # position of the next token
+        self.tail_a = None            # (rows [m, D], logits [m]) of stream a, last complete block
+        self.cur = []                 # (ca, za, cb, zb) of the block in progress
+
+    def append(self, cb_row, zb, ca_row=None, za=None):
+        """Take the token at position ``self.pos``. Returns ``(j, entry)``
+        when it closes block j, else None."""
+        self.cur.append((ca_row, za, np.asarray(cb_row, dtype=np.float64), float(zb)))
+        self.pos += 1
+        if len(self.cur) < self.m:
+            return None
+        j = self.pos // self.m - 1
+        rows, logits = [], []
+        if self.overlap and self.tail_a is not None:
+            rows.extend(self.tail_a[0])
+            logits.extend(self.tail_a[1])
+        rows.extend(t[2] for t in self.cur)
+        logits.extend(t[3] for t in self.cur)
+        w = _softmax(np.array(logits))
+        entry = np.zeros_like(rows[0])
+        for wi, r in zip(w, rows):
+            entry = entry + wi * r
+        if self.overlap:
+            self.tail_a = ([np.asarray(t[0], dtype=np.float64) for t in self.cur],
+                           [float(t[1]) for t in self.cur])
+        self.cur = []
+        return j, entry
 
 
 def rms_norm(x, weight, eps):

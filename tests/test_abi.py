@@ -108,7 +108,8 @@ def test_attend_validation(lib):
     _expect(call(D=96), -2, "D in")
     _expect(call(dt_q=0), -2, "BF16 q")
     _expect(call(dt_kv=2, R=64), -1, "kv_scale")
-    _expect(call(flags=4), -1, "LCA_INV_ROPE")
+    _expect(call(flags=4), -1, "LCA_INV_ROPE needs")
+    _expect(call(flags=8), -1, "LCA_WIN_RING apply")
     _expect(call(idx=None), -1, "missing")
     _expect(call(W=0), -1, "W must")
     _expect(call(ws=None), -4, "workspace")
@@ -148,6 +149,65 @@ def test_ragged_validation(lib):
     h = lib.hca_attend_ragged(None, 1, 1, 2, 1, 64, 512, 100, 128, 128, 1048576, None, fake, fake, None,
                               fake, None, fake, 0.04, 0, 10000.0, 0, fake, None, fake, 1 << 30)
     _expect(h, -1, "q_pos is required")
+
+
+def test_decode_state_validation(lib):
+    fake = 0x10000
+    need = lib.csa_compress_state_bytes(1, 2, 512, 4, 1)
+    assert need >= 2 * 12 * 512 * 2 + 2 * 12 * 4
+    assert lib.csa_compress_state_bytes(2, 2, 512, 4, 1) == 0          # dt_in must be F32 / BF16
+    assert lib.csa_compress_state_bytes(1, 2, 512, 128, 0) < lib.csa_compress_state_bytes(1, 2, 512, 128, 1)
+
+    def app(pos=fake, pos_max=1023, state_bytes=None, out_rows=256, m=4, ov=1, ca=fake, flags=0, dt_out=1):
+        return lib.csa_compress_append(None, 1, dt_out, 2, 512, m, ov, pos_max, pos, ca if ov else None,
+                                       fake if ov else None, fake, fake, fake,
+                                       need if state_bytes is None else state_bytes, flags, None, 1e-6,
+                                       10000.0, 0, fake, None, out_rows)
+    _expect(app(pos=None), -1, "pos is required")
+    _expect(app(pos=fake + 4), -3, "8-byte")
+    _expect(app(pos_max=-1), -1, "pos_max")
+    _expect(app(state_bytes=16), -4, "state")
+    _expect(app(out_rows=255), -1, "out_rows")
+    _expect(app(m=200), -2, "too many rows")
+    _expect(app(ca=None), -1, "overlap needs")
+    _expect(app(flags=1), -1, "norm_w")
+    _expect(app(dt_out=2), -1, "out_scale")
+
+    def win(dt_out=1, wsc=None, pos=fake, ring=128, src=fake):
+        return lib.lca_window_append(None, 1, dt_out, 2, 512, 64, ring, 1000, pos, src, fake, wsc)
+    _expect(win(dt_out=3), -2, "dt_out")
+    _expect(win(dt_out=2), -1, "win_scale")
+    _expect(win(pos=None), -1, "pos is required")
+    _expect(win(ring=0), -1, "ring_rows")
+    _expect(win(src=fake + 2), -3, "16-byte")
+
+
+def test_decode_append_validation(lib):
+    fake = 0x10000
+    need = lib.csa_compress_state_bytes(1, 2, 512, 4, 1)
+    good = L.AppendJob(L.APPEND_COMPRESS, 1, 1, 512, 4, 1, 0, 0, 1e-6, 1e4, fake, fake, fake, fake, None, fake,
+                       need, fake, None, 256)
+    win = L.AppendJob(L.APPEND_WINDOW, 1, 1, 512, 0, 0, 0, 64, 0.0, 0.0, None, None, fake, None, None, None, 0,
+                      fake, None, 128)
+
+    def call(*jobs, pos=fake, n=None):
+        arr = (L.AppendJob * len(jobs))(*jobs)
+        return lib.lca_decode_append(None, 2, 1023, pos, arr, len(jobs) if n is None else n)
+    _expect(call(good, n=0), -1, "jobs")
+    _expect(call(good, good, good, good, win), -1, "jobs")
+    _expect(call(good, pos=None), -1, "pos is required")
+    bad = L.AppendJob.from_buffer_copy(good)
+    bad.kind = 7
+    _expect(call(good, bad), -1, "unknown kind")
+    bad = L.AppendJob.from_buffer_copy(good)
+    bad.state_bytes = 8
+    _expect(call(win, bad), -4, "state")
+    bad = L.AppendJob.from_buffer_copy(win)
+    bad.dt_out = 2
+    _expect(call(good, bad), -1, "win_scale")
+    bad = L.AppendJob.from_buffer_copy(good)
+    bad.out_rows = 100
+    _expect(call(bad), -1, "out_rows")
 
 
 def test_quantize_validation(lib):

@@ -122,6 +122,46 @@ def test_chunked_equals_one_shot(T1):
     np.testing.assert_allclose(np.concatenate([first, second]), full, atol=1e-14)
 
 
+@pytest.mark.parametrize("m,overlap,T", [(4, True, 37), (128, False, 300), (2, True, 9)])
+def test_token_at_a_time_equals_one_shot(m, overlap, T):
+    # The decode-time compressor, fed one token at a time, emits entry j when
+    # token j*m + m - 1 arrives, and the entries are those of the one-shot
+    # compressor over the whole sequence (the overlap tail carried in state).
+    rng = np.random.default_rng(60 + m)
+    D = 5
+    ca, za = _rand(rng, T, D)
+    cb, zb = _rand(rng, T, D)
+    full = O.compress_sequence(cb, zb, m, ca, za, overlap=overlap) if overlap else \
+        O.compress_sequence(cb, zb, m, overlap=False)
+    st = O.CompressorState(m, overlap)
+    got = []
+    for t in range(T):
+        r = st.append(cb[t], zb[t], ca[t] if overlap else None, za[t] if overlap else None)
+        if (t + 1) % m == 0:
+            assert r is not None and r[0] == t // m
+            got.append(r[1])
+        else:
+            assert r is None
+    assert len(got) == T // m
+    np.testing.assert_allclose(np.array(got), full, atol=1e-14)
+
+
+def test_token_at_a_time_overlap_tail_matters():
+    # A wrong tail (a block other than j-1, or none) changes the entries: the
+    # state must carry exactly stream a's previous block.
+    rng = np.random.default_rng(61)
+    T, D, m = 16, 3, 4
+    ca, za = _rand(rng, T, D)
+    cb, zb = _rand(rng, T, D)
+    st = O.CompressorState(m, True)
+    ents = [st.append(cb[t], zb[t], ca[t], za[t]) for t in range(T)]
+    ents = [e[1] for e in ents if e is not None]
+    no_overlap = O.compress_sequence(cb, zb, m, overlap=False)
+    assert np.allclose(ents[0], no_overlap[0], atol=1e-14)          # block 0: no tail
+    for j in range(1, T // m):
+        assert not np.allclose(ents[j], no_overlap[j], atol=1e-3)
+
+
 def test_trailing_partial_block_emits_nothing():
     rng = np.random.default_rng(7)
     ca, za = _rand(rng, 14, 3)

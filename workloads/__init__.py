@@ -20,6 +20,9 @@ Recipe (also in DESIGN.md):
   by 4 before the bf16 cast.
 * "Student-t query norms" (mixed pair): each query row is g / |g| * |tau|
   with g ~ N(0, I) and tau ~ Student-t with 3 degrees of freedom.
+* Ragged decode batches: sequence positions drawn uniformly from the integers
+  in [lo, hi] by ``default_rng([seed, 3_000_000])``; the last sequence sits at
+  hi (the bound), so the batch always holds one full-length sequence.
 """
 
 from __future__ import annotations
@@ -36,6 +39,7 @@ __all__ = [
     "make_hca_decode",
     "make_csa_prefill",
     "make_mixed_pair",
+    "ragged_positions",
     "WINDOW",
 ]
 
@@ -274,3 +278,10 @@ def make_mixed_pair(seed=5, B=64, ctx=1048576, H=128, D=512, H_I=4, d_I=128,
     out["sink"] = s.standard_normal(H, dtype=np.float32)
     out["sink2"] = s.standard_normal(H, dtype=np.float32)
     return out
+
+
+def ragged_positions(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
+    """Per-sequence positions of a ragged decode batch (int64 [B])."""
+    pos = np.random.default_rng([seed, 3_000_000]).integers(lo, hi + 1, size=B, dtype=np.int64)
+    pos[-1] = hi
+    return pos
