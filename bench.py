@@ -15,7 +15,7 @@ as ragged batches (each sequence at its own position, the context as bound).
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Counter runs: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) over
-``bench.py --no-secondary --no-prefill --no-mixed --no-ragged --copy-calibration 1024``,
+``bench.py --no-secondary --no-prefill --no-mixed --no-ragged --no-placement --copy-calibration 1024``,
 then ``bench.py --pmc-summary F.csv W.csv --copy-calibration 1024``.
 """
 
@@ -363,6 +363,47 @@ def decode_state_leg(d, copies, steps, warmup, headline_ms):
                                  "kernels_us": {k_: round(v["avg_us"], 3) for k_, v in kt_sep.items()}}}
 
 
+def placement_leg(batches=(16, 64, 256, 512), steps=50, warmup=5, ctx=131072, H=64, D=512, k=512, W=128, m=4):
+    """CSA attention (csa_attend: selected entries + window + sink) at decode,
+    with the query's splits placed one workgroup per split + combine
+    (LCA_SPLITS_MANY_WG) or all in one workgroup (LCA_SPLITS_ONE_WG), at
+    growing batch sizes; both give the same bits. Inputs are drawn on the GPU
+    (bf16 N(0,1)/sqrt(D) rows, uniform random selections); four selection sets
+    rotate so that the 256 MB last-level cache cannot hold a step's rows."""
+    N = ctx // m
+    g = torch.Generator(device=DEV)
+    g.manual_seed(31)
+    res = {}
+    for B in batches:
+        E = torch.randn(B, N, D, generator=g, device=DEV, dtype=torch.bfloat16) * (D ** -0.5)
+        q = torch.randn(B, 1, H, D, generator=g, device=DEV, dtype=torch.bfloat16) * (D ** -0.5)
+        win = torch.randn(B, W, D, generator=g, device=DEV, dtype=torch.bfloat16) * (D ** -0.5)
+        sink = torch.randn(H, generator=g, device=DEV)
+        idxs = [torch.randint(0, N, (B, 1, k), generator=g, device=DEV, dtype=torch.int32) for _ in range(4)]
+        ws = torch.empty(L.csa_attend_workspace(L.BF16, L.BF16, B, 1, H, D, N, m, k, W, ctx), dtype=torch.uint8,
+                         device=DEV)
+        out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=DEV)
+        row = {}
+        for name, fl in (("split_per_workgroup", L.SPLITS_MANY_WG), ("query_per_workgroup", L.SPLITS_ONE_WG)):
+            def step(i, fl=fl):
+                L.csa_attend(L.BF16, L.BF16, q, E, idxs[i % 4], win, sink, out, m=m, W=W, q_pos0=ctx,
+                             scale=1 / math.sqrt(D), flags=L.INV_ROPE | fl, rope_dims=64, ws=ws)
+            us = 1e6 * timed(step, steps, warmup) / steps
+            kt = kernel_times(step, steps)
+            row[name] = {"us_per_call": round(us, 2), "kernels_us": {k_: round(v["avg_us"], 2) for k_, v in kt.items()}}
+        rows_bytes = B * (k + W) * D * 2
+        for v in row.values():
+            v["rows_GBs"] = round(rows_bytes / (v["us_per_call"] * 1e-6) / 1e9, 1)
+        row["speedup_query_per_workgroup"] = round(row["split_per_workgroup"]["us_per_call"] /
+                                                   row["query_per_workgroup"]["us_per_call"], 3)
+        res[f"B{B}"] = row
+        progress(f"placement B={B}: {row['split_per_workgroup']['us_per_call']:.1f} us split / "
+                 f"{row['query_per_workgroup']['us_per_call']:.1f} us one workgroup")
+        del E, q, win, idxs, ws, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def ragged_bytes(d, pos):
     """Algorithmic bytes of a ragged decode step: each sequence moves what its
     own position makes visible (indexer keys and, for HCA, entries)."""
@@ -522,6 +563,7 @@ def main():
     ap.add_argument("--no-mixed", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ragged", action="store_true")
+    ap.add_argument("--no-placement", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -579,6 +621,8 @@ def main():
         # (the pages report 99.7% on real-model data; here seeded synthetic inputs)
         "bf16_score_topk_recall": {"csa_decode": step.recall(), "pages": 0.997},
     }
+    if not args.no_placement:
+        result["placement"] = placement_leg()
     if not args.no_ragged:
         result["ragged"] = {"csa_decode_b16_ctx_le131072": ragged_leg(d, args.copies, args.steps, args.warmup,
                                                                       12, ms)}

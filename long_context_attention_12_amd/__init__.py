@@ -26,7 +26,7 @@ __all__ = [
 ]
 
 F32, BF16, KV_MIXED, MXFP4 = 0, 1, 2, 3
-NORM, ROPE, INV_ROPE, SCORE_BF16, WIN_RING = 1, 2, 4, 8, 16
+NORM, ROPE, INV_ROPE, SCORE_BF16, WIN_RING, SPLITS_ONE_WG, SPLITS_MANY_WG = 1, 2, 4, 8, 16, 32, 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "liblca.so")

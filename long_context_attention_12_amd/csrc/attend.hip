@@ -40,6 +40,7 @@ constexpr int kTileRows = 32;
 
 struct SplitPlan {
   int S, RS, n_hg, HG;
+  int SPW;                     // splits per workgroup: 1, or S (one workgroup per query and head group)
 };
 
 struct RowSpan {
@@ -460,7 +461,7 @@ __device__ __forceinline__ void tile_step_32(const uint16_t* X, const SwzOffsets
 // XCD, shared L2) take the two groups of one work item u and fetch its rows
 // once; successive u spread over all XCDs.
 __host__ __device__ __forceinline__ int64_t work_blocks(const SplitPlan& sp, int Tq) {
-  const int64_t U = static_cast<int64_t>(Tq) * sp.S;
+  const int64_t U = static_cast<int64_t>(Tq) * (sp.S / sp.SPW);
   return sp.n_hg == 2 ? (U + 7) / 8 * 16 : U * sp.n_hg;
 }
 
@@ -473,9 +474,10 @@ __device__ __forceinline__ bool work_item(const SplitPlan& sp, int Tq, int i, in
     hg = i % sp.n_hg;
     u = i / sp.n_hg;
   }
-  if (u >= static_cast<int64_t>(Tq) * sp.S) return false;
-  t = static_cast<int>(u / sp.S);
-  split = static_cast<int>(u % sp.S);
+  const int per_q = sp.S / sp.SPW;                // workgroups per query and head group
+  if (u >= static_cast<int64_t>(Tq) * per_q) return false;
+  t = static_cast<int>(u / per_q);
+  split = static_cast<int>(u % per_q) * sp.SPW;    // first split of this workgroup
   return true;
 }
 
@@ -496,45 +498,87 @@ __device__ __forceinline__ void fill_rope_table(const AttendArgs& a, int b, int 
   }
 }
 
-template <int D>
-__device__ __forceinline__ void write_output(const AttendArgs& a, int b, int t, int head, int g,
-                                             const f32x4 (&acc_o)[D / 16], float m_run, float z_run, bool flag,
-                                             const float2* rope_tab, float* ml) {
-  constexpr int DT = D / 16;
-  if (flag) {
-    if (g == 0) ml[0] = __builtin_nanf("");
+// Merge of a query's split results, in one fixed order and arithmetic that
+// every path shares (the combine kernel over partials in memory, an attention
+// kernel over its own registers), so the bits never depend on where a split
+// ran. The state starts at the sink (M = sink, Z = e^0 = 1, U = 0); split
+// (m_s, z_s, o_s), its sums relative to its own reference m_s, folds in as
+//   a = e^(M - m_s), c = 1, M = m_s   when m_s > M,   else   a = 1, c = e^(m_s - M)
+//   Z = fma(Z, a, z_s c),   U = fma(U, a, o_s c)  (each channel);
+// an empty split (m_s = -inf) changes nothing. The output is U * (1 / Z),
+// lse = M + log Z. Scaling by exactly 1 keeps the fused form equal to the
+// two-case form, bit for bit.
+struct SplitFold {
+  float M, Z;
+};
+__device__ __forceinline__ SplitFold fold_start(float sink) { return SplitFold{sink, 1.0f}; }
+__device__ __forceinline__ void fold_coeffs(SplitFold& f, float ms, float zs, float& ca, float& cc) {
+  if (ms == -INFINITY) {
+    ca = 1.0f;
+    cc = 0.0f;
     return;
   }
-  const float sink = a.sink[head];
-  const float M = fmaxf(sink, m_run);
-  const float so = m_run == -INFINITY ? 0.f : __expf(m_run - M);
-  const float Zt = z_run * so + __expf(sink - M);
-  const float inv = so / Zt;
+  if (ms > f.M) {
+    ca = __expf(f.M - ms);
+    cc = 1.0f;
+    f.M = ms;
+  } else {
+    ca = 1.0f;
+    cc = __expf(ms - f.M);
+  }
+  f.Z = fmaf(f.Z, ca, zs * cc);
+}
+// Inverse-RoPE turn of one channel pair by (cos, sin), in a fixed form.
+__device__ __forceinline__ void rope_turn(float& x, float& y, float2 cs) {
+  const float nx = fmaf(x, cs.x, -(y * cs.y));
+  const float ny = fmaf(x, cs.y, y * cs.x);
+  x = nx;
+  y = ny;
+}
+
+// Lane (g, r16) holds channels 16 dt + 4 g .. +3 of its head in U; writes the
+// head's output row (U / Z, inverse RoPE, q's dtype) and its lse.
+// Ufn(dt, i) gives the folded value of the lane's channel 16 dt + 4 g + i.
+template <int D, typename UFn>
+__device__ __forceinline__ void store_folded(const AttendArgs& a, int b, int t, int head, int g, UFn Ufn,
+                                             const SplitFold& f, const float2* rope_tab) {
+  constexpr int DT = D / 16;
+  const float inv = 1.0f / f.Z;
   const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + head;
   uint16_t* op = static_cast<uint16_t*>(a.out) + row * D;
   const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    float v[4] = {acc_o[dt][0] * inv, acc_o[dt][1] * inv, acc_o[dt][2] * inv, acc_o[dt][3] * inv};
+    float v[4] = {Ufn(dt, 0) * inv, Ufn(dt, 1) * inv, Ufn(dt, 2) * inv, Ufn(dt, 3) * inv};
     const int c0 = 16 * dt + 4 * g;
     if (c0 >= D - R) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const float2 cs = rope_tab[(c0 + 2 * p - (D - R)) / 2];
-        const float x = v[2 * p], y = v[2 * p + 1];
-        v[2 * p] = x * cs.x - y * cs.y;
-        v[2 * p + 1] = x * cs.y + y * cs.x;
-      }
+      for (int p = 0; p < 2; ++p) rope_turn(v[2 * p], v[2 * p + 1], rope_tab[(c0 + 2 * p - (D - R)) / 2]);
     }
     uint2 w;
     w.x = pack_bf16x2(v[0], v[1]);
     w.y = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(op + c0) = w;
   }
-  if (g == 0) {
-    if (a.lse_out) a.lse_out[row] = M + logf(Zt);
-    ml[0] = INFINITY;
+  if (g == 0 && a.lse_out) a.lse_out[row] = f.M + logf(f.Z);
+}
+
+// The query's only split, merged with the sink and written (fold of one split).
+// A split whose logits outgrew the headroom is left to the fixup kernel (max
+// slot NaN); otherwise the slot is set to +inf (done).
+template <int D>
+__device__ __forceinline__ void write_output(const AttendArgs& a, int b, int t, int head, int g,
+                                             const f32x4 (&acc_o)[D / 16], float m_run, float z_run, bool flag,
+                                             const float2* rope_tab, float* ml) {
+  if (flag) {
+    if (g == 0) ml[0] = __builtin_nanf("");
+    return;
   }
+  SplitFold f = fold_start(a.sink[head]);
+  float ca, cc;
+  fold_coeffs(f, m_run, z_run, ca, cc);
+  store_folded<D>(a, b, t, head, g, [&](int dt, int i) { return fmaf(0.0f, ca, acc_o[dt][i] * cc); }, f, rope_tab);
+  if (g == 0) ml[0] = INFINITY;
 }
 
 template <int D>
@@ -853,6 +897,203 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
       }
     }
   }
+}
+
+__device__ void recompute_split(const AttendArgs& a, int RS, int b, int t, int h, int s, float* red,
+                                float* lc, float& m_out, float& z_out, float2& o_out);
+
+// One workgroup per (query, 64-head group) walks all S splits of the query in
+// order (the placement for batches that fill the chip by themselves): no
+// partials, no combine. Each split runs its tiles one after another with the
+// same MFMA and softmax steps as attend_dma_kernel<1>, so its (max, sum, o)
+// has the same bits as that kernel's partial; it then folds into registers by
+// SplitFold, the combine's order and arithmetic. A split whose logits outgrew
+// the headroom is recomputed exactly here by the combine's own routine. So
+// the output has the same bits as the split kernel + combine.
+// (The pipelined loop of the split kernel holds the next tile's fragments in
+// the registers that the folded output takes here.)
+__global__ __launch_bounds__(kAttThreads) void attend_dma_fold_kernel(AttendArgs a, SplitPlan sp) {
+  constexpr int D = 512, KS = D / 32, DT = D / 16;
+  constexpr int RPW = kTileRows / 4;               // rows per wave per tile
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[kRing][kTileRows * D];
+  __shared__ int32_t rows[kMaxSplitRows];
+  __shared__ float2 rope_tab[D / 2];
+  __shared__ uint32_t flag_bits[2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
+  const int g = lane >> 4, r16 = lane & 15;
+  int split0, hg, t;
+  if (!work_item(sp, a.Tq, blockIdx.x, split0, hg, t)) return;
+  const int b = blockIdx.z;
+  const bool active = wid * 16 < sp.HG;
+  const int head = hg * sp.HG + wid * 16 + r16;
+  const RowSpan rs = row_span(a, b, t);
+  fill_rope_table(a, b, t, rope_tab);              // read after the tile loop's barriers
+  const int64_t win_rows = a.W - 1 + a.Tq;
+  const uint16_t* kvp = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(b) * a.N_cap * D;
+  const uint16_t* winp = static_cast<const uint16_t*>(a.win) + static_cast<int64_t>(b) * win_rows * D;
+  const SwzOffsets so = swz_offsets(g, r16);
+
+  bf16x8 qf[KS];
+  if (active) {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+  }
+  f32x4 U[DT];                                     // folded output, relative to fold.M
+#pragma unroll
+  for (int i = 0; i < DT; ++i) U[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  SplitFold fold = fold_start(active ? a.sink[head] : 0.f);
+
+  for (int split = split0; split < split0 + sp.SPW; ++split) {
+    __syncthreads();                               // the last split's reads of rows[] and the ring are done
+    const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
+    int64_t r_end = r_begin + sp.RS;
+    if (r_end > rs.nrows) r_end = rs.nrows;
+    const int nr = r_end > r_begin ? static_cast<int>(r_end - r_begin) : 0;
+    int32_t myrows[kMaxSplitRows / kAttThreads];
+#pragma unroll
+    for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) {
+      const int v = tid + kAttThreads * q;
+      myrows[q] = v < nr ? encode_row(a, b, t, rs, r_begin + v) : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) rows[tid + kAttThreads * q] = myrows[q];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // tile copies as in attend_dma_kernel (swizzled 1 KB rows, absent rows
+    // copy window row 0 and are masked out of the softmax)
+    auto issue = [&](int tile, uint16_t* dst) {
+      const int v0 = tile * kTileRows + wid * RPW;
+      uint64_t my = 0;
+      if (lane < RPW) {
+        const int v = v0 + lane;
+        const int32_t sr = v < nr ? rows[v] : -1;
+        const uint16_t* rowp = sr >= 0 ? kvp + static_cast<int64_t>(sr) * D
+                                       : winp + (sr == -1 ? 0 : static_cast<int64_t>(-2 - sr) * D);
+        my = reinterpret_cast<uint64_t>(rowp);
+      }
+      const uint32_t lds0 = lds_address(dst + wid * RPW * D);
+      const uint32_t lo = static_cast<uint32_t>(my), hi = static_cast<uint32_t>(my >> 32);
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const uint64_t rb = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), rr))) << 32) |
+                            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), rr));
+        const uint32_t src_off = 16u * static_cast<uint32_t>((lane & 48) | ((lane & 15) ^ slot_swizzle(wid * RPW + rr)));
+        lds_copy16(reinterpret_cast<const void*>(rb + src_off), lds0 + rr * D * 2);
+      }
+    };
+    const int ntiles = (nr + kTileRows - 1) / kTileRows;
+#pragma unroll
+    for (int t0 = 0; t0 < kRing - 1; ++t0)
+      if (t0 < ntiles) issue(t0, Xs[t0]);
+    f32x4 acc_o[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, z_run = 0.f;
+    bool flag = false;
+    // Tile it: wait for it (tiles it + 1, it + 2 may stay in flight), refill
+    // the slot of tile it - 1 with tile it + 3, then S^T, softmax, O update.
+    for (int it = 0; it < ntiles; ++it) {
+      const int later = min(ntiles - 1, it + kRing - 2) - it;
+      if (later >= 2) wait_vmcnt<2 * RPW>();
+      else if (later == 1) wait_vmcnt<RPW>();
+      else wait_vmcnt<0>();
+      if (it == 0) __builtin_amdgcn_s_waitcnt(0);  // query fragments too
+      __builtin_amdgcn_s_barrier();                 // bare: the freed slot's reads fed MFMAs already
+      if (it + kRing - 1 < ntiles) issue(it + kRing - 1, Xs[(it + kRing - 1) % kRing]);
+      const uint16_t* X = Xs[it % kRing];
+      const char* xb = reinterpret_cast<const char*>(X);
+      int4 rv[2];
+      rv[0] = *reinterpret_cast<const int4*>(rows + it * kTileRows + 4 * g);
+      rv[1] = *reinterpret_cast<const int4*>(rows + it * kTileRows + 16 + 4 * g);
+      // S^T = X Q^T as qk_load + qk_mfma do it (K steps in order, row halves
+      // inner), with the fragments loaded half the K steps at a time
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 xf[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int st = 8 * half + (j >> 1), h2 = j & 1;
+          xf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xb + so.qk[st & 3] + h2 * 16384 + 256 * (st >> 2)));
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int st = 8 * half + (j >> 1), h2 = j & 1;
+          sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[j], qf[st], sacc[h2], 0, 0, 0);
+        }
+      }
+      bf16x8 pf;
+      softmax_update_regs(sacc, rv, a.scale, m_run, z_run, flag, pf);
+      {
+        bf16x8 va[16];                              // channel tiles 0..15, then 16..31
+        pv_load<0, 16>(X, so, va);
+        pv_mfma<0, 16>(va, pf, acc_o);
+      }
+      {
+        bf16x8 vb[16];
+        pv_load<16, 16>(X, so, vb);
+        pv_mfma<16, 16>(vb, pf, acc_o);
+      }
+    }
+
+    // flagged heads: the whole workgroup recomputes each exactly, in the ring's
+    // LDS (now idle), and the owning lanes take the result
+    if (tid < 2) flag_bits[tid] = 0u;
+    __syncthreads();
+    if (active && g == 0 && flag) atomicOr(&flag_bits[wid >> 1], 1u << (16 * (wid & 1) + r16));
+    __syncthreads();
+    const uint64_t todo = static_cast<uint64_t>(flag_bits[0]) | (static_cast<uint64_t>(flag_bits[1]) << 32);
+    if (todo) {
+      float* scratch = reinterpret_cast<float*>(&Xs[0][0]);
+      float* lc = scratch;                          // kMaxSplitRows logits
+      float* ob = scratch + kMaxSplitRows;          // D outputs
+      float* red = ob + D;                          // 4 partial sums, then (m, z)
+      for (int hh = 0; hh < sp.HG; ++hh) {
+        if (!((todo >> hh) & 1u)) continue;         // uniform across the block
+        float mx, zx;
+        float2 ox;
+        recompute_split(a, sp.RS, b, t, hg * sp.HG + hh, split, red, lc, mx, zx, ox);
+        if (2 * tid < D) {
+          ob[2 * tid] = ox.x;
+          ob[2 * tid + 1] = ox.y;
+        }
+        if (tid == 0) {
+          red[4] = mx;
+          red[5] = zx;
+        }
+        __syncthreads();
+        if (wid == hh / 16 && r16 == hh % 16) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc_o[dt][i] = ob[16 * dt + 4 * g + i];
+          m_run = red[4];
+          z_run = red[5];
+        }
+        __syncthreads();                            // ob / red free for the next head
+      }
+    }
+    float ca, cc;
+    fold_coeffs(fold, m_run, z_run, ca, cc);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        U[dt][i] = fmaf(U[dt][i], ca, acc_o[dt][i] * cc);
+        // keep the folded output in accumulation registers across the next
+        // split's tile loop (the vector registers hold its fragments)
+        asm volatile("" : "+a"(U[dt][i]));
+      }
+  }
+  if (active) store_folded<D>(a, b, t, head, g, [&](int dt, int i) { return U[dt][i]; }, fold, rope_tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -1446,48 +1687,40 @@ __device__ void combine_row(const AttendArgs& a, int S, int RS, int b, int t, in
       __syncthreads();
     }
   }
-  float M = sink;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, sml[2 * s]);
-  float Z = expf(sink - M);
-  for (int s = 0; s < S; ++s) {
-    const float ms = sml[2 * s];
-    Z += ms == -INFINITY ? 0.f : sml[2 * s + 1] * expf(ms - M);
-  }
+  SplitFold f = fold_start(sink);
   float u = 0.f, v = 0.f;
 #pragma unroll
   for (int j = 0; j < kCombBatch; ++j) {
     if (j < S) {
-      const float ms = sml[2 * j];
-      const float w = ms == -INFINITY ? 0.f : expf(ms - M);
-      u = fmaf(w, ov[j].x, u);
-      v = fmaf(w, ov[j].y, v);
+      float ca, cc;
+      fold_coeffs(f, sml[2 * j], sml[2 * j + 1], ca, cc);
+      u = fmaf(u, ca, ov[j].x * cc);
+      v = fmaf(v, ca, ov[j].y * cc);
     }
   }
   for (int s = kCombBatch; s < S; ++s) {
-    const float ms = sml[2 * s];
-    const float w = ms == -INFINITY ? 0.f : expf(ms - M);
     float2 o = own ? *reinterpret_cast<const float2*>(po + static_cast<int64_t>(s) * D + 2 * c) : make_float2(0.f, 0.f);
+    float ms = sml[2 * s], zs = sml[2 * s + 1];
     if (any_flag && ml[2 * s] != ml[2 * s]) {       // flagged split beyond the batch: recompute again
-      float m2, z2;
-      recompute_split(a, RS, b, t, h, s, red, lc, m2, z2, o);
+      recompute_split(a, RS, b, t, h, s, red, lc, ms, zs, o);
     }
-    u = fmaf(w, o.x, u);
-    v = fmaf(w, o.y, v);
+    float ca, cc;
+    fold_coeffs(f, ms, zs, ca, cc);
+    u = fmaf(u, ca, o.x * cc);
+    v = fmaf(v, ca, o.y * cc);
   }
   if (own) {
-    const float inv = 1.0f / Z;
+    const float inv = 1.0f / f.Z;
     u *= inv;
     v *= inv;
-    if (c == 0 && a.lse_out) a.lse_out[row] = M + logf(Z);
+    if (c == 0 && a.lse_out) a.lse_out[row] = f.M + logf(f.Z);
     const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
     const int d0 = 2 * c;
     if (d0 >= D - R) {
       float sn, cs;
       rope_sincos(-static_cast<double>(seq_pos(a.q_pos, a.q_pos0, b) + t), (d0 - (D - R)) / 2, R,
                   static_cast<double>(a.rope_base), &sn, &cs);
-      const float nu = u * cs - v * sn, nv = u * sn + v * cs;
-      u = nu;
-      v = nv;
+      rope_turn(u, v, make_float2(cs, sn));
     }
     if (a.dt_q == LCA_F32) {
       float* o = static_cast<float*>(a.out) + row * D;
@@ -1543,10 +1776,7 @@ __global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int 
   const bool own = 8 * lane < D;
   const float* ml = part_ml + row * S * 2;
   const float* po = part_o + row * S * D + 8 * lane;
-  const float sink = a.sink[h];
-  float M = sink;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-  float Z = __expf(sink - M);
+  SplitFold f = fold_start(a.sink[h]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 8) {
     float4 v[8][2];
@@ -1559,35 +1789,29 @@ __global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (s0 + j < S) {
-        const float ms = ml[2 * (s0 + j)];
-        const float w = ms == -INFINITY ? 0.f : __expf(ms - M);
-        Z += w * ml[2 * (s0 + j) + 1];
-        acc[0] = fmaf(w, v[j][0].x, acc[0]);
-        acc[1] = fmaf(w, v[j][0].y, acc[1]);
-        acc[2] = fmaf(w, v[j][0].z, acc[2]);
-        acc[3] = fmaf(w, v[j][0].w, acc[3]);
-        acc[4] = fmaf(w, v[j][1].x, acc[4]);
-        acc[5] = fmaf(w, v[j][1].y, acc[5]);
-        acc[6] = fmaf(w, v[j][1].z, acc[6]);
-        acc[7] = fmaf(w, v[j][1].w, acc[7]);
+        float ca, cc;
+        fold_coeffs(f, ml[2 * (s0 + j)], ml[2 * (s0 + j) + 1], ca, cc);
+        acc[0] = fmaf(acc[0], ca, v[j][0].x * cc);
+        acc[1] = fmaf(acc[1], ca, v[j][0].y * cc);
+        acc[2] = fmaf(acc[2], ca, v[j][0].z * cc);
+        acc[3] = fmaf(acc[3], ca, v[j][0].w * cc);
+        acc[4] = fmaf(acc[4], ca, v[j][1].x * cc);
+        acc[5] = fmaf(acc[5], ca, v[j][1].y * cc);
+        acc[6] = fmaf(acc[6], ca, v[j][1].z * cc);
+        acc[7] = fmaf(acc[7], ca, v[j][1].w * cc);
       }
     }
   }
-  if (lane == 0 && a.lse_out) a.lse_out[row] = M + logf(Z);
+  if (lane == 0 && a.lse_out) a.lse_out[row] = f.M + logf(f.Z);
   if (!own) return;
-  const float inv = 1.f / Z;
+  const float inv = 1.f / f.Z;
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] *= inv;
   const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
   const int c0 = 8 * lane;
   if (c0 >= D - R) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float2 cs = rope_tab[(c0 + 2 * p - (D - R)) / 2];
-      const float x = acc[2 * p], y = acc[2 * p + 1];
-      acc[2 * p] = x * cs.x - y * cs.y;
-      acc[2 * p + 1] = x * cs.y + y * cs.x;
-    }
+    for (int p = 0; p < 4; ++p) rope_turn(acc[2 * p], acc[2 * p + 1], rope_tab[(c0 + 2 * p - (D - R)) / 2]);
   }
   if (a.dt_q == LCA_F32) {
     float* o = static_cast<float*>(a.out) + row * D + c0;
@@ -1690,6 +1914,7 @@ SplitPlan make_plan(const AttendArgs& a) {
   }
   sp.S = static_cast<int>(S);
   sp.RS = static_cast<int>(RS);
+  sp.SPW = 1;
   return sp;
 }
 
@@ -1703,6 +1928,8 @@ void launch_mfma_d(LaunchScope& sc, const AttendArgs& a, const SplitPlan& sp, fl
       sc.launch(attend_mixed_dma_kernel<1>, grid, block, 0, a, sp, po, pml);
     else if (sp.HG == 128)
       sc.launch(attend_dma_kernel<2>, grid, block, 0, a, sp, po, pml);
+    else if (sp.SPW > 1)
+      sc.launch(attend_dma_fold_kernel, grid, block, 0, a, sp);
     else
       sc.launch(attend_dma_kernel<1>, grid, block, 0, a, sp, po, pml);
   } else {
@@ -1718,8 +1945,30 @@ size_t attend_workspace(const AttendArgs& a) {
   return rows * (a.D + 2) * sizeof(float) + 256;
 }
 
+// Placement of a query's splits. The split kernel (one workgroup per split,
+// partials, combine) keeps the chip busy for small batches; one workgroup per
+// query and head group (all splits in turn, folded in registers) moves no
+// partials, which at decode shapes weigh several times the rows themselves,
+// and pays once the batch alone gives a workgroup to every CU. Both give the
+// same bits (SplitFold), so the choice may follow the batch size.
+// LCA_SPLITS_ONE_WG / LCA_SPLITS_MANY_WG force a placement.
+constexpr int64_t kOneWgMinItems = 256;
+
+bool folds_in_kernel(const AttendArgs& a, const SplitPlan& sp) {
+  return a.D == 512 && a.dt_kv == LCA_BF16 && sp.HG != 128;   // attend_dma_fold_kernel
+}
+
+void place_splits(const AttendArgs& a, SplitPlan& sp) {
+  if (!folds_in_kernel(a, sp) || sp.S == 1) return;
+  bool one = static_cast<int64_t>(a.B) * a.Tq * sp.n_hg >= kOneWgMinItems;
+  if (a.flags & LCA_SPLITS_ONE_WG) one = true;
+  if (a.flags & LCA_SPLITS_MANY_WG) one = false;
+  if (one) sp.SPW = sp.S;
+}
+
 hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
-  const SplitPlan sp = make_plan(a);
+  SplitPlan sp = make_plan(a);
+  place_splits(a, sp);
   if (work_blocks(sp, a.Tq) > 2147483647LL) return hipErrorInvalidConfiguration;
   const size_t rows = static_cast<size_t>(a.B) * a.Tq * a.H * sp.S;
   float* po = static_cast<float*>(ws);
@@ -1742,6 +1991,8 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // one workgroup per query folded its splits itself: nothing left to merge
+  if (sp.SPW > 1) return hipSuccess;
   {
     LaunchScope scope(s, a.sparse ? "csa_combine" : "hca_combine");
     const dim3 cb(a.D / 2 > 64 ? a.D / 2 : 64);

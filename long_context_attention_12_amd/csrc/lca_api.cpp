@@ -377,7 +377,10 @@ static int check_attend(const lca::AttendArgs& a, const char* fn) {
   } else {
     return fail(LCA_ERR_UNSUPPORTED, "%s: dt_kv must be F32, BF16 or KV_MIXED", fn);
   }
-  if (a.flags & ~(LCA_INV_ROPE | LCA_WIN_RING)) return fail(LCA_ERR_ARG, "%s: only LCA_INV_ROPE and LCA_WIN_RING apply", fn);
+  if (a.flags & ~(LCA_INV_ROPE | LCA_WIN_RING | LCA_SPLITS_ONE_WG | LCA_SPLITS_MANY_WG))
+    return fail(LCA_ERR_ARG, "%s: only LCA_INV_ROPE, LCA_WIN_RING and LCA_SPLITS_* apply", fn);
+  if ((a.flags & LCA_SPLITS_ONE_WG) && (a.flags & LCA_SPLITS_MANY_WG))
+    return fail(LCA_ERR_ARG, "%s: LCA_SPLITS_ONE_WG and LCA_SPLITS_MANY_WG exclude each other", fn);
   if (a.rope_dims < 0 || a.rope_dims > a.D || a.rope_dims % 2) return fail(LCA_ERR_ARG, "%s: rope_dims must be even and in [0, D]", fn);
   if ((a.flags & LCA_INV_ROPE) && (a.rope_dims == 0 || !(a.rope_base > 0.f))) return fail(LCA_ERR_ARG, "%s: LCA_INV_ROPE needs rope_dims > 0 and rope_base > 0", fn);
   if (!(a.scale == a.scale)) return fail(LCA_ERR_ARG, "%s: scale is NaN", fn);

@@ -109,7 +109,8 @@ def test_attend_validation(lib):
     _expect(call(dt_q=0), -2, "BF16 q")
     _expect(call(dt_kv=2, R=64), -1, "kv_scale")
     _expect(call(flags=4), -1, "LCA_INV_ROPE needs")
-    _expect(call(flags=8), -1, "LCA_WIN_RING apply")
+    _expect(call(flags=8), -1, "LCA_SPLITS_* apply")
+    _expect(call(flags=32 | 64), -1, "exclude each other")
     _expect(call(idx=None), -1, "missing")
     _expect(call(W=0), -1, "W must")
     _expect(call(ws=None), -4, "workspace")
