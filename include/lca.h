@@ -75,9 +75,11 @@ extern "C" {
 #define LCA_SPLITS_ONE_WG  32u /* attend: run all of a query's splits in one
                               workgroup (no partials, no combine) where a kernel
                               for it exists (bf16 rows, D = 512, heads not a
-                              multiple of 128); the default picks it when the
-                              batch gives >= 256 (query, head group) items.
-                              Same bits either way: a placement choice only  */
+                              multiple of 128); by default a cost model picks
+                              it from the batch size ([Qiaomu] 批不变 kernel,
+                              [kwkr] §4.3: a throughput and a latency kernel
+                              with one accumulation order). Same bits either
+                              way: a placement choice only                    */
 #define LCA_SPLITS_MANY_WG 64u /* attend: one workgroup per split + combine     */
 #define LCA_WIN_RING   16u /* attend: win is a ring of W-1+Tq rows per sequence,
                               position p in row p mod (W-1+Tq) (lca_window_append

@@ -904,12 +904,16 @@ __device__ void recompute_split(const AttendArgs& a, int RS, int b, int t, int h
 
 // One workgroup per (query, 64-head group) walks all S splits of the query in
 // order (the placement for batches that fill the chip by themselves): no
-// partials, no combine. Each split runs its tiles one after another with the
-// same MFMA and softmax steps as attend_dma_kernel<1>, so its (max, sum, o)
-// has the same bits as that kernel's partial; it then folds into registers by
-// SplitFold, the combine's order and arithmetic. A split whose logits outgrew
-// the headroom is recomputed exactly here by the combine's own routine. So
-// the output has the same bits as the split kernel + combine.
+// partials, no combine. Each split runs its tiles with the same MFMA and
+// softmax steps as attend_dma_kernel<1>, so its (max, sum, o) has the same
+// bits as that kernel's partial; it then folds into registers by SplitFold,
+// the combine's order and arithmetic. A split whose logits outgrew the
+// headroom is recomputed exactly here by the combine's own routine. So the
+// output has the same bits as the split kernel + combine.
+// Splits are only arithmetic boundaries here: the row table covers as many
+// whole splits as it holds, and the tile ring streams across split ends
+// (where the split's result folds in and its accumulators restart). The
+// exact recompute has LDS of its own, so tiles stay in flight meanwhile.
 // (The pipelined loop of the split kernel holds the next tile's fragments in
 // the registers that the folded output takes here.)
 __global__ __launch_bounds__(kAttThreads) void attend_dma_fold_kernel(AttendArgs a, SplitPlan sp) {
@@ -918,6 +922,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_fold_kernel(AttendArgs
   __shared__ __attribute__((aligned(16))) uint16_t Xs[kRing][kTileRows * D];
   __shared__ int32_t rows[kMaxSplitRows];
   __shared__ float2 rope_tab[D / 2];
+  __shared__ float rc_lc[kMaxSplitRows];            // exact recompute: logits of one split
+  __shared__ float rc_o[D + 8];                     // its output row, then (m, z); + partial sums
   __shared__ uint32_t flag_bits[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -934,6 +940,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_fold_kernel(AttendArgs
   const uint16_t* kvp = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(b) * a.N_cap * D;
   const uint16_t* winp = static_cast<const uint16_t*>(a.win) + static_cast<int64_t>(b) * win_rows * D;
   const SwzOffsets so = swz_offsets(g, r16);
+  const int tps = sp.RS / kTileRows;               // tiles per split
+  const int spc = kMaxSplitRows / sp.RS;           // splits per row table
 
   bf16x8 qf[KS];
   if (active) {
@@ -950,10 +958,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_fold_kernel(AttendArgs
   for (int i = 0; i < DT; ++i) U[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   SplitFold fold = fold_start(active ? a.sink[head] : 0.f);
 
-  for (int split = split0; split < split0 + sp.SPW; ++split) {
-    __syncthreads();                               // the last split's reads of rows[] and the ring are done
-    const int64_t r_begin = static_cast<int64_t>(split) * sp.RS;
-    int64_t r_end = r_begin + sp.RS;
+  for (int c0 = split0; c0 < split0 + sp.SPW; c0 += spc) {
+    const int c1 = min(c0 + spc, split0 + sp.SPW);  // splits [c0, c1) in this row table
+    __syncthreads();                               // the last table's reads of rows[] and the ring are done
+    const int64_t r_begin = static_cast<int64_t>(c0) * sp.RS;
+    int64_t r_end = static_cast<int64_t>(c1) * sp.RS;
     if (r_end > rs.nrows) r_end = rs.nrows;
     const int nr = r_end > r_begin ? static_cast<int>(r_end - r_begin) : 0;
     int32_t myrows[kMaxSplitRows / kAttThreads];
@@ -994,104 +1003,125 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_fold_kernel(AttendArgs
     for (int t0 = 0; t0 < kRing - 1; ++t0)
       if (t0 < ntiles) issue(t0, Xs[t0]);
     f32x4 acc_o[DT];
-#pragma unroll
-    for (int i = 0; i < DT; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, z_run = 0.f;
     bool flag = false;
-    // Tile it: wait for it (tiles it + 1, it + 2 may stay in flight), refill
-    // the slot of tile it - 1 with tile it + 3, then S^T, softmax, O update.
-    for (int it = 0; it < ntiles; ++it) {
-      const int later = min(ntiles - 1, it + kRing - 2) - it;
-      if (later >= 2) wait_vmcnt<2 * RPW>();
-      else if (later == 1) wait_vmcnt<RPW>();
-      else wait_vmcnt<0>();
-      if (it == 0) __builtin_amdgcn_s_waitcnt(0);  // query fragments too
-      __builtin_amdgcn_s_barrier();                 // bare: the freed slot's reads fed MFMAs already
-      if (it + kRing - 1 < ntiles) issue(it + kRing - 1, Xs[(it + kRing - 1) % kRing]);
-      const uint16_t* X = Xs[it % kRing];
-      const char* xb = reinterpret_cast<const char*>(X);
-      int4 rv[2];
-      rv[0] = *reinterpret_cast<const int4*>(rows + it * kTileRows + 4 * g);
-      rv[1] = *reinterpret_cast<const int4*>(rows + it * kTileRows + 16 + 4 * g);
-      // S^T = X Q^T as qk_load + qk_mfma do it (K steps in order, row halves
-      // inner), with the fragments loaded half the K steps at a time
-      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 xf[16];
+    for (int i = 0; i < DT; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Every split of [c0, c1) ends on a tile boundary (RS is a multiple of the
+    // tile); splits past the query's rows have no tiles and fold as empty.
+    const int nsplit = c1 - c0;
+    for (int sl = 0, it = 0; sl < nsplit; ++sl) {
+      const int it_end = min(ntiles, (sl + 1) * tps);
+      for (; it < it_end; ++it) {
+        // tile it: wait for it (tiles it + 1, it + 2 may stay in flight),
+        // refill the slot of tile it - 1 with tile it + 3, then S^T, softmax,
+        // output update
+        const int later = min(ntiles - 1, it + kRing - 2) - it;
+        if (later >= 2) wait_vmcnt<2 * RPW>();
+        else if (later == 1) wait_vmcnt<RPW>();
+        else wait_vmcnt<0>();
+        if (it == 0) __builtin_amdgcn_s_waitcnt(0);  // query fragments too
+        __builtin_amdgcn_s_barrier();               // bare: the freed slot's reads fed MFMAs already
+        if (it + kRing - 1 < ntiles) issue(it + kRing - 1, Xs[(it + kRing - 1) % kRing]);
+        const uint16_t* X = Xs[it % kRing];
+        const char* xb = reinterpret_cast<const char*>(X);
+        const int v0 = it * kTileRows;
+        int4 rv[2];
+        rv[0] = *reinterpret_cast<const int4*>(rows + v0 + 4 * g);
+        rv[1] = *reinterpret_cast<const int4*>(rows + v0 + 16 + 4 * g);
+        // S^T = X Q^T as qk_load + qk_mfma do it (K steps in order, row halves
+        // inner), with the fragments loaded half the K steps at a time
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int st = 8 * half + (j >> 1), h2 = j & 1;
-          xf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xb + so.qk[st & 3] + h2 * 16384 + 256 * (st >> 2)));
+        for (int qtr = 0; qtr < 4; ++qtr) {
+          bf16x8 xf[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int st = 4 * qtr + (j >> 1), h2 = j & 1;
+            xf[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(xb + so.qk[st & 3] + h2 * 16384 + 256 * (st >> 2)));
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int st = 4 * qtr + (j >> 1), h2 = j & 1;
+            sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[j], qf[st], sacc[h2], 0, 0, 0);
+          }
         }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int st = 8 * half + (j >> 1), h2 = j & 1;
-          sacc[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[j], qf[st], sacc[h2], 0, 0, 0);
+        bf16x8 pf;
+        softmax_update_regs(sacc, rv, a.scale, m_run, z_run, flag, pf);
+        // output update in four channel quarters (same MFMAs, fewer live fragments)
+        {
+          bf16x8 v0f[8];
+          pv_load<0, 8>(X, so, v0f);
+          pv_mfma<0, 8>(v0f, pf, acc_o);
+        }
+        {
+          bf16x8 v1f[8];
+          pv_load<8, 8>(X, so, v1f);
+          pv_mfma<8, 8>(v1f, pf, acc_o);
+        }
+        {
+          bf16x8 v2f[8];
+          pv_load<16, 8>(X, so, v2f);
+          pv_mfma<16, 8>(v2f, pf, acc_o);
+        }
+        {
+          bf16x8 v3f[8];
+          pv_load<24, 8>(X, so, v3f);
+          pv_mfma<24, 8>(v3f, pf, acc_o);
         }
       }
-      bf16x8 pf;
-      softmax_update_regs(sacc, rv, a.scale, m_run, z_run, flag, pf);
-      {
-        bf16x8 va[16];                              // channel tiles 0..15, then 16..31
-        pv_load<0, 16>(X, so, va);
-        pv_mfma<0, 16>(va, pf, acc_o);
-      }
-      {
-        bf16x8 vb[16];
-        pv_load<16, 16>(X, so, vb);
-        pv_mfma<16, 16>(vb, pf, acc_o);
-      }
-    }
 
-    // flagged heads: the whole workgroup recomputes each exactly, in the ring's
-    // LDS (now idle), and the owning lanes take the result
-    if (tid < 2) flag_bits[tid] = 0u;
-    __syncthreads();
-    if (active && g == 0 && flag) atomicOr(&flag_bits[wid >> 1], 1u << (16 * (wid & 1) + r16));
-    __syncthreads();
-    const uint64_t todo = static_cast<uint64_t>(flag_bits[0]) | (static_cast<uint64_t>(flag_bits[1]) << 32);
-    if (todo) {
-      float* scratch = reinterpret_cast<float*>(&Xs[0][0]);
-      float* lc = scratch;                          // kMaxSplitRows logits
-      float* ob = scratch + kMaxSplitRows;          // D outputs
-      float* red = ob + D;                          // 4 partial sums, then (m, z)
-      for (int hh = 0; hh < sp.HG; ++hh) {
-        if (!((todo >> hh) & 1u)) continue;         // uniform across the block
-        float mx, zx;
-        float2 ox;
-        recompute_split(a, sp.RS, b, t, hg * sp.HG + hh, split, red, lc, mx, zx, ox);
-        if (2 * tid < D) {
-          ob[2 * tid] = ox.x;
-          ob[2 * tid + 1] = ox.y;
-        }
-        if (tid == 0) {
-          red[4] = mx;
-          red[5] = zx;
-        }
-        __syncthreads();
-        if (wid == hh / 16 && r16 == hh % 16) {
+      // split c0 + sl ends: flagged heads are recomputed exactly by the whole
+      // workgroup (the owning lanes take the result), then the split folds in
+      const int split = c0 + sl;
+      if (tid < 2) flag_bits[tid] = 0u;
+      __syncthreads();
+      if (active && g == 0 && flag) atomicOr(&flag_bits[wid >> 1], 1u << (16 * (wid & 1) + r16));
+      __syncthreads();
+      const uint64_t todo = static_cast<uint64_t>(flag_bits[0]) | (static_cast<uint64_t>(flag_bits[1]) << 32);
+      if (todo) {
+        for (int hh = 0; hh < sp.HG; ++hh) {
+          if (!((todo >> hh) & 1u)) continue;       // uniform across the block
+          float mx, zx;
+          float2 ox;
+          recompute_split(a, sp.RS, b, t, hg * sp.HG + hh, split, rc_o + D + 2, rc_lc, mx, zx, ox);
+          if (2 * tid < D) {
+            rc_o[2 * tid] = ox.x;
+            rc_o[2 * tid + 1] = ox.y;
+          }
+          __syncthreads();
+          if (tid == 0) {
+            rc_o[D] = mx;
+            rc_o[D + 1] = zx;
+          }
+          __syncthreads();
+          if (wid == hh / 16 && r16 == hh % 16) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc_o[dt][i] = ob[16 * dt + 4 * g + i];
-          m_run = red[4];
-          z_run = red[5];
+              for (int i = 0; i < 4; ++i) acc_o[dt][i] = rc_o[16 * dt + 4 * g + i];
+            m_run = rc_o[D];
+            z_run = rc_o[D + 1];
+          }
+          __syncthreads();                          // rc_o free for the next head
         }
-        __syncthreads();                            // ob / red free for the next head
       }
+      float ca, cc;
+      fold_coeffs(fold, m_run, z_run, ca, cc);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          U[dt][i] = fmaf(U[dt][i], ca, acc_o[dt][i] * cc);
+          // keep the folded output in accumulation registers across the next
+          // split's tiles (the vector registers hold their fragments)
+          asm volatile("" : "+a"(U[dt][i]));
+          acc_o[dt][i] = 0.f;
+        }
+      m_run = -INFINITY;
+      z_run = 0.f;
+      flag = false;
     }
-    float ca, cc;
-    fold_coeffs(fold, m_run, z_run, ca, cc);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        U[dt][i] = fmaf(U[dt][i], ca, acc_o[dt][i] * cc);
-        // keep the folded output in accumulation registers across the next
-        // split's tile loop (the vector registers hold its fragments)
-        asm volatile("" : "+a"(U[dt][i]));
-      }
   }
   if (active) store_folded<D>(a, b, t, head, g, [&](int dt, int i) { return U[dt][i]; }, fold, rope_tab);
 }
@@ -1946,13 +1976,15 @@ size_t attend_workspace(const AttendArgs& a) {
 }
 
 // Placement of a query's splits. The split kernel (one workgroup per split,
-// partials, combine) keeps the chip busy for small batches; one workgroup per
-// query and head group (all splits in turn, folded in registers) moves no
-// partials, which at decode shapes weigh several times the rows themselves,
-// and pays once the batch alone gives a workgroup to every CU. Both give the
-// same bits (SplitFold), so the choice may follow the batch size.
+// partials, combine) spreads a query over many CUs; one workgroup per query
+// and head group (all splits in turn, folded in registers) moves no partials,
+// which at decode shapes weigh several times the rows themselves. Both give
+// the same bits (SplitFold), so the choice may follow the batch size. The
+// model: rounds of the chip (one workgroup per CU) times the bytes a workgroup
+// moves per round; rows only for one workgroup per query, rows plus the
+// split's partial (written, then read by the combine) for the split kernel.
 // LCA_SPLITS_ONE_WG / LCA_SPLITS_MANY_WG force a placement.
-constexpr int64_t kOneWgMinItems = 256;
+constexpr int64_t kCUs = 256;
 
 bool folds_in_kernel(const AttendArgs& a, const SplitPlan& sp) {
   return a.D == 512 && a.dt_kv == LCA_BF16 && sp.HG != 128;   // attend_dma_fold_kernel
@@ -1960,7 +1992,12 @@ bool folds_in_kernel(const AttendArgs& a, const SplitPlan& sp) {
 
 void place_splits(const AttendArgs& a, SplitPlan& sp) {
   if (!folds_in_kernel(a, sp) || sp.S == 1) return;
-  bool one = static_cast<int64_t>(a.B) * a.Tq * sp.n_hg >= kOneWgMinItems;
+  const int64_t items = static_cast<int64_t>(a.B) * a.Tq * sp.n_hg;
+  const double rows = static_cast<double>(sp.RS) * a.D * 2;                  // one split's rows (bf16)
+  const double part = 2.0 * sp.HG * (a.D + 2) * 4;                         // its partial, out and back
+  const double t_one = static_cast<double>((items + kCUs - 1) / kCUs) * sp.S * rows;
+  const double t_split = static_cast<double>((items * sp.S + kCUs - 1) / kCUs) * (rows + part);
+  bool one = t_one <= t_split;
   if (a.flags & LCA_SPLITS_ONE_WG) one = true;
   if (a.flags & LCA_SPLITS_MANY_WG) one = false;
   if (one) sp.SPW = sp.S;
