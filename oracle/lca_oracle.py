@@ -47,6 +47,7 @@ __all__ = [
     "e2m1_decode",
     "mxfp4_quantize",
     "mxfp4_decode",
+    "grouped_output_projection",
     "E4M3_MAX",
     "E2M1_GRID",
 ]
@@ -618,3 +619,48 @@ def mxfp4_decode(codes, scales, block=32):
     vals = e2m1_decode(codes).reshape(-1, n // block, block)
     s = np.ldexp(1.0, scales.reshape(-1, n // block) - 127)[..., None]
     return (vals * s).reshape(shp)
+
+
+# ---------------------------------------------------------------------------
+# Grouped output projection (the step after core attention)
+# ---------------------------------------------------------------------------
+
+def grouped_output_projection(o, w_g, w_o, round_mid=True):
+    """Grouped output projection of the attention output.
+
+    [Qiaomu] 预训练策略 (model configurations) and [cdjax] §1.1: the n_h heads
+    split into g groups of n_h/g consecutive heads; each group's concatenated
+    head outputs project to an intermediate width d_g (Flash: g = 8, Pro: 16,
+    d_g = 1024), the g results concatenate, and one more projection maps them
+    to the model width. [kwkr] §3.4: this cuts the output projection's
+    parameters and FLOPs when heads are many.
+
+    Args:
+      o:   [T, n_h, c] attention output rows.
+      w_g: [g, d_g, (n_h/g)*c] group projections, row j = intermediate channel j
+           (the layout of a linear layer's weight).
+      w_o: [d_model, g*d_g] the merging projection.
+      round_mid: round the intermediate to bf16 (reading: it is stored in bf16
+           between the two products, as the operand of the second one).
+    Returns: [T, d_model] float64.
+
+    Pinned by: g = 1 is the plain two-matrix product; the grouped form equals
+    the product with the explicit block-diagonal matrix; permuting heads inside
+    a group together with the matching weight columns changes nothing; scalar
+    loops on tiny inputs (tests/test_oracle_outproj.py).
+    """
+    o = np.asarray(o, dtype=np.float64)
+    w_g = np.asarray(w_g, dtype=np.float64)
+    w_o = np.asarray(w_o, dtype=np.float64)
+    T, n_h, c = o.shape
+    g, d_g, kg = w_g.shape
+    assert n_h % g == 0 and kg == (n_h // g) * c
+    mids = []
+    for gi in range(g):
+        xg = o[:, gi * (n_h // g):(gi + 1) * (n_h // g), :].reshape(T, kg)
+        mids.append(xg @ w_g[gi].T)
+    mid = np.concatenate(mids, axis=1)
+    if round_mid:
+        mid = bf16_round(mid)
+    return mid @ w_o.T
+
