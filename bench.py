@@ -15,7 +15,7 @@ as ragged batches (each sequence at its own position, the context as bound).
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Counter runs: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) over
-``bench.py --no-secondary --no-prefill --no-mixed --no-ragged --no-placement --copy-calibration 1024``,
+``bench.py --no-secondary --no-prefill --no-mixed --no-ragged --no-placement --no-outproj --copy-calibration 1024``,
 then ``bench.py --pmc-summary F.csv W.csv --copy-calibration 1024``.
 """
 
@@ -404,6 +404,48 @@ def placement_leg(batches=(16, 64, 256, 512), steps=50, warmup=5, ctx=131072, H=
     return res
 
 
+def outproj_leg(steps=50, warmup=5):
+    """Grouped output projection (lca_grouped_out_proj) at the pages' shapes:
+    Flash (64 heads x 512 -> 8 groups x 1024 -> 4096) at decode batch 16 and
+    a 4096-row prefill chunk, Pro (128 heads -> 16 x 1024 -> 7168) at batch
+    64. bf16 weights drawn on the GPU; enough weight copies rotate that the
+    256 MB last-level cache cannot serve a step's weights from the last one."""
+    g_ = torch.Generator(device=DEV)
+    g_.manual_seed(41)
+    res = {}
+    for name, T, n_h, g, d_model in (("flash_decode_b16", 16, 64, 8, 4096), ("pro_decode_b64", 64, 128, 16, 7168),
+                                     ("flash_prefill_t4096", 4096, 64, 8, 4096)):
+        c, d_g = 512, 1024
+        kg = n_h // g * c
+        wbytes = 2 * (g * d_g * kg + d_model * g * d_g)
+        copies = max(1, -(-3 * 256 * 2 ** 20 // wbytes)) if T <= 64 else 1
+        sets = [(torch.randn(g, d_g, kg, generator=g_, device=DEV, dtype=torch.bfloat16) * kg ** -0.5,
+                 torch.randn(d_model, g * d_g, generator=g_, device=DEV, dtype=torch.bfloat16) * (g * d_g) ** -0.5)
+                for _ in range(copies)]
+        o = torch.randn(T, n_h, c, generator=g_, device=DEV, dtype=torch.bfloat16)
+        mid = torch.empty((T, g * d_g), dtype=torch.bfloat16, device=DEV)
+        out = torch.empty((T, d_model), dtype=torch.bfloat16, device=DEV)
+
+        def step(i):
+            wg, wo = sets[i % copies]
+            L.lca_grouped_out_proj(o, wg, wo, out, mid=mid)
+        n = steps if T <= 64 else 5
+        us = 1e6 * timed(step, n, warmup if T <= 64 else 1) / n
+        kt = kernel_times(step, n)
+        abytes = wbytes + 2 * (T * n_h * c + 2 * T * g * d_g + T * d_model)
+        flops = 2.0 * T * (g * d_g * kg + d_model * g * d_g)
+        res[name] = {"rows": T, "us_per_call": round(us, 2), "weight_copies_rotated": copies,
+                     "kernels_us": {k_: round(v["avg_us"], 2) for k_, v in kt.items()},
+                     "algorithmic_bytes": abytes, "achieved_GBs": round(abytes / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(abytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+                     "flops": flops, "achieved_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+                     "mfma_bf16_frac": round(flops / (us * 1e-6) / 2.5e15, 3)}
+        progress(f"grouped out proj {name}: {us:.1f} us")
+        del sets, o, mid, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def ragged_bytes(d, pos):
     """Algorithmic bytes of a ragged decode step: each sequence moves what its
     own position makes visible (indexer keys and, for HCA, entries)."""
@@ -564,6 +606,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-placement", action="store_true")
+    ap.add_argument("--no-outproj", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -623,6 +666,8 @@ def main():
     }
     if not args.no_placement:
         result["placement"] = placement_leg()
+    if not args.no_outproj:
+        result["grouped_out_proj"] = outproj_leg()
     if not args.no_ragged:
         result["ragged"] = {"csa_decode_b16_ctx_le131072": ragged_leg(d, args.copies, args.steps, args.warmup,
                                                                       12, ms)}

@@ -347,7 +347,31 @@ int hca_attend_ragged(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, i
                       uint32_t flags, float rope_base, int rope_dims,
                       void* out, float* lse_out, void* ws, size_t ws_bytes);
 
-/* ---- diagnostics ------------------------------------------------------- *//* ---- diagnostics ------------------------------------------------------- */
+/* ---------------------------------------------------------------------------
+ * lca_grouped_out_proj — grouped output projection after core attention.
+ *
+ * [Qiaomu] 预训练策略 (model configurations), [cdjax] §1.1, [kwkr] §3.4: the
+ * n_h heads form g groups of n_h/g consecutive heads; group gi's outputs
+ * (n_h/g * c values per row) project to d_g channels, the g results
+ * concatenate, and one more projection maps g*d_g channels to d_model
+ * (Flash: n_h = 64, c = 512, g = 8, d_g = 1024, d_model = 4096; Pro: 128
+ * heads, g = 16, d_model = 7168).
+ *   o    [T, n_h, c] bf16        attention output rows (T = batch x queries)
+ *   w_g  [g, d_g, (n_h/g)*c] bf16  row j of group gi = intermediate channel j
+ *   w_o  [d_model, g*d_g] bf16   row n = output channel n
+ *   mid  [T, g*d_g] bf16         the concatenated intermediate (written; the
+ *                                second product reads it)
+ *   out  [T, d_model] bf16
+ * Sums are fp32; mid and out are rounded to bf16 (round to nearest even).
+ * The sum over K runs in eight fixed parts added in a fixed order:
+ * deterministic, and each row independent of T.
+ * Requirements: n_h % g == 0; (n_h/g)*c and g*d_g multiples of 256; d_g and
+ * d_model multiples of 16; buffers 16-byte aligned (device memory, caller-owned).
+ * ------------------------------------------------------------------------- */
+int lca_grouped_out_proj(void* stream, int T, int n_h, int c, int g, int d_g, int d_model,
+                         const void* o, const void* w_g, const void* w_o, void* mid, void* out);
+
+/* ---- diagnostics ------------------------------------------------------- */
 const char* lca_status_str(int status);
 const char* lca_last_error(void); /* thread-local text of the last failure */
 int lca_version(void);            /* major*10000 + minor*100 + patch       */

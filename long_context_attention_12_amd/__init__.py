@@ -98,6 +98,8 @@ def _declare(L):
     L.lca_window_append.restype = i32
     L.lca_decode_append.argtypes = [vp, i32, i64, vp, ctypes.POINTER(AppendJob), i32]
     L.lca_decode_append.restype = i32
+    L.lca_grouped_out_proj.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.lca_grouped_out_proj.restype = i32
     L.lca_status_str.argtypes = [i32]
     L.lca_status_str.restype = ctypes.c_char_p
     L.lca_last_error.argtypes = []
@@ -302,6 +304,20 @@ def hca_attend(dt_q, dt_kv, q, kv, win, sink, out, *, m, W, q_pos0, scale, N_cap
                             _p(kv), _p(kv_scale), _p(win), _p(win_scale), _p(sink), scale, flags,
                             rope_base, rope_dims, _p(out), _p(lse_out), _p(ws),
                             ws.numel() * ws.element_size()))
+
+
+def lca_grouped_out_proj(o, w_g, w_o, out, *, mid=None, stream=None):
+    """Grouped output projection: o [T, n_h, c], w_g [g, d_g, (n_h/g)*c],
+    w_o [d_model, g*d_g] (bf16) -> out [T, d_model]; see include/lca.h.
+    mid [T, g*d_g] is allocated when not given; returns it."""
+    T, n_h, c = o.shape
+    g, d_g, _ = w_g.shape
+    d_model = w_o.shape[0]
+    if mid is None:
+        mid = torch.empty((T, g * d_g), dtype=torch.bfloat16, device=o.device)
+    _check(lib().lca_grouped_out_proj(_stream(stream), T, n_h, c, g, d_g, d_model, _p(o), _p(w_g), _p(w_o),
+                                      _p(mid), _p(out)))
+    return mid
 
 
 def lca_version():

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblca.so")
-SOURCES = ["compress.hip", "index_topk.hip", "attend.hip", "lca_api.cpp"]
+SOURCES = ["compress.hip", "index_topk.hip", "attend.hip", "out_proj.hip", "lca_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -293,6 +293,27 @@ int lca_window_append(void* stream, int dt_in, int dt_out, int B, int D, int rop
   return hip_status(lca::launch_append(static_cast<hipStream_t>(stream), js, B, pos_max, pos, "window_append"), fn);
 }
 
+int lca_grouped_out_proj(void* stream, int T, int n_h, int c, int g, int d_g, int d_model, const void* o,
+                         const void* w_g, const void* w_o, void* mid, void* out) {
+  const char* fn = "lca_grouped_out_proj";
+  if (T < 1 || n_h < 1 || c < 1 || g < 1 || d_g < 1 || d_model < 1)
+    return fail(LCA_ERR_ARG, "%s: need T, n_h, c, g, d_g, d_model >= 1", fn);
+  if (n_h % g != 0) return fail(LCA_ERR_ARG, "%s: n_h (%d) must be a multiple of g (%d)", fn, n_h, g);
+  const int64_t kg = static_cast<int64_t>(n_h / g) * c, mid_w = static_cast<int64_t>(g) * d_g;
+  if (kg % 256 != 0 || mid_w % 256 != 0)
+    return fail(LCA_ERR_UNSUPPORTED, "%s: (n_h/g)*c (%lld) and g*d_g (%lld) must be multiples of 256", fn,
+                (long long)kg, (long long)mid_w);
+  if (d_g % 16 != 0 || d_model % 16 != 0) return fail(LCA_ERR_UNSUPPORTED, "%s: d_g and d_model must be multiples of 16", fn);
+  if (kg > (1 << 30) || mid_w > (1 << 30) || d_model > (1 << 30) || g > 65535)
+    return fail(LCA_ERR_UNSUPPORTED, "%s: dimensions too large", fn);
+  if ((static_cast<int64_t>(T) + 15) / 16 > 65535LL * 4) return fail(LCA_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  if (!o || !w_g || !w_o || !mid || !out) return fail(LCA_ERR_ARG, "%s: o, w_g, w_o, mid and out are required", fn);
+  if (!aligned16(o) || !aligned16(w_g) || !aligned16(w_o) || !aligned16(mid) || !aligned16(out))
+    return fail(LCA_ERR_ALIGN, "%s: buffers must be 16-byte aligned", fn);
+  lca::OutProjArgs p{T, n_h, c, g, d_g, d_model, o, w_g, w_o, mid, out};
+  return hip_status(lca::launch_grouped_out_proj(static_cast<hipStream_t>(stream), p), fn);
+}
+
 int lca_quantize_rows(void* stream, int dt_out, int64_t n_rows, int D, int rope_dims,
                       const float* src, void* out, void* out_scale) {
   if (n_rows < 0 || D < 32 || D > 1024 || D % 32 != 0)

@@ -121,4 +121,11 @@ __device__ __forceinline__ int64_t seq_pos(const int64_t* q_pos, int64_t bound, 
 }
 hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t ws_bytes);
 
+struct OutProjArgs {
+  int T, n_h, c, g, d_g, d_model;
+  const void *o, *w_g, *w_o;
+  void *mid, *out;
+};
+hipError_t launch_grouped_out_proj(hipStream_t s, const OutProjArgs& p);
+
 }  // namespace lca

@@ -625,7 +625,7 @@ def mxfp4_decode(codes, scales, block=32):
 # Grouped output projection (the step after core attention)
 # ---------------------------------------------------------------------------
 
-def grouped_output_projection(o, w_g, w_o, round_mid=True):
+def grouped_output_projection(o, w_g, w_o, round_mid=True, return_mid=False):
     """Grouped output projection of the attention output.
 
     [Qiaomu] 预训练策略 (model configurations) and [cdjax] §1.1: the n_h heads
@@ -642,7 +642,8 @@ def grouped_output_projection(o, w_g, w_o, round_mid=True):
       w_o: [d_model, g*d_g] the merging projection.
       round_mid: round the intermediate to bf16 (reading: it is stored in bf16
            between the two products, as the operand of the second one).
-    Returns: [T, d_model] float64.
+      return_mid: also return the intermediate [T, g*d_g] (before rounding).
+    Returns: [T, d_model] float64 (and the intermediate with return_mid).
 
     Pinned by: g = 1 is the plain two-matrix product; the grouped form equals
     the product with the explicit block-diagonal matrix; permuting heads inside
@@ -660,7 +661,6 @@ def grouped_output_projection(o, w_g, w_o, round_mid=True):
         xg = o[:, gi * (n_h // g):(gi + 1) * (n_h // g), :].reshape(T, kg)
         mids.append(xg @ w_g[gi].T)
     mid = np.concatenate(mids, axis=1)
-    if round_mid:
-        mid = bf16_round(mid)
-    return mid @ w_o.T
+    out = (bf16_round(mid) if round_mid else mid) @ w_o.T
+    return (out, mid) if return_mid else out
 

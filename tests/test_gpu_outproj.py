@@ -1,0 +1,74 @@
+"""Grouped output projection on the GPU against the oracle: ragged row counts
+around the 16-row MFMA tiles, the Flash and Pro shapes in full, and rows that
+keep their bits whatever the row count of the call."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+from gpu_util import DEV, dev_bf16, host, need_gpu, row_tol_check, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(rng, T, n_h, c, g, d_g, d_model):
+    o = WL.bf16_exact(rng.standard_normal((T, n_h, c)).astype(np.float32))
+    kg = (n_h // g) * c
+    w_g = WL.bf16_exact((rng.standard_normal((g, d_g, kg)) / np.sqrt(kg)).astype(np.float32))
+    w_o = WL.bf16_exact((rng.standard_normal((d_model, g * d_g)) / np.sqrt(g * d_g)).astype(np.float32))
+    return o, w_g, w_o
+
+
+def _check(L, o, w_g, w_o, what):
+    T, n_h, c = o.shape
+    g, d_g, _ = w_g.shape
+    d_model = w_o.shape[0]
+    out = torch.empty((T, d_model), dtype=torch.bfloat16, device=DEV)
+    mid = L.lca_grouped_out_proj(dev_bf16(o), dev_bf16(w_g), dev_bf16(w_o), out)
+    torch.cuda.synchronize()
+    ref, mid_ref = O.grouped_output_projection(o, w_g, w_o, round_mid=True, return_mid=True)
+    # stage 1 against the exact intermediate: bf16 rounding of fp32 sums
+    err = np.abs(host(mid) - mid_ref)
+    assert np.all(err <= 2 ** -8 * np.abs(mid_ref) + 1e-3 * np.max(np.abs(mid_ref))), f"{what}: intermediate"
+    # stage 2 against the oracle, which rounds its own intermediate to bf16
+    row_tol_check(host(out), ref, 1e-2, what)
+    return mid, out
+
+
+@pytest.mark.parametrize("T", [1, 7, 16, 33, 64, 100, 257])
+def test_grouped_out_proj_ragged_rows(T):
+    L = need_gpu()
+    rng = np.random.default_rng(200 + T)
+    o, w_g, w_o = _case(rng, T, 16, 64, 4, 128, 96)
+    say(f"grouped out proj T={T}")
+    _check(L, o, w_g, w_o, f"T={T}")
+
+
+@pytest.mark.parametrize("shape", ["flash", "pro"])
+def test_grouped_out_proj_model_shapes(shape):
+    # Flash: 64 heads x 512 in 8 groups of 1024, width 4096 (decode batch 16);
+    # Pro: 128 heads in 16 groups, width 7168 (batch 4)
+    L = need_gpu()
+    T, n_h, g, d_model = (16, 64, 8, 4096) if shape == "flash" else (4, 128, 16, 7168)
+    rng = np.random.default_rng(210 + g)
+    o, w_g, w_o = _case(rng, T, n_h, 512, g, 1024, d_model)
+    say(f"grouped out proj {shape}: T={T} n_h={n_h} g={g} d_model={d_model}")
+    _check(L, o, w_g, w_o, shape)
+
+
+def test_grouped_out_proj_rows_keep_their_bits():
+    # a row's result does not depend on how many rows the call holds
+    L = need_gpu()
+    rng = np.random.default_rng(220)
+    o, w_g, w_o = _case(rng, 70, 16, 128, 2, 128, 128)
+    od, wgd, wod = dev_bf16(o), dev_bf16(w_g), dev_bf16(w_o)
+    full = torch.empty((70, 128), dtype=torch.bfloat16, device=DEV)
+    L.lca_grouped_out_proj(od, wgd, wod, full)
+    say("grouped out proj rows vs row counts")
+    for lo, hi in ((0, 1), (5, 21), (17, 49), (3, 70)):
+        part = torch.empty((hi - lo, 128), dtype=torch.bfloat16, device=DEV)
+        L.lca_grouped_out_proj(od[lo:hi].contiguous(), wgd, wod, part)
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[lo:hi]), f"rows {lo}:{hi}"
