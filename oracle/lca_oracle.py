@@ -48,6 +48,9 @@ __all__ = [
     "mxfp4_quantize",
     "mxfp4_decode",
     "grouped_output_projection",
+    "attend_backward_query",
+    "csa_attend_backward",
+    "hca_attend_backward",
     "E4M3_MAX",
     "E2M1_GRID",
 ]
@@ -441,6 +444,96 @@ def hca_attend(q, E, m, win, sink, scale, q_pos0, W=128, inv_rope=False,
                                           scale, p, q_pos0, W, inv_rope,
                                           rope_base, rope_dims)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Backward of the core attention (training)
+# ---------------------------------------------------------------------------
+
+def attend_backward_query(q, X, sink, scale, p, dout, inv_rope=False, rope_base=10000.0, rope_dims=0):
+    """Gradients of one query's attention (all heads) over rows X, given the
+    gradient ``dout`` of its output.
+
+    The forward is ``sink_attention`` per head, then (with inv_rope) the
+    output turned by -p ([cdjax] §1.1). With K = V = X shared by the heads
+    (MQA), each row's gradient sums a value part and a key part over heads.
+    For head h, P_j = softmax weight of row j, P_s = the sink's weight:
+      do = dout turned back by +p (the adjoint of the turn by -p),
+      D = do . o,  dl_j = P_j (do . x_j - D),
+      dq = scale sum_j dl_j x_j,  dx_j = sum_h (P_j do + scale dl_j q),
+      dsink = -P_s D   (the sink has a logit and no value).
+    [kwkr] §4.3 and [Qiaomu] 批不变 kernel: the backward is deterministic; here
+    it is the plain chain rule of the forward.
+
+    Args: q [H, D], X [n, D], sink [H], dout [H, D].
+    Returns (dq [H, D], dX [n, D], dsink [H]) in float64.
+    Pinned by: central finite differences of sum(dout * out) on tiny inputs,
+    float64 torch autograd through an independent forward, and closed forms
+    (tests/test_oracle_backward.py).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    H, D = q.shape
+    dq = np.zeros((H, D))
+    dX = np.zeros_like(X)
+    dsink = np.zeros(H)
+    for h in range(H):
+        o, lse, wts = sink_attention(q[h], X, sink[h], scale)
+        do = rope_rotate(dout[h], p, rope_base, rope_dims) if (inv_rope and rope_dims) else dout[h]
+        Dv = float(do @ o)
+        if X.shape[0]:
+            dl = wts * (X @ do - Dv)
+            dq[h] = scale * (dl @ X)
+            dX += np.outer(wts, do) + scale * np.outer(dl, q[h])
+        dsink[h] = -math.exp(float(sink[h]) - lse) * Dv
+    return dq, dX, dsink
+
+
+def _backward_rows(E, sel, win, W, p, q_pos0):
+    """Sources of a query's rows: (kind, index) per row, entries then window."""
+    src = [("e", int(s)) for s in np.asarray(sel).tolist() if s >= 0]
+    src += [("w", int(pp - (q_pos0 - (W - 1)))) for pp in window_positions(p, W)]
+    return src
+
+
+def _attend_backward(q, E, sels, win, sink, scale, q_pos0, W, inv_rope, rope_base, rope_dims, dout):
+    Tq, H, D = q.shape
+    E = np.asarray(E, dtype=np.float64)
+    win = np.asarray(win, dtype=np.float64)
+    dq = np.zeros((Tq, H, D))
+    dE = np.zeros_like(E)
+    dwin = np.zeros_like(win)
+    dsink = np.zeros(H)
+    for t in range(Tq):
+        p = q_pos0 + t
+        src = _backward_rows(E, sels[t], win, W, p, q_pos0)
+        X = np.array([E[i] if k == "e" else win[i] for k, i in src]).reshape(len(src), D)
+        dq[t], dX, ds = attend_backward_query(q[t], X, sink, scale, p, dout[t], inv_rope, rope_base, rope_dims)
+        dsink += ds
+        for (k, i), g in zip(src, dX):
+            if k == "e":
+                dE[i] += g
+            else:
+                dwin[i] += g
+    return dq, dE, dwin, dsink
+
+
+def csa_attend_backward(q, E, idx, win, sink, scale, q_pos0, dout, W=128, inv_rope=False,
+                        rope_base=10000.0, rope_dims=0):
+    """Backward of ``csa_attend`` for one sequence: q [Tq, H, D], E [N, D],
+    idx [Tq, k] (-1 absent), win [W-1+Tq, D], dout [Tq, H, D].
+    Returns (dq, dE, dwin, dsink); entries and window rows collect the
+    gradients of every query that read them."""
+    return _attend_backward(q, E, list(idx), win, sink, scale, q_pos0, W, inv_rope, rope_base, rope_dims, dout)
+
+
+def hca_attend_backward(q, E, m, win, sink, scale, q_pos0, dout, W=128, inv_rope=False,
+                        rope_base=10000.0, rope_dims=0):
+    """Backward of ``hca_attend``: every query reads all its visible entries."""
+    Tq = q.shape[0]
+    sels = [np.arange(n_visible(q_pos0 + t, m)) for t in range(Tq)]
+    return _attend_backward(q, E, sels, win, sink, scale, q_pos0, W, inv_rope, rope_base, rope_dims, dout)
 
 
 # ---------------------------------------------------------------------------
