@@ -15,7 +15,7 @@ as ragged batches (each sequence at its own position, the context as bound).
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Counter runs: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) over
-``bench.py --no-secondary --no-prefill --no-mixed --no-ragged --no-placement --no-outproj --copy-calibration 1024``,
+``bench.py --no-secondary --no-prefill --no-mixed --no-ragged --no-placement --no-outproj --no-backward --copy-calibration 1024``,
 then ``bench.py --pmc-summary F.csv W.csv --copy-calibration 1024``.
 """
 
@@ -446,6 +446,47 @@ def outproj_leg(steps=50, warmup=5):
     return res
 
 
+def backward_leg(T=4096, H=64, D=512, k=512, W=128, m=4, H_I=4, d_I=128, reps=5):
+    """Training-shaped CSA attention backward: one sequence of T = 4096 tokens
+    from the start (causal: query t reads the top-k of its (t + 1) // 4
+    visible entries, made by the library's own indexer from random indexer
+    inputs, plus its window), Flash shape (64 heads x 512, k = 512). The
+    forward runs first (untimed) to give out and lse; the timed call is
+    csa_attend_backward (dq, entry and window gradients, dsink)."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(51)
+    N = T // m
+    q = torch.randn(1, T, H, D, generator=g, device=DEV, dtype=torch.bfloat16) * (4 * D ** -0.5)
+    E = torch.randn(1, N, D, generator=g, device=DEV, dtype=torch.bfloat16) * (D ** -0.5)
+    win = torch.randn(1, W - 1 + T, D, generator=g, device=DEV, dtype=torch.bfloat16) * (D ** -0.5)
+    sink = torch.randn(H, generator=g, device=DEV)
+    qI = torch.randn(1, T, H_I, d_I, generator=g, device=DEV, dtype=torch.bfloat16) * (d_I ** -0.5)
+    kI = torch.randn(1, N, d_I, generator=g, device=DEV, dtype=torch.bfloat16) * (d_I ** -0.5)
+    w = torch.randn(1, T, H_I, generator=g, device=DEV) * (H_I ** -0.5)
+    idx = torch.empty((1, T, k), dtype=torch.int32, device=DEV)
+    L.csa_index_topk(L.BF16, qI, w, kI, idx, m=m, k=k, q_pos0=0)
+    out = torch.empty((1, T, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((1, T, H), dtype=torch.float32, device=DEV)
+    kw = dict(m=m, W=W, q_pos0=0, scale=1 / math.sqrt(D), flags=L.INV_ROPE, rope_dims=64)
+    L.csa_attend(L.BF16, L.BF16, q, E, idx, win, sink, out, lse_out=lse, **kw)
+    dout = torch.randn(1, T, H, D, generator=g, device=DEV, dtype=torch.bfloat16)
+    need = int(L.lib().csa_attend_backward_workspace(L.BF16, L.BF16, 1, T, H, D, N, m, k, W, 0))
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+
+    def step(i):
+        L.attend_backward("csa", q, E, win, sink, out, lse, dout, idx=idx, ws=ws, **kw)
+    ms = 1e3 * timed(step, reps, 1) / reps
+    kt = kernel_times(step, reps)
+    # rows read: each query's selected entries (k, fewer early on) and its window
+    rows = sum(min(k, (t + 1) // m) + min(W, t + 1) for t in range(T))
+    flops = 2.0 * rows * H * D * 5                  # S, dP, dq (query side) + two head sums (row side)
+    progress(f"csa attend backward T={T}: {ms:.3f} ms")
+    return {"workload": "csa_attend_backward_t4096_flash", "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+            "kernels_us": {k_: round(v["avg_us"], 1) for k_, v in kt.items()}, "rows_read": rows, "flops": flops,
+            "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_bf16_frac": flops / (ms * 1e-3) / 2.5e15,
+            "workspace_bytes": need}
+
+
 def ragged_bytes(d, pos):
     """Algorithmic bytes of a ragged decode step: each sequence moves what its
     own position makes visible (indexer keys and, for HCA, entries)."""
@@ -607,6 +648,7 @@ def main():
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-placement", action="store_true")
     ap.add_argument("--no-outproj", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -668,6 +710,8 @@ def main():
         result["placement"] = placement_leg()
     if not args.no_outproj:
         result["grouped_out_proj"] = outproj_leg()
+    if not args.no_backward:
+        result["backward"] = backward_leg()
     if not args.no_ragged:
         result["ragged"] = {"csa_decode_b16_ctx_le131072": ragged_leg(d, args.copies, args.steps, args.warmup,
                                                                       12, ms)}

@@ -348,6 +348,48 @@ int hca_attend_ragged(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, i
                       void* out, float* lse_out, void* ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------
+ * csa_attend_backward / hca_attend_backward — gradients of the core attention.
+ *
+ * [Qiaomu] 批不变 kernel, [kwkr] §4.3: the attention backward accumulates per
+ * SM into buffers of its own and sums them in a fixed order (deterministic).
+ * Given the forward call's arguments, its output and lse, and dout (the
+ * gradient of out), per query and head (P = softmax weights from lse, do =
+ * dout turned back by +p when LCA_INV_ROPE was set, D = dout . out):
+ *   dl_j = P_j (do . x_j - D),  dq = scale sum_j dl_j x_j,
+ *   dx_j = sum_h (P_hj do_h + scale dl_hj q_h) into the entry or window row j
+ *   was read from,  dsink_h = -sum over queries of P_sink D.
+ * Every query is assigned to one of a fixed set of slots (ranges of 16 or
+ * more consecutive queries); a slot walks its queries in order and adds the
+ * rows' gradients into its own buffer; the buffers are then summed in slot
+ * order. The result depends only on the arguments (run to run identical).
+ *   q, kv, idx, win, sink, scale, flags, rope_*: as in the forward call
+ *   out  [B, Tq, H, D] bf16, lse [B, Tq, H] fp32: the forward's results
+ *   dout [B, Tq, H, D] bf16
+ *   dq   [B, Tq, H, D] fp32;  dkv [B, N_cap, D] fp32 (rows no query read: 0);
+ *   dwin [B, W-1+Tq, D] fp32 (rows at negative positions: 0);  dsink [H] fp32
+ * Requirements: bf16 q and rows, D = 512, H = 64 or 128, Tq <= 65535,
+ * window in the linear layout (no LCA_WIN_RING), one position for the batch;
+ * a query's entry indices distinct (as csa_index_topk gives them). Workspace
+ * from *_backward_workspace (it holds per-slot buffers of N_cap x D fp32).
+ * ------------------------------------------------------------------------- */
+size_t csa_attend_backward_workspace(int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+                                     int m, int k, int W, int64_t q_pos0);
+size_t hca_attend_backward_workspace(int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+                                     int m, int W, int64_t q_pos0);
+int csa_attend_backward(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+                        int m, int k, int W, int64_t q_pos0, const void* q, const void* kv,
+                        const int32_t* idx, const void* win, const float* sink, float scale,
+                        uint32_t flags, float rope_base, int rope_dims, const void* out,
+                        const float* lse, const void* dout, float* dq, float* dkv, float* dwin,
+                        float* dsink, void* ws, size_t ws_bytes);
+int hca_attend_backward(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+                        int m, int W, int64_t q_pos0, const void* q, const void* kv,
+                        const void* win, const float* sink, float scale, uint32_t flags,
+                        float rope_base, int rope_dims, const void* out, const float* lse,
+                        const void* dout, float* dq, float* dkv, float* dwin, float* dsink,
+                        void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------
  * lca_grouped_out_proj — grouped output projection after core attention.
  *
  * [Qiaomu] 预训练策略 (model configurations), [cdjax] §1.1, [kwkr] §3.4: the

@@ -100,6 +100,16 @@ def _declare(L):
     L.lca_decode_append.restype = i32
     L.lca_grouped_out_proj.argtypes = [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     L.lca_grouped_out_proj.restype = i32
+    L.csa_attend_backward_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, i64]
+    L.csa_attend_backward_workspace.restype = sz
+    L.hca_attend_backward_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, i32, i64]
+    L.hca_attend_backward_workspace.restype = sz
+    L.csa_attend_backward.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, i64, vp, vp, vp, vp,
+                                      vp, f32, u32, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz]
+    L.csa_attend_backward.restype = i32
+    L.hca_attend_backward.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i64, vp, vp, vp, vp,
+                                      f32, u32, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz]
+    L.hca_attend_backward.restype = i32
     L.lca_status_str.argtypes = [i32]
     L.lca_status_str.restype = ctypes.c_char_p
     L.lca_last_error.argtypes = []
@@ -304,6 +314,38 @@ def hca_attend(dt_q, dt_kv, q, kv, win, sink, out, *, m, W, q_pos0, scale, N_cap
                             _p(kv), _p(kv_scale), _p(win), _p(win_scale), _p(sink), scale, flags,
                             rope_base, rope_dims, _p(out), _p(lse_out), _p(ws),
                             ws.numel() * ws.element_size()))
+
+
+def attend_backward(kind, q, kv, win, sink, out, lse, dout, *, m, W, q_pos0, scale, idx=None, N_cap=None,
+                    flags=0, rope_base=10000.0, rope_dims=0, ws=None, stream=None):
+    """Gradients of csa_attend (kind "csa", idx given) or hca_attend: returns
+    (dq [B,Tq,H,D], dkv [B,N_cap,D], dwin [B,W-1+Tq,D], dsink [H]), all fp32;
+    see csa_attend_backward in include/lca.h."""
+    B, Tq, H, D = q.shape
+    N_cap = kv.shape[1] if N_cap is None else N_cap
+    dev = q.device
+    dq = torch.empty((B, Tq, H, D), dtype=torch.float32, device=dev)
+    dkv = torch.empty((B, N_cap, D), dtype=torch.float32, device=dev)
+    dwin = torch.empty((B, W - 1 + Tq, D), dtype=torch.float32, device=dev)
+    dsink = torch.empty((H,), dtype=torch.float32, device=dev)
+    if kind == "csa":
+        k = idx.shape[2]
+        need = int(lib().csa_attend_backward_workspace(BF16, BF16, B, Tq, H, D, N_cap, m, k, W, q_pos0))
+        if ws is None:
+            ws = _workspace(need, q)
+        _check(lib().csa_attend_backward(_stream(stream), BF16, BF16, B, Tq, H, D, N_cap, m, k, W, q_pos0, _p(q),
+                                         _p(kv), _p(idx), _p(win), _p(sink), scale, flags, rope_base, rope_dims,
+                                         _p(out), _p(lse), _p(dout), _p(dq), _p(dkv), _p(dwin), _p(dsink), _p(ws),
+                                         ws.numel() * ws.element_size()))
+    else:
+        need = int(lib().hca_attend_backward_workspace(BF16, BF16, B, Tq, H, D, N_cap, m, W, q_pos0))
+        if ws is None:
+            ws = _workspace(need, q)
+        _check(lib().hca_attend_backward(_stream(stream), BF16, BF16, B, Tq, H, D, N_cap, m, W, q_pos0, _p(q),
+                                         _p(kv), _p(win), _p(sink), scale, flags, rope_base, rope_dims, _p(out),
+                                         _p(lse), _p(dout), _p(dq), _p(dkv), _p(dwin), _p(dsink), _p(ws),
+                                         ws.numel() * ws.element_size()))
+    return dq, dkv, dwin, dsink
 
 
 def lca_grouped_out_proj(o, w_g, w_o, out, *, mid=None, stream=None):

@@ -2043,4 +2043,430 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
   }
 }
 
+// ===========================================================================
+// Backward of the core attention (training).
+//
+// [Qiaomu] 批不变 kernel and [kwkr] §4.3: the attention backward gives each
+// SM its own accumulation buffer and sums the buffers in a fixed order, so
+// the gradients are deterministic. Here, per query and head (P = softmax
+// weights recomputed from the forward lse, do = the output gradient turned
+// back by +p, D = do . o = dout . out):
+//   dl_j = P_j (do . x_j - D),  dq = scale sum_j dl_j x_j,
+//   dx_j = sum_h (P_hj do_h + scale dl_hj q_h),  dsink_h = -P_sink D.
+// Four kernels:
+//   bwd_prep_kernel   D, the turned gradient (row and [D, H] layouts), q in
+//                     [D, H] layout, the sink's parts;
+//   bwd_query_kernel  per (query, 64 heads): S and dP by MFMA from one set of
+//                     row fragments, P and dl stored (bf16, [row][head]), dq;
+//   bwd_kv_kernel     per slot (a fixed range of consecutive queries, walked
+//                     in order): each row's gradient (an MFMA over the heads)
+//                     added into the slot's own buffer (zeroed first);
+//   bwd_reduce_kernel every entry and window row summed over the slots in
+//                     slot order; dsink summed over the queries in order.
+// ===========================================================================
+namespace {
+
+constexpr int kBwdSlotQueries = 16;                // queries per accumulation slot (at least)
+
+struct BwdPlan {
+  int64_t nr;                                      // row slots per query in the P / dl arrays
+  int Ps, C;                                       // slots per sequence, queries per slot
+  int wrows;                                       // window rows a slot can touch: C + W - 1
+  size_t off_dor, off_dT, off_qT, off_Dv, off_dsp, off_P, off_dL, off_sE, off_sW, total;
+};
+
+BwdPlan make_bwd_plan(const AttendArgs& a) {
+  BwdPlan bp{};
+  const int64_t pl = a.q_pos0 + a.Tq - 1;          // the last query's position (the most rows)
+  int64_t n_ent = a.k;
+  if (!a.sparse) {
+    n_ent = n_visible(pl, a.m);
+    if (n_ent > a.N_cap) n_ent = a.N_cap;
+  }
+  const int64_t win = pl + 1 < a.W ? pl + 1 : a.W;
+  bp.nr = (n_ent + win + kTileRows - 1) / kTileRows * kTileRows;
+  // slots: one per 16 queries, at most 256 per sequence, and slot buffers within ~4 GB
+  int64_t ps = (a.Tq + kBwdSlotQueries - 1) / kBwdSlotQueries;
+  const double slot_bytes = static_cast<double>(a.N_cap) * a.D * 4.0 * a.B;
+  int64_t cap = static_cast<int64_t>(4.0e9 / (slot_bytes > 1.0 ? slot_bytes : 1.0));
+  if (cap < 1) cap = 1;
+  if (ps > cap) ps = cap;
+  if (ps > 256) ps = 256;
+  bp.C = static_cast<int>((a.Tq + ps - 1) / ps);
+  bp.Ps = (a.Tq + bp.C - 1) / bp.C;
+  bp.wrows = bp.C + a.W - 1;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = o;
+    o += (bytes + 255) / 256 * 256;
+    return r;
+  };
+  const size_t BT = static_cast<size_t>(a.B) * a.Tq;
+  bp.off_dor = take(BT * a.H * a.D * 2);
+  bp.off_dT = take(BT * a.H * a.D * 2);
+  bp.off_qT = take(BT * a.H * a.D * 2);
+  bp.off_Dv = take(BT * a.H * 4);
+  bp.off_dsp = take(BT * a.H * 4);
+  bp.off_P = take(BT * bp.nr * a.H * 2);
+  bp.off_dL = take(BT * bp.nr * a.H * 2);
+  bp.off_sE = take(static_cast<size_t>(a.B) * bp.Ps * a.N_cap * a.D * 4);
+  bp.off_sW = take(static_cast<size_t>(a.B) * bp.Ps * bp.wrows * a.D * 4);
+  bp.total = o;
+  return bp;
+}
+
+// One workgroup per (query, sequence): D and the sink's part per head, the
+// output gradient turned back by +p (the adjoint of the forward's turn by
+// -p), and [D, H] copies of it and of q (the operands of the head sums).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
+  const AttendArgs& a = p.a;
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int D = a.D, H = a.H;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t row0 = (static_cast<int64_t>(b) * a.Tq + t) * H;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* out = static_cast<const uint16_t*>(p.out);
+  const uint16_t* dout = static_cast<const uint16_t*>(p.dout);
+  uint16_t* dor = reinterpret_cast<uint16_t*>(ws + bp.off_dor);
+  uint16_t* dT = reinterpret_cast<uint16_t*>(ws + bp.off_dT);
+  uint16_t* qT = reinterpret_cast<uint16_t*>(ws + bp.off_qT);
+  float* Dv = reinterpret_cast<float*>(ws + bp.off_Dv);
+  float* dsp = reinterpret_cast<float*>(ws + bp.off_dsp);
+  const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
+  __shared__ float2 rt[256];                       // (cos, sin) of pair i at +p
+  __shared__ uint16_t slab[2][128 * 64];           // 64 channels of every head (H <= 128)
+  const int64_t pos = seq_pos(a.q_pos, a.q_pos0, b) + t;
+  for (int i = threadIdx.x; i < R / 2; i += 256) {
+    float sn, cs;
+    rope_sincos(static_cast<double>(pos), i, R, static_cast<double>(a.rope_base), &sn, &cs);
+    rt[i] = make_float2(cs, sn);
+  }
+  __syncthreads();
+  auto turned = [&](int64_t r, int c) -> float {   // channel c of the turned gradient of row r
+    const float x = bf16_to_f32(dout[r * D + (c & ~1)]), y = bf16_to_f32(dout[r * D + (c | 1)]);
+    if (c < D - R) return (c & 1) ? y : x;
+    const float2 cs = rt[(c - (D - R)) >> 1];
+    return (c & 1) ? fmaf(x, cs.y, y * cs.x) : fmaf(x, cs.x, -(y * cs.y));
+  };
+  for (int h = wid; h < H; h += 4) {
+    const int64_t r = row0 + h;
+    float acc = 0.f;
+    for (int c = lane; c < D; c += 64) {
+      acc = fmaf(bf16_to_f32(dout[r * D + c]), bf16_to_f32(out[r * D + c]), acc);
+      dor[r * D + c] = f32_to_bf16(turned(r, c));
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      Dv[r] = acc;
+      dsp[r] = -expf(a.sink[h] - p.lse[r]) * acc;
+    }
+  }
+  for (int c0 = 0; c0 < D; c0 += 64) {
+    for (int e = threadIdx.x; e < H * 64; e += 256) {
+      const int h = e >> 6, c = e & 63;
+      slab[0][e] = q[(row0 + h) * D + c0 + c];
+      slab[1][e] = f32_to_bf16(turned(row0 + h, c0 + c));
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < H * 64; e += 256) {
+      const int c = e / H, h = e % H;
+      const int64_t o = ((static_cast<int64_t>(b) * a.Tq + t) * D + c0 + c) * H + h;
+      qT[o] = slab[0][h * 64 + c];
+      dT[o] = slab[1][h * 64 + c];
+    }
+    __syncthreads();
+  }
+}
+
+// One workgroup per (64-head group, query, sequence), 16 heads per wave, rows
+// in 32-row tiles (swizzled LDS, two-tile ring). S^T and dP^T share the row
+// fragments; P = exp(l - lse) (the forward's lse), dl = P (dP - D); P and dl
+// go to memory as bf16 ([row][head] per query); dq^T += X^T dl^T.
+__global__ __launch_bounds__(kAttThreads) void bwd_query_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
+  constexpr int D = 512, KS = D / 32, DT = D / 16, RPW = kTileRows / 4;
+  const AttendArgs& a = p.a;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kTileRows * D];
+  __shared__ int32_t rows[kMaxSplitRows];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int hg = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const int head = hg * 64 + wid * 16 + r16;
+  const int64_t qrow = (static_cast<int64_t>(b) * a.Tq + t) * a.H + head;
+  const RowSpan rs = row_span(a, b, t);
+  const int64_t win_rows = a.W - 1 + a.Tq;
+  const uint16_t* kvp = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(b) * a.N_cap * D;
+  const uint16_t* winp = static_cast<const uint16_t*>(a.win) + static_cast<int64_t>(b) * win_rows * D;
+  const SwzOffsets so = swz_offsets(g, r16);
+  const float lse = p.lse[qrow];
+  const float Dv = reinterpret_cast<const float*>(ws + bp.off_Dv)[qrow];
+  const int64_t pl0 = (static_cast<int64_t>(b) * a.Tq + t) * bp.nr * a.H;
+  uint16_t* Pw = reinterpret_cast<uint16_t*>(ws + bp.off_P) + pl0;
+  uint16_t* Lw = reinterpret_cast<uint16_t*>(ws + bp.off_dL) + pl0;
+  bf16x8 qf[KS], df[KS];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + qrow * D;
+    const uint16_t* dp = reinterpret_cast<const uint16_t*>(ws + bp.off_dor) + qrow * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
+      df[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dp + 32 * s + 8 * g));
+    }
+  }
+  f32x4 acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t c0 = 0; c0 < rs.nrows; c0 += kMaxSplitRows) {
+    const int nr = static_cast<int>(rs.nrows - c0 < kMaxSplitRows ? rs.nrows - c0 : kMaxSplitRows);
+    __syncthreads();                               // the last chunk's reads of rows[] and the ring are done
+    int32_t myrows[kMaxSplitRows / kAttThreads];
+#pragma unroll
+    for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) {
+      const int v = tid + kAttThreads * q;
+      myrows[q] = v < nr ? encode_row(a, b, t, rs, c0 + v) : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) rows[tid + kAttThreads * q] = myrows[q];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    auto issue = [&](int tile, uint16_t* dst) {
+      const int v0 = tile * kTileRows + wid * RPW;
+      uint64_t my = 0;
+      if (lane < RPW) {
+        const int v = v0 + lane;
+        const int32_t sr = v < nr ? rows[v] : -1;
+        const uint16_t* rowp = sr >= 0 ? kvp + static_cast<int64_t>(sr) * D
+                                       : winp + (sr == -1 ? 0 : static_cast<int64_t>(-2 - sr) * D);
+        my = reinterpret_cast<uint64_t>(rowp);
+      }
+      const uint32_t lds0 = lds_address(dst + wid * RPW * D);
+      const uint32_t lo = static_cast<uint32_t>(my), hi = static_cast<uint32_t>(my >> 32);
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const uint64_t rb = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), rr))) << 32) |
+                            static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), rr));
+        const uint32_t src_off = 16u * static_cast<uint32_t>((lane & 48) | ((lane & 15) ^ slot_swizzle(wid * RPW + rr)));
+        lds_copy16(reinterpret_cast<const void*>(rb + src_off), lds0 + rr * D * 2);
+      }
+    };
+    const int ntiles = (nr + kTileRows - 1) / kTileRows;
+    issue(0, Xs[0]);
+    for (int it = 0; it < ntiles; ++it) {
+      if (it + 1 < ntiles) {
+        issue(it + 1, Xs[(it + 1) & 1]);
+        wait_vmcnt<RPW>();                         // tile it landed; tile it + 1 may stay in flight
+      } else {
+        wait_vmcnt<0>();
+      }
+      if (it == 0) __builtin_amdgcn_s_waitcnt(0);   // query and gradient fragments too
+      __builtin_amdgcn_s_barrier();
+      const uint16_t* X = Xs[it & 1];
+      f32x4 sacc[2], dacc[2];
+      int4 rv[2];
+      {
+        bf16x8 xf[32];
+        qk_load(X, so, rows, it * kTileRows, g, xf, rv);
+        qk_mfma(xf, qf, sacc);
+        qk_mfma(xf, df, dacc);
+      }
+      // lane (g, r16): head r16, rows 4g + i (i < 4) and 16 + 4g + (i - 4)
+      const int rr[8] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w, rv[1].x, rv[1].y, rv[1].z, rv[1].w};
+      float L[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float P = rr[i] != -1 ? expf(sacc[i >> 2][i & 3] * a.scale - lse) : 0.f;
+        L[i] = P * (dacc[i >> 2][i & 3] - Dv);
+        const int64_t v = c0 + it * kTileRows + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
+        Pw[v * a.H + head] = f32_to_bf16(P);
+        Lw[v * a.H + head] = f32_to_bf16(L[i]);
+      }
+      uint4 lw;
+      lw.x = pack_bf16x2(L[0], L[1]);
+      lw.y = pack_bf16x2(L[2], L[3]);
+      lw.z = pack_bf16x2(L[4], L[5]);
+      lw.w = pack_bf16x2(L[6], L[7]);
+      const bf16x8 lf = __builtin_bit_cast(bf16x8, lw);
+      {
+        bf16x8 vf[32];
+        pv_load(X, so, vf);
+        pv_mfma(vf, lf, acc);
+      }
+      __syncthreads();                             // every wave is done with this slot before its refill
+    }
+  }
+  float* dq = p.dq + qrow * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<float4*>(dq + 16 * dt + 4 * g) =
+        make_float4(acc[dt][0] * a.scale, acc[dt][1] * a.scale, acc[dt][2] * a.scale, acc[dt][3] * a.scale);
+}
+
+// The slot buffers start at zero (a fill kernel, so the work records into a
+// captured graph as plain kernels).
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float4* __restrict__ p, int64_t n4) {
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256) p[i] = z;
+}
+
+// One workgroup per (slot, sequence): queries [s C, s C + C) in order; wave w
+// owns channels [128 w, 128 w + 128). For each 32-row tile of a query, the
+// rows' gradients sum P^T dO + scale dl^T Q over the heads (MFMA, K = heads)
+// and are added into the slot's buffer row (entry or window row). A query's
+// rows are distinct, so its tiles never touch one row twice; consecutive
+// queries are ordered by a barrier (the workgroup's waves share one CU and
+// its cache, so plain loads and stores suffice).
+__global__ __launch_bounds__(256) void bwd_kv_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
+  constexpr int D = 512;
+  const AttendArgs& a = p.a;
+  const int s = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wid = threadIdx.x >> 6;
+  const int t0 = s * bp.C;
+  const int t1 = t0 + bp.C < a.Tq ? t0 + bp.C : a.Tq;
+  const int64_t slot = static_cast<int64_t>(b) * bp.Ps + s;
+  float* sE = reinterpret_cast<float*>(ws + bp.off_sE) + slot * a.N_cap * D;
+  float* sW = reinterpret_cast<float*>(ws + bp.off_sW) + slot * bp.wrows * D;
+  __shared__ int32_t src[kTileRows];
+  const int H = a.H, KSH = H / 32;
+  const int cb = 128 * wid;
+  const int kk = 8 * (lane >> 4);
+  for (int t = t0; t < t1; ++t) {
+    const RowSpan rs = row_span(a, b, t);
+    const int64_t bt = static_cast<int64_t>(b) * a.Tq + t;
+    const uint16_t* Pq = reinterpret_cast<const uint16_t*>(ws + bp.off_P) + bt * bp.nr * H;
+    const uint16_t* Lq = reinterpret_cast<const uint16_t*>(ws + bp.off_dL) + bt * bp.nr * H;
+    const uint16_t* dTq = reinterpret_cast<const uint16_t*>(ws + bp.off_dT) + bt * D * H;
+    const uint16_t* qTq = reinterpret_cast<const uint16_t*>(ws + bp.off_qT) + bt * D * H;
+    for (int64_t v0 = 0; v0 < rs.nrows; v0 += kTileRows) {
+      if (tid < kTileRows) src[tid] = v0 + tid < rs.nrows ? encode_row(a, b, t, rs, v0 + tid) : -1;
+      f32x4 c1[2][8], c2[2][8];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) c1[mt][nt] = c2[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KSH; ++ks) {
+        bf16x8 aP[2], aL[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int64_t row = v0 + 16 * mt + (lane & 15);
+          aP[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pq + row * H + 32 * ks + kk));
+          aL[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Lq + row * H + 32 * ks + kk));
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const int64_t col = cb + 16 * nt + (lane & 15);
+          const bf16x8 bD = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dTq + col * H + 32 * ks + kk));
+          const bf16x8 bQ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qTq + col * H + 32 * ks + kk));
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            c1[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aP[mt], bD, c1[mt][nt], 0, 0, 0);
+            c2[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aL[mt], bQ, c2[mt][nt], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();                             // src[] of this tile written
+      // lane l holds rows 16 mt + 4 (l / 16) + i, channel cb + 16 nt + l % 16
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t e = src[16 * mt + 4 * (lane >> 4) + i];
+          if (e == -1) continue;
+          float* dst = e >= 0 ? sE + static_cast<int64_t>(e) * D : sW + static_cast<int64_t>(-2 - e - t0) * D;
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            const int ch = cb + 16 * nt + (lane & 15);
+            dst[ch] += fmaf(a.scale, c2[mt][nt][i], c1[mt][nt][i]);
+          }
+        }
+      __syncthreads();                             // src[] consumed; the query's row updates done
+    }
+  }
+}
+
+// Sum over the slots in slot order: one workgroup per entry or window row of
+// a sequence, two channels per thread.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
+  constexpr int D = 512;
+  const AttendArgs& a = p.a;
+  const int64_t row = blockIdx.x;
+  const int b = blockIdx.y;
+  const int c = 2 * threadIdx.x;
+  const float* sE = reinterpret_cast<const float*>(ws + bp.off_sE);
+  const float* sW = reinterpret_cast<const float*>(ws + bp.off_sW);
+  float2 acc = make_float2(0.f, 0.f);
+  if (row < a.N_cap) {
+    for (int s = 0; s < bp.Ps; ++s) {
+      const int64_t slot = static_cast<int64_t>(b) * bp.Ps + s;
+      const float2 v = *reinterpret_cast<const float2*>(sE + (slot * a.N_cap + row) * D + c);
+      acc.x += v.x;
+      acc.y += v.y;
+    }
+    *reinterpret_cast<float2*>(p.dkv + (static_cast<int64_t>(b) * a.N_cap + row) * D + c) = acc;
+  } else {
+    const int r = static_cast<int>(row - a.N_cap);  // window row r: read by queries r - W + 1 .. r
+    const int tlo = r - (a.W - 1) > 0 ? r - (a.W - 1) : 0;
+    const int thi = r < a.Tq - 1 ? r : a.Tq - 1;
+    for (int s = tlo / bp.C; s <= thi / bp.C && tlo <= thi; ++s) {
+      const int loc = r - s * bp.C;
+      if (loc < 0 || loc >= bp.wrows) continue;
+      const int64_t slot = static_cast<int64_t>(b) * bp.Ps + s;
+      const float2 v = *reinterpret_cast<const float2*>(sW + (slot * bp.wrows + loc) * D + c);
+      acc.x += v.x;
+      acc.y += v.y;
+    }
+    *reinterpret_cast<float2*>(p.dwin + (static_cast<int64_t>(b) * (a.W - 1 + a.Tq) + r) * D + c) = acc;
+  }
+}
+
+// dsink[h] = the sink parts of every query, in (sequence, query) order.
+__global__ __launch_bounds__(256) void bwd_sink_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
+  const AttendArgs& a = p.a;
+  const float* dsp = reinterpret_cast<const float*>(ws + bp.off_dsp);
+  for (int h = threadIdx.x + blockIdx.x * blockDim.x; h < a.H; h += blockDim.x * gridDim.x) {
+    float acc = 0.f;
+    for (int64_t bt = 0; bt < static_cast<int64_t>(a.B) * a.Tq; ++bt) acc += dsp[bt * a.H + h];
+    p.dsink[h] = acc;
+  }
+}
+
+}  // namespace
+
+size_t attend_backward_workspace(const AttendArgs& a) { return make_bwd_plan(a).total + 256; }
+
+hipError_t launch_attend_backward(hipStream_t s, const AttendBwdArgs& p, void* ws, size_t) {
+  const AttendArgs& a = p.a;
+  const BwdPlan bp = make_bwd_plan(a);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  {
+    LaunchScope scope(s, "attend_bwd_prep");
+    scope.launch(bwd_prep_kernel, dim3(a.Tq, a.B), dim3(256), 0, p, bp, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    LaunchScope scope(s, "attend_bwd_query");
+    scope.launch(bwd_query_kernel, dim3(a.H / 64, a.Tq, a.B), dim3(kAttThreads), 0, p, bp, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    LaunchScope scope(s, "attend_bwd_kv");
+    // slot buffers (entries, then window rows: contiguous) start at zero
+    const int64_t n4 = static_cast<int64_t>(bp.off_sW - bp.off_sE) / 16 +
+                       static_cast<int64_t>(a.B) * bp.Ps * bp.wrows * a.D / 4;
+    scope.launch(bwd_zero_kernel, dim3(2048), dim3(256), 0, reinterpret_cast<float4*>(w + bp.off_sE), n4);
+    scope.launch(bwd_kv_kernel, dim3(bp.Ps, a.B), dim3(256), 0, p, bp, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    LaunchScope scope(s, "attend_bwd_reduce");
+    scope.launch(bwd_reduce_kernel, dim3(static_cast<uint32_t>(a.N_cap + a.W - 1 + a.Tq), a.B), dim3(256), 0, p, bp,
+                 w);
+    scope.launch(bwd_sink_kernel, dim3(1), dim3(256), 0, p, bp, w);
+    return hipGetLastError();
+  }
+}
+
 }  // namespace lca

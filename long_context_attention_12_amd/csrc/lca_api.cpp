@@ -473,6 +473,71 @@ int hca_attend(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, i
 }
 
 // ---------------------------------------------------------------------------
+// Backward of the core attention.
+static int run_attend_bwd(void* stream, lca::AttendArgs& a, const void* out, const float* lse, const void* dout,
+                          float* dq, float* dkv, float* dwin, float* dsink, void* ws, size_t ws_bytes,
+                          const char* fn) {
+  a.out = const_cast<void*>(out);                  // the forward's checks cover out
+  int st = check_attend(a, fn);
+  if (st != LCA_OK) return st;
+  if (a.dt_q != LCA_BF16 || a.dt_kv != LCA_BF16 || a.D != 512 || a.H % 64 != 0 || a.H > 128)
+    return fail(LCA_ERR_UNSUPPORTED, "%s: the backward takes bf16 q and rows, D = 512, H = 64 or 128", fn);
+  if (a.flags & ~LCA_INV_ROPE) return fail(LCA_ERR_ARG, "%s: only LCA_INV_ROPE applies", fn);
+  if (a.Tq > 65535) return fail(LCA_ERR_UNSUPPORTED, "%s: Tq must be <= 65535", fn);
+  if (!lse || !dout || !dq || !dkv || !dwin || !dsink)
+    return fail(LCA_ERR_ARG, "%s: lse, dout, dq, dkv, dwin and dsink are required", fn);
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dkv) || !aligned16(dwin) || !aligned4(lse) || !aligned4(dsink))
+    return fail(LCA_ERR_ALIGN, "%s: misaligned buffer", fn);
+  const size_t need = lca::attend_backward_workspace(a);
+  if (!ws || ws_bytes < need) return fail(LCA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  if (!aligned16(ws)) return fail(LCA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  lca::AttendBwdArgs p{a, out, lse, dout, dq, dkv, dwin, dsink};
+  return hip_status(lca::launch_attend_backward(static_cast<hipStream_t>(stream), p, ws, ws_bytes), fn);
+}
+
+size_t csa_attend_backward_workspace(int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int k,
+                                     int W, int64_t q_pos0) {
+  if (B < 1 || Tq < 1 || H < 1 || D < 1 || m < 1 || W < 1 || N_cap < 0) return 0;
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = k; a.W = W;
+  a.sparse = true; a.N_cap = N_cap; a.q_pos0 = q_pos0;
+  return lca::attend_backward_workspace(a);
+}
+
+size_t hca_attend_backward_workspace(int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int W,
+                                     int64_t q_pos0) {
+  if (B < 1 || Tq < 1 || H < 1 || D < 1 || m < 1 || W < 1 || N_cap < 0) return 0;
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = 0; a.W = W;
+  a.sparse = false; a.N_cap = N_cap; a.q_pos0 = q_pos0;
+  return lca::attend_backward_workspace(a);
+}
+
+int csa_attend_backward(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int k,
+                        int W, int64_t q_pos0, const void* q, const void* kv, const int32_t* idx, const void* win,
+                        const float* sink, float scale, uint32_t flags, float rope_base, int rope_dims,
+                        const void* out, const float* lse, const void* dout, float* dq, float* dkv, float* dwin,
+                        float* dsink, void* ws, size_t ws_bytes) {
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = k; a.W = W;
+  a.sparse = true; a.N_cap = N_cap; a.q_pos0 = q_pos0; a.q = q; a.kv = kv; a.win = win; a.sink = sink;
+  a.idx = idx; a.scale = scale; a.flags = flags; a.rope_base = rope_base; a.rope_dims = rope_dims;
+  return run_attend_bwd(stream, a, out, lse, dout, dq, dkv, dwin, dsink, ws, ws_bytes, "csa_attend_backward");
+}
+
+int hca_attend_backward(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int W,
+                        int64_t q_pos0, const void* q, const void* kv, const void* win, const float* sink,
+                        float scale, uint32_t flags, float rope_base, int rope_dims, const void* out,
+                        const float* lse, const void* dout, float* dq, float* dkv, float* dwin, float* dsink,
+                        void* ws, size_t ws_bytes) {
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = 0; a.W = W;
+  a.sparse = false; a.N_cap = N_cap; a.q_pos0 = q_pos0; a.q = q; a.kv = kv; a.win = win; a.sink = sink;
+  a.idx = nullptr; a.scale = scale; a.flags = flags; a.rope_base = rope_base; a.rope_dims = rope_dims;
+  return run_attend_bwd(stream, a, out, lse, dout, dq, dkv, dwin, dsink, ws, ws_bytes, "hca_attend_backward");
+}
+
+// ---------------------------------------------------------------------------
 // Ragged batches: sequence b's queries sit at q_pos[b] + t (device array),
 // with q_pos0 the bound that sizes workspaces, plans and validation.
 static int check_q_pos(const int64_t* q_pos, const char* fn) {

@@ -121,6 +121,18 @@ __device__ __forceinline__ int64_t seq_pos(const int64_t* q_pos, int64_t bound, 
 }
 hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t ws_bytes);
 
+// Backward of the core attention: the forward call's arguments plus what the
+// backward reads (forward output and lse, the output's gradient) and writes.
+struct AttendBwdArgs {
+  AttendArgs a;
+  const void* out;       // forward output [B, Tq, H, D]
+  const float* lse;      // forward lse [B, Tq, H]
+  const void* dout;      // gradient of out [B, Tq, H, D]
+  float *dq, *dkv, *dwin, *dsink;
+};
+size_t attend_backward_workspace(const AttendArgs& a);
+hipError_t launch_attend_backward(hipStream_t s, const AttendBwdArgs& p, void* ws, size_t ws_bytes);
+
 struct OutProjArgs {
   int T, n_h, c, g, d_g, d_model;
   const void *o, *w_g, *w_o;
