@@ -369,7 +369,8 @@ int hca_attend_ragged(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, i
  *   dwin [B, W-1+Tq, D] fp32 (rows at negative positions: 0);  dsink [H] fp32
  * Requirements: bf16 q and rows, D = 512, H = 64 or 128, Tq <= 65535,
  * window in the linear layout (no LCA_WIN_RING), one position for the batch;
- * a query's entry indices distinct (as csa_index_topk gives them). Workspace
+ * a query's entry indices distinct and visible to it (index < (p + 1) / m),
+ * as csa_index_topk gives them (other indices are not accumulated). Workspace
  * from *_backward_workspace (it holds per-slot buffers of N_cap x D fp32).
  * ------------------------------------------------------------------------- */
 size_t csa_attend_backward_workspace(int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,

@@ -2062,7 +2062,8 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
 //                     in order): each row's gradient (an MFMA over the heads)
 //                     added into the slot's own buffer (zeroed first);
 //   bwd_reduce_kernel every entry and window row summed over the slots in
-//                     slot order; dsink summed over the queries in order.
+//                     slot order; bwd_sink_kernel: dsink over the queries
+//                     (strided partial sums, then a fixed tree).
 // ===========================================================================
 namespace {
 
@@ -2118,10 +2119,16 @@ BwdPlan make_bwd_plan(const AttendArgs& a) {
 // One workgroup per (query, sequence): D and the sink's part per head, the
 // output gradient turned back by +p (the adjoint of the forward's turn by
 // -p), and [D, H] copies of it and of q (the operands of the head sums).
+// Requires D = 512 (eight channels per lane), H <= 128.
+__device__ __forceinline__ float bwd_turn(float x, float y, bool odd, float2 cs) {
+  return odd ? fmaf(x, cs.y, y * cs.x) : fmaf(x, cs.x, -(y * cs.y));
+}
+
 __global__ __launch_bounds__(256) void bwd_prep_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
+  constexpr int D = 512;
   const AttendArgs& a = p.a;
   const int t = blockIdx.x, b = blockIdx.y;
-  const int D = a.D, H = a.H;
+  const int H = a.H;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int64_t row0 = (static_cast<int64_t>(b) * a.Tq + t) * H;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
@@ -2142,37 +2149,52 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttendBwdArgs p, BwdPlan 
     rt[i] = make_float2(cs, sn);
   }
   __syncthreads();
-  auto turned = [&](int64_t r, int c) -> float {   // channel c of the turned gradient of row r
-    const float x = bf16_to_f32(dout[r * D + (c & ~1)]), y = bf16_to_f32(dout[r * D + (c | 1)]);
-    if (c < D - R) return (c & 1) ? y : x;
-    const float2 cs = rt[(c - (D - R)) >> 1];
-    return (c & 1) ? fmaf(x, cs.y, y * cs.x) : fmaf(x, cs.x, -(y * cs.y));
-  };
+  // row layout: lane l owns channels 8 l .. 8 l + 7 of one head per wave
   for (int h = wid; h < H; h += 4) {
-    const int64_t r = row0 + h;
+    const int64_t r = (row0 + h) * D + 8 * lane;
+    const uint4 dw = *reinterpret_cast<const uint4*>(dout + r);
+    const uint4 ow = *reinterpret_cast<const uint4*>(out + r);
+    const uint32_t dv[4] = {dw.x, dw.y, dw.z, dw.w}, ov[4] = {ow.x, ow.y, ow.z, ow.w};
     float acc = 0.f;
-    for (int c = lane; c < D; c += 64) {
-      acc = fmaf(bf16_to_f32(dout[r * D + c]), bf16_to_f32(out[r * D + c]), acc);
-      dor[r * D + c] = f32_to_bf16(turned(r, c));
+    uint32_t tw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = bf16_to_f32(static_cast<uint16_t>(dv[j] & 0xffffu));
+      const float y = bf16_to_f32(static_cast<uint16_t>(dv[j] >> 16));
+      acc = fmaf(x, bf16_to_f32(static_cast<uint16_t>(ov[j] & 0xffffu)), acc);
+      acc = fmaf(y, bf16_to_f32(static_cast<uint16_t>(ov[j] >> 16)), acc);
+      const int c = 8 * lane + 2 * j;
+      float u = x, v = y;
+      if (c >= D - R) {
+        const float2 cs = rt[(c - (D - R)) >> 1];
+        u = bwd_turn(x, y, false, cs);
+        v = bwd_turn(x, y, true, cs);
+      }
+      tw[j] = static_cast<uint32_t>(f32_to_bf16(u)) | (static_cast<uint32_t>(f32_to_bf16(v)) << 16);
     }
+    *reinterpret_cast<uint4*>(dor + r) = make_uint4(tw[0], tw[1], tw[2], tw[3]);
     acc = wave_sum(acc);
     if (lane == 0) {
-      Dv[r] = acc;
-      dsp[r] = -expf(a.sink[h] - p.lse[r]) * acc;
+      Dv[row0 + h] = acc;
+      dsp[row0 + h] = -expf(a.sink[h] - p.lse[row0 + h]) * acc;
     }
   }
+  // [D, H] layouts through LDS, 64 channels at a time
   for (int c0 = 0; c0 < D; c0 += 64) {
-    for (int e = threadIdx.x; e < H * 64; e += 256) {
-      const int h = e >> 6, c = e & 63;
-      slab[0][e] = q[(row0 + h) * D + c0 + c];
-      slab[1][e] = f32_to_bf16(turned(row0 + h, c0 + c));
+    for (int e = threadIdx.x; e < H * 8; e += 256) {  // 8 channels per thread: coalesced loads
+      const int h = e >> 3, c8 = 8 * (e & 7);
+      *reinterpret_cast<uint4*>(&slab[0][h * 64 + c8]) = *reinterpret_cast<const uint4*>(q + (row0 + h) * D + c0 + c8);
+      *reinterpret_cast<uint4*>(&slab[1][h * 64 + c8]) = *reinterpret_cast<const uint4*>(dout + (row0 + h) * D + c0 + c8);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < H * 64; e += 256) {
       const int c = e / H, h = e % H;
       const int64_t o = ((static_cast<int64_t>(b) * a.Tq + t) * D + c0 + c) * H + h;
       qT[o] = slab[0][h * 64 + c];
-      dT[o] = slab[1][h * 64 + c];
+      float x = bf16_to_f32(slab[1][h * 64 + (c & ~1)]), y = bf16_to_f32(slab[1][h * 64 + (c | 1)]);
+      float v = (c & 1) ? y : x;
+      if (c0 + c >= D - R) v = bwd_turn(x, y, (c & 1) != 0, rt[(c0 + c - (D - R)) >> 1]);
+      dT[o] = f32_to_bf16(v);
     }
     __syncthreads();
   }
@@ -2180,8 +2202,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttendBwdArgs p, BwdPlan 
 
 // One workgroup per (64-head group, query, sequence), 16 heads per wave, rows
 // in 32-row tiles (swizzled LDS, two-tile ring). S^T and dP^T share the row
-// fragments; P = exp(l - lse) (the forward's lse), dl = P (dP - D); P and dl
-// go to memory as bf16 ([row][head] per query); dq^T += X^T dl^T.
+// fragments; P = exp(l - lse) (the forward's lse), dl = P (dP - D); P and
+// scale * dl go to memory as bf16 ([row][head] per query); dq^T += X^T dl^T.
 __global__ __launch_bounds__(kAttThreads) void bwd_query_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
   constexpr int D = 512, KS = D / 32, DT = D / 16, RPW = kTileRows / 4;
   const AttendArgs& a = p.a;
@@ -2279,7 +2301,7 @@ __global__ __launch_bounds__(kAttThreads) void bwd_query_kernel(AttendBwdArgs p,
         L[i] = P * (dacc[i >> 2][i & 3] - Dv);
         const int64_t v = c0 + it * kTileRows + (i < 4 ? 4 * g + i : 16 + 4 * g + (i - 4));
         Pw[v * a.H + head] = f32_to_bf16(P);
-        Lw[v * a.H + head] = f32_to_bf16(L[i]);
+        Lw[v * a.H + head] = f32_to_bf16(a.scale * L[i]);   // the row sums take scale * dl
       }
       uint4 lw;
       lw.x = pack_bf16x2(L[0], L[1]);
@@ -2302,22 +2324,34 @@ __global__ __launch_bounds__(kAttThreads) void bwd_query_kernel(AttendBwdArgs p,
         make_float4(acc[dt][0] * a.scale, acc[dt][1] * a.scale, acc[dt][2] * a.scale, acc[dt][3] * a.scale);
 }
 
-// The slot buffers start at zero (a fill kernel, so the work records into a
-// captured graph as plain kernels).
-__global__ __launch_bounds__(256) void bwd_zero_kernel(float4* __restrict__ p, int64_t n4) {
-  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256) p[i] = z;
+// One workgroup per (slot, sequence): queries [s C, s C + C) in order; wave w
+// owns channels [128 w, 128 w + 128). A query's row sources go to LDS first;
+// then each 32-row tile's gradients, P^T dO + (scale dl)^T Q summed over the
+// heads (MFMA, K = heads, one accumulation chain), are added into the slot's
+// buffer rows (entry or window row). With 64 heads the query's dO and Q
+// operands stay in registers across its tiles. A query's rows are distinct,
+// so its tiles never touch one row twice; consecutive queries are ordered by
+// a barrier (the workgroup's waves share one CU and its cache, so plain loads
+// and stores suffice).
+template <int KSH>
+__device__ __forceinline__ void bwd_kv_load_b(const uint16_t* dTq, const uint16_t* qTq, int H, int cb, int lane,
+                                              int ks0, bf16x8 (&bD)[8][KSH], bf16x8 (&bQ)[8][KSH]) {
+  const int kk = 8 * (lane >> 4);
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const int64_t col = cb + 16 * nt + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < KSH; ++ks) {
+      bD[nt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dTq + col * H + 32 * (ks0 + ks) + kk));
+      bQ[nt][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qTq + col * H + 32 * (ks0 + ks) + kk));
+    }
+  }
 }
 
-// One workgroup per (slot, sequence): queries [s C, s C + C) in order; wave w
-// owns channels [128 w, 128 w + 128). For each 32-row tile of a query, the
-// rows' gradients sum P^T dO + scale dl^T Q over the heads (MFMA, K = heads)
-// and are added into the slot's buffer row (entry or window row). A query's
-// rows are distinct, so its tiles never touch one row twice; consecutive
-// queries are ordered by a barrier (the workgroup's waves share one CU and
-// its cache, so plain loads and stores suffice).
+template <int KSH>
 __global__ __launch_bounds__(256) void bwd_kv_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
   constexpr int D = 512;
+  constexpr int KR = KSH <= 2 ? KSH : 2;          // head steps held in registers at a time
   const AttendArgs& a = p.a;
   const int s = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wid = threadIdx.x >> 6;
@@ -2326,8 +2360,8 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(AttendBwdArgs p, BwdPlan bp
   const int64_t slot = static_cast<int64_t>(b) * bp.Ps + s;
   float* sE = reinterpret_cast<float*>(ws + bp.off_sE) + slot * a.N_cap * D;
   float* sW = reinterpret_cast<float*>(ws + bp.off_sW) + slot * bp.wrows * D;
-  __shared__ int32_t src[kTileRows];
-  const int H = a.H, KSH = H / 32;
+  __shared__ int32_t src[kMaxSplitRows];
+  const int H = a.H;
   const int cb = 128 * wid;
   const int kk = 8 * (lane >> 4);
   for (int t = t0; t < t1; ++t) {
@@ -2337,97 +2371,171 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(AttendBwdArgs p, BwdPlan bp
     const uint16_t* Lq = reinterpret_cast<const uint16_t*>(ws + bp.off_dL) + bt * bp.nr * H;
     const uint16_t* dTq = reinterpret_cast<const uint16_t*>(ws + bp.off_dT) + bt * D * H;
     const uint16_t* qTq = reinterpret_cast<const uint16_t*>(ws + bp.off_qT) + bt * D * H;
-    for (int64_t v0 = 0; v0 < rs.nrows; v0 += kTileRows) {
-      if (tid < kTileRows) src[tid] = v0 + tid < rs.nrows ? encode_row(a, b, t, rs, v0 + tid) : -1;
-      f32x4 c1[2][8], c2[2][8];
+    bf16x8 bD[8][KR], bQ[8][KR];
+    if constexpr (KSH == KR) bwd_kv_load_b<KR>(dTq, qTq, H, cb, lane, 0, bD, bQ);
+    for (int64_t c0 = 0; c0 < rs.nrows; c0 += kMaxSplitRows) {
+      const int nr = static_cast<int>(rs.nrows - c0 < kMaxSplitRows ? rs.nrows - c0 : kMaxSplitRows);
+      __syncthreads();                             // the last query's (or chunk's) src[] and row updates done
+      for (int v = tid; v < (nr + kTileRows - 1) / kTileRows * kTileRows; v += 256)
+        src[v] = v < nr ? encode_row(a, b, t, rs, c0 + v) : -1;
+      __syncthreads();
+      for (int v0 = 0; v0 < nr; v0 += kTileRows) {
+        f32x4 c[2][8];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) c1[mt][nt] = c2[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < KSH; ++ks) {
-        bf16x8 aP[2], aL[2];
+          for (int nt = 0; nt < 8; ++nt) c[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int64_t row = v0 + 16 * mt + (lane & 15);
-          aP[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pq + row * H + 32 * ks + kk));
-          aL[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Lq + row * H + 32 * ks + kk));
-        }
+        for (int k0 = 0; k0 < KSH; k0 += KR) {
+          if constexpr (KSH != KR) bwd_kv_load_b<KR>(dTq, qTq, H, cb, lane, k0, bD, bQ);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const int64_t col = cb + 16 * nt + (lane & 15);
-          const bf16x8 bD = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dTq + col * H + 32 * ks + kk));
-          const bf16x8 bQ = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qTq + col * H + 32 * ks + kk));
+          for (int ks = 0; ks < KR; ++ks) {
+            bf16x8 aP[2], aL[2];
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            c1[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aP[mt], bD, c1[mt][nt], 0, 0, 0);
-            c2[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aL[mt], bQ, c2[mt][nt], 0, 0, 0);
+            for (int mt = 0; mt < 2; ++mt) {
+              const int64_t row = c0 + v0 + 16 * mt + (lane & 15);
+              aP[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pq + row * H + 32 * (k0 + ks) + kk));
+              aL[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Lq + row * H + 32 * (k0 + ks) + kk));
+            }
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+              for (int mt = 0; mt < 2; ++mt) {
+                c[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aP[mt], bD[nt][ks], c[mt][nt], 0, 0, 0);
+                c[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aL[mt], bQ[nt][ks], c[mt][nt], 0, 0, 0);
+              }
           }
         }
+        // lane l holds rows 16 mt + 4 (l / 16) + i, channel cb + 16 nt + l % 16
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int32_t e = src[v0 + 16 * mt + 4 * (lane >> 4) + i];
+            if (e == -1) continue;
+            float* dst = e >= 0 ? sE + static_cast<int64_t>(e) * D : sW + static_cast<int64_t>(-2 - e - t0) * D;
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) dst[cb + 16 * nt + (lane & 15)] += c[mt][nt][i];
+          }
       }
-      __syncthreads();                             // src[] of this tile written
-      // lane l holds rows 16 mt + 4 (l / 16) + i, channel cb + 16 nt + l % 16
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int32_t e = src[16 * mt + 4 * (lane >> 4) + i];
-          if (e == -1) continue;
-          float* dst = e >= 0 ? sE + static_cast<int64_t>(e) * D : sW + static_cast<int64_t>(-2 - e - t0) * D;
-#pragma unroll
-          for (int nt = 0; nt < 8; ++nt) {
-            const int ch = cb + 16 * nt + (lane & 15);
-            dst[ch] += fmaf(a.scale, c2[mt][nt][i], c1[mt][nt][i]);
-          }
-        }
-      __syncthreads();                             // src[] consumed; the query's row updates done
     }
   }
 }
 
-// Sum over the slots in slot order: one workgroup per entry or window row of
-// a sequence, two channels per thread.
+// Entries slot s can touch: those visible to its last query (a causal bound;
+// a slot's other rows stay zero).
+__host__ __device__ __forceinline__ int64_t bwd_slot_entries(const AttendArgs& a, const BwdPlan& bp, int s) {
+  const int t_last = (s + 1) * bp.C < a.Tq ? (s + 1) * bp.C - 1 : a.Tq - 1;
+  const int64_t nv = n_visible(a.q_pos0 + t_last, a.m);
+  return nv < a.N_cap ? nv : a.N_cap;
+}
+
+// Sum over the slots in slot order: one workgroup per block of 8 rows (entry
+// rows, then window rows) of a sequence, 16 channels per thread (16 KB of
+// each slot read as one block). Slots that cannot touch a row are skipped
+// (their rows hold zeros).
+constexpr int kRedRows = 8;
+
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
   constexpr int D = 512;
   const AttendArgs& a = p.a;
-  const int64_t row = blockIdx.x;
   const int b = blockIdx.y;
-  const int c = 2 * threadIdx.x;
+  const int64_t nEb = (a.N_cap + kRedRows - 1) / kRedRows;
   const float* sE = reinterpret_cast<const float*>(ws + bp.off_sE);
   const float* sW = reinterpret_cast<const float*>(ws + bp.off_sW);
-  float2 acc = make_float2(0.f, 0.f);
-  if (row < a.N_cap) {
-    for (int s = 0; s < bp.Ps; ++s) {
-      const int64_t slot = static_cast<int64_t>(b) * bp.Ps + s;
-      const float2 v = *reinterpret_cast<const float2*>(sE + (slot * a.N_cap + row) * D + c);
-      acc.x += v.x;
-      acc.y += v.y;
+  const int e0 = threadIdx.x * 16;                 // element of the 8 x 512 block
+  const int rl = e0 / D, c = e0 % D;               // its row in the block and first channel
+  float4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](const float* src) {
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const float4*>(src + 4 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[j].x += v[j].x;
+      acc[j].y += v[j].y;
+      acc[j].z += v[j].z;
+      acc[j].w += v[j].w;
     }
-    *reinterpret_cast<float2*>(p.dkv + (static_cast<int64_t>(b) * a.N_cap + row) * D + c) = acc;
+  };
+  if (blockIdx.x < nEb) {
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kRedRows + rl;
+    if (row < a.N_cap) {
+      int s = 0;                                     // slots before s cannot see this entry (their bound grows with s)
+      while (s < bp.Ps && bwd_slot_entries(a, bp, s) <= row) ++s;
+      const float* base = sE + ((static_cast<int64_t>(b) * bp.Ps) * a.N_cap + row) * D + c;
+      const int64_t stride = a.N_cap * D;            // one slot to the next
+      for (; s + 8 <= bp.Ps; s += 8) {               // eight slots of loads in flight, added in slot order
+        float4 v[8][4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[u][j] = *reinterpret_cast<const float4*>(base + (s + u) * stride + 4 * j);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[j].x += v[u][j].x;
+            acc[j].y += v[u][j].y;
+            acc[j].z += v[u][j].z;
+            acc[j].w += v[u][j].w;
+          }
+      }
+      for (; s < bp.Ps; ++s) add(base + s * stride);
+      float* dst = p.dkv + (static_cast<int64_t>(b) * a.N_cap + row) * D + c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<float4*>(dst + 4 * j) = acc[j];
+    }
   } else {
-    const int r = static_cast<int>(row - a.N_cap);  // window row r: read by queries r - W + 1 .. r
-    const int tlo = r - (a.W - 1) > 0 ? r - (a.W - 1) : 0;
-    const int thi = r < a.Tq - 1 ? r : a.Tq - 1;
-    for (int s = tlo / bp.C; s <= thi / bp.C && tlo <= thi; ++s) {
-      const int loc = r - s * bp.C;
-      if (loc < 0 || loc >= bp.wrows) continue;
-      const int64_t slot = static_cast<int64_t>(b) * bp.Ps + s;
-      const float2 v = *reinterpret_cast<const float2*>(sW + (slot * bp.wrows + loc) * D + c);
-      acc.x += v.x;
-      acc.y += v.y;
+    const int r = static_cast<int>((blockIdx.x - nEb) * kRedRows + rl);   // window row r
+    if (r < a.W - 1 + a.Tq) {
+      const int tlo = r - (a.W - 1) > 0 ? r - (a.W - 1) : 0;            // read by queries r - W + 1 .. r
+      const int thi = r < a.Tq - 1 ? r : a.Tq - 1;
+      for (int s = tlo / bp.C; s <= thi / bp.C && tlo <= thi; ++s) {
+        const int loc = r - s * bp.C;
+        if (loc < 0 || loc >= bp.wrows) continue;
+        add(sW + ((static_cast<int64_t>(b) * bp.Ps + s) * bp.wrows + loc) * D + c);
+      }
+      float* dst = p.dwin + (static_cast<int64_t>(b) * (a.W - 1 + a.Tq) + r) * D + c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<float4*>(dst + 4 * j) = acc[j];
     }
-    *reinterpret_cast<float2*>(p.dwin + (static_cast<int64_t>(b) * (a.W - 1 + a.Tq) + r) * D + c) = acc;
   }
 }
 
-// dsink[h] = the sink parts of every query, in (sequence, query) order.
+// Zero the rows each slot can touch: its visible entries and its window rows.
+__global__ __launch_bounds__(256) void bwd_zero_slots_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
+  constexpr int D = 512;
+  const AttendArgs& a = p.a;
+  const int s = blockIdx.y, b = blockIdx.z;
+  const int64_t slot = static_cast<int64_t>(b) * bp.Ps + s;
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4* e = reinterpret_cast<float4*>(reinterpret_cast<float*>(ws + bp.off_sE) + slot * a.N_cap * D);
+  const int64_t ne4 = bwd_slot_entries(a, bp, s) * D / 4;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < ne4; i += static_cast<int64_t>(gridDim.x) * 256) e[i] = z;
+  float4* w = reinterpret_cast<float4*>(reinterpret_cast<float*>(ws + bp.off_sW) + slot * bp.wrows * D);
+  const int64_t nw4 = static_cast<int64_t>(bp.wrows) * D / 4;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < nw4; i += static_cast<int64_t>(gridDim.x) * 256) w[i] = z;
+}
+
+// dsink[h]: one workgroup per head; thread i sums queries i, i + 256, ... in
+// order, then the 256 partial sums add in a fixed tree (deterministic).
 __global__ __launch_bounds__(256) void bwd_sink_kernel(AttendBwdArgs p, BwdPlan bp, uint8_t* ws) {
   const AttendArgs& a = p.a;
   const float* dsp = reinterpret_cast<const float*>(ws + bp.off_dsp);
-  for (int h = threadIdx.x + blockIdx.x * blockDim.x; h < a.H; h += blockDim.x * gridDim.x) {
-    float acc = 0.f;
-    for (int64_t bt = 0; bt < static_cast<int64_t>(a.B) * a.Tq; ++bt) acc += dsp[bt * a.H + h];
-    p.dsink[h] = acc;
+  __shared__ float part[256];
+  const int h = blockIdx.x;
+  float acc = 0.f;
+  for (int64_t bt = threadIdx.x; bt < static_cast<int64_t>(a.B) * a.Tq; bt += 256) acc += dsp[bt * a.H + h];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
   }
+  if (threadIdx.x == 0) p.dsink[h] = part[0];
 }
 
 }  // namespace
@@ -2452,19 +2560,23 @@ hipError_t launch_attend_backward(hipStream_t s, const AttendBwdArgs& p, void* w
   }
   {
     LaunchScope scope(s, "attend_bwd_kv");
-    // slot buffers (entries, then window rows: contiguous) start at zero
-    const int64_t n4 = static_cast<int64_t>(bp.off_sW - bp.off_sE) / 16 +
-                       static_cast<int64_t>(a.B) * bp.Ps * bp.wrows * a.D / 4;
-    scope.launch(bwd_zero_kernel, dim3(2048), dim3(256), 0, reinterpret_cast<float4*>(w + bp.off_sE), n4);
-    scope.launch(bwd_kv_kernel, dim3(bp.Ps, a.B), dim3(256), 0, p, bp, w);
+    // the rows each slot can touch start at zero
+    scope.launch(bwd_zero_slots_kernel, dim3(8, bp.Ps, a.B), dim3(256), 0, p, bp, w);
+    if (a.H == 64) scope.launch(bwd_kv_kernel<2>, dim3(bp.Ps, a.B), dim3(256), 0, p, bp, w);
+    else scope.launch(bwd_kv_kernel<4>, dim3(bp.Ps, a.B), dim3(256), 0, p, bp, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     LaunchScope scope(s, "attend_bwd_reduce");
-    scope.launch(bwd_reduce_kernel, dim3(static_cast<uint32_t>(a.N_cap + a.W - 1 + a.Tq), a.B), dim3(256), 0, p, bp,
-                 w);
-    scope.launch(bwd_sink_kernel, dim3(1), dim3(256), 0, p, bp, w);
+    const int64_t blocks = (a.N_cap + kRedRows - 1) / kRedRows + (a.W - 1 + a.Tq + kRedRows - 1) / kRedRows;
+    scope.launch(bwd_reduce_kernel, dim3(static_cast<uint32_t>(blocks), a.B), dim3(256), 0, p, bp, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    LaunchScope scope(s, "attend_bwd_sink");
+    scope.launch(bwd_sink_kernel, dim3(a.H), dim3(256), 0, p, bp, w);
     return hipGetLastError();
   }
 }
