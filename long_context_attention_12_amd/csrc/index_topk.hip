@@ -613,17 +613,136 @@ __device__ __forceinline__ void select_by_passes(const SelRow& row, int k, bool 
   }
 }
 
+// Short lists whose threads hold at least 2k scores' worth of maxima: each
+// thread's largest key is a score of the list, so the lower edge `lo` of the
+// top-digit bin holding the k-th largest of those maxima has at least k scores
+// at or above it, and the k-th largest score is at or above `lo`. Only the
+// scores from `lo` up (a few percent of a list, typically) are candidates:
+// they go to LDS in increasing index order, and their digits are taken on the
+// offset key - lo over [lo, max key] (12 bits at a time, from the top), which
+// spreads them over the bins where the raw key's top digit would stack them
+// into one or two (a float's sign and exponent). Same threshold, same ties in
+// index order, same output as the full passes. Returns false, having written
+// nothing, when the candidates exceed kCandCap.
+constexpr int kCandCap = 4096;
+constexpr int kCandPer = kCandCap / kSelThreads;
+
+__device__ __forceinline__ bool select_filtered(const SelRow& row, int k, bool key16,
+                                                const uint32_t (&key)[kSelItems], uint32_t* hist, uint32_t* wsum,
+                                                uint32_t* ckey, int32_t* cidx, uint32_t* sh_digit_p,
+                                                uint32_t* sh_krem_p, uint32_t* sh_hi_p) {
+  uint32_t& sh_digit = *sh_digit_p;
+  uint32_t& sh_krem = *sh_krem_p;
+  const int tid = threadIdx.x;
+  const int top = key16 ? 4 : 20;                  // shift of the key's top 12-bit digit
+  uint32_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < kSelItems; ++j) mx = max(mx, key[j]);
+  uint32_t wmx = mx;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wmx = max(wmx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(wmx), o, kWave)));
+  for (int i = tid; i < kMaxBins; i += kSelThreads) hist[i] = 0;
+  if (tid == 0) *sh_hi_p = 0;
+  __syncthreads();
+  if (mx != 0u) atomicAdd(&hist[mx >> top], 1u);
+  if ((tid & 63) == 0) atomicMax(sh_hi_p, wmx);
+  __syncthreads();
+  find_digit(hist, kMaxBins, static_cast<uint32_t>(k), wsum, &sh_digit, &sh_krem);
+  const uint32_t lo = sh_digit << top, hi = *sh_hi_p;
+  uint32_t cm = 0;
+#pragma unroll
+  for (int j = 0; j < kSelItems; ++j) cm |= static_cast<uint32_t>(key[j] >= lo && key[j] != 0u) << j;
+  uint32_t tot;
+  const uint32_t pre = block_excl_scan(__builtin_popcount(cm), wsum, &tot);
+  if (tot > static_cast<uint32_t>(kCandCap)) return false;
+  {
+    uint32_t pos = pre;
+    const int32_t i0 = tid * kSelItems;
+#pragma unroll
+    for (int j = 0; j < kSelItems; ++j)
+      if ((cm >> j) & 1u) {
+        ckey[pos] = key[j];
+        cidx[pos] = i0 + j;
+        ++pos;
+      }
+  }
+  __syncthreads();
+  // candidate c = kCandPer * tid + q: contiguous per thread, so one scan orders them
+  uint32_t ck[kCandPer];
+  {
+    const uint4 v = reinterpret_cast<const uint4*>(ckey)[tid];
+    const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < kCandPer; ++q) ck[q] = static_cast<uint32_t>(kCandPer * tid + q) < tot ? e[q] : 0u;
+  }
+  // digits of key - base over [base, base + width), 12 bits at a time
+  uint32_t base = lo, krem = static_cast<uint32_t>(k);
+  uint64_t width = static_cast<uint64_t>(hi) - lo + 1;
+  while (width > 1) {
+    const int bl = 64 - __builtin_clzll(width - 1);
+    const int sh = bl > 12 ? bl - 12 : 0;
+    const int nb = static_cast<int>((width - 1) >> sh) + 1;
+    for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kCandPer; ++q) {
+      const uint32_t off = ck[q] - base;
+      if (ck[q] != 0u && static_cast<uint64_t>(off) < width) atomicAdd(&hist[off >> sh], 1u);
+    }
+    __syncthreads();
+    find_digit(hist, nb, krem, wsum, &sh_digit, &sh_krem);
+    base += sh_digit << sh;
+    krem = sh_krem;
+    width = uint64_t(1) << sh;
+  }
+  const uint32_t thr = base;       // key of the k-th largest score
+
+  uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+  for (int q = 0; q < kCandPer; ++q) {
+    gtm |= static_cast<uint32_t>(ck[q] > thr) << q;
+    eqm |= static_cast<uint32_t>(ck[q] == thr) << q;
+  }
+  uint32_t tot2;
+  const uint32_t pre2 = block_excl_scan((__builtin_popcount(gtm) << 16) | __builtin_popcount(eqm), wsum, &tot2);
+  const uint32_t gt_pre = pre2 >> 16, eq_pre = pre2 & 0xffffu;
+  uint32_t pos = gt_pre + min(eq_pre, krem);
+  uint32_t take = gtm;
+  for (uint32_t c = eq_pre; eqm && c < krem; ++c) {
+    take |= eqm & (~eqm + 1u);
+    eqm &= eqm - 1;
+  }
+  while (take) {
+    const int q = __builtin_ctz(take);
+    take &= take - 1;
+    const int32_t ix = cidx[kCandPer * tid + q];
+    row.io[pos] = ix;
+    if (row.so) row.so[pos] = row.s[ix];
+    ++pos;
+  }
+  return true;
+}
+
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t N_cap, int Tq, int t_off, int Tc,
     int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int k, bool key16, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
   __shared__ uint32_t hist[kMaxBins];
   __shared__ __attribute__((aligned(16))) uint32_t wsum[kSelThreads / 64];
-  __shared__ uint32_t sh_digit, sh_krem;
+  __shared__ __attribute__((aligned(16))) uint32_t ckey[kCandCap];
+  __shared__ int32_t cidx[kCandCap];
+  __shared__ uint32_t sh_digit, sh_krem, sh_hi;
   const SelRow row = sel_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, q_pos, m, k, idx_out, score_out);
   if (row.n <= k) {
     select_all(row, k);
     return;
+  }
+  // threads holding a score: (n + kSelItems - 1) / kSelItems, one round (n <= kRound here)
+  if ((row.n + kSelItems - 1) / kSelItems >= 2 * static_cast<int64_t>(k)) {
+    uint32_t key[kSelItems];
+    load_round(row.s, row.n, 0, key16, key);
+    if (select_filtered(row, k, key16, key, hist, wsum, ckey, cidx, &sh_digit, &sh_krem, &sh_hi)) return;
+    __syncthreads();                 // candidate and histogram memory are reused below
   }
   select_by_passes(row, k, key16, hist, wsum, &sh_digit, &sh_krem);
 }

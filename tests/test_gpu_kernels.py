@@ -404,6 +404,55 @@ def test_index_topk_all_ties_take_lowest_indices():
     np.testing.assert_array_equal(idx.cpu().numpy()[0, 0], np.arange(k))
 
 
+@pytest.mark.parametrize("case", ["spread", "spikes", "ragged", "small_k", "ties5", "zeros", "same"])
+@pytest.mark.parametrize("bf16_scores", [False, True])
+def test_index_topk_select_exact_order(case, bf16_scores):
+    # Integer indexer vectors and power-of-two head weights make every score
+    # exact in fp32, so the expected result is exact: score descending, index
+    # ascending, cut at k, returned in index order. Lists of 20000 - 32768
+    # entries with k far below n / 64 take the select that filters candidates
+    # by the threads' maxima (spread, spikes, ragged, small_k; zeros, the exact
+    # zeros of all-negative head weights, as a candidate range one key wide);
+    # 5 distinct keys and one key for every entry crowd the candidates past
+    # their cap and take the full passes.
+    L = need_gpu()
+    rng = np.random.default_rng(400 + len(case) + 7 * bf16_scores)
+    B, Tq, H_I, d_I, m = 2, 1, 4, 128, 4
+    N_cap, k = 32768, 512
+    if case == "ragged":
+        N_cap, k = 30001, 256
+    if case == "small_k":
+        k = 16
+    qI = rng.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.float32)
+    kI = rng.integers(-8, 9, size=(B, N_cap, d_I)).astype(np.float32)
+    w = np.tile(np.array([1.0, 0.5, 0.25, 0.125], np.float32), (B, Tq, 1))
+    if case == "spikes":
+        for b in range(B):
+            kI[b, rng.choice(N_cap, size=N_cap // 100, replace=False)] *= 4
+    elif case == "ties5":
+        base = rng.integers(-8, 9, size=(5, d_I)).astype(np.float32)
+        kI = np.stack([base[rng.integers(0, 5, size=N_cap)] for _ in range(B)])
+    elif case == "zeros":
+        w = -w
+    elif case == "same":
+        kI[:] = kI[:, :1]
+    q_pos0 = m * N_cap - 1                 # every entry visible
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    say(f"select exact order {case} bf16={bf16_scores}")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
+                     flags=L.SCORE_BF16 if bf16_scores else 0)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b in range(B):
+        nv = min(N_cap, O.n_visible(q_pos0, m))
+        sc = O.index_scores(qI[b, 0], w[b, 0], kI[b], nv)
+        assert np.all(np.abs(sc) < 2.0 ** 23), "scores must stay exact in fp32"
+        if bf16_scores:
+            sc = O.bf16_round(sc)
+        order = np.lexsort((np.arange(nv), -sc))
+        np.testing.assert_array_equal(got[b, 0], np.sort(order[:k]), err_msg=f"{case} b={b}")
+
+
 # ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------
