@@ -877,6 +877,38 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
     }
   }
 
+  if constexpr (NHT == 1) {
+    // Partials through LDS: the wave's 16 x D fp32 block goes to its own ring
+    // slot (32 KB; 16-byte slots XOR-swizzled by head, conflict-free both
+    // ways), then out one head row at a time, 1 KB per store instruction,
+    // streamed past the cache (the combine kernel reads it once).
+    if (sp.S > 1) {
+      __syncthreads();                               // every wave is done with the ring
+      if (active) {
+        float* wl = reinterpret_cast<float*>(Xs[wid]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *reinterpret_cast<f32x4*>(wl + r16 * D + 4 * ((4 * dt + g) ^ r16)) = acc_o[0][dt];
+        const int64_t pi0 = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + (head0 - r16)) * sp.S + split;
+#pragma unroll
+        for (int hh = 0; hh < 16; ++hh) {
+          float* po = part_o + (pi0 + static_cast<int64_t>(hh) * sp.S) * D;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int slot = lane + 64 * half;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(wl + hh * D + 4 * (slot ^ hh));
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(po + 4 * slot));
+          }
+        }
+        if (g == 0) {
+          const int64_t part_idx = pi0 + static_cast<int64_t>(r16) * sp.S;
+          part_ml[2 * part_idx] = flag[0] ? __builtin_nanf("") : m_run[0];   // NaN: recompute in combine
+          part_ml[2 * part_idx + 1] = z_run[0];
+        }
+      }
+      return;
+    }
+  }
   if (active) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
@@ -1779,23 +1811,48 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int S, int R
 __global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int RS,
                                                        const float* __restrict__ part_o,
                                                        const float* __restrict__ part_ml) {
+  constexpr int NB = 16;                            // splits per batch of partial loads
   __shared__ float sml[2 * 256];
   __shared__ float red[4];
   __shared__ float lc[kCombMaxRows];
   __shared__ float2 rope_tab[256];
+  __shared__ float2 wml[4][256];                    // each wave's split (max, sum) pairs
   __shared__ uint32_t any_nan;
   const int t = blockIdx.y, b = blockIdx.z, wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int D = a.D, h0 = blockIdx.x * 4, h = h0 + wid;
+  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + h;
+  const bool live = h < a.H;
+  const bool own = live && 8 * lane < D;
+  const float* ml = part_ml + row * S * 2;
+  const float* po = part_o + row * S * D + 8 * lane;
+  // the first batch of partial rows and the wave's (max, sum) pairs are in
+  // flight before anything waits
+  float4 v[NB][2];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const bool ok = own && j < S;
+    v[j][0] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(j) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[j][1] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(j) * D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float2 mz[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = lane + 64 * q;
+    mz[q] = live && i < S ? *reinterpret_cast<const float2*>(ml + 2 * i) : make_float2(0.f, 0.f);
+  }
   if (threadIdx.x == 0) any_nan = 0u;
   fill_rope_table(a, b, t, rope_tab);
   __syncthreads();
-  const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + h;
-  const bool live = h < a.H;
-  if (live)
-    for (int i = lane; i < S; i += 64) {
-      const float m = part_ml[(row * S + i) * 2];
-      if (m != m) any_nan = 1u;
+  bool nan_here = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = lane + 64 * q;
+    if (live && i < S) {
+      wml[wid][i] = mz[q];
+      if (mz[q].x != mz[q].x) nan_here = true;
     }
+  }
+  if (nan_here) any_nan = 1u;
   __syncthreads();
   if (any_nan) {                                    // rare: exact path, head by head
     for (int hh = h0; hh < min(h0 + 4, a.H); ++hh)
@@ -1803,24 +1860,23 @@ __global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int 
     return;
   }
   if (!live) return;
-  const bool own = 8 * lane < D;
-  const float* ml = part_ml + row * S * 2;
-  const float* po = part_o + row * S * D + 8 * lane;
   SplitFold f = fold_start(a.sink[h]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float4 v[8][2];
+  for (int s0 = 0; s0 < S; s0 += NB) {
+    if (s0 > 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = own && s0 + j < S;
-      v[j][0] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-      v[j][1] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < NB; ++j) {
+        const bool ok = own && s0 + j < S;
+        v[j][0] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[j][1] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < NB; ++j) {
       if (s0 + j < S) {
         float ca, cc;
-        fold_coeffs(f, ml[2 * (s0 + j)], ml[2 * (s0 + j) + 1], ca, cc);
+        const float2 p = wml[wid][s0 + j];
+        fold_coeffs(f, p.x, p.y, ca, cc);
         acc[0] = fmaf(acc[0], ca, v[j][0].x * cc);
         acc[1] = fmaf(acc[1], ca, v[j][0].y * cc);
         acc[2] = fmaf(acc[2], ca, v[j][0].z * cc);
