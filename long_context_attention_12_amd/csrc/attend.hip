@@ -37,6 +37,7 @@ namespace lca {
 namespace {
 
 constexpr int kTileRows = 32;
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));   // 16-byte streaming stores
 
 struct SplitPlan {
   int S, RS, n_hg, HG;
@@ -878,27 +879,26 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
   }
 
   if constexpr (NHT == 1) {
-    // Partials through LDS: the wave's 16 x D fp32 block goes to its own ring
-    // slot (32 KB; 16-byte slots XOR-swizzled by head, conflict-free both
-    // ways), then out one head row at a time, 1 KB per store instruction,
-    // streamed past the cache (the combine kernel reads it once).
+    // Partials in bf16 (the fold rounds every split's output to bf16 wherever
+    // it runs, so both placements fold the same values), through LDS: the
+    // wave's 16 x D block goes to its own ring slot (8-byte slots
+    // XOR-swizzled by head), then out one head row at a time, 1 KB per store
+    // instruction, streamed past the cache (the combine kernel reads it once).
     if (sp.S > 1) {
       __syncthreads();                               // every wave is done with the ring
       if (active) {
-        float* wl = reinterpret_cast<float*>(Xs[wid]);
+        uint8_t* wl = reinterpret_cast<uint8_t*>(Xs[wid]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<f32x4*>(wl + r16 * D + 4 * ((4 * dt + g) ^ r16)) = acc_o[0][dt];
+          *reinterpret_cast<uint2*>(wl + r16 * (2 * D) + 8 * ((4 * dt + g) ^ (r16 << 2))) =
+              make_uint2(pack_bf16x2(acc_o[0][dt][0], acc_o[0][dt][1]), pack_bf16x2(acc_o[0][dt][2], acc_o[0][dt][3]));
         const int64_t pi0 = ((static_cast<int64_t>(b) * a.Tq + t) * a.H + (head0 - r16)) * sp.S + split;
+        uint16_t* pob = reinterpret_cast<uint16_t*>(part_o);
 #pragma unroll
         for (int hh = 0; hh < 16; ++hh) {
-          float* po = part_o + (pi0 + static_cast<int64_t>(hh) * sp.S) * D;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int slot = lane + 64 * half;
-            const f32x4 v = *reinterpret_cast<const f32x4*>(wl + hh * D + 4 * (slot ^ hh));
-            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(po + 4 * slot));
-          }
+          const uint4 v = *reinterpret_cast<const uint4*>(wl + hh * (2 * D) + 8 * ((2 * lane) ^ (hh << 2)));
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, v),
+                                      reinterpret_cast<u32x4_nt*>(pob + (pi0 + static_cast<int64_t>(hh) * sp.S) * D + 8 * lane));
         }
         if (g == 0) {
           const int64_t part_idx = pi0 + static_cast<int64_t>(r16) * sp.S;
@@ -1140,6 +1140,18 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_fold_kernel(AttendArgs
       }
       float ca, cc;
       fold_coeffs(fold, m_run, z_run, ca, cc);
+      // a split's output folds as bf16, as the split kernel stores it, unless
+      // it was recomputed (the exact path keeps fp32 in both placements)
+      if (!((todo >> (wid * 16 + r16)) & 1u)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const uint32_t w = pack_bf16x2(acc_o[dt][i], acc_o[dt][i + 1]);
+            acc_o[dt][i] = bf16_to_f32(static_cast<uint16_t>(w & 0xffffu));
+            acc_o[dt][i + 1] = bf16_to_f32(static_cast<uint16_t>(w >> 16));
+          }
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -1716,20 +1728,30 @@ __device__ void recompute_split(const AttendArgs& a, int RS, int b, int t, int h
 // written to out (and lse). Every thread of the block calls it (it holds block
 // barriers); thread c < D/2 owns channel pair (2c, 2c+1). sml holds 2S floats,
 // red one float per wave, lc kCombMaxRows floats, all in LDS.
+// Channel pair (2c, 2c+1) of split s's partial: fp32, or bf16 (pb16).
+__device__ __forceinline__ float2 part_pair(const float* po, bool pb16, int64_t s, int D, int c) {
+  if (pb16) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(po) + s * D)[c];
+    return make_float2(bf16_to_f32(static_cast<uint16_t>(w & 0xffffu)), bf16_to_f32(static_cast<uint16_t>(w >> 16)));
+  }
+  return *reinterpret_cast<const float2*>(po + s * D + 2 * c);
+}
+
 __device__ void combine_row(const AttendArgs& a, int S, int RS, int b, int t, int h,
                             const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                            float* sml, float* red, float* lc) {
+                            float* sml, float* red, float* lc, bool pb16 = false) {
   const int c = threadIdx.x;
   const int D = a.D;
   const bool own = 2 * c < D;
   const int64_t row = (static_cast<int64_t>(b) * a.Tq + t) * a.H + h;
   const float* ml = part_ml + row * S * 2;
-  const float* po = part_o + row * S * D;
+  const float* po = pb16 ? reinterpret_cast<const float*>(reinterpret_cast<const uint16_t*>(part_o) + row * S * D)
+                        : part_o + row * S * D;
   for (int i = c; i < 2 * S; i += blockDim.x) sml[i] = ml[i];
   float2 ov[kCombBatch];
 #pragma unroll
   for (int j = 0; j < kCombBatch; ++j)
-    ov[j] = (j < S && own) ? *reinterpret_cast<const float2*>(po + static_cast<int64_t>(j) * D + 2 * c) : make_float2(0.f, 0.f);
+    ov[j] = (j < S && own) ? part_pair(po, pb16, j, D, c) : make_float2(0.f, 0.f);
   const float sink = a.sink[h];
   __syncthreads();
   // splits flagged by the attention kernel (NaN max) are recomputed exactly
@@ -1761,7 +1783,7 @@ __device__ void combine_row(const AttendArgs& a, int S, int RS, int b, int t, in
     }
   }
   for (int s = kCombBatch; s < S; ++s) {
-    float2 o = own ? *reinterpret_cast<const float2*>(po + static_cast<int64_t>(s) * D + 2 * c) : make_float2(0.f, 0.f);
+    float2 o = own ? part_pair(po, pb16, s, D, c) : make_float2(0.f, 0.f);
     float ms = sml[2 * s], zs = sml[2 * s + 1];
     if (any_flag && ml[2 * s] != ml[2 * s]) {       // flagged split beyond the batch: recompute again
       recompute_split(a, RS, b, t, h, s, red, lc, ms, zs, o);
@@ -1808,6 +1830,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int S, int R
 // 8l .. 8l + 7 and streams two float4 of every split's partial, so each lane
 // keeps 2S loads in flight. A workgroup whose heads hold a flagged split (max
 // NaN) merges them with combine_row instead, which recomputes that split.
+template <bool PB16>
 __global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int RS,
                                                        const float* __restrict__ part_o,
                                                        const float* __restrict__ part_ml) {
@@ -1825,15 +1848,24 @@ __global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int 
   const bool own = live && 8 * lane < D;
   const float* ml = part_ml + row * S * 2;
   const float* po = part_o + row * S * D + 8 * lane;
+  const uint16_t* pob = reinterpret_cast<const uint16_t*>(part_o) + row * S * D + 8 * lane;
   // the first batch of partial rows and the wave's (max, sum) pairs are in
   // flight before anything waits
-  float4 v[NB][2];
+  float4 v[PB16 ? 1 : NB][2];
+  uint4 vb[PB16 ? NB : 1];
+  auto load_batch = [&](int s0) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const bool ok = own && j < S;
-    v[j][0] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(j) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-    v[j][1] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(j) * D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+    for (int j = 0; j < NB; ++j) {
+      const bool ok = own && s0 + j < S;
+      if constexpr (PB16) {
+        vb[j] = ok ? *reinterpret_cast<const uint4*>(pob + static_cast<int64_t>(s0 + j) * D) : make_uint4(0, 0, 0, 0);
+      } else {
+        v[j][0] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[j][1] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  load_batch(0);
   float2 mz[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1856,35 +1888,34 @@ __global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int 
   __syncthreads();
   if (any_nan) {                                    // rare: exact path, head by head
     for (int hh = h0; hh < min(h0 + 4, a.H); ++hh)
-      combine_row(a, S, RS, b, t, hh, part_o, part_ml, sml, red, lc);
+      combine_row(a, S, RS, b, t, hh, part_o, part_ml, sml, red, lc, PB16);
     return;
   }
   if (!live) return;
   SplitFold f = fold_start(a.sink[h]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += NB) {
-    if (s0 > 0) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const bool ok = own && s0 + j < S;
-        v[j][0] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-        v[j][1] = ok ? *reinterpret_cast<const float4*>(po + static_cast<int64_t>(s0 + j) * D + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
+    if (s0 > 0) load_batch(s0);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (s0 + j < S) {
         float ca, cc;
         const float2 p = wml[wid][s0 + j];
         fold_coeffs(f, p.x, p.y, ca, cc);
-        acc[0] = fmaf(acc[0], ca, v[j][0].x * cc);
-        acc[1] = fmaf(acc[1], ca, v[j][0].y * cc);
-        acc[2] = fmaf(acc[2], ca, v[j][0].z * cc);
-        acc[3] = fmaf(acc[3], ca, v[j][0].w * cc);
-        acc[4] = fmaf(acc[4], ca, v[j][1].x * cc);
-        acc[5] = fmaf(acc[5], ca, v[j][1].y * cc);
-        acc[6] = fmaf(acc[6], ca, v[j][1].z * cc);
-        acc[7] = fmaf(acc[7], ca, v[j][1].w * cc);
+        float o[8];
+        if constexpr (PB16) {
+          const uint32_t w4[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            o[2 * q] = bf16_to_f32(static_cast<uint16_t>(w4[q] & 0xffffu));
+            o[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(w4[q] >> 16));
+          }
+        } else {
+          o[0] = v[j][0].x; o[1] = v[j][0].y; o[2] = v[j][0].z; o[3] = v[j][0].w;
+          o[4] = v[j][1].x; o[5] = v[j][1].y; o[6] = v[j][1].z; o[7] = v[j][1].w;
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(acc[q], ca, o[q] * cc);
       }
     }
   }
@@ -2092,8 +2123,11 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
     if (sp.S == 1 && a.dt_kv != LCA_F32)
       scope.launch(fixup_kernel, dim3(a.Tq, a.B), cb, 0, a, sp.RS, static_cast<const float*>(po),
                    static_cast<const float*>(pml));
+    else if (folds_in_kernel(a, sp))                 // attend_dma_kernel<1>: bf16 partials
+      scope.launch(combine4_kernel<true>, dim3((a.H + 3) / 4, a.Tq, a.B), dim3(256), 0, a, sp.S, sp.RS,
+                   static_cast<const float*>(po), static_cast<const float*>(pml));
     else
-      scope.launch(combine4_kernel, dim3((a.H + 3) / 4, a.Tq, a.B), dim3(256), 0, a, sp.S, sp.RS,
+      scope.launch(combine4_kernel<false>, dim3((a.H + 3) / 4, a.Tq, a.B), dim3(256), 0, a, sp.S, sp.RS,
                    static_cast<const float*>(po), static_cast<const float*>(pml));
     return hipGetLastError();
   }
