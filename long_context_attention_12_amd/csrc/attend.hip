@@ -2081,7 +2081,7 @@ void place_splits(const AttendArgs& a, SplitPlan& sp) {
   if (!folds_in_kernel(a, sp) || sp.S == 1) return;
   const int64_t items = static_cast<int64_t>(a.B) * a.Tq * sp.n_hg;
   const double rows = static_cast<double>(sp.RS) * a.D * 2;                  // one split's rows (bf16)
-  const double part = 2.0 * sp.HG * (a.D + 2) * 4;                         // its partial, out and back
+  const double part = 2.0 * sp.HG * (a.D * 2 + 8);                         // its bf16 partial + (max, sum), out and back
   const double t_one = static_cast<double>((items + kCUs - 1) / kCUs) * sp.S * rows;
   const double t_split = static_cast<double>((items * sp.S + kCUs - 1) / kCUs) * (rows + part);
   bool one = t_one <= t_split;
