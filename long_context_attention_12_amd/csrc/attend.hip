@@ -917,11 +917,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
       if (sp.S == 1) {
         write_output<D>(a, b, t, head, g, acc_o[ht], m_run[ht], z_run[ht], flag[ht], rope_tab, part_ml + 2 * part_idx);
       } else {
-        float* po = part_o + part_idx * D;
+        // bf16 partial (32-byte pieces per head: plain stores, which the L2 merges into lines)
+        uint16_t* pob = reinterpret_cast<uint16_t*>(part_o) + part_idx * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
-              make_float4(acc_o[ht][dt][0], acc_o[ht][dt][1], acc_o[ht][dt][2], acc_o[ht][dt][3]);
+          *reinterpret_cast<uint2*>(pob + 16 * dt + 4 * g) =
+              make_uint2(pack_bf16x2(acc_o[ht][dt][0], acc_o[ht][dt][1]), pack_bf16x2(acc_o[ht][dt][2], acc_o[ht][dt][3]));
         if (g == 0) {
           part_ml[2 * part_idx] = flag[ht] ? __builtin_nanf("") : m_run[ht];   // NaN: recompute in combine
           part_ml[2 * part_idx + 1] = z_run[ht];
@@ -1502,11 +1503,12 @@ __global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArg
       if (sp.S == 1) {
         write_output<D>(a, b, t, head, g, acc_o[ht], m_run[ht], z_run[ht], flag[ht], rope_tab, part_ml + 2 * part_idx);
       } else {
-        float* po = part_o + part_idx * D;
+        // bf16 partial (32-byte pieces per head: plain stores, which the L2 merges into lines)
+        uint16_t* pob = reinterpret_cast<uint16_t*>(part_o) + part_idx * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) =
-              make_float4(acc_o[ht][dt][0], acc_o[ht][dt][1], acc_o[ht][dt][2], acc_o[ht][dt][3]);
+          *reinterpret_cast<uint2*>(pob + 16 * dt + 4 * g) =
+              make_uint2(pack_bf16x2(acc_o[ht][dt][0], acc_o[ht][dt][1]), pack_bf16x2(acc_o[ht][dt][2], acc_o[ht][dt][3]));
         if (g == 0) {
           part_ml[2 * part_idx] = flag[ht] ? __builtin_nanf("") : m_run[ht];   // NaN: recompute in combine
           part_ml[2 * part_idx + 1] = z_run[ht];
@@ -2123,7 +2125,7 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
     if (sp.S == 1 && a.dt_kv != LCA_F32)
       scope.launch(fixup_kernel, dim3(a.Tq, a.B), cb, 0, a, sp.RS, static_cast<const float*>(po),
                    static_cast<const float*>(pml));
-    else if (folds_in_kernel(a, sp))                 // attend_dma_kernel<1>: bf16 partials
+    else if (a.D == 512 && a.dt_kv != LCA_F32)       // attend_dma_kernel, attend_mixed_dma_kernel: bf16 partials
       scope.launch(combine4_kernel<true>, dim3((a.H + 3) / 4, a.Tq, a.B), dim3(256), 0, a, sp.S, sp.RS,
                    static_cast<const float*>(po), static_cast<const float*>(pml));
     else
