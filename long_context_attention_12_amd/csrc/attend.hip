@@ -1970,8 +1970,14 @@ __global__ __launch_bounds__(256) void fixup_kernel(AttendArgs a, int RS, const 
 }
 
 // bf16 or mixed rows of 512 channels with a multiple of 128 heads: 32 heads per wave
+// 128 heads per workgroup (each row read once for all heads) for KV_MIXED rows
+// and for calls of 16+ queries; bf16 decode calls take 64-head groups
+// instead: the rows are read once per group, but each query needs about half
+// the splits, hence half the partials (HCA decode B = 8 at 1048576: combine
+// 12.0 -> 7.9 us at the same attention time).
 bool heads_128(const AttendArgs& a) {
-  return a.D == 512 && a.dt_q == LCA_BF16 && (a.dt_kv == LCA_BF16 || a.dt_kv == LCA_KV_MIXED) && a.H % 128 == 0;
+  return a.D == 512 && a.dt_q == LCA_BF16 && (a.dt_kv == LCA_KV_MIXED || (a.dt_kv == LCA_BF16 && a.Tq >= 16)) &&
+         a.H % 128 == 0;
 }
 
 SplitPlan make_plan(const AttendArgs& a) {
