@@ -24,8 +24,8 @@
 //   attend_mfma_kernel       bf16 rows, D <= 256: staged through registers
 //                            into a double-buffered padded tile.
 // The softmax keeps a fixed reference max per head (no rescaling of the
-// accumulators); see kHeadroom. Each split writes (max, sum, o) partials and
-// the combine kernel merges splits in a fixed order, adds the sink once,
+// accumulators); see kHeadroom. Each split writes (max, sum, o) partials (o
+// in bf16 at D = 512) and the combine kernel merges splits in a fixed order, adds the sink once,
 // divides and applies the inverse RoPE; a query whose rows form a single
 // split gets its output from the attention kernel itself. Split sizes depend
 // only on per-sequence shapes, so results are independent of the batch size.
@@ -1829,8 +1829,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int S, int R
 }
 
 // Four heads per workgroup, one wave per head: lane l owns channels
-// 8l .. 8l + 7 and streams two float4 of every split's partial, so each lane
-// keeps 2S loads in flight. A workgroup whose heads hold a flagged split (max
+// 8l .. 8l + 7 and loads them from every split's partial (two float4 in fp32,
+// one 16-byte load in bf16), up to 16 splits in flight per batch. A workgroup whose heads hold a flagged split (max
 // NaN) merges them with combine_row instead, which recomputes that split.
 template <bool PB16>
 __global__ __launch_bounds__(256) void combine4_kernel(AttendArgs a, int S, int RS,
@@ -2006,8 +2006,9 @@ SplitPlan make_plan(const AttendArgs& a) {
   }
   const int64_t win = p + 1 < a.W ? p + 1 : a.W;
   const int64_t nrows = n_ent + win;
-  // Split size: each split writes a (D+2)-float partial per head, so splits
-  // shorter than min_rows move more partial bytes than rows. With two head
+  // Split size: each split writes a D-channel partial (bf16 at D = 512, fp32
+  // otherwise) plus (max, sum) per head, so short splits move more partial
+  // bytes than rows. With two head
   // groups (128 heads) a sequence gets 16 splits (32 workgroups), so a batch of
   // 8 fills the 256 CUs in one round; with one head group, splits of 64 rows.
   int64_t RS;
@@ -2015,7 +2016,7 @@ SplitPlan make_plan(const AttendArgs& a) {
     // 128 heads per workgroup: as many workgroups per query as two 64-head
     // groups with 16 splits would give (32), at least 256 rows each; mixed
     // rows at least 512 (their tiles carry a conversion pass, and a split's
-    // fp32 partial weighs as much as 3.5 of their 576-byte rows)
+    // partial weighs as much as 1.8 of their 576-byte rows)
     RS = (nrows * a.Tq + 31) / 32;
     const int64_t rs_min = a.dt_kv == LCA_KV_MIXED ? 512 : 256;
     if (RS < rs_min) RS = rs_min;
