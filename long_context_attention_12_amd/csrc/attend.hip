@@ -1819,15 +1819,6 @@ __device__ void combine_row(const AttendArgs& a, int S, int RS, int b, int t, in
   __syncthreads();                                 // sml / lc free for the next row
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int S, int RS,
-                                                      const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml) {
-  __shared__ float sml[2 * 256];
-  __shared__ float red[4];
-  __shared__ float lc[kCombMaxRows];
-  combine_row(a, S, RS, blockIdx.z, blockIdx.y, blockIdx.x, part_o, part_ml, sml, red, lc);
-}
-
 // Four heads per workgroup, one wave per head: lane l owns channels
 // 8l .. 8l + 7 and loads them from every split's partial (two float4 in fp32,
 // one 16-byte load in bf16), up to 16 splits in flight per batch. A workgroup whose heads hold a flagged split (max
