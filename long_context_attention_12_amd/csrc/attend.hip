@@ -42,6 +42,7 @@ typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));   // 16-byte stre
 struct SplitPlan {
   int S, RS, n_hg, HG;
   int SPW;                     // splits per workgroup: 1, or S (one workgroup per query and head group)
+  int xcd;                     // 1: one-dimensional grid, each sequence's workgroups on one XCD
 };
 
 struct RowSpan {
@@ -482,6 +483,24 @@ __device__ __forceinline__ bool work_item(const SplitPlan& sp, int Tq, int i, in
   return true;
 }
 
+// Workgroup -> (split, head group, query, sequence). With sp.xcd the grid is
+// one-dimensional: the dispatcher hands workgroup i to XCD i % 8, and every
+// workgroup of sequence b gets i % 8 == b % 8, so all of b's workgroups share
+// one L2 (and the top-k workgroup of b at decode, which wrote b's selected
+// indices, ran there too). Otherwise the grid is (units, 1, B).
+__device__ __forceinline__ bool work_item_b(const SplitPlan& sp, int Tq, int& split, int& hg, int& t, int& b) {
+  int64_t x;
+  if (sp.xcd) {
+    const int64_t i = blockIdx.x, slot = i >> 3, W = work_blocks(sp, Tq);
+    b = static_cast<int>((i & 7) + 8 * (slot / W));
+    x = slot % W;
+  } else {
+    x = blockIdx.x;
+    b = blockIdx.z;
+  }
+  return work_item(sp, Tq, static_cast<int>(x), split, hg, t);
+}
+
 // A query's only split is its whole row set: the head's output is final here.
 // Accumulators are relative to the fixed reference m_run; with M = max(sink,
 // m_run), out = o e^(m_run - M) / (z e^(m_run - M) + e^(sink - M)), then the
@@ -600,8 +619,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_mfma_kernel(AttendArgs a, 
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
   const int g = lane >> 4, r16 = lane & 15;
   int split, hg, t;
-  if (!work_item(sp, a.Tq, blockIdx.x, split, hg, t)) return;
-  const int b = blockIdx.z;
+  int b;
+  if (!work_item_b(sp, a.Tq, split, hg, t, b)) return;
   const bool active = wid * 16 < sp.HG;
   const int head = hg * sp.HG + wid * 16 + r16;
   const RowSpan rs = row_span(a, b, t);
@@ -735,8 +754,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
   const int g = lane >> 4, r16 = lane & 15;
   int split, hg, t;
-  if (!work_item(sp, a.Tq, blockIdx.x, split, hg, t)) return;
-  const int b = blockIdx.z;
+  int b;
+  if (!work_item_b(sp, a.Tq, split, hg, t, b)) return;
   const bool active = wid * 16 * NHT < sp.HG;
   const int head0 = hg * sp.HG + wid * 16 * NHT + r16;   // + 16 ht for head tile ht
   const RowSpan rs = row_span(a, b, t);
@@ -963,8 +982,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_fold_kernel(AttendArgs
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform in a scalar register
   const int g = lane >> 4, r16 = lane & 15;
   int split0, hg, t;
-  if (!work_item(sp, a.Tq, blockIdx.x, split0, hg, t)) return;
-  const int b = blockIdx.z;
+  int b;
+  if (!work_item_b(sp, a.Tq, split0, hg, t, b)) return;
   const bool active = wid * 16 < sp.HG;
   const int head = hg * sp.HG + wid * 16 + r16;
   const RowSpan rs = row_span(a, b, t);
@@ -1388,8 +1407,8 @@ __global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArg
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   int split, hg, t;
-  if (!work_item(sp, a.Tq, blockIdx.x, split, hg, t)) return;
-  const int b = blockIdx.z;
+  int b;
+  if (!work_item_b(sp, a.Tq, split, hg, t, b)) return;
   const bool active = wid * 16 * NHT < sp.HG;
   const int head0 = hg * sp.HG + wid * 16 * NHT + r16;   // + 16 ht for head tile ht
   const RowSpan rs = row_span(a, b, t);
@@ -2032,12 +2051,15 @@ SplitPlan make_plan(const AttendArgs& a) {
   sp.S = static_cast<int>(S);
   sp.RS = static_cast<int>(RS);
   sp.SPW = 1;
+  sp.xcd = 0;
   return sp;
 }
 
 template <int D>
 void launch_mfma_d(LaunchScope& sc, const AttendArgs& a, const SplitPlan& sp, float* po, float* pml) {
-  dim3 grid(static_cast<uint32_t>(work_blocks(sp, a.Tq)), 1, a.B), block(kAttThreads);
+  const int64_t W = work_blocks(sp, a.Tq);
+  const dim3 grid = sp.xcd ? dim3(static_cast<uint32_t>(W * a.B), 1, 1) : dim3(static_cast<uint32_t>(W), 1, a.B);
+  const dim3 block(kAttThreads);
   if constexpr (D == 512) {                        // KV_MIXED rows exist only at D = 512
     if (a.dt_kv == LCA_KV_MIXED && sp.HG == 128)
       sc.launch(attend_mixed_dma_kernel<2>, grid, block, 0, a, sp, po, pml);
@@ -2093,7 +2115,12 @@ void place_splits(const AttendArgs& a, SplitPlan& sp) {
 hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
   SplitPlan sp = make_plan(a);
   place_splits(a, sp);
-  if (work_blocks(sp, a.Tq) > 2147483647LL) return hipErrorInvalidConfiguration;
+  // 128-head workgroups in batches that fill every XCD: each sequence's
+  // workgroups on one XCD, so its 128 query rows (128 KB) are fetched into one
+  // L2 for all of its splits (mixed pair B = 64: hca_attend 354 -> 316 us; the
+  // 64-head decode shapes measured slower this way)
+  sp.xcd = a.B >= 8 && a.B % 8 == 0 && a.dt_kv != LCA_F32 && sp.HG == 128;
+  if (work_blocks(sp, a.Tq) * a.B > 2147483647LL) return hipErrorInvalidConfiguration;
   const size_t rows = static_cast<size_t>(a.B) * a.Tq * a.H * sp.S;
   float* po = static_cast<float*>(ws);
   float* pml = po + rows * a.D;

@@ -155,3 +155,41 @@ def test_automatic_placement_follows_the_batch_not_the_bits():
         o1, _ = _run(L, "csa", q_d[b:b + 1], E_d[b:b + 1], idx_d[b:b + 1], win_d[b:b + 1], sink_d, m, W, q_pos0, 0,
                      q_pos=qp[b:b + 1])
         assert torch.equal(o1[0], o_r[b]), f"ragged sequence {b} differs"
+
+
+@pytest.mark.parametrize("kind,H,B,Tq", [("csa", 64, 16, 1), ("hca", 128, 8, 16), ("csa", 128, 16, 16)])
+def test_sequence_major_grid_keeps_the_bits(kind, H, B, Tq):
+    # 128-head workgroups (16+ queries per call) in batches of a multiple of 8
+    # sequences run on one-dimensional grids that keep each sequence's
+    # workgroups on one XCD; other calls on the (units, 1, B) grid. The mapping
+    # moves work, never arithmetic: a sequence gives the same bits alone and
+    # in the batch.
+    L = need_gpu()
+    rng = np.random.default_rng(190 + H + Tq)
+    D, W, k = 512, 128, 300
+    m = 4 if kind == "csa" else 128
+    q_pos0 = 4 * 2000 + 1 if kind == "csa" else 128 * 600 + 7
+    N_cap = (q_pos0 + Tq) // m
+    q, E, win, sink = _case(rng, B, Tq, H, D, N_cap, W, 5.0)
+    idx_d = None
+    idx = None
+    if kind == "csa":
+        nv = O.n_visible(q_pos0, m)
+        idx = np.stack([np.stack([np.sort(rng.choice(nv, size=k, replace=False)) for _ in range(Tq)])
+                        for _ in range(B)]).astype(np.int32)
+        idx_d = torch.from_numpy(idx).to(DEV)
+    q_d, E_d, win_d, sink_d = dev_bf16(q), dev_bf16(E), dev_bf16(win), dev_f32(sink)
+    say(f"sequence-major grid {kind} H={H} B={B} Tq={Tq}: the batch against single sequences")
+    o_all, l_all = _run(L, kind, q_d, E_d, idx_d, win_d, sink_d, m, W, q_pos0, 0)
+    for b in (0, 5, B - 1):
+        sl = slice(b, b + 1)
+        o1, l1 = _run(L, kind, q_d[sl], E_d[sl], idx_d[sl] if idx_d is not None else None, win_d[sl], sink_d, m, W,
+                      q_pos0, 0)
+        assert torch.equal(o1[0], o_all[b]), f"sequence {b}: the batch differs from the sequence alone"
+        assert torch.equal(l1[0], l_all[b])
+    b = B - 2
+    if kind == "csa":
+        ref, _ = O.csa_attend(q[b], E[b], idx[b], win[b], sink, 1 / math.sqrt(D), q_pos0, W, True, 10000.0, 64)
+    else:
+        ref, _ = O.hca_attend(q[b], E[b], m, win[b], sink, 1 / math.sqrt(D), q_pos0, W, True, 10000.0, 64)
+    row_tol_check(host(o_all)[b], ref, 2e-2, f"batch of {B}, sequence {b}")
