@@ -43,6 +43,7 @@ struct SplitPlan {
   int S, RS, n_hg, HG;
   int SPW;                     // splits per workgroup: 1, or S (one workgroup per query and head group)
   int xcd;                     // 1: one-dimensional grid, each sequence's workgroups on one XCD
+  int qmaj;                    // 1: each XCD takes a contiguous range of the units (queries)
 };
 
 struct RowSpan {
@@ -483,7 +484,16 @@ __device__ __forceinline__ bool work_item(const SplitPlan& sp, int Tq, int i, in
   return true;
 }
 
-// Workgroup -> (split, head group, query, sequence). With sp.xcd the grid is
+// Units per XCD when each XCD takes a contiguous range (sp.qmaj): whole
+// groups of 16, so the two head groups of a unit (8 apart) stay together.
+__host__ __device__ __forceinline__ int64_t qmaj_per(const SplitPlan& sp, int Tq) {
+  return (work_blocks(sp, Tq) + 127) / 128 * 16;
+}
+
+// Workgroup -> (split, head group, query, sequence). With sp.qmaj (calls of
+// many queries, one sequence) XCD c takes the c-th eighth of the units, so
+// neighbouring queries, whose window rows and many of whose selected rows
+// coincide, gather through the same L2. With sp.xcd the grid is
 // one-dimensional: the dispatcher hands workgroup i to XCD i % 8, and every
 // workgroup of sequence b gets i % 8 == b % 8, so all of b's workgroups share
 // one L2 (and the top-k workgroup of b at decode, which wrote b's selected
@@ -494,6 +504,11 @@ __device__ __forceinline__ bool work_item_b(const SplitPlan& sp, int Tq, int& sp
     const int64_t i = blockIdx.x, slot = i >> 3, W = work_blocks(sp, Tq);
     b = static_cast<int>((i & 7) + 8 * (slot / W));
     x = slot % W;
+  } else if (sp.qmaj) {
+    const int64_t i = blockIdx.x;
+    x = (i & 7) * qmaj_per(sp, Tq) + (i >> 3);
+    b = blockIdx.z;
+    if (x >= work_blocks(sp, Tq)) return false;
   } else {
     x = blockIdx.x;
     b = blockIdx.z;
@@ -2052,13 +2067,16 @@ SplitPlan make_plan(const AttendArgs& a) {
   sp.RS = static_cast<int>(RS);
   sp.SPW = 1;
   sp.xcd = 0;
+  sp.qmaj = 0;
   return sp;
 }
 
 template <int D>
 void launch_mfma_d(LaunchScope& sc, const AttendArgs& a, const SplitPlan& sp, float* po, float* pml) {
   const int64_t W = work_blocks(sp, a.Tq);
-  const dim3 grid = sp.xcd ? dim3(static_cast<uint32_t>(W * a.B), 1, 1) : dim3(static_cast<uint32_t>(W), 1, a.B);
+  const dim3 grid = sp.xcd    ? dim3(static_cast<uint32_t>(W * a.B), 1, 1)
+                    : sp.qmaj ? dim3(static_cast<uint32_t>(8 * qmaj_per(sp, a.Tq)), 1, a.B)
+                              : dim3(static_cast<uint32_t>(W), 1, a.B);
   const dim3 block(kAttThreads);
   if constexpr (D == 512) {                        // KV_MIXED rows exist only at D = 512
     if (a.dt_kv == LCA_KV_MIXED && sp.HG == 128)
@@ -2120,6 +2138,7 @@ hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
   // L2 for all of its splits (mixed pair B = 64: hca_attend 354 -> 316 us; the
   // 64-head decode shapes measured slower this way)
   sp.xcd = a.B >= 8 && a.B % 8 == 0 && a.dt_kv != LCA_F32 && sp.HG == 128;
+  sp.qmaj = !sp.xcd && a.B == 1 && a.Tq >= 64 && a.dt_kv != LCA_F32;
   if (work_blocks(sp, a.Tq) * a.B > 2147483647LL) return hipErrorInvalidConfiguration;
   const size_t rows = static_cast<size_t>(a.B) * a.Tq * a.H * sp.S;
   float* po = static_cast<float*>(ws);
