@@ -133,16 +133,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---- RoPE ----------------------------------------------------------------------
-// Angle of pair i (of R/2) at position pos, reduced to [-pi, pi] in double so
-// that positions near 2^20 keep full float32 accuracy in sin/cos.
+// Angle of pair i (of R/2) at position pos: frequency and product in double,
+// reduced to [-pi, pi] in double so that positions near 2^20 keep full float32
+// accuracy; sin and cos of the reduced angle in float32 (within a few ulp of
+// the double values, and off the fp64 transcendental path, which sat on the
+// critical path of the kernels that build these tables).
 __device__ __forceinline__ void rope_sincos(double pos, int i, int R, double base,
                                             float* s, float* c) {
   double freq = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(R));
   double ang = pos * freq;
   const double two_pi = 6.283185307179586476925286766559;
   ang = ang - two_pi * rint(ang / two_pi);
-  *s = static_cast<float>(sin(ang));
-  *c = static_cast<float>(cos(ang));
+  const float a = static_cast<float>(ang);
+  *s = sinf(a);
+  *c = cosf(a);
 }
 
 __host__ __device__ __forceinline__ int64_t n_visible(int64_t p, int m) { return (p + 1) / m; }
