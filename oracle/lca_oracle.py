@@ -39,6 +39,7 @@ __all__ = [
     "csa_attend",
     "hca_attend",
     "bf16_round",
+    "bf16_next",
     "e4m3fn_encode",
     "e4m3fn_decode",
     "kv_mixed_quantize",
@@ -234,6 +235,14 @@ def compress_epilogue(entries, pos0, m, norm_w=None, eps=1e-6, rope_base=None,
     Order (reading): merge -> RMSNorm -> RoPE at the block start position
     ``pos0 + j*m``. [Qiaomu] 混合注意力机制 (normalised entries, partial RoPE),
     [cdjax] §1.1 (RoPE on the last 64 channels).
+
+    Pinned by: chunked calls (pos0 = T1 with the overlap carried) equal one
+    call; entry j of a constant sequence equals the row rotated to pos0 + j*m
+    by an independent complex-exponential rotation, and its dot with a query
+    depends only on the relative position; rotating the output back gives a
+    row parallel to g * e with unit RMS after dividing by g (norm before
+    RoPE under a non-uniform gain); unit gain keeps unit RMS
+    (tests/test_oracle_compress.py).
     """
     e = np.array(entries, dtype=np.float64, copy=True)
     for j in range(e.shape[0]):
@@ -308,8 +317,8 @@ def topk_classes(scores, k, tau_rel=1e-3, bf16_scores=False, mid_rel=1e-5):
         kth = sb[order[k_eff - 1]]
         amb = sb == kth
         # neighbours of kth on the bf16 grid and the midpoints between them
-        up = _bf16_next(kth, +1)
-        dn = _bf16_next(kth, -1)
+        up = bf16_next(kth, +1)
+        dn = bf16_next(kth, -1)
         for mid in (0.5 * (kth + up), 0.5 * (kth + dn)):
             amb |= np.abs(s - mid) <= mid_rel * max(abs(mid), 1e-30)
         cin = (sb > kth) & ~amb
@@ -560,7 +569,7 @@ def bf16_round(x):
     return np.copysign(q, x)
 
 
-def _bf16_next(v, direction):
+def bf16_next(v, direction):
     """Neighbouring bfloat16 value of bf16 value ``v`` (direction +1 / -1)."""
     v = float(v)
     if v == 0.0:
@@ -625,10 +634,17 @@ def kv_mixed_quantize(rows, rope_dims=64):
 
     [cdjax] §1.1: RoPE channels stay in BF16, the other channels go to FP8;
     with the FP4 indexer this brings the KV cache to about 2% of a BF16 GQA8
-    cache. Reading: one fp32 scale per row, s = amax / 448 over the non-RoPE
-    channels, computed in float32 like the kernel (s = 1 when amax = 0); each
-    non-RoPE channel stores e4m3fn(float32(x / s)); RoPE channels store
-    bf16(x). Input rows are float32 values.
+    cache. Reading (the pages fix neither the scale granularity nor its
+    precision): one float32 scale per row, s = amax / 448 over the non-RoPE
+    channels (s = 1 when amax = 0), a float32 quantity because it is stored
+    as float32; each non-RoPE channel stores e4m3fn(float32(x / s)), the
+    quotient taken as one IEEE float32 division so that the stored code is a
+    function of the stored scale alone; RoPE channels store bf16(x). Input
+    rows are float32 values.
+
+    Pinned by: the scale and codes of hand-built rows (amax exactly 448,
+    zero rows, a row whose amax sits on one channel) and the decode bound
+    |x - decode| <= half an e4m3 step times s (tests/test_oracle_quant.py).
 
     Returns (fp8 codes [N, D-R] uint8, bf16 values [N, R] float64,
     scale [N] float32).

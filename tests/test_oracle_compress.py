@@ -215,3 +215,100 @@ def test_rms_norm_unit_rms():
     assert abs(np.sqrt(np.mean(y * y)) - 1.0) < 1e-14
     g = rng.standard_normal(64)
     np.testing.assert_allclose(O.rms_norm(x, g, 0.0), y * g, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Epilogue: merge -> RMSNorm -> RoPE at the block start pos0 + j*m
+# ([Qiaomu] 混合注意力机制: normalised entries; [cdjax] §1.1: RoPE on the last
+# 64 channels). Each test fails for a plausible slip: RoPE at j (or pos0 + j)
+# instead of pos0 + j*m, the chunk offset pos0 dropped, RoPE applied before
+# the norm under a gain that differs across the rotated channels, or a
+# rotation that does not preserve the row's norm.
+# ---------------------------------------------------------------------------
+
+def _rope_ref(x, pos, base, R):
+    """The rotation written from its complex-exponential definition, apart
+    from the oracle: pair (u, v) = u + iv of the last R channels times
+    exp(i * pos * base**(-2i/R))."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    D = y.shape[-1]
+    z = y[..., D - R::2] + 1j * y[..., D - R + 1::2]
+    z = z * np.exp(1j * pos * base ** (-np.arange(0, R, 2) / R))
+    y[..., D - R::2] = z.real
+    y[..., D - R + 1::2] = z.imag
+    return y
+
+
+@pytest.mark.parametrize("T1", [4, 12, 20])
+def test_epilogue_chunked_equals_one_shot(T1):
+    # Compress + epilogue over [0, T1) at pos0 = 0, then over [T1, T) at
+    # pos0 = T1 with stream a's last block carried, equals one call over
+    # [0, T). A RoPE position that ignores pos0 or scales j by anything but m
+    # breaks the second chunk.
+    rng = np.random.default_rng(70)
+    T, D, m, R, base = 32, 16, 4, 8, 10000.0
+    ca, za = _rand(rng, T, D)
+    cb, zb = _rand(rng, T, D)
+    g = 0.5 + rng.random(D)
+    ep = dict(norm_w=g, eps=1e-6, rope_base=base, rope_dims=R)
+    full = O.compress_epilogue(O.compress_sequence(cb, zb, m, ca, za), 0, m, **ep)
+    first = O.compress_epilogue(O.compress_sequence(cb[:T1], zb[:T1], m, ca[:T1], za[:T1]), 0, m, **ep)
+    second = O.compress_epilogue(
+        O.compress_sequence(cb[T1:], zb[T1:], m, ca[T1:], za[T1:], prev_ca=ca[T1 - m:T1],
+                            prev_za=za[T1 - m:T1]), T1, m, **ep)
+    np.testing.assert_allclose(np.concatenate([first, second]), full, atol=1e-13)
+
+
+@pytest.mark.parametrize("m", [4, 128])
+def test_epilogue_entry_sits_at_block_start(m):
+    # A constant sequence compresses to itself, so every entry is the same
+    # row before RoPE; after the epilogue, entry j's dot with a query rotated
+    # to position p depends only on p - (pos0 + j*m). Checked against the
+    # complex-exponential rotation written above, not the oracle's own.
+    rng = np.random.default_rng(71)
+    D, R, base, pos0 = 16, 8, 10000.0, 1048576
+    n = 6
+    T = n * m
+    c = rng.standard_normal(D)
+    rows = np.tile(c, (T, 1))
+    e = O.compress_sequence(rows, rng.standard_normal(T), m, overlap=False)
+    out = O.compress_epilogue(e, pos0, m, norm_w=None, rope_base=base, rope_dims=R)
+    for j in range(n):
+        np.testing.assert_allclose(out[j], _rope_ref(c, pos0 + j * m, base, R), atol=1e-9)
+    q = rng.standard_normal(D)
+    delta = 3 * m + 1
+    dots = [out[j] @ _rope_ref(q, pos0 + j * m + delta, base, R) for j in range(n)]
+    np.testing.assert_allclose(dots, dots[0], atol=1e-9)
+    # the same dot at a position one token off differs (the test can see a shift)
+    off = out[2] @ _rope_ref(q, pos0 + 2 * m + delta + 1, base, R)
+    assert abs(off - dots[0]) > 1e-6
+
+
+def test_epilogue_norm_before_rope_under_nonuniform_gain():
+    # Rotating the output back by -(pos0 + j*m) must give g * e / rms(e): a
+    # row parallel to g * e whose entry-wise ratio to g has unit RMS (eps 0).
+    # With RoPE before the norm, a gain that differs between the two channels
+    # of a rotated pair would leave a different row.
+    rng = np.random.default_rng(72)
+    D, R, m, pos0, base = 32, 16, 4, 4096, 10000.0
+    e = rng.standard_normal((5, D)) * 3
+    g = np.linspace(0.25, 4.0, D)
+    out = O.compress_epilogue(e, pos0, m, norm_w=g, eps=0.0, rope_base=base, rope_dims=R)
+    for j in range(5):
+        back = _rope_ref(out[j], -(pos0 + j * m), base, R)
+        u = back / g
+        assert abs(np.sqrt(np.mean(u * u)) - 1.0) < 1e-12
+        np.testing.assert_allclose(u * np.sqrt(np.mean(e[j] ** 2)), e[j], atol=1e-12)
+    # the other order gives another row (the test discriminates)
+    wrong = O.rms_norm(_rope_ref(e[1], pos0 + m, base, R), g, 0.0)
+    assert np.max(np.abs(wrong - out[1])) > 1e-3
+
+
+def test_epilogue_unit_gain_keeps_unit_rms():
+    # RMSNorm with unit gain, then a rotation: the output RMS stays 1.
+    rng = np.random.default_rng(73)
+    e = rng.standard_normal((7, 64)) * 11
+    out = O.compress_epilogue(e, 128, 4, norm_w=np.ones(64), eps=0.0, rope_base=10000.0, rope_dims=64)
+    np.testing.assert_allclose(np.sqrt(np.mean(out ** 2, axis=1)), 1.0, atol=1e-13)
+    # and without norm or RoPE the epilogue is the identity
+    np.testing.assert_array_equal(O.compress_epilogue(e, 128, 4), e)

@@ -118,3 +118,32 @@ def test_storage_layout_matches_two_percent_figure():
     # an all-bf16 layout would be twice as large: the fp8/fp4 formats matter
     pct_bf16 = 100 * ((D * 2 + dI * 2) / m + D * 2 / m2) / 2 / gqa8
     assert pct_bf16 > 3.5
+
+
+@pytest.mark.parametrize("v", [1.0, 2.0, 0.5, 2.0 ** -100, 3.0, 0.99609375, -1.0, -6.0, 2.0 ** -126])
+def test_bf16_neighbours_match_torch_nextafter(v):
+    # The bf16 ambiguity band of the top-k classes is built on the neighbours
+    # of the k-th score. At a power of two the step below is half the step
+    # above; torch's nextafter on bfloat16 fixes both independently.
+    t = torch.tensor([v], dtype=torch.bfloat16)
+    up = torch.nextafter(t, torch.tensor([1e30], dtype=torch.bfloat16)).double().item()
+    dn = torch.nextafter(t, torch.tensor([-1e30], dtype=torch.bfloat16)).double().item()
+    assert O.bf16_next(v, +1) == up
+    assert O.bf16_next(v, -1) == dn
+
+
+def test_kv_mixed_hand_built_rows():
+    # Rows whose codes follow from the e4m3fn table by hand: an amax of
+    # exactly 448 gives scale 1 and stores the channels themselves; a zero
+    # row takes scale 1 and all-zero codes; the channel that holds the amax
+    # always stores +-448 (code 0x7E / 0xFE), whatever the scale.
+    rows = np.zeros((3, 512), np.float32)
+    rows[0, :4] = [448.0, -1.0, 0.5, 2.0 ** -9]
+    rows[0, 448:] = 1.0 + 2.0 ** -8                      # a bf16 tie: rounds to 1.0
+    rows[2, :448] = np.linspace(-0.01, 0.02, 448, dtype=np.float32)
+    codes, rope, s = O.kv_mixed_quantize(rows)
+    assert s[0] == 1.0 and s[1] == 1.0
+    assert list(codes[0, :4]) == [0x7E, 0xB8, 0x30, 0x01]
+    assert np.all(codes[1] == 0) and np.all(rope[1] == 0)
+    np.testing.assert_array_equal(rope[0], 1.0)
+    assert codes[2, 447] == 0x7E and s[2] == np.float32(np.float32(0.02) / np.float32(448))
