@@ -262,8 +262,10 @@ def timed(step, steps, warmup):
 
 
 def kernel_times(step, steps):
-    """Average per-launch duration of each library kernel, from HIP events the
-    library records around its launches on the caller's stream."""
+    """Per-kernel durations from HIP events the library records around its
+    launches on the caller's stream: launches per step, the average duration
+    of one launch, and the time per step (a chunked call launches a kernel
+    several times per step)."""
     torch.cuda.synchronize()
     L.lca_profile_collect()
     L.lca_profile_enable(True)
@@ -272,7 +274,18 @@ def kernel_times(step, steps):
     torch.cuda.synchronize()
     L.lca_profile_enable(False)
     stats = L.lca_profile_collect()
-    return {name: {"launches": n, "avg_us": 1e3 * ms / n} for name, (n, ms) in stats.items()}
+    return {name: {"launches_per_step": n / steps, "avg_us": 1e3 * ms / n, "us_per_step": 1e3 * ms / steps}
+            for name, (n, ms) in stats.items()}
+
+
+def per_step(kt, nd=3):
+    """{kernel: microseconds per step} (the sum over a step's launches)."""
+    return {k: round(v["us_per_step"], nd) for k, v in kt.items()}
+
+
+def launches(kt):
+    """{kernel: launches per step}."""
+    return {k: v["launches_per_step"] for k, v in kt.items()}
 
 
 def csa_decode_bytes(d):
@@ -358,9 +371,9 @@ def decode_state_leg(d, copies, steps, warmup, headline_ms):
     progress(f"csa decode step with state updates: {ms:.4f} ms/step ({ms_sep:.4f} with separate appends)")
     return {"workload": "csa_decode_step_with_state_b16_ctx131072", "tokens_per_s": B / (ms * 1e-3),
             "ms_per_step": ms, "headline_ms": headline_ms, "state_update_ms": ms - headline_ms,
-            "kernels_us": {k_: round(v["avg_us"], 3) for k_, v in kt.items()},
+            "kernels_us": per_step(kt, 3),
             "separate_appends": {"ms_per_step": ms_sep,
-                                 "kernels_us": {k_: round(v["avg_us"], 3) for k_, v in kt_sep.items()}}}
+                                 "kernels_us": per_step(kt_sep, 3)}}
 
 
 def placement_leg(batches=(16, 64, 256, 512), steps=50, warmup=5, ctx=131072, H=64, D=512, k=512, W=128, m=4):
@@ -390,7 +403,7 @@ def placement_leg(batches=(16, 64, 256, 512), steps=50, warmup=5, ctx=131072, H=
                              scale=1 / math.sqrt(D), flags=L.INV_ROPE | fl, rope_dims=64, ws=ws)
             us = 1e6 * timed(step, steps, warmup) / steps
             kt = kernel_times(step, steps)
-            row[name] = {"us_per_call": round(us, 2), "kernels_us": {k_: round(v["avg_us"], 2) for k_, v in kt.items()}}
+            row[name] = {"us_per_call": round(us, 2), "kernels_us": per_step(kt, 2)}
         rows_bytes = B * (k + W) * D * 2
         for v in row.values():
             v["rows_GBs"] = round(rows_bytes / (v["us_per_call"] * 1e-6) / 1e9, 1)
@@ -435,7 +448,7 @@ def outproj_leg(steps=50, warmup=5):
         abytes = wbytes + 2 * (T * n_h * c + 2 * T * g * d_g + T * d_model)
         flops = 2.0 * T * (g * d_g * kg + d_model * g * d_g)
         res[name] = {"rows": T, "us_per_call": round(us, 2), "weight_copies_rotated": copies,
-                     "kernels_us": {k_: round(v["avg_us"], 2) for k_, v in kt.items()},
+                     "kernels_us": per_step(kt, 2),
                      "algorithmic_bytes": abytes, "achieved_GBs": round(abytes / (us * 1e-6) / 1e9, 1),
                      "hbm_frac": round(abytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
                      "flops": flops, "achieved_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
@@ -482,7 +495,7 @@ def backward_leg(T=4096, H=64, D=512, k=512, W=128, m=4, H_I=4, d_I=128, reps=5)
     flops = 2.0 * rows * H * D * 5                  # S, dP, dq (query side) + two head sums (row side)
     progress(f"csa attend backward T={T}: {ms:.3f} ms")
     return {"workload": "csa_attend_backward_t4096_flash", "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
-            "kernels_us": {k_: round(v["avg_us"], 1) for k_, v in kt.items()}, "rows_read": rows, "flops": flops,
+            "kernels_us": per_step(kt, 1), "rows_read": rows, "flops": flops,
             "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_bf16_frac": flops / (ms * 1e-3) / 2.5e15,
             "workspace_bytes": need}
 
@@ -513,7 +526,7 @@ def ragged_leg(d, copies, steps, warmup, seed, uniform_ms):
     return {"tokens_per_s": d["B"] / (rms * 1e-3), "ms_per_step": rms,
             "mean_context": float(np.mean(pos)), "bound": d["q_pos0"],
             "uniform_at_bound_ms": uniform_ms, "speedup_vs_uniform_at_bound": uniform_ms / rms,
-            "kernels_us": {k: round(v["avg_us"], 3) for k, v in rk.items()},
+            "kernels_us": per_step(rk, 3),
             "algorithmic_bytes": rb, "achieved_GBs": rb / (rms * 1e-3) / 1e9,
             "hbm_frac": rb / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
@@ -701,7 +714,8 @@ def main():
         "step_roofline": {"algorithmic_bytes": ib + ab,
                           "achieved_GBs": (ib + ab) / (ms * 1e-3) / 1e9,
                           "frac": (ib + ab) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-        "kernels_us": {k: round(v["avg_us"], 3) for k, v in kt.items()},
+        "kernels_us": per_step(kt, 3),
+        "kernel_launches_per_step": launches(kt),
         # secondary statistic: recall of the bf16-score top-k against the fp32-score top-k
         # (the pages report 99.7% on real-model data; here seeded synthetic inputs)
         "bf16_score_topk_recall": {"csa_decode": step.recall(), "pages": 0.997},
@@ -727,7 +741,7 @@ def main():
         att = hk.get("hca_attend", {"avg_us": float("nan")})["avg_us"]
         result["secondary"] = {
             "workload": "hca_decode_b8_ctx1048576", "tokens_per_s": h["B"] / (hms * 1e-3),
-            "ms_per_step": hms, "kernels_us": {k: round(v["avg_us"], 3) for k, v in hk.items()},
+            "ms_per_step": hms, "kernels_us": per_step(hk, 3),
             "hca_attend_GBs": hb / (att * 1e-6) / 1e9, "hca_attend_hbm_frac": hb / (att * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "hca_attend_TFLOPs": hf / (att * 1e-6) / 1e12, "mfma_bf16_frac": hf / (att * 1e-6) / 2.5e15,
             "algorithmic_bytes": hb, "flops": hf,
@@ -746,7 +760,7 @@ def main():
         progress(f"csa prefill: {pms:.3f} ms/step")
         result["prefill"] = {
             "workload": "csa_prefill_tq4096_ctx1048576", "tokens_per_s": 4096 / (pms * 1e-3),
-            "ms_per_step": pms, "kernels_us": {k: round(v["avg_us"], 3) for k, v in pk.items()},
+            "ms_per_step": pms, "kernels_us": per_step(pk, 3), "kernel_launches_per_step": launches(pk),
             "flops": pflops, "achieved_TFLOPs": pflops / (pms * 1e-3) / 1e12,
             "mfma_bf16_frac": pflops / (pms * 1e-3) / 2.5e15,
         }
@@ -759,7 +773,7 @@ def main():
         progress(f"mixed pair: {mms:.4f} ms/step")
         result["mixed_pair"] = {
             "workload": "mixed_csa_hca_pair_b64_ctx1048576", "tokens_per_s": 64 / (mms * 1e-3),
-            "ms_per_step": mms, "kernels_us": {k: round(v["avg_us"], 3) for k, v in mk.items()},
+            "ms_per_step": mms, "kernels_us": per_step(mk, 3),
             "algorithmic_bytes": mbytes, "flops": mflops,
             "achieved_GBs": mbytes / (mms * 1e-3) / 1e9, "hbm_frac": mbytes / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         }
