@@ -290,6 +290,31 @@ int csa_attend(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, i
                void* out, float* lse_out, void* ws, size_t ws_bytes);
 
 /* ---------------------------------------------------------------------------
+ * csa_attend_noalloc — csa_attend for callers that cannot allocate.
+ *
+ * For code that may not call hipMalloc or take a workspace: work under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The
+ * arguments, layouts, requirements, results and errors are those of
+ * csa_attend (same kernels, same bits) without ws / ws_bytes: the split
+ * partials go to a static device array of 64 MiB (LCA_NOALLOC_SCRATCH_BYTES)
+ * inside the library, one per GPU, held until the process ends. A call whose
+ * csa_attend_workspace() exceeds that size returns LCA_ERR_WORKSPACE and
+ * enqueues nothing (at the CSA decode shape, H = 64, D = 512, k = 512 at
+ * 131072 tokens, up to 51 sequences fit). The call allocates nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (two streams, two threads) race on it and must be serialised by
+ * the caller. Nothing in the array needs to start at zero; each call writes
+ * every partial it reads.
+ * ------------------------------------------------------------------------- */
+#define LCA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int csa_attend_noalloc(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap,
+                       int m, int k, int W, int64_t q_pos0,
+                       const void* q, const void* kv, const float* kv_scale, const int32_t* idx,
+                       const void* win, const float* win_scale, const float* sink, float scale,
+                       uint32_t flags, float rope_base, int rope_dims,
+                       void* out, float* lse_out);
+
+/* ---------------------------------------------------------------------------
  * hca_attend — HCA dense attention over every visible entry + window + sink.
  *
  * [PACMAN] §3.2 and [kwkr] §3.2: no sparse selection; dense multi-query

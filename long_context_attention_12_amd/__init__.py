@@ -20,7 +20,7 @@ __all__ = [
     "LcaError", "lib", "lib_path",
     "csa_compress", "lca_quantize_rows",
     "csa_index_topk", "csa_index_topk_workspace",
-    "csa_attend", "csa_attend_workspace",
+    "csa_attend", "csa_attend_workspace", "csa_attend_noalloc",
     "hca_attend", "hca_attend_workspace",
     "lca_version", "lca_profile_enable", "lca_profile_collect",
 ]
@@ -75,6 +75,9 @@ def _declare(L):
     L.csa_attend.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, i64, vp, vp, vp, vp,
                              vp, vp, vp, f32, u32, f32, i32, vp, vp, vp, sz]
     L.csa_attend.restype = i32
+    L.csa_attend_noalloc.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i32, i64, vp, vp, vp, vp,
+                                     vp, vp, vp, f32, u32, f32, i32, vp, vp]
+    L.csa_attend_noalloc.restype = i32
     L.hca_attend_workspace.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, i32, i64]
     L.hca_attend_workspace.restype = sz
     L.hca_attend.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, i32, i32, i64, vp, vp, vp, vp, vp,
@@ -547,6 +550,26 @@ def csa_attend(dt_q, dt_kv, q, kv, idx, win, sink, out, *, m, W, q_pos0, scale, 
     _check(lib().csa_attend(_stream(stream), dt_q, dt_kv, B, Tq, H, D, N_cap, m, k, W, q_pos0,
                             _p(q), _p(kv), _p(kv_scale), _p(idx), _p(win), _p(win_scale), _p(sink),
                             scale, flags, rope_base, rope_dims, _p(out), _p(lse_out), _p(ws), ws_bytes))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def csa_attend_noalloc(dt_q, dt_kv, q, kv, idx, win, sink, out, *, m, W, q_pos0, scale, N_cap=None,
+                       kv_scale=None, win_scale=None, flags=0, rope_base=10000.0, rope_dims=0, lse_out=None,
+                       stream=None):
+    """csa_attend with its scratch in the library's static device array (no
+    workspace, nothing allocated); see csa_attend_noalloc in include/lca.h."""
+    a = _Args("csa_attend_noalloc")
+    B, Tq, H, D, N_cap = _check_attend(a, dt_q, dt_kv, q, kv, win, sink, out, W, N_cap, kv_scale, win_scale,
+                                       rope_dims, lse_out)
+    a.t(idx, "idx", dtypes=_I32)
+    if idx.dim() != 3 or idx.shape[0] != B or idx.shape[1] != Tq:
+        a._fail(f"idx must be [{B}, {Tq}, k], not {tuple(idx.shape)}")
+    a.done()
+    _check(lib().csa_attend_noalloc(_stream(stream), dt_q, dt_kv, B, Tq, H, D, N_cap, m, idx.shape[2], W, q_pos0,
+                                    _p(q), _p(kv), _p(kv_scale), _p(idx), _p(win), _p(win_scale), _p(sink),
+                                    scale, flags, rope_base, rope_dims, _p(out), _p(lse_out)))
 
 
 def hca_attend(dt_q, dt_kv, q, kv, win, sink, out, *, m, W, q_pos0, scale, N_cap=None, kv_scale=None,

@@ -3,6 +3,7 @@
 // to the kernel launchers, error reporting and the optional kernel timing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -470,6 +471,63 @@ int hca_attend(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, i
   a.kv_scale = kv_scale; a.win_scale = win_scale; a.sink = sink; a.idx = nullptr; a.scale = scale;
   a.flags = flags; a.rope_base = rope_base; a.rope_dims = rope_dims; a.out = out; a.lse_out = lse_out;
   return run_attend(stream, a, ws, ws_bytes, "hca_attend");
+}
+
+// ---------------------------------------------------------------------------
+// csa_attend_noalloc: csa_attend with its split partials in a static device
+// array instead of a caller workspace, for callers that cannot allocate.
+// `scratch` is a host-side stand-in in host code: kernels get the device
+// address that hipGetSymbolAddress returns for the current device (each GPU
+// holds its own copy of the array, at its own address), never the name.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out, const char* fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(LCA_ERR_UNSUPPORTED, "%s: device %d is beyond the %d this library tracks", fn, dev, kMaxScratchDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {                                   // once per device, with that device current
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, fn);
+      if (!p) return fail(LCA_ERR_HIP, "%s: no device address for the static scratch array", fn);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return LCA_OK;
+}
+}  // namespace
+
+int csa_attend_noalloc(void* stream, int dt_q, int dt_kv, int B, int Tq, int H, int D, int64_t N_cap, int m, int k,
+                       int W, int64_t q_pos0, const void* q, const void* kv, const float* kv_scale,
+                       const int32_t* idx, const void* win, const float* win_scale, const float* sink,
+                       float scale, uint32_t flags, float rope_base, int rope_dims, void* out, float* lse_out) {
+  const char* fn = "csa_attend_noalloc";
+  lca::AttendArgs a{};
+  a.dt_q = dt_q; a.dt_kv = dt_kv; a.B = B; a.Tq = Tq; a.H = H; a.D = D; a.m = m; a.k = k; a.W = W;
+  a.sparse = true; a.N_cap = N_cap; a.q_pos0 = q_pos0; a.q = q; a.kv = kv; a.win = win;
+  a.kv_scale = kv_scale; a.win_scale = win_scale; a.sink = sink; a.idx = idx; a.scale = scale;
+  a.flags = flags; a.rope_base = rope_base; a.rope_dims = rope_dims; a.out = out; a.lse_out = lse_out;
+  int st = check_attend(a, fn);
+  if (st != LCA_OK) return st;
+  const size_t need = lca::attend_workspace(a);
+  if (need > kScratchBytes)
+    return fail(LCA_ERR_WORKSPACE, "%s: this call needs %zu bytes of scratch; the static array holds %zu "
+                "(use csa_attend with a workspace)", fn, need, kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_address(&ws, fn);
+  if (st != LCA_OK) return st;
+  return hip_status(lca::launch_attend(static_cast<hipStream_t>(stream), a, ws, kScratchBytes), fn);
 }
 
 // ---------------------------------------------------------------------------
