@@ -618,34 +618,71 @@ def pmc_summary(fetch_csv, write_csv, copy_mib, out_json):
     print(json.dumps(rec, indent=1))
 
 
-def cpu_baseline(d, min_seconds=10.0):
-    """The float64 oracle on the host cores, on the same workload: the whole
-    batch of sequences (scores, top-k, attention), repeated until at least
-    ``min_seconds`` of CPU work have been timed."""
-    import oracle as O
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
-    D, m, k, W, B = d["D"], d["m"], d["k"], d["W"], d["B"]
-    done, reps = 0, 0
-    t0 = time.perf_counter()
-    while True:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(d, h, reps=3):
+    """The float64 oracle on the host cores, on the same workloads: the whole
+    CSA decode batch (indexer scores, top-k, attention for every sequence) and
+    the whole HCA decode batch, each run ``reps`` times (median reported), with
+    the BLAS threads numpy has by default and again with one thread."""
+    import oracle as O
+
+    def csa_batch():
+        D, m, k, W, B = d["D"], d["m"], d["k"], d["W"], d["B"]
         for b in range(B):
             nv = O.n_visible(d["q_pos0"], m)
             s = O.index_scores(d["qI"][b, 0], d["w"][b, 0], d["kI"][b], nv)
             sel = O.topk_select(s, k)
             O.csa_attend_query(d["q"][b, 0], d["E"][b], sel, d["win"][b], d["sink"], 1 / math.sqrt(D),
                                d["q_pos0"], d["q_pos0"], W, True, 10000.0, 64)
-            done += 1
-        reps += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"the full batch of {B} sequences, {reps} times ({done} decode tokens), "
-                      f"float64 numpy oracle: indexer scores, top-k, attention; {dt:.1f} s"}
+        return B
+
+    def hca_batch():
+        for b in range(h["B"]):
+            O.hca_attend(h["q"][b], h["E"][b], h["m"], h["win"][b], h["sink"], 1 / math.sqrt(h["D"]),
+                         h["q_pos0"], h["W"], True, 10000.0, 64)
+        return h["B"]
+
+    def median_rate(fn):
+        rates = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            n = fn()
+            rates.append(n / (time.perf_counter() - t0))
+        return float(np.median(rates))
+
+    cores = _blas_threads()
+    res = {"csa": median_rate(csa_batch), "hca": median_rate(hca_batch)}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            res["csa_1t"] = median_rate(csa_batch)
+            res["hca_1t"] = median_rate(hca_batch)
+    except Exception:
+        res["csa_1t"] = res["hca_1t"] = None
+    return {"value": res["csa"], "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the whole CSA decode batch ({d['B']} sequences at {d['q_pos0']} tokens), float64 numpy "
+                      f"oracle (indexer scores, top-k, attention), median of {reps} runs",
+            "value_1thread": res["csa_1t"], "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(),
+            "hca_decode": {"value": res["hca"], "value_1thread": res["hca_1t"], "unit": "tokens/s",
+                           "sample": f"the whole HCA decode batch ({h['B']} sequences at {h['q_pos0']} tokens), "
+                                     f"median of {reps} runs"}}
 
 
 def main():
@@ -781,7 +818,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d)
+        result["cpu_baseline"] = cpu_baseline(d, WL.make_hca_decode())
     print(json.dumps(result), flush=True)
 
 

@@ -52,7 +52,23 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_validate_timing(verbose)
     return LIB
+
+
+def build_validate_timing(verbose: bool = False) -> str:
+    """The host-check timing loop (csrc/validate_timing.c), a plain C program
+    linked against liblca.so; it runs without a GPU."""
+    exe = os.path.join(OBJ, "validate_timing")
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", os.path.join(CSRC, "validate_timing.c"),
+           "-I", os.path.join(os.path.dirname(PKG), "include"), "-L", PKG, "-llca",
+           "-Wl,-rpath," + PKG, "-o", exe]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed on validate_timing.c:\n{r.stdout}\n{r.stderr}")
+    return exe
 
 
 if __name__ == "__main__":

@@ -17,6 +17,8 @@ from gpu_util import DEV, dev_bf16, dev_f32, host, need_gpu, row_tol_check, say
 
 pytestmark = pytest.mark.gpu
 
+TOL = 2e-2
+
 
 def _case(rng, B, Tq, H, N_cap, W, sharp, D=512):
     q = WL.bf16_exact((rng.standard_normal((B, Tq, H, D)) * sharp / np.sqrt(D)).astype(np.float32))
@@ -75,11 +77,13 @@ def test_attend_backward_matches_oracle(kind, Tq, H, inv):
             rq, rE, rw, rs = O.hca_attend_backward(q[b], E[b], m, win[b], sink, scale, q_pos0, dout[b], W, inv,
                                                    10000.0, R)
         ds_ref += rs
-        row_tol_check(dq[b], rq, 3e-2, f"dq b={b}")
+        # the bf16 bar (2e-2) of the forward holds for the gradients too
+        worst = [row_tol_check(dq[b], rq, TOL, f"dq b={b}")]
         touched = np.abs(rE).max(axis=1) > 0
-        row_tol_check(dkv[b][touched], rE[touched], 3e-2, f"dkv b={b}")
+        worst.append(row_tol_check(dkv[b][touched], rE[touched], TOL, f"dkv b={b}"))
         assert np.all(dkv[b][~touched] == 0), "rows no query read must be zero"
         wt = np.abs(rw).max(axis=1) > 0
-        row_tol_check(dwin[b][wt], rw[wt], 3e-2, f"dwin b={b}")
+        worst.append(row_tol_check(dwin[b][wt], rw[wt], TOL, f"dwin b={b}"))
         assert np.all(dwin[b][~wt] == 0)
-    np.testing.assert_allclose(dsink, ds_ref, rtol=3e-2, atol=3e-2 * np.abs(ds_ref).max())
+        say(f"  b={b} worst row errors dq {worst[0]:.2e} dkv {worst[1]:.2e} dwin {worst[2]:.2e}")
+    np.testing.assert_allclose(dsink, ds_ref, rtol=TOL, atol=TOL * np.abs(ds_ref).max())
