@@ -41,10 +41,12 @@ __device__ __forceinline__ void pin_uniform(f32x4& acc) { asm volatile("" : "+v"
 // dot of (query tq0 + (4g+i) / HI, head (4g+i) % HI) with key j. ReLU, the
 // head weights and the head sum are folded here, in the same order for every
 // operand type: ((p0 + p1) + (p2 + p3)), then across lane groups for HI >= 8.
+// Each stored score also enters gm[slot], the running maximum of the query
+// slot the lane owns (see emit_group_max), for the top-k's group bound.
 template <int HI>
 __device__ __forceinline__ void emit_scores(const f32x4& acc, const float (&wv)[4], const int64_t (&nvq)[4], int g,
                                             int tq0, int t_off, int t_end, int64_t j, float* srow, int64_t ld,
-                                            bool round_bf16) {
+                                            bool round_bf16, float (&gm)[4]) {
   float part[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) part[i] = wv[i] * fmaxf(acc[i], 0.f);
@@ -52,14 +54,22 @@ __device__ __forceinline__ void emit_scores(const f32x4& acc, const float (&wv)[
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int qt = tq0 + 4 * g + i;
-      if (qt < t_end && j < nvq[i]) srow[(qt - t_off) * ld + j] = round_bf16 ? bf16_round(part[i]) : part[i];
+      const float v = round_bf16 ? bf16_round(part[i]) : part[i];
+      if (qt < t_end && j < nvq[i]) {
+        srow[(qt - t_off) * ld + j] = v;
+        gm[i] = fmaxf(gm[i], v);
+      }
     }
   } else if constexpr (HI == 2) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int qt = tq0 + 2 * g + p;
       const float sc = part[2 * p] + part[2 * p + 1];
-      if (qt < t_end && j < nvq[2 * p]) srow[(qt - t_off) * ld + j] = round_bf16 ? bf16_round(sc) : sc;
+      const float v = round_bf16 ? bf16_round(sc) : sc;
+      if (qt < t_end && j < nvq[2 * p]) {
+        srow[(qt - t_off) * ld + j] = v;
+        gm[p] = fmaxf(gm[p], v);
+      }
     }
   } else {
     float sc = (part[0] + part[1]) + (part[2] + part[3]);
@@ -67,9 +77,42 @@ __device__ __forceinline__ void emit_scores(const f32x4& acc, const float (&wv)[
     if constexpr (HI >= 16) sc += __shfl_xor(sc, 32, 64);
     const int qt = tq0 + (4 * g) / HI;
     const bool writer = (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0;
-    if (writer && qt < t_end && j < nvq[0]) srow[(qt - t_off) * ld + j] = round_bf16 ? bf16_round(sc) : sc;
+    const float v = round_bf16 ? bf16_round(sc) : sc;
+    if (writer && qt < t_end && j < nvq[0]) {
+      srow[(qt - t_off) * ld + j] = v;
+      gm[0] = fmaxf(gm[0], v);
+    }
   }
 }
+
+// Group maxima for the top-k (one float per query and group of kGroup = 16
+// keys, the 16 key lanes r16 of one MFMA tile): the largest stored score of
+// the group's visible keys. Reduces the lane's gm slots over those 16 lanes;
+// lane r16 == 0 writes the slots of queries that see the group's first key.
+constexpr int kGroup = 16;
+template <int HI>
+__device__ __forceinline__ void emit_group_max(float (&gm)[4], int g, int r16, int tq0, int t_off, int t_end,
+                                               const int64_t (&nvq)[4], int64_t grp, float* gmrow, int64_t ldg) {
+  constexpr int NS = HI == 1 ? 4 : (HI == 2 ? 2 : 1);
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    float v = gm[sl];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    const int qt = HI == 1 ? tq0 + 4 * g + sl : (HI == 2 ? tq0 + 2 * g + sl : tq0 + (4 * g) / HI);
+    const int64_t nv = HI == 1 ? nvq[sl] : (HI == 2 ? nvq[2 * sl] : nvq[0]);
+    const bool writer = HI <= 4 || (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0;
+    if (r16 == 0 && writer && qt < t_end && grp * kGroup < nv) gmrow[(qt - t_off) * ldg + grp] = v;
+    gm[sl] = -INFINITY;
+  }
+}
+
+// Side output of the scoring kernels for the chunked top-k: group maxima
+// [B, Tc, ldg]; gmax == nullptr: not produced (the select takes another path).
+struct SelAux {
+  float* gmax;
+  int64_t ldg;
+};
 
 // As emit_scores, but into the wave's LDS staging block (row = query of the
 // wave, column = key of the tile) instead of the score rows: the block is then
@@ -103,10 +146,11 @@ template <int HI, int DI>
 __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
     float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
-    const int64_t* __restrict__ q_pos, int m, bool round_bf16) {
+    const int64_t* __restrict__ q_pos, int m, bool round_bf16, SelAux aux) {
   constexpr int QPB = 16 / HI;       // queries per M tile
   constexpr int KS = DI / 32;        // K steps
   constexpr int UNR = kKeysPerWave / 16;
+  static_assert(kGroup == 16, "a group is the 16 keys of one MFMA tile");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
   const int b = blockIdx.z;
@@ -149,6 +193,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
     wv[i] = qt < t_end ? w[(static_cast<int64_t>(b) * Tq + qt) * HI + h] : 0.f;
     nvq[i] = qt < t_end ? n_visible(q_pos0 + qt, m) : 0;
   }
+  float gm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -157,7 +202,10 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], __builtin_bit_cast(bf16x8, kv[u][s]), acc, 0, 0, 0);
     pin_uniform(acc);
     emit_scores<HI>(acc, wv, nvq, g, tq0, t_off, t_end, key0 + 16 * u + r16,
-                    scores + static_cast<int64_t>(b) * Tc * ld, ld, round_bf16);
+                    scores + static_cast<int64_t>(b) * Tc * ld, ld, round_bf16, gm);
+    if (aux.gmax)
+      emit_group_max<HI>(gm, g, r16, tq0, t_off, t_end, nvq, (key0 + 16 * u) / kGroup,
+                         aux.gmax + static_cast<int64_t>(b) * Tc * aux.ldg, aux.ldg);
   }
 }
 
@@ -177,7 +225,7 @@ template <int HI>
 __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
     float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
-    const int64_t* __restrict__ q_pos, int m, int64_t keys_per_wg, bool round_bf16) {
+    const int64_t* __restrict__ q_pos, int m, int64_t keys_per_wg, bool round_bf16, SelAux aux) {
   constexpr int DI = 128, KS = DI / 32, MB = 4, NB = kTileKeys / 16, QPB = 16 / HI;
   constexpr int QPW = MB * QPB, QPWG = 4 * QPW;
   constexpr int ROWB = DI * 2;                       // bytes per key row
@@ -264,11 +312,13 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         pin_uniform(acc[mb]);
-        if constexpr (kStaged)
+        if constexpr (kStaged) {
           stage_scores<HI>(acc[mb], wv[mb], g, mb * QPB, nb * 16 + r16, St[wid], round_bf16);
-        else
+        } else {
+          float gm_unused[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // no group maxima at HI = 1
           emit_scores<HI>(acc[mb], wv[mb], nvq[mb], g, tw0 + wid * QPW + mb * QPB, t_off, t_end, j, srow, ld,
-                          round_bf16);
+                          round_bf16, gm_unused);
+        }
       }
     }
     if constexpr (kStaged) {
@@ -286,6 +336,23 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
         const int qt = tw0 + wid * QPW + row;
         const float4 v = *reinterpret_cast<const float4*>(&St[wid][row * kStageStride + 4 * c4]);
         if (qt < t_end) *reinterpret_cast<float4*>(srow + static_cast<int64_t>(qt - t_off) * ld + jt0 + 4 * c4) = v;
+        if (aux.gmax) {
+          // group maxima: the 4 lanes of a row's 16-key quarter hold its 16
+          // cells; cells past the query's visible count do not count
+          int64_t nv = qt < t_end ? n_visible(q_pos0 + qt, m) : 0;
+          if (nv > N_cap) nv = N_cap;
+          const int64_t j0 = jt0 + 4 * c4;
+          float mx = -INFINITY;
+          mx = j0 < nv ? fmaxf(mx, v.x) : mx;
+          mx = j0 + 1 < nv ? fmaxf(mx, v.y) : mx;
+          mx = j0 + 2 < nv ? fmaxf(mx, v.z) : mx;
+          mx = j0 + 3 < nv ? fmaxf(mx, v.w) : mx;
+#pragma unroll
+          for (int o = 1; o < 4; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+          const int64_t grp = jt0 / kGroup + (c4 >> 2);
+          if ((c4 & 3) == 0 && qt < t_end && grp * kGroup < nv)
+            aux.gmax[(static_cast<int64_t>(b) * Tc + qt - t_off) * aux.ldg + grp] = mx;
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // reads done before the next tile's staging
     }
@@ -309,7 +376,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_fp4_kernel(
     const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, float* __restrict__ scores, int64_t ld,
     int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m,
-    bool round_bf16) {
+    bool round_bf16, SelAux aux) {
   constexpr int QPB = 16 / HI;
   constexpr int UNR = kFp4KeysPerWave / 16;
   constexpr int ROW = 64;                          // packed bytes per 128-channel row
@@ -356,6 +423,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_fp4_kernel(
   }
   const i32x8 A = {static_cast<int>(qa.x), static_cast<int>(qa.y), static_cast<int>(qa.z), static_cast<int>(qa.w),
                    0, 0, 0, 0};
+  float gm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int u = 0; u < UNR; ++u) {
     const i32x8 Bk = {static_cast<int>(kc[u].x), static_cast<int>(kc[u].y), static_cast<int>(kc[u].z),
@@ -365,7 +433,10 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_fp4_kernel(
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bk, acc, 4, 4, 0, qs, 0, sb);
     pin_uniform(acc);
     emit_scores<HI>(acc, wv, nvq, g, tq0, t_off, t_end, key0 + 16 * u + r16,
-                    scores + static_cast<int64_t>(b) * Tc * ld, ld, round_bf16);
+                    scores + static_cast<int64_t>(b) * Tc * ld, ld, round_bf16, gm);
+    if (aux.gmax)
+      emit_group_max<HI>(gm, g, r16, tq0, t_off, t_end, nvq, (key0 + 16 * u) / kGroup,
+                         aux.gmax + static_cast<int64_t>(b) * Tc * aux.ldg, aux.ldg);
   }
 }
 
@@ -375,7 +446,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_fp4_kernel(
 __global__ __launch_bounds__(kScoreThreads) void index_score_f32_kernel(
     const float* __restrict__ qI, const float* __restrict__ w, const float* __restrict__ kI,
     float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
-    const int64_t* __restrict__ q_pos, int m, int HI, int DI, bool round_bf16) {
+    const int64_t* __restrict__ q_pos, int m, int HI, int DI, bool round_bf16, SelAux aux) {
   extern __shared__ float qs[];                 // [HI * DI + HI]
   const int b = blockIdx.z, tl = blockIdx.y, t = t_off + tl;
   q_pos0 = seq_pos(q_pos, q_pos0, b);           // this sequence's position
@@ -388,16 +459,24 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_f32_kernel(
   for (int i = threadIdx.x; i < HI; i += kScoreThreads)
     qs[HI * DI + i] = w[(static_cast<int64_t>(b) * Tq + t) * HI + i];
   __syncthreads();
-  if (j >= nv) return;
-  const float* kr = kI + (static_cast<int64_t>(b) * N_cap + j) * DI;
-  float sc = 0.f;
-  for (int h = 0; h < HI; ++h) {
-    float dot = 0.f;
-    for (int d = 0; d < DI; ++d) dot = fmaf(qs[h * DI + d], kr[d], dot);
-    sc += qs[HI * DI + h] * fmaxf(dot, 0.f);
+  float sc = -INFINITY;
+  if (j < nv) {
+    const float* kr = kI + (static_cast<int64_t>(b) * N_cap + j) * DI;
+    sc = 0.f;
+    for (int h = 0; h < HI; ++h) {
+      float dot = 0.f;
+      for (int d = 0; d < DI; ++d) dot = fmaf(qs[h * DI + d], kr[d], dot);
+      sc += qs[HI * DI + h] * fmaxf(dot, 0.f);
+    }
+    if (round_bf16) sc = bf16_round(sc);
+    scores[(static_cast<int64_t>(b) * Tc + tl) * ld + j] = sc;
   }
-  if (round_bf16) sc = bf16_round(sc);
-  scores[(static_cast<int64_t>(b) * Tc + tl) * ld + j] = sc;
+  if (aux.gmax) {                               // kGroup consecutive threads: one group
+    float mx = sc;
+#pragma unroll
+    for (int o = 1; o < kGroup; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if ((threadIdx.x & (kGroup - 1)) == 0 && j < nv) aux.gmax[(static_cast<int64_t>(b) * Tc + tl) * aux.ldg + j / kGroup] = mx;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -969,27 +1048,664 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_long_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chunked select bounded by group maxima.
+//
+// A select held by one 1024-thread workgroup per query spends its time on
+// vector ALU work (four waves per SIMD) and on barrier-separated phases, so a
+// long list is cut into chunks of kFiltChunk scores, one 256-thread workgroup
+// each (topk_chunk_kernel), and a second kernel (topk_final_kernel, one
+// workgroup per query) resolves the selection from their candidates; the
+// kernel boundary makes the candidates visible to it. The scoring kernel left
+// the maximum of every group of kGroup keys. From them follows a lower bound
+// lo on the k-th largest score: wave w of a chunk workgroup takes the groups g
+// with g % 4 == w and finds t_w, the r-th largest of their maxima (r =
+// ceil(k / 4), a bitwise search on ballots over the top 16 key bits; the lower
+// edge of that 16-bit bin is still a bound); each maximum is a distinct score,
+// so at least k scores are >= lo = min_w t_w. (A wave with fewer than r groups
+// bounds nothing: lo falls to the smallest key.) Lists with too many groups
+// take lo from topk_bound_kernel. A chunk writes its scores above lo, then its
+// scores equal to lo, each list in index order, and both counts. If at least
+// k candidates lie above lo, the k-th largest is among them and radix passes
+// on their keys find it; otherwise it is lo itself, and the winners are every
+// candidate above lo plus the first (k - above) ties in index order (a crowd
+// of equal scores, e.g. the exact zeros of a query whose head weights are all
+// negative, costs nothing). The output is the same set in the same order as
+// the full passes. A chunk with more candidates than its slots, or a row with
+// more than the final workgroup holds, falls back to full passes over the row.
+// ---------------------------------------------------------------------------
+constexpr int kFiltThreads = 256;
+constexpr int kFiltItems = 16;
+constexpr int kFiltChunk = kFiltThreads * kFiltItems;   // scores per chunk workgroup
+constexpr int kRunMax = 32;                              // candidates per thread of the final workgroup
+constexpr int kStageKeys = kMaxBins;                     // candidate keys the final workgroup stages in LDS
+constexpr int kMaxChunks = 1024;                         // chunks whose counts fit LDS
+constexpr int kInlineItems = 8;                          // group maxima per lane, bound inside the chunk kernel
+constexpr int kBoundItems = 32;                          // group maxima per lane, bound kernel
+constexpr uint32_t kOverflow = 0xffffffffu;
+
+struct FiltWs {
+  float* gmax;            // [rows, ldg] group maxima
+  int64_t ldg;
+  uint32_t* bound;        // [rows, 2] lo, hi keys (bound kernel output)
+  uint32_t* ckey;         // [rows, nchs, capc] candidate keys: above lo, then equal to lo
+  int32_t* cidx;          // [rows, nchs, capc] their indices
+  uint32_t* cnt;          // [rows, nchs] (above << 16) | equal, kOverflow past capc
+  int nchs;               // chunk stride per row
+  int capc;               // candidate slots per chunk
+};
+
+// Exclusive scan over NT threads (NT / 64 waves), one value per thread.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t x = wave_incl_scan(v);
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t e = wsum[w];
+    before += w < wid ? e : 0u;
+    all += e;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+// As find_digit, for NT threads (nb <= kMaxBins).
+template <int NT>
+__device__ __forceinline__ void find_digit_t(const uint32_t* hist, int nb, uint32_t krem, uint32_t* wsum,
+                                             uint32_t* sh_digit, uint32_t* sh_krem) {
+  constexpr int BPT = kMaxBins / NT;
+  const int tid = threadIdx.x;
+  uint32_t c[BPT], tsum = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    const int d = nb - 1 - (BPT * tid + q);
+    c[q] = d >= 0 ? hist[d] : 0u;
+    tsum += c[q];
+  }
+  uint32_t total;
+  const uint32_t before = block_excl_scan_t<NT>(tsum, wsum, &total);
+  if (before < krem && before + tsum >= krem) {
+    uint32_t cum = before;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      if (cum < krem && cum + c[q] >= krem) {
+        *sh_digit = static_cast<uint32_t>(nb - 1 - (BPT * tid + q));
+        *sh_krem = krem - cum;
+      }
+      cum += c[q];
+    }
+  }
+  __syncthreads();
+}
+
+// Lower bound lo and upper bound hi (keys) of a row's k-th largest score from
+// its ng group maxima (see above); the result is the same in every workgroup
+// and thread. BI: maxima per lane kept in registers; with more groups than
+// 4 * 64 * BI, each item takes the maximum of gs consecutive groups (a coarser
+// but still valid bound).
+template <int BI>
+__device__ __forceinline__ void group_bound(const float* __restrict__ gm, int64_t ng, int k, bool key16,
+                                            uint32_t* wv, uint32_t* lo_out, uint32_t* hi_out) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  constexpr int64_t kPer = 4 * kWave * BI;
+  const int64_t gs = (ng + kPer - 1) / kPer;             // groups per item
+  const int64_t ns = (ng + gs - 1) / gs;                 // items in the row
+  // item i of this lane: groups [sg * gs, sg * gs + gs), sg = 4 (64 i + lane) + wid;
+  // the loads of one pass over d are independent and go out together
+  float fm[BI];
+#pragma unroll
+  for (int i = 0; i < BI; ++i) fm[i] = -INFINITY;
+  for (int64_t d = 0; d < gs; ++d) {
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int64_t sg = 4 * (static_cast<int64_t>(kWave) * i + lane) + wid;
+      const int64_t gg = sg * gs + d;
+      if (sg < ns && gg < ng) fm[i] = fmaxf(fm[i], gm[gg]);
+    }
+  }
+  uint32_t kv[BI], mx = 0;
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int64_t sg = 4 * (static_cast<int64_t>(kWave) * i + lane) + wid;
+    kv[i] = sg < ns ? score_key(fm[i], key16) : 0u;
+    mx = max(mx, kv[i]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), o, kWave)));
+  // the search runs on the keys' top 16 bits: the lower edge of the 16-bit
+  // bin of the r-th largest is at or below it, so still a bound
+  const int ksh = key16 ? 0 : 16;
+  const uint32_t r = static_cast<uint32_t>((k + 3) / 4);
+  const int64_t have = ns > wid ? (ns - wid + 3) / 4 : 0;    // items of this wave
+  uint32_t t = 0;
+  if (have >= r) {
+    uint32_t k16[BI];
+#pragma unroll
+    for (int i = 0; i < BI; ++i) k16[i] = kv[i] >> ksh;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t c = t | (1u << bit);
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int i = 0; i < BI; ++i) cnt += static_cast<uint32_t>(__popcll(__ballot(k16[i] >= c)));
+      if (cnt >= r) t = c;
+    }
+    t <<= ksh;
+  }
+  if (lane == 0) {
+    wv[wid] = t;
+    wv[4 + wid] = mx;
+  }
+  __syncthreads();
+  uint32_t lo = 0xffffffffu, hi = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    lo = min(lo, wv[w]);
+    hi = max(hi, wv[4 + w]);
+  }
+  *lo_out = lo > 0u ? lo : 1u;                           // key 0 is "no element"
+  *hi_out = hi;
+  __syncthreads();
+}
+
+// Row (b, tl) of a chunked call: scores, visible count, outputs.
+struct FiltRow {
+  const float* s;
+  int64_t n;
+  int64_t r;               // row index b * Tc + tl
+  int32_t* io;
+  float* so;
+};
+
+__device__ __forceinline__ FiltRow filt_row(const float* scores, int64_t ld, int64_t N_cap, int Tq, int t_off, int Tc,
+                                            int64_t q_pos0, const int64_t* q_pos, int m, int k, int32_t* idx_out,
+                                            float* score_out) {
+  const int b = blockIdx.z, tl = blockIdx.y, t = t_off + tl;
+  int64_t n = n_visible(seq_pos(q_pos, q_pos0, b) + t, m);
+  if (n > N_cap) n = N_cap;
+  FiltRow f;
+  f.r = static_cast<int64_t>(b) * Tc + tl;
+  f.s = scores + f.r * ld;
+  f.n = n;
+  f.io = idx_out + (static_cast<int64_t>(b) * Tq + t) * k;
+  f.so = score_out ? score_out + (static_cast<int64_t>(b) * Tq + t) * k : nullptr;
+  return f;
+}
+
+// Radix select by full passes over a row in global memory, NT threads: one
+// pass per digit, then the ordered output. The fallback of the chunked select.
+template <int NT>
+__device__ void select_passes_t(const FiltRow& row, int k, bool key16, uint32_t* hist, uint32_t* wsum,
+                                uint32_t* sh_digit, uint32_t* sh_krem) {
+  constexpr int IT = 16;                                 // scores per thread per round
+  constexpr int RND = NT * IT;
+  const int tid = threadIdx.x;
+  const int64_t n = row.n;
+  const int64_t rounds = (n + RND - 1) / RND;
+  auto load = [&](int64_t base, uint32_t (&key)[IT]) {
+    const int64_t i0 = base + static_cast<int64_t>(tid) * IT;
+#pragma unroll
+    for (int j = 0; j < IT; ++j) key[j] = i0 + j < n ? score_key(row.s[i0 + j], key16) : 0u;
+  };
+  const int nd = key16 ? 2 : 3;
+  uint32_t prefix = 0, pmask = 0, krem = static_cast<uint32_t>(k);
+  int shift = key16 ? 16 : 32;
+  for (int p = 0; p < nd; ++p) {
+    const int wd = key16 ? (p == 0 ? 12 : 4) : (p == 0 ? 12 : 10);
+    shift -= wd;
+    const int nb = 1 << wd;
+    for (int i = tid; i < nb; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int64_t rr = 0; rr < rounds; ++rr) {
+      uint32_t key[IT];
+      load(rr * RND, key);
+#pragma unroll
+      for (int j = 0; j < IT; ++j)
+        if (key[j] != 0u && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    find_digit_t<NT>(hist, nb, krem, wsum, sh_digit, sh_krem);
+    prefix |= *sh_digit << shift;
+    pmask |= static_cast<uint32_t>(nb - 1) << shift;
+    krem = *sh_krem;
+    __syncthreads();
+  }
+  const uint32_t thr = prefix;
+  uint32_t run_gt = 0, run_eq = 0;
+  for (int64_t rr = 0; rr < rounds; ++rr) {
+    uint32_t key[IT];
+    load(rr * RND, key);
+    uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+      gtm |= static_cast<uint32_t>(key[j] > thr) << j;
+      eqm |= static_cast<uint32_t>(key[j] == thr) << j;
+    }
+    uint32_t tg, te;
+    const uint32_t pg = block_excl_scan_t<NT>(__builtin_popcount(gtm), wsum, &tg);
+    const uint32_t pe = block_excl_scan_t<NT>(__builtin_popcount(eqm), wsum, &te);
+    const uint32_t eq_pre = run_eq + pe;
+    uint32_t pos = run_gt + pg + min(eq_pre, krem);
+    uint32_t take = gtm;
+    for (uint32_t c = eq_pre; eqm && c < krem; ++c) {
+      take |= eqm & (~eqm + 1u);
+      eqm &= eqm - 1;
+    }
+    const int64_t i0 = rr * RND + static_cast<int64_t>(tid) * IT;
+    while (take) {
+      const int j = __builtin_ctz(take);
+      take &= take - 1;
+      row.io[pos] = static_cast<int32_t>(i0 + j);
+      if (row.so) row.so[pos] = row.s[i0 + j];
+      ++pos;
+    }
+    run_gt += tg;
+    run_eq += te;
+  }
+}
+
+// One workgroup per row: the group bound, for rows whose maxima are too many
+// to take inside every chunk workgroup.
+__global__ __launch_bounds__(kFiltThreads) void topk_bound_kernel(
+    FiltWs fw, int64_t N_cap, int Tc, int64_t q_pos0, const int64_t* __restrict__ q_pos, int t_off, int m, int k,
+    bool key16) {
+  __shared__ uint32_t wv[8];
+  const int b = blockIdx.z, tl = blockIdx.y;
+  int64_t n = n_visible(seq_pos(q_pos, q_pos0, b) + t_off + tl, m);
+  if (n > N_cap) n = N_cap;
+  if (n <= k) return;
+  const int64_t r = static_cast<int64_t>(b) * Tc + tl;
+  uint32_t lo, hi;
+  group_bound<kBoundItems>(fw.gmax + r * fw.ldg, (n + kGroup - 1) / kGroup, k, key16, wv, &lo, &hi);
+  if (threadIdx.x == 0) {
+    fw.bound[2 * r] = lo;
+    fw.bound[2 * r + 1] = hi;
+  }
+}
+
+// Chunk c of row (b, tl): the bound, then this chunk's candidates.
+template <int BI>
+__global__ __launch_bounds__(kFiltThreads) void topk_chunk_kernel(
+    const float* __restrict__ scores, int64_t ld, FiltWs fw, int64_t N_cap, int Tq, int t_off, int Tc,
+    int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int k, bool key16) {
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[kFiltThreads / 64];
+  __shared__ uint32_t wv[8];
+  const int tid = threadIdx.x;
+  const FiltRow row = filt_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, q_pos, m, k, nullptr, nullptr);
+  const int c = blockIdx.x;
+  if (row.n <= k || c >= (row.n + kFiltChunk - 1) / kFiltChunk) return;
+  // this chunk's scores first: their loads are in flight during the bound
+  const int64_t i0 = static_cast<int64_t>(c) * kFiltChunk + static_cast<int64_t>(tid) * kFiltItems;
+  uint32_t key[kFiltItems];
+  if (i0 + kFiltItems <= row.n) {
+    float4 v[kFiltItems / 4];
+#pragma unroll
+    for (int q = 0; q < kFiltItems / 4; ++q) v[q] = *reinterpret_cast<const float4*>(row.s + i0 + 4 * q);
+#pragma unroll
+    for (int q = 0; q < kFiltItems / 4; ++q) {
+      key[4 * q] = score_key(v[q].x, key16);
+      key[4 * q + 1] = score_key(v[q].y, key16);
+      key[4 * q + 2] = score_key(v[q].z, key16);
+      key[4 * q + 3] = score_key(v[q].w, key16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kFiltItems; ++j) key[j] = i0 + j < row.n ? score_key(row.s[i0 + j], key16) : 0u;
+  }
+  uint32_t lo, hi;
+  if constexpr (BI > 0) {
+    group_bound<BI>(fw.gmax + row.r * fw.ldg, (row.n + kGroup - 1) / kGroup, k, key16, wv, &lo, &hi);
+  } else {
+    lo = fw.bound[2 * row.r];
+    hi = fw.bound[2 * row.r + 1];
+  }
+  uint32_t am = 0, em = 0;
+#pragma unroll
+  for (int j = 0; j < kFiltItems; ++j) {
+    am |= static_cast<uint32_t>(key[j] > lo) << j;
+    em |= static_cast<uint32_t>(key[j] == lo) << j;
+  }
+  uint32_t tot;   // both counts < 2^16
+  const uint32_t pre = block_excl_scan_t<kFiltThreads>((static_cast<uint32_t>(__builtin_popcount(am)) << 16) |
+                                                           static_cast<uint32_t>(__builtin_popcount(em)), wsum, &tot);
+  const uint32_t A = tot >> 16, E = tot & 0xffffu;
+  const bool fits = A + E <= static_cast<uint32_t>(fw.capc);
+  if (fits) {
+    const int64_t cb = (row.r * fw.nchs + c) * fw.capc;
+    uint32_t pa = pre >> 16, pe = A + (pre & 0xffffu);
+#pragma unroll
+    for (int j = 0; j < kFiltItems; ++j) {
+      if ((am >> j) & 1u) {
+        fw.ckey[cb + pa] = key[j];
+        fw.cidx[cb + pa] = static_cast<int32_t>(i0 + j);
+        ++pa;
+      }
+      if ((em >> j) & 1u) {
+        fw.ckey[cb + pe] = key[j];
+        fw.cidx[cb + pe] = static_cast<int32_t>(i0 + j);
+        ++pe;
+      }
+    }
+  }
+  if (tid == 0) fw.cnt[row.r * fw.nchs + c] = fits ? tot : kOverflow;
+  if (BI > 0 && c == 0 && tid == 0) {               // the final kernel reads the bound here
+    fw.bound[2 * row.r] = lo;
+    fw.bound[2 * row.r + 1] = hi;
+  }
+}
+
+// Map of candidate position p of a row (chunks concatenated in order) to its
+// chunk: pre[c] = candidates before chunk c (pre[nch] = all).
+__device__ __forceinline__ int chunk_of(const uint32_t* pre, int nch, uint32_t p) {
+  int lo = 0, hi = nch;                                  // pre[lo] <= p < pre[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= p) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Exclusive prefix over the 64 lanes of a wave (DPP scan), and the wave total.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
+  const uint32_t incl = wave_incl_scan(v);
+  *total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(incl), 63));
+  return incl - v;
+}
+
+// In one wave: the digit (bins in hist[0, nb), nb <= 256) whose bin holds the
+// krem-th largest element and that element's rank inside the bin.
+__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, int nb, uint32_t krem, uint32_t* digit,
+                                                uint32_t* krem_out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t c[4], tsum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int d = nb - 1 - (4 * lane + q);
+    c[q] = d >= 0 ? hist[d] : 0u;
+    tsum += c[q];
+  }
+  uint32_t total;
+  const uint32_t before = wave_excl_scan(tsum, &total);
+  uint32_t dg = 0, kr = 0;
+  const bool mine = before < krem && before + tsum >= krem;
+  if (mine) {
+    uint32_t cum = before;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (cum < krem && cum + c[q] >= krem) {
+        dg = static_cast<uint32_t>(nb - 1 - (4 * lane + q));
+        kr = krem - cum;
+      }
+      cum += c[q];
+    }
+  }
+  const uint64_t bal = __ballot(mine);
+  const int src = bal ? __builtin_ctzll(bal) : 0;
+  *digit = static_cast<uint32_t>(__shfl(static_cast<int>(dg), src, kWave));
+  *krem_out = static_cast<uint32_t>(__shfl(static_cast<int>(kr), src, kWave));
+}
+
+// The k-th largest of n keys staged in LDS (keys > base are counted; krem
+// counts from the top), taken by one wave with a private 256-bin histogram:
+// 8-bit digits of key - base over [base, base + width). Every wave may run it
+// on the same keys and reaches the same result. Returns thr; *krem_out = how
+// many keys equal to thr are taken.
+__device__ __forceinline__ uint32_t wave_kth(const uint32_t* keys, int n, uint32_t base, uint64_t width,
+                                             uint32_t krem, uint32_t* hist, uint32_t* krem_out) {
+  const int lane = threadIdx.x & 63;
+  while (width > 1) {
+    const int bl = 64 - __builtin_clzll(width - 1);
+    const int sh = bl > 8 ? bl - 8 : 0;
+    const int nb = static_cast<int>((width - 1) >> sh) + 1;
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < n; i += kWave) {
+      const uint32_t kk = keys[i];
+      const uint32_t off = kk - base;
+      if (kk >= base && static_cast<uint64_t>(off) < width) atomicAdd(&hist[off >> sh], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t dg;
+    wave_find_digit(hist, nb, krem, &dg, &krem);
+    base += dg << sh;
+    width = uint64_t(1) << sh;
+    __builtin_amdgcn_wave_barrier();
+  }
+  *krem_out = krem;
+  return base;
+}
+
+// One workgroup per row: the selection from the chunks' candidates.
+__global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
+    const float* __restrict__ scores, int64_t ld, FiltWs fw, int64_t N_cap, int Tq, int t_off, int Tc,
+    int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int k, bool key16, int32_t* __restrict__ idx_out,
+    float* __restrict__ score_out) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kMaxBins];   // staged keys / histograms
+  __shared__ uint32_t preA[kMaxChunks + 1], preE[kMaxChunks + 1];
+  __shared__ __attribute__((aligned(16))) uint32_t whist[kFiltThreads / 64][256];
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[kFiltThreads / 64];
+  __shared__ uint32_t sh_digit, sh_krem, sh_fallback;
+  const int tid = threadIdx.x;
+  const int wid = tid >> 6;
+  const FiltRow row = filt_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, q_pos, m, k, idx_out, score_out);
+  if (row.n <= k) {                                      // every visible entry, then -1
+    for (int i = tid; i < k; i += kFiltThreads) {
+      row.io[i] = i < row.n ? i : -1;
+      if (row.so) row.so[i] = i < row.n ? row.s[i] : -INFINITY;
+    }
+    return;
+  }
+  const int nch = static_cast<int>((row.n + kFiltChunk - 1) / kFiltChunk);
+  if (nch > kMaxChunks) {
+    select_passes_t<kFiltThreads>(row, k, key16, hist, wsum, &sh_digit, &sh_krem);
+    return;
+  }
+  const uint32_t lo = fw.bound[2 * row.r], hi = fw.bound[2 * row.r + 1];
+  // per-chunk counts -> exclusive prefixes preA / preE over the chunks
+  constexpr int CPT = kMaxChunks / kFiltThreads;
+  uint32_t ca[CPT], ce[CPT], sa = 0, se = 0;
+  bool ovf = false;
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int ch = CPT * tid + q;
+    const uint32_t v = ch < nch ? fw.cnt[row.r * fw.nchs + ch] : 0u;
+    ovf |= v == kOverflow;
+    ca[q] = v == kOverflow ? 0u : v >> 16;
+    ce[q] = v == kOverflow ? 0u : v & 0xffffu;
+    sa += ca[q];
+    se += ce[q];
+  }
+  if (tid == 0) sh_fallback = 0;
+  __syncthreads();
+  if (ovf) sh_fallback = 1;
+  uint32_t G, E;
+  uint32_t ra = block_excl_scan_t<kFiltThreads>(sa, wsum, &G);
+  uint32_t re = block_excl_scan_t<kFiltThreads>(se, wsum, &E);
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int ch = CPT * tid + q;
+    if (ch <= nch) {
+      preA[ch] = ra;
+      preE[ch] = re;
+    }
+    ra += ca[q];
+    re += ce[q];
+  }
+  const bool above = G >= static_cast<uint32_t>(k);      // the k-th largest lies above lo
+  if (tid == 0 && above && G > static_cast<uint32_t>(kFiltThreads * kRunMax)) sh_fallback = 1;
+  __syncthreads();
+  if (sh_fallback) {
+    select_passes_t<kFiltThreads>(row, k, key16, hist, wsum, &sh_digit, &sh_krem);
+    return;
+  }
+  const int64_t rbase = row.r * fw.nchs;
+  const uint32_t* ckr = fw.ckey + rbase * fw.capc;
+  const int32_t* cir = fw.cidx + rbase * fw.capc;
+  if (above) {
+    // the candidates above lo, concatenated over the chunks: this thread's run [p0, p1)
+    const uint32_t per = (G + kFiltThreads - 1) / kFiltThreads;
+    const uint32_t p0 = min(G, per * tid), p1 = min(G, p0 + per);
+    uint32_t rk[kRunMax];
+    int32_t rc[kRunMax];
+    {
+      int ch = p0 < p1 ? chunk_of(preA, nch, p0) : 0;
+#pragma unroll
+      for (int q = 0; q < kRunMax; ++q) {
+        const uint32_t p = p0 + q;
+        rc[q] = -1;
+        if (p < p1) {
+          while (p >= preA[ch + 1]) ++ch;
+          rc[q] = static_cast<int32_t>(ch * fw.capc + (p - preA[ch]));
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kRunMax; ++q) rk[q] = rc[q] >= 0 ? ckr[rc[q]] : 0u;
+    }
+    uint32_t thr, krem;
+    if (G <= static_cast<uint32_t>(kStageKeys)) {
+      // stage the keys; every wave finds the k-th largest on its own (no barriers)
+#pragma unroll
+      for (int q = 0; q < kRunMax; ++q)
+        if (rc[q] >= 0) hist[p0 + q] = rk[q];
+      __syncthreads();
+      thr = wave_kth(hist, static_cast<int>(G), lo + 1u, static_cast<uint64_t>(hi) - lo, static_cast<uint32_t>(k),
+                     whist[wid], &krem);
+    } else {
+      uint32_t base = lo + 1u;
+      krem = static_cast<uint32_t>(k);
+      uint64_t width = static_cast<uint64_t>(hi) - lo;
+      while (width > 1) {
+        const int bl = 64 - __builtin_clzll(width - 1);
+        const int sh = bl > 12 ? bl - 12 : 0;
+        const int nb = static_cast<int>((width - 1) >> sh) + 1;
+        for (int i = tid; i < nb; i += kFiltThreads) hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kRunMax; ++q) {
+          const uint32_t off = rk[q] - base;
+          if (rc[q] >= 0 && rk[q] >= base && static_cast<uint64_t>(off) < width) atomicAdd(&hist[off >> sh], 1u);
+        }
+        __syncthreads();
+        find_digit_t<kFiltThreads>(hist, nb, krem, wsum, &sh_digit, &sh_krem);
+        base += sh_digit << sh;
+        krem = sh_krem;
+        width = uint64_t(1) << sh;
+      }
+      thr = base;
+    }
+    // ordered output: above thr, then the first krem equal to it, in index order
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int q = 0; q < kRunMax; ++q) {
+      gt += rc[q] >= 0 && rk[q] > thr;
+      eq += rc[q] >= 0 && rk[q] == thr;
+    }
+    uint32_t tg, te;
+    const uint32_t pg = block_excl_scan_t<kFiltThreads>(gt, wsum, &tg);
+    const uint32_t pe = block_excl_scan_t<kFiltThreads>(eq, wsum, &te);
+    uint32_t pos = pg + min(pe, krem), eq_rank = pe;
+#pragma unroll
+    for (int q = 0; q < kRunMax; ++q) {
+      if (rc[q] < 0) continue;
+      bool take = rk[q] > thr;
+      if (rk[q] == thr) take = eq_rank++ < krem;
+      if (take) {
+        const int32_t ix = cir[rc[q]];
+        row.io[pos] = ix;
+        if (row.so) row.so[pos] = row.s[ix];
+        ++pos;
+      }
+    }
+    return;
+  }
+  // The k-th largest is lo: every candidate above lo wins, and the first
+  // krem = k - G ties at lo in index order. Chunk ch contributes its A
+  // candidates and its first take = clamp(krem - ties before it, 0, E) ties;
+  // inside a chunk both lists are in index order, so an entry's position is
+  // the chunk's offset plus its rank in its own list plus the entries of the
+  // other list below it (a binary search).
+  const uint32_t krem = static_cast<uint32_t>(k) - G;
+  auto take_of = [&](int ch) {
+    const uint32_t eb = preE[ch], e = preE[ch + 1] - eb;
+    return eb >= krem ? 0u : min(e, krem - eb);
+  };
+  // chunk offsets of the output: A before it plus ties taken before it
+  auto out_of = [&](int ch) { return preA[ch] + min(preE[ch], krem); };
+  for (int ch = wid; ch < nch; ch += kFiltThreads / 64) {
+    const uint32_t a_n = preA[ch + 1] - preA[ch], t_n = take_of(ch);
+    if (a_n + t_n == 0) continue;
+    const uint32_t off = out_of(ch);
+    const uint32_t* kk = ckr + static_cast<int64_t>(ch) * fw.capc;
+    const int32_t* ii = cir + static_cast<int64_t>(ch) * fw.capc;
+    const int32_t* ties = ii + a_n;                      // the equal list follows the above list
+    for (uint32_t i = tid & 63; i < a_n + t_n; i += kWave) {
+      const bool is_a = i < a_n;
+      const uint32_t r = is_a ? i : i - a_n;
+      const int32_t x = ii[is_a ? r : a_n + r];
+      // entries of the other list below x
+      const int32_t* other = is_a ? ties : ii;
+      uint32_t lo_i = 0, hi_i = is_a ? t_n : a_n;
+      while (lo_i < hi_i) {
+        const uint32_t mid = (lo_i + hi_i) >> 1;
+        if (other[mid] < x) lo_i = mid + 1;
+        else hi_i = mid;
+      }
+      const uint32_t pos = off + r + lo_i;
+      row.io[pos] = x;
+      if (row.so) row.so[pos] = row.s[x];
+      (void)kk;
+    }
+  }
+}
+
 template <int HI>
 void launch_score_bf16_hi(LaunchScope& ls, const IndexArgs& a, float* sc, int64_t ld, int t_off, int Tc,
-                          dim3 grid) {
+                          dim3 grid, SelAux aux) {
   const bool rb = (a.flags & LCA_SCORE_BF16) != 0;
   const uint16_t* q = static_cast<const uint16_t*>(a.qI);
   const uint16_t* k = static_cast<const uint16_t*>(a.kI);
   switch (a.d_I) {
-    case 64: ls.launch(index_score_bf16_kernel<HI, 64>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb); break;
-    case 128: ls.launch(index_score_bf16_kernel<HI, 128>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb); break;
-    case 256: ls.launch(index_score_bf16_kernel<HI, 256>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb); break;
-    default: ls.launch(index_score_bf16_kernel<HI, 32>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb); break;
+    case 64: ls.launch(index_score_bf16_kernel<HI, 64>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb, aux); break;
+    case 128: ls.launch(index_score_bf16_kernel<HI, 128>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb, aux); break;
+    case 256: ls.launch(index_score_bf16_kernel<HI, 256>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb, aux); break;
+    default: ls.launch(index_score_bf16_kernel<HI, 32>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb, aux); break;
   }
 }
 
 // row stride of the score buffer: 64-element aligned for vector loads
 int64_t score_ld(const IndexArgs& a) { return (a.N_cap + 63) / 64 * 64; }
 
-// queries per chunk so that the score buffer stays under a fixed budget
+// Bytes per query row of the workspace beyond the scores: group maxima,
+// candidates of the chunked select (slots per chunk capc), counts, bound, counter.
+// candidate slots per chunk: the whole chunk for lists of up to 4 register
+// rounds (no overflow), an eighth of it for longer ones
+int filt_capc(int64_t ld) { return ld <= 4 * int64_t(kRound) ? kFiltChunk : kFiltChunk / 8; }
+int64_t filt_nchs(int64_t ld) { return (ld + kFiltChunk - 1) / kFiltChunk; }
+int64_t filt_row_bytes(int64_t ld) {
+  return ld / kGroup * 4 + filt_nchs(ld) * (filt_capc(ld) * int64_t(8) + 4) + 8;
+}
+
+// Whether a chunk may take topk_select_long_kernel (which needs a spill row
+// per query): a list longer than one round whose group bound would be too
+// weak for k (the chunked select's condition, taken at the shortest such
+// list), or tiled scoring without group maxima.
+bool long_old_possible(const IndexArgs& a) {
+  if (a.N_cap <= kRound) return false;
+  const int64_t ng = (kRound + 1 + kGroup - 1) / kGroup;
+  return ng / 4 < 2 * ((a.k + 3) / 4) || (a.dt == LCA_BF16 && a.d_I == 128 && a.H_I == 1);
+}
+
+// queries per chunk so that the score buffer and the select's side arrays stay
+// under a fixed budget
 int query_chunk(const IndexArgs& a) {
-  const int64_t per_q = static_cast<int64_t>(a.B) * score_ld(a) * 4;
-  const int64_t budget = int64_t(512) << 20;
+  const int64_t ld = score_ld(a);
+  const int64_t per_q = static_cast<int64_t>(a.B) * (ld * (long_old_possible(a) ? 8 : 4) + filt_row_bytes(ld));
+  const int64_t budget = int64_t(640) << 20;
   int64_t tc = per_q > 0 ? budget / per_q : a.Tq;
   if (tc < 1) tc = 1;
   if (tc > a.Tq) tc = a.Tq;
@@ -997,27 +1713,75 @@ int query_chunk(const IndexArgs& a) {
   return static_cast<int>(tc);
 }
 
+// Workspace regions (each 256-byte aligned) for a chunk of Tc queries.
+struct IndexWs {
+  float* sc;
+  int32_t* spill;
+  FiltWs fw;
+  size_t bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+IndexWs index_ws(const IndexArgs& a, void* base) {
+  const int Tc = query_chunk(a);
+  const int64_t ld = score_ld(a), rows = static_cast<int64_t>(a.B) * Tc;
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t n) { char* q = p ? p + off : nullptr; off += align256(n); return q; };
+  IndexWs w;
+  w.sc = reinterpret_cast<float*>(take(rows * ld * 4));
+  w.spill = reinterpret_cast<int32_t*>(take(long_old_possible(a) ? rows * ld * 4 : 0));
+  w.fw.ldg = ld / kGroup;
+  w.fw.nchs = static_cast<int>(filt_nchs(ld));
+  w.fw.capc = filt_capc(ld);
+  w.fw.gmax = reinterpret_cast<float*>(take(rows * w.fw.ldg * 4));
+  w.fw.ckey = reinterpret_cast<uint32_t*>(take(rows * w.fw.nchs * w.fw.capc * 4));
+  w.fw.cidx = reinterpret_cast<int32_t*>(take(rows * w.fw.nchs * w.fw.capc * 4));
+  w.fw.cnt = reinterpret_cast<uint32_t*>(take(rows * w.fw.nchs * 4));
+  w.fw.bound = reinterpret_cast<uint32_t*>(take(rows * 8));
+  w.bytes = off + 256;
+  return w;
+}
+
 }  // namespace
 
-// Workspace: the chunk's scores [B, Tc, ld] (float32); for lists longer than
-// one register round, then the select's spill buffer [B, Tc, ld] (int32).
-bool long_lists(const IndexArgs& a) { return a.N_cap > kRound; }
+size_t index_topk_workspace(const IndexArgs& a) { return index_ws(a, nullptr).bytes; }
 
-size_t index_topk_workspace(const IndexArgs& a) {
-  const size_t cells = static_cast<size_t>(a.B) * query_chunk(a) * score_ld(a);
-  return cells * (sizeof(float) + (long_lists(a) ? sizeof(int32_t) : 0)) + 256;
+// The select of one chunk of queries whose longest list is nv_max: the
+// chunked select serves lists longer than one register round (one workgroup
+// per query is quicker below that: each extra kernel in the chain costs its
+// own latency); it needs the group maxima (every scoring path but the tiled
+// one at H_I = 1 writes them) and enough groups per wave share for a bound
+// well above the smallest score.
+bool use_chunked(const IndexArgs& a, int64_t nv_max, bool tiled) {
+  const int64_t ng_max = (nv_max + kGroup - 1) / kGroup;
+  return nv_max > kRound && !(tiled && a.H_I == 1) && nv_max > a.k && ng_max / 4 >= 2 * ((a.k + 3) / 4);
 }
 
 hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t) {
-  float* sc = static_cast<float*>(ws);
+  const IndexWs w = index_ws(a, ws);
+  float* sc = w.sc;
   const int Tc = query_chunk(a);
   const int64_t ld = score_ld(a);
-  int32_t* spill = reinterpret_cast<int32_t*>(sc + static_cast<int64_t>(a.B) * Tc * ld);
   const bool key16 = (a.flags & LCA_SCORE_BF16) != 0;
+  // before anything is enqueued: every chunk that takes the long select has its spill rows
   for (int t_off = 0; t_off < a.Tq; t_off += Tc) {
     const int tcn = min(Tc, a.Tq - t_off);
     int64_t nv_max = n_visible(a.q_pos0 + t_off + tcn - 1, a.m);
     if (nv_max > a.N_cap) nv_max = a.N_cap;
+    const bool tiled = a.dt == LCA_BF16 && a.d_I == 128 && tcn >= kTiledMinQueries;
+    if (nv_max > kRound && nv_max > a.k && !use_chunked(a, nv_max, tiled) && !long_old_possible(a))
+      return hipErrorInvalidValue;
+  }
+  for (int t_off = 0; t_off < a.Tq; t_off += Tc) {
+    const int tcn = min(Tc, a.Tq - t_off);
+    int64_t nv_max = n_visible(a.q_pos0 + t_off + tcn - 1, a.m);
+    if (nv_max > a.N_cap) nv_max = a.N_cap;
+    const bool tiled = a.dt == LCA_BF16 && a.d_I == 128 && tcn >= kTiledMinQueries;
+    const int64_t ng_max = (nv_max + kGroup - 1) / kGroup;
+    const bool filt = use_chunked(a, nv_max, tiled);
+    SelAux aux{filt ? w.fw.gmax : nullptr, w.fw.ldg};
     if (nv_max > 0) {
       LaunchScope scope(s, "index_score");
       if (a.dt == LCA_F32) {
@@ -1025,7 +1789,7 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
         scope.launch(index_score_f32_kernel, grid, dim3(kScoreThreads),
                      static_cast<uint32_t>((a.H_I * a.d_I + a.H_I) * sizeof(float)),
                            static_cast<const float*>(a.qI), a.w, static_cast<const float*>(a.kI), sc, ld,
-                           a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, a.H_I, a.d_I, key16);
+                           a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, a.H_I, a.d_I, key16, aux);
       } else if (a.dt == LCA_MXFP4) {
         const int QPB = 16 / a.H_I;
         dim3 grid((nv_max + kFp4KeysPerWG - 1) / kFp4KeysPerWG, (tcn + QPB - 1) / QPB, a.B);
@@ -1034,13 +1798,13 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
         const uint8_t* k = static_cast<const uint8_t*>(a.kI);
         const uint8_t* ks = static_cast<const uint8_t*>(a.kI_scale);
         switch (a.H_I) {
-          case 1: scope.launch(index_score_fp4_kernel<1>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
-          case 2: scope.launch(index_score_fp4_kernel<2>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
-          case 4: scope.launch(index_score_fp4_kernel<4>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
-          case 8: scope.launch(index_score_fp4_kernel<8>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
-          default: scope.launch(index_score_fp4_kernel<16>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16); break;
+          case 1: scope.launch(index_score_fp4_kernel<1>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16, aux); break;
+          case 2: scope.launch(index_score_fp4_kernel<2>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16, aux); break;
+          case 4: scope.launch(index_score_fp4_kernel<4>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16, aux); break;
+          case 8: scope.launch(index_score_fp4_kernel<8>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16, aux); break;
+          default: scope.launch(index_score_fp4_kernel<16>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16, aux); break;
         }
-      } else if (a.d_I == 128 && tcn >= kTiledMinQueries) {
+      } else if (tiled) {
         // many queries: key tiles through LDS, ~2048 workgroups over (keys, queries)
         const int qpwg = 4 * 4 * (16 / a.H_I);
         const int64_t n_qt = (tcn + qpwg - 1) / qpwg;
@@ -1055,21 +1819,21 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
         const uint16_t* q = static_cast<const uint16_t*>(a.qI);
         const uint16_t* k = static_cast<const uint16_t*>(a.kI);
         switch (a.H_I) {
-          case 1: scope.launch(index_score_tiled_kernel<1>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
-          case 2: scope.launch(index_score_tiled_kernel<2>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
-          case 4: scope.launch(index_score_tiled_kernel<4>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
-          case 8: scope.launch(index_score_tiled_kernel<8>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
-          default: scope.launch(index_score_tiled_kernel<16>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16); break;
+          case 1: scope.launch(index_score_tiled_kernel<1>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
+          case 2: scope.launch(index_score_tiled_kernel<2>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
+          case 4: scope.launch(index_score_tiled_kernel<4>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
+          case 8: scope.launch(index_score_tiled_kernel<8>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
+          default: scope.launch(index_score_tiled_kernel<16>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
         }
       } else {
         const int QPB = 16 / a.H_I;
         dim3 grid((nv_max + kKeysPerWG - 1) / kKeysPerWG, (tcn + QPB - 1) / QPB, a.B);
         switch (a.H_I) {
-          case 1: launch_score_bf16_hi<1>(scope, a, sc, ld, t_off, Tc, grid); break;
-          case 2: launch_score_bf16_hi<2>(scope, a, sc, ld, t_off, Tc, grid); break;
-          case 4: launch_score_bf16_hi<4>(scope, a, sc, ld, t_off, Tc, grid); break;
-          case 8: launch_score_bf16_hi<8>(scope, a, sc, ld, t_off, Tc, grid); break;
-          default: launch_score_bf16_hi<16>(scope, a, sc, ld, t_off, Tc, grid); break;
+          case 1: launch_score_bf16_hi<1>(scope, a, sc, ld, t_off, Tc, grid, aux); break;
+          case 2: launch_score_bf16_hi<2>(scope, a, sc, ld, t_off, Tc, grid, aux); break;
+          case 4: launch_score_bf16_hi<4>(scope, a, sc, ld, t_off, Tc, grid, aux); break;
+          case 8: launch_score_bf16_hi<8>(scope, a, sc, ld, t_off, Tc, grid, aux); break;
+          default: launch_score_bf16_hi<16>(scope, a, sc, ld, t_off, Tc, grid, aux); break;
         }
       }
       hipError_t e = hipGetLastError();
@@ -1077,13 +1841,28 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
     }
     {
       LaunchScope scope(s, "topk_select");
-      // every row's list is at most nv_max long (and nv_max > kRound implies N_cap > kRound)
-      if (nv_max > kRound)
+      if (filt) {
+        const dim3 grid(static_cast<uint32_t>((nv_max + kFiltChunk - 1) / kFiltChunk), tcn, a.B);
+        const float* scs = sc;
+        if (ng_max <= int64_t(4 * kWave) * kInlineItems) {
+          scope.launch(topk_chunk_kernel<kInlineItems>, grid, dim3(kFiltThreads), 0, scs, ld, w.fw, a.N_cap, a.Tq,
+                       t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16);
+        } else {
+          scope.launch(topk_bound_kernel, dim3(1, tcn, a.B), dim3(kFiltThreads), 0, w.fw, a.N_cap, Tc, a.q_pos0,
+                       a.q_pos, t_off, a.m, a.k, key16);
+          scope.launch(topk_chunk_kernel<0>, grid, dim3(kFiltThreads), 0, scs, ld, w.fw, a.N_cap, a.Tq, t_off, Tc,
+                       a.q_pos0, a.q_pos, a.m, a.k, key16);
+        }
+        scope.launch(topk_final_kernel, dim3(1, tcn, a.B), dim3(kFiltThreads), 0, scs, ld, w.fw, a.N_cap, a.Tq,
+                     t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16, a.idx_out, a.score_out);
+      } else if (nv_max > kRound) {
+        // every row's list is at most nv_max long (and nv_max > kRound implies N_cap > kRound)
         scope.launch(topk_select_long_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, static_cast<const float*>(sc), ld,
-                     spill, a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16, a.idx_out, a.score_out);
-      else
+                     w.spill, a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16, a.idx_out, a.score_out);
+      } else {
         scope.launch(topk_select_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, static_cast<const float*>(sc), ld,
                      a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16, a.idx_out, a.score_out);
+      }
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -453,6 +453,81 @@ def test_index_topk_select_exact_order(case, bf16_scores):
         np.testing.assert_array_equal(got[b, 0], np.sort(order[:k]), err_msg=f"{case} b={b}")
 
 
+@pytest.mark.parametrize("case", ["spread", "spikes", "zeros", "same", "ties5", "cluster"])
+@pytest.mark.parametrize("bf16_scores", [False, True])
+def test_index_topk_long_exact_order(case, bf16_scores):
+    # Lists longer than one register round take the chunked select: the bound
+    # from group maxima (here from the bound kernel, with groups merged in
+    # pairs past 8192 of them), candidates per 4096-entry chunk (512 slots
+    # above 131072 entries), then one workgroup per row. Integer vectors and
+    # power-of-two weights make every score exact, so the expected result is
+    # exact. zeros: all-negative head weights, the k-th score is 0 and a crowd
+    # of ties at the bound decides (the winners are the lowest indices); same:
+    # every entry equal; ties5: five distinct scores; cluster: the highest
+    # scores crowd one chunk past its slots (the full passes resolve the row).
+    L = need_gpu()
+    rng = np.random.default_rng(500 + len(case) + 7 * bf16_scores)
+    B, Tq, H_I, d_I, m, k = 1, 1, 4, 128, 4, 1024
+    N_cap = 140000
+    qI = rng.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.float32)
+    kI = rng.integers(-8, 9, size=(B, N_cap, d_I)).astype(np.float32)
+    w = np.tile(np.array([1.0, 0.5, 0.25, 0.125], np.float32), (B, Tq, 1))
+    if case == "spikes":
+        kI[0, rng.choice(N_cap, size=N_cap // 100, replace=False)] *= 4
+    elif case == "zeros":
+        w = -w
+    elif case == "same":
+        kI[:] = kI[:, :1]
+    elif case == "ties5":
+        base = rng.integers(-8, 9, size=(5, d_I)).astype(np.float32)
+        kI = base[rng.integers(0, 5, size=N_cap)][None]
+    elif case == "cluster":
+        kI[0, 50000:54096] *= 3
+    q_pos0 = m * N_cap - 1
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    say(f"long exact order {case} bf16={bf16_scores}")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
+                     flags=L.SCORE_BF16 if bf16_scores else 0, score_out=sco)
+    torch.cuda.synchronize()
+    got, gs = idx.cpu().numpy(), sco.cpu().numpy()
+    sc = O.index_scores(qI[0, 0], w[0, 0], kI[0], N_cap)
+    assert np.all(np.abs(sc) < 2.0 ** 23), "scores must stay exact in fp32"
+    if bf16_scores:
+        sc = O.bf16_round(sc)
+    want = np.sort(np.lexsort((np.arange(N_cap), -sc))[:k])
+    np.testing.assert_array_equal(got[0, 0], want, err_msg=case)
+    np.testing.assert_array_equal(gs[0, 0], sc[want].astype(np.float32))
+
+
+def test_index_topk_long_ragged_rows():
+    # A ragged batch bounded at 140000 entries: the long rows take the chunked
+    # select with a bound, the short ones (5000, 300 entries) have too few
+    # groups for one, every score is a candidate, their chunks overflow and
+    # the full passes resolve them; the empty row is all padding.
+    L = need_gpu()
+    rng = np.random.default_rng(520)
+    B, Tq, H_I, d_I, m, k = 5, 1, 4, 128, 4, 1024
+    N_cap = 140000
+    bound = m * N_cap - 1
+    pos = [bound, 0, 4 * 5000, 4 * 70000 + 3, 4 * 300]
+    qI = rng.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.float32)
+    kI = rng.integers(-8, 9, size=(B, N_cap, d_I)).astype(np.float32)
+    w = np.tile(np.array([1.0, -0.5, 0.25, 0.125], np.float32), (B, Tq, 1))
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    qp = torch.tensor(pos, dtype=torch.int64, device=DEV)
+    say("long ragged rows")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=bound, q_pos=qp)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b in range(B):
+        nv = O.n_visible(pos[b], m)
+        sc = O.index_scores(qI[b, 0], w[b, 0], kI[b], nv)
+        want = np.sort(np.lexsort((np.arange(nv), -sc))[:k])
+        np.testing.assert_array_equal(got[b, 0][:len(want)], want, err_msg=f"b={b}")
+        assert np.all(got[b, 0][len(want):] == -1)
+
+
 # ---------------------------------------------------------------------------
 # attention
 # ---------------------------------------------------------------------------
