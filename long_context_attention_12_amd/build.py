@@ -25,9 +25,14 @@ FLAGS = [
 ]
 
 
+# Per-source additions. The indexer's MFMA results feed a short VALU epilogue
+# per tile: in VGPR form they skip one accumulator read per result register.
+EXTRA = {"index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", out]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:

@@ -20,6 +20,8 @@
 // 32768. An order-preserving compaction follows: output indices come out in
 // increasing order and ties at the threshold go to the lowest indices, so the
 // result is deterministic.
+#include <type_traits>
+
 #include "lca_device.h"
 #include "lca_internal.h"
 #include "../../include/lca.h"
@@ -37,6 +39,46 @@ constexpr int kKeysPerWG = 4 * kKeysPerWave;
 // point every lane reaches, so the MFMA runs with the full wave.
 __device__ __forceinline__ void pin_uniform(f32x4& acc) { asm volatile("" : "+v"(acc)); }
 
+// ReLU as the median of (x, 0, FLT_MAX), and the maximum of two values as the
+// median of (a, b, FLT_MAX): one instruction each, equal to fmaxf for every
+// argument below +inf (+inf becomes FLT_MAX). fmaxf itself, on a value read
+// from an accumulator or a DPP move, first quiets it with an extra max.
+__device__ __forceinline__ float relu1(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.40282347e38f); }
+__device__ __forceinline__ float max1(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, 3.40282347e38f); }
+
+// Rank of this lane's set bit among the set bits of its 16-lane row in the
+// wave mask (bit: this lane's own bit), and the row's count of set bits, from
+// the wave prefix count (mbcnt) and two row broadcasts.
+__device__ __forceinline__ uint32_t row_rank(uint64_t mask, bool bit, uint32_t* row_count) {
+  const uint32_t pm = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+  const uint32_t first = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(pm), 0x150, 0xf, 0xf, false));          // row_newbcast:0
+  const uint32_t last = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(pm + bit), 0x15F, 0xf, 0xf, false));    // row_newbcast:15
+  *row_count = last - first;
+  return pm - first;
+}
+
+// The weighted head terms of one accumulator quad (rows 4g .. 4g + 3):
+// p01 = fma(w1, relu(a1), w0 relu(a0)), p23 = fma(w3, relu(a3), w2 relu(a2)).
+// Every scoring kernel forms its head sums from these in this order, written
+// out so that the compiler's contraction choices cannot differ between them.
+__device__ __forceinline__ void head_pairs(const f32x4& acc, const float (&wv)[4], float& p01, float& p23) {
+  p01 = __builtin_fmaf(wv[1], relu1(acc[1]), wv[0] * relu1(acc[0]));
+  p23 = __builtin_fmaf(wv[3], relu1(acc[3]), wv[2] * relu1(acc[2]));
+}
+
+// Order-preserving key: larger score -> larger unsigned key; -0 folds into +0.
+// Key 0 never comes from a real number (it would be a NaN pattern), so it
+// marks "no element" below.
+__device__ __forceinline__ uint32_t score_key(float v, bool key16) {
+  if (v == 0.f) v = 0.f;
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return key16 ? (k >> 16) : k;
+}
+
 // Scores of key j from one 16 x 16 MFMA tile: accumulator row 4g + i is the
 // dot of (query tq0 + (4g+i) / HI, head (4g+i) % HI) with key j. ReLU, the
 // head weights and the head sum are folded here, in the same order for every
@@ -47,24 +89,24 @@ template <int HI>
 __device__ __forceinline__ void emit_scores(const f32x4& acc, const float (&wv)[4], const int64_t (&nvq)[4], int g,
                                             int tq0, int t_off, int t_end, int64_t j, float* srow, int64_t ld,
                                             bool round_bf16, float (&gm)[4]) {
-  float part[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) part[i] = wv[i] * fmaxf(acc[i], 0.f);
   if constexpr (HI == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int qt = tq0 + 4 * g + i;
-      const float v = round_bf16 ? bf16_round(part[i]) : part[i];
+      const float pi = wv[i] * relu1(acc[i]);
+      const float v = round_bf16 ? bf16_round(pi) : pi;
       if (qt < t_end && j < nvq[i]) {
         srow[(qt - t_off) * ld + j] = v;
         gm[i] = fmaxf(gm[i], v);
       }
     }
   } else if constexpr (HI == 2) {
+    float pr[2];
+    head_pairs(acc, wv, pr[0], pr[1]);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int qt = tq0 + 2 * g + p;
-      const float sc = part[2 * p] + part[2 * p + 1];
+      const float sc = pr[p];
       const float v = round_bf16 ? bf16_round(sc) : sc;
       if (qt < t_end && j < nvq[2 * p]) {
         srow[(qt - t_off) * ld + j] = v;
@@ -72,7 +114,9 @@ __device__ __forceinline__ void emit_scores(const f32x4& acc, const float (&wv)[
       }
     }
   } else {
-    float sc = (part[0] + part[1]) + (part[2] + part[3]);
+    float p01, p23;
+    head_pairs(acc, wv, p01, p23);
+    float sc = p01 + p23;
     if constexpr (HI >= 8) sc += __shfl_xor(sc, 16, 64);
     if constexpr (HI >= 16) sc += __shfl_xor(sc, 32, 64);
     const int qt = tq0 + (4 * g) / HI;
@@ -107,12 +151,25 @@ __device__ __forceinline__ void emit_group_max(float (&gm)[4], int g, int r16, i
   }
 }
 
-// Side output of the scoring kernels for the chunked top-k: group maxima
-// [B, Tc, ldg]; gmax == nullptr: not produced (the select takes another path).
+// Side outputs of the scoring kernels for the chunked top-k: group maxima
+// [B, Tc, ldg] (gmax == nullptr: not produced). The tiled kernel's candidate
+// pass instead compares every score with its row's bound (bound[2 r]) and
+// writes, per row and key range, the candidates above it (key, index) at
+// slots [0, per) and the indices of those equal to it at [per, 2 per), each
+// in index order, with (above << 16) | equal in cnt[r, range].
 struct SelAux {
   float* gmax;
   int64_t ldg;
+  const uint32_t* bound;
+  uint32_t* ckey;
+  int32_t* cidx;
+  uint32_t* cnt;
+  int nchs;
+  int64_t capc;
 };
+constexpr int kTiledScores = 0;     // tiled kernel: store every score (and group maxima if asked)
+constexpr int kTiledMaxima = 1;     // group maxima only
+constexpr int kTiledCands = 2;      // candidates against the row bound only
 
 // As emit_scores, but into the wave's LDS staging block (row = query of the
 // wave, column = key of the tile) instead of the score rows: the block is then
@@ -121,17 +178,16 @@ constexpr int kStageStride = 80;     // floats per staged query row (64 keys + b
 template <int HI>
 __device__ __forceinline__ void stage_scores(const f32x4& acc, const float (&wv)[4], int g, int q0, int col,
                                              float* stage, bool round_bf16) {
-  float part[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) part[i] = wv[i] * fmaxf(acc[i], 0.f);
+  float pr[2];
+  head_pairs(acc, wv, pr[0], pr[1]);
   if constexpr (HI == 2) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const float sc = part[2 * p] + part[2 * p + 1];
+      const float sc = pr[p];
       stage[(q0 + 2 * g + p) * kStageStride + col] = round_bf16 ? bf16_round(sc) : sc;
     }
   } else {
-    float sc = (part[0] + part[1]) + (part[2] + part[3]);
+    float sc = pr[0] + pr[1];
     if constexpr (HI >= 8) sc += __shfl_xor(sc, 16, 64);
     if constexpr (HI >= 16) sc += __shfl_xor(sc, 32, 64);
     const bool writer = (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0;
@@ -221,28 +277,72 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
 constexpr int kTileKeys = 64;
 constexpr int kTiledMinQueries = 64;
 
+// The scores one lane holds after an M tile's MFMAs (the values stage_scores
+// stages, in the same arithmetic order): HI = 2, queries 2 g and 2 g + 1 of
+// the tile; HI >= 4, query 4 g / HI, valid in the lanes that hold the head
+// sum. Returns the number of slots filled.
 template <int HI>
+__device__ __forceinline__ int acc_scores(const f32x4& acc, const float (&wv)[4], int g, bool round_bf16,
+                                          float (&v)[2]) {
+  float pr[2];
+  head_pairs(acc, wv, pr[0], pr[1]);
+  if constexpr (HI == 2) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) v[p] = round_bf16 ? bf16_round(pr[p]) : pr[p];
+    return 2;
+  } else {
+    float sc = pr[0] + pr[1];
+    if constexpr (HI >= 8) sc += __shfl_xor(sc, 16, 64);
+    if constexpr (HI >= 16) sc += __shfl_xor(sc, 32, 64);
+    v[0] = round_bf16 ? bf16_round(sc) : sc;
+    v[1] = v[0];
+    (void)g;
+    return 1;
+  }
+}
+
+// R16: scores rounded to bf16 (a template parameter, so that no per-block
+// branch splits a tile's straight-line code).
+template <int HI, int MODE, bool R16>
 __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
     float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
-    const int64_t* __restrict__ q_pos, int m, int64_t keys_per_wg, bool round_bf16, SelAux aux) {
+    const int64_t* __restrict__ q_pos, int m, int64_t keys_per_wg, SelAux aux, int kc, int nq, int nbatch) {
+  constexpr bool round_bf16 = R16;
   constexpr int DI = 128, KS = DI / 32, MB = 4, NB = kTileKeys / 16, QPB = 16 / HI;
   constexpr int QPW = MB * QPB, QPWG = 4 * QPW;
   constexpr int ROWB = DI * 2;                       // bytes per key row
   constexpr bool kStaged = HI >= 2;                  // HI = 1: 64 queries per wave, stored directly
+  static_assert(kStaged || MODE == kTiledScores, "maxima and candidates come from the staged tile");
+  constexpr int RPL = kStaged ? QPW / 4 : 1;         // staged rows a lane writes out per tile
   __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kTileKeys * DI];
   __shared__ __attribute__((aligned(16))) float St[4][kStaged ? QPW * kStageStride : 4];
+  __shared__ int64_t nv_tab[QPWG];                   // visible entries of the workgroup's queries
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  const int b = blockIdx.z;
+  // XCD-aware block order: the hardware hands consecutive blocks to the 8
+  // XCDs in turn. Block L runs on XCD L % 8 as that XCD's (L / 8)-th block;
+  // those take the nq query tiles of one (sequence, key range) pair back to
+  // back, so the range's keys are read from HBM once into that XCD's L2 and
+  // the other query tiles hit there. Pairs are padded to a multiple of 8.
+  const int xcd = static_cast<int>(blockIdx.x) & 7, jx = static_cast<int>(blockIdx.x) >> 3;
+  const int krb = (jx / nq) * 8 + xcd;
+  if (krb >= kc * nbatch) return;
+  const int b = krb / kc, kr = krb - b * kc, qtile = jx % nq;
   q_pos0 = seq_pos(q_pos, q_pos0, b);                // this sequence's position
   const int t_end = min(Tq, t_off + Tc);
-  const int tw0 = t_off + static_cast<int>(blockIdx.y) * QPWG;
+  const int tw0 = t_off + qtile * QPWG;
   if (tw0 >= t_end) return;
-  int64_t nv_max = n_visible(q_pos0 + min(tw0 + QPWG, t_end) - 1, m);
-  if (nv_max > N_cap) nv_max = N_cap;
-  const int64_t k_begin = static_cast<int64_t>(blockIdx.x) * keys_per_wg;
+  // one division per query (not one per lane and slot)
+  for (int i = threadIdx.x; i < QPWG; i += kScoreThreads) {
+    int64_t nv = tw0 + i < t_end ? n_visible(q_pos0 + tw0 + i, m) : 0;
+    nv_tab[i] = nv < N_cap ? nv : N_cap;
+  }
+  __syncthreads();
+  auto nv_of = [&](int qt) { return qt < t_end ? nv_tab[qt - tw0] : int64_t(0); };   // clamped to N_cap
+  const int64_t nv_max = nv_of(min(tw0 + QPWG, t_end) - 1);
+  const int64_t k_begin = static_cast<int64_t>(kr) * keys_per_wg;
   if (k_begin >= nv_max) return;
   const int64_t k_end = min(k_begin + keys_per_wg, nv_max);
   const int ntiles = static_cast<int>((k_end - k_begin + kTileKeys - 1) / kTileKeys);
@@ -282,12 +382,170 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * g + i, q2 = tq0 + row / HI, h2 = row % HI;
       wv[mb][i] = q2 < t_end ? w[(static_cast<int64_t>(b) * Tq + q2) * HI + h2] : 0.f;
-      int64_t nv = q2 < t_end ? n_visible(q_pos0 + q2, m) : 0;
+      const int64_t nv = nv_of(q2);
       nvq[mb][i] = nv < k_end ? nv : k_end;        // this workgroup scores keys < k_end only
     }
   }
   float* srow = scores + static_cast<int64_t>(b) * Tc * ld;
   const int slot_r = r16;                          // key & 15 of the keys this lane reads
+  // the staged rows this lane writes out (row i * 4 + lane / 16 of the wave): visible count
+  int64_t nv_l[RPL];
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) nv_l[i] = nv_of(tw0 + wid * QPW + i * 4 + (lane >> 4));
+  // maxima and candidate passes: the (M tile, slot) queries of this lane's
+  // accumulators (acc_scores), their visible count past k_begin, row index,
+  // whether the lane holds them; for maxima the running maximum and the row's
+  // first group slot of this lane, for candidates the bound (as a key, and as
+  // a float below which no candidate lies) and the running counts
+  int nvl_l[2 * MB];
+  int64_t rix_l[2 * MB];
+  bool writer_l[2 * MB];
+  uint32_t lo_c[2 * MB], run_a[2 * MB], run_e[2 * MB];
+  float gm_l[2 * MB], lof_l[2 * MB];
+  int64_t gslot_l[2 * MB], cb_l[2 * MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      const int ci = mb * 2 + sl;
+      const int ql = HI == 2 ? 2 * g + sl : (4 * g) / HI;          // query of the M tile
+      const int qt = tw0 + wid * QPW + mb * QPB + ql;
+      const bool holds = (HI == 2 || sl == 0) && (HI <= 4 || (g % (HI / 4 > 0 ? HI / 4 : 1)) == 0);
+      int64_t nv = nv_of(qt);
+      if (nv > k_end) nv = k_end;
+      nvl_l[ci] = static_cast<int>(nv > k_begin ? nv - k_begin : 0);
+      rix_l[ci] = static_cast<int64_t>(b) * Tc + qt - t_off;
+      writer_l[ci] = holds && qt < t_end;
+      gm_l[ci] = -INFINITY;
+      gslot_l[ci] = rix_l[ci] * aux.ldg + k_begin / kGroup + (r16 >> 2);
+      cb_l[ci] = (rix_l[ci] * aux.nchs + kr) * aux.capc;
+      lo_c[ci] = 0;
+      lof_l[ci] = INFINITY;
+      run_a[ci] = run_e[ci] = 0;
+    }
+  }
+  if constexpr (MODE == kTiledCands) {
+    // all loads first (clamped rows of non-writers are read and ignored)
+    uint32_t lo_raw[2 * MB];
+#pragma unroll
+    for (int ci = 0; ci < 2 * MB; ++ci) lo_raw[ci] = aux.bound[2 * (writer_l[ci] ? rix_l[ci] : int64_t(0))];
+#pragma unroll
+    for (int ci = 0; ci < 2 * MB; ++ci) {
+      if (!writer_l[ci]) continue;
+      lo_c[ci] = lo_raw[ci];
+      // key(x) >= lo implies x >= lof: lof is the bound's own float when
+      // that is a normal number, and -FLT_MIN for a bound among the
+      // subnormals and zeros (a superset either way, whether or not the
+      // comparison flushes subnormals)
+      const uint32_t lo32 = round_bf16 ? lo_raw[ci] << 16 : lo_raw[ci];
+      if (lo32 >= 0x80800000u) lof_l[ci] = __uint_as_float(lo32 & 0x7fffffffu);      // >= +FLT_MIN
+      else if (lo32 >= 0x7f7fffffu) lof_l[ci] = -1.17549435e-38f;                  // >= key(-FLT_MIN)
+      else lof_l[ci] = __uint_as_float(~lo32);                                     // <= -FLT_MIN
+    }
+  }
+  // the smallest visible count past k_begin among this wave's queries (its
+  // first query): tiles below it need no visibility masks
+  int nvl_w = 0;
+  {
+    const int qw0 = tw0 + wid * QPW;
+    int64_t nv = nv_of(qw0);
+    if (nv > k_end) nv = k_end;
+    nvl_w = __builtin_amdgcn_readfirstlane(static_cast<int>(nv > k_begin ? nv - k_begin : 0));
+  }
+
+  // One tile of the maxima or candidate pass; FULL: every key of the tile is
+  // visible to every query of the wave (no per-key masks).
+  auto sel_tile = [&](int tt, const char* xb, auto full_c) __attribute__((always_inline)) {
+    constexpr bool full = decltype(full_c)::value;
+    constexpr int NSL = HI == 2 ? 2 : 1;             // query slots per lane (acc_scores)
+    float vs[NB][2 * MB];                            // candidate pass: the tile's scores
+    uint64_t mk[NB][2 * MB];                         // and which may be candidates
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4 acc[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(xb + (nb * 16 + r16) * ROWB + 16 * ((4 * s + g) ^ slot_r));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[mb][s], __builtin_bit_cast(bf16x8, kv), acc[mb], 0, 0, 0);
+      }
+      // lanes 16 gr .. 16 gr + 15 hold one query's scores of these 16 keys
+      const int jl = tt * kTileKeys + nb * 16 + r16;                 // key - k_begin
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        pin_uniform(acc[mb]);
+        float v[2];
+        acc_scores<HI>(acc[mb], wv[mb], g, round_bf16, v);
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+          const int ci = mb * 2 + sl;
+          const bool vis = full || jl < nvl_l[ci];
+          if constexpr (MODE == kTiledMaxima) {
+            gm_l[ci] = fmaxf(gm_l[ci], vis ? v[sl] : -INFINITY);     // over the tile's 4 key slabs
+          } else {
+            vs[nb][ci] = v[sl];
+            mk[nb][ci] = __ballot(v[sl] >= lof_l[ci] && vis);
+          }
+        }
+      }
+    }
+    if constexpr (MODE == kTiledMaxima) {
+      // Lane r16 now holds the maximum of keys r16 + 16 s (s < 4) of the
+      // tile; a quad of lanes (r16 = 4c .. 4c + 3) then covers the group of
+      // keys 4c + i + 16 s. Group c of tile tt takes slot
+      // gs = (k_begin + 64 tt) / 16 + c: a partition of the row into groups
+      // of 16 keys. The bound reads the slots with key 16 gs visible; the
+      // group's first key, 16 gs - 12 c, is then visible too, and the slot
+      // is written.
+#pragma unroll
+      for (int ci = 0; ci < 2 * MB; ++ci) {
+        if (ci % 2 >= NSL) continue;
+        float x = gm_l[ci];
+        x = max1(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));
+        x = max1(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));
+        const int c = r16 >> 2;
+        if ((r16 & 3) == 0 && writer_l[ci] && tt * kTileKeys + 4 * c < nvl_l[ci]) aux.gmax[gslot_l[ci] + 4 * tt] = x;
+        gm_l[ci] = -INFINITY;
+      }
+    } else {
+      // Candidates are rare: only the blocks with scores at or above the
+      // float filter (a superset of those at or above the bound) take the
+      // exact key comparisons. Each query's candidates go to its lists in key
+      // order (slab by slab, lane by lane).
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int jl = tt * kTileKeys + nb * 16 + r16;
+#pragma unroll
+        for (int ci = 0; ci < 2 * MB; ++ci) {
+          if (ci % 2 >= NSL) continue;
+          if (mk[nb][ci] == 0) continue;                             // uniform
+          const bool maybe = (mk[nb][ci] >> lane) & 1u;
+          const uint32_t kk = score_key(vs[nb][ci], round_bf16);
+          const bool is_a = maybe && writer_l[ci] && kk > lo_c[ci];
+          const bool is_e = maybe && writer_l[ci] && kk == lo_c[ci];
+          const uint64_t ba = __ballot(is_a), be = __ballot(is_e);
+          if (ba != 0) {
+            uint32_t na;
+            const uint32_t pa = run_a[ci] + row_rank(ba, is_a, &na);
+            if (is_a) {
+              aux.ckey[cb_l[ci] + pa] = kk;
+              aux.cidx[cb_l[ci] + pa] = static_cast<int32_t>(k_begin + jl);
+            }
+            run_a[ci] += na;
+          }
+          if (be != 0) {
+            uint32_t ne;
+            const uint32_t pe = run_e[ci] + row_rank(be, is_e, &ne);
+            if (is_e) aux.cidx[cb_l[ci] + aux.capc / 2 + pe] = static_cast<int32_t>(k_begin + jl);
+            run_e[ci] += ne;
+          }
+        }
+      }
+    }
+  };
 
   for (int tt = 0; tt < ntiles; ++tt) {
     // tile tt has landed (every wave waited for its own copies) and every wave
@@ -296,6 +554,13 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
     __builtin_amdgcn_s_barrier();
     if (tt + 1 < ntiles) issue(tt + 1, (tt + 1) & 1);
     const char* xb = reinterpret_cast<const char*>(&Ks[tt & 1][0]);
+    if constexpr (MODE != kTiledScores) {
+      if ((tt + 1) * kTileKeys <= nvl_w)                               // uniform
+        sel_tile(tt, xb, std::true_type{});
+      else
+        sel_tile(tt, xb, std::false_type{});
+      continue;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       f32x4 acc[MB];
@@ -321,7 +586,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
         }
       }
     }
-    if constexpr (kStaged) {
+    if constexpr (kStaged && MODE == kTiledScores) {
       // The wave's QPW x 64 tile of scores leaves as 16-byte stores, 16 lanes
       // per 256-byte row segment. Every key of the tile is written: cells past
       // a query's visible count lie inside its row (the stride is a multiple of
@@ -331,17 +596,17 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       const int64_t jt0 = k_begin + static_cast<int64_t>(tt) * kTileKeys;
 #pragma unroll
-      for (int i = 0; i < QPW / 4; ++i) {
+      for (int i = 0; i < RPL; ++i) {
         const int u = i * 64 + lane, row = u >> 4, c4 = u & 15;
         const int qt = tw0 + wid * QPW + row;
+        const int64_t rix = static_cast<int64_t>(b) * Tc + qt - t_off;
         const float4 v = *reinterpret_cast<const float4*>(&St[wid][row * kStageStride + 4 * c4]);
-        if (qt < t_end) *reinterpret_cast<float4*>(srow + static_cast<int64_t>(qt - t_off) * ld + jt0 + 4 * c4) = v;
+        const int64_t j0 = jt0 + 4 * c4;
+        if (qt < t_end) *reinterpret_cast<float4*>(srow + static_cast<int64_t>(qt - t_off) * ld + j0) = v;
         if (aux.gmax) {
           // group maxima: the 4 lanes of a row's 16-key quarter hold its 16
           // cells; cells past the query's visible count do not count
-          int64_t nv = qt < t_end ? n_visible(q_pos0 + qt, m) : 0;
-          if (nv > N_cap) nv = N_cap;
-          const int64_t j0 = jt0 + 4 * c4;
+          const int64_t nv = nv_l[i];
           float mx = -INFINITY;
           mx = j0 < nv ? fmaxf(mx, v.x) : mx;
           mx = j0 + 1 < nv ? fmaxf(mx, v.y) : mx;
@@ -350,12 +615,16 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
 #pragma unroll
           for (int o = 1; o < 4; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
           const int64_t grp = jt0 / kGroup + (c4 >> 2);
-          if ((c4 & 3) == 0 && qt < t_end && grp * kGroup < nv)
-            aux.gmax[(static_cast<int64_t>(b) * Tc + qt - t_off) * aux.ldg + grp] = mx;
+          if ((c4 & 3) == 0 && qt < t_end && grp * kGroup < nv) aux.gmax[rix * aux.ldg + grp] = mx;
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // reads done before the next tile's staging
     }
+  }
+  if constexpr (MODE == kTiledCands) {
+#pragma unroll
+    for (int ci = 0; ci < 2 * MB; ++ci)
+      if (r16 == 0 && writer_l[ci]) aux.cnt[rix_l[ci] * aux.nchs + kr] = (run_a[ci] << 16) | run_e[ci];
   }
 }
 
@@ -487,15 +756,6 @@ constexpr int kSelItems = 32;                   // scores per thread per round
 constexpr int kRound = kSelThreads * kSelItems; // scores per round (registers)
 constexpr int kMaxBins = 4096;
 
-// Order-preserving key: larger score -> larger unsigned key; -0 folds into +0.
-// Key 0 never comes from a real number (it would be a NaN pattern), so it
-// marks "no element" below.
-__device__ __forceinline__ uint32_t score_key(float v, bool key16) {
-  if (v == 0.f) v = 0.f;
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return key16 ? (k >> 16) : k;
-}
 
 // Inclusive scan over the 64 lanes of a wave in registers (DPP): shifts of
 // 1, 2, 4, 8 lanes inside each 16-lane row, then the row totals carried across
@@ -1161,11 +1421,19 @@ __device__ __forceinline__ void group_bound(const float* __restrict__ gm, int64_
 #pragma unroll
   for (int i = 0; i < BI; ++i) fm[i] = -INFINITY;
   for (int64_t d = 0; d < gs; ++d) {
+    // every load of the pass is issued unconditionally (out-of-row items read
+    // group 0) before any is used
+    float x[BI];
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
       const int64_t sg = 4 * (static_cast<int64_t>(kWave) * i + lane) + wid;
       const int64_t gg = sg * gs + d;
-      if (sg < ns && gg < ng) fm[i] = fmaxf(fm[i], gm[gg]);
+      x[i] = gm[sg < ns && gg < ng ? gg : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int64_t sg = 4 * (static_cast<int64_t>(kWave) * i + lane) + wid;
+      if (sg < ns && sg * gs + d < ng) fm[i] = fmaxf(fm[i], x[i]);
     }
   }
   uint32_t kv[BI], mx = 0;
@@ -1480,11 +1748,24 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t* keys, int n, uint32
   return base;
 }
 
-// One workgroup per row: the selection from the chunks' candidates.
+// The score a selection key stands for (score_key inverted; with 16-bit keys
+// the score was rounded to bf16, so its low 16 bits are zero). -0 comes back
+// as +0, which compares equal.
+__device__ __forceinline__ float key_score(uint32_t k, bool key16) {
+  uint32_t u;
+  if (key16) u = (k & 0x8000u) ? (k & 0x7fffu) << 16 : (~k & 0xffffu) << 16;
+  else u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// One workgroup per row: the selection from the chunks' candidates. chunk:
+// scores per chunk (the row has ceil(n / chunk) chunks); e_off: where a
+// chunk's equal list starts in its slots (0: right after its above list);
+// have_scores: the row's scores are in memory (the full passes can run).
 __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
     const float* __restrict__ scores, int64_t ld, FiltWs fw, int64_t N_cap, int Tq, int t_off, int Tc,
     int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int k, bool key16, int32_t* __restrict__ idx_out,
-    float* __restrict__ score_out) {
+    float* __restrict__ score_out, int64_t chunk, int64_t e_off, bool have_scores) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[kMaxBins];   // staged keys / histograms
   __shared__ uint32_t preA[kMaxChunks + 1], preE[kMaxChunks + 1];
   __shared__ __attribute__((aligned(16))) uint32_t whist[kFiltThreads / 64][256];
@@ -1494,15 +1775,17 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
   const int wid = tid >> 6;
   const FiltRow row = filt_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, q_pos, m, k, idx_out, score_out);
   if (row.n <= k) {                                      // every visible entry, then -1
+    // (rows without stored scores are never this short: the host sends only
+    // rows longer than k down that path)
     for (int i = tid; i < k; i += kFiltThreads) {
       row.io[i] = i < row.n ? i : -1;
-      if (row.so) row.so[i] = i < row.n ? row.s[i] : -INFINITY;
+      if (row.so) row.so[i] = i < row.n && have_scores ? row.s[i] : -INFINITY;
     }
     return;
   }
-  const int nch = static_cast<int>((row.n + kFiltChunk - 1) / kFiltChunk);
-  if (nch > kMaxChunks) {
-    select_passes_t<kFiltThreads>(row, k, key16, hist, wsum, &sh_digit, &sh_krem);
+  const int nch = static_cast<int>((row.n + chunk - 1) / chunk);
+  if (nch > kMaxChunks) {                                // (the host keeps the candidate passes within this)
+    if (have_scores) select_passes_t<kFiltThreads>(row, k, key16, hist, wsum, &sh_digit, &sh_krem);
     return;
   }
   const uint32_t lo = fw.bound[2 * row.r], hi = fw.bound[2 * row.r + 1];
@@ -1537,16 +1820,15 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
     re += ce[q];
   }
   const bool above = G >= static_cast<uint32_t>(k);      // the k-th largest lies above lo
-  if (tid == 0 && above && G > static_cast<uint32_t>(kFiltThreads * kRunMax)) sh_fallback = 1;
   __syncthreads();
-  if (sh_fallback) {
+  if (sh_fallback && have_scores) {                      // a chunk ran out of slots
     select_passes_t<kFiltThreads>(row, k, key16, hist, wsum, &sh_digit, &sh_krem);
     return;
   }
   const int64_t rbase = row.r * fw.nchs;
   const uint32_t* ckr = fw.ckey + rbase * fw.capc;
   const int32_t* cir = fw.cidx + rbase * fw.capc;
-  if (above) {
+  if (above && G <= static_cast<uint32_t>(kFiltThreads * kRunMax)) {
     // the candidates above lo, concatenated over the chunks: this thread's run [p0, p1)
     const uint32_t per = (G + kFiltThreads - 1) / kFiltThreads;
     const uint32_t p0 = min(G, per * tid), p1 = min(G, p0 + per);
@@ -1615,10 +1897,56 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
       bool take = rk[q] > thr;
       if (rk[q] == thr) take = eq_rank++ < krem;
       if (take) {
-        const int32_t ix = cir[rc[q]];
-        row.io[pos] = ix;
-        if (row.so) row.so[pos] = row.s[ix];
+        row.io[pos] = cir[rc[q]];
+        if (row.so) row.so[pos] = key_score(rk[q], key16);
         ++pos;
+      }
+    }
+    return;
+  }
+  if (above) {
+    // more candidates than the threads hold: streamed from their chunk lists,
+    // radix passes over all of them, then the output chunk by chunk
+    uint32_t base = lo + 1u, krem = static_cast<uint32_t>(k);
+    uint64_t width = static_cast<uint64_t>(hi) - lo;
+    while (width > 1) {
+      const int bl = 64 - __builtin_clzll(width - 1);
+      const int sh = bl > 12 ? bl - 12 : 0;
+      const int nb = static_cast<int>((width - 1) >> sh) + 1;
+      for (int i = tid; i < nb; i += kFiltThreads) hist[i] = 0;
+      __syncthreads();
+      for (int ch = 0; ch < nch; ++ch)
+        for (uint32_t i = tid; i < preA[ch + 1] - preA[ch]; i += kFiltThreads) {
+          const uint32_t kk = ckr[static_cast<int64_t>(ch) * fw.capc + i];
+          const uint32_t off = kk - base;
+          if (kk >= base && static_cast<uint64_t>(off) < width) atomicAdd(&hist[off >> sh], 1u);
+        }
+      __syncthreads();
+      find_digit_t<kFiltThreads>(hist, nb, krem, wsum, &sh_digit, &sh_krem);
+      base += sh_digit << sh;
+      krem = sh_krem;
+      width = uint64_t(1) << sh;
+    }
+    const uint32_t thr = base;
+    uint32_t run_gt = 0, run_eq = 0;
+    for (int ch = 0; ch < nch; ++ch) {
+      const uint32_t cn = preA[ch + 1] - preA[ch];
+      for (uint32_t s0 = 0; s0 < cn; s0 += kFiltThreads) {
+        const uint32_t i = s0 + tid;
+        const int64_t ci = static_cast<int64_t>(ch) * fw.capc + i;
+        const uint32_t kk = i < cn ? ckr[ci] : 0u;
+        const uint32_t gt = i < cn && kk > thr, eq = i < cn && kk == thr;
+        uint32_t tg, te;
+        const uint32_t pg = block_excl_scan_t<kFiltThreads>(gt, wsum, &tg);
+        const uint32_t pe = block_excl_scan_t<kFiltThreads>(eq, wsum, &te);
+        const uint32_t eq_rank = run_eq + pe;
+        if (gt || (eq && eq_rank < krem)) {
+          const uint32_t pos = run_gt + pg + min(eq_rank, krem);
+          row.io[pos] = cir[ci];
+          if (row.so) row.so[pos] = key_score(kk, key16);
+        }
+        run_gt += tg;
+        run_eq += te;
       }
     }
     return;
@@ -1630,25 +1958,21 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
   // the chunk's offset plus its rank in its own list plus the entries of the
   // other list below it (a binary search).
   const uint32_t krem = static_cast<uint32_t>(k) - G;
-  auto take_of = [&](int ch) {
-    const uint32_t eb = preE[ch], e = preE[ch + 1] - eb;
-    return eb >= krem ? 0u : min(e, krem - eb);
-  };
-  // chunk offsets of the output: A before it plus ties taken before it
-  auto out_of = [&](int ch) { return preA[ch] + min(preE[ch], krem); };
+  const float lo_score = key_score(lo, key16);
   for (int ch = wid; ch < nch; ch += kFiltThreads / 64) {
-    const uint32_t a_n = preA[ch + 1] - preA[ch], t_n = take_of(ch);
+    const uint32_t a_n = preA[ch + 1] - preA[ch];
+    const uint32_t eb = preE[ch], e_n = preE[ch + 1] - eb;
+    const uint32_t t_n = eb >= krem ? 0u : min(e_n, krem - eb);
     if (a_n + t_n == 0) continue;
-    const uint32_t off = out_of(ch);
-    const uint32_t* kk = ckr + static_cast<int64_t>(ch) * fw.capc;
+    const uint32_t off = preA[ch] + min(eb, krem);       // winners before this chunk
     const int32_t* ii = cir + static_cast<int64_t>(ch) * fw.capc;
-    const int32_t* ties = ii + a_n;                      // the equal list follows the above list
+    const uint32_t* kk = ckr + static_cast<int64_t>(ch) * fw.capc;
+    const int32_t* ties = ii + (e_off ? e_off : static_cast<int64_t>(a_n));
     for (uint32_t i = tid & 63; i < a_n + t_n; i += kWave) {
       const bool is_a = i < a_n;
       const uint32_t r = is_a ? i : i - a_n;
-      const int32_t x = ii[is_a ? r : a_n + r];
-      // entries of the other list below x
-      const int32_t* other = is_a ? ties : ii;
+      const int32_t x = is_a ? ii[r] : ties[r];
+      const int32_t* other = is_a ? ties : ii;            // entries of the other list below x
       uint32_t lo_i = 0, hi_i = is_a ? t_n : a_n;
       while (lo_i < hi_i) {
         const uint32_t mid = (lo_i + hi_i) >> 1;
@@ -1657,8 +1981,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
       }
       const uint32_t pos = off + r + lo_i;
       row.io[pos] = x;
-      if (row.so) row.so[pos] = row.s[x];
-      (void)kk;
+      if (row.so) row.so[pos] = is_a ? key_score(kk[r], key16) : lo_score;
     }
   }
 }
@@ -1700,16 +2023,61 @@ bool long_old_possible(const IndexArgs& a) {
   return ng / 4 < 2 * ((a.k + 3) / 4) || (a.dt == LCA_BF16 && a.d_I == 128 && a.H_I == 1);
 }
 
+// The prefill path that stores no scores: tiled scoring writes only the group
+// maxima, topk_bound_kernel takes each row's bound from them, tiled scoring
+// runs again and writes only each row's candidates against its bound (per key
+// range of a workgroup, with room for the whole range, so nothing overflows),
+// and topk_final_kernel selects. Writing and reading every score costs more
+// than the second pass of MFMA scoring. For calls of many queries (the tiled
+// kernel, bf16 keys of 128 channels, H_I >= 2, its staged tile), one position
+// for the batch, long lists, and every row longer than k (so every output
+// score comes from a candidate's key).
+bool cand_mode(const IndexArgs& a) {
+  if (!(a.dt == LCA_BF16 && a.d_I == 128 && a.H_I >= 2 && a.Tq >= kTiledMinQueries && !a.q_pos)) return false;
+  int64_t nv0 = n_visible(a.q_pos0, a.m), nv1 = n_visible(a.q_pos0 + a.Tq - 1, a.m);
+  if (nv0 > a.N_cap) nv0 = a.N_cap;
+  if (nv1 > a.N_cap) nv1 = a.N_cap;
+  return nv0 > a.k && nv1 > kRound;
+}
+
+// key ranges of the tiled kernel: about 2048 workgroups over (keys, queries);
+// in candidate mode at most kMaxChunks ranges (the final kernel's count
+// table) of at most 32768 keys (the counts pack in 16 bits)
+void tiled_ranges(const IndexArgs& a, int64_t nv_max, int tcn, bool cands, int64_t* kc_out, int64_t* per_out) {
+  const int qpwg = 4 * 4 * (16 / a.H_I);
+  const int64_t n_qt = (tcn + qpwg - 1) / qpwg;
+  int64_t kc = (2048 + n_qt * a.B - 1) / (n_qt * a.B);
+  const int64_t kc_max = (nv_max + 255) / 256;
+  if (kc > kc_max) kc = kc_max;
+  if (cands) {
+    if (kc < (nv_max + 32767) / 32768) kc = (nv_max + 32767) / 32768;
+    if (kc > kMaxChunks) kc = kMaxChunks;
+  }
+  if (kc < 1) kc = 1;
+  int64_t per = (nv_max + kc - 1) / kc;
+  per = (per + kTileKeys - 1) / kTileKeys * kTileKeys;
+  *kc_out = (nv_max + per - 1) / per;
+  *per_out = per;
+}
+
+// candidate slots per row in candidate mode: 2 per key of every range
+// (kc * per <= nv + 64 kc and per >= 256, so under 2.5 ld)
+int64_t cand_slots(int64_t ld) { return (ld * 5 + 1) / 2 + 2 * kTileKeys; }
+
 // queries per chunk so that the score buffer and the select's side arrays stay
-// under a fixed budget
+// under a fixed budget (in candidate mode: the candidate slots, in whole tiles
+// of queries)
 int query_chunk(const IndexArgs& a) {
   const int64_t ld = score_ld(a);
-  const int64_t per_q = static_cast<int64_t>(a.B) * (ld * (long_old_possible(a) ? 8 : 4) + filt_row_bytes(ld));
-  const int64_t budget = int64_t(640) << 20;
+  const bool cm = cand_mode(a);
+  const int64_t per_q = cm ? static_cast<int64_t>(a.B) * (ld / kGroup * 4 + 8 + kMaxChunks * 4 + cand_slots(ld) * 8)
+                           : static_cast<int64_t>(a.B) * (ld * (long_old_possible(a) ? 8 : 4) + filt_row_bytes(ld));
+  const int64_t budget = cm ? int64_t(4) << 30 : int64_t(640) << 20;
   int64_t tc = per_q > 0 ? budget / per_q : a.Tq;
   if (tc < 1) tc = 1;
   if (tc > a.Tq) tc = a.Tq;
-  if (tc < a.Tq && tc >= 16) tc -= tc % 16;          // whole M tiles per chunk
+  const int gran = cm ? kTiledMinQueries : 16;
+  if (tc < a.Tq && tc >= gran) tc -= tc % gran;      // whole query tiles per chunk
   return static_cast<int>(tc);
 }
 
@@ -1725,19 +2093,21 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 IndexWs index_ws(const IndexArgs& a, void* base) {
   const int Tc = query_chunk(a);
+  const bool cm = cand_mode(a);
   const int64_t ld = score_ld(a), rows = static_cast<int64_t>(a.B) * Tc;
   char* p = static_cast<char*>(base);
   size_t off = 0;
   auto take = [&](size_t n) { char* q = p ? p + off : nullptr; off += align256(n); return q; };
   IndexWs w;
-  w.sc = reinterpret_cast<float*>(take(rows * ld * 4));
-  w.spill = reinterpret_cast<int32_t*>(take(long_old_possible(a) ? rows * ld * 4 : 0));
+  w.sc = reinterpret_cast<float*>(take(cm ? 0 : rows * ld * 4));
+  w.spill = reinterpret_cast<int32_t*>(take(!cm && long_old_possible(a) ? rows * ld * 4 : 0));
   w.fw.ldg = ld / kGroup;
-  w.fw.nchs = static_cast<int>(filt_nchs(ld));
+  w.fw.nchs = cm ? kMaxChunks : static_cast<int>(filt_nchs(ld));
   w.fw.capc = filt_capc(ld);
+  const int64_t slots = cm ? cand_slots(ld) : w.fw.nchs * int64_t(w.fw.capc);   // per row
   w.fw.gmax = reinterpret_cast<float*>(take(rows * w.fw.ldg * 4));
-  w.fw.ckey = reinterpret_cast<uint32_t*>(take(rows * w.fw.nchs * w.fw.capc * 4));
-  w.fw.cidx = reinterpret_cast<int32_t*>(take(rows * w.fw.nchs * w.fw.capc * 4));
+  w.fw.ckey = reinterpret_cast<uint32_t*>(take(rows * slots * 4));
+  w.fw.cidx = reinterpret_cast<int32_t*>(take(rows * slots * 4));
   w.fw.cnt = reinterpret_cast<uint32_t*>(take(rows * w.fw.nchs * 4));
   w.fw.bound = reinterpret_cast<uint32_t*>(take(rows * 8));
   w.bytes = off + 256;
@@ -1747,6 +2117,33 @@ IndexWs index_ws(const IndexArgs& a, void* base) {
 }  // namespace
 
 size_t index_topk_workspace(const IndexArgs& a) { return index_ws(a, nullptr).bytes; }
+
+template <int MODE>
+void launch_tiled(LaunchScope& scope, const IndexArgs& a, int64_t kc, int tcn, float* sc, int64_t ld, int t_off,
+                  int Tc, int64_t per, bool key16, SelAux aux) {
+  const uint16_t* q = static_cast<const uint16_t*>(a.qI);
+  const uint16_t* k = static_cast<const uint16_t*>(a.kI);
+  const int qpwg = 4 * 4 * (16 / a.H_I);
+  const int nq = (tcn + qpwg - 1) / qpwg;
+  const int64_t pairs = (kc * a.B + 7) / 8 * 8;        // (sequence, key range) pairs, padded
+  const dim3 grid(static_cast<uint32_t>(pairs * nq));
+  const int kci = static_cast<int>(kc);
+#define LCA_TILED(H)                                                                                         \
+  (key16 ? scope.launch(index_score_tiled_kernel<H, MODE, true>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, \
+                        a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, aux, kci, nq, a.B)                 \
+         : scope.launch(index_score_tiled_kernel<H, MODE, false>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, \
+                        a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, aux, kci, nq, a.B))
+  switch (a.H_I) {
+    case 1:
+      if constexpr (MODE == kTiledScores) LCA_TILED(1);
+      break;
+    case 2: LCA_TILED(2); break;
+    case 4: LCA_TILED(4); break;
+    case 8: LCA_TILED(8); break;
+    default: LCA_TILED(16); break;
+  }
+#undef LCA_TILED
+}
 
 // The select of one chunk of queries whose longest list is nv_max: the
 // chunked select serves lists longer than one register round (one workgroup
@@ -1774,14 +2171,52 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
     if (nv_max > kRound && nv_max > a.k && !use_chunked(a, nv_max, tiled) && !long_old_possible(a))
       return hipErrorInvalidValue;
   }
+  const bool cm = cand_mode(a);
   for (int t_off = 0; t_off < a.Tq; t_off += Tc) {
     const int tcn = min(Tc, a.Tq - t_off);
     int64_t nv_max = n_visible(a.q_pos0 + t_off + tcn - 1, a.m);
     if (nv_max > a.N_cap) nv_max = a.N_cap;
+    if (cm) {
+      // no scores stored: maxima, bound, candidates, final
+      int64_t kc, per;
+      tiled_ranges(a, nv_max, tcn, true, &kc, &per);
+      FiltWs fw = w.fw;
+      fw.nchs = static_cast<int>(kc);
+      fw.capc = static_cast<int>(2 * per);
+      SelAux aux{fw.gmax, fw.ldg, fw.bound, fw.ckey, fw.cidx, fw.cnt, fw.nchs, fw.capc};
+      {
+        LaunchScope scope(s, "index_score");
+        launch_tiled<kTiledMaxima>(scope, a, kc, tcn, nullptr, ld, t_off, Tc, per, key16, aux);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      {
+        LaunchScope scope(s, "topk_select");
+        scope.launch(topk_bound_kernel, dim3(1, tcn, a.B), dim3(kFiltThreads), 0, fw, a.N_cap, Tc, a.q_pos0,
+                     a.q_pos, t_off, a.m, a.k, key16);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      {
+        LaunchScope scope(s, "index_score");
+        launch_tiled<kTiledCands>(scope, a, kc, tcn, nullptr, ld, t_off, Tc, per, key16, aux);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      {
+        LaunchScope scope(s, "topk_select");
+        scope.launch(topk_final_kernel, dim3(1, tcn, a.B), dim3(kFiltThreads), 0, static_cast<const float*>(nullptr),
+                     ld, fw, a.N_cap, a.Tq, t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16, a.idx_out, a.score_out,
+                     per, per, false);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      continue;
+    }
     const bool tiled = a.dt == LCA_BF16 && a.d_I == 128 && tcn >= kTiledMinQueries;
     const int64_t ng_max = (nv_max + kGroup - 1) / kGroup;
     const bool filt = use_chunked(a, nv_max, tiled);
-    SelAux aux{filt ? w.fw.gmax : nullptr, w.fw.ldg};
+    SelAux aux{filt ? w.fw.gmax : nullptr, w.fw.ldg, nullptr, nullptr, nullptr, nullptr, 0, 0};
     if (nv_max > 0) {
       LaunchScope scope(s, "index_score");
       if (a.dt == LCA_F32) {
@@ -1806,25 +2241,9 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
         }
       } else if (tiled) {
         // many queries: key tiles through LDS, ~2048 workgroups over (keys, queries)
-        const int qpwg = 4 * 4 * (16 / a.H_I);
-        const int64_t n_qt = (tcn + qpwg - 1) / qpwg;
-        int64_t kc = (2048 + n_qt * a.B - 1) / (n_qt * a.B);
-        const int64_t kc_max = (nv_max + 255) / 256;
-        if (kc > kc_max) kc = kc_max;
-        if (kc < 1) kc = 1;
-        int64_t per = (nv_max + kc - 1) / kc;
-        per = (per + kTileKeys - 1) / kTileKeys * kTileKeys;
-        kc = (nv_max + per - 1) / per;
-        dim3 grid(static_cast<uint32_t>(kc), static_cast<uint32_t>(n_qt), a.B);
-        const uint16_t* q = static_cast<const uint16_t*>(a.qI);
-        const uint16_t* k = static_cast<const uint16_t*>(a.kI);
-        switch (a.H_I) {
-          case 1: scope.launch(index_score_tiled_kernel<1>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
-          case 2: scope.launch(index_score_tiled_kernel<2>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
-          case 4: scope.launch(index_score_tiled_kernel<4>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
-          case 8: scope.launch(index_score_tiled_kernel<8>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
-          default: scope.launch(index_score_tiled_kernel<16>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, key16, aux); break;
-        }
+        int64_t kc, per;
+        tiled_ranges(a, nv_max, tcn, false, &kc, &per);
+        launch_tiled<kTiledScores>(scope, a, kc, tcn, sc, ld, t_off, Tc, per, key16, aux);
       } else {
         const int QPB = 16 / a.H_I;
         dim3 grid((nv_max + kKeysPerWG - 1) / kKeysPerWG, (tcn + QPB - 1) / QPB, a.B);
@@ -1854,7 +2273,8 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
                        a.q_pos0, a.q_pos, a.m, a.k, key16);
         }
         scope.launch(topk_final_kernel, dim3(1, tcn, a.B), dim3(kFiltThreads), 0, scs, ld, w.fw, a.N_cap, a.Tq,
-                     t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16, a.idx_out, a.score_out);
+                     t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16, a.idx_out, a.score_out,
+                     static_cast<int64_t>(kFiltChunk), static_cast<int64_t>(0), true);
       } else if (nv_max > kRound) {
         // every row's list is at most nv_max long (and nv_max > kRound implies N_cap > kRound)
         scope.launch(topk_select_long_kernel, dim3(tcn, a.B), dim3(kSelThreads), 0, static_cast<const float*>(sc), ld,

@@ -149,6 +149,13 @@ __device__ __forceinline__ void rope_sincos(double pos, int i, int R, double bas
   *c = cosf(a);
 }
 
-__host__ __device__ __forceinline__ int64_t n_visible(int64_t p, int m) { return (p + 1) / m; }
+// Entries visible at position p (p >= 0, m >= 1): (p + 1) / m. Positions below
+// 2^32 take a 32-bit unsigned division (a 64-bit one costs several times the
+// instructions, and kernels evaluate this in their prologues).
+__host__ __device__ __forceinline__ int64_t n_visible(int64_t p, int m) {
+  const uint64_t q = static_cast<uint64_t>(p) + 1u;
+  if (q <= 0xffffffffull) return static_cast<int64_t>(static_cast<uint32_t>(q) / static_cast<uint32_t>(m));
+  return static_cast<int64_t>(q / static_cast<uint64_t>(m));
+}
 
 }  // namespace lca

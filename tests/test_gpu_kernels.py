@@ -500,6 +500,49 @@ def test_index_topk_long_exact_order(case, bf16_scores):
     np.testing.assert_array_equal(gs[0, 0], sc[want].astype(np.float32))
 
 
+@pytest.mark.parametrize("case,H_I", [("mixed_w", 4), ("cluster", 4), ("mixed_w", 2), ("mixed_w", 8)])
+@pytest.mark.parametrize("bf16_scores", [False, True])
+def test_index_topk_prefill_without_stored_scores(case, H_I, bf16_scores):
+    # Many queries over long lists take the prefill path that stores no
+    # scores: tiled scoring writes group maxima, the bound kernel bounds each
+    # row, tiled scoring runs again and writes only the candidates, the final
+    # kernel selects (output scores rebuilt from the candidates' keys). Exact
+    # integer scores; per-query head weights, one query in four with all of
+    # them negative (the k-th score is 0, a crowd of ties at the bound);
+    # cluster: the highest scores of every query crowd 3 key ranges, more
+    # candidates than the final workgroup holds in registers. H_I = 2 puts
+    # two queries in each lane's accumulators, H_I = 8 one query in two lane
+    # groups.
+    L = need_gpu()
+    rng = np.random.default_rng(540 + 3 * bf16_scores + len(case) + H_I)
+    B, Tq, d_I, m, k = 1, 70, 128, 4, 1024
+    q_pos0 = 4 * 140000
+    N_cap = (q_pos0 + Tq) // m + 3
+    qI = rng.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.float32)
+    kI = rng.integers(-8, 9, size=(B, N_cap, d_I)).astype(np.float32)
+    w = np.tile((0.5 ** np.arange(H_I)).astype(np.float32), (B, Tq, 1))
+    w[:, ::4] *= -1
+    if case == "cluster":
+        w = np.abs(w)
+        kI[0, 60000:63072] *= 3
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    say(f"prefill without stored scores {case} H_I={H_I} bf16={bf16_scores}")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
+                     flags=L.SCORE_BF16 if bf16_scores else 0, score_out=sco)
+    torch.cuda.synchronize()
+    got, gs = idx.cpu().numpy(), sco.cpu().numpy()
+    for t in range(Tq):
+        nv = O.n_visible(q_pos0 + t, m)
+        sc = O.index_scores(qI[0, t], w[0, t], kI[0], nv)
+        assert np.all(np.abs(sc) < 2.0 ** 23), "scores must stay exact in fp32"
+        if bf16_scores:
+            sc = O.bf16_round(sc)
+        want = np.sort(np.lexsort((np.arange(nv), -sc))[:k])
+        np.testing.assert_array_equal(got[0, t], want, err_msg=f"{case} t={t}")
+        np.testing.assert_array_equal(gs[0, t], sc[want].astype(np.float32), err_msg=f"{case} t={t}")
+
+
 def test_index_topk_long_ragged_rows():
     # A ragged batch bounded at 140000 entries: the long rows take the chunked
     # select with a bound, the short ones (5000, 300 entries) have too few
