@@ -41,10 +41,32 @@ import workloads as WL  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 COPY_REPS = 3                  # calibration copies per counter run
 DEV = "cuda"
-# sources of the CSA decode scoring kernel: stored counter readings hold for these bytes only
-SCORE_SOURCES = ["long_context_attention_12_amd/csrc/index_topk.hip",
-                 "long_context_attention_12_amd/csrc/lca_device.h",
-                 "long_context_attention_12_amd/csrc/lca_internal.h"]
+MFMA_BF16_PEAK = 2.5e15        # dense bf16 MFMA, FLOP/s
+N_CU = 256
+N_XCD = 8
+# sources of each kernel: stored counter readings hold for these bytes only
+_HDRS = ["long_context_attention_12_amd/csrc/lca_device.h", "long_context_attention_12_amd/csrc/lca_internal.h"]
+SCORE_SOURCES = ["long_context_attention_12_amd/csrc/index_topk.hip"] + _HDRS
+ATTEND_SOURCES = ["long_context_attention_12_amd/csrc/attend.hip"] + _HDRS
+# kernels whose HBM traffic (FETCH_SIZE, WRITE_SIZE) a counter run of one leg
+# records: leg -> [(key, kernel-name substring, sources)]
+TRAFFIC_KERNELS = {
+    "csa": ("csa_decode_b16_ctx131072", [("index_score", "index_score_bf16_kernel", SCORE_SOURCES),
+                                         ("topk_select", "topk_select_kernel", SCORE_SOURCES),
+                                         ("csa_attend", "attend_dma_kernel<1>", ATTEND_SOURCES),
+                                         ("csa_combine", "combine4_kernel<true>", ATTEND_SOURCES)]),
+    "hca": ("hca_decode_b8_ctx1048576", [("hca_attend", "attend_dma_kernel<1>", ATTEND_SOURCES),
+                                         ("hca_combine", "combine4_kernel<true>", ATTEND_SOURCES)]),
+    "mixed": ("mixed_csa_hca_pair_b64_ctx1048576", [("index_score", "index_score_fp4_kernel", SCORE_SOURCES),
+                                                    ("attend_mixed", "attend_mixed_dma_kernel<2>", ATTEND_SOURCES)]),
+}
+# kernels whose MFMA counters the prefill counter run records
+MFMA_KERNELS = {"prefill": ("csa_prefill_tq4096_ctx1048576",
+                            [("index_score_tiled_maxima", "index_score_tiled_kernel<4, 1, false>", SCORE_SOURCES),
+                             ("index_score_tiled_cands", "index_score_tiled_kernel<4, 2, false>", SCORE_SOURCES),
+                             ("csa_attend", "attend_dma_kernel<2>", ATTEND_SOURCES)])}
+SQ_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVES",
+               "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE"]
 
 
 def _bf16(x):
@@ -531,6 +553,21 @@ def ragged_leg(d, copies, steps, warmup, seed, uniform_ms):
             "hbm_frac": rb / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def csa_prefill_flops_split(Tq=4096, ctx=1048576, m=4, H_I=4, d_I=128, H=128, D=512, k=1024, W=128):
+    """Algorithmic flops of the prefill's indexer scoring (every visible key of
+    every query, H_I heads of d_I) and of its attention (k selected + W window
+    rows per query and head, QK^T and PV)."""
+    nv = sum((ctx + t + 1) // m for t in range(Tq))
+    return 2.0 * nv * H_I * d_I, 4.0 * Tq * H * (k + W) * D
+
+
+def mixed_hca_work(B=64, ctx=1048576, m2=128, H=128, D=512, W=128):
+    """Flops and HBM bytes of the mixed pair's HCA attention: every entry and
+    window row (576 stored bytes + a 4-byte scale) for all heads, q in, out."""
+    rows = ctx // m2 + W
+    return 4.0 * B * H * rows * D, B * (rows * (D + 64 + 4) + 2 * H * D * 2)
+
+
 def hca_decode_flops(d):
     B, H, D, W = d["B"], d["H"], d["D"], d["W"]
     N = d["E"].shape[1]
@@ -583,39 +620,84 @@ def _read_counter_csv(path, counter):
     return rows
 
 
-def pmc_summary(fetch_csv, write_csv, copy_mib, out_json):
-    """Turn two rocprofv3 --pmc runs of ``bench.py --copy-calibration MIB`` (one
-    with FETCH_SIZE, one with WRITE_SIZE) into HBM bytes per launch of the index
-    scoring kernel. Each counter is scaled by what it reads for the plain copy of
-    known size: the last COPY_REPS copy dispatches of the run."""
+def _merge_json(path, workload, recs):
+    try:
+        allrec = json.load(open(path))
+    except (OSError, ValueError):
+        allrec = {}
+    allrec.setdefault(workload, {}).update(recs)
+    with open(path, "w") as f:
+        json.dump(allrec, f, indent=1)
+
+
+def pmc_summary(leg, fetch_csv, write_csv, copy_mib, out_json):
+    """Turn two rocprofv3 --pmc runs of ``bench.py --only LEG --copy-calibration
+    MIB`` (one with FETCH_SIZE, one with WRITE_SIZE) into HBM bytes per launch of
+    the leg's kernels. Each counter is scaled by what it reads for the plain copy
+    of known size: the last COPY_REPS copy dispatches of the run."""
     n = copy_mib << 20
+    workload, kernels = TRAFFIC_KERNELS[leg]
 
     def stats(path, counter):
         rows = _read_counter_csv(path, counter)
         copies = [r for r in rows if "copyBuffer" in r[1]][-COPY_REPS:]
-        score = [r for r in rows if "index_score_bf16_kernel" in r[1]]     # the CSA decode scoring kernel
-        if len(copies) < COPY_REPS or not score:
-            raise SystemExit(f"{path}: calibration copies or index_score dispatches missing")
-        c = sum(r[3] for r in copies) / len(copies)
-        k = sum(r[3] for r in score) / len(score)
-        return c, k, score[0][1], len(score)
+        if len(copies) < COPY_REPS:
+            raise SystemExit(f"{path}: calibration copies missing")
+        out = {}
+        for key, pat, _ in kernels:
+            ks = [r for r in rows if pat in r[1]]
+            if ks:
+                out[key] = (sum(r[3] for r in ks) / len(ks), ks[0][1], len(ks))
+        return sum(r[3] for r in copies) / len(copies), out
 
-    cf, kf, name, nd = stats(fetch_csv, "FETCH_SIZE")
-    cw, kw, _, _ = stats(write_csv, "WRITE_SIZE")
-    f_scale = n / (cf * 1024.0)
-    w_scale = n / (cw * 1024.0)
-    fb, wb = kf * 1024.0 * f_scale, kw * 1024.0 * w_scale
-    src = source_hash(SCORE_SOURCES)
-    rec = {"csa_decode_b16_ctx131072": {"index_score": {
-        "source_hash": src, "kernel": name, "dispatches": nd,
-        "fetch_kib_raw": kf, "write_kib_raw": kw, "copy_bytes": n,
-        "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
-        "fetch_scale": f_scale, "write_scale": w_scale,
-        "hbm_read_bytes_per_launch": fb, "hbm_write_bytes_per_launch": wb,
-        "hbm_bytes_per_launch": fb + wb}}}
-    with open(out_json, "w") as f:
-        json.dump(rec, f, indent=1)
-    print(json.dumps(rec, indent=1))
+    cf, kf = stats(fetch_csv, "FETCH_SIZE")
+    cw, kw = stats(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = n / (cf * 1024.0), n / (cw * 1024.0)
+    recs = {}
+    for key, pat, srcs in kernels:
+        if key not in kf or key not in kw:
+            continue
+        fb, wb = kf[key][0] * 1024.0 * f_scale, kw[key][0] * 1024.0 * w_scale
+        recs[key] = {"source_hash": source_hash(srcs), "kernel": kf[key][1], "dispatches": kf[key][2],
+                     "fetch_kib_raw": kf[key][0], "write_kib_raw": kw[key][0], "copy_bytes": n,
+                     "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
+                     "fetch_scale": f_scale, "write_scale": w_scale,
+                     "hbm_read_bytes_per_launch": fb, "hbm_write_bytes_per_launch": wb,
+                     "hbm_bytes_per_launch": fb + wb}
+    _merge_json(out_json, workload, recs)
+    print(json.dumps({workload: recs}, indent=1))
+
+
+def sq_summary(leg, csv_path, out_json):
+    """MFMA counters per dispatch (averaged over the leg's dispatches of each
+    kernel) from one rocprofv3 --pmc run with SQ_COUNTERS. MFMA busy is
+    SQ_VALU_MFMA_BUSY_CYCLES (SIMD-cycles of matrix-core work: the bf16 flops
+    over 1024) over the kernel's cycles times the 4 SIMDs of each of the 256
+    CUs; the kernel's cycles are GRBM_GUI_ACTIVE over the 8 XCDs, whose
+    counts it sums. Flops are the bf16 MFMA ops counter times 512."""
+    import csv
+    workload, kernels = MFMA_KERNELS[leg]
+    per = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            for key, pat, _ in kernels:
+                if pat in row["Kernel_Name"]:
+                    d = per.setdefault(key, {"kernel": row["Kernel_Name"], "dispatch": set(), "sum": {}})
+                    d["dispatch"].add(row["Dispatch_Id"])
+                    d["sum"][row["Counter_Name"]] = d["sum"].get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    recs = {}
+    for key, pat, srcs in kernels:
+        if key not in per:
+            continue
+        d = per[key]
+        nd = len(d["dispatch"])
+        c = {k: v / nd for k, v in d["sum"].items()}
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(1.0, c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD * N_CU * 4)
+        recs[key] = {"source_hash": source_hash(srcs), "kernel": d["kernel"], "dispatches": nd,
+                     "counters_per_dispatch": c, "mfma_busy_frac": busy,
+                     "mfma_bf16_flops_per_dispatch": c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512}
+    _merge_json(out_json, workload, recs)
+    print(json.dumps({workload: recs}, indent=1))
 
 
 def _cpu_model():
@@ -701,12 +783,19 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device (counter calibration)")
-    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="summarise two rocprofv3 --pmc runs into profiles/counters.json (no GPU)")
+    ap.add_argument("--only", choices=["csa", "hca", "prefill", "mixed"],
+                    help="run one leg's timed loop only (for counter runs); prints its ms per step")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("LEG", "FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc runs of --only LEG into profiles/counters.json (no GPU)")
+    ap.add_argument("--sq-summary", nargs=2, metavar=("LEG", "CSV"),
+                    help="summarise a rocprofv3 --pmc run of SQ_COUNTERS into profiles/counters.json (no GPU)")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.copy_calibration or 1024,
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.pmc_summary[2], args.copy_calibration or 1024,
                     os.path.join(ROOT, "profiles", "counters.json"))
+        return
+    if args.sq_summary:
+        sq_summary(args.sq_summary[0], args.sq_summary[1], os.path.join(ROOT, "profiles", "counters.json"))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -715,6 +804,20 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     L.lib()
+    if args.only:
+        if args.only == "csa":
+            step, warm = csa_decode_setup(WL.make_csa_decode(), args.copies), args.warmup
+        elif args.only == "hca":
+            step, warm = hca_decode_setup(WL.make_hca_decode(), args.copies), args.warmup
+        elif args.only == "prefill":
+            step, warm = csa_prefill_setup(WL.make_csa_prefill())[0], 1
+        else:
+            step, warm = mixed_pair_setup()[0], 2
+        el = timed(step, args.steps, warm)
+        if args.copy_calibration:
+            copy_calibration(args.copy_calibration)
+        print(json.dumps({"only": args.only, "steps": args.steps, "ms_per_step": 1e3 * el / args.steps}), flush=True)
+        return
 
     d = WL.make_csa_decode()
     step = csa_decode_setup(d, args.copies)
@@ -776,9 +879,16 @@ def main():
         progress(f"hca decode: {hms:.4f} ms/step")
         hb, hf = hca_decode_bytes(h), hca_decode_flops(h)
         att = hk.get("hca_attend", {"avg_us": float("nan")})["avg_us"]
+        hga = hb / (att * 1e-6) / 1e9
         result["secondary"] = {
             "workload": "hca_decode_b8_ctx1048576", "tokens_per_s": h["B"] / (hms * 1e-3),
             "ms_per_step": hms, "kernels_us": per_step(hk, 3),
+            "roofline": {"bound": "hbm", "kernel": "hca_attend", "achieved": hga, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": hga / HBM_PEAK_GBS,
+                         "traffic": load_traffic("hca_attend", "hca_decode_b8_ctx1048576",
+                                                 source_hash(ATTEND_SOURCES)),
+                         "algorithmic_bytes_per_launch": hb,
+                         "mfma_bf16_frac": hf / (att * 1e-6) / MFMA_BF16_PEAK},
             "hca_attend_GBs": hb / (att * 1e-6) / 1e9, "hca_attend_hbm_frac": hb / (att * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "hca_attend_TFLOPs": hf / (att * 1e-6) / 1e12, "mfma_bf16_frac": hf / (att * 1e-6) / 2.5e15,
             "algorithmic_bytes": hb, "flops": hf,
@@ -795,9 +905,22 @@ def main():
         pms = 1e3 * pe / n_p
         pk = kernel_times(pstep, n_p)
         progress(f"csa prefill: {pms:.3f} ms/step")
+        pks = per_step(pk, 3)
+        pfi, pfa = csa_prefill_flops_split()
+        i_us, a_us = pks.get("index_score", float("nan")), pks.get("csa_attend", float("nan"))
         result["prefill"] = {
             "workload": "csa_prefill_tq4096_ctx1048576", "tokens_per_s": 4096 / (pms * 1e-3),
-            "ms_per_step": pms, "kernels_us": per_step(pk, 3), "kernel_launches_per_step": launches(pk),
+            "ms_per_step": pms, "kernels_us": pks, "kernel_launches_per_step": launches(pk),
+            "roofline": {"bound": "mfma", "kernel": "index_score", "achieved": pfi / (i_us * 1e-6) / 1e12,
+                         "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": pfi / (i_us * 1e-6) / MFMA_BF16_PEAK, "traffic": None,
+                         "algorithmic_flops_per_step": pfi,
+                         "note": "scores are never stored: two tiled passes (group maxima, then candidates) "
+                                 "each do these flops; achieved counts them once"},
+            "csa_attend_roofline": {"bound": "mfma", "achieved": pfa / (a_us * 1e-6) / 1e12,
+                                    "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                                    "frac": pfa / (a_us * 1e-6) / MFMA_BF16_PEAK,
+                                    "algorithmic_flops_per_step": pfa},
             "flops": pflops, "achieved_TFLOPs": pflops / (pms * 1e-3) / 1e12,
             "mfma_bf16_frac": pflops / (pms * 1e-3) / 2.5e15,
         }
@@ -808,9 +931,19 @@ def main():
         mms = 1e3 * me / n_m
         mk = kernel_times(mstep, n_m)
         progress(f"mixed pair: {mms:.4f} ms/step")
+        mks = per_step(mk, 3)
+        hfl, hby = mixed_hca_work()
+        h_us = mks.get("hca_attend", float("nan"))
         result["mixed_pair"] = {
             "workload": "mixed_csa_hca_pair_b64_ctx1048576", "tokens_per_s": 64 / (mms * 1e-3),
-            "ms_per_step": mms, "kernels_us": per_step(mk, 3),
+            "ms_per_step": mms, "kernels_us": mks,
+            "roofline": {"bound": "mfma", "kernel": "hca_attend", "achieved": hfl / (h_us * 1e-6) / 1e12,
+                         "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": hfl / (h_us * 1e-6) / MFMA_BF16_PEAK,
+                         "traffic": None, "algorithmic_flops_per_launch": hfl,
+                         "algorithmic_bytes_per_launch": hby,
+                         "hbm_frac": hby / (h_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "note": "fp8 channels are widened to bf16 before the MFMA: priced at the bf16 peak"},
             "algorithmic_bytes": mbytes, "flops": mflops,
             "achieved_GBs": mbytes / (mms * 1e-3) / 1e9, "hbm_frac": mbytes / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         }
