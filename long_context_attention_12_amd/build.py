@@ -25,9 +25,11 @@ FLAGS = [
 ]
 
 
-# Per-source additions. The indexer's MFMA results feed a short VALU epilogue
-# per tile: in VGPR form they skip one accumulator read per result register.
-EXTRA = {"index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source additions: MFMA results in VGPRs. The indexer's feed a short VALU
+# epilogue per tile (no accumulator read per result register); the tiled
+# projection's would otherwise move between the register files every K step.
+EXTRA = {"index_topk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "out_proj.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -121,6 +121,153 @@ __global__ __launch_bounds__(kProjThreads) void proj_nt_kernel(const uint16_t* _
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many rows (prefill): a 256 x 128 block of C per workgroup, each of its four
+// waves a 128 x 64 quarter (8 x 4 MFMA tiles), operand tiles of 32 K values
+// copied HBM -> LDS by the load units into a ring of three stages. Every
+// fragment read from LDS feeds four (A) or eight (B) MFMAs: 12 KB of LDS reads
+// per wave per 32 MFMAs, under the LDS rate at one workgroup per CU.
+// The sum over K keeps the arithmetic of proj_nt_kernel: K in eight slices,
+// each an MFMA chain in K order from zero, the slices added in order. So a
+// row's result does not depend on which kernel, or how many rows, computed it.
+// LDS rows are 64 bytes (4 slots of 16 B); slot c of row r sits at physical
+// slot c ^ ((r >> 2) & 3), which spreads a fragment read (16 rows, one slot)
+// over all 64 banks.
+// ---------------------------------------------------------------------------
+constexpr int kGemmBM = 256, kGemmBN = 128, kGemmBK = 32, kGemmStages = 4;
+constexpr int kGemmThreads = 256;
+
+__global__ __launch_bounds__(kGemmThreads) void gemm_nt_tiled_kernel(
+    const uint16_t* __restrict__ A, int64_t lda, int64_t a_group, const uint16_t* __restrict__ Bw, int64_t b_group,
+    uint16_t* __restrict__ C, int64_t ldc, int64_t c_group, int M, int K, int nb, int mb, int groups) {
+  constexpr int AT = kGemmBM * kGemmBK, BT = kGemmBN * kGemmBK;   // elements per stage
+  __shared__ __attribute__((aligned(1024))) uint16_t Ls[kGemmStages][AT + BT];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  // XCD-aware order: the hardware hands consecutive blocks to the 8 XCDs in
+  // turn; block L is the (L / 8)-th of XCD L % 8, and an XCD's blocks take the
+  // nb column blocks of one (group, row block) pair back to back, so the
+  // pair's A rows come from HBM once and then from that XCD's L2. Pairs are
+  // padded to a multiple of 8.
+  const int xcd = static_cast<int>(blockIdx.x) & 7, jx = static_cast<int>(blockIdx.x) >> 3;
+  const int pair = (jx / nb) * 8 + xcd;
+  if (pair >= groups * mb) return;
+  const int gi = pair / mb;
+  const int n0 = (jx % nb) * kGemmBN, m0 = (pair % mb) * kGemmBM;
+  const int wm = wid >> 1, wn = wid & 1;           // wave quarter: rows 128 wm, columns 64 wn
+  const uint16_t* Ag = A + gi * a_group;
+  const uint16_t* Bg = Bw + gi * b_group;
+  // copies: instruction j of a stage fills LDS bytes [1 KB j, 1 KB j + 1 KB) =
+  // 16 rows; lane l -> row 16 j' + l / 4 of its operand, physical slot l % 4
+  const int crow = lane >> 2, cslot = lane & 3;
+  auto issue = [&](int kt, int st) {
+    const int k0 = kt * kGemmBK;
+    const uint32_t base = lds_address(&Ls[st][0]);
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {                  // 24 copies per stage, 6 per wave
+      const int j = wid * 6 + q;                   // 0..15: A rows 16 j ..; 16..23: B rows 16 (j - 16) ..
+      const bool isA = j < 16;
+      const int row = (isA ? 16 * j : 16 * (j - 16)) + crow;
+      const int ls = cslot ^ ((row >> 2) & 3);     // logical slot stored at this physical slot
+      const uint16_t* src;
+      if (isA) {
+        int r = m0 + row;
+        if (r > M - 1) r = M - 1;                  // rows past M: any valid row, results dropped
+        src = Ag + static_cast<int64_t>(r) * lda + k0 + 8 * ls;
+      } else {
+        src = Bg + static_cast<int64_t>(n0 + row) * K + k0 + 8 * ls;
+      }
+      lds_copy16(src, base + 1024u * static_cast<uint32_t>(j));
+    }
+  };
+  const int nk = K / kGemmBK, per_slice = nk / 8;  // stages per K slice (K % 256 == 0)
+  f32x4 acc[8][4], tot[8][4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = tot[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Stages: three copies in flight ahead of the one being summed; the
+  // fragments of stage kt + 1 are read from LDS while stage kt's MFMAs run.
+#pragma unroll
+  for (int s0 = 0; s0 < kGemmStages - 1; ++s0)
+    if (s0 < nk) issue(s0, s0);
+  // fragment byte offsets in a stage: A tile rows 128 wm + 16 mt + r16, B rows 64 wn + 16 nt + r16
+  const int ra = 128 * wm + r16, rb = 64 * wn + r16;
+  struct Frags {
+    bf16x8 a[8], b[4];
+  };
+  auto read_frags = [&](int kt, Frags& f) {
+    const char* st = reinterpret_cast<const char*>(&Ls[kt % kGemmStages][0]);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const int r = ra + 16 * mt;
+      f.a[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + r * 64 + 16 * (g ^ ((r >> 2) & 3))));
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int r = rb + 16 * nt;
+      f.b[nt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(st + 2 * AT + r * 64 + 16 * (g ^ ((r >> 2) & 3))));
+    }
+  };
+  // Stage s landed for every wave: this wave's 6 copies of it are done (the
+  // stage after it, the only later one issued yet, may stay in flight), then
+  // a bare barrier (a fence would drain that stage too). Every wave is then
+  // also past the MFMAs of stage s - 2, whose slot the next copies overwrite.
+  auto land = [&](int st) {
+    if (st + 1 < nk) wait_vmcnt<6>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+  auto step = [&](int kt, const Frags& cur, Frags& nxt) {
+    if (kt + 1 < nk) {
+      land(kt + 1);
+      if (kt + 3 < nk) issue(kt + 3, (kt + 3) % kGemmStages);
+      read_frags(kt + 1, nxt);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[mt], cur.b[nt], acc[mt][nt], 0, 0, 0);
+    if ((kt + 1) % per_slice == 0) {               // a K slice ends: add it, restart the chain
+      const bool first = kt + 1 == per_slice;      // the first slice is taken as it is (as red[0])
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          tot[mt][nt] = first ? acc[mt][nt] : tot[mt][nt] + acc[mt][nt];
+          acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+  };
+  Frags f0, f1;
+  if (nk > 0) {
+    if (nk > 2) wait_vmcnt<12>();
+    else if (nk > 1) wait_vmcnt<6>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    read_frags(0, f0);
+  }
+  for (int kt = 0; kt < nk; kt += 2) {             // two steps per pass: the fragment sets swap roles
+    step(kt, f0, f1);
+    if (kt + 1 < nk) step(kt + 1, f1, f0);
+  }
+  // lane (g, r16) holds C rows 4 g + i, column r16 of each tile
+  uint16_t* Cg = C + gi * c_group;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 128 * wm + 16 * mt + 4 * g + i;
+      if (m < M) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          Cg[static_cast<int64_t>(m) * ldc + n0 + 64 * wn + 16 * nt + r16] = f32_to_bf16(tot[mt][nt][i]);
+      }
+    }
+}
+
 template <int MT>
 void launch_proj(LaunchScope& sc, const uint16_t* A, int64_t lda, int64_t a_group, const uint16_t* Bw,
                  int64_t b_group, uint16_t* C, int64_t ldc, int64_t c_group, int M, int N, int K, int groups) {
@@ -130,6 +277,14 @@ void launch_proj(LaunchScope& sc, const uint16_t* A, int64_t lda, int64_t a_grou
 
 void launch_proj_any(LaunchScope& sc, const uint16_t* A, int64_t lda, int64_t a_group, const uint16_t* Bw,
                      int64_t b_group, uint16_t* C, int64_t ldc, int64_t c_group, int M, int N, int K, int groups) {
+  // many rows: the tiled kernel (same arithmetic)
+  if (M >= kGemmBM && N % kGemmBN == 0 && K % (8 * kGemmBK) == 0) {
+    const int nb = N / kGemmBN, mb = (M + kGemmBM - 1) / kGemmBM;
+    const int64_t pairs = (static_cast<int64_t>(groups) * mb + 7) / 8 * 8;
+    sc.launch(gemm_nt_tiled_kernel, dim3(static_cast<uint32_t>(pairs * nb)), dim3(kGemmThreads), 0, A, lda, a_group,
+              Bw, b_group, C, ldc, c_group, M, K, nb, mb, groups);
+    return;
+  }
   // rows per workgroup: as few 16-row tiles as cover M, up to four (64 rows)
   if (M <= 16) launch_proj<1>(sc, A, lda, a_group, Bw, b_group, C, ldc, c_group, M, N, K, groups);
   else if (M <= 32) launch_proj<2>(sc, A, lda, a_group, Bw, b_group, C, ldc, c_group, M, N, K, groups);

@@ -72,3 +72,21 @@ def test_grouped_out_proj_rows_keep_their_bits():
         L.lca_grouped_out_proj(od[lo:hi].contiguous(), wgd, wod, part)
         torch.cuda.synchronize()
         assert torch.equal(part, full[lo:hi]), f"rows {lo}:{hi}"
+
+
+def test_grouped_out_proj_tiled_rows_keep_their_bits():
+    # 300 rows take the tiled kernel in both stages (256-row blocks, a ragged
+    # tail), a few rows the per-row-tile kernel: the same K slices summed in
+    # the same order, so the same bits
+    L = need_gpu()
+    rng = np.random.default_rng(230)
+    o, w_g, w_o = _case(rng, 300, 16, 128, 2, 128, 256)
+    say("grouped out proj tiled: 300 rows vs row subsets")
+    mid, full = _check(L, o, w_g, w_o, "tiled T=300")
+    od, wgd, wod = dev_bf16(o), dev_bf16(w_g), dev_bf16(w_o)
+    for lo, hi in ((0, 16), (250, 300), (37, 101)):
+        part = torch.empty((hi - lo, 256), dtype=torch.bfloat16, device=DEV)
+        pm = L.lca_grouped_out_proj(od[lo:hi].contiguous(), wgd, wod, part)
+        torch.cuda.synchronize()
+        assert torch.equal(pm, mid[lo:hi]), f"intermediate rows {lo}:{hi}"
+        assert torch.equal(part, full[lo:hi]), f"rows {lo}:{hi}"
