@@ -543,6 +543,33 @@ def test_index_topk_prefill_without_stored_scores(case, H_I, bf16_scores):
         np.testing.assert_array_equal(gs[0, t], sc[want].astype(np.float32), err_msg=f"{case} t={t}")
 
 
+def test_index_topk_prefill_without_stored_scores_ragged_query_tiles():
+    # 130 queries: two whole 64-query tiles and a 2-query tail, over lists
+    # between 2^15 and 2^18 entries, real-valued scores (oracle set check with
+    # the near-tie classes) on the path that stores no scores
+    L = need_gpu()
+    rng = np.random.default_rng(560)
+    B, Tq, H_I, d_I, m, k = 1, 130, 4, 128, 4, 512
+    q_pos0 = 4 * 70000
+    N_cap = (q_pos0 + Tq) // m + 5
+    qI = WL.bf16_exact(rng.standard_normal((B, Tq, H_I, d_I)).astype(np.float32) / np.sqrt(d_I))
+    kI = rng.standard_normal((B, N_cap, d_I)).astype(np.float32) / np.sqrt(d_I)
+    kI[:, ::89] *= 4
+    kI = WL.bf16_exact(kI)
+    w = (rng.standard_normal((B, Tq, H_I)) / np.sqrt(H_I)).astype(np.float32)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    say("prefill without stored scores, ragged query tiles")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for t in list(range(0, Tq, 9)) + [Tq - 2, Tq - 1]:
+        nv = O.n_visible(q_pos0 + t, m)
+        s = O.index_scores(qI[0, t], w[0, t], kI[0], nv)
+        check_topk_set(got[0, t], s, k)
+        sel = got[0, t][got[0, t] >= 0]
+        assert np.all(np.diff(sel) > 0), "indices not increasing"
+
+
 def test_index_topk_long_ragged_rows():
     # A ragged batch bounded at 140000 entries: the long rows take the chunked
     # select with a bound, the short ones (5000, 300 entries) have too few

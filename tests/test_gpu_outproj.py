@@ -90,3 +90,21 @@ def test_grouped_out_proj_tiled_rows_keep_their_bits():
         torch.cuda.synchronize()
         assert torch.equal(pm, mid[lo:hi]), f"intermediate rows {lo}:{hi}"
         assert torch.equal(part, full[lo:hi]), f"rows {lo}:{hi}"
+
+
+@pytest.mark.parametrize("T,g", [(256, 2), (513, 3)])
+def test_grouped_out_proj_tiled_edges(T, g):
+    # the tiled kernel at exactly one 256-row block, and at three groups of
+    # three row blocks each (nine (group, row block) pairs, padded to 16 in the
+    # XCD-aware order) with a one-row tail
+    L = need_gpu()
+    rng = np.random.default_rng(240 + T + g)
+    o, w_g, w_o = _case(rng, T, 4 * g, 64, g, 256, 128)
+    say(f"grouped out proj tiled edges: T={T} g={g}")
+    mid, full = _check(L, o, w_g, w_o, f"tiled T={T} g={g}")
+    od, wgd, wod = dev_bf16(o), dev_bf16(w_g), dev_bf16(w_o)
+    lo, hi = T - 40, T
+    part = torch.empty((hi - lo, 128), dtype=torch.bfloat16, device=DEV)
+    pm = L.lca_grouped_out_proj(od[lo:hi].contiguous(), wgd, wod, part)
+    torch.cuda.synchronize()
+    assert torch.equal(pm, mid[lo:hi]) and torch.equal(part, full[lo:hi]), f"rows {lo}:{hi}"
