@@ -1480,6 +1480,69 @@ __device__ __forceinline__ void group_bound(const float* __restrict__ gm, int64_
   __syncthreads();
 }
 
+// group_bound for rows of at most 256 * 4 * NV maxima (the bound kernel's
+// common case): thread i loads maxima 4 (i + 256 j) .. + 3 as one 16-byte
+// load for j < NV (all loads issued before any is used), and each load's two
+// pairs are its items (the maximum of 2 groups): 2 NV items per lane, the
+// waves' items a partition of the row. Then as group_bound: each wave the
+// ceil(k / 4)-th largest of its items on the keys' top 16 bits, lo the
+// smallest of the four.
+template <int NV>
+__device__ __forceinline__ void group_bound_v4(const float* __restrict__ gm, int64_t ng, int k, bool key16,
+                                               uint32_t* wv, uint32_t* lo_out, uint32_t* hi_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  float4 v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int64_t f = tid + static_cast<int64_t>(kFiltThreads) * j;
+    v[j] = 4 * f < ng ? *reinterpret_cast<const float4*>(gm + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  uint32_t kv[2 * NV], mx = 0, have = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int64_t g0 = 4 * (tid + static_cast<int64_t>(kFiltThreads) * j);
+    // an item counts the groups of its pair that exist (a row's last pair may hold one)
+    const float a0 = g0 < ng ? v[j].x : -INFINITY, a1 = g0 + 1 < ng ? v[j].y : -INFINITY;
+    const float b0 = g0 + 2 < ng ? v[j].z : -INFINITY, b1 = g0 + 3 < ng ? v[j].w : -INFINITY;
+    kv[2 * j] = g0 < ng ? score_key(fmaxf(a0, a1), key16) : 0u;
+    kv[2 * j + 1] = g0 + 2 < ng ? score_key(fmaxf(b0, b1), key16) : 0u;
+    mx = max(mx, max(kv[2 * j], kv[2 * j + 1]));
+    have += static_cast<uint32_t>(__popcll(__ballot(g0 < ng))) + static_cast<uint32_t>(__popcll(__ballot(g0 + 2 < ng)));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), o, kWave)));
+  const int ksh = key16 ? 0 : 16;
+  const uint32_t r = static_cast<uint32_t>((k + 3) / 4);
+  uint32_t t = 0;
+  if (have >= r) {
+    uint32_t k16[2 * NV];
+#pragma unroll
+    for (int i = 0; i < 2 * NV; ++i) k16[i] = kv[i] >> ksh;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t c = t | (1u << bit);
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int i = 0; i < 2 * NV; ++i) cnt += static_cast<uint32_t>(__popcll(__ballot(k16[i] >= c)));
+      if (cnt >= r) t = c;
+    }
+    t <<= ksh;
+  }
+  if (lane == 0) {
+    wv[wid] = t;
+    wv[4 + wid] = mx;
+  }
+  __syncthreads();
+  uint32_t lo = 0xffffffffu, hi = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    lo = min(lo, wv[w]);
+    hi = max(hi, wv[4 + w]);
+  }
+  *lo_out = lo > 0u ? lo : 1u;                           // key 0 is "no element"
+  *hi_out = hi;
+  __syncthreads();
+}
+
 // Row (b, tl) of a chunked call: scores, visible count, outputs.
 struct FiltRow {
   const float* s;
@@ -1588,7 +1651,11 @@ __global__ __launch_bounds__(kFiltThreads) void topk_bound_kernel(
   if (n <= k) return;
   const int64_t r = static_cast<int64_t>(b) * Tc + tl;
   uint32_t lo, hi;
-  group_bound<kBoundItems>(fw.gmax + r * fw.ldg, (n + kGroup - 1) / kGroup, k, key16, wv, &lo, &hi);
+  const int64_t ng = (n + kGroup - 1) / kGroup;
+  if (ng <= 4 * kFiltThreads * 16)
+    group_bound_v4<16>(fw.gmax + r * fw.ldg, ng, k, key16, wv, &lo, &hi);
+  else
+    group_bound<kBoundItems>(fw.gmax + r * fw.ldg, ng, k, key16, wv, &lo, &hi);
   if (threadIdx.x == 0) {
     fw.bound[2 * r] = lo;
     fw.bound[2 * r + 1] = hi;
