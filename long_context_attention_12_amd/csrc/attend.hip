@@ -528,7 +528,7 @@ __device__ __forceinline__ void fill_rope_table(const AttendArgs& a, int b, int 
   const int R = ((a.flags & LCA_INV_ROPE) && a.rope_dims > 0) ? a.rope_dims : 0;
   for (int i = threadIdx.x; i < R / 2; i += blockDim.x) {
     float sn, cs;
-    rope_sincos(-static_cast<double>(seq_pos(a.q_pos, a.q_pos0, b) + t), i, R, static_cast<double>(a.rope_base), &sn, &cs);
+    rope_sincos(-static_cast<double>(seq_pos(a.q_pos, a.q_pos0, b) + t), i, a.rope_r, &sn, &cs);
     rope_tab[i] = make_float2(cs, sn);
   }
 }
@@ -1838,8 +1838,7 @@ __device__ void combine_row(const AttendArgs& a, int S, int RS, int b, int t, in
     const int d0 = 2 * c;
     if (d0 >= D - R) {
       float sn, cs;
-      rope_sincos(-static_cast<double>(seq_pos(a.q_pos, a.q_pos0, b) + t), (d0 - (D - R)) / 2, R,
-                  static_cast<double>(a.rope_base), &sn, &cs);
+      rope_sincos(-static_cast<double>(seq_pos(a.q_pos, a.q_pos0, b) + t), (d0 - (D - R)) / 2, a.rope_r, &sn, &cs);
       rope_turn(u, v, make_float2(cs, sn));
     }
     if (a.dt_q == LCA_F32) {
@@ -2130,7 +2129,9 @@ void place_splits(const AttendArgs& a, SplitPlan& sp) {
   if (one) sp.SPW = sp.S;
 }
 
-hipError_t launch_attend(hipStream_t s, const AttendArgs& a, void* ws, size_t) {
+hipError_t launch_attend(hipStream_t s, const AttendArgs& a_in, void* ws, size_t) {
+  AttendArgs a = a_in;
+  a.rope_r = rope_ratio(a.rope_base, a.rope_dims);
   SplitPlan sp = make_plan(a);
   place_splits(a, sp);
   // 128-head workgroups in batches that fill every XCD: each sequence's
@@ -2281,7 +2282,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttendBwdArgs p, BwdPlan 
   const int64_t pos = seq_pos(a.q_pos, a.q_pos0, b) + t;
   for (int i = threadIdx.x; i < R / 2; i += 256) {
     float sn, cs;
-    rope_sincos(static_cast<double>(pos), i, R, static_cast<double>(a.rope_base), &sn, &cs);
+    rope_sincos(static_cast<double>(pos), i, a.rope_r, &sn, &cs);
     rt[i] = make_float2(cs, sn);
   }
   __syncthreads();
@@ -2678,7 +2679,9 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(AttendBwdArgs p, BwdPlan 
 
 size_t attend_backward_workspace(const AttendArgs& a) { return make_bwd_plan(a).total + 256; }
 
-hipError_t launch_attend_backward(hipStream_t s, const AttendBwdArgs& p, void* ws, size_t) {
+hipError_t launch_attend_backward(hipStream_t s, const AttendBwdArgs& p_in, void* ws, size_t) {
+  AttendBwdArgs p = p_in;
+  p.a.rope_r = rope_ratio(p.a.rope_base, p.a.rope_dims);
   const AttendArgs& a = p.a;
   const BwdPlan bp = make_bwd_plan(a);
   uint8_t* w = static_cast<uint8_t*>(ws);

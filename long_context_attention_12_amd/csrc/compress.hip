@@ -140,7 +140,7 @@ __device__ void merge_and_emit(const CompressArgs& a, int nl, LogitF logit, RowF
     const int R = a.rope_dims;
     for (int i = tid; i < R / 2; i += kThreads) {
       float s, cs;
-      rope_sincos(static_cast<double>(entry_pos), i, R, static_cast<double>(a.rope_base), &s, &cs);
+      rope_sincos(static_cast<double>(entry_pos), i, a.rope_r, &s, &cs);
       const int c0 = D - R + 2 * i;
       const float u = e[c0], v = e[c0 + 1];
       e[c0] = u * cs - v * s;
@@ -274,7 +274,9 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(int dt_out, int
 
 }  // namespace
 
-hipError_t launch_compress(hipStream_t s, const CompressArgs& a) {
+hipError_t launch_compress(hipStream_t s, const CompressArgs& a_in) {
+  CompressArgs a = a_in;
+  a.rope_r = rope_ratio(a.rope_base, a.rope_dims);
   const int n_out = a.T / a.m;
   if (n_out == 0) return hipSuccess;
   LaunchScope scope(s, "compress");
@@ -286,8 +288,10 @@ hipError_t launch_compress(hipStream_t s, const CompressArgs& a) {
   return hipGetLastError();
 }
 
-hipError_t launch_append(hipStream_t s, const AppendJobs& jobs, int B, int64_t pos_max, const int64_t* pos,
+hipError_t launch_append(hipStream_t s, const AppendJobs& jobs_in, int B, int64_t pos_max, const int64_t* pos,
                          const char* name) {
+  AppendJobs jobs = jobs_in;
+  for (int i = 0; i < jobs.n; ++i) jobs.j[i].a.rope_r = rope_ratio(jobs.j[i].a.rope_base, jobs.j[i].a.rope_dims);
   LaunchScope scope(s, name);
   scope.launch(decode_append_kernel, dim3(B, jobs.n), dim3(kThreads), 0, jobs, pos_max, pos);
   return hipGetLastError();

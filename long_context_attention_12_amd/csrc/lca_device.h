@@ -133,15 +133,30 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---- RoPE ----------------------------------------------------------------------
-// Angle of pair i (of R/2) at position pos: frequency and product in double,
-// reduced to [-pi, pi] in double so that positions near 2^20 keep full float32
-// accuracy; sin and cos of the reduced angle in float32 (within a few ulp of
-// the double values, and off the fp64 transcendental path, which sat on the
-// critical path of the kernels that build these tables).
-__device__ __forceinline__ void rope_sincos(double pos, int i, int R, double base,
-                                            float* s, float* c) {
-  double freq = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(R));
-  double ang = pos * freq;
+// Pair i of the R rotated channels turns at frequency theta_i = base^(-2i/R),
+// i.e. the i-th power of the ratio r = base^(-2/R). The host takes r once per
+// call (rope_ratio); a kernel raises it to the i-th power by squaring, eight
+// fp64 steps for i < 256, in place of an fp64 power per lane (the power sat on
+// the critical path of the kernels that build angle tables). The product with
+// the position and the reduction to [-pi, pi] stay in double, so positions
+// near 2^20 keep full float32 accuracy; sin and cos of the reduced angle are
+// taken in float32.
+inline double rope_ratio(float base, int R) {
+  return R > 0 && base > 0.f ? pow(static_cast<double>(base), -2.0 / static_cast<double>(R)) : 1.0;
+}
+
+__device__ __forceinline__ double rope_freq(double r, int i) {
+  double f = 1.0, p = r;
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    if ((i >> bit) & 1) f *= p;
+    p *= p;
+  }
+  return f;
+}
+
+__device__ __forceinline__ void rope_sincos(double pos, int i, double r, float* s, float* c) {
+  double ang = pos * rope_freq(r, i);
   const double two_pi = 6.283185307179586476925286766559;
   ang = ang - two_pi * rint(ang / two_pi);
   const float a = static_cast<float>(ang);

@@ -46,6 +46,7 @@ struct CompressArgs {
   void* out;
   void* out_scale;
   int64_t out_rows;
+  double rope_r;             // base^(-2/R), set by the launchers
 };
 hipError_t launch_compress(hipStream_t s, const CompressArgs& a);
 
@@ -108,6 +109,7 @@ struct AttendArgs {
   void* out;
   float* lse_out;
   const int64_t* q_pos;      // per-sequence positions (ragged batch) or null: all at q_pos0
+  double rope_r;             // base^(-2/R), set by the launchers
 };
 size_t attend_workspace(const AttendArgs& a);
 
