@@ -166,6 +166,7 @@ struct SelAux {
   uint32_t* cnt;
   int nchs;
   int64_t capc;
+  const uint32_t* lim;     // per row: keys at or past it hold no candidate (bound kernel)
 };
 constexpr int kTiledScores = 0;     // tiled kernel: store every score (and group maxima if asked)
 constexpr int kTiledMaxima = 1;     // group maxima only
@@ -402,6 +403,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
   bool writer_l[2 * MB];
   uint32_t lo_c[2 * MB], run_a[2 * MB], run_e[2 * MB];
   float gm_l[2 * MB], lof_l[2 * MB];
+  int limt_l[2 * MB];                                // candidate pass: first tile past the row's index limit
   int64_t gslot_l[2 * MB], cb_l[2 * MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -421,18 +423,26 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
       cb_l[ci] = (rix_l[ci] * aux.nchs + kr) * aux.capc;
       lo_c[ci] = 0;
       lof_l[ci] = INFINITY;
+      limt_l[ci] = 0x7fffffff;
       run_a[ci] = run_e[ci] = 0;
     }
   }
   if constexpr (MODE == kTiledCands) {
     // all loads first (clamped rows of non-writers are read and ignored)
-    uint32_t lo_raw[2 * MB];
+    uint32_t lo_raw[2 * MB], lim_raw[2 * MB];
 #pragma unroll
-    for (int ci = 0; ci < 2 * MB; ++ci) lo_raw[ci] = aux.bound[2 * (writer_l[ci] ? rix_l[ci] : int64_t(0))];
+    for (int ci = 0; ci < 2 * MB; ++ci) {
+      const int64_t rr = writer_l[ci] ? rix_l[ci] : int64_t(0);
+      lo_raw[ci] = aux.bound[2 * rr];
+      lim_raw[ci] = aux.lim[rr];
+    }
 #pragma unroll
     for (int ci = 0; ci < 2 * MB; ++ci) {
       if (!writer_l[ci]) continue;
       lo_c[ci] = lo_raw[ci];
+      // tiles from limt on start at or past the index limit: no candidates
+      const int64_t lrel = static_cast<int64_t>(lim_raw[ci]) - k_begin;
+      limt_l[ci] = lrel <= 0 ? 0 : static_cast<int>((lrel + kTileKeys - 1) / kTileKeys);
       // key(x) >= lo implies x >= lof: lof is the bound's own float when
       // that is a normal number, and -FLT_MIN for a bound among the
       // subnormals and zeros (a superset either way, whether or not the
@@ -460,6 +470,9 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
     constexpr int NSL = HI == 2 ? 2 : 1;             // query slots per lane (acc_scores)
     float vs[NB][2 * MB];                            // candidate pass: the tile's scores
     uint64_t mk[NB][2 * MB];                         // and which may be candidates
+    float lof_t[2 * MB];                             // the float filter, or +inf past the index limit
+#pragma unroll
+    for (int ci = 0; ci < 2 * MB; ++ci) lof_t[ci] = tt >= limt_l[ci] ? INFINITY : lof_l[ci];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       f32x4 acc[MB];
@@ -487,7 +500,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
             gm_l[ci] = fmaxf(gm_l[ci], vis ? v[sl] : -INFINITY);     // over the tile's 4 key slabs
           } else {
             vs[nb][ci] = v[sl];
-            mk[nb][ci] = __ballot(v[sl] >= lof_l[ci] && vis);
+            mk[nb][ci] = __ballot(v[sl] >= lof_t[ci] && vis);
           }
         }
       }
@@ -1353,6 +1366,7 @@ struct FiltWs {
   uint32_t* cnt;          // [rows, nchs] (above << 16) | equal, kOverflow past capc
   int nchs;               // chunk stride per row
   int capc;               // candidate slots per chunk
+  uint32_t* lim;          // [rows] candidate index limit (bound kernel output)
 };
 
 // Exclusive scan over NT threads (NT / 64 waves), one value per thread.
@@ -1641,10 +1655,19 @@ __device__ void select_passes_t(const FiltRow& row, int k, bool key16, uint32_t*
 
 // One workgroup per row: the group bound, for rows whose maxima are too many
 // to take inside every chunk workgroup.
+// Also the row's candidate index limit: when the bound equals the row's
+// largest key (every key at or above it ties at it, as in a row whose head
+// weights are all negative, with its many exact zeros), the k selected are
+// the first k ties in index order, and they lie in the groups up to the k-th
+// group (in index order) whose maximum reaches the bound: at least k ties sit
+// there. Keys past that group are no candidates. Otherwise the limit is the
+// visible count.
 __global__ __launch_bounds__(kFiltThreads) void topk_bound_kernel(
     FiltWs fw, int64_t N_cap, int Tc, int64_t q_pos0, const int64_t* __restrict__ q_pos, int t_off, int m, int k,
     bool key16) {
   __shared__ uint32_t wv[8];
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[kFiltThreads / 64];
+  __shared__ uint32_t sh_lim;
   const int b = blockIdx.z, tl = blockIdx.y;
   int64_t n = n_visible(seq_pos(q_pos, q_pos0, b) + t_off + tl, m);
   if (n > N_cap) n = N_cap;
@@ -1652,13 +1675,40 @@ __global__ __launch_bounds__(kFiltThreads) void topk_bound_kernel(
   const int64_t r = static_cast<int64_t>(b) * Tc + tl;
   uint32_t lo, hi;
   const int64_t ng = (n + kGroup - 1) / kGroup;
+  const float* gm = fw.gmax + r * fw.ldg;
   if (ng <= 4 * kFiltThreads * 16)
-    group_bound_v4<16>(fw.gmax + r * fw.ldg, ng, k, key16, wv, &lo, &hi);
+    group_bound_v4<16>(gm, ng, k, key16, wv, &lo, &hi);
   else
-    group_bound<kBoundItems>(fw.gmax + r * fw.ldg, ng, k, key16, wv, &lo, &hi);
+    group_bound<kBoundItems>(gm, ng, k, key16, wv, &lo, &hi);
+  if (threadIdx.x == 0) sh_lim = static_cast<uint32_t>(n);
+  if (hi == lo) {                                   // uniform across the block
+    const int tid = threadIdx.x;
+    uint32_t need = static_cast<uint32_t>(k);
+    for (int64_t g0 = 0; g0 < ng; g0 += 4 * kFiltThreads) {
+      const int64_t gi = g0 + 4 * tid;             // 4 consecutive groups per thread
+      const float4 v = gi < ng ? *reinterpret_cast<const float4*>(gm + gi) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint32_t c0 = gi < ng && score_key(v.x, key16) >= lo;
+      const uint32_t c1 = gi + 1 < ng && score_key(v.y, key16) >= lo;
+      const uint32_t c2 = gi + 2 < ng && score_key(v.z, key16) >= lo;
+      const uint32_t c3 = gi + 3 < ng && score_key(v.w, key16) >= lo;
+      const uint32_t c = c0 + c1 + c2 + c3;
+      uint32_t tot;
+      const uint32_t pre = block_excl_scan_t<kFiltThreads>(c, wsum, &tot);
+      if (pre < need && pre + c >= need) {          // the need-th such group is one of this thread's
+        const uint32_t q = need - pre;              // 1..4
+        const int j = c0 >= q ? 0 : (c0 + c1 >= q ? 1 : (c0 + c1 + c2 >= q ? 2 : 3));
+        const int64_t lim = (gi + j + 1) * kGroup;
+        sh_lim = static_cast<uint32_t>(lim < n ? lim : n);
+      }
+      if (tot >= need) break;                       // uniform
+      need -= tot;
+    }
+    __syncthreads();
+  }
   if (threadIdx.x == 0) {
     fw.bound[2 * r] = lo;
     fw.bound[2 * r + 1] = hi;
+    fw.lim[r] = sh_lim;
   }
 }
 
@@ -2177,6 +2227,7 @@ IndexWs index_ws(const IndexArgs& a, void* base) {
   w.fw.cidx = reinterpret_cast<int32_t*>(take(rows * slots * 4));
   w.fw.cnt = reinterpret_cast<uint32_t*>(take(rows * w.fw.nchs * 4));
   w.fw.bound = reinterpret_cast<uint32_t*>(take(rows * 8));
+  w.fw.lim = reinterpret_cast<uint32_t*>(take(rows * 4));
   w.bytes = off + 256;
   return w;
 }
@@ -2250,7 +2301,7 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
       FiltWs fw = w.fw;
       fw.nchs = static_cast<int>(kc);
       fw.capc = static_cast<int>(2 * per);
-      SelAux aux{fw.gmax, fw.ldg, fw.bound, fw.ckey, fw.cidx, fw.cnt, fw.nchs, fw.capc};
+      SelAux aux{fw.gmax, fw.ldg, fw.bound, fw.ckey, fw.cidx, fw.cnt, fw.nchs, fw.capc, fw.lim};
       {
         LaunchScope scope(s, "index_score");
         launch_tiled<kTiledMaxima>(scope, a, kc, tcn, nullptr, ld, t_off, Tc, per, key16, aux);
@@ -2283,7 +2334,7 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
     const bool tiled = a.dt == LCA_BF16 && a.d_I == 128 && tcn >= kTiledMinQueries;
     const int64_t ng_max = (nv_max + kGroup - 1) / kGroup;
     const bool filt = use_chunked(a, nv_max, tiled);
-    SelAux aux{filt ? w.fw.gmax : nullptr, w.fw.ldg, nullptr, nullptr, nullptr, nullptr, 0, 0};
+    SelAux aux{filt ? w.fw.gmax : nullptr, w.fw.ldg, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr};
     if (nv_max > 0) {
       LaunchScope scope(s, "index_score");
       if (a.dt == LCA_F32) {

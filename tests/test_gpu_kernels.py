@@ -570,6 +570,32 @@ def test_index_topk_prefill_without_stored_scores_ragged_query_tiles():
         assert np.all(np.diff(sel) > 0), "indices not increasing"
 
 
+def test_index_topk_prefill_without_stored_scores_all_ties():
+    # Every key identical, so every score of a row ties: the bound equals the
+    # row's largest key, the bound kernel limits the candidates to the groups
+    # up to the k-th one, and the answer is the k lowest indices. Odd queries
+    # take negative head weights (their ties sit below zero or at zero).
+    L = need_gpu()
+    rng = np.random.default_rng(570)
+    B, Tq, H_I, d_I, m, k = 1, 66, 4, 128, 4, 1024
+    q_pos0 = 4 * 40000 + 2
+    N_cap = (q_pos0 + Tq) // m + 1
+    kI = np.tile(rng.integers(-4, 5, size=(1, 1, d_I)), (B, N_cap, 1)).astype(np.float32)
+    qI = rng.integers(-4, 5, size=(B, Tq, H_I, d_I)).astype(np.float32)
+    w = np.tile(np.array([0.5, 0.25, 1.0, 0.125], np.float32), (B, Tq, 1))
+    w[:, 1::2] *= -1
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    say("prefill without stored scores, every score tied")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for t in range(Tq):
+        nv = O.n_visible(q_pos0 + t, m)
+        sc = O.index_scores(qI[0, t], w[0, t], kI[0], nv)
+        assert np.all(sc == sc[0])
+        np.testing.assert_array_equal(got[0, t], np.arange(k), err_msg=f"t={t}")
+
+
 def test_index_topk_long_ragged_rows():
     # A ragged batch bounded at 140000 entries: the long rows take the chunked
     # select with a bound, the short ones (5000, 300 entries) have too few
