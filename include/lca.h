@@ -74,8 +74,9 @@ extern "C" {
 #define LCA_SCORE_BF16  8u /* index_topk: round scores to bf16 before top-k    */
 #define LCA_SPLITS_ONE_WG  32u /* attend: run all of a query's splits in one
                               workgroup (no partials, no combine) where a kernel
-                              for it exists (bf16 rows, D = 512, heads not a
-                              multiple of 128); by default a cost model picks
+                              for it exists (bf16 rows, D = 512: fewer than
+                              64 heads, or a multiple of 64, 128-head plans as
+                              two 64-head groups); by default a cost model picks
                               it from the batch size ([Qiaomu] 批不变 kernel,
                               [kwkr] §4.3: a throughput and a latency kernel
                               with one accumulation order). Same bits either

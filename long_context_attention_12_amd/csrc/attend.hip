@@ -2112,21 +2112,32 @@ size_t attend_workspace(const AttendArgs& a) {
 // LCA_SPLITS_ONE_WG / LCA_SPLITS_MANY_WG force a placement.
 constexpr int64_t kCUs = 256;
 
+// attend_dma_fold_kernel: bf16 rows of 512 channels, 64 heads per workgroup.
+// A 128-head plan (attend_dma_kernel<2>) folds there too, as two 64-head
+// groups over the same splits: per head that kernel runs the same MFMA chains
+// and softmax as the 64-head one, so the splits' results, and the fold of
+// them, keep their bits.
 bool folds_in_kernel(const AttendArgs& a, const SplitPlan& sp) {
-  return a.D == 512 && a.dt_kv == LCA_BF16 && sp.HG != 128;   // attend_dma_fold_kernel
+  return a.D == 512 && a.dt_kv == LCA_BF16 && (sp.HG != 128 || a.H % 64 == 0);
 }
 
 void place_splits(const AttendArgs& a, SplitPlan& sp) {
   if (!folds_in_kernel(a, sp) || sp.S == 1) return;
-  const int64_t items = static_cast<int64_t>(a.B) * a.Tq * sp.n_hg;
+  const int fold_hg = sp.HG == 128 ? 64 : sp.HG;                          // head group of the fold kernel
+  const int64_t q_items = static_cast<int64_t>(a.B) * a.Tq;
   const double rows = static_cast<double>(sp.RS) * a.D * 2;                  // one split's rows (bf16)
   const double part = 2.0 * sp.HG * (a.D * 2 + 8);                         // its bf16 partial + (max, sum), out and back
-  const double t_one = static_cast<double>((items + kCUs - 1) / kCUs) * sp.S * rows;
-  const double t_split = static_cast<double>((items * sp.S + kCUs - 1) / kCUs) * (rows + part);
+  const int64_t one_items = q_items * (a.H / fold_hg), split_items = q_items * sp.n_hg * sp.S;
+  const double t_one = static_cast<double>((one_items + kCUs - 1) / kCUs) * sp.S * rows;
+  const double t_split = static_cast<double>((split_items + kCUs - 1) / kCUs) * (rows + part);
   bool one = t_one <= t_split;
   if (a.flags & LCA_SPLITS_ONE_WG) one = true;
   if (a.flags & LCA_SPLITS_MANY_WG) one = false;
-  if (one) sp.SPW = sp.S;
+  if (one) {
+    sp.SPW = sp.S;
+    sp.HG = fold_hg;
+    sp.n_hg = a.H / fold_hg;
+  }
 }
 
 hipError_t launch_attend(hipStream_t s, const AttendArgs& a_in, void* ws, size_t) {

@@ -44,7 +44,10 @@ def _run(L, kind, q_d, E_d, idx_d, win_d, sink_d, m, W, q_pos0, flags, q_pos=Non
 
 
 @pytest.mark.parametrize("kind,Tq,H,q_pos0", [("csa", 1, 64, 12001), ("csa", 3, 64, 12001), ("hca", 1, 64, 60001),
-                                              ("csa", 1, 32, 45), ("hca", 2, 16, 300001)])
+                                              ("csa", 1, 32, 45), ("hca", 2, 16, 300001),
+                                              # 128 heads, 16 queries: the 128-head split kernel
+                                              # against the fold kernel as two 64-head groups
+                                              ("csa", 16, 128, 12001), ("hca", 16, 128, 128 * 1000 + 5)])
 def test_placements_give_the_same_bits(kind, Tq, H, q_pos0):
     L = need_gpu()
     rng = np.random.default_rng(160 + Tq + H)
