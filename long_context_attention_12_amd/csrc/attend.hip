@@ -1552,6 +1552,197 @@ __global__ __launch_bounds__(kAttThreads) void attend_mixed_dma_kernel(AttendArg
   }
 }
 
+// One workgroup per (query, 64-head group) over all S splits of the query,
+// for mixed rows: attend_dma_fold_kernel's placement with
+// attend_mixed_dma_kernel's tiles (raw ring, conversion pass, per-head MFMA
+// chains and softmax of the 64-head mixed kernel, which are those of the
+// 128-head one too). Each split's (max, sum, o) therefore has the bits of the
+// split kernels' partial, and it folds by SplitFold as the combine does.
+__global__ __launch_bounds__(kAttThreads) void attend_mixed_fold_kernel(AttendArgs a, SplitPlan sp) {
+  constexpr int D = 512, KS = D / 32, DT = D / 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t Raw[kRawRing][kRawSlot];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kTileRows * D];
+  __shared__ __attribute__((aligned(16))) int32_t rows[kMaxSplitRows];
+  __shared__ float2 rope_tab[D / 2];
+  __shared__ float rc_lc[kMaxSplitRows];            // exact recompute: logits of one split
+  __shared__ float rc_o[D + 8];                     // its output row, then (m, z); + partial sums
+  __shared__ uint32_t flag_bits[2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  int split0, hg, t;
+  int b;
+  if (!work_item_b(sp, a.Tq, split0, hg, t, b)) return;
+  const bool active = wid * 16 < sp.HG;
+  const int head = hg * sp.HG + wid * 16 + r16;
+  const RowSpan rs = row_span(a, b, t);
+  fill_rope_table(a, b, t, rope_tab);              // read after the tile loop's barriers
+  const int64_t win_rows = a.W - 1 + a.Tq;
+  const uint8_t* kvb = static_cast<const uint8_t*>(a.kv) + static_cast<int64_t>(b) * a.N_cap * kMixRow;
+  const uint8_t* winb = static_cast<const uint8_t*>(a.win) + static_cast<int64_t>(b) * win_rows * kMixRow;
+  const float* kvs = a.kv_scale + static_cast<int64_t>(b) * a.N_cap;
+  const float* wins = a.win_scale + static_cast<int64_t>(b) * win_rows;
+  const SwzOffsets so = swz_offsets(g, r16);
+  const int tps = sp.RS / kTileRows;               // tiles per split
+  const int spc = kMaxSplitRows / sp.RS;           // splits per row table
+
+  bf16x8 qf[KS];
+  if (active) {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+  }
+  f32x4 U[DT];                                     // folded output, relative to fold.M
+#pragma unroll
+  for (int i = 0; i < DT; ++i) U[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  SplitFold fold = fold_start(active ? a.sink[head] : 0.f);
+
+  for (int c0 = split0; c0 < split0 + sp.SPW; c0 += spc) {
+    const int c1 = min(c0 + spc, split0 + sp.SPW);  // splits [c0, c1) in this row table
+    __syncthreads();                               // the last table's reads of rows[] and the rings are done
+    const int64_t r_begin = static_cast<int64_t>(c0) * sp.RS;
+    int64_t r_end = static_cast<int64_t>(c1) * sp.RS;
+    if (r_end > rs.nrows) r_end = rs.nrows;
+    const int nr = r_end > r_begin ? static_cast<int>(r_end - r_begin) : 0;
+    int32_t myrows[kMaxSplitRows / kAttThreads];
+#pragma unroll
+    for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) {
+      const int v = tid + kAttThreads * q;
+      myrows[q] = v < nr ? encode_row(a, b, t, rs, r_begin + v) : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxSplitRows / kAttThreads; ++q) rows[tid + kAttThreads * q] = myrows[q];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // tile copies as in attend_mixed_dma_kernel: 18 of 1 KB and the row
+    // scales, five per wave; absent rows copy window row 0
+    auto issue = [&](int tile, int slot) {
+      const int v0 = tile * kTileRows;
+      uint8_t* base = &Raw[slot][0];
+#pragma unroll
+      for (int cc = 0; cc < 5; ++cc) {
+        const int c = wid * 5 + cc;
+        if (c < 18) {
+          const int q = c * 1024 + 16 * lane;
+          const int r = q / kMixRow, off = q - r * kMixRow;
+          const int v = v0 + r;
+          const int32_t sr = v < nr ? rows[v] : -1;
+          const uint8_t* rowp = sr >= 0 ? kvb + static_cast<int64_t>(sr) * kMixRow
+                                        : winb + (sr == -1 ? 0 : static_cast<int64_t>(-2 - sr) * kMixRow);
+          lds_copy16(rowp + off, lds_address(base) + c * 1024);
+        } else {
+          const int v = v0 + (lane < kTileRows ? lane : 0);
+          const int32_t sr = v < nr ? rows[v] : -1;
+          const float* sp_ = sr >= 0 ? kvs + sr : wins + (sr == -1 ? 0 : -2 - sr);
+          lds_copy4(sp_, lds_address(base + kRawTile));
+        }
+      }
+    };
+    const int ntiles = (nr + kTileRows - 1) / kTileRows;
+#pragma unroll
+    for (int t0 = 0; t0 < 3; ++t0)
+      if (t0 < ntiles) issue(t0, t0);
+    f32x4 acc_o[DT];
+    float m_run = -INFINITY, z_run = 0.f;
+    bool flag = false;
+#pragma unroll
+    for (int i = 0; i < DT; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_waitcnt(0);                 // tiles 0..2 (and the query fragments)
+    __builtin_amdgcn_s_barrier();
+    if (0 < ntiles) convert_mixed_tile(&Raw[0][0], Xs[0]);
+    // Every split of [c0, c1) ends on a tile boundary (RS is a multiple of the
+    // tile); splits past the query's rows have no tiles and fold as empty.
+    const int nsplit = c1 - c0;
+    for (int sl = 0, it = 0; sl < nsplit; ++sl) {
+      const int it_end = min(ntiles, (sl + 1) * tps);
+      for (; it < it_end; ++it) {
+        // as attend_mixed_dma_kernel: raw tile it+1 landed and everyone is
+        // past tile it-1 -> refill its raw slot with tile it+3, convert tile
+        // it+1, consume tile it
+        if (it + 1 < ntiles) {
+          if (it + 2 < ntiles) wait_vmcnt<5>();    // tile it+2's copies may stay in flight
+          else wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        if (it + 3 < ntiles) issue(it + 3, (it + 3) % kRawRing);
+        if (it + 1 < ntiles) convert_mixed_tile(&Raw[(it + 1) % kRawRing][0], Xs[(it + 1) & 1]);
+        const float* rsc = reinterpret_cast<const float*>(&Raw[it % kRawRing][kRawTile]);
+        bf16x8 pa, pb;
+        tile_softmax_mixed(Xs[it & 1], so, it * kTileRows, rows, rsc, qf, a.scale, g, m_run, z_run, flag, pa, pb);
+        tile_pv_mixed(Xs[it & 1], so, pa, pb, acc_o);
+      }
+
+      // split c0 + sl ends: flagged heads are recomputed exactly by the whole
+      // workgroup (the owning lanes take the result), then the split folds in
+      const int split = c0 + sl;
+      if (tid < 2) flag_bits[tid] = 0u;
+      __syncthreads();
+      if (active && g == 0 && flag) atomicOr(&flag_bits[wid >> 1], 1u << (16 * (wid & 1) + r16));
+      __syncthreads();
+      const uint64_t todo = static_cast<uint64_t>(flag_bits[0]) | (static_cast<uint64_t>(flag_bits[1]) << 32);
+      if (todo) {
+        for (int hh = 0; hh < sp.HG; ++hh) {
+          if (!((todo >> hh) & 1u)) continue;       // uniform across the block
+          float mx, zx;
+          float2 ox;
+          recompute_split(a, sp.RS, b, t, hg * sp.HG + hh, split, rc_o + D + 2, rc_lc, mx, zx, ox);
+          if (2 * tid < D) {
+            rc_o[2 * tid] = ox.x;
+            rc_o[2 * tid + 1] = ox.y;
+          }
+          __syncthreads();
+          if (tid == 0) {
+            rc_o[D] = mx;
+            rc_o[D + 1] = zx;
+          }
+          __syncthreads();
+          if (wid == hh / 16 && r16 == hh % 16) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc_o[dt][i] = rc_o[16 * dt + 4 * g + i];
+            m_run = rc_o[D];
+            z_run = rc_o[D + 1];
+          }
+          __syncthreads();                          // rc_o free for the next head
+        }
+      }
+      float ca, cc;
+      fold_coeffs(fold, m_run, z_run, ca, cc);
+      // a split's output folds as bf16, as the split kernels store it, unless
+      // it was recomputed (the exact path keeps fp32 in both placements)
+      if (!((todo >> (wid * 16 + r16)) & 1u)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const uint32_t w = pack_bf16x2(acc_o[dt][i], acc_o[dt][i + 1]);
+            acc_o[dt][i] = bf16_to_f32(static_cast<uint16_t>(w & 0xffffu));
+            acc_o[dt][i + 1] = bf16_to_f32(static_cast<uint16_t>(w >> 16));
+          }
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          U[dt][i] = fmaf(U[dt][i], ca, acc_o[dt][i] * cc);
+          asm volatile("" : "+a"(U[dt][i]));
+          acc_o[dt][i] = 0.f;
+        }
+      m_run = -INFINITY;
+      z_run = 0.f;
+      flag = false;
+    }
+  }
+  if (active) store_folded<D>(a, b, t, head, g, [&](int dt, int i) { return U[dt][i]; }, fold, rope_tab);
+}
+
 // ---------------------------------------------------------------------------
 // float32 kernel on the vector ALUs
 // ---------------------------------------------------------------------------
@@ -2078,7 +2269,9 @@ void launch_mfma_d(LaunchScope& sc, const AttendArgs& a, const SplitPlan& sp, fl
                               : dim3(static_cast<uint32_t>(W), 1, a.B);
   const dim3 block(kAttThreads);
   if constexpr (D == 512) {                        // KV_MIXED rows exist only at D = 512
-    if (a.dt_kv == LCA_KV_MIXED && sp.HG == 128)
+    if (a.dt_kv == LCA_KV_MIXED && sp.SPW > 1)
+      sc.launch(attend_mixed_fold_kernel, grid, block, 0, a, sp);
+    else if (a.dt_kv == LCA_KV_MIXED && sp.HG == 128)
       sc.launch(attend_mixed_dma_kernel<2>, grid, block, 0, a, sp, po, pml);
     else if (a.dt_kv == LCA_KV_MIXED)
       sc.launch(attend_mixed_dma_kernel<1>, grid, block, 0, a, sp, po, pml);
@@ -2112,20 +2305,21 @@ size_t attend_workspace(const AttendArgs& a) {
 // LCA_SPLITS_ONE_WG / LCA_SPLITS_MANY_WG force a placement.
 constexpr int64_t kCUs = 256;
 
-// attend_dma_fold_kernel: bf16 rows of 512 channels, 64 heads per workgroup.
+// attend_dma_fold_kernel (bf16 rows) and attend_mixed_fold_kernel (mixed
+// rows): 512 channels, 64 heads per workgroup.
 // A 128-head plan (attend_dma_kernel<2>) folds there too, as two 64-head
 // groups over the same splits: per head that kernel runs the same MFMA chains
 // and softmax as the 64-head one, so the splits' results, and the fold of
 // them, keep their bits.
 bool folds_in_kernel(const AttendArgs& a, const SplitPlan& sp) {
-  return a.D == 512 && a.dt_kv == LCA_BF16 && (sp.HG != 128 || a.H % 64 == 0);
+  return a.D == 512 && (a.dt_kv == LCA_BF16 || a.dt_kv == LCA_KV_MIXED) && (sp.HG != 128 || a.H % 64 == 0);
 }
 
 void place_splits(const AttendArgs& a, SplitPlan& sp) {
   if (!folds_in_kernel(a, sp) || sp.S == 1) return;
   const int fold_hg = sp.HG == 128 ? 64 : sp.HG;                          // head group of the fold kernel
   const int64_t q_items = static_cast<int64_t>(a.B) * a.Tq;
-  const double rows = static_cast<double>(sp.RS) * a.D * 2;                  // one split's rows (bf16)
+  const double rows = static_cast<double>(sp.RS) * (a.dt_kv == LCA_KV_MIXED ? kMixRow + 4 : a.D * 2);   // one split's rows
   const double part = 2.0 * sp.HG * (a.D * 2 + 8);                         // its bf16 partial + (max, sum), out and back
   const int64_t one_items = q_items * (a.H / fold_hg), split_items = q_items * sp.n_hg * sp.S;
   const double t_one = static_cast<double>((one_items + kCUs - 1) / kCUs) * sp.S * rows;

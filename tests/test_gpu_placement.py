@@ -198,3 +198,83 @@ def test_sequence_major_grid_keeps_the_bits(kind, H, B, Tq):
     else:
         ref, _ = O.hca_attend(q[b], E[b], m, win[b], sink, 1 / math.sqrt(D), q_pos0, W, True, 10000.0, 64)
     row_tol_check(host(o_all)[b], ref, 2e-2, f"batch of {B}, sequence {b}")
+
+
+def _mixed(L, src):
+    """KV_MIXED rows (448 e4m3fn + 64 bf16 channels, fp32 row scale) of fp32 rows."""
+    B, N, D = src.shape
+    rows = torch.empty((B, N, D + 64), dtype=torch.uint8, device=DEV)
+    scale = torch.empty((B, N), dtype=torch.float32, device=DEV)
+    L.lca_quantize_rows(L.KV_MIXED, dev_f32(src), rows, scale)
+    return rows, scale
+
+
+def _run_mixed(L, kind, q_d, E, idx_d, win, sink_d, m, W, q_pos0, flags):
+    B, Tq, H, D = q_d.shape
+    out = torch.empty((B, Tq, H, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+    kw = dict(m=m, W=W, q_pos0=q_pos0, scale=1 / math.sqrt(D), flags=L.INV_ROPE | flags, rope_dims=64,
+              lse_out=lse, kv_scale=E[1], win_scale=win[1])
+    if kind == "csa":
+        L.csa_attend(L.BF16, L.KV_MIXED, q_d, E[0], idx_d, win[0], sink_d, out, **kw)
+    else:
+        L.hca_attend(L.BF16, L.KV_MIXED, q_d, E[0], win[0], sink_d, out, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("kind,ramp", [("csa", False), ("hca", False), ("hca", True)])
+def test_mixed_row_placements_give_the_same_bits(kind, ramp):
+    # KV_MIXED rows, 128 heads, one query: 2 splits of 512 rows. The split
+    # placement (128-head mixed kernel, bf16 partials, combine) against the
+    # mixed fold kernel (two 64-head groups walking both splits); with the
+    # logit ramp, splits are flagged and recomputed exactly in both.
+    L = need_gpu()
+    rng = np.random.default_rng(180 + len(kind) + ramp)
+    B, Tq, H, D, W, k = 2, 1, 128, 512, 128, 517
+    m = 4 if kind == "csa" else 128
+    q_pos0 = 12001 if kind == "csa" else 128 * 700 + 9
+    N_cap = (q_pos0 + Tq) // m + 2
+    if ramp:
+        u = rng.standard_normal(D)
+        u /= np.linalg.norm(u)
+        lin = np.linspace(-1.0, 1.0, N_cap)
+        Esrc = np.stack([(lin[:, None] * u[None, :] + 0.05 * rng.standard_normal((N_cap, D)) / np.sqrt(D))
+                         for _ in range(B)]).astype(np.float32)
+        sharp = np.geomspace(1.0, 4000.0, H)
+        q = sharp[None, None, :, None] * (u + 0.1 * rng.standard_normal((B, Tq, H, D)) / np.sqrt(D))
+        q = WL.bf16_exact((q * np.sqrt(D)).astype(np.float32))
+    else:
+        Esrc = (rng.standard_normal((B, N_cap, D)) / np.sqrt(D)).astype(np.float32)
+        q = WL.bf16_exact((rng.standard_normal((B, Tq, H, D)) * 6.0 / np.sqrt(D)).astype(np.float32))
+    wsrc = (rng.standard_normal((B, W - 1 + Tq, D)) / np.sqrt(D)).astype(np.float32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    idx = None
+    idx_d = None
+    if kind == "csa":
+        idx = np.full((B, Tq, k), -1, np.int32)
+        for b in range(B):
+            nv = O.n_visible(q_pos0, m)
+            sel = rng.choice(nv, size=k - 3, replace=False)
+            idx[b, 0, :len(sel)] = sel
+        idx_d = torch.from_numpy(idx).to(DEV)
+    E, win = _mixed(L, Esrc), _mixed(L, wsrc)
+    args = (dev_bf16(q), E, idx_d, win, dev_f32(sink), m, W, q_pos0)
+    say(f"mixed-row placements {kind} ramp={ramp}")
+    o1, l1 = _run_mixed(L, kind, *args, L.SPLITS_MANY_WG)
+    o2, l2 = _run_mixed(L, kind, *args, L.SPLITS_ONE_WG)
+    assert torch.equal(o1, o2), "the two placements differ"
+    assert torch.equal(l1, l2)
+    scale = 1 / math.sqrt(D)
+    for b in range(B):
+        Ed = O.kv_mixed_decode(*O.kv_mixed_quantize(Esrc[b], 64))
+        Wd = O.kv_mixed_decode(*O.kv_mixed_quantize(wsrc[b], 64))
+        if kind == "csa":
+            ref, rl = O.csa_attend(q[b], Ed, idx[b], Wd, sink, scale, q_pos0, W, True, 10000.0, 64)
+        else:
+            ref, rl = O.hca_attend(q[b], Ed, m, Wd, sink, scale, q_pos0, W, True, 10000.0, 64)
+        if ramp:
+            assert np.ptp(rl) > 100.0, "the case must span a wide logit range"
+        row_tol_check(host(o2)[b], ref, 2e-2, f"mixed one-workgroup placement {kind} b={b}")
+        lse_err = np.abs(l2.cpu().numpy()[b] - rl) / np.maximum(1.0, np.abs(rl))
+        assert lse_err.max() <= 2e-2, f"lse relative error {lse_err.max()}"
