@@ -268,6 +268,40 @@ def csa_prefill_setup(d):
     return step, flops
 
 
+def small_layer_leg(steps, warmup):
+    """Workload 1: one fp32 CSA layer forward over 1024 causal tokens from
+    position 0 (8 heads, D = 128, indexer 4 x 64, k = 64): both compressions
+    (entries with RMSNorm + RoPE, indexer keys), index top-k and attention.
+    Returns the generated inputs (the oracle sample reuses them) and the leg."""
+    d = WL.make_csa_layer()
+    B, T, D, m, dI, H_I, k, H, W = d["B"], d["T"], d["D"], d["m"], d["d_I"], d["H_I"], d["k"], d["H"], d["W"]
+    t = {n: _f32(d[n]) for n in ("ca", "za", "cb", "zb", "ica", "iza", "icb", "izb", "q", "qI", "w", "win",
+                                 "sink", "norm_w")}
+    N = T // m
+    E = torch.empty((B, N, D), dtype=torch.float32, device=DEV)
+    KI = torch.empty((B, N, dI), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, T, H, D), dtype=torch.float32, device=DEV)
+    ws_i = torch.empty(L.csa_index_topk_workspace(L.F32, B, T, H_I, dI, N, m, k, 0), dtype=torch.uint8, device=DEV)
+    ws_a = torch.empty(L.csa_attend_workspace(L.F32, L.F32, B, T, H, D, N, m, k, W, 0), dtype=torch.uint8,
+                       device=DEV)
+
+    def step(i):
+        L.csa_compress(L.F32, L.F32, t["cb"], t["zb"], m, ca=t["ca"], za=t["za"], pos0=0, flags=L.NORM | L.ROPE,
+                       norm_w=t["norm_w"], eps=d["eps"], rope_base=d["rope_base"], rope_dims=d["rope_dims"], out=E)
+        L.csa_compress(L.F32, L.F32, t["icb"], t["izb"], m, ca=t["ica"], za=t["iza"], pos0=0, out=KI)
+        L.csa_index_topk(L.F32, t["qI"], t["w"], KI, idx, m=m, k=k, q_pos0=0, ws=ws_i)
+        L.csa_attend(L.F32, L.F32, t["q"], E, idx, t["win"], t["sink"], out, m=m, W=W, q_pos0=0,
+                     scale=1 / math.sqrt(D), flags=L.INV_ROPE, rope_dims=d["rope_dims"], ws=ws_a)
+
+    el = timed(step, steps, warmup)
+    ms = 1e3 * el / steps
+    kt = kernel_times(step, steps)
+    progress(f"csa layer fp32: {ms:.4f} ms/step")
+    return d, {"workload": "csa_layer_fp32_t1024_h8_d128", "tokens_per_s": B * T / (ms * 1e-3), "ms_per_step": ms,
+               "kernels_us": per_step(kt), "kernel_launches_per_step": launches(kt), "dtype": "f32"}
+
+
 def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -718,11 +752,14 @@ def _blas_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(d, h, reps=3):
+def cpu_baseline(d, h, layer=None, samples=True, reps=3):
     """The float64 oracle on the host cores, on the same workloads: the whole
     CSA decode batch (indexer scores, top-k, attention for every sequence) and
     the whole HCA decode batch, each run ``reps`` times (median reported), with
-    the BLAS threads numpy has by default and again with one thread."""
+    the BLAS threads numpy has by default and again with one thread. Beside
+    them, with the default threads: the whole fp32 layer of workload 1 (median
+    of ``reps``), and one run each of bounded samples of the prefill and the
+    mixed pair (inputs generated outside the timed region)."""
     import oracle as O
 
     def csa_batch():
@@ -749,8 +786,29 @@ def cpu_baseline(d, h, reps=3):
             rates.append(n / (time.perf_counter() - t0))
         return float(np.median(rates))
 
+    def layer_run():
+        x = layer
+        m, R, T = x["m"], x["rope_dims"], x["T"]
+        Eo = O.compress_epilogue(O.compress_sequence(x["cb"][0], x["zb"][0], m, x["ca"][0], x["za"][0]),
+                                 0, m, x["norm_w"], x["eps"], x["rope_base"], R)
+        Ko = O.compress_sequence(x["icb"][0], x["izb"][0], m, x["ica"][0], x["iza"][0])
+        idx = np.full((T, x["k"]), -1, np.int64)
+        for t in range(T):
+            sel = O.topk_select(O.index_scores(x["qI"][0, t], x["w"][0, t], Ko, O.n_visible(t, m)), x["k"])
+            idx[t, :len(sel)] = sel
+        O.csa_attend(x["q"][0], Eo, idx, x["win"][0], x["sink"], 1 / math.sqrt(x["D"]), 0, x["W"], True,
+                     x["rope_base"], R)
+        return T
+
     cores = _blas_threads()
     res = {"csa": median_rate(csa_batch), "hca": median_rate(hca_batch)}
+    extra = {}
+    if layer is not None:
+        extra["csa_layer_fp32"] = {"value": median_rate(layer_run), "unit": "tokens/s",
+                                   "sample": f"the whole layer of 1024 tokens (both compressions, every query's "
+                                             f"scores, top-k and attention), median of {reps} runs"}
+    if samples:
+        extra.update(oracle_samples(O))
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
@@ -764,7 +822,66 @@ def cpu_baseline(d, h, reps=3):
             "value_1thread": res["csa_1t"], "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(),
             "hca_decode": {"value": res["hca"], "value_1thread": res["hca_1t"], "unit": "tokens/s",
                            "sample": f"the whole HCA decode batch ({h['B']} sequences at {h['q_pos0']} tokens), "
-                                     f"median of {reps} runs"}}
+                                     f"median of {reps} runs"}, **extra}
+
+
+PREFILL_SAMPLE_ROWS = [0, 1, 1024, 2047, 3000, 4093, 4094, 4095]
+
+
+def oracle_samples(O):
+    """One run each (the cfg 4 / 5 rule) of the oracle on bounded samples:
+    the prefill's compression of its 4096 new tokens (both streams) plus 8 of
+    its queries (scores over 263168 keys, top-k 1024, attention over 1152 rows
+    x 128 heads), reported as queries per second with the compression charged
+    at 8/4096 of its time; and one sequence of the mixed pair (MXFP4 indexer
+    operands, bf16 scores, top-k, attention over KV_MIXED rows, and the HCA
+    layer over 8192 + 128 rows)."""
+    out = {}
+    pd = WL.make_csa_prefill(q_rows=PREFILL_SAMPLE_ROWS)
+    m, D, R = pd["m"], pd["D"], pd["rope_dims"]
+    t0 = time.perf_counter()
+    E_new = O.compress_epilogue(O.compress_sequence(pd["cb"][0], pd["zb"][0], m, pd["ca"][0], pd["za"][0],
+                                                    pd["prev_ca"][0], pd["prev_za"][0]),
+                                pd["pos0"], m, pd["norm_w"], pd["eps"], pd["rope_base"], R)
+    K_new = O.compress_sequence(pd["icb"][0], pd["izb"][0], m, pd["ica"][0], pd["iza"][0], pd["iprev_ca"][0],
+                                pd["iprev_za"][0])
+    t_comp = time.perf_counter() - t0
+    E_all = np.concatenate([pd["E_prefix"][0], O.bf16_round(E_new)])
+    K_all = np.concatenate([pd["kI_prefix"][0], O.bf16_round(K_new)])
+    t0 = time.perf_counter()
+    for t in PREFILL_SAMPLE_ROWS:
+        p = pd["q_pos0"] + t
+        sel = O.topk_select(O.index_scores(pd["qI"][0, t], pd["w"][0, t], K_all, O.n_visible(p, m)), pd["k"])
+        O.csa_attend_query(pd["q"][0, t], E_all, sel, pd["win"][0], pd["sink"], 1 / math.sqrt(D), p, pd["q_pos0"],
+                           pd["W"], True, pd["rope_base"], R)
+    t_q = time.perf_counter() - t0
+    nq = len(PREFILL_SAMPLE_ROWS)
+    out["csa_prefill"] = {"value": nq / (t_q + t_comp * nq / pd["Tq"]), "unit": "tokens/s",
+                          "compress_s": t_comp, "queries_s": t_q,
+                          "sample": f"compression of the {pd['Tq']} new tokens + {nq} queries of the 4096 "
+                                    f"(rows {PREFILL_SAMPLE_ROWS}), one run"}
+    del pd, E_all, K_all
+    x = WL.make_mixed_pair(seqs=[0])
+    q_pos0, m, m2, k, W, D = x["q_pos0"], x["m"], x["m2"], x["k"], x["W"], x["D"]
+    scale = 1 / math.sqrt(D)
+    t0 = time.perf_counter()
+    qd = O.mxfp4_decode(*O.mxfp4_quantize(x["qI"][0, 0]))
+    kd = O.mxfp4_decode(*O.mxfp4_quantize(x["kI"][0]))
+    s = O.bf16_round(O.index_scores(qd, x["w"][0, 0], kd, O.n_visible(q_pos0, m)))
+    sel = O.topk_select(s, k)
+    Esel = O.kv_mixed_decode(*O.kv_mixed_quantize(x["E"][0][sel], 64))
+    Wd = O.kv_mixed_decode(*O.kv_mixed_quantize(x["win"][0], 64))
+    O.csa_attend_query(x["q"][0, 0], Esel, np.arange(len(sel)), Wd, x["sink"], scale, q_pos0, q_pos0, W, True,
+                       10000.0, 64)
+    E2d = O.kv_mixed_decode(*O.kv_mixed_quantize(x["E2"][0], 64))
+    W2d = O.kv_mixed_decode(*O.kv_mixed_quantize(x["win2"][0], 64))
+    O.hca_attend_query(x["q2"][0, 0], E2d, O.n_visible(q_pos0, m2), W2d, x["sink2"], scale, q_pos0, q_pos0, W,
+                       True, 10000.0, 64)
+    t_m = time.perf_counter() - t0
+    out["mixed_pair"] = {"value": 1.0 / t_m, "unit": "tokens/s",
+                         "sample": "sequence 0 of the 64 (both layers, the quantisation of its rows and indexer "
+                                   "operands included), one run"}
+    return out
 
 
 def main():
@@ -781,6 +898,9 @@ def main():
     ap.add_argument("--no-placement", action="store_true")
     ap.add_argument("--no-outproj", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-small-layer", action="store_true")
+    ap.add_argument("--no-oracle-samples", action="store_true",
+                    help="cpu_baseline without the prefill and mixed-pair samples")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB device to device (counter calibration)")
     ap.add_argument("--only", choices=["csa", "hca", "prefill", "mixed"],
@@ -896,6 +1016,9 @@ def main():
         if not args.no_ragged:
             result.setdefault("ragged", {})["hca_decode_b8_ctx_le1048576"] = ragged_leg(
                 h, args.copies, max(20, args.steps // 2), args.warmup, 13, hms)
+    layer_d = None
+    if not args.no_small_layer:
+        layer_d, result["small_layer"] = small_layer_leg(max(20, args.steps // 4), max(2, args.warmup // 4))
     if not args.no_prefill:
         pd = WL.make_csa_prefill()
         pstep, pflops = csa_prefill_setup(pd)
@@ -951,7 +1074,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, WL.make_hca_decode())
+        result["cpu_baseline"] = cpu_baseline(d, WL.make_hca_decode(), layer=layer_d,
+                                              samples=not args.no_oracle_samples)
     print(json.dumps(result), flush=True)
 
 
