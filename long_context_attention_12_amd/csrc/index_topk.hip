@@ -267,6 +267,87 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 32 or 64 indexer heads in bf16: one query's heads fill MT = HI / 16 MFMA M
+// tiles, and each wave scores 32 keys of one query (grid y = query). Per tile
+// the head sum is folded as for 16 heads (head pairs, then across the lane
+// groups), and the tiles' sums add in tile order.
+// ---------------------------------------------------------------------------
+template <int MT, int DI>
+__global__ __launch_bounds__(kScoreThreads) void index_score_bf16_wide_kernel(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
+    float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
+    const int64_t* __restrict__ q_pos, int m, bool round_bf16, SelAux aux) {
+  constexpr int HI = 16 * MT;
+  constexpr int KS = DI / 32;
+  constexpr int UNR = kKeysPerWave / 16;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int b = blockIdx.z;
+  q_pos0 = seq_pos(q_pos, q_pos0, b);
+  const int qt = t_off + blockIdx.y;                 // this workgroup's query
+  if (qt >= min(Tq, t_off + Tc)) return;
+  int64_t nv = n_visible(q_pos0 + qt, m);
+  if (nv > N_cap) nv = N_cap;
+  const int64_t key0 = static_cast<int64_t>(blockIdx.x) * kKeysPerWG + wid * kKeysPerWave;
+  if (key0 >= nv) return;
+
+  const uint16_t* kb = kI + static_cast<int64_t>(b) * N_cap * DI;
+  uint4 kv[UNR][KS];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    int64_t j = key0 + 16 * u + r16;
+    if (j >= nv) j = nv - 1;                        // stay in bounds; result discarded
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kv[u][s] = *reinterpret_cast<const uint4*>(kb + j * DI + 32 * s + 8 * g);
+  }
+  // A operand of tile mt: row r16 -> head 16 mt + r16; K chunk 8g .. 8g + 7
+  const int64_t qrow = (static_cast<int64_t>(b) * Tq + qt) * HI;
+  bf16x8 aq[MT][KS];
+  float wv[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      aq[mt][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qI + (qrow + 16 * mt + r16) * DI + 32 * s + 8 * g));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[mt][i] = w[qrow + 16 * mt + 4 * g + i];   // accumulator row 4g + i
+  }
+  float* srow = scores + (static_cast<int64_t>(b) * Tc + (qt - t_off)) * ld;
+  float* gmrow = aux.gmax ? aux.gmax + (static_cast<int64_t>(b) * Tc + (qt - t_off)) * aux.ldg : nullptr;
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    float sc = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[mt][s], __builtin_bit_cast(bf16x8, kv[u][s]), acc, 0, 0, 0);
+      pin_uniform(acc);
+      float p01, p23;
+      head_pairs(acc, wv[mt], p01, p23);
+      float t = p01 + p23;
+      t += __shfl_xor(t, 16, 64);
+      t += __shfl_xor(t, 32, 64);
+      sc = mt == 0 ? t : sc + t;
+    }
+    const int64_t j = key0 + 16 * u + r16;
+    const float v = round_bf16 ? bf16_round(sc) : sc;
+    if (g == 0 && j < nv) srow[j] = v;
+    if (gmrow) {
+      // the group's largest visible score (lanes r16 of one row of 16)
+      float x = j < nv ? v : -INFINITY;
+      x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false)));
+      x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false)));
+      x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));
+      x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));
+      const int64_t grp = (key0 + 16 * u) / kGroup;
+      if (lane == 0 && grp * kGroup < nv) gmrow[grp] = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Many queries per call (prefill): the decode kernel above would re-read every
 // key once per 16-row query tile. Here a workgroup holds 256 / H_I queries in
 // registers (4 waves x 4 M tiles of 16 query-head rows, d_I = 128) and walks a
@@ -2103,6 +2184,20 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
   }
 }
 
+template <int MT>
+void launch_score_bf16_wide(LaunchScope& ls, const IndexArgs& a, float* sc, int64_t ld, int t_off, int Tc,
+                            dim3 grid, SelAux aux) {
+  const bool rb = (a.flags & LCA_SCORE_BF16) != 0;
+  const uint16_t* q = static_cast<const uint16_t*>(a.qI);
+  const uint16_t* k = static_cast<const uint16_t*>(a.kI);
+  switch (a.d_I) {
+    case 64: ls.launch(index_score_bf16_wide_kernel<MT, 64>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb, aux); break;
+    case 128: ls.launch(index_score_bf16_wide_kernel<MT, 128>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb, aux); break;
+    case 256: ls.launch(index_score_bf16_wide_kernel<MT, 256>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb, aux); break;
+    default: ls.launch(index_score_bf16_wide_kernel<MT, 32>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, rb, aux); break;
+  }
+}
+
 template <int HI>
 void launch_score_bf16_hi(LaunchScope& ls, const IndexArgs& a, float* sc, int64_t ld, int t_off, int Tc,
                           dim3 grid, SelAux aux) {
@@ -2150,7 +2245,8 @@ bool long_old_possible(const IndexArgs& a) {
 // for the batch, long lists, and every row longer than k (so every output
 // score comes from a candidate's key).
 bool cand_mode(const IndexArgs& a) {
-  if (!(a.dt == LCA_BF16 && a.d_I == 128 && a.H_I >= 2 && a.Tq >= kTiledMinQueries && !a.q_pos)) return false;
+  if (!(a.dt == LCA_BF16 && a.d_I == 128 && a.H_I >= 2 && a.H_I <= 16 && a.Tq >= kTiledMinQueries && !a.q_pos))
+    return false;
   int64_t nv0 = n_visible(a.q_pos0, a.m), nv1 = n_visible(a.q_pos0 + a.Tq - 1, a.m);
   if (nv0 > a.N_cap) nv0 = a.N_cap;
   if (nv1 > a.N_cap) nv1 = a.N_cap;
@@ -2285,7 +2381,7 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
     const int tcn = min(Tc, a.Tq - t_off);
     int64_t nv_max = n_visible(a.q_pos0 + t_off + tcn - 1, a.m);
     if (nv_max > a.N_cap) nv_max = a.N_cap;
-    const bool tiled = a.dt == LCA_BF16 && a.d_I == 128 && tcn >= kTiledMinQueries;
+    const bool tiled = a.dt == LCA_BF16 && a.d_I == 128 && a.H_I <= 16 && tcn >= kTiledMinQueries;
     if (nv_max > kRound && nv_max > a.k && !use_chunked(a, nv_max, tiled) && !long_old_possible(a))
       return hipErrorInvalidValue;
   }
@@ -2331,7 +2427,7 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
       }
       continue;
     }
-    const bool tiled = a.dt == LCA_BF16 && a.d_I == 128 && tcn >= kTiledMinQueries;
+    const bool tiled = a.dt == LCA_BF16 && a.d_I == 128 && a.H_I <= 16 && tcn >= kTiledMinQueries;
     const int64_t ng_max = (nv_max + kGroup - 1) / kGroup;
     const bool filt = use_chunked(a, nv_max, tiled);
     SelAux aux{filt ? w.fw.gmax : nullptr, w.fw.ldg, nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr};
@@ -2362,6 +2458,11 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
         int64_t kc, per;
         tiled_ranges(a, nv_max, tcn, false, &kc, &per);
         launch_tiled<kTiledScores>(scope, a, kc, tcn, sc, ld, t_off, Tc, per, key16, aux);
+      } else if (a.H_I > 16) {
+        // 32 or 64 heads: one query per grid row
+        dim3 grid((nv_max + kKeysPerWG - 1) / kKeysPerWG, tcn, a.B);
+        if (a.H_I == 32) launch_score_bf16_wide<2>(scope, a, sc, ld, t_off, Tc, grid, aux);
+        else launch_score_bf16_wide<4>(scope, a, sc, ld, t_off, Tc, grid, aux);
       } else {
         const int QPB = 16 / a.H_I;
         dim3 grid((nv_max + kKeysPerWG - 1) / kKeysPerWG, (tcn + QPB - 1) / QPB, a.B);

@@ -162,7 +162,7 @@ def _index_case(rng, B, Tq, H_I, d_I, N_cap, spikes=True, ties=False):
     return qI, w, kI
 
 
-@pytest.mark.parametrize("H_I", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("H_I", [1, 2, 4, 8, 16, 32, 64])
 def test_index_topk_decode_bf16(H_I):
     L = need_gpu()
     rng = np.random.default_rng(20 + H_I)
@@ -231,6 +231,34 @@ def test_index_topk_many_queries_tiled(H_I, bf16_scores):
             ref = O.bf16_round(s[sel]) if bf16_scores else s[sel]
             tol = np.abs(ref) * (2.0 ** -7 if bf16_scores else 1e-4) + 1e-6 * np.max(np.abs(s))
             assert np.all(np.abs(sco_h[b, t][:len(sel)] - ref) <= tol), (b, t)
+
+
+@pytest.mark.parametrize("H_I,bf16_scores", [(32, False), (64, True)])
+def test_index_topk_wide_heads_many_queries(H_I, bf16_scores):
+    # The pages' 64 indexer heads (and 32): one query's heads span several
+    # MFMA tiles. 70 queries over lists longer than one register round: the
+    # scores and group maxima of the wide kernel feed the chunked select.
+    L = need_gpu()
+    rng = np.random.default_rng(62 + H_I)
+    B, Tq, d_I, m, k = 1, 70, 128, 4, 300
+    q_pos0 = 4 * 40000 + 3
+    N_cap = (q_pos0 + Tq) // m + 2
+    qI, w, kI = _index_case(rng, B, Tq, H_I, d_I, N_cap)
+    idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+    sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    say(f"wide-head index H_I={H_I} bf16={bf16_scores}")
+    L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
+                     flags=L.SCORE_BF16 if bf16_scores else 0, score_out=sco)
+    torch.cuda.synchronize()
+    idx_h, sco_h = idx.cpu().numpy(), sco.cpu().numpy()
+    for t in list(range(0, Tq, 7)) + [Tq - 1]:
+        nv = O.n_visible(q_pos0 + t, m)
+        s = O.index_scores(qI[0, t], w[0, t], kI[0], nv)
+        check_topk_set(idx_h[0, t], s, k, bf16_scores=bf16_scores)
+        sel = idx_h[0, t][idx_h[0, t] >= 0]
+        ref = O.bf16_round(s[sel]) if bf16_scores else s[sel]
+        tol = np.abs(ref) * (2.0 ** -7 if bf16_scores else 1e-4) + 1e-6 * np.max(np.abs(s))
+        assert np.all(np.abs(sco_h[0, t][:len(sel)] - ref) <= tol), t
 
 
 def test_index_topk_many_queries_from_sequence_start():
