@@ -242,9 +242,9 @@ int lca_quantize_rows(void* stream, int dt_out, int64_t n_rows, int D, int rope_
  *   score_out [B, Tq, k] float32 or NULL: the score of each idx_out entry
  *             (-inf for padding)
  * Requirements: N_cap >= n_vis of the last query; 1 <= k <= 4096;
- *   d_I % 32 == 0 and d_I <= 256; H_I in {1, 2, 4, 8, 16} for LCA_BF16 and
- *   LCA_MXFP4, also 32 and 64 for LCA_BF16 (the pages' indexer has 64 heads,
- *   [Qiaomu] 训练配置; any H_I <= 64 for LCA_F32); MXFP4 needs d_I == 128.
+ *   d_I % 32 == 0 and d_I <= 256; H_I in {1, 2, 4, 8, 16, 32, 64} for LCA_BF16
+ *   and LCA_MXFP4 (the pages' indexer has 64 heads, [Qiaomu] 训练配置; any
+ *   H_I <= 64 for LCA_F32); MXFP4 needs d_I == 128.
  * ------------------------------------------------------------------------- */
 size_t csa_index_topk_workspace(int dt, int B, int Tq, int H_I, int d_I, int64_t N_cap,
                                 int m, int k, int64_t q_pos0, uint32_t flags);

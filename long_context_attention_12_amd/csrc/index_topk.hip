@@ -803,6 +803,89 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_fp4_kernel(
   }
 }
 
+// 32 or 64 heads in MXFP4: as index_score_bf16_wide_kernel (one query per
+// grid row, its heads over MT M tiles, tile sums added in order), one scaled
+// MFMA per tile and key group.
+template <int MT>
+__global__ __launch_bounds__(kScoreThreads) void index_score_fp4_wide_kernel(
+    const uint8_t* __restrict__ qI, const uint8_t* __restrict__ qI_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ kI, const uint8_t* __restrict__ kI_scale, float* __restrict__ scores, int64_t ld,
+    int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m,
+    bool round_bf16, SelAux aux) {
+  constexpr int HI = 16 * MT;
+  constexpr int UNR = kFp4KeysPerWave / 16;
+  constexpr int ROW = 64;                          // packed bytes per 128-channel row
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int b = blockIdx.z;
+  q_pos0 = seq_pos(q_pos, q_pos0, b);
+  const int qt = t_off + blockIdx.y;
+  if (qt >= min(Tq, t_off + Tc)) return;
+  int64_t nv = n_visible(q_pos0 + qt, m);
+  if (nv > N_cap) nv = N_cap;
+  const int64_t key0 = static_cast<int64_t>(blockIdx.x) * kFp4KeysPerWG + wid * kFp4KeysPerWave;
+  if (key0 >= nv) return;
+
+  const uint8_t* kb = kI + static_cast<int64_t>(b) * N_cap * ROW;
+  const uint32_t* ksb = reinterpret_cast<const uint32_t*>(kI_scale) + static_cast<int64_t>(b) * N_cap;
+  uint4 kc[UNR];
+  uint32_t ks[UNR];
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    int64_t j = key0 + 16 * u + r16;
+    if (j >= nv) j = nv - 1;                        // stay in bounds; result discarded
+    kc[u] = *reinterpret_cast<const uint4*>(kb + j * ROW + 16 * g);
+    ks[u] = ksb[j];
+  }
+  const int64_t qrow = (static_cast<int64_t>(b) * Tq + qt) * HI;
+  i32x8 A[MT];
+  int qs[MT];
+  float wv[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int64_t r = qrow + 16 * mt + r16;         // tile row r16: head 16 mt + r16
+    const uint4 qa = *reinterpret_cast<const uint4*>(qI + r * ROW + 16 * g);
+    A[mt] = i32x8{static_cast<int>(qa.x), static_cast<int>(qa.y), static_cast<int>(qa.z), static_cast<int>(qa.w),
+                  0, 0, 0, 0};
+    qs[mt] = qI_scale[r * 4 + g];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[mt][i] = w[qrow + 16 * mt + 4 * g + i];
+  }
+  float* srow = scores + (static_cast<int64_t>(b) * Tc + (qt - t_off)) * ld;
+  float* gmrow = aux.gmax ? aux.gmax + (static_cast<int64_t>(b) * Tc + (qt - t_off)) * aux.ldg : nullptr;
+#pragma unroll
+  for (int u = 0; u < UNR; ++u) {
+    const i32x8 Bk = {static_cast<int>(kc[u].x), static_cast<int>(kc[u].y), static_cast<int>(kc[u].z),
+                      static_cast<int>(kc[u].w), 0, 0, 0, 0};
+    const int sb = static_cast<int>((ks[u] >> (8 * g)) & 0xffu);
+    float sc = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[mt], Bk, acc, 4, 4, 0, qs[mt], 0, sb);
+      pin_uniform(acc);
+      float p01, p23;
+      head_pairs(acc, wv[mt], p01, p23);
+      float t = p01 + p23;
+      t += __shfl_xor(t, 16, 64);
+      t += __shfl_xor(t, 32, 64);
+      sc = mt == 0 ? t : sc + t;
+    }
+    const int64_t j = key0 + 16 * u + r16;
+    const float v = round_bf16 ? bf16_round(sc) : sc;
+    if (g == 0 && j < nv) srow[j] = v;
+    if (gmrow) {
+      float x = j < nv ? v : -INFINITY;
+      x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false)));
+      x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false)));
+      x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));
+      x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));
+      const int64_t grp = (key0 + 16 * u) / kGroup;
+      if (lane == 0 && grp * kGroup < nv) gmrow[grp] = x;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // float32 scoring on the vector ALUs (small fp32 layers)
 // ---------------------------------------------------------------------------
@@ -2439,6 +2522,16 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
                      static_cast<uint32_t>((a.H_I * a.d_I + a.H_I) * sizeof(float)),
                            static_cast<const float*>(a.qI), a.w, static_cast<const float*>(a.kI), sc, ld,
                            a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, a.H_I, a.d_I, key16, aux);
+      } else if (a.dt == LCA_MXFP4 && a.H_I > 16) {
+        dim3 grid((nv_max + kFp4KeysPerWG - 1) / kFp4KeysPerWG, tcn, a.B);
+        const uint8_t* q = static_cast<const uint8_t*>(a.qI);
+        const uint8_t* qs = static_cast<const uint8_t*>(a.qI_scale);
+        const uint8_t* k = static_cast<const uint8_t*>(a.kI);
+        const uint8_t* ks = static_cast<const uint8_t*>(a.kI_scale);
+        if (a.H_I == 32)
+          scope.launch(index_score_fp4_wide_kernel<2>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16, aux);
+        else
+          scope.launch(index_score_fp4_wide_kernel<4>, grid, dim3(kScoreThreads), 0, q, qs, a.w, k, ks, sc, ld, a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, key16, aux);
       } else if (a.dt == LCA_MXFP4) {
         const int QPB = 16 / a.H_I;
         dim3 grid((nv_max + kFp4KeysPerWG - 1) / kFp4KeysPerWG, (tcn + QPB - 1) / QPB, a.B);

@@ -339,8 +339,8 @@ static int check_index(const lca::IndexArgs& a) {
     if (a.H_I > 64) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: F32 supports H_I <= 64");
   } else if (a.dt == LCA_BF16 || a.dt == LCA_MXFP4) {
     const bool pow2 = a.H_I == 1 || a.H_I == 2 || a.H_I == 4 || a.H_I == 8 || a.H_I == 16;
-    if (!(pow2 || (a.dt == LCA_BF16 && (a.H_I == 32 || a.H_I == 64))))
-      return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: H_I must be 1, 2, 4, 8 or 16, or 32 or 64 for BF16 (H_I=%d)", a.H_I);
+    if (!(pow2 || a.H_I == 32 || a.H_I == 64))
+      return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: H_I must be 1, 2, 4, 8, 16, 32 or 64 (H_I=%d)", a.H_I);
     if (a.dt == LCA_MXFP4) {
       if (a.d_I != 128) return fail(LCA_ERR_UNSUPPORTED, "csa_index_topk: MXFP4 needs d_I == 128");
       if (!a.qI_scale || !a.kI_scale) return fail(LCA_ERR_ARG, "csa_index_topk: MXFP4 needs qI_scale and kI_scale");

@@ -86,7 +86,6 @@ def test_index_topk_validation(lib):
     _expect(call(k=0), -2, "k must")
     _expect(call(H_I=3), -2, "H_I")
     _expect(call(H_I=48), -2, "H_I")
-    _expect(call(dt=3, H_I=32), -2, "H_I")
     _expect(call(d_I=100), -2, "d_I")
     _expect(call(N=100), -1, "N_cap")
     _expect(call(dt=3), -1, "MXFP4 needs qI_scale")

@@ -346,7 +346,7 @@ def _mxfp4_on_gpu(L, x):
     return codes.reshape(x.shape[:-1] + (x.shape[-1] // 2,)), scales.reshape(x.shape[:-1] + (x.shape[-1] // 32,))
 
 
-@pytest.mark.parametrize("H_I", [1, 4, 16])
+@pytest.mark.parametrize("H_I", [1, 4, 16, 32, 64])
 @pytest.mark.parametrize("bf16_scores", [True, False])
 def test_index_topk_mxfp4(H_I, bf16_scores):
     # MXFP4 indexer operands (queries and keys), heavy-tailed query norms; the
