@@ -29,6 +29,7 @@ __all__ = [
     "rms_norm",
     "rope_rotate",
     "compress_epilogue",
+    "compress_backward",
     "index_scores",
     "topk_select",
     "topk_classes",
@@ -543,6 +544,84 @@ def hca_attend_backward(q, E, m, win, sink, scale, q_pos0, dout, W=128, inv_rope
     Tq = q.shape[0]
     sels = [np.arange(n_visible(q_pos0 + t, m)) for t in range(Tq)]
     return _attend_backward(q, E, sels, win, sink, scale, q_pos0, W, inv_rope, rope_base, rope_dims, dout)
+
+
+def compress_backward(dout, cb, zb, m, ca=None, za=None, prev_ca=None, prev_za=None, overlap=True,
+                      pos0=0, norm_w=None, eps=1e-6, rope_base=None, rope_dims=0):
+    """Gradients of ``compress_epilogue(compress_sequence(...))`` with respect to
+    its inputs, given ``dout`` = dL/d(entries) [T // m, D].
+
+    [kwkr] §4.3 names the backward of the whole attention block as a training
+    workload; this is the compressor's part, written from the forward's own
+    definition by the chain rule, block by block:
+      RoPE at pos0 + j*m is a rotation, so its adjoint turns dy back by the
+      same angle; RMSNorm y = e g / r with r = sqrt(mean(e^2) + eps) gives
+      de = g dy / r - e (sum g dy e) / (D r^3) and dg += dy e / r;
+      the merge e = sum_i w_i x_i with w = softmax(l) gives dx_i = w_i de and
+      dl_i = w_i (x_i . de - e . de).
+    Every stream-a row feeds one entry (the next block's) and every stream-b
+    row one (its own), so nothing sums across blocks but dnorm_w. Rows no
+    entry reads (stream a of the last block, a trailing partial block) get 0.
+
+    Returns a dict of float64 arrays: dcb [T, D], dzb [T], and with overlap
+    dca [T, D], dza [T], dprev_ca [m, D] and dprev_za [m] (when prev_ca is
+    given); dnorm_w [D] when norm_w is given.
+
+    Pinned by: central finite differences of the forward on small random
+    inputs for every output, with and without the epilogue and the carried
+    rows, CSA and HCA shapes; equal logits give dx_i = de / n and
+    dl_i = (x_i - mean x) . de / n (tests/test_oracle_compress_backward.py).
+    """
+    cb = np.asarray(cb, dtype=np.float64)
+    zb = np.asarray(zb, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    T, D = cb.shape
+    n_out = T // m
+    res = {"dcb": np.zeros((T, D)), "dzb": np.zeros(T)}
+    if overlap:
+        ca = np.asarray(ca, dtype=np.float64)
+        za = np.asarray(za, dtype=np.float64)
+        res["dca"] = np.zeros((T, D))
+        res["dza"] = np.zeros(T)
+        if prev_ca is not None:
+            res["dprev_ca"] = np.zeros((m, D))
+            res["dprev_za"] = np.zeros(m)
+    if norm_w is not None:
+        g = np.asarray(norm_w, dtype=np.float64)
+        res["dnorm_w"] = np.zeros(D)
+    for j in range(n_out):
+        # the block's rows and logits, with where each goes back to
+        parts = []                                   # (rows, logits, grad rows, grad logits, offset)
+        if overlap:
+            if j == 0:
+                if prev_ca is not None:
+                    parts.append((np.asarray(prev_ca, dtype=np.float64), np.asarray(prev_za, dtype=np.float64),
+                                  res["dprev_ca"], res["dprev_za"], 0))
+            else:
+                parts.append((ca[(j - 1) * m: j * m], za[(j - 1) * m: j * m], res["dca"], res["dza"], (j - 1) * m))
+        parts.append((cb[j * m: (j + 1) * m], zb[j * m: (j + 1) * m], res["dcb"], res["dzb"], j * m))
+        x = np.concatenate([p_[0] for p_ in parts], axis=0)
+        w = _softmax(np.concatenate([p_[1] for p_ in parts]))
+        e = w @ x
+        dy = dout[j].copy()
+        if rope_dims:
+            dy = rope_rotate(dy, -(pos0 + j * m), rope_base, rope_dims)
+        if norm_w is not None:
+            r = math.sqrt(float(np.mean(e * e)) + eps)
+            res["dnorm_w"] += dy * e / r
+            gdy = g * dy
+            de = gdy / r - e * float(np.dot(gdy, e)) / (D * r ** 3)
+        else:
+            de = dy
+        dx = w[:, None] * de[None, :]
+        dl = w * (x @ de - float(np.dot(e, de)))
+        i = 0
+        for rows, _, grows, glog, off in parts:
+            n = rows.shape[0]
+            grows[off: off + n] = dx[i: i + n]
+            glog[off: off + n] = dl[i: i + n]
+            i += n
+    return res
 
 
 # ---------------------------------------------------------------------------
