@@ -126,6 +126,36 @@ int csa_compress(void* stream, int dt_in, int dt_out, int B, int T, int D, int m
                  void* out, void* out_scale, int64_t out_rows);
 
 /* ---------------------------------------------------------------------------
+ * csa_compress_backward — gradients of csa_compress's entries (before the
+ * conversion to dt_out) with respect to its inputs. [kwkr] §4.3 names the
+ * attention block's backward as the training workload; this is the
+ * compressor's part, by the chain rule through the RoPE (its adjoint turns
+ * the gradient back by the same angle), the RMSNorm and the gated merge.
+ *
+ *   forward arguments as csa_compress (dt_in, B, T, D, m, overlap, pos0, ca,
+ *             za, cb, zb, prev_ca, prev_za, flags, norm_w, eps, rope_base,
+ *             rope_dims); no dt_out, out or out_scale
+ *   dout      [B, T/m, D] float32: gradient of the entries
+ *   dcb [B, T, D], dzb [B, T] float32, written in full (rows that no entry
+ *             reads get 0)
+ *   dca [B, T, D], dza [B, T] float32: required with overlap, else NULL
+ *   dprev_ca [B, m, D], dprev_za [B, m] float32: required with prev_ca, else NULL
+ *   dnorm_w [D] float32: required with LCA_NORM (summed over every entry of
+ *             every sequence, in a fixed order), else NULL
+ *   ws        workspace of csa_compress_backward_workspace() bytes (B*(T/m)*D
+ *             floats with LCA_NORM); NULL allowed without LCA_NORM.
+ * Deterministic: every row gradient is written once; dnorm_w sums per-entry
+ * rows in order. Requirements as csa_compress; buffers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+size_t csa_compress_backward_workspace(int B, int T, int D, int m, uint32_t flags);
+int csa_compress_backward(void* stream, int dt_in, int B, int T, int D, int m, int overlap, int64_t pos0,
+                          const void* ca, const float* za, const void* cb, const float* zb,
+                          const void* prev_ca, const float* prev_za,
+                          uint32_t flags, const float* norm_w, float eps, float rope_base, int rope_dims,
+                          const float* dout, float* dca, float* dza, float* dcb, float* dzb,
+                          float* dprev_ca, float* dprev_za, float* dnorm_w, void* ws, size_t ws_bytes);
+
+/* ---------------------------------------------------------------------------
  * Decode-time state: csa_compress_append, lca_window_append.
  *
  * [kwkr] §4.4: the KV cache of a request splits into a state cache (what stays

@@ -18,7 +18,7 @@ __all__ = [
     "F32", "BF16", "KV_MIXED", "MXFP4",
     "NORM", "ROPE", "INV_ROPE", "SCORE_BF16",
     "LcaError", "lib", "lib_path",
-    "csa_compress", "lca_quantize_rows",
+    "csa_compress", "csa_compress_backward", "lca_quantize_rows",
     "csa_index_topk", "csa_index_topk_workspace",
     "csa_attend", "csa_attend_workspace", "csa_attend_noalloc",
     "hca_attend", "hca_attend_workspace",
@@ -63,6 +63,11 @@ def _declare(L):
     L.csa_compress.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp,
                                u32, vp, f32, f32, i32, vp, vp, i64]
     L.csa_compress.restype = i32
+    L.csa_compress_backward_workspace.argtypes = [i32, i32, i32, i32, u32]
+    L.csa_compress_backward_workspace.restype = sz
+    L.csa_compress_backward.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp,
+                                        u32, vp, f32, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz]
+    L.csa_compress_backward.restype = i32
     L.lca_quantize_rows.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp]
     L.lca_quantize_rows.restype = i32
     L.csa_index_topk_workspace.argtypes = [i32, i32, i32, i32, i32, i64, i32, i32, i64, u32]
@@ -326,6 +331,45 @@ def csa_compress(dt_in, dt_out, cb, zb, m, *, ca=None, za=None, prev_ca=None, pr
     st = lib().csa_compress(_stream(stream), dt_in, dt_out, B, T, D, m, 1 if overlap else 0, pos0,
                             _p(ca), _p(za), _p(cb), _p(zb), _p(prev_ca), _p(prev_za), flags,
                             _p(norm_w), eps, rope_base, rope_dims, _p(out), _p(out_scale), out_rows)
+    _check(st)
+
+
+def csa_compress_backward(dt_in, cb, zb, m, dout, dcb, dzb, *, ca=None, za=None, prev_ca=None, prev_za=None,
+                          overlap=True, pos0=0, flags=0, norm_w=None, eps=1e-6, rope_base=10000.0, rope_dims=0,
+                          dca=None, dza=None, dprev_ca=None, dprev_za=None, dnorm_w=None, ws=None, stream=None):
+    """Gradients of the compressor's entries with respect to its inputs; see
+    csa_compress_backward in include/lca.h. cb: [B, T, D]; dout: [B, T/m, D]."""
+    a = _Args("csa_compress_backward")
+    a.t(cb, "cb", dtypes=_ELEM.get(dt_in))
+    if cb.dim() != 3:
+        a._fail(f"cb must be [B, T, D], not {tuple(cb.shape)}")
+    B, T, D = cb.shape
+    if m < 1:
+        a._fail("m must be >= 1")
+    a.t(zb, "zb", dtypes=_F32, numel=B * T)
+    a.t(ca, "ca", dtypes=_ELEM.get(dt_in), shape=cb.shape, optional=not overlap)
+    a.t(za, "za", dtypes=_F32, numel=B * T, optional=not overlap)
+    a.t(prev_ca, "prev_ca", dtypes=_ELEM.get(dt_in), numel=B * m * D, optional=True)
+    a.t(prev_za, "prev_za", dtypes=_F32, numel=B * m, optional=True)
+    a.t(norm_w, "norm_w", dtypes=_F32, numel=D, optional=not (flags & NORM))
+    a.t(dout, "dout", dtypes=_F32, numel=B * (T // m) * D)
+    a.t(dcb, "dcb", dtypes=_F32, numel=B * T * D)
+    a.t(dzb, "dzb", dtypes=_F32, numel=B * T)
+    a.t(dca, "dca", dtypes=_F32, numel=B * T * D, optional=not overlap)
+    a.t(dza, "dza", dtypes=_F32, numel=B * T, optional=not overlap)
+    a.t(dprev_ca, "dprev_ca", dtypes=_F32, numel=B * m * D, optional=True)
+    a.t(dprev_za, "dprev_za", dtypes=_F32, numel=B * m, optional=True)
+    a.t(dnorm_w, "dnorm_w", dtypes=_F32, numel=D, optional=not (flags & NORM))
+    need = int(lib().csa_compress_backward_workspace(B, T, D, m, flags))
+    if ws is None and (flags & NORM):
+        ws = torch.empty(need, dtype=torch.uint8, device=cb.device)
+    a.t(ws, "ws", optional=True)
+    a.done()
+    st = lib().csa_compress_backward(_stream(stream), dt_in, B, T, D, m, 1 if overlap else 0, pos0,
+                                     _p(ca), _p(za), _p(cb), _p(zb), _p(prev_ca), _p(prev_za), flags,
+                                     _p(norm_w), eps, rope_base, rope_dims, _p(dout), _p(dca), _p(dza),
+                                     _p(dcb), _p(dzb), _p(dprev_ca), _p(dprev_za), _p(dnorm_w), _p(ws),
+                                     _nbytes(ws) if ws is not None else 0)
     _check(st)
 
 

@@ -272,6 +272,177 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(int dt_out, int
   emit_row(e, D, dt_out, rope_dims, out, row, out_scale, red, blk_exp);
 }
 
+// ---------------------------------------------------------------------------
+// Backward of the compressor ([kwkr] §4.3: the attention block's backward is
+// the training workload). One workgroup per entry j of sequence b, the
+// forward's merge recomputed in the same order, then the chain rule: the
+// RoPE adjoint turns the entry's gradient back by the same angle; RMSNorm
+// y = e r g (r = 1 / sqrt(mean(e^2) + eps)) gives de = g dy r - e (sum g dy e)
+// r^3 / D and the gain's gradient dy e r (one row per entry in the
+// workspace, summed over entries in a fixed order by the next kernel); the
+// gated merge e = sum_i w_i x_i gives dx_i = w_i de and
+// dl_i = w_i (x_i . de - e . de). Every stream-a row feeds the next block's
+// entry only and every stream-b row its own, so the row gradients are written
+// once, without atomics; rows that no entry reads (stream a of the last block,
+// a trailing partial block) are written as zeros by the last workgroup.
+// ---------------------------------------------------------------------------
+struct CompressBwdArgs {
+  CompressArgs a;                      // the forward's arguments (out and out_scale unused)
+  const float* dout;                   // [B, T/m, D]
+  float *dca, *dza, *dcb, *dzb;        // [B, T, D], [B, T]
+  float *dprev_ca, *dprev_za;          // [B, m, D], [B, m] (with prev_ca)
+  float* dg_rows;                      // [B * T/m, D] workspace (with LCA_NORM)
+};
+
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void compress_bwd_kernel(CompressBwdArgs p) {
+  const CompressArgs& a = p.a;
+  __shared__ float wts[256];
+  __shared__ float e[kMaxD];
+  __shared__ float de[kMaxD];
+  __shared__ float red[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int m = a.m, D = a.D, T = a.T;
+  const int n_out = T / m;
+  const int64_t tok0 = static_cast<int64_t>(b) * T;
+  // rows no entry reads: stream a of the last block and the tokens of a
+  // trailing partial block (every token when there is no whole block)
+  if (j == (n_out > 0 ? n_out - 1 : 0)) {
+    const int64_t za0 = n_out > 0 ? static_cast<int64_t>(n_out - 1) * m : 0;
+    const int64_t zb0 = static_cast<int64_t>(n_out) * m;
+    if (a.overlap) {
+      for (int64_t i = za0 * D + tid; i < static_cast<int64_t>(T) * D; i += kThreads) p.dca[tok0 * D + i] = 0.f;
+      for (int64_t t = za0 + tid; t < T; t += kThreads) p.dza[tok0 + t] = 0.f;
+    }
+    for (int64_t i = zb0 * D + tid; i < static_cast<int64_t>(T) * D; i += kThreads) p.dcb[tok0 * D + i] = 0.f;
+    for (int64_t t = zb0 + tid; t < T; t += kThreads) p.dzb[tok0 + t] = 0.f;
+    if (n_out == 0) {
+      if (a.overlap && a.prev_ca) {
+        for (int i = tid; i < m * D; i += kThreads) p.dprev_ca[static_cast<int64_t>(b) * m * D + i] = 0.f;
+        for (int i = tid; i < m; i += kThreads) p.dprev_za[static_cast<int64_t>(b) * m + i] = 0.f;
+      }
+      return;
+    }
+  }
+  const bool has_a = a.overlap && (j > 0 || a.prev_ca != nullptr);
+  const int na = has_a ? m : 0, nl = na + m;
+  const int64_t tok_a = tok0 + static_cast<int64_t>(j - 1) * m;   // block j-1
+  const int64_t tok_b = tok0 + static_cast<int64_t>(j) * m;       // block j
+  auto logit = [&](int i) -> float {
+    if (i < na) return j > 0 ? a.za[tok_a + i] : a.prev_za[b * m + i];
+    return a.zb[tok_b + (i - na)];
+  };
+  auto row = [&](int i) -> const Tin* {
+    if (i < na) return j > 0 ? row_ptr<Tin>(a.ca, tok_a + i, D) : row_ptr<Tin>(a.prev_ca, static_cast<int64_t>(b) * m + i, D);
+    return row_ptr<Tin>(a.cb, tok_b + (i - na), D);
+  };
+  // where row i's gradients go
+  auto drow = [&](int i) -> float* {
+    if (i < na) return j > 0 ? p.dca + (tok_a + i) * D : p.dprev_ca + (static_cast<int64_t>(b) * m + i) * D;
+    return p.dcb + (tok_b + (i - na)) * D;
+  };
+  auto dlog = [&](int i) -> float* {
+    if (i < na) return j > 0 ? p.dza + tok_a + i : p.dprev_za + static_cast<int64_t>(b) * m + i;
+    return p.dzb + tok_b + (i - na);
+  };
+
+  // the forward's gate weights and merge
+  float lmax = -INFINITY;
+  for (int i = tid; i < nl; i += kThreads) {
+    const float z = logit(i);
+    wts[i] = z;
+    lmax = fmaxf(lmax, z);
+  }
+  lmax = block_reduce(lmax, red, true);
+  float lsum = 0.f;
+  for (int i = tid; i < nl; i += kThreads) {
+    const float w = expf(wts[i] - lmax);
+    wts[i] = w;
+    lsum += w;
+  }
+  lsum = block_reduce(lsum, red, false);
+  const float inv = 1.0f / lsum;
+  for (int i = tid; i < nl; i += kThreads) wts[i] *= inv;
+  for (int c = tid; c < D; c += kThreads) {
+    float acc = 0.f;
+    for (int i = 0; i < nl; ++i) acc = fmaf(wts[i], load_elem<Tin>(row(i), c), acc);
+    e[c] = acc;
+  }
+  // the entry's gradient, turned back through the RoPE
+  const float* dy = p.dout + (static_cast<int64_t>(b) * n_out + j) * D;
+  for (int c = tid; c < D; c += kThreads) de[c] = dy[c];
+  __syncthreads();
+  if (a.flags & LCA_ROPE) {
+    const int R = a.rope_dims;
+    for (int i = tid; i < R / 2; i += kThreads) {
+      float sn, cs;
+      rope_sincos(static_cast<double>(a.pos0 + static_cast<int64_t>(j) * m), i, a.rope_r, &sn, &cs);
+      const int c0 = D - R + 2 * i;
+      const float u = de[c0], v = de[c0 + 1];
+      de[c0] = u * cs + v * sn;
+      de[c0 + 1] = v * cs - u * sn;
+    }
+    __syncthreads();
+  }
+  if (a.flags & LCA_NORM) {
+    float ss = 0.f, sg = 0.f;
+    for (int c = tid; c < D; c += kThreads) {
+      ss += e[c] * e[c];
+      sg += a.norm_w[c] * de[c] * e[c];
+    }
+    ss = block_reduce(ss, red, false);
+    sg = block_reduce(sg, red, false);
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(D) + a.eps);
+    const float k3 = sg * r * r * r / static_cast<float>(D);
+    float* dg = p.dg_rows + (static_cast<int64_t>(b) * n_out + j) * D;
+    for (int c = tid; c < D; c += kThreads) {
+      dg[c] = de[c] * e[c] * r;
+      de[c] = a.norm_w[c] * de[c] * r - e[c] * k3;
+    }
+    __syncthreads();
+  }
+  // the gated merge: e . de once, then row i's dot with de (one wave per row)
+  float ed = 0.f;
+  for (int c = tid; c < D; c += kThreads) ed += e[c] * de[c];
+  ed = block_reduce(ed, red, false);
+  for (int i = wid; i < nl; i += kThreads / 64) {
+    const Tin* x = row(i);
+    float* dx = drow(i);
+    const float wi = wts[i];
+    float dot = 0.f;
+    for (int c = lane; c < D; c += 64) {
+      dot = fmaf(load_elem<Tin>(x, c), de[c], dot);
+      dx[c] = wi * de[c];
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) *dlog(i) = wi * (dot - ed);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ x, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n) x[i] = 0.f;
+}
+
+// dnorm_w[c] = the sum over every entry's row of the workspace, in row order.
+__global__ __launch_bounds__(kThreads) void compress_bwd_gain_kernel(const float* __restrict__ dg_rows, int64_t rows,
+                                                                     int D, float* __restrict__ dnorm_w) {
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  if (c >= D) return;
+  float acc = 0.f;
+  int64_t r = 0;
+  for (; r + 8 <= rows; r += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = dg_rows[(r + u) * D + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += x[u];
+  }
+  for (; r < rows; ++r) acc += dg_rows[r * D + c];
+  dnorm_w[c] = acc;
+}
+
 }  // namespace
 
 hipError_t launch_compress(hipStream_t s, const CompressArgs& a_in) {
@@ -295,6 +466,41 @@ hipError_t launch_append(hipStream_t s, const AppendJobs& jobs_in, int B, int64_
   LaunchScope scope(s, name);
   scope.launch(decode_append_kernel, dim3(B, jobs.n), dim3(kThreads), 0, jobs, pos_max, pos);
   return hipGetLastError();
+}
+
+size_t compress_backward_workspace(int B, int T, int D, int m, uint32_t flags) {
+  return (flags & LCA_NORM) ? static_cast<size_t>(B) * (T / m) * D * sizeof(float) + 256 : 256;
+}
+
+hipError_t launch_compress_backward(hipStream_t s, const CompressArgs& a_in, const float* dout, float* dca,
+                                    float* dza, float* dcb, float* dzb, float* dprev_ca, float* dprev_za,
+                                    float* dnorm_w, void* ws) {
+  CompressBwdArgs p{a_in, dout, dca, dza, dcb, dzb, dprev_ca, dprev_za, static_cast<float*>(ws)};
+  p.a.rope_r = rope_ratio(p.a.rope_base, p.a.rope_dims);
+  const int n_out = p.a.T / p.a.m;
+  {
+    LaunchScope scope(s, "compress_bwd");
+    const dim3 grid(n_out > 0 ? n_out : 1, p.a.B);
+    if (p.a.dt_in == LCA_F32)
+      scope.launch(compress_bwd_kernel<float>, grid, dim3(kThreads), 0, p);
+    else
+      scope.launch(compress_bwd_kernel<uint16_t>, grid, dim3(kThreads), 0, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if ((p.a.flags & LCA_NORM) && dnorm_w) {
+    LaunchScope scope(s, "compress_bwd_gain");
+    const int64_t rows = static_cast<int64_t>(p.a.B) * n_out;
+    if (rows == 0) {
+      scope.launch(fill_zero_kernel, dim3((p.a.D + kThreads - 1) / kThreads), dim3(kThreads), 0, dnorm_w,
+                   static_cast<int64_t>(p.a.D));
+    } else {
+      scope.launch(compress_bwd_gain_kernel, dim3((p.a.D + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                   static_cast<const float*>(p.dg_rows), rows, p.a.D, dnorm_w);
+    }
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_quantize_rows(hipStream_t s, int dt_out, int64_t n_rows, int D, int rope_dims,

@@ -171,6 +171,57 @@ int csa_compress(void* stream, int dt_in, int dt_out, int B, int T, int D, int m
   return hip_status(lca::launch_compress(static_cast<hipStream_t>(stream), a), "csa_compress");
 }
 
+size_t csa_compress_backward_workspace(int B, int T, int D, int m, uint32_t flags) {
+  if (B < 1 || T < 0 || m < 1 || D < 1) return 0;
+  return lca::compress_backward_workspace(B, T, D, m, flags);
+}
+
+int csa_compress_backward(void* stream, int dt_in, int B, int T, int D, int m, int overlap, int64_t pos0,
+                          const void* ca, const float* za, const void* cb, const float* zb,
+                          const void* prev_ca, const float* prev_za, uint32_t flags, const float* norm_w,
+                          float eps, float rope_base, int rope_dims, const float* dout, float* dca, float* dza,
+                          float* dcb, float* dzb, float* dprev_ca, float* dprev_za, float* dnorm_w, void* ws,
+                          size_t ws_bytes) {
+  const char* fn = "csa_compress_backward";
+  if (B < 1 || T < 0 || m < 1 || D < 32 || D > 1024 || D % 32 != 0)
+    return fail(LCA_ERR_ARG, "%s: need B>=1, T>=0, m>=1, 32<=D<=1024, D%%32==0 (B=%d T=%d m=%d D=%d)", fn, B, T, m, D);
+  if (overlap != 0 && overlap != 1) return fail(LCA_ERR_ARG, "%s: overlap must be 0 or 1", fn);
+  if (overlap == 1 ? 2 * m > 256 : m > 256) return fail(LCA_ERR_UNSUPPORTED, "%s: too many rows per entry (m=%d)", fn, m);
+  if (pos0 < 0 || pos0 % m != 0) return fail(LCA_ERR_ARG, "%s: pos0 must be >= 0 and a multiple of m", fn);
+  if (dt_in != LCA_F32 && dt_in != LCA_BF16) return fail(LCA_ERR_UNSUPPORTED, "%s: dt_in must be F32 or BF16", fn);
+  if (flags & ~(LCA_NORM | LCA_ROPE)) return fail(LCA_ERR_ARG, "%s: only LCA_NORM and LCA_ROPE apply", fn);
+  if (!cb || !zb || !dcb || !dzb || (T / m > 0 && !dout))
+    return fail(LCA_ERR_ARG, "%s: cb, zb, dcb, dzb (and dout when T >= m) are required", fn);
+  if (overlap) {
+    if (!ca || !za || !dca || !dza) return fail(LCA_ERR_ARG, "%s: overlap needs ca, za, dca and dza", fn);
+    if ((prev_ca == nullptr) != (prev_za == nullptr)) return fail(LCA_ERR_ARG, "%s: prev_ca and prev_za go together", fn);
+    if (prev_ca && (!dprev_ca || !dprev_za)) return fail(LCA_ERR_ARG, "%s: prev_ca needs dprev_ca and dprev_za", fn);
+    if (!prev_ca && (dprev_ca || dprev_za)) return fail(LCA_ERR_ARG, "%s: dprev_* without prev_ca", fn);
+  } else if (ca || za || prev_ca || prev_za || dca || dza || dprev_ca || dprev_za) {
+    return fail(LCA_ERR_ARG, "%s: stream a, prev_* and their gradients must be NULL without overlap", fn);
+  }
+  if ((flags & LCA_NORM) && (!norm_w || !dnorm_w)) return fail(LCA_ERR_ARG, "%s: LCA_NORM needs norm_w and dnorm_w", fn);
+  if (!(flags & LCA_NORM) && dnorm_w) return fail(LCA_ERR_ARG, "%s: dnorm_w without LCA_NORM", fn);
+  if ((flags & LCA_NORM) && !(eps >= 0.f)) return fail(LCA_ERR_ARG, "%s: eps must be >= 0", fn);
+  if (rope_dims < 0 || rope_dims > D || rope_dims % 2 != 0) return fail(LCA_ERR_ARG, "%s: rope_dims must be even and in [0, D]", fn);
+  if ((flags & LCA_ROPE) && (rope_dims == 0 || !(rope_base > 0.f))) return fail(LCA_ERR_ARG, "%s: LCA_ROPE needs rope_dims > 0 and rope_base > 0", fn);
+  if (!aligned16(ca) || !aligned16(cb) || !aligned16(prev_ca) || !aligned16(dout) || !aligned16(dca) ||
+      !aligned16(dcb) || !aligned16(dprev_ca))
+    return fail(LCA_ERR_ALIGN, "%s: row buffers must be 16-byte aligned", fn);
+  if (!aligned4(za) || !aligned4(zb) || !aligned4(prev_za) || !aligned4(norm_w) || !aligned4(dza) || !aligned4(dzb) ||
+      !aligned4(dprev_za) || !aligned4(dnorm_w))
+    return fail(LCA_ERR_ALIGN, "%s: float arrays must be 4-byte aligned", fn);
+  if (T / m > 2147483647LL) return fail(LCA_ERR_UNSUPPORTED, "%s: too many entries", fn);
+  const size_t need = lca::compress_backward_workspace(B, T, D, m, flags);
+  if ((flags & LCA_NORM) && (!ws || ws_bytes < need))
+    return fail(LCA_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+  if (!aligned16(ws)) return fail(LCA_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  lca::CompressArgs a{dt_in, LCA_F32, B, T, D, m, overlap, pos0, ca, cb, prev_ca, za, zb, prev_za,
+                      flags, norm_w, eps, rope_base, rope_dims, nullptr, nullptr, T / m};
+  return hip_status(lca::launch_compress_backward(static_cast<hipStream_t>(stream), a, dout, dca, dza, dcb, dzb,
+                                                  dprev_ca, dprev_za, dnorm_w, ws), fn);
+}
+
 // ---------------------------------------------------------------------------
 // Decode-time state: token-at-a-time compressor and the sliding-window ring.
 static int check_positions(const int64_t* pos, int64_t pos_max, const char* fn) {

@@ -49,6 +49,10 @@ struct CompressArgs {
   double rope_r;             // base^(-2/R), set by the launchers
 };
 hipError_t launch_compress(hipStream_t s, const CompressArgs& a);
+size_t compress_backward_workspace(int B, int T, int D, int m, uint32_t flags);
+hipError_t launch_compress_backward(hipStream_t s, const CompressArgs& a, const float* dout, float* dca,
+                                    float* dza, float* dcb, float* dzb, float* dprev_ca, float* dprev_za,
+                                    float* dnorm_w, void* ws);
 
 // Token-at-a-time compressor state, per sequence: R = 3m rows with overlap (a
 // ring of 2m stream-a rows, then m stream-b rows), R = m without; rows in the

@@ -250,3 +250,22 @@ def test_host_validation_under_a_microsecond_in_c(lib):
     assert set(ns) == {"csa_index_topk", "csa_attend", "hca_attend", "csa_attend_noalloc"}
     for name, t in ns.items():
         assert t < 1000.0, (name, t)
+
+
+def test_compress_backward_validation(lib):
+    fake = 0x10000
+    f = ctypes.c_void_p
+
+    def call(B=1, T=8, D=64, m=4, overlap=1, pos0=0, flags=0, ca=fake, za=fake, dca=fake, dza=fake,
+             dout=fake, norm_w=None, dnorm_w=None, ws=None, wsb=0):
+        return lib.csa_compress_backward(None, 0, B, T, D, m, overlap, pos0, ca, za, fake, fake, None, None,
+                                         flags, norm_w, 1e-6, 10000.0, 0, dout, dca, dza, fake, fake, None, None,
+                                         dnorm_w, ws, wsb)
+    _expect(call(D=100), -1, "D%")
+    _expect(call(pos0=2), -1, "pos0")
+    _expect(call(dca=None), -1, "overlap needs")
+    _expect(call(overlap=0), -1, "must be NULL without overlap")
+    _expect(call(flags=1, norm_w=fake), -1, "LCA_NORM needs")
+    _expect(call(flags=1, norm_w=fake, dnorm_w=fake), -4, "workspace")
+    _expect(call(dout=None), -1, "required")
+    assert lib.csa_compress_backward_workspace(2, 16, 64, 4, 1) >= 2 * 4 * 64 * 4
