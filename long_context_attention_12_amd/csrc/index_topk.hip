@@ -1840,8 +1840,12 @@ __global__ __launch_bounds__(kFiltThreads) void topk_bound_kernel(
   uint32_t lo, hi;
   const int64_t ng = (n + kGroup - 1) / kGroup;
   const float* gm = fw.gmax + r * fw.ldg;
+  // 16-byte loads of 4 groups for rows up to 4 * 256 * 17 groups (lists of
+  // 278528 entries: the 1M-token prefill's rows are just past 262144)
   if (ng <= 4 * kFiltThreads * 16)
     group_bound_v4<16>(gm, ng, k, key16, wv, &lo, &hi);
+  else if (ng <= 4 * kFiltThreads * 17)
+    group_bound_v4<17>(gm, ng, k, key16, wv, &lo, &hi);
   else
     group_bound<kBoundItems>(gm, ng, k, key16, wv, &lo, &hi);
   if (threadIdx.x == 0) sh_lim = static_cast<uint32_t>(n);
