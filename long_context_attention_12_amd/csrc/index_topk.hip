@@ -389,7 +389,7 @@ template <int HI, int MODE, bool R16>
 __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const uint16_t* __restrict__ kI,
     float* __restrict__ scores, int64_t ld, int Tq, int t_off, int Tc, int64_t N_cap, int64_t q_pos0,
-    const int64_t* __restrict__ q_pos, int m, int64_t keys_per_wg, SelAux aux, int kc, int nq, int nbatch) {
+    const int64_t* __restrict__ q_pos, int m, int64_t keys_per_wg, SelAux aux, int kc, int nq, int nbatch, int ss) {
   constexpr bool round_bf16 = R16;
   constexpr int DI = 128, KS = DI / 32, MB = 4, NB = kTileKeys / 16, QPB = 16 / HI;
   constexpr int QPW = MB * QPB, QPWG = 4 * QPW;
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
   int64_t rix_l[2 * MB];
   bool writer_l[2 * MB];
   uint32_t lo_c[2 * MB], run_a[2 * MB], run_e[2 * MB];
-  float gm_l[2 * MB], lof_l[2 * MB];
+  float gm_l[2 * MB], lof_l[2 * MB], lofg_l[2 * MB];
   int limt_l[2 * MB];                                // candidate pass: first tile past the row's index limit
   int64_t gslot_l[2 * MB], cb_l[2 * MB];
 #pragma unroll
@@ -500,10 +500,13 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
       rix_l[ci] = static_cast<int64_t>(b) * Tc + qt - t_off;
       writer_l[ci] = holds && qt < t_end;
       gm_l[ci] = -INFINITY;
-      gslot_l[ci] = rix_l[ci] * aux.ldg + k_begin / kGroup + (r16 >> 2);
+      // maxima of every ss-th tile only (sampled pass): tile u ss of the row
+      // keeps slots 4 u .. 4 u + 3 (k_begin is a multiple of 64 ss)
+      gslot_l[ci] = rix_l[ci] * aux.ldg + k_begin / (kGroup * ss) + (r16 >> 2);
       cb_l[ci] = (rix_l[ci] * aux.nchs + kr) * aux.capc;
       lo_c[ci] = 0;
       lof_l[ci] = INFINITY;
+      lofg_l[ci] = INFINITY;
       limt_l[ci] = 0x7fffffff;
       run_a[ci] = run_e[ci] = 0;
     }
@@ -521,17 +524,31 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
     for (int ci = 0; ci < 2 * MB; ++ci) {
       if (!writer_l[ci]) continue;
       lo_c[ci] = lo_raw[ci];
-      // tiles from limt on start at or past the index limit: no candidates
+      // tiles from limt on start at or past the index limit: no ties with
+      // lo there, only scores above it
       const int64_t lrel = static_cast<int64_t>(lim_raw[ci]) - k_begin;
       limt_l[ci] = lrel <= 0 ? 0 : static_cast<int>((lrel + kTileKeys - 1) / kTileKeys);
       // key(x) >= lo implies x >= lof: lof is the bound's own float when
       // that is a normal number, and -FLT_MIN for a bound among the
       // subnormals and zeros (a superset either way, whether or not the
-      // comparison flushes subnormals)
-      const uint32_t lo32 = round_bf16 ? lo_raw[ci] << 16 : lo_raw[ci];
-      if (lo32 >= 0x80800000u) lof_l[ci] = __uint_as_float(lo32 & 0x7fffffffu);      // >= +FLT_MIN
-      else if (lo32 >= 0x7f7fffffu) lof_l[ci] = -1.17549435e-38f;                  // >= key(-FLT_MIN)
-      else lof_l[ci] = __uint_as_float(~lo32);                                     // <= -FLT_MIN
+      // comparison flushes subnormals); lofg the same for lo + 1
+      auto key_floor = [&](uint32_t key) {
+        const uint32_t k32 = round_bf16 ? key << 16 : key;
+        if (k32 >= 0x80800000u) return __uint_as_float(k32 & 0x7fffffffu);        // >= +FLT_MIN
+        if (k32 >= 0x7f7fffffu) return -1.17549435e-38f;                         // >= key(-FLT_MIN)
+        if (k32 > 0x007fffffu) return __uint_as_float(~k32);                      // <= -FLT_MIN
+        return -INFINITY;                                                         // key(-inf) and below (no number)
+      };
+      // (a key above that of +0 is a positive number, whose own float is a
+      // superset filter in either subnormal mode: it keeps the exact zeros,
+      // a crowd of ties when every head weight is negative, out of the
+      // exact comparisons)
+      const uint32_t kmax = round_bf16 ? 0xffffu : 0xffffffffu;
+      lof_l[ci] = key_floor(lo_raw[ci]);
+      const uint32_t g32 = round_bf16 ? (lo_raw[ci] + 1u) << 16 : lo_raw[ci] + 1u;
+      lofg_l[ci] = lo_raw[ci] >= kmax         ? INFINITY
+                   : g32 >= 0x80000001u      ? __uint_as_float(g32 & 0x7fffffffu)
+                                             : key_floor(lo_raw[ci] + 1u);
     }
   }
   // the smallest visible count past k_begin among this wave's queries (its
@@ -546,14 +563,14 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
 
   // One tile of the maxima or candidate pass; FULL: every key of the tile is
   // visible to every query of the wave (no per-key masks).
-  auto sel_tile = [&](int tt, const char* xb, auto full_c) __attribute__((always_inline)) {
+  auto sel_tile = [&](int tt, int it, const char* xb, auto full_c) __attribute__((always_inline)) {
     constexpr bool full = decltype(full_c)::value;
     constexpr int NSL = HI == 2 ? 2 : 1;             // query slots per lane (acc_scores)
     float vs[NB][2 * MB];                            // candidate pass: the tile's scores
     uint64_t mk[NB][2 * MB];                         // and which may be candidates
-    float lof_t[2 * MB];                             // the float filter, or +inf past the index limit
+    float lof_t[2 * MB];                             // the float filter: key >= lo, or key > lo past the limit
 #pragma unroll
-    for (int ci = 0; ci < 2 * MB; ++ci) lof_t[ci] = tt >= limt_l[ci] ? INFINITY : lof_l[ci];
+    for (int ci = 0; ci < 2 * MB; ++ci) lof_t[ci] = tt >= limt_l[ci] ? lofg_l[ci] : lof_l[ci];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       f32x4 acc[MB];
@@ -601,7 +618,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
         x = max1(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));
         x = max1(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));
         const int c = r16 >> 2;
-        if ((r16 & 3) == 0 && writer_l[ci] && tt * kTileKeys + 4 * c < nvl_l[ci]) aux.gmax[gslot_l[ci] + 4 * tt] = x;
+        if ((r16 & 3) == 0 && writer_l[ci] && tt * kTileKeys + 4 * c < nvl_l[ci]) aux.gmax[gslot_l[ci] + 4 * it] = x;
         gm_l[ci] = -INFINITY;
       }
     } else {
@@ -619,7 +636,7 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
           const bool maybe = (mk[nb][ci] >> lane) & 1u;
           const uint32_t kk = score_key(vs[nb][ci], round_bf16);
           const bool is_a = maybe && writer_l[ci] && kk > lo_c[ci];
-          const bool is_e = maybe && writer_l[ci] && kk == lo_c[ci];
+          const bool is_e = maybe && writer_l[ci] && kk == lo_c[ci] && tt < limt_l[ci];
           const uint64_t ba = __ballot(is_a), be = __ballot(is_e);
           if (ba != 0) {
             uint32_t na;
@@ -641,18 +658,20 @@ __global__ __launch_bounds__(kScoreThreads) void index_score_tiled_kernel(
     }
   };
 
-  for (int tt = 0; tt < ntiles; ++tt) {
+  // the maxima pass takes every ss-th tile (tile 0 of the range is one)
+  const int tstep = MODE == kTiledMaxima ? ss : 1;
+  for (int tt = 0, it = 0; tt < ntiles; tt += tstep, ++it) {
     // tile tt has landed (every wave waited for its own copies) and every wave
-    // is done with the buffer that tile tt + 1 overwrites
+    // is done with the buffer that the next tile overwrites
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (tt + 1 < ntiles) issue(tt + 1, (tt + 1) & 1);
-    const char* xb = reinterpret_cast<const char*>(&Ks[tt & 1][0]);
+    if (tt + tstep < ntiles) issue(tt + tstep, (it + 1) & 1);
+    const char* xb = reinterpret_cast<const char*>(&Ks[it & 1][0]);
     if constexpr (MODE != kTiledScores) {
       if ((tt + 1) * kTileKeys <= nvl_w)                               // uniform
-        sel_tile(tt, xb, std::true_type{});
+        sel_tile(tt, it, xb, std::true_type{});
       else
-        sel_tile(tt, xb, std::false_type{});
+        sel_tile(tt, it, xb, std::false_type{});
       continue;
     }
 #pragma unroll
@@ -1665,27 +1684,43 @@ __device__ __forceinline__ void group_bound(const float* __restrict__ gm, int64_
 // waves' items a partition of the row. Then as group_bound: each wave the
 // ceil(k / 4)-th largest of its items on the keys' top 16 bits, lo the
 // smallest of the four.
-template <int NV>
+// SINGLE: every group its own item (4 NV items per lane), for the sampled
+// maxima, which are few and spread over the row; the loads are dealt to the
+// waves in turn (load f to wave f % 4), so that each wave holds a quarter of
+// a short row and bounds it.
+template <int NV, bool SINGLE = false>
 __device__ __forceinline__ void group_bound_v4(const float* __restrict__ gm, int64_t ng, int k, bool key16,
                                                uint32_t* wv, uint32_t* lo_out, uint32_t* hi_out) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int IPL = SINGLE ? 4 : 2;              // items per load
+  const int fl = SINGLE ? 4 * lane + wid : tid;     // this thread's load within a round of 256
   float4 v[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int64_t f = tid + static_cast<int64_t>(kFiltThreads) * j;
+    const int64_t f = fl + static_cast<int64_t>(kFiltThreads) * j;
     v[j] = 4 * f < ng ? *reinterpret_cast<const float4*>(gm + 4 * f) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  uint32_t kv[2 * NV], mx = 0, have = 0;
+  uint32_t kv[IPL * NV], mx = 0, have = 0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int64_t g0 = 4 * (tid + static_cast<int64_t>(kFiltThreads) * j);
-    // an item counts the groups of its pair that exist (a row's last pair may hold one)
-    const float a0 = g0 < ng ? v[j].x : -INFINITY, a1 = g0 + 1 < ng ? v[j].y : -INFINITY;
-    const float b0 = g0 + 2 < ng ? v[j].z : -INFINITY, b1 = g0 + 3 < ng ? v[j].w : -INFINITY;
-    kv[2 * j] = g0 < ng ? score_key(fmaxf(a0, a1), key16) : 0u;
-    kv[2 * j + 1] = g0 + 2 < ng ? score_key(fmaxf(b0, b1), key16) : 0u;
-    mx = max(mx, max(kv[2 * j], kv[2 * j + 1]));
-    have += static_cast<uint32_t>(__popcll(__ballot(g0 < ng))) + static_cast<uint32_t>(__popcll(__ballot(g0 + 2 < ng)));
+    const int64_t g0 = 4 * (fl + static_cast<int64_t>(kFiltThreads) * j);
+    if constexpr (SINGLE) {
+      const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kv[4 * j + i] = g0 + i < ng ? score_key(x[i], key16) : 0u;
+        mx = max(mx, kv[4 * j + i]);
+        have += static_cast<uint32_t>(__popcll(__ballot(g0 + i < ng)));
+      }
+    } else {
+      // an item counts the groups of its pair that exist (a row's last pair may hold one)
+      const float a0 = g0 < ng ? v[j].x : -INFINITY, a1 = g0 + 1 < ng ? v[j].y : -INFINITY;
+      const float b0 = g0 + 2 < ng ? v[j].z : -INFINITY, b1 = g0 + 3 < ng ? v[j].w : -INFINITY;
+      kv[2 * j] = g0 < ng ? score_key(fmaxf(a0, a1), key16) : 0u;
+      kv[2 * j + 1] = g0 + 2 < ng ? score_key(fmaxf(b0, b1), key16) : 0u;
+      mx = max(mx, max(kv[2 * j], kv[2 * j + 1]));
+      have += static_cast<uint32_t>(__popcll(__ballot(g0 < ng))) + static_cast<uint32_t>(__popcll(__ballot(g0 + 2 < ng)));
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), o, kWave)));
@@ -1693,14 +1728,14 @@ __device__ __forceinline__ void group_bound_v4(const float* __restrict__ gm, int
   const uint32_t r = static_cast<uint32_t>((k + 3) / 4);
   uint32_t t = 0;
   if (have >= r) {
-    uint32_t k16[2 * NV];
+    uint32_t k16[IPL * NV];
 #pragma unroll
-    for (int i = 0; i < 2 * NV; ++i) k16[i] = kv[i] >> ksh;
+    for (int i = 0; i < IPL * NV; ++i) k16[i] = kv[i] >> ksh;
     for (int bit = 15; bit >= 0; --bit) {
       const uint32_t c = t | (1u << bit);
       uint32_t cnt = 0;
 #pragma unroll
-      for (int i = 0; i < 2 * NV; ++i) cnt += static_cast<uint32_t>(__popcll(__ballot(k16[i] >= c)));
+      for (int i = 0; i < IPL * NV; ++i) cnt += static_cast<uint32_t>(__popcll(__ballot(k16[i] >= c)));
       if (cnt >= r) t = c;
     }
     t <<= ksh;
@@ -1826,9 +1861,15 @@ __device__ void select_passes_t(const FiltRow& row, int k, bool key16, uint32_t*
 // group (in index order) whose maximum reaches the bound: at least k ties sit
 // there. Keys past that group are no candidates. Otherwise the limit is the
 // visible count.
+// ss > 1: the row holds the maxima of every ss-th 64-key tile only (the
+// sampled maxima pass), tile u ss at slots 4 u .. 4 u + 3; each is still the
+// largest of distinct scores, so the bound holds, only less tight. The index
+// limit then ends at the tile of the k-th sampled group at or above lo: when
+// hi == lo, each such group holds a tie, so the first k ties lie before it
+// (scores above lo may lie anywhere: the candidate pass keeps those past it).
 __global__ __launch_bounds__(kFiltThreads) void topk_bound_kernel(
     FiltWs fw, int64_t N_cap, int Tc, int64_t q_pos0, const int64_t* __restrict__ q_pos, int t_off, int m, int k,
-    bool key16) {
+    bool key16, int ss) {
   __shared__ uint32_t wv[8];
   __shared__ __attribute__((aligned(16))) uint32_t wsum[kFiltThreads / 64];
   __shared__ uint32_t sh_lim;
@@ -1838,11 +1879,19 @@ __global__ __launch_bounds__(kFiltThreads) void topk_bound_kernel(
   if (n <= k) return;
   const int64_t r = static_cast<int64_t>(b) * Tc + tl;
   uint32_t lo, hi;
-  const int64_t ng = (n + kGroup - 1) / kGroup;
+  // groups held: with sampling, the slots whose first key (tile base + 4 c)
+  // is visible
+  const int64_t tspan = int64_t(kTileKeys) * ss;
+  const int64_t ulast = (n - 1) / tspan, rem = n - ulast * tspan;
+  const int64_t ng = ss == 1 ? (n + kGroup - 1) / kGroup : 4 * ulast + (rem >= 13 ? 4 : (rem + 3) / 4);
   const float* gm = fw.gmax + r * fw.ldg;
   // 16-byte loads of 4 groups for rows up to 4 * 256 * 17 groups (lists of
   // 278528 entries: the 1M-token prefill's rows are just past 262144)
-  if (ng <= 4 * kFiltThreads * 16)
+  if (ss > 1 && ng <= 4 * kFiltThreads * 4)
+    group_bound_v4<4, true>(gm, ng, k, key16, wv, &lo, &hi);
+  else if (ss > 1 && ng <= 4 * kFiltThreads * 8)
+    group_bound_v4<8, true>(gm, ng, k, key16, wv, &lo, &hi);
+  else if (ng <= 4 * kFiltThreads * 16)
     group_bound_v4<16>(gm, ng, k, key16, wv, &lo, &hi);
   else if (ng <= 4 * kFiltThreads * 17)
     group_bound_v4<17>(gm, ng, k, key16, wv, &lo, &hi);
@@ -1865,7 +1914,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_bound_kernel(
       if (pre < need && pre + c >= need) {          // the need-th such group is one of this thread's
         const uint32_t q = need - pre;              // 1..4
         const int j = c0 >= q ? 0 : (c0 + c1 >= q ? 1 : (c0 + c1 + c2 >= q ? 2 : 3));
-        const int64_t lim = (gi + j + 1) * kGroup;
+        const int64_t lim = ((gi + j) / 4 * ss + 1) * kTileKeys;   // the end of its tile
         sh_lim = static_cast<uint32_t>(lim < n ? lim : n);
       }
       if (tot >= need) break;                       // uniform
@@ -2055,9 +2104,23 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
   __shared__ uint32_t preA[kMaxChunks + 1], preE[kMaxChunks + 1];
   __shared__ __attribute__((aligned(16))) uint32_t whist[kFiltThreads / 64][256];
   __shared__ __attribute__((aligned(16))) uint32_t wsum[kFiltThreads / 64];
+  __shared__ uint32_t wmx[kFiltThreads / 64];
   __shared__ uint32_t sh_digit, sh_krem, sh_fallback;
   const int tid = threadIdx.x;
   const int wid = tid >> 6;
+  // the largest candidate key over the block (hi of the bound kernel is the
+  // largest of the maxima it read, which a sampled maxima pass leaves below
+  // the row's largest score)
+  auto block_max = [&](uint32_t x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o, kWave)));
+    if ((tid & 63) == 0) wmx[wid] = x;
+    __syncthreads();
+    uint32_t y = 0;
+#pragma unroll
+    for (int w = 0; w < kFiltThreads / 64; ++w) y = max(y, wmx[w]);
+    return y;
+  };
   const FiltRow row = filt_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, q_pos, m, k, idx_out, score_out);
   if (row.n <= k) {                                      // every visible entry, then -1
     // (rows without stored scores are never this short: the host sends only
@@ -2073,7 +2136,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
     if (have_scores) select_passes_t<kFiltThreads>(row, k, key16, hist, wsum, &sh_digit, &sh_krem);
     return;
   }
-  const uint32_t lo = fw.bound[2 * row.r], hi = fw.bound[2 * row.r + 1];
+  const uint32_t lo = fw.bound[2 * row.r];
   // per-chunk counts -> exclusive prefixes preA / preE over the chunks
   constexpr int CPT = kMaxChunks / kFiltThreads;
   uint32_t ca[CPT], ce[CPT], sa = 0, se = 0;
@@ -2133,6 +2196,10 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
 #pragma unroll
       for (int q = 0; q < kRunMax; ++q) rk[q] = rc[q] >= 0 ? ckr[rc[q]] : 0u;
     }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int q = 0; q < kRunMax; ++q) mx = rc[q] >= 0 ? max(mx, rk[q]) : mx;
+    const uint32_t hi = block_max(mx);
     uint32_t thr, krem;
     if (G <= static_cast<uint32_t>(kStageKeys)) {
       // stage the keys; every wave finds the k-th largest on its own (no barriers)
@@ -2181,7 +2248,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
       if (rc[q] < 0) continue;
       bool take = rk[q] > thr;
       if (rk[q] == thr) take = eq_rank++ < krem;
-      if (take) {
+      if (take && pos < static_cast<uint32_t>(k)) {       // (never past k; the bound keeps a bad row in its row)
         row.io[pos] = cir[rc[q]];
         if (row.so) row.so[pos] = key_score(rk[q], key16);
         ++pos;
@@ -2192,6 +2259,11 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
   if (above) {
     // more candidates than the threads hold: streamed from their chunk lists,
     // radix passes over all of them, then the output chunk by chunk
+    uint32_t mx = 0;
+    for (int ch = 0; ch < nch; ++ch)
+      for (uint32_t i = tid; i < preA[ch + 1] - preA[ch]; i += kFiltThreads)
+        mx = max(mx, ckr[static_cast<int64_t>(ch) * fw.capc + i]);
+    const uint32_t hi = block_max(mx);
     uint32_t base = lo + 1u, krem = static_cast<uint32_t>(k);
     uint64_t width = static_cast<uint64_t>(hi) - lo;
     while (width > 1) {
@@ -2225,8 +2297,8 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
         const uint32_t pg = block_excl_scan_t<kFiltThreads>(gt, wsum, &tg);
         const uint32_t pe = block_excl_scan_t<kFiltThreads>(eq, wsum, &te);
         const uint32_t eq_rank = run_eq + pe;
-        if (gt || (eq && eq_rank < krem)) {
-          const uint32_t pos = run_gt + pg + min(eq_rank, krem);
+        const uint32_t pos = run_gt + pg + min(eq_rank, krem);
+        if ((gt || (eq && eq_rank < krem)) && pos < static_cast<uint32_t>(k)) {
           row.io[pos] = cir[ci];
           if (row.so) row.so[pos] = key_score(kk, key16);
         }
@@ -2265,6 +2337,7 @@ __global__ __launch_bounds__(kFiltThreads) void topk_final_kernel(
         else hi_i = mid;
       }
       const uint32_t pos = off + r + lo_i;
+      if (pos >= static_cast<uint32_t>(k)) continue;
       row.io[pos] = x;
       if (row.so) row.so[pos] = is_a ? key_score(kk[r], key16) : lo_score;
     }
@@ -2343,7 +2416,8 @@ bool cand_mode(const IndexArgs& a) {
 // key ranges of the tiled kernel: about 2048 workgroups over (keys, queries);
 // in candidate mode at most kMaxChunks ranges (the final kernel's count
 // table) of at most 32768 keys (the counts pack in 16 bits)
-void tiled_ranges(const IndexArgs& a, int64_t nv_max, int tcn, bool cands, int64_t* kc_out, int64_t* per_out) {
+void tiled_ranges(const IndexArgs& a, int64_t nv_max, int tcn, bool cands, int64_t* kc_out, int64_t* per_out,
+                  int ss = 1) {
   const int qpwg = 4 * 4 * (16 / a.H_I);
   const int64_t n_qt = (tcn + qpwg - 1) / qpwg;
   int64_t kc = (2048 + n_qt * a.B - 1) / (n_qt * a.B);
@@ -2355,9 +2429,24 @@ void tiled_ranges(const IndexArgs& a, int64_t nv_max, int tcn, bool cands, int64
   }
   if (kc < 1) kc = 1;
   int64_t per = (nv_max + kc - 1) / kc;
-  per = (per + kTileKeys - 1) / kTileKeys * kTileKeys;
+  const int64_t span = int64_t(kTileKeys) * ss;     // whole sampling periods per range
+  per = (per + span - 1) / span * span;
   *kc_out = (nv_max + per - 1) / per;
   *per_out = per;
+}
+
+// The maxima pass of candidate mode scores every ss-th tile of 64 keys. The
+// bound from those maxima is looser (about ss times the candidates, whose
+// exact comparisons and stores the candidate pass pays), so ss grows only
+// while the shortest row of the chunk keeps at least kSampleGroups k sampled
+// groups, and to 2 at most (1M-token prefill, per step: 4.80 ms at 1, 4.53 at
+// 2, 4.70 at 4).
+constexpr int kMaxSample = 2;
+constexpr int kSampleGroups = 3;
+int maxima_sample(const IndexArgs& a, int64_t nv_min) {
+  int ss = 1;
+  while (ss < kMaxSample && nv_min / (int64_t(kTileKeys) * 2 * ss) * 4 >= int64_t(kSampleGroups) * a.k) ss *= 2;
+  return ss;
 }
 
 // candidate slots per row in candidate mode: 2 per key of every range
@@ -2421,7 +2510,7 @@ size_t index_topk_workspace(const IndexArgs& a) { return index_ws(a, nullptr).by
 
 template <int MODE>
 void launch_tiled(LaunchScope& scope, const IndexArgs& a, int64_t kc, int tcn, float* sc, int64_t ld, int t_off,
-                  int Tc, int64_t per, bool key16, SelAux aux) {
+                  int Tc, int64_t per, bool key16, SelAux aux, int ss = 1) {
   const uint16_t* q = static_cast<const uint16_t*>(a.qI);
   const uint16_t* k = static_cast<const uint16_t*>(a.kI);
   const int qpwg = 4 * 4 * (16 / a.H_I);
@@ -2431,9 +2520,9 @@ void launch_tiled(LaunchScope& scope, const IndexArgs& a, int64_t kc, int tcn, f
   const int kci = static_cast<int>(kc);
 #define LCA_TILED(H)                                                                                         \
   (key16 ? scope.launch(index_score_tiled_kernel<H, MODE, true>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, \
-                        a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, aux, kci, nq, a.B)                 \
+                        a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, aux, kci, nq, a.B, ss)             \
          : scope.launch(index_score_tiled_kernel<H, MODE, false>, grid, dim3(kScoreThreads), 0, q, a.w, k, sc, ld, \
-                        a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, aux, kci, nq, a.B))
+                        a.Tq, t_off, Tc, a.N_cap, a.q_pos0, a.q_pos, a.m, per, aux, kci, nq, a.B, ss))
   switch (a.H_I) {
     case 1:
       if constexpr (MODE == kTiledScores) LCA_TILED(1);
@@ -2478,23 +2567,26 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
     int64_t nv_max = n_visible(a.q_pos0 + t_off + tcn - 1, a.m);
     if (nv_max > a.N_cap) nv_max = a.N_cap;
     if (cm) {
-      // no scores stored: maxima, bound, candidates, final
+      // no scores stored: maxima (of every ss-th tile), bound, candidates, final
+      int64_t nv_min = n_visible(a.q_pos0 + t_off, a.m);
+      if (nv_min > a.N_cap) nv_min = a.N_cap;
+      const int ss = maxima_sample(a, nv_min);
       int64_t kc, per;
-      tiled_ranges(a, nv_max, tcn, true, &kc, &per);
+      tiled_ranges(a, nv_max, tcn, true, &kc, &per, ss);
       FiltWs fw = w.fw;
       fw.nchs = static_cast<int>(kc);
       fw.capc = static_cast<int>(2 * per);
       SelAux aux{fw.gmax, fw.ldg, fw.bound, fw.ckey, fw.cidx, fw.cnt, fw.nchs, fw.capc, fw.lim};
       {
         LaunchScope scope(s, "index_score");
-        launch_tiled<kTiledMaxima>(scope, a, kc, tcn, nullptr, ld, t_off, Tc, per, key16, aux);
+        launch_tiled<kTiledMaxima>(scope, a, kc, tcn, nullptr, ld, t_off, Tc, per, key16, aux, ss);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
       }
       {
         LaunchScope scope(s, "topk_select");
         scope.launch(topk_bound_kernel, dim3(1, tcn, a.B), dim3(kFiltThreads), 0, fw, a.N_cap, Tc, a.q_pos0,
-                     a.q_pos, t_off, a.m, a.k, key16);
+                     a.q_pos, t_off, a.m, a.k, key16, ss);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
       }
@@ -2584,7 +2676,7 @@ hipError_t launch_index_topk(hipStream_t s, const IndexArgs& a, void* ws, size_t
                        t_off, Tc, a.q_pos0, a.q_pos, a.m, a.k, key16);
         } else {
           scope.launch(topk_bound_kernel, dim3(1, tcn, a.B), dim3(kFiltThreads), 0, w.fw, a.N_cap, Tc, a.q_pos0,
-                       a.q_pos, t_off, a.m, a.k, key16);
+                       a.q_pos, t_off, a.m, a.k, key16, 1);
           scope.launch(topk_chunk_kernel<0>, grid, dim3(kFiltThreads), 0, scs, ld, w.fw, a.N_cap, a.Tq, t_off, Tc,
                        a.q_pos0, a.q_pos, a.m, a.k, key16);
         }

@@ -528,9 +528,10 @@ def test_index_topk_long_exact_order(case, bf16_scores):
     np.testing.assert_array_equal(gs[0, 0], sc[want].astype(np.float32))
 
 
-@pytest.mark.parametrize("case,H_I", [("mixed_w", 4), ("cluster", 4), ("mixed_w", 2), ("mixed_w", 8)])
+@pytest.mark.parametrize("case,H_I,k", [("mixed_w", 4, 1024), ("cluster", 4, 1024), ("mixed_w", 2, 1024),
+                                        ("mixed_w", 8, 1024), ("mixed_w", 4, 256), ("cluster", 16, 256)])
 @pytest.mark.parametrize("bf16_scores", [False, True])
-def test_index_topk_prefill_without_stored_scores(case, H_I, bf16_scores):
+def test_index_topk_prefill_without_stored_scores(case, H_I, k, bf16_scores):
     # Many queries over long lists take the prefill path that stores no
     # scores: tiled scoring writes group maxima, the bound kernel bounds each
     # row, tiled scoring runs again and writes only the candidates, the final
@@ -540,10 +541,12 @@ def test_index_topk_prefill_without_stored_scores(case, H_I, bf16_scores):
     # cluster: the highest scores of every query crowd 3 key ranges, more
     # candidates than the final workgroup holds in registers. H_I = 2 puts
     # two queries in each lane's accumulators, H_I = 8 one query in two lane
-    # groups.
+    # groups. The maxima pass takes every second 64-key tile (140000
+    # entries: 4375 such groups, at least 3 k), so the bound comes from a
+    # sample of the maxima.
     L = need_gpu()
-    rng = np.random.default_rng(540 + 3 * bf16_scores + len(case) + H_I)
-    B, Tq, d_I, m, k = 1, 70, 128, 4, 1024
+    rng = np.random.default_rng(540 + 3 * bf16_scores + len(case) + H_I + k)
+    B, Tq, d_I, m = 1, 70, 128, 4
     q_pos0 = 4 * 140000
     N_cap = (q_pos0 + Tq) // m + 3
     qI = rng.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.float32)
@@ -555,7 +558,7 @@ def test_index_topk_prefill_without_stored_scores(case, H_I, bf16_scores):
         kI[0, 60000:63072] *= 3
     idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
     sco = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
-    say(f"prefill without stored scores {case} H_I={H_I} bf16={bf16_scores}")
+    say(f"prefill without stored scores {case} H_I={H_I} k={k} bf16={bf16_scores}")
     L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0,
                      flags=L.SCORE_BF16 if bf16_scores else 0, score_out=sco)
     torch.cuda.synchronize()
@@ -598,14 +601,18 @@ def test_index_topk_prefill_without_stored_scores_ragged_query_tiles():
         assert np.all(np.diff(sel) > 0), "indices not increasing"
 
 
-def test_index_topk_prefill_without_stored_scores_all_ties():
+@pytest.mark.parametrize("k", [1024, 256, 128])
+def test_index_topk_prefill_without_stored_scores_all_ties(k):
     # Every key identical, so every score of a row ties: the bound equals the
     # row's largest key, the bound kernel limits the candidates to the groups
     # up to the k-th one, and the answer is the k lowest indices. Odd queries
-    # take negative head weights (their ties sit below zero or at zero).
+    # take negative head weights (their ties sit below zero or at zero). The
+    # maxima pass takes every tile at k = 1024 and every second one at
+    # k = 256 and 128 (40000 entries); the limit is then the end of the tile
+    # of the k-th sampled group.
     L = need_gpu()
-    rng = np.random.default_rng(570)
-    B, Tq, H_I, d_I, m, k = 1, 66, 4, 128, 4, 1024
+    rng = np.random.default_rng(570 + k)
+    B, Tq, H_I, d_I, m = 1, 66, 4, 128, 4
     q_pos0 = 4 * 40000 + 2
     N_cap = (q_pos0 + Tq) // m + 1
     kI = np.tile(rng.integers(-4, 5, size=(1, 1, d_I)), (B, N_cap, 1)).astype(np.float32)
@@ -613,7 +620,7 @@ def test_index_topk_prefill_without_stored_scores_all_ties():
     w = np.tile(np.array([0.5, 0.25, 1.0, 0.125], np.float32), (B, Tq, 1))
     w[:, 1::2] *= -1
     idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
-    say("prefill without stored scores, every score tied")
+    say(f"prefill without stored scores, every score tied, k={k}")
     L.csa_index_topk(L.BF16, dev_bf16(qI), dev_f32(w), dev_bf16(kI), idx, m=m, k=k, q_pos0=q_pos0)
     torch.cuda.synchronize()
     got = idx.cpu().numpy()
