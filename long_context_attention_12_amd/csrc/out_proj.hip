@@ -12,8 +12,8 @@
 // weight ([N, K], row n = output channel n), bf16 operands, fp32 sums, bf16
 // results (the intermediate stays bf16 as the operand of the second stage).
 // At decode the rows are few (16 - 64) and the weights are many (128 MB for
-// Flash): the kernel is a weight stream. A workgroup owns 16 output columns;
-// its eight waves take an eighth of K each, load their weight rows with
+// Flash): the kernel is a weight stream. A workgroup owns 16, 32 or 64 output
+// columns (one to four 16-column MFMA tiles); its eight waves take an eighth of K each, load their weight rows with
 // 16-byte loads straight into MFMA operands (a batch of 4 - 8 steps in flight
 // behind the one being summed), and keep every row of the block in up to four
 // 16-row MFMA tiles, so each weight byte is read once per 64 rows. The eight
@@ -28,54 +28,66 @@ namespace {
 constexpr int kProjWaves = 8;                      // waves per workgroup, one eighth of K each
 constexpr int kProjThreads = 64 * kProjWaves;
 
-// Batch of U K-steps (32 each) of one wave: B fragments of its 16 columns and
-// A fragments of its MT row tiles, 16 bytes per lane per fragment.
-template <int MT, int U>
+// Batch of U K-steps (32 each) of one wave: B fragments of its NT column
+// tiles and A fragments of its MT row tiles, 16 bytes per lane per fragment.
+template <int MT, int NT, int U>
 struct ProjBatch {
-  bf16x8 b[U];
+  bf16x8 b[NT][U];
   bf16x8 a[MT][U];
 };
 
-template <int MT, int U>
-__device__ __forceinline__ void proj_load(ProjBatch<MT, U>& x, const uint16_t* bp, const uint16_t* const (&ap)[MT],
-                                          int ks) {
+template <int MT, int NT, int U>
+__device__ __forceinline__ void proj_load(ProjBatch<MT, NT, U>& x, const uint16_t* const (&bp)[NT],
+                                          const uint16_t* const (&ap)[MT], int ks) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    x.b[u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bp + ks + 32 * u));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      x.b[nt][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bp[nt] + ks + 32 * u));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       x.a[mt][u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ap[mt] + ks + 32 * u));
   }
 }
 
-template <int MT, int U>
-__device__ __forceinline__ void proj_mfma(const ProjBatch<MT, U>& x, f32x4 (&acc)[MT]) {
+template <int MT, int NT, int U>
+__device__ __forceinline__ void proj_mfma(const ProjBatch<MT, NT, U>& x, f32x4 (&acc)[MT][NT]) {
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.a[mt][u], x.b[u], acc[mt], 0, 0, 0);
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.a[mt][u], x.b[nt][u], acc[mt][nt], 0, 0, 0);
 }
 
 // C[m, n] = sum_k A[m, k] B[n, k] for the rows [m0, m0 + 16 MT) and columns
-// [n0, n0 + 16) of group blockIdx.y. Wave w sums K in [w K/8, (w + 1) K/8) in
-// batches of U steps, the next batch's loads in flight while the current one
-// feeds the MFMAs; the eight partial tiles add in a fixed order.
-template <int MT>
+// [n0, n0 + 16 NT) of group blockIdx.y. Wave w sums K in [w K/8, (w + 1) K/8)
+// in batches of U steps, the next batch's loads in flight while the current
+// one feeds the MFMAs; the eight partial tiles add in a fixed order. Every
+// A fragment a wave loads feeds NT column tiles, so the rows' activations are
+// read from the L2 once per 16 NT columns. Each column's sum is the same MFMA
+// chain whatever NT is, so its bits do not depend on NT.
+template <int MT, int NT>
 __global__ __launch_bounds__(kProjThreads) void proj_nt_kernel(const uint16_t* __restrict__ A, int64_t lda,
                                                                int64_t a_group, const uint16_t* __restrict__ Bw,
                                                                int64_t b_group, uint16_t* __restrict__ C,
                                                                int64_t ldc, int64_t c_group, int M, int K) {
-  constexpr int U = MT <= 2 ? 4 : 2;              // two batches of U steps in flight (registers for 2+ workgroups per CU)
-  __shared__ float red[kProjWaves][MT * 256];
+  // two batches of U steps in flight (registers for 2+ workgroups per CU)
+  constexpr int U = MT + NT <= 3 ? 4 : 2;
+  __shared__ float red[kProjWaves][MT * NT * 256];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int gi = blockIdx.y;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * NT;
   const int m0 = blockIdx.z * 16 * MT;
   const int kq = K / kProjWaves, k0 = wid * kq;
   const int kk = 8 * (lane >> 4);                  // the lane's 8 K values in each step of 32
-  // lane l: column n0 + l % 16 of B, rows m0 + 16 mt + l % 16 of A (rows past M
-  // read row M - 1, and their results are dropped)
-  const uint16_t* bp = Bw + gi * b_group + static_cast<int64_t>(n0 + (lane & 15)) * K + k0 + kk;
+  // lane l: columns n0 + 16 nt + l % 16 of B, rows m0 + 16 mt + l % 16 of A
+  // (rows past M read row M - 1, and their results are dropped)
+  const uint16_t* bp[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    bp[nt] = Bw + gi * b_group + static_cast<int64_t>(n0 + 16 * nt + (lane & 15)) * K + k0 + kk;
   const uint16_t* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -83,41 +95,50 @@ __global__ __launch_bounds__(kProjThreads) void proj_nt_kernel(const uint16_t* _
     if (r > M - 1) r = M - 1;
     ap[mt] = A + gi * a_group + static_cast<int64_t>(r) * lda + k0 + kk;
   }
-  f32x4 acc[MT];
+  f32x4 acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nb = kq / (32 * U);                    // whole batches
-  ProjBatch<MT, U> x0, x1;
-  if (nb > 0) proj_load<MT, U>(x0, bp, ap, 0);
+  ProjBatch<MT, NT, U> x0, x1;
+  if (nb > 0) proj_load<MT, NT, U>(x0, bp, ap, 0);
   for (int j = 0; j < nb; j += 2) {
-    if (j + 1 < nb) proj_load<MT, U>(x1, bp, ap, (j + 1) * 32 * U);
-    proj_mfma<MT, U>(x0, acc);
-    if (j + 2 < nb) proj_load<MT, U>(x0, bp, ap, (j + 2) * 32 * U);
-    if (j + 1 < nb) proj_mfma<MT, U>(x1, acc);
+    if (j + 1 < nb) proj_load<MT, NT, U>(x1, bp, ap, (j + 1) * 32 * U);
+    proj_mfma<MT, NT, U>(x0, acc);
+    if (j + 2 < nb) proj_load<MT, NT, U>(x0, bp, ap, (j + 2) * 32 * U);
+    if (j + 1 < nb) proj_mfma<MT, NT, U>(x1, acc);
   }
   for (int ks = nb * 32 * U; ks < kq; ks += 32) {
-    const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bp + ks));
+    bf16x8 b1[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) b1[nt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bp[nt] + ks));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ap[mt] + ks));
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[mt], 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[nt], acc[mt][nt], 0, 0, 0);
     }
   }
   // lane l holds C rows 4 (l / 16) + i, column l % 16 of each tile
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wid][mt * 256 + lane * 4 + i] = acc[mt][i];
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wid][(mt * NT + nt) * 256 + lane * 4 + i] = acc[mt][nt][i];
   __syncthreads();
   uint16_t* c = C + gi * c_group;
-  for (int e = threadIdx.x; e < MT * 256; e += kProjThreads) {
-    const int mt = e >> 8, el = e & 255;
+  for (int e = threadIdx.x; e < MT * NT * 256; e += kProjThreads) {
+    const int tile = e >> 8, el = e & 255;
+    const int mt = tile / NT, nt = tile % NT;
     const int row = 4 * ((el >> 2) >> 4) + (el & 3), col = (el >> 2) & 15;
     float v = red[0][e];
 #pragma unroll
     for (int w = 1; w < kProjWaves; ++w) v += red[w][e];
     const int m = m0 + 16 * mt + row;
-    if (m < M) c[static_cast<int64_t>(m) * ldc + n0 + col] = f32_to_bf16(v);
+    if (m < M) c[static_cast<int64_t>(m) * ldc + n0 + 16 * nt + col] = f32_to_bf16(v);
   }
 }
 
@@ -268,11 +289,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_nt_tiled_kernel(
     }
 }
 
+template <int MT, int NT>
+void launch_proj_nt(LaunchScope& sc, const uint16_t* A, int64_t lda, int64_t a_group, const uint16_t* Bw,
+                    int64_t b_group, uint16_t* C, int64_t ldc, int64_t c_group, int M, int N, int K, int groups) {
+  const dim3 grid(N / (16 * NT), groups, (M + 16 * MT - 1) / (16 * MT));
+  sc.launch(proj_nt_kernel<MT, NT>, grid, dim3(kProjThreads), 0, A, lda, a_group, Bw, b_group, C, ldc, c_group, M, K);
+}
+
+// Column tiles per workgroup: the most (up to four) that still leave the
+// launch at least kProjMinWG workgroups. More columns per workgroup read the
+// activations from the L2 fewer times (Pro decode, 64 rows: the first stage
+// 74 -> 36 us with four tiles, the second 144 -> 91 us with two); fewer than
+// about 200 workgroups leave CUs idle (Flash second stage at 16 rows: 17 us with
+// one tile and 256 workgroups, 24 us with two and 128).
+constexpr int64_t kProjMinWG = 200;
+
 template <int MT>
 void launch_proj(LaunchScope& sc, const uint16_t* A, int64_t lda, int64_t a_group, const uint16_t* Bw,
                  int64_t b_group, uint16_t* C, int64_t ldc, int64_t c_group, int M, int N, int K, int groups) {
-  const dim3 grid(N / 16, groups, (M + 16 * MT - 1) / (16 * MT));
-  sc.launch(proj_nt_kernel<MT>, grid, dim3(kProjThreads), 0, A, lda, a_group, Bw, b_group, C, ldc, c_group, M, K);
+  const int64_t rb = (M + 16 * MT - 1) / (16 * MT);
+  auto fits = [&](int nt) { return N % (16 * nt) == 0 && static_cast<int64_t>(N / (16 * nt)) * groups * rb >= kProjMinWG; };
+  const int nt = fits(4) ? 4 : fits(2) ? 2 : 1;
+  if (nt == 4) launch_proj_nt<MT, 4>(sc, A, lda, a_group, Bw, b_group, C, ldc, c_group, M, N, K, groups);
+  else if (nt == 2) launch_proj_nt<MT, 2>(sc, A, lda, a_group, Bw, b_group, C, ldc, c_group, M, N, K, groups);
+  else launch_proj_nt<MT, 1>(sc, A, lda, a_group, Bw, b_group, C, ldc, c_group, M, N, K, groups);
 }
 
 void launch_proj_any(LaunchScope& sc, const uint16_t* A, int64_t lda, int64_t a_group, const uint16_t* Bw,

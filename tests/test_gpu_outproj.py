@@ -108,3 +108,21 @@ def test_grouped_out_proj_tiled_edges(T, g):
     pm = L.lca_grouped_out_proj(od[lo:hi].contiguous(), wgd, wod, part)
     torch.cuda.synchronize()
     assert torch.equal(pm, mid[lo:hi]) and torch.equal(part, full[lo:hi]), f"rows {lo}:{hi}"
+
+
+def test_grouped_out_proj_column_tiles_keep_their_bits():
+    # 100 rows (two 64-row blocks) give the first stage 256 workgroups with
+    # four 16-column tiles each; 64 rows (one block) take two tiles per
+    # workgroup: a column's MFMA chain is the same, so are its bits
+    L = need_gpu()
+    rng = np.random.default_rng(250)
+    o, w_g, w_o = _case(rng, 100, 16, 128, 8, 1024, 64)
+    say("grouped out proj: column tiles per workgroup vs row subsets")
+    mid, full = _check(L, o, w_g, w_o, "column tiles T=100")
+    od, wgd, wod = dev_bf16(o), dev_bf16(w_g), dev_bf16(w_o)
+    for lo, hi in ((0, 64), (36, 100), (50, 66)):
+        part = torch.empty((hi - lo, 64), dtype=torch.bfloat16, device=DEV)
+        pm = L.lca_grouped_out_proj(od[lo:hi].contiguous(), wgd, wod, part)
+        torch.cuda.synchronize()
+        assert torch.equal(pm, mid[lo:hi]), f"intermediate rows {lo}:{hi}"
+        assert torch.equal(part, full[lo:hi]), f"rows {lo}:{hi}"
