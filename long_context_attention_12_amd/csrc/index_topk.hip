@@ -1011,6 +1011,50 @@ __device__ __forceinline__ void load_round(const float* __restrict__ s, int64_t 
   }
 }
 
+// One register round in the thread-contiguous layout of load_round, fetched
+// coalesced: wave w reads its kSelItems * 64 scores as 1 KB rows (lane l: 16
+// bytes at 256 q + 4 l), parks them in its own 8 KB of LDS, and each lane
+// reads back its kSelItems consecutive scores. Read straight from memory,
+// each load instruction of load_round spreads over 64 cache lines. The 16-byte
+// slot f of a wave's block sits at f ^ ((f >> 4) & 15), which keeps both the
+// row-wise writes and the lane-contiguous reads free of bank conflicts. stage:
+// kRound floats; the caller syncs the block before reusing it.
+__device__ __forceinline__ void load_round_staged(const float* __restrict__ s, int64_t n, bool key16,
+                                                  uint32_t (&key)[kSelItems], float4* stage) {
+  constexpr int NQ = kSelItems / 4;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t i0 = static_cast<int64_t>(w) * (64 * kSelItems) + 4 * lane;
+  const float pad = __uint_as_float(0xffffffffu);  // key 0: "no element"
+  float4 v[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t i = i0 + 256 * q;
+    if (i + 4 <= n) {
+      v[q] = *reinterpret_cast<const float4*>(s + i);
+    } else {
+      v[q].x = i + 0 < n ? s[i + 0] : pad;
+      v[q].y = i + 1 < n ? s[i + 1] : pad;
+      v[q].z = i + 2 < n ? s[i + 2] : pad;
+      v[q].w = pad;
+    }
+  }
+  float4* st = stage + (64 * kSelItems / 4) * w;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int f = 64 * q + lane;
+    st[f ^ ((f >> 4) & 15)] = v[q];
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int f = NQ * lane + q;
+    const float4 u = st[f ^ ((f >> 4) & 15)];
+    key[4 * q + 0] = score_key(u.x, key16);
+    key[4 * q + 1] = score_key(u.y, key16);
+    key[4 * q + 2] = score_key(u.z, key16);
+    key[4 * q + 3] = score_key(u.w, key16);
+  }
+}
+
 // Histogram of one digit is in hist[0, nb); find the digit whose bin holds the
 // krem-th largest element (bins scanned in descending digit order) and that
 // element's rank inside the bin. Four bins per thread; on return the result
@@ -1262,10 +1306,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t N_cap, int Tq, int t_off, int Tc,
     int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int k, bool key16, int32_t* __restrict__ idx_out,
     float* __restrict__ score_out) {
-  __shared__ uint32_t hist[kMaxBins];
+  // the staging area of the coalesced load, then the histogram and candidates
+  __shared__ __attribute__((aligned(16))) uint32_t pool[kRound];
+  static_assert(kMaxBins + 2 * kCandCap <= kRound, "LDS pool");
+  uint32_t* hist = pool;
+  uint32_t* ckey = pool + kMaxBins;
+  int32_t* cidx = reinterpret_cast<int32_t*>(pool + kMaxBins + kCandCap);
   __shared__ __attribute__((aligned(16))) uint32_t wsum[kSelThreads / 64];
-  __shared__ __attribute__((aligned(16))) uint32_t ckey[kCandCap];
-  __shared__ int32_t cidx[kCandCap];
   __shared__ uint32_t sh_digit, sh_krem, sh_hi;
   const SelRow row = sel_row(scores, ld, N_cap, Tq, t_off, Tc, q_pos0, q_pos, m, k, idx_out, score_out);
   if (row.n <= k) {
@@ -1275,7 +1322,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   // threads holding a score: (n + kSelItems - 1) / kSelItems, one round (n <= kRound here)
   if ((row.n + kSelItems - 1) / kSelItems >= 2 * static_cast<int64_t>(k)) {
     uint32_t key[kSelItems];
-    load_round(row.s, row.n, 0, key16, key);
+    load_round_staged(row.s, row.n, key16, key, reinterpret_cast<float4*>(pool));
+    __syncthreads();                 // every wave has read its staged scores back
     if (select_filtered(row, k, key16, key, hist, wsum, ckey, cidx, &sh_digit, &sh_krem, &sh_hi)) return;
     __syncthreads();                 // candidate and histogram memory are reused below
   }
