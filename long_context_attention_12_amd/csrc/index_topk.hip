@@ -1205,6 +1205,7 @@ __device__ __forceinline__ void select_by_passes(const SelRow& row, int k, bool 
 // nothing, when the candidates exceed kCandCap.
 constexpr int kCandCap = 4096;
 constexpr int kCandPer = kCandCap / kSelThreads;
+constexpr int kFewMax = 64;        // boundary-bin candidates one wave ranks directly
 
 __device__ __forceinline__ bool select_filtered(const SelRow& row, int k, bool key16,
                                                 const uint32_t (&key)[kSelItems], uint32_t* hist, uint32_t* wsum,
@@ -1214,6 +1215,7 @@ __device__ __forceinline__ bool select_filtered(const SelRow& row, int k, bool k
   uint32_t& sh_krem = *sh_krem_p;
   const int tid = threadIdx.x;
   const int top = key16 ? 4 : 20;                  // shift of the key's top 12-bit digit
+  __shared__ uint32_t sh_nfew, few[kFewMax];       // a boundary bin's few candidates (any order)
   uint32_t mx = 0;
 #pragma unroll
   for (int j = 0; j < kSelItems; ++j) mx = max(mx, key[j]);
@@ -1221,7 +1223,10 @@ __device__ __forceinline__ bool select_filtered(const SelRow& row, int k, bool k
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) wmx = max(wmx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(wmx), o, kWave)));
   for (int i = tid; i < kMaxBins; i += kSelThreads) hist[i] = 0;
-  if (tid == 0) *sh_hi_p = 0;
+  if (tid == 0) {
+    *sh_hi_p = 0;
+    sh_nfew = 0;
+  }
   __syncthreads();
   if (mx != 0u) atomicAdd(&hist[mx >> top], 1u);
   if ((tid & 63) == 0) atomicMax(sh_hi_p, wmx);
@@ -1273,6 +1278,38 @@ __device__ __forceinline__ bool select_filtered(const SelRow& row, int k, bool k
     base += sh_digit << sh;
     krem = sh_krem;
     width = uint64_t(1) << sh;
+    const uint32_t nbin = hist[sh_digit];           // candidates in [base, base + width)
+    __syncthreads();                                 // read by all before a next pass clears it
+    if (width > 1 && nbin <= static_cast<uint32_t>(kFewMax)) {
+      // A boundary bin of at most 64 candidates (the usual case after one
+      // digit: the k-th largest sits a few key steps above its neighbours):
+      // one wave ranks them by comparison instead of more block-wide passes.
+      // Key v is the threshold when (#keys > v) < krem <= (#keys >= v);
+      // krem becomes krem - (#keys > v), as the remaining digits would give.
+#pragma unroll
+      for (int q = 0; q < kCandPer; ++q) {
+        const uint32_t off = ck[q] - base;
+        if (ck[q] != 0u && static_cast<uint64_t>(off) < width) few[atomicAdd(&sh_nfew, 1u)] = ck[q];
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const uint32_t mine = tid < static_cast<int>(nbin) ? few[tid] : 0u;
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t j = 0; j < nbin; ++j) {
+          const uint32_t o = few[j];
+          gt += o > mine;
+          ge += o >= mine;
+        }
+        if (tid < static_cast<int>(nbin) && gt < krem && krem <= ge) {
+          sh_digit = mine;                           // equal keys write equal values
+          sh_krem = krem - gt;
+        }
+      }
+      __syncthreads();
+      base = sh_digit;
+      krem = sh_krem;
+      break;
+    }
   }
   const uint32_t thr = base;       // key of the k-th largest score
 
