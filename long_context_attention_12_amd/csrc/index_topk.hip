@@ -1195,7 +1195,9 @@ __device__ __forceinline__ void select_by_passes(const SelRow& row, int k, bool 
 // Short lists whose threads hold at least 2k scores' worth of maxima: each
 // thread's largest key is a score of the list, so the lower edge `lo` of the
 // top-digit bin holding the k-th largest of those maxima has at least k scores
-// at or above it, and the k-th largest score is at or above `lo`. Only the
+// at or above it, and the k-th largest score is at or above `lo`. Lists too
+// short for 2k thread maxima (ragged batches) take four maxima per thread, one
+// per run of 8 scores (fine): the same bound over smaller disjoint groups. Only the
 // scores from `lo` up (a few percent of a list, typically) are candidates:
 // they go to LDS in increasing index order, and their digits are taken on the
 // offset key - lo over [lo, max key] (12 bits at a time, from the top), which
@@ -1210,7 +1212,7 @@ constexpr int kFewMax = 64;        // boundary-bin candidates one wave ranks dir
 __device__ __forceinline__ bool select_filtered(const SelRow& row, int k, bool key16,
                                                 const uint32_t (&key)[kSelItems], uint32_t* hist, uint32_t* wsum,
                                                 uint32_t* ckey, int32_t* cidx, uint32_t* sh_digit_p,
-                                                uint32_t* sh_krem_p, uint32_t* sh_hi_p) {
+                                                uint32_t* sh_krem_p, uint32_t* sh_hi_p, bool fine) {
   uint32_t& sh_digit = *sh_digit_p;
   uint32_t& sh_krem = *sh_krem_p;
   const int tid = threadIdx.x;
@@ -1228,7 +1230,14 @@ __device__ __forceinline__ bool select_filtered(const SelRow& row, int k, bool k
     sh_nfew = 0;
   }
   __syncthreads();
-  if (mx != 0u) atomicAdd(&hist[mx >> top], 1u);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {                    // fine: the maxima of the runs of 8; else mx alone
+    uint32_t mq = 0;
+#pragma unroll
+    for (int j = 8 * c; j < 8 * c + 8; ++j) mq = max(mq, key[j]);
+    const uint32_t v = fine ? mq : (c == 0 ? mx : 0u);
+    if (v != 0u) atomicAdd(&hist[v >> top], 1u);
+  }
   if ((tid & 63) == 0) atomicMax(sh_hi_p, wmx);
   __syncthreads();
   find_digit(hist, kMaxBins, static_cast<uint32_t>(k), wsum, &sh_digit, &sh_krem);
@@ -1356,12 +1365,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     select_all(row, k);
     return;
   }
-  // threads holding a score: (n + kSelItems - 1) / kSelItems, one round (n <= kRound here)
-  if ((row.n + kSelItems - 1) / kSelItems >= 2 * static_cast<int64_t>(k)) {
+  // threads holding a score: (n + kSelItems - 1) / kSelItems, one round (n <= kRound here);
+  // below 2k of them, runs of 8 scores: (n + 7) / 8
+  if ((row.n + 7) / 8 >= 2 * static_cast<int64_t>(k)) {
+    const bool fine = (row.n + kSelItems - 1) / kSelItems < 2 * static_cast<int64_t>(k);
     uint32_t key[kSelItems];
     load_round_staged(row.s, row.n, key16, key, reinterpret_cast<float4*>(pool));
     __syncthreads();                 // every wave has read its staged scores back
-    if (select_filtered(row, k, key16, key, hist, wsum, ckey, cidx, &sh_digit, &sh_krem, &sh_hi)) return;
+    if (select_filtered(row, k, key16, key, hist, wsum, ckey, cidx, &sh_digit, &sh_krem, &sh_hi, fine)) return;
     __syncthreads();                 // candidate and histogram memory are reused below
   }
   select_by_passes(row, k, key16, hist, wsum, &sh_digit, &sh_krem);
