@@ -780,6 +780,22 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
   if (r_end > rs.nrows) r_end = rs.nrows;
   const int nr = r_end > r_begin ? static_cast<int>(r_end - r_begin) : 0;
 
+  // query fragments first: their loads are in flight with the row table's
+  // (a wave past the block's heads computes on zero queries and writes nothing)
+  bf16x8 qf[NHT][KS];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    if (active) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                           ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head0 + 16 * ht) * D;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        qf[ht][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[ht][s] = bf16x8{};
+    }
+  }
   // row table (its index loads all in flight together)
   int32_t myrows[kMaxSplitRows / kAttThreads];
 #pragma unroll
@@ -835,22 +851,6 @@ __global__ __launch_bounds__(kAttThreads) void attend_dma_kernel(AttendArgs a, S
 #pragma unroll
   for (int t0 = 0; t0 < kRing - 1; ++t0)
     if (t0 < ntiles) issue(t0, Xs[t0]);
-  // query fragments load while the first tiles are in flight
-  // (a wave past the block's heads computes on zero queries and writes nothing)
-  bf16x8 qf[NHT][KS];
-#pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    if (active) {
-      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                           ((static_cast<int64_t>(b) * a.Tq + t) * a.H + head0 + 16 * ht) * D;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        qf[ht][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + 32 * s + 8 * g));
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qf[ht][s] = bf16x8{};
-    }
-  }
   f32x4 acc_o[NHT][DT];
   float m_run[NHT], z_run[NHT];
   bool flag[NHT];
