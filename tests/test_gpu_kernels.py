@@ -432,7 +432,8 @@ def test_index_topk_all_ties_take_lowest_indices():
     np.testing.assert_array_equal(idx.cpu().numpy()[0, 0], np.arange(k))
 
 
-@pytest.mark.parametrize("case", ["spread", "spikes", "ragged", "small_k", "ties5", "zeros", "same"])
+@pytest.mark.parametrize("case", ["spread", "spikes", "ragged", "small_k", "ties5", "zeros", "same",
+                                  "fine", "fine_spikes", "fine_ties5"])
 @pytest.mark.parametrize("bf16_scores", [False, True])
 def test_index_topk_select_exact_order(case, bf16_scores):
     # Integer indexer vectors and power-of-two head weights make every score
@@ -442,7 +443,10 @@ def test_index_topk_select_exact_order(case, bf16_scores):
     # by the threads' maxima (spread, spikes, ragged, small_k; zeros, the exact
     # zeros of all-negative head weights, as a candidate range one key wide);
     # 5 distinct keys and one key for every entry crowd the candidates past
-    # their cap and take the full passes.
+    # their cap and take the full passes. The fine cases (12000 - 20001 entries,
+    # k = 512: fewer than 2k threads hold a score) bound the k-th score by the
+    # maxima of runs of 8 scores. With integer scores the boundary bin is often
+    # a crowd of equal keys, ranked directly when it holds at most 64.
     L = need_gpu()
     rng = np.random.default_rng(400 + len(case) + 7 * bf16_scores)
     B, Tq, H_I, d_I, m = 2, 1, 4, 128, 4
@@ -451,13 +455,15 @@ def test_index_topk_select_exact_order(case, bf16_scores):
         N_cap, k = 30001, 256
     if case == "small_k":
         k = 16
+    if case.startswith("fine"):
+        N_cap = 12000 if case == "fine" else 20001
     qI = rng.integers(-8, 9, size=(B, Tq, H_I, d_I)).astype(np.float32)
     kI = rng.integers(-8, 9, size=(B, N_cap, d_I)).astype(np.float32)
     w = np.tile(np.array([1.0, 0.5, 0.25, 0.125], np.float32), (B, Tq, 1))
-    if case == "spikes":
+    if case in ("spikes", "fine_spikes"):
         for b in range(B):
             kI[b, rng.choice(N_cap, size=N_cap // 100, replace=False)] *= 4
-    elif case == "ties5":
+    elif case in ("ties5", "fine_ties5"):
         base = rng.integers(-8, 9, size=(5, d_I)).astype(np.float32)
         kI = np.stack([base[rng.integers(0, 5, size=N_cap)] for _ in range(B)])
     elif case == "zeros":
