@@ -15,11 +15,13 @@
 //
 // Selection is an MSB-first radix select per query in one 1024-thread
 // workgroup (LDS histograms of 12/10/10-bit digits, 12/4 bits for bf16
-// scores). Up to 32768 scores stay in registers (32 per thread, loaded once,
-// all loads in flight together); longer lists are processed in rounds of
-// 32768. An order-preserving compaction follows: output indices come out in
-// increasing order and ties at the threshold go to the lowest indices, so the
-// result is deterministic.
+// scores). Up to 32768 scores stay in registers (32 consecutive scores per
+// thread, fetched once as coalesced 1 KB rows and passed through LDS into each
+// thread's run); longer lists are processed in rounds of 32768. Short lists
+// first bound the k-th score by thread (or run-of-8) maxima and take only the
+// candidates above the bound through the digits. An order-preserving
+// compaction follows: output indices come out in increasing order and ties at
+// the threshold go to the lowest indices, so the result is deterministic.
 #include <type_traits>
 
 #include "lca_device.h"
