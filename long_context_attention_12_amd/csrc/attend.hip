@@ -2727,38 +2727,68 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(AttendBwdArgs p, BwdPlan bp
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int nt = 0; nt < 8; ++nt) c[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // lane l holds rows 16 mt + 4 (l / 16) + i, channel cb + 16 nt + l % 16.
+        // A tile's rows are distinct entries (or window rows) of one query, so
+        // the slot values of all eight of the lane's rows are loaded before
+        // any is written back: one memory round trip per tile, not one per row.
+        // When every head step's operands fit in registers, those loads go out
+        // first and the slot loads right after them (loads complete in issue
+        // order), so both round trips overlap and the MFMAs wait only for the
+        // operands.
+        float* dst[2][4];
+        float old[2][4][8];
+        auto slot_ptrs = [&]() {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int32_t e = src[v0 + 16 * mt + 4 * (lane >> 4) + i];
+              dst[mt][i] = e == -1 ? nullptr
+                           : (e >= 0 ? sE + static_cast<int64_t>(e) * D : sW + static_cast<int64_t>(-2 - e - t0) * D) +
+                                 cb + (lane & 15);
+            }
+        };
+        auto slot_loads = [&]() {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int nt = 0; nt < 8; ++nt) old[mt][i][nt] = dst[mt][i] ? dst[mt][i][16 * nt] : 0.f;
+        };
+        slot_ptrs();
 #pragma unroll
         for (int k0 = 0; k0 < KSH; k0 += KR) {
           if constexpr (KSH != KR) bwd_kv_load_b<KR>(dTq, qTq, H, cb, lane, k0, bD, bQ);
+          bf16x8 aP[KR][2], aL[KR][2];
 #pragma unroll
-          for (int ks = 0; ks < KR; ++ks) {
-            bf16x8 aP[2], aL[2];
+          for (int ks = 0; ks < KR; ++ks)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
               const int64_t row = c0 + v0 + 16 * mt + (lane & 15);
-              aP[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pq + row * H + 32 * (k0 + ks) + kk));
-              aL[mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Lq + row * H + 32 * (k0 + ks) + kk));
+              aP[ks][mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Pq + row * H + 32 * (k0 + ks) + kk));
+              aL[ks][mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Lq + row * H + 32 * (k0 + ks) + kk));
             }
+          if constexpr (KSH == KR) slot_loads();
+#pragma unroll
+          for (int ks = 0; ks < KR; ++ks)
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
               for (int mt = 0; mt < 2; ++mt) {
-                c[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aP[mt], bD[nt][ks], c[mt][nt], 0, 0, 0);
-                c[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aL[mt], bQ[nt][ks], c[mt][nt], 0, 0, 0);
+                c[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aP[ks][mt], bD[nt][ks], c[mt][nt], 0, 0, 0);
+                c[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aL[ks][mt], bQ[nt][ks], c[mt][nt], 0, 0, 0);
               }
-          }
         }
-        // lane l holds rows 16 mt + 4 (l / 16) + i, channel cb + 16 nt + l % 16
+        if constexpr (KSH != KR) slot_loads();
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int32_t e = src[v0 + 16 * mt + 4 * (lane >> 4) + i];
-            if (e == -1) continue;
-            float* dst = e >= 0 ? sE + static_cast<int64_t>(e) * D : sW + static_cast<int64_t>(-2 - e - t0) * D;
+          for (int i = 0; i < 4; ++i)
+            if (dst[mt][i]) {
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) dst[cb + 16 * nt + (lane & 15)] += c[mt][nt][i];
-          }
+              for (int nt = 0; nt < 8; ++nt) dst[mt][i][16 * nt] = old[mt][i][nt] + c[mt][nt][i];
+            }
       }
     }
   }
